@@ -1,0 +1,134 @@
+"""fp64 CPU oracle for Kimi Delta Attention (KDA).
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the benchmark's CPU
+baseline leg may import this package; the product path (the HIP library and its
+Python binding) never does, and shares no code with it.
+
+The arithmetic lives in ``kda_oracle.c`` (plain C, fp64, one token at a time, OpenMP over
+(sequence, head)). This module only builds/loads that file and marshals numpy arrays.
+Inputs are converted to float32 first, which is exact for bf16 and fp32 values, so the
+oracle consumes exactly the numbers the GPU received.
+
+The definition it follows is the KDA update of "Kimi Linear's Hybrid Linear Attention
+Architecture: A Technical Breakdown" section 3.3 (decay, then erase along k, then write),
+with the orientation of the update-rule code block of "Kimi Linear: How Moonshot AI Built
+a Hybrid Attention Architecture That Beats Full Attention" (S is K x V, write k v^T), and
+the output read after the write ("Kimi Linear" explainer, "Step 4: Query").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_kda_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (fp64, no fast-math) into oracle/_kda_oracle.so."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            f = lib.kda_oracle_fwd
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int32] * 4 + [
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                ctypes.c_void_p, ctypes.c_int32]
+            s = lib.kda_oracle_step
+            s.restype = ctypes.c_int
+            s.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 4 + [
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+            lib.kda_oracle_max_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    """Number of OpenMP threads the oracle uses by default."""
+    return int(_load().kda_oracle_max_threads())
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def kda_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, heads=None,
+            threads: int = 0):
+    """Token-by-token fp64 KDA forward.
+
+    q, k, log_alpha: [T, H, K]; v: [T, H, V]; beta: [T, H] (any float dtype numpy arrays).
+    cu_seqlens: [N+1] int (None = one sequence of length T).
+    init_state: [N, H, K, V] (None = zeros).
+    heads: optional list of head indices to compute (outputs then hold only those heads).
+    Returns (o [T, Hs, V] float64, final_state [N, Hs, K, V] float64).
+    """
+    lib = _load()
+    q, k, v, g, b = _f32(q), _f32(k), _f32(v), _f32(log_alpha), _f32(beta)
+    T, H, K = q.shape
+    V = v.shape[2]
+    assert k.shape == (T, H, K) and g.shape == (T, H, K) and v.shape[:2] == (T, H)
+    assert b.shape == (T, H)
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    N = cu.shape[0] - 1
+    assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    if heads is None:
+        hs = None
+        nsel = H
+    else:
+        hs = np.ascontiguousarray(np.asarray(heads, dtype=np.int32))
+        nsel = hs.shape[0]
+    init = None
+    if init_state is not None:
+        init = np.ascontiguousarray(np.asarray(init_state, dtype=np.float64))
+        assert init.shape == (N, H, K, V)
+    o = np.zeros((T, nsel, V), dtype=np.float64)
+    fin = np.zeros((N, nsel, K, V), dtype=np.float64)
+    rc = lib.kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(cu), N, H, K, V,
+                            _ptr(init) if init is not None else None,
+                            _ptr(hs) if hs is not None else None, nsel, _ptr(o), _ptr(fin),
+                            int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_fwd failed (%d)" % rc)
+    return o, fin
+
+
+def kda_step(q, k, v, log_alpha, beta, state: np.ndarray, threads: int = 0):
+    """One fp64 recurrent step for N x H heads; ``state`` [N, H, K, V] float64 is updated
+    in place. q, k, log_alpha: [N, H, K]; v: [N, H, V]; beta: [N, H]. Returns o [N, H, V]."""
+    lib = _load()
+    q, k, v, g, b = _f32(q), _f32(k), _f32(v), _f32(log_alpha), _f32(beta)
+    N, H, K = q.shape
+    V = v.shape[2]
+    assert state.dtype == np.float64 and state.flags["C_CONTIGUOUS"]
+    assert state.shape == (N, H, K, V)
+    o = np.zeros((N, H, V), dtype=np.float64)
+    rc = lib.kda_oracle_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), N, H, K, V,
+                             _ptr(state), _ptr(o), int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_step failed (%d)" % rc)
+    return o

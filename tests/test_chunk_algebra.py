@@ -1,0 +1,66 @@
+"""The chunkwise algebra (tests/chunk_ref.py) against the oracle, on the CPU.
+
+This pins the chunk form the GPU kernels implement to the token recurrence: the chunk
+result must not depend on the chunk size (C=1 is the recurrence itself), chunks restart at
+sequence starts, and the chunk transition equals the product of the per-token DPLR
+transitions with a correction of rank at most min(C, K) ("Kimi Linear" explainer, "The
+Woodbury Identity Trick": a product of c diagonal-plus-rank-1 matrices is diagonal plus
+rank at most c).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from chunk_ref import chunk_fwd, chunk_transition
+
+
+def _inputs(rng, T, H, K, V, alpha_lo=0.5):
+    q = rng.standard_normal((T, H, K))
+    k = rng.standard_normal((T, H, K))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, V))
+    g = np.log(rng.uniform(alpha_lo, 1.0, (T, H, K)))
+    beta = rng.uniform(0, 1, (T, H))
+    return [a.astype(np.float32).astype(np.float64) for a in (q, k, v, g, beta)]
+
+
+@pytest.mark.parametrize("C", [1, 4, 16, 64])
+def test_chunk_form_matches_oracle(C):
+    rng = np.random.default_rng(C)
+    lens = [70, 1, 33, 64, 0, 17]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    K, V, H = 8, 6, 2
+    q, k, v, g, beta = _inputs(rng, int(cu[-1]), H, K, V)
+    S0 = rng.standard_normal((len(lens), H, K, V))
+    o, fin = oracle.kda_fwd(q, k, v, g, beta, cu_seqlens=cu, init_state=S0)
+    oc, fc = chunk_fwd(q, k, v, g, beta, C, cu_seqlens=cu, init_state=S0)
+    np.testing.assert_allclose(oc, o, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(fc, fin, rtol=1e-10, atol=1e-10)
+
+
+def test_chunk_transition_is_product_of_token_transitions():
+    rng = np.random.default_rng(21)
+    n, K = 5, 9
+    k = rng.standard_normal((n, K))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    g = np.log(rng.uniform(0.4, 1.0, (n, K)))
+    beta = rng.uniform(0, 1, n)
+    M = np.eye(K)
+    for t in range(n):
+        a = np.exp(g[t])
+        M = (np.diag(a) - beta[t] * np.outer(k[t], a * k[t])) @ M
+    Mc = chunk_transition(k, g, beta)
+    np.testing.assert_allclose(Mc, M, rtol=1e-12, atol=1e-12)
+    corr = np.diag(np.exp(g.sum(0))) - Mc
+    assert np.linalg.matrix_rank(corr, tol=1e-10) <= min(n, K)
+
+
+def test_chunk_form_with_strong_decay():
+    """Strong per-channel decay (alpha down to 0.01) through the exact chunk form."""
+    rng = np.random.default_rng(22)
+    K, V = 8, 4
+    q, k, v, g, beta = _inputs(rng, 50, 1, K, V, alpha_lo=0.01)
+    o, fin = oracle.kda_fwd(q, k, v, g, beta)
+    oc, fc = chunk_fwd(q, k, v, g, beta, 16)
+    np.testing.assert_allclose(oc, o, rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(fc, fin, rtol=1e-9, atol=1e-9)

@@ -1,0 +1,104 @@
+"""Planted mistakes in a temporary copy of the oracle must be caught by the pins.
+
+Each mutation is applied to a copy of oracle/kda_oracle.c in a temp directory, compiled
+with gcc and swapped in for the duration of the check; the real oracle is never touched.
+"""
+import ctypes
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "kda_oracle.c")
+
+DECAY_BLOCK = """  /* 1. per-channel decay of the old memory */
+  for (int c = 0; c < K; ++c) {
+    const double a = exp((double)g[c]);
+    double* row = S + (size_t)c * V;
+    for (int j = 0; j < V; ++j) row[j] *= a;
+  }
+"""
+READ_BLOCK_HEAD = "  /* 4. read with the query after the write */\n"
+
+MUTATIONS = {
+    "no_decay": [("row[j] *= a;", "row[j] *= 1.0;")],
+    "gate_sign": [("exp((double)g[c])", "exp(-(double)g[c])")],
+    "no_beta": [("const double bk = beta * (double)k[c];", "const double bk = (double)k[c];")],
+    "no_erase": [("row[j] += bk * ((double)v[j] - u[j]);", "row[j] += bk * ((double)v[j]);")],
+    "erase_sign": [("row[j] += bk * ((double)v[j] - u[j]);", "row[j] += bk * ((double)v[j] + u[j]);")],
+    "transposed_read": [("for (int j = 0; j < V; ++j) o[j] += row[j] * qc;",
+                         "for (int j = 0; j < V; ++j) o[c < V ? c : 0] += row[j] * (double)q[j < K ? j : 0] * (c < V);")],
+    "decay_after_write": [(DECAY_BLOCK, ""), (READ_BLOCK_HEAD, DECAY_BLOCK + READ_BLOCK_HEAD)],
+    "transposed_key_in_prediction": [("u[j] += row[j] * kc;", "u[j] += row[j] * (double)k[j < K ? j : 0] * (c == 0);")],
+}
+
+PIN_TESTS = [
+    lambda: pins.test_hand_example(),
+    lambda: pins.test_bruteforce_dplr(3, 5, 7),
+    lambda: pins.test_beta_zero_is_pure_decay(),
+    lambda: pins.test_unit_key_beta_one_recalls_value(),
+    lambda: pins.test_alpha_one_orthonormal_keys_is_linear_attention(),
+    lambda: pins.test_basis_keys_are_per_channel_gated_attention(),
+    lambda: pins.test_first_order_in_beta_is_diagonal_decay_attention(),
+    lambda: pins.test_scalar_gate_is_gated_delta_rule(),
+]
+
+
+def _build_mutant(edits, tmp):
+    src = open(SRC).read()
+    for old, new in edits:
+        assert old in src, "mutation anchor not found: %r" % old[:60]
+        src = src.replace(old, new, 1)
+    c = os.path.join(tmp, "m.c")
+    so = os.path.join(tmp, "m.so")
+    open(c, "w").write(src)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-o", so, c, "-lm"],
+                   check=True)
+    return so
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name):
+    oracle._load()
+    real = oracle._lib
+    tmp = tempfile.mkdtemp()
+    try:
+        lib = ctypes.CDLL(_build_mutant(MUTATIONS[name], tmp))
+        for fn in ("kda_oracle_fwd", "kda_oracle_step"):
+            getattr(lib, fn).argtypes = getattr(real, fn).argtypes
+            getattr(lib, fn).restype = ctypes.c_int
+        lib.kda_oracle_max_threads.restype = ctypes.c_int
+        oracle._lib = lib
+        caught = []
+        for i, t in enumerate(PIN_TESTS):
+            try:
+                t()
+            except AssertionError:
+                caught.append(i)
+        assert caught, "mutation %s survived every pin" % name
+    finally:
+        oracle._lib = real
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+def test_unmutated_copy_passes_every_pin():
+    """Control: the same harness with no edit passes all pins."""
+    oracle._load()
+    real = oracle._lib
+    tmp = tempfile.mkdtemp()
+    try:
+        lib = ctypes.CDLL(_build_mutant([], tmp))
+        for fn in ("kda_oracle_fwd", "kda_oracle_step"):
+            getattr(lib, fn).argtypes = getattr(real, fn).argtypes
+            getattr(lib, fn).restype = ctypes.c_int
+        oracle._lib = lib
+        for t in PIN_TESTS:
+            t()
+    finally:
+        oracle._lib = real
+        shutil.rmtree(tmp, ignore_errors=True)
