@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one kda_chunk_fwd over the long-prefill workload (B=1, H=32, T=65536,
+K=V=128, bf16 inputs, fp32 initial state 0.1*N(0,1)) followed by one kda_decode_step over
+the decode workload (256 sequences x 32 heads, K=V=128, fp32 state 0.1*N(0,1), bf16 step
+inputs). Inputs are synthetic, seeded and resident in HBM before timing starts.
+
+Prints one JSON line. `value` is whole-step throughput (prefill tokens + decode tokens per
+second); per-call figures, roofline fractions and the oracle's CPU rate are attached.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA chunk_fwd tokens/s (H=32,d=128) + decode_step GB/s, % of roofline"
+PEAK_HBM = 8.0e12         # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15        # FLOP/s, dense bf16 MFMA
+CHUNK = 64
+
+
+def chunk_alg_bytes(T, H, K, V, es, n_seqs, init, final):
+    per_tok_head = es * (3 * K + V + 1 + V)  # q, k, log_alpha, v, beta in; o out
+    return T * H * per_tok_head + 4 * n_seqs * H * K * V * ((1 if init else 0) + (1 if final else 0))
+
+
+def chunk_alg_flops(T, H, K, V, C=CHUNK):
+    # state GEMMs W.S, Q.S, Kt^T.Delta (6KV), triangular A, P, W (C*K each) and U, P.Delta
+    # (C*V each), triangular solve (C^2/3), per token-head
+    return T * H * (6 * K * V + C * (3 * K + 2 * V) + C * C / 3.0)
+
+
+def chunk_dense_flops(T, H, K, V, C=CHUNK):
+    return T * H * (6 * K * V + 2 * C * (3 * K + 2 * V))
+
+
+def decode_alg_bytes(N, H, K, V, es):
+    return N * H * (2 * 4 * K * V + es * (3 * K + V + 1) + es * V)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32768,
+                    help="tokens (all 32 heads) of the prefill workload the oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures a single GPU: every (sequence, head) chain of the operator is "
+              "independent and no multi-GPU path is built; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_30_amd as kda
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    names = ("q", "k", "v", "log_alpha", "beta")
+
+    # ---------------- inputs, resident in HBM
+    wl = workloads.WORKLOADS["long"]
+    T, H, K, V = wl["T"], wl["H"], wl["K"], wl["V"]
+    inp = workloads.make_workload("long", device=dev)
+    o = torch.empty((T, H, V), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((1, H, K, V), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_size(1, T, H, K, V, torch.bfloat16), dtype=torch.uint8, device=dev)
+
+    wd = workloads.WORKLOADS["decode"]
+    Nd, Hd = wd["num_seqs"], wd["H"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wd["seed"])
+    state = wd["state_std"] * torch.randn((Nd, Hd, K, V), generator=gen, device=dev)
+    dinp = workloads.gen_decode_inputs(Nd, Hd, K, V, dtype=torch.bfloat16, device=dev, gen=gen)
+    od = torch.empty((Nd, Hd, V), dtype=torch.bfloat16, device=dev)
+
+    def chunk_call():
+        kda.chunk_fwd(*(inp[x] for x in names), init_state=inp["init_state"], o=o,
+                      final_state=fin, workspace=ws)
+
+    def decode_call():
+        kda.decode_step(*(dinp[x] for x in names), state=state, o=od)
+
+    for _ in range(args.warmup):
+        chunk_call()
+        decode_call()
+    torch.cuda.synchronize()
+
+    # ---------------- timed region
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        chunk_call()
+        ev[s][1].record()
+        decode_call()
+        ev[s][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    chunk_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    cb = chunk_alg_bytes(T, H, K, V, 2, 1, True, True)
+    cf = chunk_alg_flops(T, H, K, V)
+    cfd = chunk_dense_flops(T, H, K, V)
+    db = decode_alg_bytes(Nd, Hd, K, V, 2)
+    chunk_s = chunk_ms * 1e-3
+    decode_s = decode_ms * 1e-3
+    chunk = {
+        "workload": "B=1 H=32 T=65536 K=V=128 bf16, init state 0.1*N(0,1)",
+        "ms": chunk_ms,
+        "tokens_per_s": T / chunk_s,
+        "alg_bytes": cb,
+        "hbm_GBps": cb / chunk_s / 1e9,
+        "hbm_frac": cb / chunk_s / PEAK_HBM,
+        "chunk_size": CHUNK,
+        "mfma_frac_alg": cf / chunk_s / PEAK_BF16,
+        "mfma_frac_dense": cfd / chunk_s / PEAK_BF16,
+    }
+    decode = {
+        "workload": "256 seqs x 32 heads, K=V=128, fp32 state, bf16 inputs",
+        "ms": decode_ms,
+        "GB_per_s": db / decode_s / 1e9,
+        "hbm_frac": db / decode_s / PEAK_HBM,
+        "tokens_per_s": Nd / decode_s,
+        "alg_bytes": db,
+    }
+    # dominant work of the step: the chunkwise forward (HBM-bound at K=V=128, bf16 I/O)
+    roofline = {"bound": "hbm", "achieved": cb / chunk_s / 1e9, "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": cb / chunk_s / PEAK_HBM, "traffic": None,
+                "kernel": "kda_chunk_fwd (prep + state kernels per segment)"}
+    roofline_decode = {"bound": "hbm", "achieved": db / decode_s / 1e9, "peak": PEAK_HBM / 1e9,
+                       "unit": "GB/s", "frac": db / decode_s / PEAK_HBM, "traffic": None,
+                       "kernel": "decode_step_kernel<128,128,bf16>"}
+    value = (T + Nd) / (ms_per_step * 1e-3)
+
+    # ---------------- parity spot check and CPU baseline (oracle on the same inputs)
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        S = min(args.cpu_sample_tokens, T)
+        f = lambda t: t.float().cpu().numpy()
+        sample = [f(inp[x][:S]) for x in names]
+        init_np = inp["init_state"].double().cpu().numpy()
+        ta = time.perf_counter()
+        o_ref, _ = oracle.kda_fwd(*sample, init_state=init_np)
+        tb = time.perf_counter()
+        cpu = {"value": S / (tb - ta), "unit": "tokens/s", "cores": oracle.max_threads(),
+               "kind": "oracle",
+               "sample": "first %d tokens x all %d heads of the prefill workload (fp64 token "
+                         "recurrence, %.1f s wall)" % (S, H, tb - ta)}
+        got = o[:S].float().cpu().numpy().astype(np.float64)
+        parity = float(np.abs(got - o_ref).max() / np.abs(o_ref).max())
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "KDA long prefill B=1 H=32 T=65536 K=V=128 + decode step "
+                               "256x32 heads", "global_batch": 1, "seq_len": T,
+                   "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "chunk_fwd": chunk,
+        "decode_step": decode,
+        "roofline_decode": roofline_decode,
+        "parity_sample_max_rel_err": parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

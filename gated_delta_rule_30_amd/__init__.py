@@ -1,0 +1,10 @@
+"""MI355X-native Kimi Delta Attention (KDA): chunkwise prefill and recurrent decode.
+
+The operator lives in libkda.so (hand-written HIP kernels for gfx950, C ABI in
+include/kda.h); this package is its thin Python binding.
+"""
+from ._binding import (KDA_DTYPE_BF16, KDA_DTYPE_F32, LIB_PATH, KdaError, chunk_fwd,
+                       decode_step, declared_functions, lib, workspace_size)
+
+__all__ = ["chunk_fwd", "decode_step", "workspace_size", "KdaError", "lib", "LIB_PATH",
+           "declared_functions", "KDA_DTYPE_BF16", "KDA_DTYPE_F32"]

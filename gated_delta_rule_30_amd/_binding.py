@@ -1,0 +1,169 @@
+"""ctypes binding of libkda.so: argument marshalling only.
+
+Torch supplies device memory and the current stream; every step of the operator runs in
+the library's HIP kernels. If the library has not been built the import fails loudly:
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "kda.h")
+
+KDA_DTYPE_F32 = 0
+KDA_DTYPE_BF16 = 1
+STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
+          3: "KDA_ERROR_WORKSPACE_TOO_SMALL", 4: "KDA_ERROR_LAUNCH"}
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s" % (what, _lib().kda_status_string(status).decode()))
+        self.status = status
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libkda.so is not built (expected at %s); run "
+                              "python -m gated_delta_rule_30_amd.build" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lib.kda_status_string.restype = ctypes.c_char_p
+        lib.kda_status_string.argtypes = [ctypes.c_int]
+        lib.kda_chunk_fwd_workspace_size.restype = sz
+        lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
+        lib.kda_chunk_fwd.restype = ctypes.c_int
+        lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                      ctypes.c_int, vp, vp, vp, sz, vp]
+        lib.kda_decode_step.restype = ctypes.c_int
+        lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                        ctypes.c_int, vp]
+        _LIB = lib
+    return _LIB
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError if it is not built)."""
+    return _lib()
+
+
+def declared_functions():
+    """Names of the functions declared in include/kda.h."""
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return KDA_DTYPE_F32
+    raise TypeError("q/k/v/log_alpha/beta must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype) -> int:
+    code = KDA_DTYPE_BF16 if dtype == torch.bfloat16 else KDA_DTYPE_F32
+    return int(_lib().kda_chunk_fwd_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, code))
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, num_seqs=None,
+              output_final_state=True, o=None, final_state=None, workspace=None):
+    """kda_chunk_fwd on torch tensors (token-major [T, H, .], see include/kda.h).
+
+    Returns (o [T, H, V] in the input dtype, final_state [N, H, K, V] fp32 or None).
+    ``final_state`` may be passed as the same tensor as ``init_state`` (in-place update).
+    """
+    device = q.device
+    T, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, device)
+        N = cu_seqlens.shape[0] - 1
+        if num_seqs is not None and num_seqs != N:
+            raise ValueError("num_seqs does not match cu_seqlens")
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
+    for name, t, shp in (("q", q, (T, H, K)), ("k", k, (T, H, K)), ("v", v, (T, H, V)),
+                         ("log_alpha", log_alpha, (T, H, K)), ("beta", beta, (T, H))):
+        _check(t, name, shp, dt, device)
+    if init_state is not None:
+        _check(init_state, "init_state", (N, H, K, V), torch.float32, device)
+    if o is None:
+        o = torch.empty((T, H, V), dtype=dt, device=device)
+    else:
+        _check(o, "o", (T, H, V), dt, device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, K, V), dtype=torch.float32, device=device)
+    elif final_state is not None:
+        _check(final_state, "final_state", (N, H, K, V), torch.float32, device)
+    need = int(_lib().kda_chunk_fwd_workspace_size(N, T, H, K, V, code))
+    if need == 0:
+        raise KdaError(2 if K not in (32, 64, 128) or V not in (32, 64, 128) else 1,
+                       "kda_chunk_fwd_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    st = _lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                              _ptr(init_state), _ptr(cu_seqlens), N, T, H, K, V, code,
+                              _ptr(o), _ptr(final_state), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(device))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd")
+    return o, final_state
+
+
+def decode_step(q, k, v, log_alpha, beta, state, o=None):
+    """kda_decode_step on torch tensors: q, k, log_alpha [N, H, K], v [N, H, V], beta [N, H],
+    state [N, H, K, V] fp32 updated in place. Returns o [N, H, V] in the input dtype."""
+    device = q.device
+    N, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    for name, t, shp in (("q", q, (N, H, K)), ("k", k, (N, H, K)), ("v", v, (N, H, V)),
+                         ("log_alpha", log_alpha, (N, H, K)), ("beta", beta, (N, H))):
+        _check(t, name, shp, dt, device)
+    _check(state, "state", (N, H, K, V), torch.float32, device)
+    if o is None:
+        o = torch.empty((N, H, V), dtype=dt, device=device)
+    else:
+        _check(o, "o", (N, H, V), dt, device)
+    st = _lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                _ptr(state), _ptr(o), N, H, K, V, code, _stream(device))
+    if st != 0:
+        raise KdaError(st, "kda_decode_step")
+    return o

@@ -1,0 +1,148 @@
+// C ABI of libkda.so: argument validation, workspace planning and launch.
+// Every check here runs on the host before anything is enqueued.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kda_internal.h"
+
+namespace {
+
+bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool valid_dtype(kda_dtype t) { return t == KDA_DTYPE_F32 || t == KDA_DTYPE_BF16; }
+size_t esize(kda_dtype t) { return t == KDA_DTYPE_BF16 ? 2 : 4; }
+
+// [a, a+na) and [b, b+nb) overlap
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Largest packed token count the 32-bit chunk table indexes.
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+
+}  // namespace
+
+extern "C" const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_SUCCESS: return "KDA_SUCCESS";
+    case KDA_ERROR_INVALID_VALUE: return "KDA_ERROR_INVALID_VALUE";
+    case KDA_ERROR_NOT_SUPPORTED: return "KDA_ERROR_NOT_SUPPORTED";
+    case KDA_ERROR_WORKSPACE_TOO_SMALL: return "KDA_ERROR_WORKSPACE_TOO_SMALL";
+    case KDA_ERROR_LAUNCH: return "KDA_ERROR_LAUNCH";
+  }
+  return "KDA_ERROR_UNKNOWN";
+}
+
+static kda_status check_chunk_shape(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                    int32_t dk, int32_t dv, kda_dtype dtype) {
+  if (num_seqs <= 0 || num_heads <= 0 || total_tokens < 0 || total_tokens > kMaxTokens)
+    return KDA_ERROR_INVALID_VALUE;
+  if (!valid_dtype(dtype) || !supported_dim(dk) || !supported_dim(dv)) return KDA_ERROR_NOT_SUPPORTED;
+  // fp32 operands at K = 128 exceed the prep kernel's LDS budget
+  if (dtype == KDA_DTYPE_F32 && dk == 128) return KDA_ERROR_NOT_SUPPORTED;
+  return KDA_SUCCESS;
+}
+
+extern "C" size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens,
+                                               int32_t num_heads, int32_t dk, int32_t dv,
+                                               kda_dtype dtype) {
+  if (check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype) != KDA_SUCCESS) return 0;
+  kda::ChunkPlan pl;
+  if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16, &pl))
+    return 0;
+  return pl.total_bytes;
+}
+
+extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
+                                    const void* log_alpha, const void* beta,
+                                    const float* init_state, const int32_t* cu_seqlens,
+                                    int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                    int32_t dk, int32_t dv, kda_dtype dtype, void* o,
+                                    float* final_state, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  kda_status st = check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
+  if (st != KDA_SUCCESS) return st;
+  if (cu_seqlens == nullptr && total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
+  if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERROR_INVALID_VALUE;
+  if (!workspace) return KDA_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {q, k, v, log_alpha, init_state, o, final_state};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
+  if ((beta && !aligned_to(beta, esize(dtype))) || (cu_seqlens && !aligned_to(cu_seqlens, 4)))
+    return KDA_ERROR_INVALID_VALUE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERROR_INVALID_VALUE;
+  const size_t sbytes = (size_t)num_seqs * num_heads * dk * dv * sizeof(float);
+  if (init_state && final_state && init_state != final_state &&
+      overlap(init_state, sbytes, final_state, sbytes))
+    return KDA_ERROR_INVALID_VALUE;
+  if (total_tokens > 0) {
+    const size_t obytes = (size_t)total_tokens * num_heads * dv * esize(dtype);
+    const size_t ibytes = (size_t)total_tokens * num_heads * dk * esize(dtype);
+    if (overlap(o, obytes, q, ibytes) || overlap(o, obytes, k, ibytes) ||
+        overlap(o, obytes, log_alpha, ibytes) || overlap(o, obytes, v, obytes))
+      return KDA_ERROR_INVALID_VALUE;
+  }
+  kda::ChunkPlan pl;
+  if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16, &pl))
+    return KDA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < pl.total_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+
+  kda::ChunkArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = log_alpha;
+  a.beta = beta;
+  a.init_state = init_state;
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.num_heads = num_heads;
+  a.dk = dk;
+  a.dv = dv;
+  a.dtype_bf16 = dtype == KDA_DTYPE_BF16;
+  a.o = o;
+  a.final_state = final_state;
+  a.workspace = workspace;
+  a.stream = stream;
+  hipError_t e = kda::launch_chunk_fwd(a, pl);
+  return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+}
+
+extern "C" kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                                      const void* log_alpha, const void* beta, float* state,
+                                      void* o, int32_t num_seqs, int32_t num_heads, int32_t dk,
+                                      int32_t dv, kda_dtype dtype, void* stream) {
+  if (num_seqs <= 0 || num_heads <= 0) return KDA_ERROR_INVALID_VALUE;
+  if (!valid_dtype(dtype) || !supported_dim(dk) || !supported_dim(dv)) return KDA_ERROR_NOT_SUPPORTED;
+  if (!q || !k || !v || !log_alpha || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
+  const void* ptrs[] = {q, k, v, log_alpha, state, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return KDA_ERROR_INVALID_VALUE;
+  if (!aligned_to(beta, esize(dtype))) return KDA_ERROR_INVALID_VALUE;
+  const size_t heads = (size_t)num_seqs * num_heads;
+  const size_t obytes = heads * dv * esize(dtype);
+  if (overlap(o, obytes, state, heads * dk * dv * sizeof(float)) ||
+      overlap(o, obytes, q, heads * dk * esize(dtype)) || overlap(o, obytes, k, heads * dk * esize(dtype)) ||
+      overlap(o, obytes, v, obytes) || overlap(o, obytes, log_alpha, heads * dk * esize(dtype)))
+    return KDA_ERROR_INVALID_VALUE;
+  kda::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = log_alpha;
+  a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.dk = dk;
+  a.dv = dv;
+  a.dtype_bf16 = dtype == KDA_DTYPE_BF16;
+  a.stream = stream;
+  hipError_t e = kda::launch_decode(a);
+  return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+}

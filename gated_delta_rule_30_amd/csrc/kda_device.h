@@ -1,0 +1,100 @@
+// Device-side helpers shared by the KDA kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// ------------------------------------------------------------------ scalar conversions
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<bf16>(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+// e^x through the hardware base-2 exponential.
+__device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+// ------------------------------------------------------------------ MFMA 16x16 tiles
+// A "fragment" is what one lane feeds to one 16x16xKS reduction step: 16 bytes.
+// Lane l has row/column index m = l % 16 and group g = l / 16.
+// Within a reduction step of KS elements, element e of group g covers the index
+//     kk(g, e) = 16 * (e / 4) + 4 * g + (e % 4)
+// (bf16: KS = 32, 8 elements per lane; fp32: KS = 16, 4 elements per lane).
+// A-operand fragments and B-operand fragments use the same kk mapping, so the products pair
+// up whatever order the hardware sums in. The 16x16 fp32 result tile has lane l holding
+// rows 4 * g + r (r = 0..3) of column m. With this kk mapping a 16-row result tile (two
+// tiles for bf16) is directly a fragment along its row index.
+template <typename MT> struct Mma;
+
+template <> struct Mma<bf16> {
+  static constexpr int KS = 32;
+  static constexpr int EPL = 8;
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int KS = 16;
+  static constexpr int EPL = 4;
+  typedef f32x4 frag;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    return c;
+  }
+};
+
+// Fragment of reduction step s for group g from a row whose reduction index is contiguous.
+__device__ __forceinline__ bf16x8 load_frag(const bf16* row, int s, int g) {
+  const bf16* p = row + 32 * s + 4 * g;
+  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ f32x4 load_frag(const float* row, int s, int g) {
+  return *reinterpret_cast<const f32x4*>(row + 16 * s + 4 * g);
+}
+
+// Same, from an fp32 row scaled elementwise by an fp32 vector, rounded to MT.
+__device__ __forceinline__ bf16x8 load_frag_scaled(const float* row, const float* scale, int s,
+                                                   int g, bf16) {
+  const int o = 32 * s + 4 * g;
+  f32x4 a = *reinterpret_cast<const f32x4*>(row + o);
+  f32x4 b = *reinterpret_cast<const f32x4*>(row + o + 16);
+  f32x4 sa = *reinterpret_cast<const f32x4*>(scale + o);
+  f32x4 sb = *reinterpret_cast<const f32x4*>(scale + o + 16);
+  a *= sa;
+  b *= sb;
+  return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+}
+__device__ __forceinline__ f32x4 load_frag_scaled(const float* row, const float* scale, int s,
+                                                  int g, float) {
+  const int o = 16 * s + 4 * g;
+  return *reinterpret_cast<const f32x4*>(row + o) * *reinterpret_cast<const f32x4*>(scale + o);
+}
+
+// Fragment made of two fp32 result tiles (rows 0-15 and 16-31 of a reduction step): bf16.
+__device__ __forceinline__ bf16x8 frag_from_acc(f32x4 lo, f32x4 hi, bf16) {
+  return bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
+                (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+}  // namespace kda

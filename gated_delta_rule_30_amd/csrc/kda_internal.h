@@ -1,0 +1,73 @@
+// Internal host-side declarations of the KDA library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int CHUNK = 64;     // tokens per chunk
+constexpr int SUBBLK = 16;    // sub-block edge = MFMA tile edge
+constexpr int NSUB = CHUNK / SUBBLK;
+constexpr int NTHREADS = 256;  // threads per workgroup of every chunk kernel
+
+// Target number of (chunk, head) records per segment: the two record buffers of a segment
+// pair then stay resident in the 256 MB Infinity Cache at K=V=128 bf16.
+constexpr int64_t SEG_CHUNK_HEADS = 1024;
+
+struct DecodeArgs {
+  const void *q, *k, *v, *g, *beta;
+  float* state;
+  void* o;
+  int num_seqs, num_heads, dk, dv;
+  bool dtype_bf16;
+  void* stream;
+};
+
+// One entry of the device chunk table (32 bytes).
+struct Entry {
+  int32_t seq;    // sequence index
+  int32_t tok;    // first token (packed index)
+  int32_t len;    // tokens in this chunk, 1..CHUNK
+  int32_t depth;  // chunk index inside its sequence
+  int32_t prev;   // entry index of the previous chunk of the sequence, -1 if none
+  int32_t next;   // entry index of the next chunk of the sequence, -1 if none
+  int32_t pad0, pad1;
+};
+
+// Host-side launch plan of one kda_chunk_fwd call; a pure function of the shape.
+struct ChunkPlan {
+  int64_t ub_entries;   // upper bound of the number of chunks over all sequences
+  int64_t seg_entries;  // E: chunks per segment
+  int64_t num_segs;
+  int64_t slots;        // max distinct sequences in one segment = min(N, E)
+  int64_t rec_bytes;    // bytes of one (chunk, head) record
+  int n_slices;         // V split into n_slices slices of vs columns
+  int vs;
+  // workspace offsets (bytes)
+  size_t off_header, off_entries, off_seg_first, off_seg_count, off_state, off_rec, rec_buf_bytes;
+  size_t total_bytes;
+};
+
+bool make_chunk_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv,
+                     bool bf16, ChunkPlan* p);
+
+struct ChunkArgs {
+  const void *q, *k, *v, *g, *beta;
+  const float* init_state;
+  const int32_t* cu_seqlens;
+  int num_seqs;
+  int64_t total_tokens;
+  int num_heads, dk, dv;
+  bool dtype_bf16;
+  void* o;
+  float* final_state;
+  void* workspace;
+  void* stream;
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkPlan& p);
+
+}  // namespace kda

@@ -1,0 +1,115 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) library, libkda.so.
+ *
+ * The operator (per sequence and head, state S in R^{K x V}, rows = key channels):
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t
+ * Update rule: "Kimi Linear's Hybrid Linear Attention Architecture: A Technical Breakdown",
+ * section 3.3 (per-channel decay first, then directional erase and write); orientation from
+ * the update-rule code block of "Kimi Linear: How Moonshot AI Built a Hybrid Attention
+ * Architecture That Beats Full Attention"; the query reads the state after the token's write
+ * ("Kimi Linear" explainer, "Step 4: Query").
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library never allocates
+ *    or frees device memory and keeps no per-call state. Tensor pointers must be 16-byte
+ *    aligned, except beta and cu_seqlens, which need only their element alignment.
+ *  - Layouts are row-major and token-major. q, k, log_alpha: [rows][H][K]; v: [rows][H][V];
+ *    beta: [rows][H]; o: [rows][H][V]; states: [N][H][K][V] fp32 (element (c, j) of S at
+ *    c*V + j, c = key channel, j = value channel).
+ *  - dtype selects the element type of q, k, v, log_alpha, beta and o (fp32 or bf16). States
+ *    are always fp32. Outputs are rounded to nearest even when dtype is bf16.
+ *  - log_alpha is the natural log of the per-channel decay alpha (expected <= 0); no query
+ *    scale is applied and q, k are used as given (no normalisation inside).
+ *  - Supported head dims: K, V in {32, 64, 128}. Other values give KDA_ERROR_NOT_SUPPORTED.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
+ *    returns without waiting. Argument errors are reported synchronously before anything is
+ *    enqueued; a failed launch gives KDA_ERROR_LAUNCH. Values are not checked on the device:
+ *    NaN/Inf propagate. No exception crosses the ABI.
+ *  - Calls on different streams are independent; calls that share a workspace or a state
+ *    buffer must be ordered by the caller.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_SUCCESS = 0,
+  KDA_ERROR_INVALID_VALUE = 1,       /* NULL pointer, misaligned pointer, bad size/count */
+  KDA_ERROR_NOT_SUPPORTED = 2,       /* head dims outside {32, 64, 128}, unknown dtype */
+  KDA_ERROR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below kda_chunk_fwd_workspace_size */
+  KDA_ERROR_LAUNCH = 4               /* a kernel launch or stream operation failed */
+} kda_status;
+
+typedef enum {
+  KDA_DTYPE_F32 = 0,  /* IEEE fp32 */
+  KDA_DTYPE_BF16 = 1  /* bfloat16 */
+} kda_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kda_status_string(kda_status s);
+
+/*
+ * Workspace bytes kda_chunk_fwd needs for this shape (0 if the arguments are invalid).
+ * The value depends only on the arguments; it covers the device chunk table, a running state
+ * and two chunk-record buffers, and is bounded (about 140 MB at H=32, K=V=128, bf16) plus
+ * 32 bytes per chunk and 4*N*H*K*V bytes, whatever the sequence length.
+ */
+size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                    int32_t dk, int32_t dv, kda_dtype dtype);
+
+/*
+ * Chunkwise KDA forward (prefill / training forward) over packed variable-length sequences.
+ * Method: "A Technical Breakdown", section 4 "Hardware-Friendly Chunkwise Computation"
+ * (in-chunk cumulative decay, WY / UT representation of the chunk's rank-1 updates through
+ * a triangular solve, state passing between chunks, masked intra-chunk output).
+ *
+ *   q, k, log_alpha : [T_total][H][K]   dtype
+ *   v               : [T_total][H][V]   dtype
+ *   beta            : [T_total][H]      dtype
+ *   init_state      : [N][H][K][V] fp32, or NULL for zero initial states
+ *   cu_seqlens      : device int32 [N+1], cu[0] = 0, non-decreasing, cu[N] = T_total;
+ *                     sequence n is tokens cu[n] .. cu[n+1]-1. NULL means N sequences of
+ *                     equal length T_total / N (T_total must then be divisible by N).
+ *                     A malformed cu_seqlens is undefined behaviour (it is not read on the host).
+ *   o               : [T_total][H][V]   dtype, written for every token
+ *   final_state     : [N][H][K][V] fp32 out, or NULL. May be the same pointer as init_state
+ *                     (then updated in place); other partial overlaps are not allowed.
+ *   workspace       : device buffer of at least kda_chunk_fwd_workspace_size(...) bytes,
+ *                     256-byte aligned, contents need not be initialised; used only during
+ *                     the call's stream work.
+ * A sequence of length 0 gets final = init (or zero). T_total = 0 is a no-op apart from that.
+ * States never cross sequence boundaries.
+ * Numerical domain: the in-chunk factorisation keeps every factor within fp32 range when the
+ * decay of any key channel over 16 consecutive tokens is at most e^80 (e.g. log_alpha >= -5
+ * everywhere); stronger decays can overflow to Inf/NaN.
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* beta, const float* init_state, const int32_t* cu_seqlens,
+                         int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t dk,
+                         int32_t dv, kda_dtype dtype, void* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent KDA token step per (sequence, head), state updated in place (decode).
+ * The decay, prediction u = (Diag(alpha) S)^T k, erase-and-write and read are fused into one
+ * pass that streams each fp32 state once from HBM and writes it once.
+ *   q, k, log_alpha : [N][H][K] dtype;  v : [N][H][V] dtype;  beta : [N][H] dtype
+ *   state           : [N][H][K][V] fp32, read and overwritten
+ *   o               : [N][H][V] dtype out (must not overlap the other buffers)
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                           const void* beta, float* state, void* o, int32_t num_seqs,
+                           int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: symbols, header, workspace planning and every synchronous error
+path (each returns before anything is enqueued, so no device is touched)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import gated_delta_rule_30_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+SUCCESS, INVALID, NOT_SUPPORTED, WS_SMALL, LAUNCH = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+
+
+def test_every_declared_symbol_is_exported():
+    names = kda.declared_functions()
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_decode_step",
+                          "kda_status_string"}
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in names:
+        assert n in exported, n
+
+
+@pytest.mark.parametrize("lang,std", [("c", "c99"), ("c++", "c++11")])
+def test_header_compiles_standalone(lang, std, tmp_path):
+    src = tmp_path / ("t." + ("c" if lang == "c" else "cpp"))
+    src.write_text('#include "kda.h"\nint main(void){ return (int)kda_chunk_fwd_workspace_size(1,0,1,32,32,KDA_DTYPE_F32) < 0; }\n')
+    cc = "gcc" if lang == "c" else "g++"
+    subprocess.run([cc, "-std=" + std, "-Wall", "-Werror", "-fsyntax-only", "-I",
+                    os.path.dirname(HEADER), str(src)], check=True)
+
+
+def test_status_strings():
+    L = kda.lib()
+    for code, name in kda._binding.STATUS.items():
+        assert L.kda_status_string(code).decode() == name
+    assert L.kda_status_string(99).decode() == "KDA_ERROR_UNKNOWN"
+
+
+def test_workspace_size_is_bounded_and_valid():
+    import torch
+    ws = lambda *a: kda.workspace_size(*a)
+    small = ws(1, 256, 1, 32, 32, torch.float32)
+    assert small > 0
+    big = ws(1, 1 << 20, 32, 128, 128, torch.bfloat16)
+    long_ = ws(1, 65536, 32, 128, 128, torch.bfloat16)
+    # bounded by the two segment record buffers, not by the sequence length
+    assert big - long_ < 1 << 20
+    assert big < 200 * (1 << 20)
+    # invalid shapes give 0
+    assert ws(0, 10, 1, 32, 32, torch.float32) == 0
+    assert ws(1, 10, 1, 48, 32, torch.float32) == 0
+    assert ws(1, 10, 0, 32, 32, torch.float32) == 0
+    assert ws(1, -1, 1, 32, 32, torch.float32) == 0
+    # zero tokens still plans the table
+    assert ws(3, 0, 2, 64, 64, torch.bfloat16) > 0
+
+
+# fake device addresses: never dereferenced because every case fails validation first
+A = 1 << 20
+
+
+def _chunk(L, **kw):
+    a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, init=None, cu=None, N=1, T=64, H=2,
+             dk=32, dv=32, dtype=BF16, o=6 * A, fin=7 * A, ws=8 * A, wsb=1 << 40, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kda_chunk_fwd(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]),
+                           vp(a["init"]), vp(a["cu"]), a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                           a["dtype"], vp(a["o"]), vp(a["fin"]), vp(a["ws"]), a["wsb"], vp(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=0), INVALID),
+    (dict(H=0), INVALID),
+    (dict(T=-5), INVALID),
+    (dict(T=1 << 31), INVALID),
+    (dict(dk=48), NOT_SUPPORTED),
+    (dict(dv=256), NOT_SUPPORTED),
+    (dict(dtype=7), NOT_SUPPORTED),
+    (dict(dtype=F32, dk=128), NOT_SUPPORTED),
+    (dict(N=3, T=64), INVALID),            # equal lengths need T % N == 0
+    (dict(q=None), INVALID),
+    (dict(beta=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(q=A + 8), INVALID),              # misaligned
+    (dict(beta=5 * A + 1), INVALID),       # beta needs its element alignment
+    (dict(fin=7 * A + 4), INVALID),
+    (dict(ws=8 * A + 16), INVALID),        # workspace must be 256-byte aligned
+    (dict(wsb=1024), WS_SMALL),
+    (dict(init=9 * A, fin=9 * A + 256), INVALID),   # partial overlap of init and final
+    (dict(o=A), INVALID),                  # o overlaps q
+])
+def test_chunk_fwd_argument_errors(kw, expect):
+    assert _chunk(kda.lib(), **kw) == expect
+
+
+def _decode(L, **kw):
+    a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, state=6 * A, o=7 * A, N=2, H=2, dk=32,
+             dv=32, dtype=BF16, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kda_decode_step(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]),
+                             vp(a["state"]), vp(a["o"]), a["N"], a["H"], a["dk"], a["dv"],
+                             a["dtype"], vp(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=0), INVALID),
+    (dict(H=-1), INVALID),
+    (dict(dk=100), NOT_SUPPORTED),
+    (dict(dtype=3), NOT_SUPPORTED),
+    (dict(state=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(k=2 * A + 2), INVALID),
+    (dict(beta=5 * A + 1), INVALID),
+    (dict(o=6 * A), INVALID),              # o overlaps the state
+])
+def test_decode_step_argument_errors(kw, expect):
+    assert _decode(kda.lib(), **kw) == expect
