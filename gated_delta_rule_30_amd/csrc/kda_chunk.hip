@@ -30,6 +30,8 @@
 // the diagonal sub-block using e^{-(block decay)} >= 1 (the renormalisation the Technical
 // Breakdown asks for in section 4's numerical-stability note). The solve runs in fp32 on
 // VALU (diagonal 16x16 blocks) and fp32 MFMA (off-diagonal blocks). The state stays fp32.
+#include <mutex>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -49,7 +51,7 @@ struct Rec {
   static constexpr size_t oPb = oTb + (size_t)CHUNK * CHUNK;     // [CHUNK rows][CHUNK]
   static constexpr size_t nMat = oPb + (size_t)CHUNK * CHUNK;
   static constexpr size_t oGamBytes = nMat * sizeof(MT);         // K fp32
-  static constexpr size_t bytes = (oGamBytes + K * 4 + 255) / 256 * 256;
+  static constexpr size_t bytes = (oGamBytes + K * 4 + 1023) / 1024 * 1024;  // whole 1 KB slots
 };
 
 template <typename MT>
@@ -59,19 +61,39 @@ __device__ __forceinline__ size_t slot_elem(int tile, int step, int lane, int L)
 
 // four consecutive MT values from fp32
 __device__ __forceinline__ void st4(bf16* p, f32x4 x) {
-  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+  *reinterpret_cast<bf16x4*>(p) = __builtin_convertvector(x, bf16x4);
 }
 __device__ __forceinline__ void st4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
 __device__ __forceinline__ f32x4 ld4f(const bf16* p) {
-  bf16x4 b = *reinterpret_cast<const bf16x4*>(p);
-  return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+  return __builtin_convertvector(*reinterpret_cast<const bf16x4*>(p), f32x4);
 }
 __device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
+// N consecutive elements of T <-> fp32, with one vector memory access (N * sizeof(T) bytes,
+// naturally aligned).
+template <typename T, int N>
+struct VecN {
+  typedef T vec __attribute__((ext_vector_type(N)));
+  __device__ __forceinline__ static void load(const T* p, float* out) {
+    const vec x = *reinterpret_cast<const vec*>(p);
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = to_f32<T>(x[i]);
+  }
+  __device__ __forceinline__ static void store(T* p, const float* in) {
+    vec x;
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = from_f32<T>(in[i]);
+    *reinterpret_cast<vec*>(p) = x;
+  }
+};
+
 // ====================================================================== chunk table
-// Entries are ordered depth-major: chunk d of every sequence that has one, then chunk d+1,
-// so one segment advances many sequences at once and short sequences drop out early.
-// position(n, d) = sum_{n'} min(nc_{n'}, d) + #{n' < n : nc_{n'} > d}.
+// Entries are ordered depth-major (chunk d of every sequence that has one, then chunk d+1),
+// so one segment advances many sequences at once and short sequences drop out early. Within a
+// depth, sequences are ordered by decreasing chunk count (ties by index). With r_n the rank of
+// sequence n in that order, every sequence ranked before n has at least as many chunks, so
+//     pos(n, d) = base[d] + r_n,   base[d] = sum_{n'} min(nc_{n'}, d),
+// and a sequence's chunk indices follow from base[] alone, without walking the table.
 struct SeqView {
   const int32_t* cu;
   int num_seqs;
@@ -87,27 +109,50 @@ __global__ __launch_bounds__(256) void table_kernel(SeqView sv, int H, int64_t K
                                                     const float* __restrict__ init,
                                                     float* __restrict__ fin,
                                                     Entry* __restrict__ entries,
-                                                    int32_t* __restrict__ header) {
+                                                    int32_t* __restrict__ header,
+                                                    int32_t* __restrict__ basetab,
+                                                    float* __restrict__ zeros) {
   const int n = blockIdx.x;
+  if (n == 0) zeros[threadIdx.x] = 0.f;  // 1 KB zero block read by the state kernel
   const int64_t len = sv.len(n);
   const int64_t nc = sv.nchunks(n);
+  // rank of n: sequences with more chunks, or as many and a smaller index, come first
+  __shared__ int64_t red[256];
+  int64_t rk = 0;
+  for (int j = threadIdx.x; j < sv.num_seqs; j += blockDim.x) {
+    const int64_t cj = sv.nchunks(j);
+    rk += (cj > nc || (cj == nc && j < n)) ? 1 : 0;
+  }
+  red[threadIdx.x] = rk;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  const int64_t rank = red[0];
   for (int64_t d = threadIdx.x; d < nc; d += blockDim.x) {
-    int64_t pos = 0, posm = 0, posp = 0;
+    int64_t base = 0, cnt = 0, cntm = 0;  // base[d], #{nc > d}, #{nc > d-1}
     for (int j = 0; j < sv.num_seqs; ++j) {
       const int64_t cj = sv.nchunks(j);
-      pos += min(cj, d) + ((j < n && cj > d) ? 1 : 0);
-      posm += min(cj, d - 1) + ((j < n && cj > d - 1) ? 1 : 0);
-      posp += min(cj, d + 1) + ((j < n && cj > d + 1) ? 1 : 0);
+      base += min(cj, d);
+      cnt += cj > d ? 1 : 0;
+      cntm += cj > d - 1 ? 1 : 0;
     }
+    const int64_t pos = base + rank;
     Entry en;
     en.seq = n;
     en.tok = (int32_t)(sv.start(n) + d * CHUNK);
     en.len = (int32_t)min((int64_t)CHUNK, len - d * CHUNK);
     en.depth = (int32_t)d;
-    en.prev = d > 0 ? (int32_t)posm : -1;
-    en.next = d + 1 < nc ? (int32_t)posp : -1;
-    en.pad0 = en.pad1 = 0;
+    en.prev = d > 0 ? (int32_t)(base - cntm + rank) : -1;
+    en.next = d + 1 < nc ? (int32_t)(base + cnt + rank) : -1;
+    en.end = (int32_t)(sv.start(n) + len);
+    en.pad = 0;
     if (pos < ub) entries[pos] = en;  // always true for a well-formed cu_seqlens
+    if (rank == 0 && d <= ub) {       // the longest sequence has a chunk at every depth
+      basetab[d] = (int32_t)base;
+      if (d + 1 == nc && d + 1 <= ub) basetab[d + 1] = (int32_t)(base + cnt);
+    }
   }
   if (nc == 0 && fin != nullptr) {  // empty sequence: final state = initial state (or zero)
     const int64_t base = (int64_t)n * H * KV;
@@ -244,80 +289,109 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
   const int gq = lane >> 4;
   const int64_t rowstride = (int64_t)H * K;  // elements between consecutive tokens
 
-  // ---------------- phase 1a: in-block cumulative log decay per (channel, sub-block)
-  constexpr int NPAIRS_CB = K * NSUB;
-  constexpr int PPT = (NPAIRS_CB + NTHREADS - 1) / NTHREADS;
-  float lreg[PPT][SUBBLK];
-  if (tid < CHUNK) sBeta[tid] = tid < len ? to_f32(gb_[(tok0 + tid) * H + h]) : 0.f;
+  // ---------------- phase 1: wave w owns sub-block I = w (16 tokens). Lane (tg, cg) holds
+  // tokens 16I + 4tg .. +3 and channels CPL*cg .. +CPL-1, loaded with one vector load per token.
+  constexpr int CPL = K / 16;
+  using vin = VecN<MT, CPL>;
+  const int I = w;
+  const int tg = lane >> 4, cg = lane & 15;
+  const int c0 = CPL * cg;
+  float qv[4][CPL], kv[4][CPL], lv[4][CPL];
 #pragma unroll
-  for (int pp = 0; pp < PPT; ++pp) {
-    const int pidx = tid + pp * NTHREADS;
-    if (pidx < NPAIRS_CB) {
-      const int c = pidx % K, I = pidx / K;
-      float acc = 0.f;
+  for (int jt = 0; jt < 4; ++jt) {
+    const int t = 16 * I + 4 * tg + jt;
+    if (t < len) {
+      const int64_t off = (tok0 + t) * rowstride + (int64_t)h * K + c0;
+      vin::load(gq_ + off, qv[jt]);
+      vin::load(gk_ + off, kv[jt]);
+      vin::load(gg_ + off, lv[jt]);
+    } else {
 #pragma unroll
-      for (int i = 0; i < SUBBLK; ++i) {
-        const int t = I * SUBBLK + i;
-        const float gv = t < len ? to_f32(gg_[(tok0 + t) * rowstride + (int64_t)h * K + c]) : 0.f;
-        acc += gv;
-        lreg[pp][i] = acc;
-      }
-      sDel[I * K + c] = acc;
+      for (int i = 0; i < CPL; ++i) qv[jt][i] = kv[jt][i] = lv[jt][i] = 0.f;
     }
+    if (cg == 0) sBeta[t] = t < len ? to_f32(gb_[(tok0 + t) * H + h]) : 0.f;
   }
+  // in-block inclusive cumsum of log alpha: 4 tokens in-lane, then across the 4 token groups
+  // (all channels' shuffles issued together)
+  float tot[CPL], x[CPL], y[CPL], dI[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    float acc = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      acc += lv[jt][i];
+      lv[jt][i] = acc;
+    }
+    tot[i] = acc;
+    x[i] = acc;
+  }
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) y[i] = __shfl_up(x[i], 16);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) x[i] += (tg >= 1) ? y[i] : 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) y[i] = __shfl_up(x[i], 32);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) x[i] += (tg >= 2) ? y[i] : 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) dI[i] = __shfl(x[i], 48 + cg);  // log decay of the sub-block
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const float excl = x[i] - tot[i];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) lv[jt][i] += excl;
+  }
+  if (tg == 0) VecN<float, CPL>::store(sDel + I * K + c0, dI);
   __syncthreads();
-
-  // ---------------- phase 1b: decayed operands, D table, Ktilde^T and gamma to the record
+  // chunk-level factors per channel, the D table and gamma
+  float Eprev[CPL], tailf[CPL];
 #pragma unroll
-  for (int pp = 0; pp < PPT; ++pp) {
-    const int pidx = tid + pp * NTHREADS;
-    if (pidx < NPAIRS_CB) {
-      const int c = pidx % K, I = pidx / K;
-      float ecum[NSUB + 1];  // ecum[J+1] = e_J, ecum[0] = 0 (chunk start)
-      ecum[0] = 0.f;
+  for (int i = 0; i < CPL; ++i) {
+    const int c = c0 + i;
+    float ecum[NSUB + 1];  // ecum[J+1] = e_J: log decay from the chunk start to the end of block J
+    ecum[0] = 0.f;
 #pragma unroll
-      for (int J = 0; J < NSUB; ++J) ecum[J + 1] = ecum[J] + sDel[J * K + c];
-      const float eprev = ecum[I];          // e_{I-1}
-      const float dI = sDel[I * K + c];     // block decay (log), <= 0
-      const float elast = ecum[NSUB];
-      const float Eprev = exp_f(eprev);
-      const float tailf = exp_f(elast - ecum[I + 1]);  // e^{e_last - e_I}
-      sEx[I * K + c] = Eprev;
-      // D table for pairs (I, J <= I)
+    for (int J = 0; J < NSUB; ++J) ecum[J + 1] = ecum[J] + sDel[J * K + c];
+    Eprev[i] = exp_f(ecum[I]);                     // e^{e_{I-1}}
+    tailf[i] = exp_f(ecum[NSUB] - ecum[I + 1]);    // e^{e_last - e_I}
+    if (tg == 0) {
+      sEx[I * K + c] = Eprev[i];
       const int pbase = I * (I + 1) / 2;
 #pragma unroll
       for (int J = 0; J < NSUB; ++J)
-        if (J <= I) sD[(pbase + J) * K + c] = (J < I) ? exp_f(eprev - ecum[J + 1]) : exp_f(-dI);
-      if (I == NSUB - 1) recGam[c] = exp_f(elast);
-      float ktv[SUBBLK];
-#pragma unroll
-      for (int i = 0; i < SUBBLK; ++i) {
-        const int t = I * SUBBLK + i;
-        float qv = 0.f, kv = 0.f;
-        if (t < len) {
-          const int64_t off = (tok0 + t) * rowstride + (int64_t)h * K + c;
-          qv = to_f32(gq_[off]);
-          kv = to_f32(gk_[off]);
-        }
-        const float l = lreg[pp][i];
-        const float r = exp_f(l);          // e^{b_t - e_{I-1}} <= 1
-        const float cc = exp_f(dI - l);    // e^{e_I - b_t} <= 1
-        sQh[t * L::LK + c] = from_f32<MT>(qv * r);
-        sKh[t * L::LK + c] = from_f32<MT>(kv * r);
-        sKb[t * L::LKF + c] = kv * cc;
-        sKaT[c * L::LC + t] = from_f32<MT>(kv * r * Eprev);
-        ktv[i] = kv * cc * tailf;          // k * e^{b_last - b_t}
-      }
-      // Ktilde^T rows = channels, reduction = tokens: 4 quads of consecutive tokens
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int t0 = I * SUBBLK + 4 * qd;
-        const int s = t0 / KS, kp = t0 % KS;
-        const int ln = ((kp & 15) >> 2) * 16 + (c & 15);
-        st4(recM + R::oKt + slot_elem<MT>(c >> 4, s, ln, CHUNK) + 4 * (kp >> 4),
-            f32x4{ktv[4 * qd], ktv[4 * qd + 1], ktv[4 * qd + 2], ktv[4 * qd + 3]});
-      }
+        if (J <= I) sD[(pbase + J) * K + c] = (J < I) ? exp_f(ecum[I] - ecum[J + 1]) : exp_f(-dI[i]);
+      if (I == NSUB - 1) recGam[c] = exp_f(ecum[NSUB]);
     }
+  }
+  // decayed operands of the four tokens
+  float ka[4][CPL], kt[4][CPL];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    const int t = 16 * I + 4 * tg + jt;
+    float qr[CPL], kr[CPL], kc[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const float r = exp_f(lv[jt][i]);          // e^{b_t - e_{I-1}} <= 1
+      const float cc = exp_f(dI[i] - lv[jt][i]);  // e^{e_I - b_t} <= 1
+      qr[i] = qv[jt][i] * r;
+      kr[i] = kv[jt][i] * r;
+      kc[i] = kv[jt][i] * cc;
+      ka[jt][i] = kr[i] * Eprev[i];               // k e^{b_t}
+      kt[jt][i] = kc[i] * tailf[i];               // k e^{b_last - b_t}
+    }
+    vin::store(sQh + t * L::LK + c0, qr);
+    vin::store(sKh + t * L::LK + c0, kr);
+    VecN<float, CPL>::store(sKb + t * L::LKF + c0, kc);
+  }
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = c0 + i;
+    st4(sKaT + c * L::LC + 16 * I + 4 * tg, f32x4{ka[0][i], ka[1][i], ka[2][i], ka[3][i]});
+    // Ktilde^T: rows = channels, reduction = tokens; the 4 tokens form one quad of a slot
+    const int t0 = 16 * I + 4 * tg;
+    const int kp = t0 % KS;
+    st4(recM + R::oKt + slot_elem<MT>(c >> 4, t0 / KS, tg * 16 + (c & 15), CHUNK) + 4 * (kp >> 4),
+        f32x4{kt[0][i], kt[1][i], kt[2][i], kt[3][i]});
   }
   __syncthreads();
 
@@ -364,57 +438,68 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
   __syncthreads();
 
   // ---------------- phase 3: T = (I + A)^{-1}
-  // Diagonal 16x16 blocks: forward substitution, one lane per column, in place.
-  if (w == 0) {
-    const int I = lane >> 4, c = lane & 15;
-    float* Ab = sA + (16 * I) * L::LCF + 16 * I;
+  // (a) Diagonal 16x16 blocks, one per wave, by forward substitution. Lane c keeps column c of
+  //     T_II in registers; the coefficients A_II[i][j] are broadcast from registers (readlane).
+  {
+    float* Ab = sA + (16 * w) * L::LCF + 16 * w;
+    const f32x4 arow = *reinterpret_cast<const f32x4*>(Ab + (lane >> 2) * L::LCF + 4 * (lane & 3));
+    const int c = lane & 15;
     float t[SUBBLK];
 #pragma unroll
     for (int i = 0; i < SUBBLK; ++i) {
       float x = (i == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int jj = 0; jj < i; ++jj) x -= Ab[i * L::LCF + jj] * t[jj];
+      for (int jj = 0; jj < i; ++jj) {
+        const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(arow[jj & 3]), 4 * i + (jj >> 2)));
+        x -= a * t[jj];
+      }
       t[i] = x;
     }
+    if (lane < 16) {
 #pragma unroll
-    for (int i = 0; i < SUBBLK; ++i) Ab[i * L::LCF + c] = t[i];
+      for (int i = 0; i < SUBBLK; ++i) Ab[i * L::LCF + c] = t[i];
+    }
   }
   __syncthreads();
-  // T[16I+a][16J+b] for I > J is stored at sA[(16J+a)][16I+b] (the unused upper block).
-  auto Tget = [&](int i, int jj) -> float {
-    const int I = i >> 4, J = jj >> 4;
-    if (I == J) return sA[i * L::LCF + jj];
-    if (I > J) return sA[(16 * J + (i & 15)) * L::LCF + 16 * I + (jj & 15)];
-    return 0.f;
-  };
-  // Off-diagonal blocks by block distance: T_IJ = -T_II sum_{M=J}^{I-1} A_IM T_MJ (fp32 MFMA).
+  // (b) Off-diagonal blocks of row block I = w, right to left, with no further barrier:
+  //     T_IJ = -(sum_{M=J+1}^{I} T_IM A_MJ) T_JJ, computed transposed so that every operand
+  //     is a column read, a row read or the previous result tile. T_IJ (I > J) is stored
+  //     row-major in the unused upper block (J, I) of sA.
+  {
+    const int Ib = w;
+    auto tblock = [&](int I, int M) -> float* {  // base of T_IM (I >= M)
+      return (I == M) ? sA + (16 * I) * L::LCF + 16 * I : sA + (16 * M) * L::LCF + 16 * I;
+    };
+    for (int J = Ib - 1; J >= 0; --J) {
+      f32x4 X = {0.f, 0.f, 0.f, 0.f};  // X^T = sum_M A_MJ^T T_IM^T
+      for (int M = J + 1; M <= Ib; ++M) {
+        f32x4 af;
 #pragma unroll
-  for (int d = 1; d < NSUB; ++d) {
-    if (w < NSUB - d) {
-      const int J = w, I = w + d;
-      f32x4 X = {0.f, 0.f, 0.f, 0.f};
-      for (int M = J; M < I; ++M) {
-        const f32x4 af = *reinterpret_cast<const f32x4*>(sA + (16 * I + m) * L::LCF + 16 * M + 4 * gq);
-        f32x4 bf;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bf[r] = Tget(16 * M + 4 * gq + r, 16 * J + m);
+        for (int r = 0; r < 4; ++r) af[r] = sA[(16 * M + 4 * gq + r) * L::LCF + 16 * J + m];
+        const f32x4 bf = *reinterpret_cast<const f32x4*>(tblock(Ib, M) + m * L::LCF + 4 * gq);
         X = Mma<float>::mma(af, bf, X);
       }
-      const f32x4 tf = *reinterpret_cast<const f32x4*>(sA + (16 * I + m) * L::LCF + 16 * I + 4 * gq);
-      const f32x4 Y = Mma<float>::mma(tf, X, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 tjj;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sA[(16 * J + 4 * gq + r) * L::LCF + 16 * I + m] = -Y[r];
+      for (int r = 0; r < 4; ++r) tjj[r] = sA[(16 * J + 4 * gq + r) * L::LCF + 16 * J + m];
+      const f32x4 Y = Mma<float>::mma(tjj, X, f32x4{0.f, 0.f, 0.f, 0.f});  // (T_IJ)^T
+      *reinterpret_cast<f32x4*>(tblock(Ib, J) + m * L::LCF + 4 * gq) = -Y;
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   // ---------------- phase 4: T' = T diag(beta) (and its transpose), -P, all in MT
-  for (int idx = tid; idx < CHUNK * CHUNK; idx += NTHREADS) {
-    const int i = idx / CHUNK, jj = idx % CHUNK;
-    const float tb = (i >= jj) ? Tget(i, jj) * sBeta[jj] : 0.f;
-    sTb[i * L::LC + jj] = from_f32<MT>(tb);
-    sTbT[jj * L::LC + i] = from_f32<MT>(tb);
-    sPn[i * L::LC + jj] = from_f32<MT>(-sP[i * L::LCF + jj]);
+  for (int idx = tid; idx < CHUNK * CHUNK / 4; idx += NTHREADS) {
+    const int i = idx / (CHUNK / 4), j0 = 4 * (idx % (CHUNK / 4));
+    const int Ii = i >> 4, Jj = j0 >> 4;
+    f32x4 tv = {0.f, 0.f, 0.f, 0.f};
+    if (Ii == Jj) tv = *reinterpret_cast<const f32x4*>(sA + i * L::LCF + j0);
+    else if (Ii > Jj) tv = *reinterpret_cast<const f32x4*>(sA + (16 * Jj + (i & 15)) * L::LCF + 16 * Ii + (j0 & 15));
+    tv *= *reinterpret_cast<const f32x4*>(sBeta + j0);
+    st4(sTb + i * L::LC + j0, tv);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sTbT[(j0 + k) * L::LC + i] = from_f32<MT>(tv[k]);
+    st4(sPn + i * L::LC + j0, -*reinterpret_cast<const f32x4*>(sP + i * L::LCF + j0));
   }
   __syncthreads();
   // T' to the record
@@ -483,18 +568,48 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
 }
 
 // ====================================================================== STATE kernel
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory operations of this
+// wave are outstanding (loads, LDS-DMA loads and stores alike), or until its LDS operations
+// have completed.
+#define KDA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+#define KDA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
+
+// Workgroup barrier for LDS data: waits for this wave's LDS accesses, not for its outstanding
+// global loads (so a prefetch stays in flight across it). The signal fences keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  KDA_WAIT_LGKM0();
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave writes
+// lds_wave_base + 16 * l (gfx950 global_load_lds_dwordx4).
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
 template <int K, int NVT, typename MT>
 struct StateLayout {
   static constexpr int VS = 16 * NVT;
   static constexpr int PADM = 16 / (int)sizeof(MT);
   static constexpr int LKs = K + PADM;
   static constexpr int LCs = CHUNK + PADM;
-  static constexpr int LOs = VS + PADM;
-  static constexpr size_t oS = 0;
-  static constexpr size_t oDl = oS + (size_t)VS * LKs * sizeof(MT);
-  static constexpr size_t oV = oDl + (size_t)VS * LCs * sizeof(MT);
-  static constexpr size_t oO = oV + (size_t)VS * LCs * sizeof(MT);
-  static constexpr size_t total = oO + (size_t)CHUNK * LOs * sizeof(MT);
+  static constexpr size_t RB = Rec<K, MT>::bytes;                 // one chunk record
+  static constexpr size_t VSB = (size_t)CHUNK * VS * sizeof(MT);  // one chunk of the V slice
+  static constexpr size_t FIX = (size_t)VS * LKs * sizeof(MT) + (size_t)VS * LCs * sizeof(MT) +
+                                (SEG_CHUNK_HEADS + 16) * 4;
+  static constexpr int NBUF = (2 * (RB + VSB) + FIX <= 160 * 1024) ? 2 : 1;
+  static constexpr size_t oRec = 0;                                // [NBUF] records
+  static constexpr size_t oVst = oRec + NBUF * RB;                 // [NBUF][CHUNK][VS] token-major
+  static constexpr size_t oS = oVst + NBUF * VSB;                  // S^T: [VS][K]
+  static constexpr size_t oDl = oS + (size_t)VS * LKs * sizeof(MT);  // Delta^T: [VS][CHUNK]
+  static constexpr size_t oRun = oDl + (size_t)VS * LCs * sizeof(MT);
+  static constexpr size_t total = oRun + (SEG_CHUNK_HEADS + 16) * 4;
+  static_assert(total <= 160 * 1024, "state LDS budget");
+  static_assert(RB % 1024 == 0 && VSB % 1024 == 0, "DMA slots");
 };
 
 struct StateParams {
@@ -504,6 +619,7 @@ struct StateParams {
   float* state;  // running and final state [N][H][K][V]
   const Entry* entries;
   const int32_t* header;
+  const int32_t* basetab;    // base[d] of the chunk table
   const int32_t* seg_first;  // this segment's list
   const int32_t* seg_count;  // this segment's count
   int64_t seg_begin, E;
@@ -511,22 +627,48 @@ struct StateParams {
   int64_t chains;  // slots * H
   const char* rec;
   int64_t rec_bytes;
+  const char* zeros;  // >= 1 KB of zeros (V rows past a chunk's end are loaded from here)
+  char* trash;        // >= 1 KB sink for output rows past a chunk's end
+};
+
+// Work split of one state workgroup: 8 waves over a V-slice of VS = 16*NVT columns.
+// Wave w computes the result tiles of token tile w % 4 for CT column tiles starting at
+// (w / 4) * CT (U, P'V, W S, Q_eff S, Delta, O), and the state update of row tiles w, w+8, ...
+template <int K, int NVT, typename MT>
+struct StateWork {
+  static constexpr int NW = 8;
+  static constexpr int NT = NW * 64;
+  static constexpr int WPT = NW / 4;                // waves per token tile
+  static constexpr int CT = NVT / WPT;              // column tiles per wave
+  static constexpr int NKT = K / 16;                // row tiles of S
+  static constexpr int TPW = (NKT + NW - 1) / NW;   // S row tiles per wave
+  static_assert(CT >= 1 && NVT % WPT == 0, "state work split");
 };
 
 template <int K, int NVT, typename MT>
-__global__ __launch_bounds__(256) void state_kernel(StateParams p) {
+__global__ __launch_bounds__(512) void state_kernel(StateParams p) {
   using SL = StateLayout<K, NVT, MT>;
   using R = Rec<K, MT>;
+  using WK = StateWork<K, NVT, MT>;
   using frag = typename Mma<MT>::frag;
   constexpr int KS = Mma<MT>::KS;
   constexpr int VS = SL::VS;
-  constexpr int NKT = K / 16;             // row tiles of S
-  constexpr int TPW = (NKT + 3) / 4;      // S row tiles per wave
+  constexpr int NW = WK::NW;
+  constexpr int NT = WK::NT;
+  constexpr int CT = WK::CT;
+  constexpr int NKT = WK::NKT;
+  constexpr int TPW = WK::TPW;
+  constexpr int NBUF = SL::NBUF;
+  constexpr int NSR = (int)(SL::RB / 1024);        // DMA slots of a record
+  constexpr int NSV = (int)(SL::VSB / 1024);       // DMA slots of a V chunk
+  constexpr int LPT = VS * (int)sizeof(MT) / 16;   // lanes per token row in a V slot
+  constexpr int TPS = 64 / LPT;                    // token rows per V slot
+  constexpr int NST = 4 * CT;                      // output stores per lane per chunk
   __shared__ __align__(16) char smem[SL::total];
   MT* sS = reinterpret_cast<MT*>(smem + SL::oS);    // S^T: [VS][K]
   MT* sDl = reinterpret_cast<MT*>(smem + SL::oDl);  // Delta^T: [VS][CHUNK]
-  MT* sV = reinterpret_cast<MT*>(smem + SL::oV);    // V^T: [VS][CHUNK]
-  MT* sO = reinterpret_cast<MT*>(smem + SL::oO);    // O: [CHUNK][VS]
+  int32_t* sRun = reinterpret_cast<int32_t*>(smem + SL::oRun);
+  int32_t* sLen = sRun + SEG_CHUNK_HEADS;
 
   // XCD-aware decode: all V-slices of a chain share blockIdx % 8 (the same XCD / L2).
   const int bid = blockIdx.x;
@@ -541,21 +683,37 @@ __global__ __launch_bounds__(256) void state_kernel(StateParams p) {
   if (slot >= p.seg_count[0]) return;
   const int64_t total = p.header[0];
   const int64_t seg_end = min(p.seg_begin + p.E, total);
-  int64_t e = p.seg_first[slot];
-  const Entry e0 = p.entries[e];
+  const int64_t e0 = p.seg_first[slot];
+  const Entry en = p.entries[e0];
   const int col0 = slice * VS;
-
+  const int tid = threadIdx.x;
   const int w = wave_id();
   const int lane = lane_id();
   const int m = lane & 15;
   const int gq = lane >> 4;
+  const int tw = w & 3;             // token tile of this wave's result tiles
+  const int ct0 = (w >> 2) * CT;    // first column tile of this wave's result tiles
 
-  const size_t sbase = ((size_t)e0.seq * H + h) * (size_t)K * V + col0;
-  const float* src = (e0.depth == 0) ? p.init_state : p.state;
+  // This workgroup's run: chunks d0, d0+1, ... of sequence en.seq inside the segment. Chunk
+  // d0+k is entry base[d0+k] + rank; the run ends at the sequence's end or the segment's end.
+  const int seq_start = en.tok - CHUNK * en.depth;
+  const int nc = (en.end - seq_start + CHUNK - 1) / CHUNK;
+  const int64_t rank = e0 - p.basetab[en.depth];
+  const int kmax = (int)min((int64_t)(nc - en.depth), p.E);
+  if (tid == 0) sLen[0] = kmax;
+  __syncthreads();
+  for (int k = tid; k < kmax; k += NT) {
+    const int64_t ek = p.basetab[en.depth + k] + rank;
+    sRun[k] = (int32_t)ek;
+    if (ek >= seg_end) atomicMin(&sLen[0], k);
+  }
+
+  const size_t sbase = ((size_t)en.seq * H + h) * (size_t)K * V + col0;
+  const float* src = (en.depth == 0) ? p.init_state : p.state;
   f32x4 Sr[TPW][NVT];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
-    const int t = w + 4 * tt;
+    const int t = w + NW * tt;
 #pragma unroll
     for (int nt = 0; nt < NVT; ++nt) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
@@ -567,107 +725,132 @@ __global__ __launch_bounds__(256) void state_kernel(StateParams p) {
       if (t < NKT) st4(sS + (16 * nt + m) * SL::LKs + 16 * t + 4 * gq, x);
     }
   }
+  __syncthreads();
+  const int run = sLen[0];
 
-  const MT* gv = reinterpret_cast<const MT*>(p.v);
-  MT* go = reinterpret_cast<MT*>(p.o);
+  const char* gv = reinterpret_cast<const char*>(reinterpret_cast<const MT*>(p.v) + (int64_t)h * V + col0);
+  MT* go = reinterpret_cast<MT*>(p.o) + (int64_t)h * V + col0;
   const int64_t vrow = (int64_t)H * V;
-  const int nst_tri = (16 * w + 16 + KS - 1) / KS;  // reduction steps of T', P' for row tile w
+  const int nst_tri = (16 * tw + 16 + KS - 1) / KS;  // reduction steps of T', P' for tile tw
+  auto tok_of = [&](int k) { return seq_start + CHUNK * (en.depth + k); };
+  auto len_of = [&](int k) { return min(CHUNK, en.end - tok_of(k)); };
 
-  while (e >= 0 && e < seg_end) {
-    const Entry en = p.entries[e];
-    const char* rc = p.rec + ((e - p.seg_begin) * H + h) * p.rec_bytes;
-    const MT* rm = reinterpret_cast<const MT*>(rc);
-    const float* rg = reinterpret_cast<const float*>(rc + R::oGamBytes);
+  // DMA of chunk k (clamped to the run's last chunk) into buffer b: the record slots and the
+  // V slice (token-major; rows past the chunk's length come from the zero block).
+  auto issue = [&](int k, int b) {
+    const int kk = min(k, run - 1);
+    const char* rc = p.rec + ((int64_t)sRun[kk] - p.seg_begin) * H * p.rec_bytes + (int64_t)h * p.rec_bytes;
+    char* lrec = smem + SL::oRec + b * SL::RB;
+#pragma unroll
+    for (int i = 0; i < (NSR + NW - 1) / NW; ++i) {
+      const int sl = w + NW * i;
+      if (sl < NSR) dma16(rc + sl * 1024 + lane * 16, lrec + sl * 1024);
+    }
+    const int tok = tok_of(kk), len = len_of(kk);
+    char* lv = smem + SL::oVst + b * SL::VSB;
+#pragma unroll
+    for (int i = 0; i < (NSV + NW - 1) / NW; ++i) {
+      const int sv = w + NW * i;
+      if (sv >= NSV) continue;
+      const int t = sv * TPS + lane / LPT, part = lane % LPT;
+      const char* g = t < len ? gv + ((int64_t)tok + t) * vrow * (int64_t)sizeof(MT) + part * 16
+                              : p.zeros + part * 16;
+      dma16(g, lv + sv * 1024);
+    }
+  };
 
-    // V slice of the chunk, transposed into LDS, zero beyond the chunk's length
-    for (int idx = threadIdx.x; idx < CHUNK * VS; idx += NTHREADS) {
-      const int t = idx / VS, cc = idx % VS;
-      const float x = t < en.len ? to_f32(gv[((int64_t)en.tok + t) * vrow + (int64_t)h * V + col0 + cc]) : 0.f;
-      sV[cc * SL::LCs + t] = from_f32<MT>(x);
-    }
-    // this wave's record fragments
-    frag wf[K / KS], qf[K / KS], tf[CHUNK / KS], pf[CHUNK / KS], kf[TPW][CHUNK / KS];
+  auto process = [&](int k, int b) {
+    const int tok = tok_of(k), len = len_of(k);
+    const char* lrec = smem + SL::oRec + b * SL::RB;
+    const MT* lv = reinterpret_cast<const MT*>(smem + SL::oVst + b * SL::VSB);
+    auto afrag = [&](size_t off_elems) -> frag {  // A fragment of this lane from the LDS record
+      return *reinterpret_cast<const frag*>(lrec + off_elems * sizeof(MT));
+    };
 #pragma unroll
-    for (int s = 0; s < K / KS; ++s) {
-      wf[s] = *reinterpret_cast<const frag*>(rm + R::oW + slot_elem<MT>(w, s, lane, K));
-      qf[s] = *reinterpret_cast<const frag*>(rm + R::oQ + slot_elem<MT>(w, s, lane, K));
-    }
-#pragma unroll
-    for (int s = 0; s < CHUNK / KS; ++s) {
-      tf[s] = *reinterpret_cast<const frag*>(rm + R::oTb + slot_elem<MT>(w, s, lane, CHUNK));
-      pf[s] = *reinterpret_cast<const frag*>(rm + R::oPb + slot_elem<MT>(w, s, lane, CHUNK));
-    }
-    f32x4 gam[TPW];
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-      const int t = w + 4 * tt;
-      if (t < NKT) {
-#pragma unroll
-        for (int s = 0; s < CHUNK / KS; ++s)
-          kf[tt][s] = *reinterpret_cast<const frag*>(rm + R::oKt + slot_elem<MT>(t, s, lane, CHUNK));
-        gam[tt] = *reinterpret_cast<const f32x4*>(rg + 16 * t + 4 * gq);
-      }
-    }
-    __syncthreads();  // sV and sS ready
-
-#pragma unroll
-    for (int nt = 0; nt < NVT; ++nt) {
+    for (int c = 0; c < CT; ++c) {
+      const int nt = ct0 + c;
       f32x4 U = {0.f, 0.f, 0.f, 0.f}, Ol = U, Y = U, Z = U;
-      for (int s = 0; s < nst_tri; ++s) {
-        const auto bv = load_frag(sV + (16 * nt + m) * SL::LCs, s, gq);
-        U = Mma<MT>::mma(tf[s], bv, U);
-        Ol = Mma<MT>::mma(pf[s], bv, Ol);
+#pragma unroll
+      for (int s = 0; s < CHUNK / KS; ++s) {
+        if (s < nst_tri) {
+          frag bv;  // B fragment of V: tokens kk(g, e) of column 16nt + m
+#pragma unroll
+          for (int e = 0; e < Mma<MT>::EPL; ++e)
+            bv[e] = lv[(KS * s + 16 * (e / 4) + 4 * gq + (e % 4)) * VS + 16 * nt + m];
+          U = Mma<MT>::mma(afrag(R::oTb + slot_elem<MT>(tw, s, lane, CHUNK)), bv, U);
+          Ol = Mma<MT>::mma(afrag(R::oPb + slot_elem<MT>(tw, s, lane, CHUNK)), bv, Ol);
+        }
       }
 #pragma unroll
       for (int s = 0; s < K / KS; ++s) {
         const auto bs = load_frag(sS + (16 * nt + m) * SL::LKs, s, gq);
-        Y = Mma<MT>::mma(wf[s], bs, Y);
-        Z = Mma<MT>::mma(qf[s], bs, Z);
+        Y = Mma<MT>::mma(afrag(R::oW + slot_elem<MT>(tw, s, lane, K)), bs, Y);
+        Z = Mma<MT>::mma(afrag(R::oQ + slot_elem<MT>(tw, s, lane, K)), bs, Z);
       }
       const f32x4 D = U - Y;
       const f32x4 O = Ol + Z;
-      st4(sDl + (16 * nt + m) * SL::LCs + 16 * w + 4 * gq, D);
+      st4(sDl + (16 * nt + m) * SL::LCs + 16 * tw + 4 * gq, D);
+      // output rows straight from the result tile; rows past the chunk's end go to the sink,
+      // so every lane issues the same number of stores
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sO[(16 * w + 4 * gq + r) * SL::LOs + 16 * nt + m] = from_f32<MT>(O[r]);
-    }
-    __syncthreads();  // Delta and O complete
-
-    // output rows of this chunk
-    {
-      constexpr int EPV = 16 / (int)sizeof(MT);
-      constexpr int VPR = VS / EPV;
-      for (int idx = threadIdx.x; idx < CHUNK * VPR; idx += NTHREADS) {
-        const int t = idx / VPR, vi = idx % VPR;
-        if (t < en.len) {
-          const uint4 x = *reinterpret_cast<const uint4*>(sO + t * SL::LOs + vi * EPV);
-          *reinterpret_cast<uint4*>(go + ((int64_t)en.tok + t) * vrow + (int64_t)h * V + col0 + vi * EPV) = x;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tw + 4 * gq + r;
+        MT* dst = t < len ? go + ((int64_t)tok + t) * vrow + 16 * nt + m
+                          : reinterpret_cast<MT*>(p.trash) + lane;
+        *dst = from_f32<MT>(O[r]);
       }
     }
+    lds_barrier();  // Delta complete; everyone is done reading sS
     // state update S = gamma * S + Ktilde^T Delta
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-      const int t = w + 4 * tt;
+      const int t = w + NW * tt;
       if (t < NKT) {
+        const f32x4 gam = *reinterpret_cast<const f32x4*>(lrec + R::oGamBytes + (16 * t + 4 * gq) * 4);
 #pragma unroll
         for (int nt = 0; nt < NVT; ++nt) {
-          f32x4 acc = gam[tt] * Sr[tt][nt];
+          f32x4 acc = gam * Sr[tt][nt];
 #pragma unroll
           for (int s = 0; s < CHUNK / KS; ++s) {
             const auto bd = load_frag(sDl + (16 * nt + m) * SL::LCs, s, gq);
-            acc = Mma<MT>::mma(kf[tt][s], bd, acc);
+            acc = Mma<MT>::mma(afrag(R::oKt + slot_elem<MT>(t, s, lane, CHUNK)), bd, acc);
           }
           Sr[tt][nt] = acc;
           st4(sS + (16 * nt + m) * SL::LKs + 16 * t + 4 * gq, acc);
         }
       }
     }
-    e = en.next > e ? en.next : -1;  // entries of a sequence are strictly increasing
+  };
+
+  KDA_WAIT_VM(0);  // initial state loads done before counting DMA operations
+  if constexpr (NBUF == 2) {
+    // chunk k+1 streams into the other buffer while chunk k is computed; at the top of each
+    // step only the previous chunk's NST output stores may still be outstanding
+    issue(0, 0);
+    for (int k = 0; k < run; ++k) {
+      if (k == 0) {
+        KDA_WAIT_VM(0);
+      } else {
+        KDA_WAIT_VM(NST);
+      }
+      lds_barrier();  // chunk k's record and V are in LDS; sS holds the current state
+      issue(k + 1, (k + 1) & 1);
+      process(k, k & 1);
+    }
+  } else {
+    for (int k = 0; k < run; ++k) {
+      lds_barrier();  // the previous chunk is done with the single buffer
+      issue(k, 0);
+      KDA_WAIT_VM(0);
+      lds_barrier();
+      process(k, 0);
+    }
   }
+  KDA_WAIT_VM(0);
 
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
-    const int t = w + 4 * tt;
+    const int t = w + NW * tt;
     if (t < NKT) {
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt)
@@ -691,26 +874,27 @@ bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan
   p->seg_entries = E;
   p->num_segs = ub > 0 ? (ub + E - 1) / E : 0;
   p->slots = N < E ? N : E;
-  p->rec_bytes = ((3LL * CHUNK * K + 2LL * CHUNK * CHUNK) * es + 4LL * K + 255) / 256 * 256;
-  // V split: enough (sequence, head, slice) workgroups to cover the CUs, slices of 16..64
-  const int64_t chains = p->slots * H;
-  int ns = 1;
-  while (chains * ns < 512 && ns < V / 16) ns *= 2;
-  while (V / ns > 64) ns *= 2;
-  p->n_slices = ns;
-  p->vs = V / ns;
+  p->rec_bytes = ((3LL * CHUNK * K + 2LL * CHUNK * CHUNK) * es + 4LL * K + 1023) / 1024 * 1024;
+  // V split: slices of 32 columns (8-wave workgroups; the double-buffered chunk record in LDS
+  // leaves room for 32 columns of state)
+  p->n_slices = V / 32;
+  p->vs = 32;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = 0;
   p->off_header = off;
   off += 256;
   p->off_entries = off;
   off += al((size_t)ub * sizeof(Entry));
+  p->off_basetab = off;
+  off += al((size_t)(ub + 1) * 4);
   p->off_seg_first = off;
   off += al((size_t)p->num_segs * p->slots * 4);
   p->off_seg_count = off;
   off += al((size_t)p->num_segs * 4);
   p->off_state = off;
   off += al((size_t)N * H * K * V * 4);
+  p->off_zeros = off;  // 1 KB of zeros, then a 1 KB sink
+  off += 2048;
   p->off_rec = off;
   p->rec_buf_bytes = (size_t)E * H * p->rec_bytes;
   off += 2 * p->rec_buf_bytes;
@@ -718,12 +902,44 @@ bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan
   return true;
 }
 
+// Per-device auxiliary stream and events, created once and kept for the life of the process:
+// the prep kernel of segment s+1 runs on the auxiliary stream while the state kernel of
+// segment s runs on the caller's stream. Both streams have the default priority.
+namespace {
+struct Aux {
+  bool ready = false;
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, prep_done[2] = {nullptr, nullptr}, state_done[2] = {nullptr, nullptr};
+};
+constexpr int kMaxDevices = 64;
+Aux g_aux[kMaxDevices];
+std::mutex g_aux_mutex;  // also serialises the enqueue sequence that uses the shared events
+
+Aux* get_aux(bool may_create) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  Aux& x = g_aux[dev];
+  if (x.ready) return &x;
+  if (!may_create) return nullptr;
+  if (hipStreamCreateWithFlags(&x.side, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  bool ok = hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess;
+  for (int i = 0; i < 2 && ok; ++i) {
+    ok = hipEventCreateWithFlags(&x.prep_done[i], hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&x.state_done[i], hipEventDisableTiming) == hipSuccess;
+  }
+  if (!ok) return nullptr;
+  x.ready = true;
+  return &x;
+}
+}  // namespace
+
 template <int K, typename MT>
 static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
   hipStream_t st = (hipStream_t)a.stream;
   char* ws = reinterpret_cast<char*>(a.workspace);
   Entry* entries = reinterpret_cast<Entry*>(ws + pl.off_entries);
   int32_t* header = reinterpret_cast<int32_t*>(ws + pl.off_header);
+  int32_t* basetab = reinterpret_cast<int32_t*>(ws + pl.off_basetab);
   int32_t* seg_first = reinterpret_cast<int32_t*>(ws + pl.off_seg_first);
   int32_t* seg_count = reinterpret_cast<int32_t*>(ws + pl.off_seg_count);
   float* run_state = a.final_state ? a.final_state : reinterpret_cast<float*>(ws + pl.off_state);
@@ -732,7 +948,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
   SeqView sv{a.cu_seqlens, a.num_seqs, a.total_tokens};
   hipLaunchKernelGGL(table_kernel, dim3(a.num_seqs), dim3(256), 0, st, sv, a.num_heads,
                      (int64_t)a.dk * a.dv, pl.ub_entries, a.init_state, a.final_state, entries,
-                     header);
+                     header, basetab, reinterpret_cast<float*>(ws + pl.off_zeros));
   if (pl.num_segs == 0) return hipGetLastError();
   hipLaunchKernelGGL(segment_kernel, dim3(pl.num_segs), dim3(256), 0, st, entries, header,
                      pl.seg_entries, pl.slots, seg_first, seg_count);
@@ -741,20 +957,47 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
   const int64_t chains8 = (chains + 7) / 8 * 8;
   const dim3 sgrid((unsigned)(chains8 * pl.n_slices));
   const dim3 pgrid((unsigned)(pl.seg_entries * a.num_heads));
-  for (int64_t s = 0; s < pl.num_segs; ++s) {
+  auto prep = [&](int64_t s, hipStream_t q) {
     char* rec = ws + pl.off_rec + (s & 1) * pl.rec_buf_bytes;
     PrepParams pp{a.q, a.k, a.g, a.beta, entries, header, a.num_heads, s * pl.seg_entries,
                   pl.seg_entries, rec, pl.rec_bytes};
-    hipLaunchKernelGGL((prep_kernel<K, MT>), pgrid, dim3(NTHREADS), 0, st, pp);
-    StateParams sp{a.v, a.o, a.init_state, run_state, entries, header,
+    hipLaunchKernelGGL((prep_kernel<K, MT>), pgrid, dim3(NTHREADS), 0, q, pp);
+  };
+  auto state = [&](int64_t s, hipStream_t q) -> bool {
+    const char* rec = ws + pl.off_rec + (s & 1) * pl.rec_buf_bytes;
+    StateParams sp{a.v, a.o, a.init_state, run_state, entries, header, basetab,
                    seg_first + s * pl.slots, seg_count + s, s * pl.seg_entries, pl.seg_entries,
-                   a.num_heads, a.dv, pl.n_slices, chains, rec, pl.rec_bytes};
-    switch (pl.vs) {
-      case 16: hipLaunchKernelGGL((state_kernel<K, 1, MT>), sgrid, dim3(NTHREADS), 0, st, sp); break;
-      case 32: hipLaunchKernelGGL((state_kernel<K, 2, MT>), sgrid, dim3(NTHREADS), 0, st, sp); break;
-      case 64: hipLaunchKernelGGL((state_kernel<K, 4, MT>), sgrid, dim3(NTHREADS), 0, st, sp); break;
-      default: return hipErrorInvalidValue;
+                   a.num_heads, a.dv, pl.n_slices, chains, rec, pl.rec_bytes,
+                   ws + pl.off_zeros, ws + pl.off_zeros + 1024};
+    if (pl.vs != 32) return false;
+    hipLaunchKernelGGL((state_kernel<K, 2, MT>), sgrid, dim3(512), 0, q, sp);
+    return true;
+  };
+
+  std::lock_guard<std::mutex> lock(g_aux_mutex);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cap) != hipSuccess) cap = hipStreamCaptureStatusNone;
+  Aux* aux = pl.num_segs > 1 ? get_aux(cap == hipStreamCaptureStatusNone) : nullptr;
+  if (aux == nullptr) {  // one stream: prep(s), state(s), prep(s+1), ...
+    for (int64_t s = 0; s < pl.num_segs; ++s) {
+      prep(s, st);
+      if (!state(s, st)) return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+  }
+  // two streams: prep(s) on the auxiliary stream overlaps state(s-1) on the caller's stream;
+  // record buffer s&1 is reused only after state(s-2) has finished with it.
+  if (hipEventRecord(aux->fork, st) != hipSuccess) return hipErrorLaunchFailure;
+  if (hipStreamWaitEvent(aux->side, aux->fork, 0) != hipSuccess) return hipErrorLaunchFailure;
+  for (int64_t s = 0; s < pl.num_segs; ++s) {
+    const int b = (int)(s & 1);
+    if (s >= 2 && hipStreamWaitEvent(aux->side, aux->state_done[b], 0) != hipSuccess)
+      return hipErrorLaunchFailure;
+    prep(s, aux->side);
+    if (hipEventRecord(aux->prep_done[b], aux->side) != hipSuccess) return hipErrorLaunchFailure;
+    if (hipStreamWaitEvent(st, aux->prep_done[b], 0) != hipSuccess) return hipErrorLaunchFailure;
+    if (!state(s, st)) return hipErrorInvalidValue;
+    if (hipEventRecord(aux->state_done[b], st) != hipSuccess) return hipErrorLaunchFailure;
   }
   return hipGetLastError();
 }

@@ -61,9 +61,9 @@ template <> struct Mma<float> {
 // Fragment of reduction step s for group g from a row whose reduction index is contiguous.
 __device__ __forceinline__ bf16x8 load_frag(const bf16* row, int s, int g) {
   const bf16* p = row + 32 * s + 4 * g;
-  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 __device__ __forceinline__ f32x4 load_frag(const float* row, int s, int g) {
   return *reinterpret_cast<const f32x4*>(row + 16 * s + 4 * g);
@@ -79,8 +79,8 @@ __device__ __forceinline__ bf16x8 load_frag_scaled(const float* row, const float
   f32x4 sb = *reinterpret_cast<const f32x4*>(scale + o + 16);
   a *= sa;
   b *= sb;
-  return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
-                (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+  return __builtin_shufflevector(__builtin_convertvector(a, bf16x4), __builtin_convertvector(b, bf16x4),
+                                 0, 1, 2, 3, 4, 5, 6, 7);
 }
 __device__ __forceinline__ f32x4 load_frag_scaled(const float* row, const float* scale, int s,
                                                   int g, float) {
@@ -90,8 +90,8 @@ __device__ __forceinline__ f32x4 load_frag_scaled(const float* row, const float*
 
 // Fragment made of two fp32 result tiles (rows 0-15 and 16-31 of a reduction step): bf16.
 __device__ __forceinline__ bf16x8 frag_from_acc(f32x4 lo, f32x4 hi, bf16) {
-  return bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3],
-                (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+  return __builtin_shufflevector(__builtin_convertvector(lo, bf16x4), __builtin_convertvector(hi, bf16x4),
+                                 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

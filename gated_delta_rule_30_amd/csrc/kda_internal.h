@@ -33,7 +33,8 @@ struct Entry {
   int32_t depth;  // chunk index inside its sequence
   int32_t prev;   // entry index of the previous chunk of the sequence, -1 if none
   int32_t next;   // entry index of the next chunk of the sequence, -1 if none
-  int32_t pad0, pad1;
+  int32_t end;    // one past the last token of the sequence (packed index)
+  int32_t pad;
 };
 
 // Host-side launch plan of one kda_chunk_fwd call; a pure function of the shape.
@@ -46,7 +47,8 @@ struct ChunkPlan {
   int n_slices;         // V split into n_slices slices of vs columns
   int vs;
   // workspace offsets (bytes)
-  size_t off_header, off_entries, off_seg_first, off_seg_count, off_state, off_rec, rec_buf_bytes;
+  size_t off_header, off_entries, off_basetab, off_seg_first, off_seg_count, off_state, off_zeros,
+      off_rec, rec_buf_bytes;
   size_t total_bytes;
 };
 
