@@ -10,6 +10,8 @@ Prints one JSON line. `value` is whole-step throughput (prefill tokens + decode 
 second); per-call figures, roofline fractions and the oracle's CPU rate are attached.
 """
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -44,15 +46,89 @@ def decode_alg_bytes(N, H, K, V, es):
     return N * H * (2 * 4 * K * V + es * (3 * K + V + 1) + es * V)
 
 
+# ---------------------------------------------------------------- measured HBM traffic
+# The counters come from two `rocprofv3 --pmc` runs of this script (FETCH_SIZE, then
+# WRITE_SIZE; KiB per dispatch). Each is scaled by what the same counter reads for a plain
+# elementwise kernel of known size (torch.neg over COPY_MIB MiB of fp32: reads and writes
+# exactly that many bytes), and the result is stored with a hash of the kernel sources; the
+# JSON line carries it only while the sources are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_long_prefill_and_decode.json")
+SOURCES = [os.path.join(ROOT, "gated_delta_rule_30_amd", "csrc", f)
+           for f in ("kda_chunk.hip", "kda_decode.hip", "kda_device.h", "kda_internal.h")]
+CHUNK_KERNELS = ("table_kernel", "segment_kernel", "prep_kernel", "state_kernel")
+DECODE_KERNEL = "decode_step_kernel"
+CALIB_KERNEL = "neg_kernel"
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _per_kernel(csv_path, counter):
+    rows = [r for r in csv.DictReader(open(csv_path)) if r["Counter_Name"] == counter]
+    out = []
+    for r in rows:
+        out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_mib, command):
+    """Per-call HBM bytes of kda_chunk_fwd and kda_decode_step from two counter runs."""
+    res = {"source_sha256": source_hash(), "command": command, "copy_mib": copy_mib}
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = _per_kernel(path, counter)
+        calib = [v for n, v in rows if CALIB_KERNEL in n]
+        if not calib:
+            raise SystemExit("no calibration kernel in " + path)
+        factor = copy_mib * 1024.0 / calib[-1]  # true KiB / counted KiB
+        calls = sum(1 for n, _ in rows if "table_kernel" in n)
+        chunk_kib = sum(v for n, v in rows if any(k in n for k in CHUNK_KERNELS))
+        dec = [v for n, v in rows if DECODE_KERNEL in n]
+        res[key] = {"factor": factor, "chunk_calls": calls,
+                    "chunk_bytes_per_call": chunk_kib * 1024.0 * factor / max(calls, 1),
+                    "decode_calls": len(dec),
+                    "decode_bytes_per_call": sum(dec) * 1024.0 * factor / max(len(dec), 1)}
+    res["chunk_bytes_per_call"] = res["fetch"]["chunk_bytes_per_call"] + res["write"]["chunk_bytes_per_call"]
+    res["decode_bytes_per_call"] = res["fetch"]["decode_bytes_per_call"] + res["write"]["decode_bytes_per_call"]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res))
+
+
+def measured_traffic():
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None, None
+    if t.get("source_sha256") != source_hash():
+        return None, None
+    return t.get("chunk_bytes_per_call"), t.get("decode_bytes_per_call")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=32768,
+    ap.add_argument("--cpu-sample-tokens", type=int, default=65536,
                     help="tokens (all 32 heads) of the prefill workload the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run torch.neg over this many MiB of fp32 (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the per-call HBM traffic record from two counter runs and exit")
+    ap.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_calibration_mib,
+                      args.pmc_command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures a single GPU: every (sequence, head) chain of the operator is "
@@ -96,6 +172,12 @@ def main():
         chunk_call()
         decode_call()
     torch.cuda.synchronize()
+    if args.copy_calibration_mib > 0:
+        x = torch.ones(args.copy_calibration_mib * (1 << 18), dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        del x, y
 
     # ---------------- timed region
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -138,12 +220,14 @@ def main():
         "tokens_per_s": Nd / decode_s,
         "alg_bytes": db,
     }
-    # dominant work of the step: the chunkwise forward (HBM-bound at K=V=128, bf16 I/O)
+    # dominant work of the step: the chunkwise forward (HBM-bound at K=V=128, bf16 I/O); one
+    # kda_chunk_fwd call is the launch unit (its kernels run back to back on one stream)
+    traffic_chunk, traffic_decode = measured_traffic()
     roofline = {"bound": "hbm", "achieved": cb / chunk_s / 1e9, "peak": PEAK_HBM / 1e9,
-                "unit": "GB/s", "frac": cb / chunk_s / PEAK_HBM, "traffic": None,
-                "kernel": "kda_chunk_fwd (prep + state kernels per segment)"}
+                "unit": "GB/s", "frac": cb / chunk_s / PEAK_HBM, "traffic": traffic_chunk,
+                "kernel": "kda_chunk_fwd call (table, segment, then prep + state kernel per segment)"}
     roofline_decode = {"bound": "hbm", "achieved": db / decode_s / 1e9, "peak": PEAK_HBM / 1e9,
-                       "unit": "GB/s", "frac": db / decode_s / PEAK_HBM, "traffic": None,
+                       "unit": "GB/s", "frac": db / decode_s / PEAK_HBM, "traffic": traffic_decode,
                        "kernel": "decode_step_kernel<128,128,bf16>"}
     value = (T + Nd) / (ms_per_step * 1e-3)
 

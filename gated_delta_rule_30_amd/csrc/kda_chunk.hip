@@ -21,7 +21,7 @@
 // workgroup per (sequence, head, V-slice) -- the columns of S evolve independently, so the
 // V split is exact -- and does only U = T'V, O = Q_eff S + P'V, Delta = U - W S and the
 // update S' = Diag(gamma) S + Ktilde^T Delta on the matrix cores. The sequence is processed
-// in segments of about SEG_CHUNK_HEADS records so the record buffers stay resident in the
+// in segments of about SEG_CHUNK_HEADS records so the record buffer stays resident in the
 // Infinity Cache between the two kernels.
 //
 // Numerics. Inside a chunk every decay factor is formed relative to a 16-token sub-block
@@ -30,8 +30,6 @@
 // the diagonal sub-block using e^{-(block decay)} >= 1 (the renormalisation the Technical
 // Breakdown asks for in section 4's numerical-stability note). The solve runs in fp32 on
 // VALU (diagonal 16x16 blocks) and fp32 MFMA (off-diagonal blocks). The state stays fp32.
-#include <mutex>
-
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -197,39 +195,49 @@ __global__ __launch_bounds__(256) void segment_kernel(const Entry* __restrict__ 
 }
 
 // ====================================================================== PREP kernel
+constexpr int PREP_THREADS = 256;
+
+// Sub-block pairs (I, J), J <= I, in the order (0,0) (1,0) (1,1) (2,0) ... (3,3).
+__host__ __device__ constexpr int pair_index(int I, int J) { return I * (I + 1) / 2 + J; }
+
+// Lane m of each 16-lane row reads lane m - SH of the same row; lanes below SH read 0.
+template <int SH>
+__device__ __forceinline__ float row_shr(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + SH, 0xf, 0xf, true));
+}
+
+// A fragment (EPL elements) from fp32 values.
+__device__ __forceinline__ bf16x8 to_frag(f32x4 lo, f32x4 hi, bf16) { return frag_from_acc(lo, hi, bf16()); }
+__device__ __forceinline__ f32x4 to_frag(f32x4 lo, f32x4, float) { return lo; }
+
+// LDS of one prep workgroup. Regions are reused across phases (each reuse follows a barrier
+// after which the earlier contents are dead); the total stays under half the CU's LDS at
+// K = 128 bf16 so that two workgroups share a CU.
 template <int K, typename MT>
 struct PrepLayout {
-  static constexpr int PADM = 16 / (int)sizeof(MT);
-  static constexpr int LK = K + PADM;        // MT rows of length K
+  static constexpr int PADM = 4;
   static constexpr int LC = CHUNK + PADM;    // MT rows of length CHUNK
-  static constexpr int LKF = K + 4;          // fp32 rows of length K
   static constexpr int LCF = CHUNK + 4;      // fp32 rows of length CHUNK
   static constexpr int NPAIR = NSUB * (NSUB + 1) / 2;
-  static constexpr size_t szQh = (size_t)CHUNK * LK * sizeof(MT);
-  static constexpr size_t szKh = szQh;
-  static constexpr size_t szKb = (size_t)CHUNK * LKF * 4;
-  static constexpr size_t szTri = (size_t)CHUNK * LC * sizeof(MT);
-  static constexpr size_t szX = (szKh + szKb) > 3 * szTri ? (szKh + szKb) : 3 * szTri;
-  static constexpr size_t szKaT = (size_t)K * LC * sizeof(MT);
-  static constexpr size_t szD = (size_t)NPAIR * K * 4;
-  static constexpr size_t szEx = (size_t)NSUB * K * 4;
-  static constexpr size_t szDel = (size_t)NSUB * K * 4;
-  static constexpr size_t szBeta = (size_t)CHUNK * 4;
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t szFrag = (size_t)CHUNK * K * sizeof(MT);  // [CHUNK][K] as fragments
+  static constexpr size_t szKT = (size_t)K * LC * sizeof(MT);       // [K][CHUNK]
+  static constexpr size_t szTri = (size_t)CHUNK * LC * sizeof(MT);  // [CHUNK][CHUNK]
   static constexpr size_t szAf = (size_t)CHUNK * LCF * 4;
-  static constexpr size_t szY = 2 * szAf > szKaT ? 2 * szAf : szKaT;
-  static constexpr size_t oQh = 0;
-  static constexpr size_t oX = oQh + szQh;
-  static constexpr size_t oKh = oX, oKb = oX + szKh;                             // phases 1-2
-  static constexpr size_t oTb = oX, oTbT = oX + szTri, oPn = oX + 2 * szTri;     // phases 4-6
-  static constexpr size_t oKaT = oX + szX;
-  static constexpr size_t oD = oKaT + szKaT;
-  static constexpr size_t oEx = oD + szD;
-  static constexpr size_t oDel = oEx + szEx;
-  static constexpr size_t oBeta = oDel + szDel;
-  static constexpr size_t oY = oBeta + szBeta;
-  static constexpr size_t oA = oY, oP = oY + szAf;                               // phases 2-4
-  static constexpr size_t oWT = oY;                                               // phases 5-6
-  static constexpr size_t total = oY + szY;
+  static constexpr size_t szTab = (size_t)(NSUB + NPAIR + NSUB) * K * 4;
+  // X: Q^ and K^ fragments (phases 1-2); T' and T'^T (phases 4-6)
+  static constexpr size_t szX = mx(2 * szFrag, 2 * szTri);
+  // R1: Ktilde^T staging (phase 1); A, then T (phases 2-4); W^T (phases 5-6)
+  static constexpr size_t szR1 = mx(szKT, szAf);
+  // P: block decays and per-channel factor tables (phases 1-2); -P (phases 2-6)
+  static constexpr size_t szP = mx(szTri, szTab);
+  static constexpr size_t oQh = 0, oKh = szFrag, oTb = 0, oTbT = szTri;
+  static constexpr size_t oR1 = szX;
+  static constexpr size_t oKaT = oR1 + szR1;  // Ka^T (phases 1-5)
+  static constexpr size_t oP = oKaT + szKT;
+  static constexpr size_t oEx = oP + szP;     // e^{e_{J-1}} per block and channel (phases 1-6)
+  static constexpr size_t oBeta = oEx + (size_t)NSUB * K * 4;
+  static constexpr size_t total = oBeta + (size_t)CHUNK * 4;
 };
 
 struct PrepParams {
@@ -243,28 +251,47 @@ struct PrepParams {
   int64_t rec_bytes;
 };
 
+// Record slot offset (elements) of the 4 consecutive reduction indices j0 .. j0+3 (j0 % 4 == 0)
+// of row r in a matrix with reduction length L.
+template <typename MT>
+__device__ __forceinline__ size_t slot4(int r, int j0, int L) {
+  constexpr int KS = Mma<MT>::KS;
+  const int jj = j0 % KS;
+  return slot_elem<MT>(r >> 4, j0 / KS, (r & 15) + 16 * ((jj & 15) >> 2), L) + 4 * (jj >> 4);
+}
+
+// One workgroup of 4 waves per (chunk, head); wave w owns sub-block w (tokens 16w .. 16w+15).
+// Lane (m, g) = (lane % 16, lane / 16) holds token 16w + m and the channels 16u + 4g .. +3,
+// u = 0 .. K/16-1, which is exactly that token's MFMA fragment over the channels. Phases are
+// separated by LDS-only barriers; record stores stay in flight.
 template <int K, typename MT>
-__global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
+__global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   using L = PrepLayout<K, MT>;
   using R = Rec<K, MT>;
+  using frag = typename Mma<MT>::frag;
   constexpr int KS = Mma<MT>::KS;
   constexpr int EPL = Mma<MT>::EPL;
+  constexpr int NG = K / 16;     // 4-channel groups per lane
+  constexpr int NS = K / KS;     // reduction steps over the channels
+  constexpr int GPS = KS / 16;   // groups per reduction step
+  constexpr int NKT = K / 16;
+  constexpr int NPAIR = L::NPAIR;
   static_assert(L::total <= 160 * 1024, "LDS budget");
   __shared__ __align__(16) char smem[L::total];
   MT* sQh = reinterpret_cast<MT*>(smem + L::oQh);
   MT* sKh = reinterpret_cast<MT*>(smem + L::oKh);
-  float* sKb = reinterpret_cast<float*>(smem + L::oKb);
   MT* sTb = reinterpret_cast<MT*>(smem + L::oTb);
   MT* sTbT = reinterpret_cast<MT*>(smem + L::oTbT);
-  MT* sPn = reinterpret_cast<MT*>(smem + L::oPn);
+  MT* sKtT = reinterpret_cast<MT*>(smem + L::oR1);
+  float* sA = reinterpret_cast<float*>(smem + L::oR1);
+  MT* sWT = reinterpret_cast<MT*>(smem + L::oR1);
   MT* sKaT = reinterpret_cast<MT*>(smem + L::oKaT);
-  float* sD = reinterpret_cast<float*>(smem + L::oD);
+  float* sDel = reinterpret_cast<float*>(smem + L::oP);
+  float* sD = sDel + NSUB * K;
+  float* sTail = sD + NPAIR * K;
+  MT* sPn = reinterpret_cast<MT*>(smem + L::oP);
   float* sEx = reinterpret_cast<float*>(smem + L::oEx);
-  float* sDel = reinterpret_cast<float*>(smem + L::oDel);
   float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
-  float* sA = reinterpret_cast<float*>(smem + L::oA);
-  float* sP = reinterpret_cast<float*>(smem + L::oP);
-  MT* sWT = reinterpret_cast<MT*>(smem + L::oWT);
 
   const int H = p.H;
   const int64_t j = blockIdx.x / H;
@@ -272,170 +299,188 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
   const int64_t e = p.seg_begin + j;
   if (j >= p.E || e >= (int64_t)p.header[0]) return;
   const Entry en = p.entries[e];
-  const int len = en.len;
+  const int len = en.len;  // 1 .. CHUNK
   const int64_t tok0 = en.tok;
   const MT* gq_ = reinterpret_cast<const MT*>(p.q);
   const MT* gk_ = reinterpret_cast<const MT*>(p.k);
   const MT* gg_ = reinterpret_cast<const MT*>(p.g);
   const MT* gb_ = reinterpret_cast<const MT*>(p.beta);
-  char* rec = p.rec + (j * H + h) * p.rec_bytes;
-  MT* recM = reinterpret_cast<MT*>(rec);
-  float* recGam = reinterpret_cast<float*>(rec + R::oGamBytes);
+  MT* recM = reinterpret_cast<MT*>(p.rec + (j * H + h) * p.rec_bytes);
+  float* recGam = reinterpret_cast<float*>(p.rec + (j * H + h) * p.rec_bytes + R::oGamBytes);
 
   const int tid = threadIdx.x;
   const int w = wave_id();
   const int lane = lane_id();
   const int m = lane & 15;
-  const int gq = lane >> 4;
-  const int64_t rowstride = (int64_t)H * K;  // elements between consecutive tokens
+  const int g = lane >> 4;
+  const int t = 16 * w + m;  // this lane's token in the chunk
+  const bool valid = t < len;
 
-  // ---------------- phase 1: wave w owns sub-block I = w (16 tokens). Lane (tg, cg) holds
-  // tokens 16I + 4tg .. +3 and channels CPL*cg .. +CPL-1, loaded with one vector load per token.
-  constexpr int CPL = K / 16;
-  using vin = VecN<MT, CPL>;
-  const int I = w;
-  const int tg = lane >> 4, cg = lane & 15;
-  const int c0 = CPL * cg;
-  float qv[4][CPL], kv[4][CPL], lv[4][CPL];
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    const int t = 16 * I + 4 * tg + jt;
-    if (t < len) {
-      const int64_t off = (tok0 + t) * rowstride + (int64_t)h * K + c0;
-      vin::load(gq_ + off, qv[jt]);
-      vin::load(gk_ + off, kv[jt]);
-      vin::load(gg_ + off, lv[jt]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) qv[jt][i] = kv[jt][i] = lv[jt][i] = 0.f;
-    }
-    if (cg == 0) sBeta[t] = t < len ? to_f32(gb_[(tok0 + t) * H + h]) : 0.f;
-  }
-  // in-block inclusive cumsum of log alpha: 4 tokens in-lane, then across the 4 token groups
-  // (all channels' shuffles issued together)
-  float tot[CPL], x[CPL], y[CPL], dI[CPL];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    float acc = 0.f;
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      acc += lv[jt][i];
-      lv[jt][i] = acc;
-    }
-    tot[i] = acc;
-    x[i] = acc;
-  }
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) y[i] = __shfl_up(x[i], 16);
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) x[i] += (tg >= 1) ? y[i] : 0.f;
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) y[i] = __shfl_up(x[i], 32);
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) x[i] += (tg >= 2) ? y[i] : 0.f;
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) dI[i] = __shfl(x[i], 48 + cg);  // log decay of the sub-block
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const float excl = x[i] - tot[i];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) lv[jt][i] += excl;
-  }
-  if (tg == 0) VecN<float, CPL>::store(sDel + I * K + c0, dI);
-  __syncthreads();
-  // chunk-level factors per channel, the D table and gamma
-  float Eprev[CPL], tailf[CPL];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = c0 + i;
-    float ecum[NSUB + 1];  // ecum[J+1] = e_J: log decay from the chunk start to the end of block J
-    ecum[0] = 0.f;
-#pragma unroll
-    for (int J = 0; J < NSUB; ++J) ecum[J + 1] = ecum[J] + sDel[J * K + c];
-    Eprev[i] = exp_f(ecum[I]);                     // e^{e_{I-1}}
-    tailf[i] = exp_f(ecum[NSUB] - ecum[I + 1]);    // e^{e_last - e_I}
-    if (tg == 0) {
-      sEx[I * K + c] = Eprev[i];
-      const int pbase = I * (I + 1) / 2;
-#pragma unroll
-      for (int J = 0; J < NSUB; ++J)
-        if (J <= I) sD[(pbase + J) * K + c] = (J < I) ? exp_f(ecum[I] - ecum[J + 1]) : exp_f(-dI[i]);
-      if (I == NSUB - 1) recGam[c] = exp_f(ecum[NSUB]);
-    }
-  }
-  // decayed operands of the four tokens
-  float ka[4][CPL], kt[4][CPL];
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    const int t = 16 * I + 4 * tg + jt;
-    float qr[CPL], kr[CPL], kc[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const float r = exp_f(lv[jt][i]);          // e^{b_t - e_{I-1}} <= 1
-      const float cc = exp_f(dI[i] - lv[jt][i]);  // e^{e_I - b_t} <= 1
-      qr[i] = qv[jt][i] * r;
-      kr[i] = kv[jt][i] * r;
-      kc[i] = kv[jt][i] * cc;
-      ka[jt][i] = kr[i] * Eprev[i];               // k e^{b_t}
-      kt[jt][i] = kc[i] * tailf[i];               // k e^{b_last - b_t}
-    }
-    vin::store(sQh + t * L::LK + c0, qr);
-    vin::store(sKh + t * L::LK + c0, kr);
-    VecN<float, CPL>::store(sKb + t * L::LKF + c0, kc);
-  }
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = c0 + i;
-    st4(sKaT + c * L::LC + 16 * I + 4 * tg, f32x4{ka[0][i], ka[1][i], ka[2][i], ka[3][i]});
-    // Ktilde^T: rows = channels, reduction = tokens; the 4 tokens form one quad of a slot
-    const int t0 = 16 * I + 4 * tg;
-    const int kp = t0 % KS;
-    st4(recM + R::oKt + slot_elem<MT>(c >> 4, t0 / KS, tg * 16 + (c & 15), CHUNK) + 4 * (kp >> 4),
-        f32x4{kt[0][i], kt[1][i], kt[2][i], kt[3][i]});
-  }
-  __syncthreads();
-
-  // ---------------- phase 2: A (strictly lower, row-scaled by beta) and P (lower) blocks
+  // ---------------- phase 1: the token's q, k, log alpha. Rows past the chunk's end load the
+  // last valid row again and are zeroed (q = k = 0, log alpha = 0, beta = 0 there), so every
+  // load is unconditional and all are in flight together.
+  float qv[NG][4], kv[NG][4], lv[NG][4];
   {
-    int pr = 0;
+    const int64_t row = (tok0 + min(t, len - 1)) * (int64_t)H * K + (int64_t)h * K + 4 * g;
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      VecN<MT, 4>::load(gq_ + row + 16 * u, qv[u]);
+      VecN<MT, 4>::load(gk_ + row + 16 * u, kv[u]);
+      VecN<MT, 4>::load(gg_ + row + 16 * u, lv[u]);
+    }
+  }
+  const float bval = to_f32(gb_[(tok0 + min(t, len - 1)) * H + h]);
+#pragma unroll
+  for (int u = 0; u < NG; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      qv[u][r] = valid ? qv[u][r] : 0.f;
+      kv[u][r] = valid ? kv[u][r] : 0.f;
+      lv[u][r] = valid ? lv[u][r] : 0.f;
+    }
+  if (g == 0) sBeta[t] = valid ? bval : 0.f;
+  // inclusive cumsum of log alpha over the 16 tokens of the sub-block (one 16-lane row):
+  // lv becomes b_t - e_{w-1}; dI = e_w - e_{w-1} is the row's last value
+  float dI[NG][4];
+#pragma unroll
+  for (int u = 0; u < NG; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = lv[u][r];
+      x += row_shr<1>(x);
+      x += row_shr<2>(x);
+      x += row_shr<4>(x);
+      x += row_shr<8>(x);
+      lv[u][r] = x;
+    }
+#pragma unroll
+  for (int u = 0; u < NG; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dI[u][r] = __shfl(lv[u][r], lane | 15);
+  if (m == 0) {
+#pragma unroll
+    for (int u = 0; u < NG; ++u)
+      *reinterpret_cast<f32x4*>(sDel + w * K + 16 * u + 4 * g) = f32x4{dI[u][0], dI[u][1], dI[u][2], dI[u][3]};
+  }
+  lds_barrier();
+  // per-channel factors, each computed once: e^{e_{J-1}} (sEx), gamma = e^{e_3} (record),
+  // D_{IJ} = e^{e_{I-1} - e_J} <= 1 for I > J and e^{e_{J-1} - e_J} for I = J (sD), and
+  // e^{e_3 - e_J} (sTail); e_J is the log decay from the chunk start to the end of block J
+  {
+    constexpr int NROLE = PREP_THREADS / K;
+    const int c = tid % K, role = tid / K;
+    float ec[NSUB + 1];
+    ec[0] = 0.f;
+#pragma unroll
+    for (int J = 0; J < NSUB; ++J) ec[J + 1] = ec[J] + sDel[J * K + c];
+#pragma unroll
+    for (int v = 0; v < 2 * NSUB + 1 + NPAIR; ++v) {
+      if (v % NROLE != role) continue;
+      if (v < NSUB) {
+        sEx[v * K + c] = exp_f(ec[v]);
+      } else if (v == NSUB) {
+        recGam[c] = exp_f(ec[NSUB]);
+      } else if (v < NSUB + 1 + NPAIR) {
+        const int pi = v - NSUB - 1;
+        const int I = (pi >= 1) + (pi >= 3) + (pi >= 6);
+        const int J = pi - I * (I + 1) / 2;
+        sD[pi * K + c] = exp_f((I == J ? ec[J] : ec[I]) - ec[J + 1]);
+      } else {
+        const int J = v - NSUB - 1 - NPAIR;
+        sTail[J * K + c] = exp_f(ec[NSUB] - ec[J + 1]);
+      }
+    }
+  }
+  lds_barrier();
+  // decayed operands of the lane's token:
+  //   Q^ = q e^{b_t - e_{w-1}}, K^ = k e^{b_t - e_{w-1}}  (<= 1 factors, MFMA row operands)
+  //   kc = k e^{e_w - b_t}                                (<= 1, column operand, registers)
+  //   qe = q e^{b_t}  (registers, for Q_eff),  Ka = k e^{b_t},  Kt = k e^{b_last - b_t}
+  float qe[NG][4], kc[NG][4];
+  {
+    f32x4 qh[NG], kh[NG];
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const f32x4 ex = *reinterpret_cast<const f32x4*>(sEx + w * K + 16 * u + 4 * g);
+      const f32x4 tl = *reinterpret_cast<const f32x4*>(sTail + w * K + 16 * u + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float rr = exp_f(lv[u][r]);
+        const float cc = exp_f(dI[u][r] - lv[u][r]);
+        qh[u][r] = qv[u][r] * rr;
+        kh[u][r] = kv[u][r] * rr;
+        kc[u][r] = kv[u][r] * cc;
+        qe[u][r] = qh[u][r] * ex[r];
+        const int c = 16 * u + 4 * g + r;
+        sKaT[c * L::LC + t] = from_f32<MT>(kh[u][r] * ex[r]);
+        sKtT[c * L::LC + t] = from_f32<MT>(kc[u][r] * tl[r]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const size_t slot = ((size_t)(w * NS + s) * 64 + lane) * EPL;
+      *reinterpret_cast<frag*>(sQh + slot) = to_frag(qh[GPS * s], qh[GPS * s + GPS - 1], MT());
+      *reinterpret_cast<frag*>(sKh + slot) = to_frag(kh[GPS * s], kh[GPS * s + GPS - 1], MT());
+    }
+  }
+  lds_barrier();
+  // Ktilde^T (rows = channels, reduction = tokens) to the record as fragment slots
+  {
+    constexpr int NSL = NKT * (CHUNK / KS) * 64;
+    static_assert(NSL % PREP_THREADS == 0, "slot split");
+#pragma unroll
+    for (int i = 0; i < NSL / PREP_THREADS; ++i) {
+      const int sl = tid + PREP_THREADS * i;
+      const int ln = sl & 63, ts = sl >> 6;
+      const int s = ts % (CHUNK / KS), tile = ts / (CHUNK / KS);
+      *reinterpret_cast<frag*>(recM + R::oKt + (size_t)sl * EPL) =
+          load_frag(sKtT + (16 * tile + (ln & 15)) * L::LC, s, ln >> 4);
+    }
+  }
+
+  // ---------------- phase 2: blocks (I, w), I >= w, of A and P. The column operand (token
+  // block w, scaled per channel by D_{Iw}) is this wave's own kc; the row operands are read as
+  // fragments. Results stay in registers until every wave is done with Q^, K^ and D.
+  f32x4 tA[NSUB], tP[NSUB];
+#pragma unroll
+  for (int I = 0; I < NSUB; ++I) {
+    tA[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+    tP[I] = tA[I];
+    if (I < w) continue;
+    const float* drow = sD + pair_index(I, w) * K + 4 * g;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(drow + KS * s);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(drow + KS * s + 16 * (GPS - 1));
+      f32x4 c0, c1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        c0[r] = kc[GPS * s][r] * d0[r];
+        c1[r] = kc[GPS * s + GPS - 1][r] * d1[r];
+      }
+      const frag bfr = to_frag(c0, c1, MT());
+      const size_t slot = ((size_t)(I * NS + s) * 64 + lane) * EPL;
+      tA[I] = Mma<MT>::mma(*reinterpret_cast<const frag*>(sKh + slot), bfr, tA[I]);
+      tP[I] = Mma<MT>::mma(*reinterpret_cast<const frag*>(sQh + slot), bfr, tP[I]);
+    }
+  }
+  lds_barrier();
+  // A (row-scaled by beta, strictly lower) -> sA; -P (lower, upper blocks zero) -> sPn
+  {
+    const int jj = 16 * w + m;
 #pragma unroll
     for (int I = 0; I < NSUB; ++I) {
 #pragma unroll
-      for (int J = 0; J <= I; ++J, ++pr) {
-        if ((pr & 3) != w) continue;
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < K / KS; ++s) {
-          auto ak = load_frag(sKh + (16 * I + m) * L::LK, s, gq);
-          auto aq = load_frag(sQh + (16 * I + m) * L::LK, s, gq);
-          auto b = load_frag_scaled(sKb + (16 * J + m) * L::LKF, sD + pr * K, s, gq, MT());
-          accA = Mma<MT>::mma(ak, b, accA);
-          accP = Mma<MT>::mma(aq, b, accP);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * I + 4 * gq + r, jj = 16 * J + m;
-          float a = accA[r] * sBeta[i];
-          float pv = accP[r];
-          if (I == J) {
-            if (jj >= i) a = 0.f;
-            if (jj > i) pv = 0.f;
-          }
-          sA[i * L::LCF + jj] = a;
-          sP[i * L::LCF + jj] = pv;
-        }
-      }
-    }
-    // upper blocks (J > I) of P are zero; those of A are never read
-    for (int idx = tid; idx < NSUB * NSUB * 256; idx += NTHREADS) {
-      const int blk = idx >> 8, I = blk / NSUB, J = blk % NSUB;
-      if (J > I) {
-        const int i = 16 * I + ((idx >> 4) & 15), jj = 16 * J + (idx & 15);
-        sP[i * L::LCF + jj] = 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * g + r;
+        const bool lowA = I > w || (I == w && jj < i);
+        const bool lowP = I > w || (I == w && jj <= i);
+        if (I >= w) sA[i * L::LCF + jj] = lowA ? tA[I][r] * sBeta[i] : 0.f;
+        sPn[i * L::LC + jj] = from_f32<MT>(lowP ? -tP[I][r] : 0.f);
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---------------- phase 3: T = (I + A)^{-1}
   // (a) Diagonal 16x16 blocks, one per wave, by forward substitution. Lane c keeps column c of
@@ -444,28 +489,29 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
     float* Ab = sA + (16 * w) * L::LCF + 16 * w;
     const f32x4 arow = *reinterpret_cast<const f32x4*>(Ab + (lane >> 2) * L::LCF + 4 * (lane & 3));
     const int c = lane & 15;
-    float t[SUBBLK];
+    float tt[SUBBLK];
 #pragma unroll
     for (int i = 0; i < SUBBLK; ++i) {
-      float x = (i == c) ? 1.f : 0.f;
+      float x0 = (i == c) ? 1.f : 0.f, x1 = 0.f;
 #pragma unroll
       for (int jj = 0; jj < i; ++jj) {
         const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(arow[jj & 3]), 4 * i + (jj >> 2)));
-        x -= a * t[jj];
+        if (jj & 1) x1 -= a * tt[jj];
+        else x0 -= a * tt[jj];
       }
-      t[i] = x;
+      tt[i] = x0 + x1;
     }
     if (lane < 16) {
 #pragma unroll
-      for (int i = 0; i < SUBBLK; ++i) Ab[i * L::LCF + c] = t[i];
+      for (int i = 0; i < SUBBLK; ++i) Ab[i * L::LCF + c] = tt[i];
     }
   }
-  __syncthreads();
+  lds_barrier();
   // (b) Off-diagonal blocks of row block I = w, right to left, with no further barrier:
   //     T_IJ = -(sum_{M=J+1}^{I} T_IM A_MJ) T_JJ, computed transposed so that every operand
   //     is a column read, a row read or the previous result tile. T_IJ (I > J) is stored
   //     row-major in the unused upper block (J, I) of sA.
-  {
+  if (w >= 1) {
     const int Ib = w;
     auto tblock = [&](int I, int M) -> float* {  // base of T_IM (I >= M)
       return (I == M) ? sA + (16 * I) * L::LCF + 16 * I : sA + (16 * M) * L::LCF + 16 * I;
@@ -475,95 +521,83 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
       for (int M = J + 1; M <= Ib; ++M) {
         f32x4 af;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) af[r] = sA[(16 * M + 4 * gq + r) * L::LCF + 16 * J + m];
-        const f32x4 bf = *reinterpret_cast<const f32x4*>(tblock(Ib, M) + m * L::LCF + 4 * gq);
+        for (int r = 0; r < 4; ++r) af[r] = sA[(16 * M + 4 * g + r) * L::LCF + 16 * J + m];
+        const f32x4 bf = *reinterpret_cast<const f32x4*>(tblock(Ib, M) + m * L::LCF + 4 * g);
         X = Mma<float>::mma(af, bf, X);
       }
       f32x4 tjj;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tjj[r] = sA[(16 * J + 4 * gq + r) * L::LCF + 16 * J + m];
+      for (int r = 0; r < 4; ++r) tjj[r] = sA[(16 * J + 4 * g + r) * L::LCF + 16 * J + m];
       const f32x4 Y = Mma<float>::mma(tjj, X, f32x4{0.f, 0.f, 0.f, 0.f});  // (T_IJ)^T
-      *reinterpret_cast<f32x4*>(tblock(Ib, J) + m * L::LCF + 4 * gq) = -Y;
+      *reinterpret_cast<f32x4*>(tblock(Ib, J) + m * L::LCF + 4 * g) = -Y;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---------------- phase 4: T' = T diag(beta) (and its transpose), -P, all in MT
-  for (int idx = tid; idx < CHUNK * CHUNK / 4; idx += NTHREADS) {
+  // ---------------- phase 4: T' = T diag(beta) -> LDS (row-major and transposed) and record
+#pragma unroll
+  for (int it = 0; it < CHUNK * CHUNK / 4 / PREP_THREADS; ++it) {
+    const int idx = tid + PREP_THREADS * it;
     const int i = idx / (CHUNK / 4), j0 = 4 * (idx % (CHUNK / 4));
     const int Ii = i >> 4, Jj = j0 >> 4;
-    f32x4 tv = {0.f, 0.f, 0.f, 0.f};
-    if (Ii == Jj) tv = *reinterpret_cast<const f32x4*>(sA + i * L::LCF + j0);
-    else if (Ii > Jj) tv = *reinterpret_cast<const f32x4*>(sA + (16 * Jj + (i & 15)) * L::LCF + 16 * Ii + (j0 & 15));
+    const int src = (Ii == Jj) ? i * L::LCF + j0 : (16 * Jj + (i & 15)) * L::LCF + 16 * Ii + (j0 & 15);
+    f32x4 tv = *reinterpret_cast<const f32x4*>(sA + src);
     tv *= *reinterpret_cast<const f32x4*>(sBeta + j0);
+    if (Ii < Jj) tv = f32x4{0.f, 0.f, 0.f, 0.f};
     st4(sTb + i * L::LC + j0, tv);
 #pragma unroll
     for (int k = 0; k < 4; ++k) sTbT[(j0 + k) * L::LC + i] = from_f32<MT>(tv[k]);
-    st4(sPn + i * L::LC + j0, -*reinterpret_cast<const f32x4*>(sP + i * L::LCF + j0));
+    st4(recM + R::oTb + slot4<MT>(i, j0, CHUNK), tv);
   }
-  __syncthreads();
-  // T' to the record
-  {
-    constexpr int NSL = (CHUNK / 16) * (CHUNK / KS) * 64;
-    for (int sl = tid; sl < NSL; sl += NTHREADS) {
-      const int ln = sl & 63, ts = sl >> 6;
-      const int s = ts % (CHUNK / KS), tile = ts / (CHUNK / KS);
-      const auto f = load_frag(sTb + (16 * tile + (ln & 15)) * L::LC, s, ln >> 4);
-      *reinterpret_cast<typename Mma<MT>::frag*>(recM + R::oTb + (size_t)sl * EPL) = f;
-    }
-  }
+  lds_barrier();
 
-  // ---------------- phase 5: W^T = Ka^T T'^T  -> record (as W fragments) and LDS (W^T)
+  // ---------------- phase 5: W^T = Ka^T T'^T -> record (as W fragments) and LDS (W^T)
 #pragma unroll
-  for (int a = w; a < K / 16; a += 4) {
-#pragma unroll
-    for (int b = 0; b < NSUB; ++b) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int nsteps = (16 * b + 16 + KS - 1) / KS;
-      for (int s = 0; s < nsteps; ++s) {
-        const auto af = load_frag(sKaT + (16 * a + m) * L::LC, s, gq);
-        const auto bfr = load_frag(sTb + (16 * b + m) * L::LC, s, gq);
-        acc = Mma<MT>::mma(af, bfr, acc);
-      }
-      st4(recM + R::oW + slot_elem<MT>(b, (16 * a) / KS, lane, K) + 4 * ((16 * a % KS) / 16), acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sWT[(16 * a + 4 * gq + r) * L::LC + 16 * b + m] = from_f32<MT>(acc[r]);
-    }
-  }
-  __syncthreads();
-
-  // ---------------- phase 6a: Q_eff^T = (Q e^{b})^T + W^T (-P)^T -> record (as Q_eff fragments)
-#pragma unroll
-  for (int a = w; a < K / 16; a += 4) {
-#pragma unroll
-    for (int b = 0; b < NSUB; ++b) {
-      const int i = 16 * b + m;
-      const f32x4 qh = ld4f(sQh + i * L::LK + 16 * a + 4 * gq);
-      const f32x4 ex = *reinterpret_cast<const f32x4*>(sEx + b * K + 16 * a + 4 * gq);
-      f32x4 acc = qh * ex;
-      const int nsteps = (16 * b + 16 + KS - 1) / KS;
-      for (int s = 0; s < nsteps; ++s) {
-        const auto af = load_frag(sWT + (16 * a + m) * L::LC, s, gq);
-        const auto bfr = load_frag(sPn + (16 * b + m) * L::LC, s, gq);
-        acc = Mma<MT>::mma(af, bfr, acc);
-      }
-      st4(recM + R::oQ + slot_elem<MT>(b, (16 * a) / KS, lane, K) + 4 * ((16 * a % KS) / 16), acc);
-    }
-  }
-  // ---------------- phase 6b: P'^T = -(T'^T (-P)^T) -> record (as P' fragments)
-  for (int tix = w; tix < NSUB * NSUB; tix += 4) {
-    const int a = tix % NSUB, b = tix / NSUB;  // a: column tile (j), b: row tile (i)
+  for (int tix = 0; tix < NKT * NSUB; ++tix) {
+    const int a = tix % NKT, b = tix / NKT;
+    if (tix % 4 != w) continue;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (a <= b) {
+    const int nsteps = (16 * b + 16 + KS - 1) / KS;
+#pragma unroll
+    for (int s = 0; s < CHUNK / KS; ++s)
+      if (s < nsteps)
+        acc = Mma<MT>::mma(load_frag(sKaT + (16 * a + m) * L::LC, s, g),
+                           load_frag(sTb + (16 * b + m) * L::LC, s, g), acc);
+    st4(recM + R::oW + slot4<MT>(16 * b + m, 16 * a + 4 * g, K), acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sWT[(16 * a + 4 * g + r) * L::LC + 16 * b + m] = from_f32<MT>(acc[r]);
+  }
+  lds_barrier();
+
+  // ---------------- phase 6a: Q_eff^T = (Q e^{b})^T + W^T (-P)^T, column tile b = w. The
+  // accumulator starts from this lane's own q e^{b_t} (token 16w + m, channels 16a + 4g + r).
+  {
+    const int nsteps = (16 * w + 16 + KS - 1) / KS;
+#pragma unroll
+    for (int a = 0; a < NKT; ++a) {
+      f32x4 acc = {qe[a][0], qe[a][1], qe[a][2], qe[a][3]};
+#pragma unroll
+      for (int s = 0; s < CHUNK / KS; ++s)
+        if (s < nsteps)
+          acc = Mma<MT>::mma(load_frag(sWT + (16 * a + m) * L::LC, s, g),
+                             load_frag(sPn + (16 * w + m) * L::LC, s, g), acc);
+      st4(recM + R::oQ + slot4<MT>(16 * w + m, 16 * a + 4 * g, K), acc);
+    }
+  }
+  // ---------------- phase 6b: P'^T = -(T'^T (-P)^T) -> record (as P' fragments); column tile a = w
+#pragma unroll
+  for (int b = 0; b < NSUB; ++b) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (w <= b) {
       const int nsteps = (16 * b + 16 + KS - 1) / KS;
-      for (int s = 0; s < nsteps; ++s) {
-        const auto af = load_frag(sTbT + (16 * a + m) * L::LC, s, gq);
-        const auto bfr = load_frag(sPn + (16 * b + m) * L::LC, s, gq);
-        acc = Mma<MT>::mma(af, bfr, acc);
-      }
+#pragma unroll
+      for (int s = 0; s < CHUNK / KS; ++s)
+        if (s < nsteps)
+          acc = Mma<MT>::mma(load_frag(sTbT + (16 * w + m) * L::LC, s, g),
+                             load_frag(sPn + (16 * b + m) * L::LC, s, g), acc);
       acc = -acc;
     }
-    st4(recM + R::oPb + slot_elem<MT>(b, (16 * a) / KS, lane, CHUNK) + 4 * ((16 * a % KS) / 16), acc);
+    st4(recM + R::oPb + slot4<MT>(16 * b + m, 16 * w + 4 * g, CHUNK), acc);
   }
 }
 
@@ -572,17 +606,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams p) {
 // wave are outstanding (loads, LDS-DMA loads and stores alike), or until its LDS operations
 // have completed.
 #define KDA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-#define KDA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
-
-// Workgroup barrier for LDS data: waits for this wave's LDS accesses, not for its outstanding
-// global loads (so a prefetch stays in flight across it). The signal fences keep the compiler
-// from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  KDA_WAIT_LGKM0();
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // 16 bytes per lane from global memory straight into LDS: lane l of the wave writes
 // lds_wave_base + 16 * l (gfx950 global_load_lds_dwordx4).
@@ -897,41 +920,10 @@ bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan
   off += 2048;
   p->off_rec = off;
   p->rec_buf_bytes = (size_t)E * H * p->rec_bytes;
-  off += 2 * p->rec_buf_bytes;
+  off += p->rec_buf_bytes;
   p->total_bytes = off;
   return true;
 }
-
-// Per-device auxiliary stream and events, created once and kept for the life of the process:
-// the prep kernel of segment s+1 runs on the auxiliary stream while the state kernel of
-// segment s runs on the caller's stream. Both streams have the default priority.
-namespace {
-struct Aux {
-  bool ready = false;
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, prep_done[2] = {nullptr, nullptr}, state_done[2] = {nullptr, nullptr};
-};
-constexpr int kMaxDevices = 64;
-Aux g_aux[kMaxDevices];
-std::mutex g_aux_mutex;  // also serialises the enqueue sequence that uses the shared events
-
-Aux* get_aux(bool may_create) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  Aux& x = g_aux[dev];
-  if (x.ready) return &x;
-  if (!may_create) return nullptr;
-  if (hipStreamCreateWithFlags(&x.side, hipStreamNonBlocking) != hipSuccess) return nullptr;
-  bool ok = hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess;
-  for (int i = 0; i < 2 && ok; ++i) {
-    ok = hipEventCreateWithFlags(&x.prep_done[i], hipEventDisableTiming) == hipSuccess &&
-         hipEventCreateWithFlags(&x.state_done[i], hipEventDisableTiming) == hipSuccess;
-  }
-  if (!ok) return nullptr;
-  x.ready = true;
-  return &x;
-}
-}  // namespace
 
 template <int K, typename MT>
 static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
@@ -958,13 +950,13 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
   const dim3 sgrid((unsigned)(chains8 * pl.n_slices));
   const dim3 pgrid((unsigned)(pl.seg_entries * a.num_heads));
   auto prep = [&](int64_t s, hipStream_t q) {
-    char* rec = ws + pl.off_rec + (s & 1) * pl.rec_buf_bytes;
+    char* rec = ws + pl.off_rec;
     PrepParams pp{a.q, a.k, a.g, a.beta, entries, header, a.num_heads, s * pl.seg_entries,
                   pl.seg_entries, rec, pl.rec_bytes};
-    hipLaunchKernelGGL((prep_kernel<K, MT>), pgrid, dim3(NTHREADS), 0, q, pp);
+    hipLaunchKernelGGL((prep_kernel<K, MT>), pgrid, dim3(PREP_THREADS), 0, q, pp);
   };
   auto state = [&](int64_t s, hipStream_t q) -> bool {
-    const char* rec = ws + pl.off_rec + (s & 1) * pl.rec_buf_bytes;
+    const char* rec = ws + pl.off_rec;
     StateParams sp{a.v, a.o, a.init_state, run_state, entries, header, basetab,
                    seg_first + s * pl.slots, seg_count + s, s * pl.seg_entries, pl.seg_entries,
                    a.num_heads, a.dv, pl.n_slices, chains, rec, pl.rec_bytes,
@@ -974,30 +966,11 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
     return true;
   };
 
-  std::lock_guard<std::mutex> lock(g_aux_mutex);
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(st, &cap) != hipSuccess) cap = hipStreamCaptureStatusNone;
-  Aux* aux = pl.num_segs > 1 ? get_aux(cap == hipStreamCaptureStatusNone) : nullptr;
-  if (aux == nullptr) {  // one stream: prep(s), state(s), prep(s+1), ...
-    for (int64_t s = 0; s < pl.num_segs; ++s) {
-      prep(s, st);
-      if (!state(s, st)) return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-  }
-  // two streams: prep(s) on the auxiliary stream overlaps state(s-1) on the caller's stream;
-  // record buffer s&1 is reused only after state(s-2) has finished with it.
-  if (hipEventRecord(aux->fork, st) != hipSuccess) return hipErrorLaunchFailure;
-  if (hipStreamWaitEvent(aux->side, aux->fork, 0) != hipSuccess) return hipErrorLaunchFailure;
+  // Segments run in order on the caller's stream, each kernel with the whole device: the
+  // prep kernel fills the record buffer, then the state kernel consumes it.
   for (int64_t s = 0; s < pl.num_segs; ++s) {
-    const int b = (int)(s & 1);
-    if (s >= 2 && hipStreamWaitEvent(aux->side, aux->state_done[b], 0) != hipSuccess)
-      return hipErrorLaunchFailure;
-    prep(s, aux->side);
-    if (hipEventRecord(aux->prep_done[b], aux->side) != hipSuccess) return hipErrorLaunchFailure;
-    if (hipStreamWaitEvent(st, aux->prep_done[b], 0) != hipSuccess) return hipErrorLaunchFailure;
+    prep(s, st);
     if (!state(s, st)) return hipErrorInvalidValue;
-    if (hipEventRecord(aux->state_done[b], st) != hipSuccess) return hipErrorLaunchFailure;
   }
   return hipGetLastError();
 }

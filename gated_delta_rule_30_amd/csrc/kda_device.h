@@ -94,6 +94,15 @@ __device__ __forceinline__ bf16x8 frag_from_acc(f32x4 lo, f32x4 hi, bf16) {
                                  0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Workgroup barrier that orders LDS accesses only: the fences are workgroup-scope and limited
+// to the local address space, so the wait before s_barrier covers this wave's LDS operations
+// but not its outstanding global loads and stores, which stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 

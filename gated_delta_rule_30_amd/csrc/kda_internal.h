@@ -12,8 +12,8 @@ constexpr int SUBBLK = 16;    // sub-block edge = MFMA tile edge
 constexpr int NSUB = CHUNK / SUBBLK;
 constexpr int NTHREADS = 256;  // threads per workgroup of every chunk kernel
 
-// Target number of (chunk, head) records per segment: the two record buffers of a segment
-// pair then stay resident in the 256 MB Infinity Cache at K=V=128 bf16.
+// Target number of (chunk, head) records per segment: the segment's record buffer (66 KB per
+// record at K=V=128 bf16) then stays resident in the 256 MB Infinity Cache.
 constexpr int64_t SEG_CHUNK_HEADS = 1024;
 
 struct DecodeArgs {
