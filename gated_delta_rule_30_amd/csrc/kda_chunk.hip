@@ -30,6 +30,8 @@
 // the diagonal sub-block using e^{-(block decay)} >= 1 (the renormalisation the Technical
 // Breakdown asks for in section 4's numerical-stability note). The solve runs in fp32 on
 // VALU (diagonal 16x16 blocks) and fp32 MFMA (off-diagonal blocks). The state stays fp32.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -85,6 +87,15 @@ struct VecN {
   }
 };
 
+// Compile-time loop: f(std::integral_constant<int, I>()) for I = B .. E-1, in order.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    static_for<B + 1, E>(f);
+  }
+}
+
 // ====================================================================== chunk table
 // Entries are ordered depth-major (chunk d of every sequence that has one, then chunk d+1),
 // so one segment advances many sequences at once and short sequences drop out early. Within a
@@ -108,10 +119,8 @@ __global__ __launch_bounds__(256) void table_kernel(SeqView sv, int H, int64_t K
                                                     float* __restrict__ fin,
                                                     Entry* __restrict__ entries,
                                                     int32_t* __restrict__ header,
-                                                    int32_t* __restrict__ basetab,
-                                                    float* __restrict__ zeros) {
+                                                    int32_t* __restrict__ basetab) {
   const int n = blockIdx.x;
-  if (n == 0) zeros[threadIdx.x] = 0.f;  // 1 KB zero block read by the state kernel
   const int64_t len = sv.len(n);
   const int64_t nc = sv.nchunks(n);
   // rank of n: sequences with more chunks, or as many and a smaller index, come first
@@ -602,38 +611,55 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
 }
 
 // ====================================================================== STATE kernel
-// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory operations of this
-// wave are outstanding (loads, LDS-DMA loads and stores alike), or until its LDS operations
-// have completed.
-#define KDA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-
-// 16 bytes per lane from global memory straight into LDS: lane l of the wave writes
-// lds_wave_base + 16 * l (gfx950 global_load_lds_dwordx4).
-__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
-
+// One workgroup of 4 waves per (sequence run, head, V-slice of VS = 16*NVT columns). The state
+// GEMMs are computed transposed, with the chunk record as the B operand:
+//   U^T = V^T T'^T,  (P'V)^T = V^T P'^T,  (W S)^T = S^T W^T,  (Q_eff S)^T = S^T Q_eff^T,
+//   S'^T = S^T Diag(gamma) + Delta^T Ktilde
+// so the record's fragment slots feed the matrix cores as loaded, and a result tile holds four
+// consecutive V columns of one token (output, Delta) or of one key channel (state) per lane.
+// Wave w owns token tile w (U, P'V, W S, Q_eff S, Delta, O for every column tile) and
+// key-channel tiles w, w+4 of the state update, so each record byte is loaded once per
+// workgroup, straight into registers, one chunk ahead of its use.
+//
+// S, V and Delta sit in LDS row-major (rows = key channel or token, VS columns), written with
+// 8- and 16-byte stores straight from the result layout; the A fragments of S^T, V^T and
+// Delta^T are read back with the transposing LDS read (bf16) or four scalar reads (fp32).
 template <int K, int NVT, typename MT>
 struct StateLayout {
   static constexpr int VS = 16 * NVT;
-  static constexpr int PADM = 16 / (int)sizeof(MT);
-  static constexpr int LKs = K + PADM;
-  static constexpr int LCs = CHUNK + PADM;
-  static constexpr size_t RB = Rec<K, MT>::bytes;                 // one chunk record
-  static constexpr size_t VSB = (size_t)CHUNK * VS * sizeof(MT);  // one chunk of the V slice
-  static constexpr size_t FIX = (size_t)VS * LKs * sizeof(MT) + (size_t)VS * LCs * sizeof(MT) +
-                                (SEG_CHUNK_HEADS + 16) * 4;
-  static constexpr int NBUF = (2 * (RB + VSB) + FIX <= 160 * 1024) ? 2 : 1;
-  static constexpr size_t oRec = 0;                                // [NBUF] records
-  static constexpr size_t oVst = oRec + NBUF * RB;                 // [NBUF][CHUNK][VS] token-major
-  static constexpr size_t oS = oVst + NBUF * VSB;                  // S^T: [VS][K]
-  static constexpr size_t oDl = oS + (size_t)VS * LKs * sizeof(MT);  // Delta^T: [VS][CHUNK]
-  static constexpr size_t oRun = oDl + (size_t)VS * LCs * sizeof(MT);
+  static constexpr int LD = VS + 16 / (int)sizeof(MT);  // row length in elements (16-byte aligned rows)
+  static constexpr size_t oS = 0;                                      // S: [K][VS]
+  static constexpr size_t oV = oS + (size_t)K * LD * sizeof(MT);       // V: [CHUNK][VS]
+  static constexpr size_t oD = oV + (size_t)CHUNK * LD * sizeof(MT);   // Delta: [CHUNK][VS]
+  static constexpr size_t oRun = oD + (size_t)CHUNK * LD * sizeof(MT);
   static constexpr size_t total = oRun + (SEG_CHUNK_HEADS + 16) * 4;
-  static_assert(total <= 160 * 1024, "state LDS budget");
-  static_assert(RB % 1024 == 0 && VSB % 1024 == 0, "DMA slots");
+  static_assert((LD * sizeof(MT)) % 16 == 0, "row alignment");
 };
+
+// A fragment (reduction step s) of X^T for the 16 rows c0 .. c0+15 of X^T, where X is stored
+// row-major with ld elements per row and rows = reduction index: lane (m, g) receives
+// X[KS*s + kk(g, e)][c0 + m]. ds_read_b64_tr_b16 works per group of 16 lanes: lane 4p + r of
+// the group receives element r of the 8 bytes addressed by lanes 4e + p (e = 0..3). So lane
+// (m, g) supplies the address of row 4g + m/4, columns c0 + 4(m%4) .. +3, and receives rows
+// 4g .. 4g+3 of column c0 + m.
+__device__ __forceinline__ bf16x4 ds_read_tr4(const bf16* p) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
+  const v4bf v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) v4bf*)(__attribute__((address_space(3))) void*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x8 frag_t(const bf16* X, int ld, int c0, int s, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+  const bf16* p = X + (32 * s + 4 * g + (m >> 2)) * ld + c0 + 4 * (m & 3);
+  const bf16x4 lo = ds_read_tr4(p);
+  const bf16x4 hi = ds_read_tr4(p + 16 * ld);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 frag_t(const float* X, int ld, int c0, int s, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+  const float* p = X + (16 * s + 4 * g) * ld + c0 + m;
+  return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
 
 struct StateParams {
   const void* v;
@@ -650,46 +676,42 @@ struct StateParams {
   int64_t chains;  // slots * H
   const char* rec;
   int64_t rec_bytes;
-  const char* zeros;  // >= 1 KB of zeros (V rows past a chunk's end are loaded from here)
-  char* trash;        // >= 1 KB sink for output rows past a chunk's end
+  char* trash;  // >= 1 KB sink for output rows past a chunk's end
 };
 
-// Work split of one state workgroup: 8 waves over a V-slice of VS = 16*NVT columns.
-// Wave w computes the result tiles of token tile w % 4 for CT column tiles starting at
-// (w / 4) * CT (U, P'V, W S, Q_eff S, Delta, O), and the state update of row tiles w, w+8, ...
+constexpr int STATE_THREADS = 256;
+
+// What one wave loads for one chunk.
 template <int K, int NVT, typename MT>
-struct StateWork {
-  static constexpr int NW = 8;
-  static constexpr int NT = NW * 64;
-  static constexpr int WPT = NW / 4;                // waves per token tile
-  static constexpr int CT = NVT / WPT;              // column tiles per wave
-  static constexpr int NKT = K / 16;                // row tiles of S
-  static constexpr int TPW = (NKT + NW - 1) / NW;   // S row tiles per wave
-  static_assert(CT >= 1 && NVT % WPT == 0, "state work split");
+struct StateBundle {
+  using frag = typename Mma<MT>::frag;
+  static constexpr int KS = Mma<MT>::KS;
+  static constexpr int NKT = K / 16;
+  static constexpr int TPW = (NKT + 3) / 4;  // key-channel tiles per wave
+  static constexpr int VE = 4 * NVT;         // V elements per lane: one token, VE columns
+  frag tf[CHUNK / KS], pf[CHUNK / KS], wf[K / KS], qf[K / KS], kf[TPW][CHUNK / KS];
+  float gam[TPW];
+  typename VecN<MT, VE>::vec v;
 };
 
 template <int K, int NVT, typename MT>
-__global__ __launch_bounds__(512) void state_kernel(StateParams p) {
+__global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_kernel(StateParams p) {
   using SL = StateLayout<K, NVT, MT>;
   using R = Rec<K, MT>;
-  using WK = StateWork<K, NVT, MT>;
+  using B = StateBundle<K, NVT, MT>;
   using frag = typename Mma<MT>::frag;
+  using vvec = typename VecN<MT, B::VE>::vec;
   constexpr int KS = Mma<MT>::KS;
   constexpr int VS = SL::VS;
-  constexpr int NW = WK::NW;
-  constexpr int NT = WK::NT;
-  constexpr int CT = WK::CT;
-  constexpr int NKT = WK::NKT;
-  constexpr int TPW = WK::TPW;
-  constexpr int NBUF = SL::NBUF;
-  constexpr int NSR = (int)(SL::RB / 1024);        // DMA slots of a record
-  constexpr int NSV = (int)(SL::VSB / 1024);       // DMA slots of a V chunk
-  constexpr int LPT = VS * (int)sizeof(MT) / 16;   // lanes per token row in a V slot
-  constexpr int TPS = 64 / LPT;                    // token rows per V slot
-  constexpr int NST = 4 * CT;                      // output stores per lane per chunk
+  constexpr int LD = SL::LD;
+  constexpr int NKT = B::NKT;
+  constexpr int TPW = B::TPW;
+  constexpr int VE = B::VE;
+  static_assert(SL::total <= 64 * 1024, "state LDS budget");
   __shared__ __align__(16) char smem[SL::total];
-  MT* sS = reinterpret_cast<MT*>(smem + SL::oS);    // S^T: [VS][K]
-  MT* sDl = reinterpret_cast<MT*>(smem + SL::oDl);  // Delta^T: [VS][CHUNK]
+  MT* sS = reinterpret_cast<MT*>(smem + SL::oS);
+  MT* sV = reinterpret_cast<MT*>(smem + SL::oV);
+  MT* sD = reinterpret_cast<MT*>(smem + SL::oD);
   int32_t* sRun = reinterpret_cast<int32_t*>(smem + SL::oRun);
   int32_t* sLen = sRun + SEG_CHUNK_HEADS;
 
@@ -713,9 +735,7 @@ __global__ __launch_bounds__(512) void state_kernel(StateParams p) {
   const int w = wave_id();
   const int lane = lane_id();
   const int m = lane & 15;
-  const int gq = lane >> 4;
-  const int tw = w & 3;             // token tile of this wave's result tiles
-  const int ct0 = (w >> 2) * CT;    // first column tile of this wave's result tiles
+  const int g = lane >> 4;
 
   // This workgroup's run: chunks d0, d0+1, ... of sequence en.seq inside the segment. Chunk
   // d0+k is entry base[d0+k] + rank; the run ends at the sequence's end or the segment's end.
@@ -725,161 +745,222 @@ __global__ __launch_bounds__(512) void state_kernel(StateParams p) {
   const int kmax = (int)min((int64_t)(nc - en.depth), p.E);
   if (tid == 0) sLen[0] = kmax;
   __syncthreads();
-  for (int k = tid; k < kmax; k += NT) {
+  for (int k = tid; k < kmax; k += STATE_THREADS) {
     const int64_t ek = p.basetab[en.depth + k] + rank;
-    sRun[k] = (int32_t)ek;
+    sRun[k] = (int32_t)(ek - p.seg_begin);
     if (ek >= seg_end) atomicMin(&sLen[0], k);
   }
 
+  // State tiles (nt, kt = w + 4 tt): lane (m, g) holds S[16kt + m][16nt + 4g .. +3] of the slice.
   const size_t sbase = ((size_t)en.seq * H + h) * (size_t)K * V + col0;
   const float* src = (en.depth == 0) ? p.init_state : p.state;
   f32x4 Sr[TPW][NVT];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
-    const int t = w + NW * tt;
+    const int kt = w + 4 * tt;
 #pragma unroll
     for (int nt = 0; nt < NVT; ++nt) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (t < NKT && src != nullptr) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = src[sbase + (size_t)(16 * t + 4 * gq + r) * V + 16 * nt + m];
-      }
+      if (kt < NKT && src != nullptr)
+        x = *reinterpret_cast<const f32x4*>(src + sbase + (size_t)(16 * kt + m) * V + 16 * nt + 4 * g);
       Sr[tt][nt] = x;
-      if (t < NKT) st4(sS + (16 * nt + m) * SL::LKs + 16 * t + 4 * gq, x);
+      if (kt < NKT) st4(sS + (16 * kt + m) * LD + 16 * nt + 4 * g, x);
     }
   }
   __syncthreads();
   const int run = sLen[0];
 
-  const char* gv = reinterpret_cast<const char*>(reinterpret_cast<const MT*>(p.v) + (int64_t)h * V + col0);
+  const MT* gv = reinterpret_cast<const MT*>(p.v) + (int64_t)h * V + col0;
   MT* go = reinterpret_cast<MT*>(p.o) + (int64_t)h * V + col0;
+  MT* trash = reinterpret_cast<MT*>(p.trash) + 4 * lane;
   const int64_t vrow = (int64_t)H * V;
-  const int nst_tri = (16 * tw + 16 + KS - 1) / KS;  // reduction steps of T', P' for tile tw
+  const char* rec_h = p.rec + (int64_t)h * p.rec_bytes;
+  const int64_t rec_stride = (int64_t)H * p.rec_bytes;
   auto tok_of = [&](int k) { return seq_start + CHUNK * (en.depth + k); };
   auto len_of = [&](int k) { return min(CHUNK, en.end - tok_of(k)); };
 
-  // DMA of chunk k (clamped to the run's last chunk) into buffer b: the record slots and the
-  // V slice (token-major; rows past the chunk's length come from the zero block).
-  auto issue = [&](int k, int b) {
+  // Loop-invariant per-lane byte offsets inside a record; a chunk's loads then use one
+  // wave-uniform base address plus these offsets (reduction steps are 1 KB apart).
+  constexpr uint32_t STEP = 64 * 16;
+  const uint32_t lo_t = (uint32_t)((R::oTb + slot_elem<MT>(w, 0, lane, CHUNK)) * sizeof(MT));
+  const uint32_t lo_p = (uint32_t)((R::oPb + slot_elem<MT>(w, 0, lane, CHUNK)) * sizeof(MT));
+  const uint32_t lo_w = (uint32_t)((R::oW + slot_elem<MT>(w, 0, lane, K)) * sizeof(MT));
+  const uint32_t lo_q = (uint32_t)((R::oQ + slot_elem<MT>(w, 0, lane, K)) * sizeof(MT));
+  uint32_t lo_k[TPW], lo_g[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int kt = min(w + 4 * tt, NKT - 1);
+    lo_k[tt] = (uint32_t)((R::oKt + slot_elem<MT>(kt, 0, lane, CHUNK)) * sizeof(MT));
+    lo_g[tt] = (uint32_t)(R::oGamBytes + (16 * kt + m) * 4);
+  }
+  auto ldf = [](const char* base, uint32_t off) -> frag { return *reinterpret_cast<const frag*>(base + off); };
+
+  // Loads of chunk k (clamped to the run's last chunk; a duplicate load past the end is never
+  // used). The V row of a token past the chunk's end repeats the last valid row and is zeroed
+  // when staged, so every load is unconditional. Load i of the record part is piece(b, rc, i).
+  constexpr int NTS = CHUNK / KS, NKS = K / KS;
+  constexpr int NLOADS = 2 * NTS + 2 * NKS + TPW * (NTS + 1);
+  auto rec_of = [&](int k) {
     const int kk = min(k, run - 1);
-    const char* rc = p.rec + ((int64_t)sRun[kk] - p.seg_begin) * H * p.rec_bytes + (int64_t)h * p.rec_bytes;
-    char* lrec = smem + SL::oRec + b * SL::RB;
-#pragma unroll
-    for (int i = 0; i < (NSR + NW - 1) / NW; ++i) {
-      const int sl = w + NW * i;
-      if (sl < NSR) dma16(rc + sl * 1024 + lane * 16, lrec + sl * 1024);
-    }
+    const int ri = __builtin_amdgcn_readfirstlane(sRun[kk]);  // uniform record index
+    return rec_h + (int64_t)ri * rec_stride;
+  };
+  auto load_v = [&](B& b, int k) {
+    const int kk = min(k, run - 1);
     const int tok = tok_of(kk), len = len_of(kk);
-    char* lv = smem + SL::oVst + b * SL::VSB;
+    b.v = *reinterpret_cast<const vvec*>(gv + ((int64_t)tok + min(lane, len - 1)) * vrow + VE * w);
+  };
+  auto piece = [&](B& b, const char* rc, auto I) {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i < NTS) {
+      b.tf[i] = ldf(rc, lo_t + STEP * i);
+    } else if constexpr (i < 2 * NTS) {
+      b.pf[i - NTS] = ldf(rc, lo_p + STEP * (i - NTS));
+    } else if constexpr (i < 2 * NTS + NKS) {
+      b.wf[i - 2 * NTS] = ldf(rc, lo_w + STEP * (i - 2 * NTS));
+    } else if constexpr (i < 2 * NTS + 2 * NKS) {
+      b.qf[i - 2 * NTS - NKS] = ldf(rc, lo_q + STEP * (i - 2 * NTS - NKS));
+    } else {
+      constexpr int j = i - 2 * NTS - 2 * NKS, tt = j / (NTS + 1), s = j % (NTS + 1);
+      if constexpr (s < NTS) b.kf[tt][s] = ldf(rc, lo_k[tt] + STEP * s);
+      else b.gam[tt] = *reinterpret_cast<const float*>(rc + lo_g[tt]);
+    }
+  };
+  auto issue_all = [&](B& b, int k) {
+    load_v(b, k);
+    __builtin_amdgcn_sched_barrier(0);
+    const char* rc = rec_of(k);
+    static_for<0, NLOADS>([&](auto I) { piece(b, rc, I); });
+  };
+
+  // V of chunk k into LDS: lane = token, wave w = columns VE*w .. +VE-1
+  auto stage = [&](const B& b, int k) {
+    const bool valid = lane < len_of(k);
+    vvec x = b.v;
 #pragma unroll
-    for (int i = 0; i < (NSV + NW - 1) / NW; ++i) {
-      const int sv = w + NW * i;
-      if (sv >= NSV) continue;
-      const int t = sv * TPS + lane / LPT, part = lane % LPT;
-      const char* g = t < len ? gv + ((int64_t)tok + t) * vrow * (int64_t)sizeof(MT) + part * 16
-                              : p.zeros + part * 16;
-      dma16(g, lv + sv * 1024);
+    for (int i = 0; i < VE; ++i) x[i] = valid ? x[i] : from_f32<MT>(0.f);
+    *reinterpret_cast<vvec*>(sV + lane * LD + VE * w) = x;
+  };
+
+  // Chunk k for token tile w: U, P'V, W S, Q_eff S (Delta to LDS, O to memory), with the loads
+  // of chunk k+1 spread between the matrix operations. The loads go through the CU's
+  // vector-memory path at about 64 B per clock and a wave waits at a load until that path
+  // accepts it, so one load follows each MFMA instead of all loads going out in one burst; the
+  // scheduling barriers keep that order. Branch-free: the record holds zeros above the
+  // diagonal of T' and P', so every reduction step runs.
+  // MFMA j: reduction step s = j / (2 NVT) of U, P'V (j < NMF_T), then of W S, Q_eff S,
+  // round-robin over the independent accumulators.
+  constexpr int NMF_T = 2 * NVT * NTS, NMF_K = 2 * NVT * NKS, NMF = NMF_T + NMF_K;
+  constexpr int NLC = 2 * NTS + 2 * NKS;  // pieces loaded during compute: T', P', W, Q_eff
+  constexpr int LSTRIDE = NMF / NLC;      // MFMAs per piece
+  static_assert(LSTRIDE >= 1, "one load per MFMA at most");
+  f32x4 Opend[NVT];
+  MT* Odst[NVT];
+  auto compute = [&](const B& b, B& nxt, int k) {
+    const int tok = tok_of(k), len = len_of(k);
+    const int t = 16 * w + m;
+    // fragments of reduction step s: V^T (s < NTS) and S^T (s < NKS), read one step ahead
+    frag vf[2][NVT], sf[2][NVT];
+#pragma unroll
+    for (int nt = 0; nt < NVT; ++nt) {
+      vf[0][nt] = frag_t(sV, LD, 16 * nt, 0, lane);
+      sf[0][nt] = frag_t(sS, LD, 16 * nt, 0, lane);
+    }
+    load_v(nxt, k + 1);
+    const char* rc = rec_of(k + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 U[NVT], Ol[NVT], Y[NVT], Z[NVT];
+#pragma unroll
+    for (int nt = 0; nt < NVT; ++nt) U[nt] = Ol[nt] = Y[nt] = Z[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    static_for<0, NMF>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      constexpr int s = j < NMF_T ? j / (2 * NVT) : (j - NMF_T) / (2 * NVT);
+      constexpr bool first_of_step = (j < NMF_T ? j % (2 * NVT) : (j - NMF_T) % (2 * NVT)) == 0;
+      if constexpr (first_of_step && j < NMF_T && s + 1 < NTS) {
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt) vf[(s + 1) & 1][nt] = frag_t(sV, LD, 16 * nt, s + 1, lane);
+      }
+      if constexpr (first_of_step && j >= NMF_T && s + 1 < NKS) {
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt) sf[(s + 1) & 1][nt] = frag_t(sS, LD, 16 * nt, s + 1, lane);
+      }
+      if constexpr (j < NMF_T) {
+        constexpr int nt = (j % (2 * NVT)) / 2;
+        if constexpr (j % 2 == 0) U[nt] = Mma<MT>::mma(vf[s & 1][nt], b.tf[s], U[nt]);
+        else Ol[nt] = Mma<MT>::mma(vf[s & 1][nt], b.pf[s], Ol[nt]);
+      } else {
+        constexpr int jj = j - NMF_T, nt = (jj % (2 * NVT)) / 2;
+        if constexpr (jj % 2 == 0) Y[nt] = Mma<MT>::mma(sf[s & 1][nt], b.wf[s], Y[nt]);
+        else Z[nt] = Mma<MT>::mma(sf[s & 1][nt], b.qf[s], Z[nt]);
+      }
+      if constexpr (j % LSTRIDE == 0 && j / LSTRIDE < NLC)
+        piece(nxt, rc, std::integral_constant<int, j / LSTRIDE>());
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int nt = 0; nt < NVT; ++nt) {
+      st4(sD + t * LD + 16 * nt + 4 * g, U[nt] - Y[nt]);
+      Opend[nt] = Ol[nt] + Z[nt];
+      Odst[nt] = t < len ? go + ((int64_t)tok + t) * vrow + 16 * nt + 4 * g : trash;
     }
   };
 
-  auto process = [&](int k, int b) {
-    const int tok = tok_of(k), len = len_of(k);
-    const char* lrec = smem + SL::oRec + b * SL::RB;
-    const MT* lv = reinterpret_cast<const MT*>(smem + SL::oVst + b * SL::VSB);
-    auto afrag = [&](size_t off_elems) -> frag {  // A fragment of this lane from the LDS record
-      return *reinterpret_cast<const frag*>(lrec + off_elems * sizeof(MT));
-    };
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      const int nt = ct0 + c;
-      f32x4 U = {0.f, 0.f, 0.f, 0.f}, Ol = U, Y = U, Z = U;
-#pragma unroll
-      for (int s = 0; s < CHUNK / KS; ++s) {
-        if (s < nst_tri) {
-          frag bv;  // B fragment of V: tokens kk(g, e) of column 16nt + m
-#pragma unroll
-          for (int e = 0; e < Mma<MT>::EPL; ++e)
-            bv[e] = lv[(KS * s + 16 * (e / 4) + 4 * gq + (e % 4)) * VS + 16 * nt + m];
-          U = Mma<MT>::mma(afrag(R::oTb + slot_elem<MT>(tw, s, lane, CHUNK)), bv, U);
-          Ol = Mma<MT>::mma(afrag(R::oPb + slot_elem<MT>(tw, s, lane, CHUNK)), bv, Ol);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < K / KS; ++s) {
-        const auto bs = load_frag(sS + (16 * nt + m) * SL::LKs, s, gq);
-        Y = Mma<MT>::mma(afrag(R::oW + slot_elem<MT>(tw, s, lane, K)), bs, Y);
-        Z = Mma<MT>::mma(afrag(R::oQ + slot_elem<MT>(tw, s, lane, K)), bs, Z);
-      }
-      const f32x4 D = U - Y;
-      const f32x4 O = Ol + Z;
-      st4(sDl + (16 * nt + m) * SL::LCs + 16 * tw + 4 * gq, D);
-      // output rows straight from the result tile; rows past the chunk's end go to the sink,
-      // so every lane issues the same number of stores
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tw + 4 * gq + r;
-        MT* dst = t < len ? go + ((int64_t)tok + t) * vrow + 16 * nt + m
-                          : reinterpret_cast<MT*>(p.trash) + lane;
-        *dst = from_f32<MT>(O[r]);
-      }
+  // S'^T = S^T Diag(gamma) + Delta^T Ktilde for key-channel tiles w, w+4
+  auto update = [&](const B& b, B& nxt, int k) {
+    {
+      const char* rc = rec_of(k + 1);
+      static_for<NLC, NLOADS>([&](auto I) { piece(nxt, rc, I); });
     }
-    lds_barrier();  // Delta complete; everyone is done reading sS
-    // state update S = gamma * S + Ktilde^T Delta
+    frag df[NVT][NTS];
+#pragma unroll
+    for (int nt = 0; nt < NVT; ++nt)
+#pragma unroll
+      for (int s = 0; s < NTS; ++s) df[nt][s] = frag_t(sD, LD, 16 * nt, s, lane);
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-      const int t = w + NW * tt;
-      if (t < NKT) {
-        const f32x4 gam = *reinterpret_cast<const f32x4*>(lrec + R::oGamBytes + (16 * t + 4 * gq) * 4);
+      const int kt = w + 4 * tt;
+      if (kt < NKT) {
 #pragma unroll
         for (int nt = 0; nt < NVT; ++nt) {
-          f32x4 acc = gam * Sr[tt][nt];
+          f32x4 acc = Sr[tt][nt] * b.gam[tt];
 #pragma unroll
-          for (int s = 0; s < CHUNK / KS; ++s) {
-            const auto bd = load_frag(sDl + (16 * nt + m) * SL::LCs, s, gq);
-            acc = Mma<MT>::mma(afrag(R::oKt + slot_elem<MT>(t, s, lane, CHUNK)), bd, acc);
-          }
+          for (int s = 0; s < NTS; ++s) acc = Mma<MT>::mma(df[nt][s], b.kf[tt][s], acc);
           Sr[tt][nt] = acc;
-          st4(sS + (16 * nt + m) * SL::LKs + 16 * t + 4 * gq, acc);
+          st4(sS + (16 * kt + m) * LD + 16 * nt + 4 * g, acc);
         }
       }
     }
+    // the output rows of chunk k leave after the update, behind the loads issued above
+#pragma unroll
+    for (int nt = 0; nt < NVT; ++nt) st4(Odst[nt], Opend[nt]);
   };
 
-  KDA_WAIT_VM(0);  // initial state loads done before counting DMA operations
-  if constexpr (NBUF == 2) {
-    // chunk k+1 streams into the other buffer while chunk k is computed; at the top of each
-    // step only the previous chunk's NST output stores may still be outstanding
-    issue(0, 0);
-    for (int k = 0; k < run; ++k) {
-      if (k == 0) {
-        KDA_WAIT_VM(0);
-      } else {
-        KDA_WAIT_VM(NST);
-      }
-      lds_barrier();  // chunk k's record and V are in LDS; sS holds the current state
-      issue(k + 1, (k + 1) & 1);
-      process(k, k & 1);
-    }
-  } else {
-    for (int k = 0; k < run; ++k) {
-      lds_barrier();  // the previous chunk is done with the single buffer
-      issue(k, 0);
-      KDA_WAIT_VM(0);
-      lds_barrier();
-      process(k, 0);
-    }
+  // Two register bundles in turn: chunk k+1's loads are issued while chunk k is computed. The
+  // second half differs from the first (an extra scheduling barrier) so that the compiler keeps
+  // both halves instead of folding them into one with register copies between bundles.
+  auto chunk = [&](const B& cur, B& nxt, int k, auto PAR) {
+    stage(cur, k);
+    lds_barrier();  // V and S of chunk k ready
+    compute(cur, nxt, k);
+    if constexpr (decltype(PAR)::value) __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();  // Delta complete; S and V no longer read
+    update(cur, nxt, k);
+  };
+  B b0, b1;
+  issue_all(b0, 0);
+  for (int k = 0; k < run; k += 2) {
+    chunk(b0, b1, k, std::false_type());
+    if (k + 1 >= run) break;
+    chunk(b1, b0, k + 1, std::true_type());
   }
-  KDA_WAIT_VM(0);
 
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
-    const int t = w + NW * tt;
-    if (t < NKT) {
+    const int kt = w + 4 * tt;
+    if (kt < NKT) {
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          p.state[sbase + (size_t)(16 * t + 4 * gq + r) * V + 16 * nt + m] = Sr[tt][nt][r];
+        *reinterpret_cast<f32x4*>(p.state + sbase + (size_t)(16 * kt + m) * V + 16 * nt + 4 * g) = Sr[tt][nt];
     }
   }
 }
@@ -898,8 +979,7 @@ bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan
   p->num_segs = ub > 0 ? (ub + E - 1) / E : 0;
   p->slots = N < E ? N : E;
   p->rec_bytes = ((3LL * CHUNK * K + 2LL * CHUNK * CHUNK) * es + 4LL * K + 1023) / 1024 * 1024;
-  // V split: slices of 32 columns (8-wave workgroups; the double-buffered chunk record in LDS
-  // leaves room for 32 columns of state)
+  // V split: slices of 32 columns, one 4-wave workgroup each
   p->n_slices = V / 32;
   p->vs = 32;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -916,8 +996,8 @@ bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan
   off += al((size_t)p->num_segs * 4);
   p->off_state = off;
   off += al((size_t)N * H * K * V * 4);
-  p->off_zeros = off;  // 1 KB of zeros, then a 1 KB sink
-  off += 2048;
+  p->off_sink = off;  // 1 KB sink for output rows past a chunk's end
+  off += 1024;
   p->off_rec = off;
   p->rec_buf_bytes = (size_t)E * H * p->rec_bytes;
   off += p->rec_buf_bytes;
@@ -940,7 +1020,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
   SeqView sv{a.cu_seqlens, a.num_seqs, a.total_tokens};
   hipLaunchKernelGGL(table_kernel, dim3(a.num_seqs), dim3(256), 0, st, sv, a.num_heads,
                      (int64_t)a.dk * a.dv, pl.ub_entries, a.init_state, a.final_state, entries,
-                     header, basetab, reinterpret_cast<float*>(ws + pl.off_zeros));
+                     header, basetab);
   if (pl.num_segs == 0) return hipGetLastError();
   hipLaunchKernelGGL(segment_kernel, dim3(pl.num_segs), dim3(256), 0, st, entries, header,
                      pl.seg_entries, pl.slots, seg_first, seg_count);
@@ -960,9 +1040,9 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
     StateParams sp{a.v, a.o, a.init_state, run_state, entries, header, basetab,
                    seg_first + s * pl.slots, seg_count + s, s * pl.seg_entries, pl.seg_entries,
                    a.num_heads, a.dv, pl.n_slices, chains, rec, pl.rec_bytes,
-                   ws + pl.off_zeros, ws + pl.off_zeros + 1024};
+                   ws + pl.off_sink};
     if (pl.vs != 32) return false;
-    hipLaunchKernelGGL((state_kernel<K, 2, MT>), sgrid, dim3(512), 0, q, sp);
+    hipLaunchKernelGGL((state_kernel<K, 2, MT>), sgrid, dim3(STATE_THREADS), 0, q, sp);
     return true;
   };
 
