@@ -303,50 +303,70 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
 
   const int H = p.H;
-  const int64_t j = blockIdx.x / H;
-  const int h = blockIdx.x % H;
-  const int64_t e = p.seg_begin + j;
-  if (j >= p.E || e >= (int64_t)p.header[0]) return;
-  const Entry en = p.entries[e];
-  const int len = en.len;  // 1 .. CHUNK
-  const int64_t tok0 = en.tok;
   const MT* gq_ = reinterpret_cast<const MT*>(p.q);
   const MT* gk_ = reinterpret_cast<const MT*>(p.k);
   const MT* gg_ = reinterpret_cast<const MT*>(p.g);
   const MT* gb_ = reinterpret_cast<const MT*>(p.beta);
-  MT* recM = reinterpret_cast<MT*>(p.rec + (j * H + h) * p.rec_bytes);
-  float* recGam = reinterpret_cast<float*>(p.rec + (j * H + h) * p.rec_bytes + R::oGamBytes);
-
-  const int tid = threadIdx.x;
   const int w = wave_id();
-  const int lane = lane_id();
-  const int m = lane & 15;
-  const int g = lane >> 4;
-  const int t = 16 * w + m;  // this lane's token in the chunk
-  const bool valid = t < len;
+  const int t0 = 16 * w + (lane_id() & 15);  // this lane's token in the chunk
+  const int g0 = lane_id() >> 4;
 
-  // ---------------- phase 1: the token's q, k, log alpha. Rows past the chunk's end load the
-  // last valid row again and are zeroed (q = k = 0, log alpha = 0, beta = 0 there), so every
-  // load is unconditional and all are in flight together.
-  float qv[NG][4], kv[NG][4], lv[NG][4];
-  {
-    const int64_t row = (tok0 + min(t, len - 1)) * (int64_t)H * K + (int64_t)h * K + 4 * g;
+  // Persistent workgroups: task = (chunk j of the segment, head h) = (task / H, task % H). The
+  // raw inputs of the next task are loaded while the current one is computed (phases 2-6).
+  const int64_t ntask = min(p.E, (int64_t)p.header[0] - p.seg_begin) * H;
+  using raw4 = typename VecN<MT, 4>::vec;
+  struct Raw {
+    raw4 q[NG], k[NG], g[NG];
+    MT b;
+  };
+  // Rows past the chunk's end load the last valid row again; they are zeroed after conversion
+  // (q = k = 0, log alpha = 0, beta = 0 there), so every load is unconditional.
+  auto load_raw = [&](Raw& r, int64_t task) {
+    const Entry en = p.entries[p.seg_begin + task / H];
+    const int hh = (int)(task % H);
+    const int64_t tl = en.tok + min(t0, en.len - 1);
+    const int64_t row = tl * (int64_t)H * K + (int64_t)hh * K + 4 * g0;
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
-      VecN<MT, 4>::load(gq_ + row + 16 * u, qv[u]);
-      VecN<MT, 4>::load(gk_ + row + 16 * u, kv[u]);
-      VecN<MT, 4>::load(gg_ + row + 16 * u, lv[u]);
+      r.q[u] = *reinterpret_cast<const raw4*>(gq_ + row + 16 * u);
+      r.k[u] = *reinterpret_cast<const raw4*>(gk_ + row + 16 * u);
+      r.g[u] = *reinterpret_cast<const raw4*>(gg_ + row + 16 * u);
     }
-  }
-  const float bval = to_f32(gb_[(tok0 + min(t, len - 1)) * H + h]);
+    r.b = gb_[tl * H + hh];
+  };
+  int64_t task = blockIdx.x;
+  if (task >= ntask) return;
+  Raw cur, nxt;
+  load_raw(cur, task);
+#pragma clang loop unroll(disable)
+  for (; task < ntask; task += gridDim.x) {
+  // Lane-dependent addresses are recomputed in every iteration: without the opaque copy the
+  // compiler hoists all of them out of the loop and keeps them live, which spills.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  const int t = 16 * w + m;
+  const int64_t j = task / H;
+  const int h = (int)(task % H);
+  const Entry en = p.entries[p.seg_begin + j];
+  const int len = en.len;  // 1 .. CHUNK
+  MT* recM = reinterpret_cast<MT*>(p.rec + (j * H + h) * p.rec_bytes);
+  float* recGam = reinterpret_cast<float*>(p.rec + (j * H + h) * p.rec_bytes + R::oGamBytes);
+  const bool valid = t < len;
+
+  // ---------------- phase 1: the token's q, k, log alpha (fp32), masked past the chunk's end
+  float qv[NG][4], kv[NG][4], lv[NG][4];
 #pragma unroll
   for (int u = 0; u < NG; ++u)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      qv[u][r] = valid ? qv[u][r] : 0.f;
-      kv[u][r] = valid ? kv[u][r] : 0.f;
-      lv[u][r] = valid ? lv[u][r] : 0.f;
+      qv[u][r] = valid ? to_f32(cur.q[u][r]) : 0.f;
+      kv[u][r] = valid ? to_f32(cur.k[u][r]) : 0.f;
+      lv[u][r] = valid ? to_f32(cur.g[u][r]) : 0.f;
     }
+  const float bval = to_f32(cur.b);
   if (g == 0) sBeta[t] = valid ? bval : 0.f;
   // inclusive cumsum of log alpha over the 16 tokens of the sub-block (one 16-lane row):
   // lv becomes b_t - e_{w-1}; dI = e_w - e_{w-1} is the row's last value
@@ -446,6 +466,9 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
           load_frag(sKtT + (16 * tile + (ln & 15)) * L::LC, s, ln >> 4);
     }
   }
+
+  // the next task's inputs load during phases 2-6 (phase 1's fp32 copies are dead by now)
+  load_raw(nxt, task + gridDim.x < ntask ? task + gridDim.x : task);
 
   // ---------------- phase 2: blocks (I, w), I >= w, of A and P. The column operand (token
   // block w, scaled per channel by D_{Iw}) is this wave's own kc; the row operands are read as
@@ -607,6 +630,9 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
       acc = -acc;
     }
     st4(recM + R::oPb + slot4<MT>(16 * b + m, 16 * w + 4 * g, CHUNK), acc);
+  }
+  lds_barrier();  // the next task reuses every LDS region
+  cur = nxt;
   }
 }
 
@@ -1028,7 +1054,13 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
   const int64_t chains = pl.slots * a.num_heads;
   const int64_t chains8 = (chains + 7) / 8 * 8;
   const dim3 sgrid((unsigned)(chains8 * pl.n_slices));
-  const dim3 pgrid((unsigned)(pl.seg_entries * a.num_heads));
+  // prep: persistent workgroups, two per CU (its LDS and register budget), looping over tasks
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+    ncu = 256;
+  const int64_t ptasks = pl.seg_entries * a.num_heads;
+  const dim3 pgrid((unsigned)min(ptasks, (int64_t)2 * ncu));
   auto prep = [&](int64_t s, hipStream_t q) {
     char* rec = ws + pl.off_rec;
     PrepParams pp{a.q, a.k, a.g, a.beta, entries, header, a.num_heads, s * pl.seg_entries,

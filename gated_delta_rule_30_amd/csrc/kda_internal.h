@@ -13,8 +13,8 @@ constexpr int NSUB = CHUNK / SUBBLK;
 constexpr int NTHREADS = 256;  // threads per workgroup of every chunk kernel
 
 // Target number of (chunk, head) records per segment: the segment's record buffer (66 KB per
-// record at K=V=128 bf16) then stays resident in the 256 MB Infinity Cache.
-constexpr int64_t SEG_CHUNK_HEADS = 1024;
+// record at K=V=128 bf16, 135 MB) then stays resident in the 256 MB Infinity Cache.
+constexpr int64_t SEG_CHUNK_HEADS = 2048;
 
 struct DecodeArgs {
   const void *q, *k, *v, *g, *beta;
