@@ -230,20 +230,21 @@ struct PrepLayout {
   static constexpr int NPAIR = NSUB * (NSUB + 1) / 2;
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t szFrag = (size_t)CHUNK * K * sizeof(MT);  // [CHUNK][K] as fragments
-  static constexpr size_t szKT = (size_t)K * LC * sizeof(MT);       // [K][CHUNK]
+  static constexpr int LDK = K + 16 / (int)sizeof(MT);                // MT rows of length K
+  static constexpr size_t szKR = (size_t)CHUNK * LDK * sizeof(MT);    // [CHUNK][K], token-major
   static constexpr size_t szTri = (size_t)CHUNK * LC * sizeof(MT);  // [CHUNK][CHUNK]
   static constexpr size_t szAf = (size_t)CHUNK * LCF * 4;
   static constexpr size_t szTab = (size_t)(NSUB + NPAIR + NSUB) * K * 4;
-  // X: Q^ and K^ fragments (phases 1-2); T' and T'^T (phases 4-6)
-  static constexpr size_t szX = mx(2 * szFrag, 2 * szTri);
-  // R1: Ktilde^T staging (phase 1); A, then T (phases 2-4); W^T (phases 5-6)
-  static constexpr size_t szR1 = mx(szKT, szAf);
-  // P: block decays and per-channel factor tables (phases 1-2); -P (phases 2-6)
+  // X: Q^ and K^ fragments (phases 1-2); T' (phases 4-6)
+  static constexpr size_t szX = mx(2 * szFrag, szTri);
+  // R1: Ktilde staging (phase 1); A, then T (phases 2-4); W (phases 5-6)
+  static constexpr size_t szR1 = mx(szKR, szAf);
+  // P: block decays and per-channel factor tables (phases 1-2); -P^T (phases 2-6)
   static constexpr size_t szP = mx(szTri, szTab);
-  static constexpr size_t oQh = 0, oKh = szFrag, oTb = 0, oTbT = szTri;
+  static constexpr size_t oQh = 0, oKh = szFrag, oTb = 0;
   static constexpr size_t oR1 = szX;
-  static constexpr size_t oKaT = oR1 + szR1;  // Ka^T (phases 1-5)
-  static constexpr size_t oP = oKaT + szKT;
+  static constexpr size_t oKa = oR1 + szR1;  // Ka, token-major (phases 1-5)
+  static constexpr size_t oP = oKa + szKR;
   static constexpr size_t oEx = oP + szP;     // e^{e_{J-1}} per block and channel (phases 1-6)
   static constexpr size_t oBeta = oEx + (size_t)NSUB * K * 4;
   static constexpr size_t total = oBeta + (size_t)CHUNK * 4;
@@ -290,15 +291,14 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   MT* sQh = reinterpret_cast<MT*>(smem + L::oQh);
   MT* sKh = reinterpret_cast<MT*>(smem + L::oKh);
   MT* sTb = reinterpret_cast<MT*>(smem + L::oTb);
-  MT* sTbT = reinterpret_cast<MT*>(smem + L::oTbT);
-  MT* sKtT = reinterpret_cast<MT*>(smem + L::oR1);
+  MT* sKt = reinterpret_cast<MT*>(smem + L::oR1);
   float* sA = reinterpret_cast<float*>(smem + L::oR1);
-  MT* sWT = reinterpret_cast<MT*>(smem + L::oR1);
-  MT* sKaT = reinterpret_cast<MT*>(smem + L::oKaT);
+  MT* sW = reinterpret_cast<MT*>(smem + L::oR1);
+  MT* sKa = reinterpret_cast<MT*>(smem + L::oKa);
   float* sDel = reinterpret_cast<float*>(smem + L::oP);
   float* sD = sDel + NSUB * K;
   float* sTail = sD + NPAIR * K;
-  MT* sPn = reinterpret_cast<MT*>(smem + L::oP);
+  MT* sPnT = reinterpret_cast<MT*>(smem + L::oP);
   float* sEx = reinterpret_cast<float*>(smem + L::oEx);
   float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
 
@@ -356,20 +356,23 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   float* recGam = reinterpret_cast<float*>(p.rec + (j * H + h) * p.rec_bytes + R::oGamBytes);
   const bool valid = t < len;
 
-  // ---------------- phase 1: the token's q, k, log alpha (fp32), masked past the chunk's end
+  // ---------------- phase 1: the token's q, k and log2 alpha (fp32). Past the chunk's end only
+  // log alpha (and beta) are zeroed: the q and k rows there repeat the last valid token and are
+  // never used -- beta = 0 zeroes their rows of A, their columns of T' and P', and so their
+  // rows of W and Delta -- while log alpha = 0 keeps the decay products of the valid tokens.
   float qv[NG][4], kv[NG][4], lv[NG][4];
 #pragma unroll
   for (int u = 0; u < NG; ++u)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      qv[u][r] = valid ? to_f32(cur.q[u][r]) : 0.f;
-      kv[u][r] = valid ? to_f32(cur.k[u][r]) : 0.f;
-      lv[u][r] = valid ? to_f32(cur.g[u][r]) : 0.f;
+      qv[u][r] = to_f32(cur.q[u][r]);
+      kv[u][r] = to_f32(cur.k[u][r]);
+      lv[u][r] = valid ? to_f32(cur.g[u][r]) * LOG2E : 0.f;
     }
   const float bval = to_f32(cur.b);
   if (g == 0) sBeta[t] = valid ? bval : 0.f;
-  // inclusive cumsum of log alpha over the 16 tokens of the sub-block (one 16-lane row):
-  // lv becomes b_t - e_{w-1}; dI = e_w - e_{w-1} is the row's last value
+  // inclusive cumsum of log2 alpha over the 16 tokens of the sub-block (one 16-lane row):
+  // lv becomes b_t - e_{w-1}; dI = e_w - e_{w-1} is the row's last value (log2 units)
   float dI[NG][4];
 #pragma unroll
   for (int u = 0; u < NG; ++u)
@@ -406,17 +409,17 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     for (int v = 0; v < 2 * NSUB + 1 + NPAIR; ++v) {
       if (v % NROLE != role) continue;
       if (v < NSUB) {
-        sEx[v * K + c] = exp_f(ec[v]);
+        sEx[v * K + c] = exp2_f(ec[v]);
       } else if (v == NSUB) {
-        recGam[c] = exp_f(ec[NSUB]);
+        recGam[c] = exp2_f(ec[NSUB]);
       } else if (v < NSUB + 1 + NPAIR) {
         const int pi = v - NSUB - 1;
         const int I = (pi >= 1) + (pi >= 3) + (pi >= 6);
         const int J = pi - I * (I + 1) / 2;
-        sD[pi * K + c] = exp_f((I == J ? ec[J] : ec[I]) - ec[J + 1]);
+        sD[pi * K + c] = exp2_f((I == J ? ec[J] : ec[I]) - ec[J + 1]);
       } else {
         const int J = v - NSUB - 1 - NPAIR;
-        sTail[J * K + c] = exp_f(ec[NSUB] - ec[J + 1]);
+        sTail[J * K + c] = exp2_f(ec[NSUB] - ec[J + 1]);
       }
     }
   }
@@ -432,18 +435,20 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     for (int u = 0; u < NG; ++u) {
       const f32x4 ex = *reinterpret_cast<const f32x4*>(sEx + w * K + 16 * u + 4 * g);
       const f32x4 tl = *reinterpret_cast<const f32x4*>(sTail + w * K + 16 * u + 4 * g);
+      f32x4 ka, kt;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float rr = exp_f(lv[u][r]);
-        const float cc = exp_f(dI[u][r] - lv[u][r]);
+        const float rr = exp2_f(lv[u][r]);
+        const float cc = exp2_f(dI[u][r] - lv[u][r]);
         qh[u][r] = qv[u][r] * rr;
         kh[u][r] = kv[u][r] * rr;
         kc[u][r] = kv[u][r] * cc;
         qe[u][r] = qh[u][r] * ex[r];
-        const int c = 16 * u + 4 * g + r;
-        sKaT[c * L::LC + t] = from_f32<MT>(kh[u][r] * ex[r]);
-        sKtT[c * L::LC + t] = from_f32<MT>(kc[u][r] * tl[r]);
+        ka[r] = kh[u][r] * ex[r];
+        kt[r] = kc[u][r] * tl[r];
       }
+      st4(sKa + t * L::LDK + 16 * u + 4 * g, ka);
+      st4(sKt + t * L::LDK + 16 * u + 4 * g, kt);
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -462,8 +467,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
       const int sl = tid + PREP_THREADS * i;
       const int ln = sl & 63, ts = sl >> 6;
       const int s = ts % (CHUNK / KS), tile = ts / (CHUNK / KS);
-      *reinterpret_cast<frag*>(recM + R::oKt + (size_t)sl * EPL) =
-          load_frag(sKtT + (16 * tile + (ln & 15)) * L::LC, s, ln >> 4);
+      *reinterpret_cast<frag*>(recM + R::oKt + (size_t)sl * EPL) = frag_t(sKt, L::LDK, 16 * tile, s, ln);
     }
   }
 
@@ -497,7 +501,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     }
   }
   lds_barrier();
-  // A (row-scaled by beta, strictly lower) -> sA; -P (lower, upper blocks zero) -> sPn
+  // A (row-scaled by beta, strictly lower) -> sA; -P (lower, upper blocks zero) -> sPnT, transposed
   {
     const int jj = 16 * w + m;
 #pragma unroll
@@ -506,10 +510,16 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * g + r;
         const bool lowA = I > w || (I == w && jj < i);
-        const bool lowP = I > w || (I == w && jj <= i);
         if (I >= w) sA[i * L::LCF + jj] = lowA ? tA[I][r] * sBeta[i] : 0.f;
-        sPn[i * L::LC + jj] = from_f32<MT>(lowP ? -tP[I][r] : 0.f);
       }
+      // -P^T row jj, columns 16I + 4g .. +3
+      f32x4 pn;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * g + r;
+        pn[r] = (I > w || (I == w && jj <= i)) ? -tP[I][r] : 0.f;
+      }
+      st4(sPnT + jj * L::LC + 16 * I + 4 * g, pn);
     }
   }
   lds_barrier();
@@ -577,8 +587,6 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     tv *= *reinterpret_cast<const f32x4*>(sBeta + j0);
     if (Ii < Jj) tv = f32x4{0.f, 0.f, 0.f, 0.f};
     st4(sTb + i * L::LC + j0, tv);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) sTbT[(j0 + k) * L::LC + i] = from_f32<MT>(tv[k]);
     st4(recM + R::oTb + slot4<MT>(i, j0, CHUNK), tv);
   }
   lds_barrier();
@@ -593,11 +601,10 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
 #pragma unroll
     for (int s = 0; s < CHUNK / KS; ++s)
       if (s < nsteps)
-        acc = Mma<MT>::mma(load_frag(sKaT + (16 * a + m) * L::LC, s, g),
+        acc = Mma<MT>::mma(frag_t(sKa, L::LDK, 16 * a, s, lane),
                            load_frag(sTb + (16 * b + m) * L::LC, s, g), acc);
     st4(recM + R::oW + slot4<MT>(16 * b + m, 16 * a + 4 * g, K), acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sWT[(16 * a + 4 * g + r) * L::LC + 16 * b + m] = from_f32<MT>(acc[r]);
+    st4(sW + (16 * b + m) * L::LDK + 16 * a + 4 * g, acc);  // W row 16b + m
   }
   lds_barrier();
 
@@ -611,8 +618,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
 #pragma unroll
       for (int s = 0; s < CHUNK / KS; ++s)
         if (s < nsteps)
-          acc = Mma<MT>::mma(load_frag(sWT + (16 * a + m) * L::LC, s, g),
-                             load_frag(sPn + (16 * w + m) * L::LC, s, g), acc);
+          acc = Mma<MT>::mma(frag_t(sW, L::LDK, 16 * a, s, lane), frag_t(sPnT, L::LC, 16 * w, s, lane), acc);
       st4(recM + R::oQ + slot4<MT>(16 * w + m, 16 * a + 4 * g, K), acc);
     }
   }
@@ -625,8 +631,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
 #pragma unroll
       for (int s = 0; s < CHUNK / KS; ++s)
         if (s < nsteps)
-          acc = Mma<MT>::mma(load_frag(sTbT + (16 * w + m) * L::LC, s, g),
-                             load_frag(sPn + (16 * b + m) * L::LC, s, g), acc);
+          acc = Mma<MT>::mma(frag_t(sTb, L::LC, 16 * w, s, lane), frag_t(sPnT, L::LC, 16 * b, s, lane), acc);
       acc = -acc;
     }
     st4(recM + R::oPb + slot4<MT>(16 * b + m, 16 * w + 4 * g, CHUNK), acc);
@@ -661,31 +666,6 @@ struct StateLayout {
   static constexpr size_t total = oRun + (SEG_CHUNK_HEADS + 16) * 4;
   static_assert((LD * sizeof(MT)) % 16 == 0, "row alignment");
 };
-
-// A fragment (reduction step s) of X^T for the 16 rows c0 .. c0+15 of X^T, where X is stored
-// row-major with ld elements per row and rows = reduction index: lane (m, g) receives
-// X[KS*s + kk(g, e)][c0 + m]. ds_read_b64_tr_b16 works per group of 16 lanes: lane 4p + r of
-// the group receives element r of the 8 bytes addressed by lanes 4e + p (e = 0..3). So lane
-// (m, g) supplies the address of row 4g + m/4, columns c0 + 4(m%4) .. +3, and receives rows
-// 4g .. 4g+3 of column c0 + m.
-__device__ __forceinline__ bf16x4 ds_read_tr4(const bf16* p) {
-  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
-  const v4bf v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (__attribute__((address_space(3))) v4bf*)(__attribute__((address_space(3))) void*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
-__device__ __forceinline__ bf16x8 frag_t(const bf16* X, int ld, int c0, int s, int lane) {
-  const int m = lane & 15, g = lane >> 4;
-  const bf16* p = X + (32 * s + 4 * g + (m >> 2)) * ld + c0 + 4 * (m & 3);
-  const bf16x4 lo = ds_read_tr4(p);
-  const bf16x4 hi = ds_read_tr4(p + 16 * ld);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ f32x4 frag_t(const float* X, int ld, int c0, int s, int lane) {
-  const int m = lane & 15, g = lane >> 4;
-  const float* p = X + (16 * s + 4 * g) * ld + c0 + m;
-  return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
-}
 
 struct StateParams {
   const void* v;

@@ -21,8 +21,10 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
 
-// e^x through the hardware base-2 exponential.
+// e^x through the hardware base-2 exponential; exp2_f takes the exponent in log2 units.
 __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float LOG2E = 1.4426950408889634f;
 
 // ------------------------------------------------------------------ MFMA 16x16 tiles
 // A "fragment" is what one lane feeds to one 16x16xKS reduction step: 16 bytes.
@@ -92,6 +94,31 @@ __device__ __forceinline__ f32x4 load_frag_scaled(const float* row, const float*
 __device__ __forceinline__ bf16x8 frag_from_acc(f32x4 lo, f32x4 hi, bf16) {
   return __builtin_shufflevector(__builtin_convertvector(lo, bf16x4), __builtin_convertvector(hi, bf16x4),
                                  0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// A fragment (reduction step s) of X^T for the 16 rows c0 .. c0+15 of X^T, where X is stored
+// row-major with ld elements per row and rows = reduction index: lane (m, g) receives
+// X[KS*s + kk(g, e)][c0 + m]. ds_read_b64_tr_b16 works per group of 16 lanes: lane 4p + r of
+// the group receives element r of the 8 bytes addressed by lanes 4e + p (e = 0..3). So lane
+// (m, g) supplies the address of row 4g + m/4, columns c0 + 4(m%4) .. +3, and receives rows
+// 4g .. 4g+3 of column c0 + m.
+__device__ __forceinline__ bf16x4 ds_read_tr4(const bf16* p) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
+  const v4bf v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) v4bf*)(__attribute__((address_space(3))) void*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x8 frag_t(const bf16* X, int ld, int c0, int s, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+  const bf16* p = X + (32 * s + 4 * g + (m >> 2)) * ld + c0 + 4 * (m & 3);
+  const bf16x4 lo = ds_read_tr4(p);
+  const bf16x4 hi = ds_read_tr4(p + 16 * ld);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 frag_t(const float* X, int ld, int c0, int s, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+  const float* p = X + (16 * s + 4 * g) * ld + c0 + m;
+  return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
 }
 
 // Workgroup barrier that orders LDS accesses only: the fences are workgroup-scope and limited
