@@ -313,7 +313,8 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
 
   // Persistent workgroups: task = (chunk j of the segment, head h) = (task / H, task % H). The
   // raw inputs of the next task are loaded while the current one is computed (phases 2-6).
-  const int64_t ntask = min(p.E, (int64_t)p.header[0] - p.seg_begin) * H;
+  // (32-bit: a segment holds at most SEG_CHUNK_HEADS records)
+  const int ntask = (int)min(p.E, (int64_t)p.header[0] - p.seg_begin) * H;
   using raw4 = typename VecN<MT, 4>::vec;
   struct Raw {
     raw4 q[NG], k[NG], g[NG];
@@ -321,9 +322,10 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   };
   // Rows past the chunk's end load the last valid row again; they are zeroed after conversion
   // (q = k = 0, log alpha = 0, beta = 0 there), so every load is unconditional.
-  auto load_raw = [&](Raw& r, int64_t task) {
-    const Entry en = p.entries[p.seg_begin + task / H];
-    const int hh = (int)(task % H);
+  auto load_raw = [&](Raw& r, int task) {
+    const int jt = task / H;
+    const Entry en = p.entries[p.seg_begin + jt];
+    const int hh = task - jt * H;
     const int64_t tl = en.tok + min(t0, en.len - 1);
     const int64_t row = tl * (int64_t)H * K + (int64_t)hh * K + 4 * g0;
 #pragma unroll
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     }
     r.b = gb_[tl * H + hh];
   };
-  int64_t task = blockIdx.x;
+  int task = blockIdx.x;
   if (task >= ntask) return;
   Raw cur, nxt;
   load_raw(cur, task);
@@ -348,8 +350,8 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   const int m = lane & 15;
   const int g = lane >> 4;
   const int t = 16 * w + m;
-  const int64_t j = task / H;
-  const int h = (int)(task % H);
+  const int j = task / H;
+  const int h = task - j * H;
   const Entry en = p.entries[p.seg_begin + j];
   const int len = en.len;  // 1 .. CHUNK
   MT* recM = reinterpret_cast<MT*>(p.rec + (j * H + h) * p.rec_bytes);
@@ -501,7 +503,11 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     }
   }
   lds_barrier();
-  // A (row-scaled by beta, strictly lower) -> sA; -P (lower, upper blocks zero) -> sPnT, transposed
+  // A (row-scaled by beta, strictly lower) -> sA for the off-diagonal blocks; -P (lower, upper
+  // blocks zero) -> sPnT, transposed. The diagonal block A_ww stays in registers for phase 3(a).
+  f32x4 adiag = tA[0];
+#pragma unroll
+  for (int I = 1; I < NSUB; ++I) adiag = (I == w) ? tA[I] : adiag;
   {
     const int jj = 16 * w + m;
 #pragma unroll
@@ -509,8 +515,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * g + r;
-        const bool lowA = I > w || (I == w && jj < i);
-        if (I >= w) sA[i * L::LCF + jj] = lowA ? tA[I][r] * sBeta[i] : 0.f;
+        if (I > w) sA[i * L::LCF + jj] = tA[I][r] * sBeta[i];
       }
       // -P^T row jj, columns 16I + 4g .. +3
       f32x4 pn;
@@ -522,30 +527,40 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
       st4(sPnT + jj * L::LC + 16 * I + 4 * g, pn);
     }
   }
-  lds_barrier();
 
   // ---------------- phase 3: T = (I + A)^{-1}
-  // (a) Diagonal 16x16 blocks, one per wave, by forward substitution. Lane c keeps column c of
-  //     T_II in registers; the coefficients A_II[i][j] are broadcast from registers (readlane).
+  // (a) Diagonal 16x16 block of wave w by right-looking forward substitution: lane c keeps
+  //     column c of T_ww; once row j is final, column j of A_ww updates rows i > j
+  //     independently. A_ww is staged transposed in the wave's own diagonal block of sA, so
+  //     column j is one broadcast row read; T_ww then overwrites it.
   {
     float* Ab = sA + (16 * w) * L::LCF + 16 * w;
-    const f32x4 arow = *reinterpret_cast<const f32x4*>(Ab + (lane >> 2) * L::LCF + 4 * (lane & 3));
+    f32x4 a;  // lane (m, g): A_ww[4g + r][m] = A_ww^T[m][4g + r], beta-scaled, strictly lower
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * g + r;
+      a[r] = (m < i) ? adiag[r] * sBeta[16 * w + i] : 0.f;
+    }
+    *reinterpret_cast<f32x4*>(Ab + m * L::LCF + 4 * g) = a;
     const int c = lane & 15;
-    float tt[SUBBLK];
+    float x[SUBBLK];
 #pragma unroll
-    for (int i = 0; i < SUBBLK; ++i) {
-      float x0 = (i == c) ? 1.f : 0.f, x1 = 0.f;
+    for (int i = 0; i < SUBBLK; ++i) x[i] = (i == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int jj = 0; jj < i; ++jj) {
-        const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(arow[jj & 3]), 4 * i + (jj >> 2)));
-        if (jj & 1) x1 -= a * tt[jj];
-        else x0 -= a * tt[jj];
+    for (int j = 0; j < SUBBLK - 1; ++j) {
+      float col[SUBBLK];  // A_ww[.][j], the same in every lane
+#pragma unroll
+      for (int q = 0; q < SUBBLK / 4; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(Ab + j * L::LCF + 4 * q);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) col[4 * q + r] = v[r];
       }
-      tt[i] = x0 + x1;
+#pragma unroll
+      for (int i = j + 1; i < SUBBLK; ++i) x[i] -= col[i] * x[j];
     }
     if (lane < 16) {
 #pragma unroll
-      for (int i = 0; i < SUBBLK; ++i) Ab[i * L::LCF + c] = tt[i];
+      for (int i = 0; i < SUBBLK; ++i) Ab[i * L::LCF + c] = x[i];
     }
   }
   lds_barrier();
