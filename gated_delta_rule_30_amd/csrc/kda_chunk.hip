@@ -618,7 +618,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
       if (s < nsteps)
         acc = Mma<MT>::mma(frag_t(sKa, L::LDK, 16 * a, s, lane),
                            load_frag(sTb + (16 * b + m) * L::LC, s, g), acc);
-    st4(recM + R::oW + slot4<MT>(16 * b + m, 16 * a + 4 * g, K), acc);
+    st4(recM + R::oW + slot4<MT>(16 * b + m, 16 * a + 4 * g, K), -acc);  // the record holds -W
     st4(sW + (16 * b + m) * L::LDK + 16 * a + 4 * g, acc);  // W row 16b + m
   }
   lds_barrier();
@@ -657,29 +657,60 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
 }
 
 // ====================================================================== STATE kernel
-// One workgroup of 4 waves per (sequence run, head, V-slice of VS = 16*NVT columns). The state
-// GEMMs are computed transposed, with the chunk record as the B operand:
-//   U^T = V^T T'^T,  (P'V)^T = V^T P'^T,  (W S)^T = S^T W^T,  (Q_eff S)^T = S^T Q_eff^T,
-//   S'^T = S^T Diag(gamma) + Delta^T Ktilde
-// so the record's fragment slots feed the matrix cores as loaded, and a result tile holds four
-// consecutive V columns of one token (output, Delta) or of one key channel (state) per lane.
-// Wave w owns token tile w (U, P'V, W S, Q_eff S, Delta, O for every column tile) and
-// key-channel tiles w, w+4 of the state update, so each record byte is loaded once per
-// workgroup, straight into registers, one chunk ahead of its use.
-//
-// S, V and Delta sit in LDS row-major (rows = key channel or token, VS columns), written with
-// 8- and 16-byte stores straight from the result layout; the A fragments of S^T, V^T and
-// Delta^T are read back with the transposing LDS read (bf16) or four scalar reads (fp32).
-template <int K, int NVT, typename MT>
-struct StateLayout {
-  static constexpr int VS = 16 * NVT;
-  static constexpr int LD = VS + 16 / (int)sizeof(MT);  // row length in elements (16-byte aligned rows)
-  static constexpr size_t oS = 0;                                      // S: [K][VS]
-  static constexpr size_t oV = oS + (size_t)K * LD * sizeof(MT);       // V: [CHUNK][VS]
-  static constexpr size_t oD = oV + (size_t)CHUNK * LD * sizeof(MT);   // Delta: [CHUNK][VS]
-  static constexpr size_t oRun = oD + (size_t)CHUNK * LD * sizeof(MT);
-  static constexpr size_t total = oRun + (SEG_CHUNK_HEADS + 16) * 4;
-  static_assert((LD * sizeof(MT)) % 16 == 0, "row alignment");
+// One wave per (sequence run, head, 16-column slice of V). The columns of S evolve
+// independently, so a slice needs nothing from its neighbours: its state S [K x 16] (fp32),
+// U and Delta [CHUNK x 16] and its output tile all live in registers. Each product takes the
+// chunk record's fragments as loaded, and every result tile is already in the operand layout
+// of the product that consumes it (a 16-row result tile -- two for bf16 -- is a fragment
+// along its row index):
+//   Delta = U + (-W) S                       B operand: S as fragments along K
+//   O^T   = (P'V)^T + S^T Q_eff^T            A operand: the same S fragments
+//   S'    = Diag(gamma) S + Ktilde^T Delta   B operand: Delta as fragments along the tokens
+//   U = T'V and (P'V)^T of the next chunk    V through LDS and the transposing read
+// so the state path has no workgroup barrier and no LDS round trip. A chunk is NF matrix-core
+// operations, each consuming one record fragment; the fragments stream through a ring of D
+// registers, each load issued D operations ahead of its use. V and gamma pass through this
+// wave's own LDS (the transposing read and the per-lane gamma layout need it).
+template <int K, typename MT>
+struct StateShape {
+  static constexpr int KS = Mma<MT>::KS;
+  static constexpr int NKT = K / 16;      // key-channel tiles of S
+  static constexpr int NKS = K / KS;      // reduction steps over K
+  static constexpr int NTT = CHUNK / 16;  // token tiles
+  static constexpr int NTS = CHUNK / KS;  // reduction steps over tokens
+  // fragment (tile t, step s) of a lower-triangular CHUNK x CHUNK matrix may be nonzero
+  static constexpr bool tri_nz(int t, int s) { return KS * s < 16 * (t + 1); }
+  static constexpr int NTRI = [] {
+    int n = 0;
+    for (int s = 0; s < NTS; ++s)
+      for (int t = 0; t < NTT; ++t) n += tri_nz(t, s) ? 1 : 0;
+    return n;
+  }();
+  // i-th nonzero fragment, steps outer: tile and step
+  static constexpr int tri_t(int i) {
+    for (int s = 0; s < NTS; ++s)
+      for (int t = 0; t < NTT; ++t)
+        if (tri_nz(t, s) && i-- == 0) return t;
+    return 0;
+  }
+  static constexpr int tri_s(int i) {
+    for (int s = 0; s < NTS; ++s)
+      for (int t = 0; t < NTT; ++t)
+        if (tri_nz(t, s) && i-- == 0) return s;
+    return 0;
+  }
+  // the chunk's operations in issue order: W and Q_eff interleaved per K step (2*NTT per
+  // step), Ktilde^T (steps outer), then T' and P' of the next chunk
+  static constexpr int NA = 2 * NTT * NKS;
+  static constexpr int NB = NKT * NTS;
+  static constexpr int NF = NA + NB + 2 * NTRI;
+  static constexpr int DMAX = 60;  // ring length limit (4 registers per fragment)
+  static constexpr int D = [] {
+    for (int d = DMAX; d > 1; --d)
+      if (NF % d == 0) return d;
+    return 1;
+  }();
+  static constexpr int LDV = 16 + 16 / (int)sizeof(MT);  // LDS row of V (16-byte aligned)
 };
 
 struct StateParams {
@@ -696,47 +727,54 @@ struct StateParams {
   int H, V, n_slices;
   int64_t chains;  // slots * H
   const char* rec;
-  int64_t rec_bytes;
-  char* trash;  // >= 1 KB sink for output rows past a chunk's end
+  uint32_t rec_bytes;
+  uint32_t rec_buf_bytes;  // the whole record buffer (addressed with 32-bit offsets)
 };
 
-constexpr int STATE_THREADS = 256;
+constexpr int STATE_THREADS = 64;
 
-// What one wave loads for one chunk.
-template <int K, int NVT, typename MT>
-struct StateBundle {
-  using frag = typename Mma<MT>::frag;
-  static constexpr int KS = Mma<MT>::KS;
-  static constexpr int NKT = K / 16;
-  static constexpr int TPW = (NKT + 3) / 4;  // key-channel tiles per wave
-  static constexpr int VE = 4 * NVT;         // V elements per lane: one token, VE columns
-  frag tf[CHUNK / KS], pf[CHUNK / KS], wf[K / KS], qf[K / KS], kf[TPW][CHUNK / KS];
-  float gam[TPW];
-  typename VecN<MT, VE>::vec v;
-};
+// Raw buffer access (gfx9 descriptor: byte-addressed, range-checked against num_records: loads
+// past the end return zero and stores past the end are dropped).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <typename T>
+__device__ __forceinline__ T buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  static_assert(sizeof(T) == 16, "16-byte load");
+  return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ void buf_store(rsrc_t r, uint32_t voff, uint32_t soff, bf16x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, x), r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void buf_store(rsrc_t r, uint32_t voff, uint32_t soff, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, x), r, (int)voff, (int)soff, 0);
+}
+template <typename MT>
+__device__ __forceinline__ auto to_mt4(f32x4 x) {
+  if constexpr (std::is_same_v<MT, bf16>) return __builtin_convertvector(x, bf16x4);
+  else return x;
+}
 
-template <int K, int NVT, typename MT>
+template <int K, typename MT>
 __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_kernel(StateParams p) {
-  using SL = StateLayout<K, NVT, MT>;
+  using SH = StateShape<K, MT>;
   using R = Rec<K, MT>;
-  using B = StateBundle<K, NVT, MT>;
-  using frag = typename Mma<MT>::frag;
-  using vvec = typename VecN<MT, B::VE>::vec;
-  constexpr int KS = Mma<MT>::KS;
-  constexpr int VS = SL::VS;
-  constexpr int LD = SL::LD;
-  constexpr int NKT = B::NKT;
-  constexpr int TPW = B::TPW;
-  constexpr int VE = B::VE;
-  static_assert(SL::total <= 64 * 1024, "state LDS budget");
-  __shared__ __align__(16) char smem[SL::total];
-  MT* sS = reinterpret_cast<MT*>(smem + SL::oS);
-  MT* sV = reinterpret_cast<MT*>(smem + SL::oV);
-  MT* sD = reinterpret_cast<MT*>(smem + SL::oD);
-  int32_t* sRun = reinterpret_cast<int32_t*>(smem + SL::oRun);
-  int32_t* sLen = sRun + SEG_CHUNK_HEADS;
+  using M = Mma<MT>;
+  using frag = typename M::frag;
+  constexpr int KS = SH::KS, NKT = SH::NKT, NKS = SH::NKS, NTT = SH::NTT, NTS = SH::NTS;
+  constexpr int NA = SH::NA, NB = SH::NB, NTRI = SH::NTRI, NF = SH::NF, D = SH::D;
+  constexpr int LDV = SH::LDV;
+  constexpr int VL = 16 / (int)sizeof(MT);  // V elements per 16-byte load
+  constexpr int NVL = 16 / VL;              // 16-byte loads per token row of the slice
+  using vload = typename VecN<MT, VL>::vec;
+  static_assert(K % KS == 0 && K % 16 == 0, "K tiling");
+  __shared__ __align__(16) MT sV[CHUNK * LDV];
+  __shared__ __align__(16) float sG[K];
+  __shared__ int32_t sRun[SEG_CHUNK_HEADS + 16];
+  __shared__ int32_t sLen;
 
-  // XCD-aware decode: all V-slices of a chain share blockIdx % 8 (the same XCD / L2).
+  // XCD-aware decode: all slices of a chain share blockIdx % 8 (the same XCD / L2).
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
   const int rr = bid >> 3;
@@ -751,238 +789,230 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
   const int64_t seg_end = min(p.seg_begin + p.E, total);
   const int64_t e0 = p.seg_first[slot];
   const Entry en = p.entries[e0];
-  const int col0 = slice * VS;
-  const int tid = threadIdx.x;
-  const int w = wave_id();
+  const int col0 = slice * 16;
   const int lane = lane_id();
   const int m = lane & 15;
   const int g = lane >> 4;
 
-  // This workgroup's run: chunks d0, d0+1, ... of sequence en.seq inside the segment. Chunk
-  // d0+k is entry base[d0+k] + rank; the run ends at the sequence's end or the segment's end.
+  // This wave's run: chunks d0, d0+1, ... of sequence en.seq inside the segment. Chunk d0+k is
+  // entry base[d0+k] + rank; the run ends at the sequence's end or the segment's end.
   const int seq_start = en.tok - CHUNK * en.depth;
   const int nc = (en.end - seq_start + CHUNK - 1) / CHUNK;
   const int64_t rank = e0 - p.basetab[en.depth];
   const int kmax = (int)min((int64_t)(nc - en.depth), p.E);
-  if (tid == 0) sLen[0] = kmax;
+  if (lane == 0) sLen = kmax;
   __syncthreads();
-  for (int k = tid; k < kmax; k += STATE_THREADS) {
+  for (int k = lane; k < kmax; k += STATE_THREADS) {
     const int64_t ek = p.basetab[en.depth + k] + rank;
     sRun[k] = (int32_t)(ek - p.seg_begin);
-    if (ek >= seg_end) atomicMin(&sLen[0], k);
-  }
-
-  // State tiles (nt, kt = w + 4 tt): lane (m, g) holds S[16kt + m][16nt + 4g .. +3] of the slice.
-  const size_t sbase = ((size_t)en.seq * H + h) * (size_t)K * V + col0;
-  const float* src = (en.depth == 0) ? p.init_state : p.state;
-  f32x4 Sr[TPW][NVT];
-#pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    const int kt = w + 4 * tt;
-#pragma unroll
-    for (int nt = 0; nt < NVT; ++nt) {
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (kt < NKT && src != nullptr)
-        x = *reinterpret_cast<const f32x4*>(src + sbase + (size_t)(16 * kt + m) * V + 16 * nt + 4 * g);
-      Sr[tt][nt] = x;
-      if (kt < NKT) st4(sS + (16 * kt + m) * LD + 16 * nt + 4 * g, x);
-    }
+    if (ek >= seg_end) atomicMin(&sLen, k);
   }
   __syncthreads();
-  const int run = sLen[0];
+  const int run = sLen;
 
+  // state tile kt: lane (m, g) holds S[16kt + 4g + i][col0 + m], i = 0..3
+  const size_t sbase = ((size_t)en.seq * H + h) * (size_t)K * V + col0;
+  const float* src = (en.depth == 0) ? p.init_state : p.state;
+  f32x4 S[NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) {
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (src != nullptr) {
+      const float* ps = src + sbase + (size_t)(16 * kt + 4 * g) * V + m;
+      x = f32x4{ps[0], ps[V], ps[2 * V], ps[3 * V]};
+    }
+    S[kt] = x;
+  }
+
+  // Per-chunk descriptors cover the chunk's valid rows of V and of the output, so rows past
+  // the end load as zero (T' and P' are zero in those columns anyway) and are never stored.
+  const uint32_t rowb = (uint32_t)(H * V * (int)sizeof(MT));  // bytes between token rows
   const MT* gv = reinterpret_cast<const MT*>(p.v) + (int64_t)h * V + col0;
   MT* go = reinterpret_cast<MT*>(p.o) + (int64_t)h * V + col0;
-  MT* trash = reinterpret_cast<MT*>(p.trash) + 4 * lane;
-  const int64_t vrow = (int64_t)H * V;
-  const char* rec_h = p.rec + (int64_t)h * p.rec_bytes;
-  const int64_t rec_stride = (int64_t)H * p.rec_bytes;
   auto tok_of = [&](int k) { return seq_start + CHUNK * (en.depth + k); };
   auto len_of = [&](int k) { return min(CHUNK, en.end - tok_of(k)); };
-
-  // Loop-invariant per-lane byte offsets inside a record; a chunk's loads then use one
-  // wave-uniform base address plus these offsets (reduction steps are 1 KB apart).
-  constexpr uint32_t STEP = 64 * 16;
-  const uint32_t lo_t = (uint32_t)((R::oTb + slot_elem<MT>(w, 0, lane, CHUNK)) * sizeof(MT));
-  const uint32_t lo_p = (uint32_t)((R::oPb + slot_elem<MT>(w, 0, lane, CHUNK)) * sizeof(MT));
-  const uint32_t lo_w = (uint32_t)((R::oW + slot_elem<MT>(w, 0, lane, K)) * sizeof(MT));
-  const uint32_t lo_q = (uint32_t)((R::oQ + slot_elem<MT>(w, 0, lane, K)) * sizeof(MT));
-  uint32_t lo_k[TPW], lo_g[TPW];
-#pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    const int kt = min(w + 4 * tt, NKT - 1);
-    lo_k[tt] = (uint32_t)((R::oKt + slot_elem<MT>(kt, 0, lane, CHUNK)) * sizeof(MT));
-    lo_g[tt] = (uint32_t)(R::oGamBytes + (16 * kt + m) * 4);
-  }
-  auto ldf = [](const char* base, uint32_t off) -> frag { return *reinterpret_cast<const frag*>(base + off); };
-
-  // Loads of chunk k (clamped to the run's last chunk; a duplicate load past the end is never
-  // used). The V row of a token past the chunk's end repeats the last valid row and is zeroed
-  // when staged, so every load is unconditional. Load i of the record part is piece(b, rc, i).
-  constexpr int NTS = CHUNK / KS, NKS = K / KS;
-  constexpr int NLOADS = 2 * NTS + 2 * NKS + TPW * (NTS + 1);
-  auto rec_of = [&](int k) {
+  auto rows_rsrc = [&](const MT* base, int k) {
     const int kk = min(k, run - 1);
-    const int ri = __builtin_amdgcn_readfirstlane(sRun[kk]);  // uniform record index
-    return rec_h + (int64_t)ri * rec_stride;
+    return make_rsrc(base + (int64_t)tok_of(kk) * (H * V), (uint32_t)len_of(kk) * rowb);
   };
-  auto load_v = [&](B& b, int k) {
-    const int kk = min(k, run - 1);
-    const int tok = tok_of(kk), len = len_of(kk);
-    b.v = *reinterpret_cast<const vvec*>(gv + ((int64_t)tok + min(lane, len - 1)) * vrow + VE * w);
+  const uint32_t v_voff = (uint32_t)lane * rowb;                          // lane = token
+  const uint32_t o_voff = (uint32_t)m * rowb + 4u * g * (uint32_t)sizeof(MT);  // token m of a tile
+
+  // records: one descriptor over the buffer, 32-bit offsets; chunk k of the run (clamped to the
+  // run's last chunk -- a load past the end is never used)
+  const rsrc_t rrec = make_rsrc(p.rec, p.rec_buf_bytes);
+  const uint32_t rec_h = (uint32_t)h * p.rec_bytes;
+  const uint32_t rec_stride = (uint32_t)H * p.rec_bytes;
+  auto rec_off = [&](int ri) { return rec_h + (uint32_t)ri * rec_stride; };
+  const uint32_t lo = 16u * (uint32_t)lane;  // a fragment slot is 64 lanes x 16 bytes
+  auto ldf = [&](uint32_t rc, uint32_t off) -> frag {
+    return buf_load16<frag>(rrec, lo + (off & 4095u), rc + (off & ~4095u));
   };
-  auto piece = [&](B& b, const char* rc, auto I) {
-    constexpr int i = decltype(I)::value;
-    if constexpr (i < NTS) {
-      b.tf[i] = ldf(rc, lo_t + STEP * i);
-    } else if constexpr (i < 2 * NTS) {
-      b.pf[i - NTS] = ldf(rc, lo_p + STEP * (i - NTS));
-    } else if constexpr (i < 2 * NTS + NKS) {
-      b.wf[i - 2 * NTS] = ldf(rc, lo_w + STEP * (i - 2 * NTS));
-    } else if constexpr (i < 2 * NTS + 2 * NKS) {
-      b.qf[i - 2 * NTS - NKS] = ldf(rc, lo_q + STEP * (i - 2 * NTS - NKS));
+
+  // byte offset (without the lane part) of operation j's fragment in its record
+  auto frag_off = [](auto J) constexpr -> uint32_t {
+    constexpr int j = decltype(J)::value;
+    constexpr uint32_t SLOT = 64 * 16;
+    if constexpr (j < NA) {
+      constexpr int s = j / (2 * NTT), r = j % (2 * NTT), tt = r % NTT;
+      constexpr size_t base = (r < NTT ? R::oW : R::oQ) * sizeof(MT);
+      return (uint32_t)(base + (size_t)(tt * NKS + s) * SLOT);
+    } else if constexpr (j < NA + NB) {
+      constexpr int jj = j - NA, s = jj / NKT, kt = jj % NKT;
+      return (uint32_t)(R::oKt * sizeof(MT) + (size_t)(kt * NTS + s) * SLOT);
     } else {
-      constexpr int j = i - 2 * NTS - 2 * NKS, tt = j / (NTS + 1), s = j % (NTS + 1);
-      if constexpr (s < NTS) b.kf[tt][s] = ldf(rc, lo_k[tt] + STEP * s);
-      else b.gam[tt] = *reinterpret_cast<const float*>(rc + lo_g[tt]);
+      constexpr int jj = (j - NA - NB) % NTRI;
+      constexpr size_t base = (j - NA - NB < NTRI ? R::oTb : R::oPb) * sizeof(MT);
+      return (uint32_t)(base + (size_t)(SH::tri_t(jj) * NTS + SH::tri_s(jj)) * SLOT);
     }
   };
-  auto issue_all = [&](B& b, int k) {
-    load_v(b, k);
-    __builtin_amdgcn_sched_barrier(0);
-    const char* rc = rec_of(k);
-    static_for<0, NLOADS>([&](auto I) { piece(b, rc, I); });
-  };
 
-  // V of chunk k into LDS: lane = token, wave w = columns VE*w .. +VE-1
-  auto stage = [&](const B& b, int k) {
-    const bool valid = lane < len_of(k);
-    vvec x = b.v;
+  // V rows of chunk k (lane = token) and gamma of chunk k
+  auto load_v = [&](int k, vload (&x)[NVL]) {
+    const rsrc_t r = rows_rsrc(gv, k);
 #pragma unroll
-    for (int i = 0; i < VE; ++i) x[i] = valid ? x[i] : from_f32<MT>(0.f);
-    *reinterpret_cast<vvec*>(sV + lane * LD + VE * w) = x;
+    for (int i = 0; i < NVL; ++i) x[i] = buf_load16<vload>(r, v_voff + 16u * i, 0);
   };
+  auto stage_v = [&](const vload (&x)[NVL]) {
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) *reinterpret_cast<vload*>(sV + lane * LDV + VL * i) = x[i];
+  };
+  constexpr int GPL = (K + 63) / 64;  // gamma values per lane (1 or 2)
+  using gvec = std::conditional_t<GPL == 2, f32x2, float>;
+  const uint32_t g_voff = 4u * (uint32_t)min(GPL * lane, K - GPL);
+  auto load_g = [&](uint32_t rc) -> gvec {
+    if constexpr (GPL == 2)
+      return __builtin_bit_cast(gvec, __builtin_amdgcn_raw_buffer_load_b64(rrec, (int)(g_voff + R::oGamBytes % 4096), (int)(rc + R::oGamBytes / 4096 * 4096), 0));
+    else
+      return __builtin_bit_cast(gvec, __builtin_amdgcn_raw_buffer_load_b32(rrec, (int)(g_voff + R::oGamBytes % 4096), (int)(rc + R::oGamBytes / 4096 * 4096), 0));
+  };
+  auto stage_g = [&](gvec x) {
+    if (GPL * lane < K) *reinterpret_cast<gvec*>(sG + GPL * lane) = x;
+  };
+  auto rec_index = [&](int k) { return __builtin_amdgcn_readfirstlane(sRun[min(k, run - 1)]); };
 
-  // Chunk k for token tile w: U, P'V, W S, Q_eff S (Delta to LDS, O to memory), with the loads
-  // of chunk k+1 spread between the matrix operations. The loads go through the CU's
-  // vector-memory path at about 64 B per clock and a wave waits at a load until that path
-  // accepts it, so one load follows each MFMA instead of all loads going out in one burst; the
-  // scheduling barriers keep that order. Branch-free: the record holds zeros above the
-  // diagonal of T' and P', so every reduction step runs.
-  // MFMA j: reduction step s = j / (2 NVT) of U, P'V (j < NMF_T), then of W S, Q_eff S,
-  // round-robin over the independent accumulators.
-  constexpr int NMF_T = 2 * NVT * NTS, NMF_K = 2 * NVT * NKS, NMF = NMF_T + NMF_K;
-  constexpr int NLC = 2 * NTS + 2 * NKS;  // pieces loaded during compute: T', P', W, Q_eff
-  constexpr int LSTRIDE = NMF / NLC;      // MFMAs per piece
-  static_assert(LSTRIDE >= 1, "one load per MFMA at most");
-  f32x4 Opend[NVT];
-  MT* Odst[NVT];
-  auto compute = [&](const B& b, B& nxt, int k) {
-    const int tok = tok_of(k), len = len_of(k);
-    const int t = 16 * w + m;
-    // fragments of reduction step s: V^T (s < NTS) and S^T (s < NKS), read one step ahead
-    frag vf[2][NVT], sf[2][NVT];
+  // ---- prologue: U and (P'V)^T of chunk 0, the ring for chunk 0, gamma of chunk 0
+  uint32_t rc0 = rec_off(rec_index(0));
+  uint32_t rc1 = rec_off(rec_index(1));
+  uint32_t rc2 = rec_off(rec_index(2));
+  f32x4 U[NTT], O[NTT];
+  frag Vf[NTS];
+  {
+    vload vx[NVL];
+    load_v(0, vx);
+    stage_v(vx);
 #pragma unroll
-    for (int nt = 0; nt < NVT; ++nt) {
-      vf[0][nt] = frag_t(sV, LD, 16 * nt, 0, lane);
-      sf[0][nt] = frag_t(sS, LD, 16 * nt, 0, lane);
-    }
-    load_v(nxt, k + 1);
-    const char* rc = rec_of(k + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 U[NVT], Ol[NVT], Y[NVT], Z[NVT];
+    for (int s = 0; s < NTS; ++s) Vf[s] = frag_t(sV, LDV, 0, s, lane);
 #pragma unroll
-    for (int nt = 0; nt < NVT; ++nt) U[nt] = Ol[nt] = Y[nt] = Z[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    static_for<0, NMF>([&](auto J) {
-      constexpr int j = decltype(J)::value;
-      constexpr int s = j < NMF_T ? j / (2 * NVT) : (j - NMF_T) / (2 * NVT);
-      constexpr bool first_of_step = (j < NMF_T ? j % (2 * NVT) : (j - NMF_T) % (2 * NVT)) == 0;
-      if constexpr (first_of_step && j < NMF_T && s + 1 < NTS) {
-#pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) vf[(s + 1) & 1][nt] = frag_t(sV, LD, 16 * nt, s + 1, lane);
-      }
-      if constexpr (first_of_step && j >= NMF_T && s + 1 < NKS) {
-#pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) sf[(s + 1) & 1][nt] = frag_t(sS, LD, 16 * nt, s + 1, lane);
-      }
-      if constexpr (j < NMF_T) {
-        constexpr int nt = (j % (2 * NVT)) / 2;
-        if constexpr (j % 2 == 0) U[nt] = Mma<MT>::mma(vf[s & 1][nt], b.tf[s], U[nt]);
-        else Ol[nt] = Mma<MT>::mma(vf[s & 1][nt], b.pf[s], Ol[nt]);
-      } else {
-        constexpr int jj = j - NMF_T, nt = (jj % (2 * NVT)) / 2;
-        if constexpr (jj % 2 == 0) Y[nt] = Mma<MT>::mma(sf[s & 1][nt], b.wf[s], Y[nt]);
-        else Z[nt] = Mma<MT>::mma(sf[s & 1][nt], b.qf[s], Z[nt]);
-      }
-      if constexpr (j % LSTRIDE == 0 && j / LSTRIDE < NLC)
-        piece(nxt, rc, std::integral_constant<int, j / LSTRIDE>());
-      __builtin_amdgcn_sched_barrier(0);
+    for (int tt = 0; tt < NTT; ++tt) U[tt] = O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    static_for<0, NTRI>([&](auto I) {
+      constexpr int i = decltype(I)::value, tt = SH::tri_t(i), s = SH::tri_s(i);
+      U[tt] = M::mma(ldf(rc0, frag_off(std::integral_constant<int, NA + NB + i>())), Vf[s], U[tt]);
+      O[tt] = M::mma(Vf[s], ldf(rc0, frag_off(std::integral_constant<int, NA + NB + NTRI + i>())), O[tt]);
     });
-#pragma unroll
-    for (int nt = 0; nt < NVT; ++nt) {
-      st4(sD + t * LD + 16 * nt + 4 * g, U[nt] - Y[nt]);
-      Opend[nt] = Ol[nt] + Z[nt];
-      Odst[nt] = t < len ? go + ((int64_t)tok + t) * vrow + 16 * nt + 4 * g : trash;
-    }
-  };
+  }
+  // gamma first, then the ring: in the loop gamma is waited for long after the loads behind it
+  gvec gnext = load_g(rc0);
+  __builtin_amdgcn_sched_barrier(0);
+  frag ring[D];
+  static_for<0, D>([&](auto J) {
+    constexpr int j = decltype(J)::value;
+    ring[j] = ldf(j < NA + NB ? rc0 : rc1, frag_off(J));
+  });
+  __builtin_amdgcn_sched_barrier(0);
+  int ri_pre = sRun[min(3, run - 1)];  // record index of chunk k + 3, read one chunk ahead
+  vload vx[NVL];                         // V rows of chunk k + 1, loaded a chunk ahead
+  load_v(1, vx);
 
-  // S'^T = S^T Diag(gamma) + Delta^T Ktilde for key-channel tiles w, w+4
-  auto update = [&](const B& b, B& nxt, int k) {
-    {
-      const char* rc = rec_of(k + 1);
-      static_for<NLC, NLOADS>([&](auto I) { piece(nxt, rc, I); });
-    }
-    frag df[NVT][NTS];
+  for (int k = 0; k < run; ++k) {
+    // records of chunks k, k+1, k+2 (rc0 .. rc2 on entry), and k+3 for the next iteration
+    const uint32_t rc3 = rec_off(__builtin_amdgcn_readfirstlane(ri_pre));
+    ri_pre = sRun[min(k + 4, run - 1)];
+    const rsrc_t ro = rows_rsrc(go, k);
+    const gvec gcur = gnext;
+    gnext = load_g(rc1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    frag Sb[NKS], Db[NTS];
+    f32x4 gam[NKT];
+    static_for<0, NF>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      // --- work placed before operation j
+      if constexpr (j < NA && j % (2 * NTT) == 0) {
+        constexpr int s = j / (2 * NTT);
+        if constexpr (KS == 32) Sb[s] = frag_from_acc(S[2 * s], S[2 * s + 1], MT());
+        else Sb[s] = S[s];
+      }
+      // gamma of chunk k into LDS, then per key-channel tile: read gamma GLEAD operations ahead
+      // and scale S (every S fragment is formed by then) as the update's accumulator
+      constexpr int GLEAD = 6;
+      static_assert(NA > GLEAD, "gamma lead");
+      if constexpr (j == NA - GLEAD - 1) stage_g(gcur);
+      static_for<0, NKT>([&](auto KT) {
+        constexpr int kt = decltype(KT)::value;
+        if constexpr (j == NA + kt - GLEAD) gam[kt] = *reinterpret_cast<const f32x4*>(sG + 16 * kt + 4 * g);
+        if constexpr (j == NA + kt) S[kt] *= gam[kt];
+      });
+      if constexpr (j == NA) {
 #pragma unroll
-    for (int nt = 0; nt < NVT; ++nt)
-#pragma unroll
-      for (int s = 0; s < NTS; ++s) df[nt][s] = frag_t(sD, LD, 16 * nt, s, lane);
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-      const int kt = w + 4 * tt;
-      if (kt < NKT) {
-#pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) {
-          f32x4 acc = Sr[tt][nt] * b.gam[tt];
-#pragma unroll
-          for (int s = 0; s < NTS; ++s) acc = Mma<MT>::mma(df[nt][s], b.kf[tt][s], acc);
-          Sr[tt][nt] = acc;
-          st4(sS + (16 * kt + m) * LD + 16 * nt + 4 * g, acc);
+        for (int s = 0; s < NTS; ++s) {
+          if constexpr (KS == 32) Db[s] = frag_from_acc(U[2 * s], U[2 * s + 1], MT());
+          else Db[s] = U[s];
         }
       }
-    }
-    // the output rows of chunk k leave after the update, behind the loads issued above
+      if constexpr (j == NA + NB / 2) {
+        // output rows of chunk k, then V of chunk k+1 into LDS and its fragments
 #pragma unroll
-    for (int nt = 0; nt < NVT; ++nt) st4(Odst[nt], Opend[nt]);
-  };
-
-  // Two register bundles in turn: chunk k+1's loads are issued while chunk k is computed. The
-  // second half differs from the first (an extra scheduling barrier) so that the compiler keeps
-  // both halves instead of folding them into one with register copies between bundles.
-  auto chunk = [&](const B& cur, B& nxt, int k, auto PAR) {
-    stage(cur, k);
-    lds_barrier();  // V and S of chunk k ready
-    compute(cur, nxt, k);
-    if constexpr (decltype(PAR)::value) __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();  // Delta complete; S and V no longer read
-    update(cur, nxt, k);
-  };
-  B b0, b1;
-  issue_all(b0, 0);
-  for (int k = 0; k < run; k += 2) {
-    chunk(b0, b1, k, std::false_type());
-    if (k + 1 >= run) break;
-    chunk(b1, b0, k + 1, std::true_type());
+        for (int tt = 0; tt < NTT; ++tt) buf_store(ro, o_voff, (uint32_t)(16 * tt) * rowb, to_mt4<MT>(O[tt]));
+        stage_v(vx);
+#pragma unroll
+        for (int s = 0; s < NTS; ++s) Vf[s] = frag_t(sV, LDV, 0, s, lane);
+      }
+      if constexpr (j == NA + NB) {
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) U[tt] = O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        load_v(k + 2, vx);
+      }
+      // --- operation j
+      const frag f = ring[j % D];
+      if constexpr (j < NA) {
+        constexpr int s = j / (2 * NTT), r = j % (2 * NTT), tt = r % NTT;
+        if constexpr (r < NTT) U[tt] = M::mma(f, Sb[s], U[tt]);  // U - W S
+        else O[tt] = M::mma(Sb[s], f, O[tt]);                    // + S^T Q_eff^T
+      } else if constexpr (j < NA + NB) {
+        constexpr int jj = j - NA, s = jj / NKT, kt = jj % NKT;
+        S[kt] = M::mma(f, Db[s], S[kt]);  // + Ktilde^T Delta
+      } else if constexpr (j < NA + NB + NTRI) {
+        constexpr int i = j - NA - NB;
+        U[SH::tri_t(i)] = M::mma(f, Vf[SH::tri_s(i)], U[SH::tri_t(i)]);  // T'V, next chunk
+      } else {
+        constexpr int i = j - NA - NB - NTRI;
+        O[SH::tri_t(i)] = M::mma(Vf[SH::tri_s(i)], f, O[SH::tri_t(i)]);  // (P'V)^T, next chunk
+      }
+      // --- refill: operation j + D of the stream
+      {
+        constexpr int jn = j + D;
+        if constexpr (jn < NF) {
+          ring[j % D] = ldf(jn < NA + NB ? rc0 : rc1, frag_off(std::integral_constant<int, jn>()));
+        } else {
+          constexpr int jw = jn - NF;
+          ring[j % D] = ldf(jw < NA + NB ? rc1 : rc2, frag_off(std::integral_constant<int, jw>()));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    rc0 = rc1;
+    rc1 = rc2;
+    rc2 = rc3;
   }
 
 #pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    const int kt = w + 4 * tt;
-    if (kt < NKT) {
-#pragma unroll
-      for (int nt = 0; nt < NVT; ++nt)
-        *reinterpret_cast<f32x4*>(p.state + sbase + (size_t)(16 * kt + m) * V + 16 * nt + 4 * g) = Sr[tt][nt];
-    }
+  for (int kt = 0; kt < NKT; ++kt) {
+    float* ps = p.state + sbase + (size_t)(16 * kt + 4 * g) * V + m;
+    ps[0] = S[kt][0];
+    ps[V] = S[kt][1];
+    ps[2 * V] = S[kt][2];
+    ps[3 * V] = S[kt][3];
   }
 }
 
@@ -1000,9 +1030,9 @@ bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan
   p->num_segs = ub > 0 ? (ub + E - 1) / E : 0;
   p->slots = N < E ? N : E;
   p->rec_bytes = ((3LL * CHUNK * K + 2LL * CHUNK * CHUNK) * es + 4LL * K + 1023) / 1024 * 1024;
-  // V split: slices of 32 columns, one 4-wave workgroup each
-  p->n_slices = V / 32;
-  p->vs = 32;
+  // V split: slices of 16 columns, one wave each
+  p->n_slices = V / 16;
+  p->vs = 16;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = 0;
   p->off_header = off;
@@ -1017,11 +1047,11 @@ bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan
   off += al((size_t)p->num_segs * 4);
   p->off_state = off;
   off += al((size_t)N * H * K * V * 4);
-  p->off_sink = off;  // 1 KB sink for output rows past a chunk's end
-  off += 1024;
   p->off_rec = off;
   p->rec_buf_bytes = (size_t)E * H * p->rec_bytes;
   off += p->rec_buf_bytes;
+  // the state kernel addresses the record buffer and a chunk's rows with 32-bit offsets
+  if (p->rec_buf_bytes >= (1ull << 31) || (int64_t)CHUNK * H * V * es >= (1ll << 31)) return false;
   p->total_bytes = off;
   return true;
 }
@@ -1066,10 +1096,10 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
     const char* rec = ws + pl.off_rec;
     StateParams sp{a.v, a.o, a.init_state, run_state, entries, header, basetab,
                    seg_first + s * pl.slots, seg_count + s, s * pl.seg_entries, pl.seg_entries,
-                   a.num_heads, a.dv, pl.n_slices, chains, rec, pl.rec_bytes,
-                   ws + pl.off_sink};
-    if (pl.vs != 32) return false;
-    hipLaunchKernelGGL((state_kernel<K, 2, MT>), sgrid, dim3(STATE_THREADS), 0, q, sp);
+                   a.num_heads, a.dv, pl.n_slices, chains, rec, (uint32_t)pl.rec_bytes,
+                   (uint32_t)pl.rec_buf_bytes};
+    if (pl.vs != 16) return false;
+    hipLaunchKernelGGL((state_kernel<K, MT>), sgrid, dim3(STATE_THREADS), 0, q, sp);
     return true;
   };
 

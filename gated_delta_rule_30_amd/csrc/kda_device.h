@@ -11,6 +11,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) unsigned v2u32;
+typedef __attribute__((ext_vector_type(4))) unsigned v4u32;
 
 // ------------------------------------------------------------------ scalar conversions
 template <typename T> __device__ __forceinline__ float to_f32(T x);

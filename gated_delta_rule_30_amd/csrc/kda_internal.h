@@ -47,7 +47,7 @@ struct ChunkPlan {
   int n_slices;         // V split into n_slices slices of vs columns
   int vs;
   // workspace offsets (bytes)
-  size_t off_header, off_entries, off_basetab, off_seg_first, off_seg_count, off_state, off_sink,
+  size_t off_header, off_entries, off_basetab, off_seg_first, off_seg_count, off_state,
       off_rec, rec_buf_bytes;
   size_t total_bytes;
 };
