@@ -18,8 +18,8 @@
 // GEMMs) is independent per (chunk, head) and runs in the chunk-parallel PREP kernel, which
 // writes one compact record per (chunk, head): W, Q_eff, Ktilde^T, T', P' (bf16 MFMA
 // fragments) and e^{b_last}. The STATE kernel walks each sequence's chunks in order, one
-// workgroup per (sequence, head, V-slice) -- the columns of S evolve independently, so the
-// V split is exact -- and does only U = T'V, O = Q_eff S + P'V, Delta = U - W S and the
+// wave per (sequence, head, 16-column V-slice) -- the columns of S evolve independently, so
+// the V split is exact -- and does only U = T'V, O = Q_eff S + P'V, Delta = U - W S and the
 // update S' = Diag(gamma) S + Ktilde^T Delta on the matrix cores. The sequence is processed
 // in segments of about SEG_CHUNK_HEADS records so the record buffer stays resident in the
 // Infinity Cache between the two kernels.
