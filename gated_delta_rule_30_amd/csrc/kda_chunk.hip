@@ -9,17 +9,16 @@
 //   T'    = T diag(beta),  W = T' (K * e^{b}),  U = T' V               WY factors
 //   P_ij  = sum_c q_ic k_jc e^{b_ic - b_jc}           (j <= i)       QGammaK^T block
 //   Delta = U - W S                                                    delta corrections
-//   O     = (Q * e^{b}) S + P Delta = Q_eff S + P' V,  Q_eff = Q*e^{b} - P W,  P' = P T'
+//   O     = (Q * e^{b}) S + P Delta                                   read after the write
 //   S'    = Diag(e^{b_last}) S + (K * e^{b_last - b})^T Delta          state passing
 // The WY / UT form of the chunk's rank-1 updates and the triangular solve follow the pages'
 // description ("Kimi Linear" explainer, "WY Representation"; wpnews article, DPLR paragraph).
 //
-// Execution. Work that does not depend on the state (everything but the three state
-// GEMMs) is independent per (chunk, head) and runs in the chunk-parallel PREP kernel, which
-// writes one compact record per (chunk, head): W, Q_eff, Ktilde^T, T', P' (bf16 MFMA
-// fragments) and e^{b_last}. The STATE kernel walks each sequence's chunks in order, one
+// Execution. Work that does not depend on the state is independent per (chunk, head) and runs
+// in the chunk-parallel PREP kernel, which writes one compact record per (chunk, head): -W,
+// Qe = Q * e^{b}, Ktilde^T, T', P (bf16 MFMA fragments) and e^{b_last}. The STATE kernel walks each sequence's chunks in order, one
 // wave per (sequence, head, 16-column V-slice) -- the columns of S evolve independently, so
-// the V split is exact -- and does only U = T'V, O = Q_eff S + P'V, Delta = U - W S and the
+// the V split is exact -- and does only U = T'V, Delta = U - W S, O = Qe S + P Delta and the
 // update S' = Diag(gamma) S + Ktilde^T Delta on the matrix cores. The sequence is processed
 // in segments of about SEG_CHUNK_HEADS records so the record buffer stays resident in the
 // Infinity Cache between the two kernels.
@@ -293,7 +292,6 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   MT* sTb = reinterpret_cast<MT*>(smem + L::oTb);
   MT* sKt = reinterpret_cast<MT*>(smem + L::oR1);
   float* sA = reinterpret_cast<float*>(smem + L::oR1);
-  MT* sW = reinterpret_cast<MT*>(smem + L::oR1);
   MT* sKa = reinterpret_cast<MT*>(smem + L::oKa);
   float* sDel = reinterpret_cast<float*>(smem + L::oP);
   float* sD = sDel + NSUB * K;
@@ -322,7 +320,8 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   };
   // Rows past the chunk's end load the last valid row again; they are zeroed after conversion
   // (q = k = 0, log alpha = 0, beta = 0 there), so every load is unconditional.
-  auto load_raw = [&](Raw& r, int task) {
+  // part 0: q; part 1: k; part 2: log alpha and beta; part -1: everything
+  auto load_raw = [&](Raw& r, int task, int part) {
     const int jt = task / H;
     const Entry en = p.entries[p.seg_begin + jt];
     const int hh = task - jt * H;
@@ -330,16 +329,16 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     const int64_t row = tl * (int64_t)H * K + (int64_t)hh * K + 4 * g0;
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
-      r.q[u] = *reinterpret_cast<const raw4*>(gq_ + row + 16 * u);
-      r.k[u] = *reinterpret_cast<const raw4*>(gk_ + row + 16 * u);
-      r.g[u] = *reinterpret_cast<const raw4*>(gg_ + row + 16 * u);
+      if (part < 0 || part == 0) r.q[u] = *reinterpret_cast<const raw4*>(gq_ + row + 16 * u);
+      if (part < 0 || part == 1) r.k[u] = *reinterpret_cast<const raw4*>(gk_ + row + 16 * u);
+      if (part < 0 || part == 2) r.g[u] = *reinterpret_cast<const raw4*>(gg_ + row + 16 * u);
     }
-    r.b = gb_[tl * H + hh];
+    if (part < 0 || part == 2) r.b = gb_[tl * H + hh];
   };
   int task = blockIdx.x;
   if (task >= ntask) return;
   Raw cur, nxt;
-  load_raw(cur, task);
+  load_raw(cur, task, -1);
 #pragma clang loop unroll(disable)
   for (; task < ntask; task += gridDim.x) {
   // Lane-dependent addresses are recomputed in every iteration: without the opaque copy the
@@ -359,9 +358,10 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   const bool valid = t < len;
 
   // ---------------- phase 1: the token's q, k and log2 alpha (fp32). Past the chunk's end only
-  // log alpha (and beta) are zeroed: the q and k rows there repeat the last valid token and are
-  // never used -- beta = 0 zeroes their rows of A, their columns of T' and P', and so their
-  // rows of W and Delta -- while log alpha = 0 keeps the decay products of the valid tokens.
+  // log alpha (and beta) are zeroed: the q and k rows there repeat the last valid token and
+  // have no effect -- beta = 0 zeroes their rows of A and their rows and columns of T', and so
+  // their rows of W and Delta (their columns of P meet only those zero rows of Delta) -- while
+  // log alpha = 0 keeps the decay products of the valid tokens.
   float qv[NG][4], kv[NG][4], lv[NG][4];
 #pragma unroll
   for (int u = 0; u < NG; ++u)
@@ -429,10 +429,10 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   // decayed operands of the lane's token:
   //   Q^ = q e^{b_t - e_{w-1}}, K^ = k e^{b_t - e_{w-1}}  (<= 1 factors, MFMA row operands)
   //   kc = k e^{e_w - b_t}                                (<= 1, column operand, registers)
-  //   qe = q e^{b_t}  (registers, for Q_eff),  Ka = k e^{b_t},  Kt = k e^{b_last - b_t}
-  float qe[NG][4], kc[NG][4];
+  //   Qe = q e^{b_t} (record, from registers),  Ka = k e^{b_t},  Kt = k e^{b_last - b_t}
+  float kc[NG][4];
   {
-    f32x4 qh[NG], kh[NG];
+    f32x4 qh[NG], kh[NG], qe[NG];
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
       const f32x4 ex = *reinterpret_cast<const f32x4*>(sEx + w * K + 16 * u + 4 * g);
@@ -457,6 +457,8 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
       const size_t slot = ((size_t)(w * NS + s) * 64 + lane) * EPL;
       *reinterpret_cast<frag*>(sQh + slot) = to_frag(qh[GPS * s], qh[GPS * s + GPS - 1], MT());
       *reinterpret_cast<frag*>(sKh + slot) = to_frag(kh[GPS * s], kh[GPS * s + GPS - 1], MT());
+      // this lane's slot of Qe's row tile w, step s is exactly its own token and channels
+      *reinterpret_cast<frag*>(recM + R::oQ + slot) = to_frag(qe[GPS * s], qe[GPS * s + GPS - 1], MT());
     }
   }
   lds_barrier();
@@ -473,8 +475,10 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     }
   }
 
-  // the next task's inputs load during phases 2-6 (phase 1's fp32 copies are dead by now)
-  load_raw(nxt, task + gridDim.x < ntask ? task + gridDim.x : task);
+  // the next task's inputs load during phases 2-5 (phase 1's fp32 copies are dead by now)
+  // (in three parts, so that the loads enter the memory pipeline in smaller bursts)
+  const int ntsk = task + gridDim.x < ntask ? task + gridDim.x : task;
+  load_raw(nxt, ntsk, 0);
 
   // ---------------- phase 2: blocks (I, w), I >= w, of A and P. The column operand (token
   // block w, scaled per channel by D_{Iw}) is this wave's own kc; the row operands are read as
@@ -503,8 +507,9 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     }
   }
   lds_barrier();
-  // A (row-scaled by beta, strictly lower) -> sA for the off-diagonal blocks; -P (lower, upper
-  // blocks zero) -> sPnT, transposed. The diagonal block A_ww stays in registers for phase 3(a).
+  // A (row-scaled by beta, strictly lower) -> sA for the off-diagonal blocks; P (lower with the
+  // diagonal, zero above) -> sPnT, transposed. The diagonal block A_ww stays in registers for
+  // phase 3(a).
   f32x4 adiag = tA[0];
 #pragma unroll
   for (int I = 1; I < NSUB; ++I) adiag = (I == w) ? tA[I] : adiag;
@@ -517,16 +522,18 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
         const int i = 16 * I + 4 * g + r;
         if (I > w) sA[i * L::LCF + jj] = tA[I][r] * sBeta[i];
       }
-      // -P^T row jj, columns 16I + 4g .. +3
+      // P^T row jj, columns 16I + 4g .. +3
       f32x4 pn;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * g + r;
-        pn[r] = (I > w || (I == w && jj <= i)) ? -tP[I][r] : 0.f;
+        pn[r] = (I > w || (I == w && jj <= i)) ? tP[I][r] : 0.f;
       }
       st4(sPnT + jj * L::LC + 16 * I + 4 * g, pn);
     }
   }
+
+  load_raw(nxt, ntsk, 1);
 
   // ---------------- phase 3: T = (I + A)^{-1}
   // (a) Diagonal 16x16 block of wave w by right-looking forward substitution: lane c keeps
@@ -567,7 +574,19 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   // (b) Off-diagonal blocks of row block I = w, right to left, with no further barrier:
   //     T_IJ = -(sum_{M=J+1}^{I} T_IM A_MJ) T_JJ, computed transposed so that every operand
   //     is a column read, a row read or the previous result tile. T_IJ (I > J) is stored
-  //     row-major in the unused upper block (J, I) of sA.
+  //     row-major in the unused upper block (J, I) of sA. Before that, every wave copies its
+  //     share of P's fragment slots from sPnT to the record (wave 0 has no block to solve).
+  {
+    constexpr int NSL = NSUB * (CHUNK / KS) * 64;
+    static_assert(NSL % PREP_THREADS == 0, "slot split");
+#pragma unroll
+    for (int i = 0; i < NSL / PREP_THREADS; ++i) {
+      const int sl = tid + PREP_THREADS * i;
+      const int ln = sl & 63, ts = sl >> 6;
+      const int s = ts % (CHUNK / KS), tile = ts / (CHUNK / KS);
+      *reinterpret_cast<frag*>(recM + R::oPb + (size_t)sl * EPL) = frag_t(sPnT, L::LC, 16 * tile, s, ln);
+    }
+  }
   if (w >= 1) {
     const int Ib = w;
     auto tblock = [&](int I, int M) -> float* {  // base of T_IM (I >= M)
@@ -591,6 +610,8 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   }
   lds_barrier();
 
+  load_raw(nxt, ntsk, 2);
+
   // ---------------- phase 4: T' = T diag(beta) -> LDS (row-major and transposed) and record
 #pragma unroll
   for (int it = 0; it < CHUNK * CHUNK / 4 / PREP_THREADS; ++it) {
@@ -606,7 +627,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   }
   lds_barrier();
 
-  // ---------------- phase 5: W^T = Ka^T T'^T -> record (as W fragments) and LDS (W^T)
+  // ---------------- phase 5: W^T = Ka^T T'^T -> record (as -W fragments)
 #pragma unroll
   for (int tix = 0; tix < NKT * NSUB; ++tix) {
     const int a = tix % NKT, b = tix / NKT;
@@ -619,38 +640,8 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
         acc = Mma<MT>::mma(frag_t(sKa, L::LDK, 16 * a, s, lane),
                            load_frag(sTb + (16 * b + m) * L::LC, s, g), acc);
     st4(recM + R::oW + slot4<MT>(16 * b + m, 16 * a + 4 * g, K), -acc);  // the record holds -W
-    st4(sW + (16 * b + m) * L::LDK + 16 * a + 4 * g, acc);  // W row 16b + m
   }
-  lds_barrier();
 
-  // ---------------- phase 6a: Q_eff^T = (Q e^{b})^T + W^T (-P)^T, column tile b = w. The
-  // accumulator starts from this lane's own q e^{b_t} (token 16w + m, channels 16a + 4g + r).
-  {
-    const int nsteps = (16 * w + 16 + KS - 1) / KS;
-#pragma unroll
-    for (int a = 0; a < NKT; ++a) {
-      f32x4 acc = {qe[a][0], qe[a][1], qe[a][2], qe[a][3]};
-#pragma unroll
-      for (int s = 0; s < CHUNK / KS; ++s)
-        if (s < nsteps)
-          acc = Mma<MT>::mma(frag_t(sW, L::LDK, 16 * a, s, lane), frag_t(sPnT, L::LC, 16 * w, s, lane), acc);
-      st4(recM + R::oQ + slot4<MT>(16 * w + m, 16 * a + 4 * g, K), acc);
-    }
-  }
-  // ---------------- phase 6b: P'^T = -(T'^T (-P)^T) -> record (as P' fragments); column tile a = w
-#pragma unroll
-  for (int b = 0; b < NSUB; ++b) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (w <= b) {
-      const int nsteps = (16 * b + 16 + KS - 1) / KS;
-#pragma unroll
-      for (int s = 0; s < CHUNK / KS; ++s)
-        if (s < nsteps)
-          acc = Mma<MT>::mma(frag_t(sTb, L::LC, 16 * w, s, lane), frag_t(sPnT, L::LC, 16 * b, s, lane), acc);
-      acc = -acc;
-    }
-    st4(recM + R::oPb + slot4<MT>(16 * b + m, 16 * w + 4 * g, CHUNK), acc);
-  }
   lds_barrier();  // the next task reuses every LDS region
   cur = nxt;
   }
@@ -664,9 +655,9 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
 // of the product that consumes it (a 16-row result tile -- two for bf16 -- is a fragment
 // along its row index):
 //   Delta = U + (-W) S                       B operand: S as fragments along K
-//   O^T   = (P'V)^T + S^T Q_eff^T            A operand: the same S fragments
 //   S'    = Diag(gamma) S + Ktilde^T Delta   B operand: Delta as fragments along the tokens
-//   U = T'V and (P'V)^T of the next chunk    V through LDS and the transposing read
+//   O^T   = S^T Qe^T + Delta^T P^T           A operands: the same S and Delta fragments
+//   U = T'V of the next chunk                V through LDS and the transposing read
 // so the state path has no workgroup barrier and no LDS round trip. A chunk is NF matrix-core
 // operations, each consuming one record fragment; the fragments stream through a ring of D
 // registers, each load issued D operations ahead of its use. V and gamma pass through this
@@ -699,8 +690,8 @@ struct StateShape {
         if (tri_nz(t, s) && i-- == 0) return s;
     return 0;
   }
-  // the chunk's operations in issue order: W and Q_eff interleaved per K step (2*NTT per
-  // step), Ktilde^T (steps outer), then T' and P' of the next chunk
+  // the chunk's operations in issue order: -W and Qe interleaved per K step (2*NTT per step),
+  // Ktilde^T (steps outer), T' of the next chunk, then P of this chunk
   static constexpr int NA = 2 * NTT * NKS;
   static constexpr int NB = NKT * NTS;
   static constexpr int NF = NA + NB + 2 * NTRI;
@@ -825,7 +816,7 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
   }
 
   // Per-chunk descriptors cover the chunk's valid rows of V and of the output, so rows past
-  // the end load as zero (T' and P' are zero in those columns anyway) and are never stored.
+  // the end load as zero (T' is zero in those columns anyway) and are never stored.
   const uint32_t rowb = (uint32_t)(H * V * (int)sizeof(MT));  // bytes between token rows
   const MT* gv = reinterpret_cast<const MT*>(p.v) + (int64_t)h * V + col0;
   MT* go = reinterpret_cast<MT*>(p.o) + (int64_t)h * V + col0;
@@ -849,6 +840,8 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
     return buf_load16<frag>(rrec, lo + (off & 4095u), rc + (off & ~4095u));
   };
 
+  // operation j reads the next chunk's record (T') or this chunk's (everything else)
+  auto next_rec = [](int j) constexpr { return j >= NA + NB && j < NA + NB + NTRI; };
   // byte offset (without the lane part) of operation j's fragment in its record
   auto frag_off = [](auto J) constexpr -> uint32_t {
     constexpr int j = decltype(J)::value;
@@ -891,7 +884,7 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
   };
   auto rec_index = [&](int k) { return __builtin_amdgcn_readfirstlane(sRun[min(k, run - 1)]); };
 
-  // ---- prologue: U and (P'V)^T of chunk 0, the ring for chunk 0, gamma of chunk 0
+  // ---- prologue: U of chunk 0, the ring for chunk 0, gamma of chunk 0
   uint32_t rc0 = rec_off(rec_index(0));
   uint32_t rc1 = rec_off(rec_index(1));
   uint32_t rc2 = rec_off(rec_index(2));
@@ -908,7 +901,6 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
     static_for<0, NTRI>([&](auto I) {
       constexpr int i = decltype(I)::value, tt = SH::tri_t(i), s = SH::tri_s(i);
       U[tt] = M::mma(ldf(rc0, frag_off(std::integral_constant<int, NA + NB + i>())), Vf[s], U[tt]);
-      O[tt] = M::mma(Vf[s], ldf(rc0, frag_off(std::integral_constant<int, NA + NB + NTRI + i>())), O[tt]);
     });
   }
   // gamma first, then the ring: in the loop gamma is waited for long after the loads behind it
@@ -917,7 +909,7 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
   frag ring[D];
   static_for<0, D>([&](auto J) {
     constexpr int j = decltype(J)::value;
-    ring[j] = ldf(j < NA + NB ? rc0 : rc1, frag_off(J));
+    ring[j] = ldf(next_rec(j) ? rc1 : rc0, frag_off(J));
   });
   __builtin_amdgcn_sched_barrier(0);
   int ri_pre = sRun[min(3, run - 1)];  // record index of chunk k + 3, read one chunk ahead
@@ -961,16 +953,14 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
         }
       }
       if constexpr (j == NA + NB / 2) {
-        // output rows of chunk k, then V of chunk k+1 into LDS and its fragments
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) buf_store(ro, o_voff, (uint32_t)(16 * tt) * rowb, to_mt4<MT>(O[tt]));
+        // V of chunk k+1 into LDS and its fragments
         stage_v(vx);
 #pragma unroll
         for (int s = 0; s < NTS; ++s) Vf[s] = frag_t(sV, LDV, 0, s, lane);
       }
       if constexpr (j == NA + NB) {
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) U[tt] = O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < NTT; ++tt) U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
         load_v(k + 2, vx);
       }
       // --- operation j
@@ -978,7 +968,7 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
       if constexpr (j < NA) {
         constexpr int s = j / (2 * NTT), r = j % (2 * NTT), tt = r % NTT;
         if constexpr (r < NTT) U[tt] = M::mma(f, Sb[s], U[tt]);  // U - W S
-        else O[tt] = M::mma(Sb[s], f, O[tt]);                    // + S^T Q_eff^T
+        else O[tt] = M::mma(Sb[s], f, O[tt]);                    // S^T Qe^T
       } else if constexpr (j < NA + NB) {
         constexpr int jj = j - NA, s = jj / NKT, kt = jj % NKT;
         S[kt] = M::mma(f, Db[s], S[kt]);  // + Ktilde^T Delta
@@ -987,20 +977,26 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
         U[SH::tri_t(i)] = M::mma(f, Vf[SH::tri_s(i)], U[SH::tri_t(i)]);  // T'V, next chunk
       } else {
         constexpr int i = j - NA - NB - NTRI;
-        O[SH::tri_t(i)] = M::mma(Vf[SH::tri_s(i)], f, O[SH::tri_t(i)]);  // (P'V)^T, next chunk
+        O[SH::tri_t(i)] = M::mma(Db[SH::tri_s(i)], f, O[SH::tri_t(i)]);  // + Delta^T P^T
       }
       // --- refill: operation j + D of the stream
       {
         constexpr int jn = j + D;
         if constexpr (jn < NF) {
-          ring[j % D] = ldf(jn < NA + NB ? rc0 : rc1, frag_off(std::integral_constant<int, jn>()));
+          ring[j % D] = ldf(next_rec(jn) ? rc1 : rc0, frag_off(std::integral_constant<int, jn>()));
         } else {
           constexpr int jw = jn - NF;
-          ring[j % D] = ldf(jw < NA + NB ? rc1 : rc2, frag_off(std::integral_constant<int, jw>()));
+          ring[j % D] = ldf(next_rec(jw) ? rc2 : rc1, frag_off(std::integral_constant<int, jw>()));
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+    // output rows of chunk k; the accumulators restart for chunk k+1
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      buf_store(ro, o_voff, (uint32_t)(16 * tt) * rowb, to_mt4<MT>(O[tt]));
+      O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     rc0 = rc1;
     rc1 = rc2;
     rc2 = rc3;
