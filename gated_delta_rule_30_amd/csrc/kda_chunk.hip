@@ -260,15 +260,6 @@ struct PrepParams {
   int64_t rec_bytes;
 };
 
-// Record slot offset (elements) of the 4 consecutive reduction indices j0 .. j0+3 (j0 % 4 == 0)
-// of row r in a matrix with reduction length L.
-template <typename MT>
-__device__ __forceinline__ size_t slot4(int r, int j0, int L) {
-  constexpr int KS = Mma<MT>::KS;
-  const int jj = j0 % KS;
-  return slot_elem<MT>(r >> 4, j0 / KS, (r & 15) + 16 * ((jj & 15) >> 2), L) + 4 * (jj >> 4);
-}
-
 // One workgroup of 4 waves per (chunk, head); wave w owns sub-block w (tokens 16w .. 16w+15).
 // Lane (m, g) = (lane % 16, lane / 16) holds token 16w + m and the channels 16u + 4g .. +3,
 // u = 0 .. K/16-1, which is exactly that token's MFMA fragment over the channels. Phases are
@@ -612,7 +603,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
 
   load_raw(nxt, ntsk, 2);
 
-  // ---------------- phase 4: T' = T diag(beta) -> LDS (row-major and transposed) and record
+  // ---------------- phase 4: T' = T diag(beta) -> LDS (row-major)
 #pragma unroll
   for (int it = 0; it < CHUNK * CHUNK / 4 / PREP_THREADS; ++it) {
     const int idx = tid + PREP_THREADS * it;
@@ -623,23 +614,45 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     tv *= *reinterpret_cast<const f32x4*>(sBeta + j0);
     if (Ii < Jj) tv = f32x4{0.f, 0.f, 0.f, 0.f};
     st4(sTb + i * L::LC + j0, tv);
-    st4(recM + R::oTb + slot4<MT>(i, j0, CHUNK), tv);
   }
   lds_barrier();
 
-  // ---------------- phase 5: W^T = Ka^T T'^T -> record (as -W fragments)
+  // ---------------- phase 5: T' fragments to the record (whole 16-byte lane slots), then
+  // W^T = Ka^T T'^T -> record (as -W fragments)
+  {
+    constexpr int NSL = NSUB * (CHUNK / KS) * 64;
 #pragma unroll
-  for (int tix = 0; tix < NKT * NSUB; ++tix) {
-    const int a = tix % NKT, b = tix / NKT;
-    if (tix % 4 != w) continue;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int nsteps = (16 * b + 16 + KS - 1) / KS;
+    for (int i = 0; i < NSL / PREP_THREADS; ++i) {
+      const int sl = tid + PREP_THREADS * i;
+      const int ln = sl & 63, ts = sl >> 6;
+      const int s = ts % (CHUNK / KS), tile = ts / (CHUNK / KS);
+      *reinterpret_cast<frag*>(recM + R::oTb + (size_t)sl * EPL) =
+          load_frag(sTb + (16 * tile + (ln & 15)) * L::LC, s, ln >> 4);
+    }
+  }
+  // Result tile (channel tile a, token tile b): lane (m, g) holds W[16b + m][16a + 4g + r]. A
+  // wave takes the KS / 16 channel tiles of one reduction step together, which together are
+  // exactly its lanes' slots of W's fragment (token tile b, step ap).
+  {
+    constexpr int TPS = KS / 16;  // channel tiles per reduction step
 #pragma unroll
-    for (int s = 0; s < CHUNK / KS; ++s)
-      if (s < nsteps)
-        acc = Mma<MT>::mma(frag_t(sKa, L::LDK, 16 * a, s, lane),
-                           load_frag(sTb + (16 * b + m) * L::LC, s, g), acc);
-    st4(recM + R::oW + slot4<MT>(16 * b + m, 16 * a + 4 * g, K), -acc);  // the record holds -W
+    for (int tix = 0; tix < (NKT / TPS) * NSUB; ++tix) {
+      const int ap = tix % (NKT / TPS), b = tix / (NKT / TPS);
+      if (tix % 4 != w) continue;
+      const int nsteps = (16 * b + 16 + KS - 1) / KS;
+      f32x4 acc[TPS];
+#pragma unroll
+      for (int t = 0; t < TPS; ++t) {
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < CHUNK / KS; ++s)
+          if (s < nsteps)
+            acc[t] = Mma<MT>::mma(frag_t(sKa, L::LDK, 16 * (TPS * ap + t), s, lane),
+                                  load_frag(sTb + (16 * b + m) * L::LC, s, g), acc[t]);
+        acc[t] = -acc[t];  // the record holds -W
+      }
+      *reinterpret_cast<frag*>(recM + R::oW + slot_elem<MT>(b, ap, lane, K)) = to_frag(acc[0], acc[TPS - 1], MT());
+    }
   }
 
   lds_barrier();  // the next task reuses every LDS region
