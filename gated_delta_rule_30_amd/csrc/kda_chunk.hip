@@ -309,14 +309,21 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     raw4 q[NG], k[NG], g[NG];
     MT b;
   };
+  // first token and length of a task's chunk (read one task ahead: the prefetch addresses
+  // depend on them, and a load issued only there would stall every part of the prefetch)
+  struct TaskPos {
+    int tok, len;
+  };
+  auto task_pos = [&](int tk) -> TaskPos {
+    const Entry* e = p.entries + p.seg_begin + tk / H;
+    return TaskPos{e->tok, e->len};
+  };
   // Rows past the chunk's end load the last valid row again; they are zeroed after conversion
   // (q = k = 0, log alpha = 0, beta = 0 there), so every load is unconditional.
   // part 0: q; part 1: k; part 2: log alpha and beta; part -1: everything
-  auto load_raw = [&](Raw& r, int task, int part) {
-    const int jt = task / H;
-    const Entry en = p.entries[p.seg_begin + jt];
-    const int hh = task - jt * H;
-    const int64_t tl = en.tok + min(t0, en.len - 1);
+  auto load_raw = [&](Raw& r, TaskPos tp, int task, int part) {
+    const int hh = task % H;
+    const int64_t tl = tp.tok + min(t0, tp.len - 1);
     const int64_t row = tl * (int64_t)H * K + (int64_t)hh * K + 4 * g0;
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
@@ -328,8 +335,9 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   };
   int task = blockIdx.x;
   if (task >= ntask) return;
+  TaskPos pc = task_pos(task);
   Raw cur, nxt;
-  load_raw(cur, task, -1);
+  load_raw(cur, pc, task, -1);
 #pragma clang loop unroll(disable)
   for (; task < ntask; task += gridDim.x) {
   // Lane-dependent addresses are recomputed in every iteration: without the opaque copy the
@@ -342,8 +350,9 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   const int t = 16 * w + m;
   const int j = task / H;
   const int h = task - j * H;
-  const Entry en = p.entries[p.seg_begin + j];
-  const int len = en.len;  // 1 .. CHUNK
+  const int len = pc.len;  // 1 .. CHUNK
+  const int ntsk = task + gridDim.x < ntask ? task + gridDim.x : task;
+  const TaskPos pn = task_pos(ntsk);
   MT* recM = reinterpret_cast<MT*>(p.rec + (j * H + h) * p.rec_bytes);
   float* recGam = reinterpret_cast<float*>(p.rec + (j * H + h) * p.rec_bytes + R::oGamBytes);
   const bool valid = t < len;
@@ -468,8 +477,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
 
   // the next task's inputs load during phases 2-5 (phase 1's fp32 copies are dead by now)
   // (in three parts, so that the loads enter the memory pipeline in smaller bursts)
-  const int ntsk = task + gridDim.x < ntask ? task + gridDim.x : task;
-  load_raw(nxt, ntsk, 0);
+  load_raw(nxt, pn, ntsk, 0);
 
   // ---------------- phase 2: blocks (I, w), I >= w, of A and P. The column operand (token
   // block w, scaled per channel by D_{Iw}) is this wave's own kc; the row operands are read as
@@ -524,7 +532,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     }
   }
 
-  load_raw(nxt, ntsk, 1);
+  load_raw(nxt, pn, ntsk, 1);
 
   // ---------------- phase 3: T = (I + A)^{-1}
   // (a) Diagonal 16x16 block of wave w by right-looking forward substitution: lane c keeps
@@ -601,7 +609,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   }
   lds_barrier();
 
-  load_raw(nxt, ntsk, 2);
+  load_raw(nxt, pn, ntsk, 2);
 
   // ---------------- phase 4: T' = T diag(beta) -> LDS (row-major)
 #pragma unroll
@@ -657,6 +665,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
 
   lds_barrier();  // the next task reuses every LDS region
   cur = nxt;
+  pc = pn;
   }
 }
 
