@@ -615,9 +615,13 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
 #pragma unroll
   for (int it = 0; it < CHUNK * CHUNK / 4 / PREP_THREADS; ++it) {
     const int idx = tid + PREP_THREADS * it;
-    const int i = idx / (CHUNK / 4), j0 = 4 * (idx % (CHUNK / 4));
-    const int Ii = i >> 4, Jj = j0 >> 4;
-    const int src = (Ii == Jj) ? i * L::LCF + j0 : (16 * Jj + (i & 15)) * L::LCF + 16 * Ii + (j0 & 15);
+    const unsigned i = (unsigned)idx / (CHUNK / 4), j0 = 4u * ((unsigned)idx % (CHUNK / 4));
+    const unsigned Ii = i >> 4, Jj = j0 >> 4;
+    // diagonal blocks of T sit in place, block (Ii, Jj < Ii) transposed in the upper block (Jj, Ii)
+    // (selected arithmetically: a branch here made the compiler wait on the pending prefetch)
+    const unsigned srcd = i * L::LCF + j0, srco = (16u * Jj + (i & 15u)) * L::LCF + 16u * Ii + (j0 & 15u);
+    const unsigned sel = 0u - (unsigned)(Ii == Jj);
+    const unsigned src = (srcd & sel) | (srco & ~sel);
     f32x4 tv = *reinterpret_cast<const f32x4*>(sA + src);
     tv *= *reinterpret_cast<const f32x4*>(sBeta + j0);
     if (Ii < Jj) tv = f32x4{0.f, 0.f, 0.f, 0.f};
