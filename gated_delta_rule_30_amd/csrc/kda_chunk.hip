@@ -335,149 +335,166 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   };
   int task = blockIdx.x;
   if (task >= ntask) return;
-  TaskPos pc = task_pos(task);
-  Raw cur, nxt;
-  load_raw(cur, pc, task, -1);
+  Raw raw;  // raw inputs of one task: filled one task ahead, consumed by phase 1
+  load_raw(raw, task_pos(task), task, -1);
+  float kc[NG][4];  // phase 1 -> phase 2: this wave's column operand
+
+  // Phase 1 of a task: its raw inputs become the LDS operands, the per-channel tables, kc and
+  // the record parts that need nothing else (Qe, gamma, Ktilde^T).
+  auto front = [&](const int task, const TaskPos pc, const Raw& cur) {
+    // Lane-dependent addresses are recomputed for every task: without the opaque copy the
+    // compiler hoists all of them out of the loop and keeps them live, which spills.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int m = lane & 15;
+    const int g = lane >> 4;
+    const int t = 16 * w + m;
+    const int j = task / H;
+    const int h = task - j * H;
+    const int len = pc.len;  // 1 .. CHUNK
+    MT* recM = reinterpret_cast<MT*>(p.rec + (j * H + h) * p.rec_bytes);
+    float* recGam = reinterpret_cast<float*>(p.rec + (j * H + h) * p.rec_bytes + R::oGamBytes);
+    const bool valid = t < len;
+
+    // ---------------- phase 1: the token's q, k and log2 alpha (fp32). Past the chunk's end only
+    // log alpha (and beta) are zeroed: the q and k rows there repeat the last valid token and
+    // have no effect -- beta = 0 zeroes their rows of A and their rows and columns of T', and so
+    // their rows of W and Delta (their columns of P meet only those zero rows of Delta) -- while
+    // log alpha = 0 keeps the decay products of the valid tokens.
+    float qv[NG][4], kv[NG][4], lv[NG][4];
+  #pragma unroll
+    for (int u = 0; u < NG; ++u)
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        qv[u][r] = to_f32(cur.q[u][r]);
+        kv[u][r] = to_f32(cur.k[u][r]);
+        lv[u][r] = valid ? to_f32(cur.g[u][r]) * LOG2E : 0.f;
+      }
+    const float bval = to_f32(cur.b);
+    if (g == 0) sBeta[t] = valid ? bval : 0.f;
+    // inclusive cumsum of log2 alpha over the 16 tokens of the sub-block (one 16-lane row):
+    // lv becomes b_t - e_{w-1}; dI = e_w - e_{w-1} is the row's last value (log2 units)
+    float dI[NG][4];
+  #pragma unroll
+    for (int u = 0; u < NG; ++u)
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = lv[u][r];
+        x += row_shr<1>(x);
+        x += row_shr<2>(x);
+        x += row_shr<4>(x);
+        x += row_shr<8>(x);
+        lv[u][r] = x;
+      }
+  #pragma unroll
+    for (int u = 0; u < NG; ++u)
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) dI[u][r] = __shfl(lv[u][r], lane | 15);
+    if (m == 0) {
+  #pragma unroll
+      for (int u = 0; u < NG; ++u)
+        *reinterpret_cast<f32x4*>(sDel + w * K + 16 * u + 4 * g) = f32x4{dI[u][0], dI[u][1], dI[u][2], dI[u][3]};
+    }
+    lds_barrier();
+    // per-channel factors, each computed once: e^{e_{J-1}} (sEx), gamma = e^{e_3} (record),
+    // D_{IJ} = e^{e_{I-1} - e_J} <= 1 for I > J and e^{e_{J-1} - e_J} for I = J (sD), and
+    // e^{e_3 - e_J} (sTail); e_J is the log decay from the chunk start to the end of block J
+    {
+      constexpr int NROLE = PREP_THREADS / K;
+      const int c = tid % K, role = tid / K;
+      float ec[NSUB + 1];
+      ec[0] = 0.f;
+  #pragma unroll
+      for (int J = 0; J < NSUB; ++J) ec[J + 1] = ec[J] + sDel[J * K + c];
+  #pragma unroll
+      for (int v = 0; v < 2 * NSUB + 1 + NPAIR; ++v) {
+        if (v % NROLE != role) continue;
+        if (v < NSUB) {
+          sEx[v * K + c] = exp2_f(ec[v]);
+        } else if (v == NSUB) {
+          recGam[c] = exp2_f(ec[NSUB]);
+        } else if (v < NSUB + 1 + NPAIR) {
+          const int pi = v - NSUB - 1;
+          const int I = (pi >= 1) + (pi >= 3) + (pi >= 6);
+          const int J = pi - I * (I + 1) / 2;
+          sD[pi * K + c] = exp2_f((I == J ? ec[J] : ec[I]) - ec[J + 1]);
+        } else {
+          const int J = v - NSUB - 1 - NPAIR;
+          sTail[J * K + c] = exp2_f(ec[NSUB] - ec[J + 1]);
+        }
+      }
+    }
+    lds_barrier();
+    // decayed operands of the lane's token:
+    //   Q^ = q e^{b_t - e_{w-1}}, K^ = k e^{b_t - e_{w-1}}  (<= 1 factors, MFMA row operands)
+    //   kc = k e^{e_w - b_t}                                (<= 1, column operand, registers)
+    //   Qe = q e^{b_t} (record, from registers),  Ka = k e^{b_t},  Kt = k e^{b_last - b_t}
+    {
+      f32x4 qh[NG], kh[NG], qe[NG];
+  #pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        const f32x4 ex = *reinterpret_cast<const f32x4*>(sEx + w * K + 16 * u + 4 * g);
+        const f32x4 tl = *reinterpret_cast<const f32x4*>(sTail + w * K + 16 * u + 4 * g);
+        f32x4 ka, kt;
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float rr = exp2_f(lv[u][r]);
+          const float cc = exp2_f(dI[u][r] - lv[u][r]);
+          qh[u][r] = qv[u][r] * rr;
+          kh[u][r] = kv[u][r] * rr;
+          kc[u][r] = kv[u][r] * cc;
+          qe[u][r] = qh[u][r] * ex[r];
+          ka[r] = kh[u][r] * ex[r];
+          kt[r] = kc[u][r] * tl[r];
+        }
+        st4(sKa + t * L::LDK + 16 * u + 4 * g, ka);
+        st4(sKt + t * L::LDK + 16 * u + 4 * g, kt);
+      }
+  #pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const size_t slot = ((size_t)(w * NS + s) * 64 + lane) * EPL;
+        *reinterpret_cast<frag*>(sQh + slot) = to_frag(qh[GPS * s], qh[GPS * s + GPS - 1], MT());
+        *reinterpret_cast<frag*>(sKh + slot) = to_frag(kh[GPS * s], kh[GPS * s + GPS - 1], MT());
+        // this lane's slot of Qe's row tile w, step s is exactly its own token and channels
+        *reinterpret_cast<frag*>(recM + R::oQ + slot) = to_frag(qe[GPS * s], qe[GPS * s + GPS - 1], MT());
+      }
+    }
+    lds_barrier();
+    // Ktilde^T (rows = channels, reduction = tokens) to the record as fragment slots
+    {
+      constexpr int NSL = NKT * (CHUNK / KS) * 64;
+      static_assert(NSL % PREP_THREADS == 0, "slot split");
+  #pragma unroll
+      for (int i = 0; i < NSL / PREP_THREADS; ++i) {
+        const int sl = tid + PREP_THREADS * i;
+        const int ln = sl & 63, ts = sl >> 6;
+        const int s = ts % (CHUNK / KS), tile = ts / (CHUNK / KS);
+        *reinterpret_cast<frag*>(recM + R::oKt + (size_t)sl * EPL) = frag_t(sKt, L::LDK, 16 * tile, s, ln);
+      }
+    }
+
+  };
+  front(task, task_pos(task), raw);
+
+  // Each iteration runs phases 2-5 of one task and then phase 1 of the next, so the waits for
+  // the prefetched inputs come after the record stores in straight-line code.
 #pragma clang loop unroll(disable)
-  for (; task < ntask; task += gridDim.x) {
-  // Lane-dependent addresses are recomputed in every iteration: without the opaque copy the
-  // compiler hoists all of them out of the loop and keeps them live, which spills.
+  for (;;) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int m = lane & 15;
   const int g = lane >> 4;
-  const int t = 16 * w + m;
   const int j = task / H;
   const int h = task - j * H;
-  const int len = pc.len;  // 1 .. CHUNK
   const int ntsk = task + gridDim.x < ntask ? task + gridDim.x : task;
   const TaskPos pn = task_pos(ntsk);
   MT* recM = reinterpret_cast<MT*>(p.rec + (j * H + h) * p.rec_bytes);
-  float* recGam = reinterpret_cast<float*>(p.rec + (j * H + h) * p.rec_bytes + R::oGamBytes);
-  const bool valid = t < len;
-
-  // ---------------- phase 1: the token's q, k and log2 alpha (fp32). Past the chunk's end only
-  // log alpha (and beta) are zeroed: the q and k rows there repeat the last valid token and
-  // have no effect -- beta = 0 zeroes their rows of A and their rows and columns of T', and so
-  // their rows of W and Delta (their columns of P meet only those zero rows of Delta) -- while
-  // log alpha = 0 keeps the decay products of the valid tokens.
-  float qv[NG][4], kv[NG][4], lv[NG][4];
-#pragma unroll
-  for (int u = 0; u < NG; ++u)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      qv[u][r] = to_f32(cur.q[u][r]);
-      kv[u][r] = to_f32(cur.k[u][r]);
-      lv[u][r] = valid ? to_f32(cur.g[u][r]) * LOG2E : 0.f;
-    }
-  const float bval = to_f32(cur.b);
-  if (g == 0) sBeta[t] = valid ? bval : 0.f;
-  // inclusive cumsum of log2 alpha over the 16 tokens of the sub-block (one 16-lane row):
-  // lv becomes b_t - e_{w-1}; dI = e_w - e_{w-1} is the row's last value (log2 units)
-  float dI[NG][4];
-#pragma unroll
-  for (int u = 0; u < NG; ++u)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float x = lv[u][r];
-      x += row_shr<1>(x);
-      x += row_shr<2>(x);
-      x += row_shr<4>(x);
-      x += row_shr<8>(x);
-      lv[u][r] = x;
-    }
-#pragma unroll
-  for (int u = 0; u < NG; ++u)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dI[u][r] = __shfl(lv[u][r], lane | 15);
-  if (m == 0) {
-#pragma unroll
-    for (int u = 0; u < NG; ++u)
-      *reinterpret_cast<f32x4*>(sDel + w * K + 16 * u + 4 * g) = f32x4{dI[u][0], dI[u][1], dI[u][2], dI[u][3]};
-  }
-  lds_barrier();
-  // per-channel factors, each computed once: e^{e_{J-1}} (sEx), gamma = e^{e_3} (record),
-  // D_{IJ} = e^{e_{I-1} - e_J} <= 1 for I > J and e^{e_{J-1} - e_J} for I = J (sD), and
-  // e^{e_3 - e_J} (sTail); e_J is the log decay from the chunk start to the end of block J
-  {
-    constexpr int NROLE = PREP_THREADS / K;
-    const int c = tid % K, role = tid / K;
-    float ec[NSUB + 1];
-    ec[0] = 0.f;
-#pragma unroll
-    for (int J = 0; J < NSUB; ++J) ec[J + 1] = ec[J] + sDel[J * K + c];
-#pragma unroll
-    for (int v = 0; v < 2 * NSUB + 1 + NPAIR; ++v) {
-      if (v % NROLE != role) continue;
-      if (v < NSUB) {
-        sEx[v * K + c] = exp2_f(ec[v]);
-      } else if (v == NSUB) {
-        recGam[c] = exp2_f(ec[NSUB]);
-      } else if (v < NSUB + 1 + NPAIR) {
-        const int pi = v - NSUB - 1;
-        const int I = (pi >= 1) + (pi >= 3) + (pi >= 6);
-        const int J = pi - I * (I + 1) / 2;
-        sD[pi * K + c] = exp2_f((I == J ? ec[J] : ec[I]) - ec[J + 1]);
-      } else {
-        const int J = v - NSUB - 1 - NPAIR;
-        sTail[J * K + c] = exp2_f(ec[NSUB] - ec[J + 1]);
-      }
-    }
-  }
-  lds_barrier();
-  // decayed operands of the lane's token:
-  //   Q^ = q e^{b_t - e_{w-1}}, K^ = k e^{b_t - e_{w-1}}  (<= 1 factors, MFMA row operands)
-  //   kc = k e^{e_w - b_t}                                (<= 1, column operand, registers)
-  //   Qe = q e^{b_t} (record, from registers),  Ka = k e^{b_t},  Kt = k e^{b_last - b_t}
-  float kc[NG][4];
-  {
-    f32x4 qh[NG], kh[NG], qe[NG];
-#pragma unroll
-    for (int u = 0; u < NG; ++u) {
-      const f32x4 ex = *reinterpret_cast<const f32x4*>(sEx + w * K + 16 * u + 4 * g);
-      const f32x4 tl = *reinterpret_cast<const f32x4*>(sTail + w * K + 16 * u + 4 * g);
-      f32x4 ka, kt;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float rr = exp2_f(lv[u][r]);
-        const float cc = exp2_f(dI[u][r] - lv[u][r]);
-        qh[u][r] = qv[u][r] * rr;
-        kh[u][r] = kv[u][r] * rr;
-        kc[u][r] = kv[u][r] * cc;
-        qe[u][r] = qh[u][r] * ex[r];
-        ka[r] = kh[u][r] * ex[r];
-        kt[r] = kc[u][r] * tl[r];
-      }
-      st4(sKa + t * L::LDK + 16 * u + 4 * g, ka);
-      st4(sKt + t * L::LDK + 16 * u + 4 * g, kt);
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const size_t slot = ((size_t)(w * NS + s) * 64 + lane) * EPL;
-      *reinterpret_cast<frag*>(sQh + slot) = to_frag(qh[GPS * s], qh[GPS * s + GPS - 1], MT());
-      *reinterpret_cast<frag*>(sKh + slot) = to_frag(kh[GPS * s], kh[GPS * s + GPS - 1], MT());
-      // this lane's slot of Qe's row tile w, step s is exactly its own token and channels
-      *reinterpret_cast<frag*>(recM + R::oQ + slot) = to_frag(qe[GPS * s], qe[GPS * s + GPS - 1], MT());
-    }
-  }
-  lds_barrier();
-  // Ktilde^T (rows = channels, reduction = tokens) to the record as fragment slots
-  {
-    constexpr int NSL = NKT * (CHUNK / KS) * 64;
-    static_assert(NSL % PREP_THREADS == 0, "slot split");
-#pragma unroll
-    for (int i = 0; i < NSL / PREP_THREADS; ++i) {
-      const int sl = tid + PREP_THREADS * i;
-      const int ln = sl & 63, ts = sl >> 6;
-      const int s = ts % (CHUNK / KS), tile = ts / (CHUNK / KS);
-      *reinterpret_cast<frag*>(recM + R::oKt + (size_t)sl * EPL) = frag_t(sKt, L::LDK, 16 * tile, s, ln);
-    }
-  }
 
   // the next task's inputs load during phases 2-5 (phase 1's fp32 copies are dead by now)
   // (in three parts, so that the loads enter the memory pipeline in smaller bursts)
-  load_raw(nxt, pn, ntsk, 0);
+  load_raw(raw, pn, ntsk, 0);
 
   // ---------------- phase 2: blocks (I, w), I >= w, of A and P. The column operand (token
   // block w, scaled per channel by D_{Iw}) is this wave's own kc; the row operands are read as
@@ -532,7 +549,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     }
   }
 
-  load_raw(nxt, pn, ntsk, 1);
+  load_raw(raw, pn, ntsk, 1);
 
   // ---------------- phase 3: T = (I + A)^{-1}
   // (a) Diagonal 16x16 block of wave w by right-looking forward substitution: lane c keeps
@@ -609,7 +626,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   }
   lds_barrier();
 
-  load_raw(nxt, pn, ntsk, 2);
+  load_raw(raw, pn, ntsk, 2);
 
   // ---------------- phase 4: T' = T diag(beta) -> LDS (row-major)
 #pragma unroll
@@ -668,8 +685,9 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   }
 
   lds_barrier();  // the next task reuses every LDS region
-  cur = nxt;
-  pc = pn;
+  task += gridDim.x;
+  if (task >= ntask) break;
+  front(task, pn, raw);
   }
 }
 
