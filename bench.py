@@ -27,8 +27,9 @@ PEAK_BF16 = 2.5e15        # FLOP/s, dense bf16 MFMA
 CHUNK = 64
 
 
-def chunk_alg_bytes(T, H, K, V, es, n_seqs, init, final):
-    per_tok_head = es * (3 * K + V + 1 + V)  # q, k, log_alpha, v, beta in; o out
+def chunk_alg_bytes(T, H, K, V, es, n_seqs, init, final, gate_dim=None):
+    gd = K if gate_dim is None else gate_dim  # gate values per token and head (1: scalar gate)
+    per_tok_head = es * (2 * K + gd + V + 1 + V)  # q, k, log_alpha, v, beta in; o out
     return T * H * per_tok_head + 4 * n_seqs * H * K * V * ((1 if init else 0) + (1 if final else 0))
 
 
@@ -42,8 +43,9 @@ def chunk_dense_flops(T, H, K, V, C=CHUNK):
     return T * H * (6 * K * V + 2 * C * (3 * K + 2 * V))
 
 
-def decode_alg_bytes(N, H, K, V, es):
-    return N * H * (2 * 4 * K * V + es * (3 * K + V + 1) + es * V)
+def decode_alg_bytes(N, H, K, V, es, gate_dim=None):
+    gd = K if gate_dim is None else gate_dim
+    return N * H * (2 * 4 * K * V + es * (2 * K + gd + V + 1) + es * V)
 
 
 # ---------------------------------------------------------------- measured HBM traffic
@@ -119,6 +121,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536,
                     help="tokens (all 32 heads) of the prefill workload the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-options-bench", action="store_true",
+                    help="skip the timing of the input-option entry points (counter runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run torch.neg over this many MiB of fp32 (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -231,6 +235,52 @@ def main():
                        "kernel": "decode_step_kernel<128,128,bf16>"}
     value = (T + Nd) / (ms_per_step * 1e-3)
 
+    # ---------------- the input options on the same shapes, timed after the headline steps:
+    # the gated delta rule's scalar gate from logits, beta from logits, unit-norm q and k
+    options = None
+    if not args.no_options_bench:
+        allo = kda.OPT_SCALAR_GATE | kda.OPT_GATE_LOGITS | kda.OPT_BETA_LOGITS | kda.OPT_L2NORM_QK
+        raw = workloads.gen_raw(T, H, K, V, allo, dtype=torch.bfloat16, device=dev,
+                                seed=wl["seed"], init_std=wl["init_std"])
+        draw = workloads.gen_raw(Nd, Hd, K, V, allo, dtype=torch.bfloat16, device=dev,
+                                 seed=wd["seed"] + 1)
+        o2, fin2, od2 = torch.empty_like(o), torch.empty_like(fin), torch.empty_like(od)
+        state2 = state.clone()
+
+        def chunk_opt():
+            kda.chunk_fwd(*(raw[x] for x in names), init_state=raw["init_state"], o=o2,
+                          final_state=fin2, workspace=ws, options=allo)
+
+        def decode_opt():
+            kda.decode_step(*(draw[x] for x in names), state=state2, o=od2, options=allo)
+
+        for _ in range(args.warmup):
+            chunk_opt()
+            decode_opt()
+        evo = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for s in range(args.steps):
+            evo[s][0].record()
+            chunk_opt()
+            evo[s][1].record()
+            decode_opt()
+            evo[s][2].record()
+        torch.cuda.synchronize()
+        cms = float(np.mean([e[0].elapsed_time(e[1]) for e in evo]))
+        dms = float(np.mean([e[1].elapsed_time(e[2]) for e in evo]))
+        cbo = chunk_alg_bytes(T, H, K, V, 2, 1, True, True, gate_dim=1)
+        dbo = decode_alg_bytes(Nd, Hd, K, V, 2, gate_dim=1)
+        options = {
+            "options": "SCALAR_GATE|GATE_LOGITS|BETA_LOGITS|L2NORM_QK",
+            "chunk_fwd": {"workload": "B=1 H=32 T=65536 K=V=128 bf16, gate [T,H] logits, beta "
+                                      "logits, raw q/k", "ms": cms, "tokens_per_s": T / (cms * 1e-3),
+                          "alg_bytes": cbo, "hbm_frac": cbo / (cms * 1e-3) / PEAK_HBM,
+                          "mfma_frac_alg": cf / (cms * 1e-3) / PEAK_BF16},
+            "decode_step": {"workload": "256 seqs x 32 heads, K=V=128, gate [N,H] logits",
+                            "ms": dms, "GB_per_s": dbo / (dms * 1e-3) / 1e9,
+                            "hbm_frac": dbo / (dms * 1e-3) / PEAK_HBM, "alg_bytes": dbo},
+        }
+        del raw, draw, o2, fin2, od2, state2
+
     # ---------------- parity spot check and CPU baseline (oracle on the same inputs)
     cpu = None
     parity = None
@@ -271,6 +321,7 @@ def main():
         "chunk_fwd": chunk,
         "decode_step": decode,
         "roofline_decode": roofline_decode,
+        "input_options": options,
         "parity_sample_max_rel_err": parity,
     }
     print(json.dumps(out), flush=True)

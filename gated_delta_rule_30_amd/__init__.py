@@ -3,8 +3,10 @@
 The operator lives in libkda.so (hand-written HIP kernels for gfx950, C ABI in
 include/kda.h); this package is its thin Python binding.
 """
-from ._binding import (KDA_DTYPE_BF16, KDA_DTYPE_F32, LIB_PATH, KdaError, chunk_fwd,
+from ._binding import (KDA_DTYPE_BF16, KDA_DTYPE_F32, LIB_PATH, OPT_BETA_LOGITS,
+                       OPT_GATE_LOGITS, OPT_L2NORM_QK, OPT_SCALAR_GATE, KdaError, chunk_fwd,
                        decode_step, declared_functions, lib, workspace_size)
 
 __all__ = ["chunk_fwd", "decode_step", "workspace_size", "KdaError", "lib", "LIB_PATH",
-           "declared_functions", "KDA_DTYPE_BF16", "KDA_DTYPE_F32"]
+           "declared_functions", "KDA_DTYPE_BF16", "KDA_DTYPE_F32", "OPT_SCALAR_GATE",
+           "OPT_GATE_LOGITS", "OPT_BETA_LOGITS", "OPT_L2NORM_QK"]

@@ -18,6 +18,11 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "kda.h")
 
 KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
+# input options of the _ex entry points (KDA_OPT_* in include/kda.h)
+OPT_SCALAR_GATE = 1
+OPT_GATE_LOGITS = 2
+OPT_BETA_LOGITS = 4
+OPT_L2NORM_QK = 8
 STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
           3: "KDA_ERROR_WORKSPACE_TOO_SMALL", 4: "KDA_ERROR_LAUNCH"}
 
@@ -49,6 +54,13 @@ def _lib():
         lib.kda_decode_step.restype = ctypes.c_int
         lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                         ctypes.c_int, vp]
+        u32 = ctypes.c_uint32
+        lib.kda_chunk_fwd_ex.restype = ctypes.c_int
+        lib.kda_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                         ctypes.c_int, u32, vp, vp, vp, sz, vp]
+        lib.kda_decode_step_ex.restype = ctypes.c_int
+        lib.kda_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                           ctypes.c_int, u32, vp]
         _LIB = lib
     return _LIB
 
@@ -100,11 +112,12 @@ def workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype) -> int:
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, num_seqs=None,
-              output_final_state=True, o=None, final_state=None, workspace=None):
+              output_final_state=True, o=None, final_state=None, workspace=None, options=0):
     """kda_chunk_fwd on torch tensors (token-major [T, H, .], see include/kda.h).
 
     Returns (o [T, H, V] in the input dtype, final_state [N, H, K, V] fp32 or None).
     ``final_state`` may be passed as the same tensor as ``init_state`` (in-place update).
+    ``options`` (OPT_* bits) selects kda_chunk_fwd_ex; with OPT_SCALAR_GATE log_alpha is [T, H].
     """
     device = q.device
     T, H, K = q.shape
@@ -118,8 +131,9 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, num_se
             raise ValueError("num_seqs does not match cu_seqlens")
     else:
         N = 1 if num_seqs is None else int(num_seqs)
+    gshape = (T, H) if options & OPT_SCALAR_GATE else (T, H, K)
     for name, t, shp in (("q", q, (T, H, K)), ("k", k, (T, H, K)), ("v", v, (T, H, V)),
-                         ("log_alpha", log_alpha, (T, H, K)), ("beta", beta, (T, H))):
+                         ("log_alpha", log_alpha, gshape), ("beta", beta, (T, H))):
         _check(t, name, shp, dt, device)
     if init_state is not None:
         _check(init_state, "init_state", (N, H, K, V), torch.float32, device)
@@ -133,37 +147,41 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, num_se
         _check(final_state, "final_state", (N, H, K, V), torch.float32, device)
     need = int(_lib().kda_chunk_fwd_workspace_size(N, T, H, K, V, code))
     if need == 0:
-        raise KdaError(2 if K not in (32, 64, 128) or V not in (32, 64, 128) else 1,
+        raise KdaError(2 if K not in (32, 64, 128) or V not in (32, 64, 128, 256) else 1,
                        "kda_chunk_fwd_workspace_size")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
-    st = _lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                              _ptr(init_state), _ptr(cu_seqlens), N, T, H, K, V, code,
-                              _ptr(o), _ptr(final_state), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _stream(device))
+    st = _lib().kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                 _ptr(init_state), _ptr(cu_seqlens), N, T, H, K, V, code,
+                                 int(options), _ptr(o), _ptr(final_state), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(device))
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd")
     return o, final_state
 
 
-def decode_step(q, k, v, log_alpha, beta, state, o=None):
+def decode_step(q, k, v, log_alpha, beta, state, o=None, options=0):
     """kda_decode_step on torch tensors: q, k, log_alpha [N, H, K], v [N, H, V], beta [N, H],
-    state [N, H, K, V] fp32 updated in place. Returns o [N, H, V] in the input dtype."""
+    state [N, H, K, V] fp32 updated in place. Returns o [N, H, V] in the input dtype.
+    ``options`` (OPT_* bits) selects kda_decode_step_ex; with OPT_SCALAR_GATE log_alpha is
+    [N, H]."""
     device = q.device
     N, H, K = q.shape
     V = v.shape[-1]
     dt = q.dtype
     code = _dtype_code(q)
+    gshape = (N, H) if options & OPT_SCALAR_GATE else (N, H, K)
     for name, t, shp in (("q", q, (N, H, K)), ("k", k, (N, H, K)), ("v", v, (N, H, V)),
-                         ("log_alpha", log_alpha, (N, H, K)), ("beta", beta, (N, H))):
+                         ("log_alpha", log_alpha, gshape), ("beta", beta, (N, H))):
         _check(t, name, shp, dt, device)
     _check(state, "state", (N, H, K, V), torch.float32, device)
     if o is None:
         o = torch.empty((N, H, V), dtype=dt, device=device)
     else:
         _check(o, "o", (N, H, V), dt, device)
-    st = _lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                _ptr(state), _ptr(o), N, H, K, V, code, _stream(device))
+    st = _lib().kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                   _ptr(state), _ptr(o), N, H, K, V, code, int(options),
+                                   _stream(device))
     if st != 0:
         raise KdaError(st, "kda_decode_step")
     return o

@@ -8,7 +8,14 @@
 
 namespace {
 
-bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }
+bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+// the chunk path's prep kernel holds K-wide operand tiles in LDS: K <= 128
+bool supported_chunk_dk(int32_t d) { return d == 32 || d == 64 || d == 128; }
+constexpr uint32_t kAllOptions =
+    KDA_OPT_SCALAR_GATE | KDA_OPT_GATE_LOGITS | KDA_OPT_BETA_LOGITS | KDA_OPT_L2NORM_QK;
+static_assert(KDA_OPT_SCALAR_GATE == kda::OPT_SCALAR_GATE && KDA_OPT_GATE_LOGITS == kda::OPT_GATE_LOGITS &&
+                  KDA_OPT_BETA_LOGITS == kda::OPT_BETA_LOGITS && KDA_OPT_L2NORM_QK == kda::OPT_L2NORM_QK,
+              "option bits of the ABI and the kernels");
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool valid_dtype(kda_dtype t) { return t == KDA_DTYPE_F32 || t == KDA_DTYPE_BF16; }
@@ -40,7 +47,7 @@ static kda_status check_chunk_shape(int32_t num_seqs, int64_t total_tokens, int3
                                     int32_t dk, int32_t dv, kda_dtype dtype) {
   if (num_seqs <= 0 || num_heads <= 0 || total_tokens < 0 || total_tokens > kMaxTokens)
     return KDA_ERROR_INVALID_VALUE;
-  if (!valid_dtype(dtype) || !supported_dim(dk) || !supported_dim(dv)) return KDA_ERROR_NOT_SUPPORTED;
+  if (!valid_dtype(dtype) || !supported_chunk_dk(dk) || !supported_dim(dv)) return KDA_ERROR_NOT_SUPPORTED;
   // fp32 operands at K = 128 exceed the prep kernel's LDS budget
   if (dtype == KDA_DTYPE_F32 && dk == 128) return KDA_ERROR_NOT_SUPPORTED;
   return KDA_SUCCESS;
@@ -56,22 +63,27 @@ extern "C" size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_t
   return pl.total_bytes;
 }
 
-extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
-                                    const void* log_alpha, const void* beta,
-                                    const float* init_state, const int32_t* cu_seqlens,
-                                    int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
-                                    int32_t dk, int32_t dv, kda_dtype dtype, void* o,
-                                    float* final_state, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v,
+                                       const void* log_alpha, const void* beta,
+                                       const float* init_state, const int32_t* cu_seqlens,
+                                       int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                       int32_t dk, int32_t dv, kda_dtype dtype, uint32_t options,
+                                       void* o, float* final_state, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
   kda_status st = check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_SUCCESS) return st;
+  if (options & ~kAllOptions) return KDA_ERROR_NOT_SUPPORTED;
+  const int32_t gdim = (options & KDA_OPT_SCALAR_GATE) ? 1 : dk;  // gate values per token and head
   if (cu_seqlens == nullptr && total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
   if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERROR_INVALID_VALUE;
   if (!workspace) return KDA_ERROR_INVALID_VALUE;
-  const void* ptrs[] = {q, k, v, log_alpha, init_state, o, final_state};
+  // vectors of K or V elements need 16 bytes; per-token scalars (beta, a scalar gate) their element
+  const bool scalar_gate = (options & KDA_OPT_SCALAR_GATE) != 0;
+  const void* ptrs[] = {q, k, v, scalar_gate ? nullptr : log_alpha, init_state, o, final_state};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
-  if ((beta && !aligned_to(beta, esize(dtype))) || (cu_seqlens && !aligned_to(cu_seqlens, 4)))
+  if ((beta && !aligned_to(beta, esize(dtype))) || (cu_seqlens && !aligned_to(cu_seqlens, 4)) ||
+      (log_alpha && !aligned_to(log_alpha, esize(dtype))))
     return KDA_ERROR_INVALID_VALUE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERROR_INVALID_VALUE;
   const size_t sbytes = (size_t)num_seqs * num_heads * dk * dv * sizeof(float);
@@ -81,8 +93,9 @@ extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
   if (total_tokens > 0) {
     const size_t obytes = (size_t)total_tokens * num_heads * dv * esize(dtype);
     const size_t ibytes = (size_t)total_tokens * num_heads * dk * esize(dtype);
+    const size_t gbytes = (size_t)total_tokens * num_heads * gdim * esize(dtype);
     if (overlap(o, obytes, q, ibytes) || overlap(o, obytes, k, ibytes) ||
-        overlap(o, obytes, log_alpha, ibytes) || overlap(o, obytes, v, obytes))
+        overlap(o, obytes, log_alpha, gbytes) || overlap(o, obytes, v, obytes))
       return KDA_ERROR_INVALID_VALUE;
   }
   kda::ChunkPlan pl;
@@ -104,6 +117,7 @@ extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
   a.dk = dk;
   a.dv = dv;
   a.dtype_bf16 = dtype == KDA_DTYPE_BF16;
+  a.options = options;
   a.o = o;
   a.final_state = final_state;
   a.workspace = workspace;
@@ -112,22 +126,39 @@ extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
   return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
 }
 
-extern "C" kda_status kda_decode_step(const void* q, const void* k, const void* v,
-                                      const void* log_alpha, const void* beta, float* state,
-                                      void* o, int32_t num_seqs, int32_t num_heads, int32_t dk,
-                                      int32_t dv, kda_dtype dtype, void* stream) {
+extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
+                                    const void* log_alpha, const void* beta,
+                                    const float* init_state, const int32_t* cu_seqlens,
+                                    int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                    int32_t dk, int32_t dv, kda_dtype dtype, void* o,
+                                    float* final_state, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return kda_chunk_fwd_ex(q, k, v, log_alpha, beta, init_state, cu_seqlens, num_seqs,
+                          total_tokens, num_heads, dk, dv, dtype, 0u, o, final_state, workspace,
+                          workspace_bytes, stream);
+}
+
+extern "C" kda_status kda_decode_step_ex(const void* q, const void* k, const void* v,
+                                         const void* log_alpha, const void* beta, float* state,
+                                         void* o, int32_t num_seqs, int32_t num_heads,
+                                         int32_t dk, int32_t dv, kda_dtype dtype,
+                                         uint32_t options, void* stream) {
   if (num_seqs <= 0 || num_heads <= 0) return KDA_ERROR_INVALID_VALUE;
   if (!valid_dtype(dtype) || !supported_dim(dk) || !supported_dim(dv)) return KDA_ERROR_NOT_SUPPORTED;
+  if (options & ~kAllOptions) return KDA_ERROR_NOT_SUPPORTED;
+  const int32_t gdim = (options & KDA_OPT_SCALAR_GATE) ? 1 : dk;
   if (!q || !k || !v || !log_alpha || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
-  const void* ptrs[] = {q, k, v, log_alpha, state, o};
+  const bool scalar_gate = (options & KDA_OPT_SCALAR_GATE) != 0;
+  const void* ptrs[] = {q, k, v, scalar_gate ? state : log_alpha, state, o};
   for (const void* p : ptrs)
     if (!aligned16(p)) return KDA_ERROR_INVALID_VALUE;
-  if (!aligned_to(beta, esize(dtype))) return KDA_ERROR_INVALID_VALUE;
+  if (!aligned_to(beta, esize(dtype)) || !aligned_to(log_alpha, esize(dtype)))
+    return KDA_ERROR_INVALID_VALUE;
   const size_t heads = (size_t)num_seqs * num_heads;
   const size_t obytes = heads * dv * esize(dtype);
   if (overlap(o, obytes, state, heads * dk * dv * sizeof(float)) ||
       overlap(o, obytes, q, heads * dk * esize(dtype)) || overlap(o, obytes, k, heads * dk * esize(dtype)) ||
-      overlap(o, obytes, v, obytes) || overlap(o, obytes, log_alpha, heads * dk * esize(dtype)))
+      overlap(o, obytes, v, obytes) || overlap(o, obytes, log_alpha, heads * gdim * esize(dtype)))
     return KDA_ERROR_INVALID_VALUE;
   kda::DecodeArgs a;
   a.q = q;
@@ -142,7 +173,16 @@ extern "C" kda_status kda_decode_step(const void* q, const void* k, const void* 
   a.dk = dk;
   a.dv = dv;
   a.dtype_bf16 = dtype == KDA_DTYPE_BF16;
+  a.options = options;
   a.stream = stream;
   hipError_t e = kda::launch_decode(a);
   return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+}
+
+extern "C" kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                                      const void* log_alpha, const void* beta, float* state,
+                                      void* o, int32_t num_seqs, int32_t num_heads, int32_t dk,
+                                      int32_t dv, kda_dtype dtype, void* stream) {
+  return kda_decode_step_ex(q, k, v, log_alpha, beta, state, o, num_seqs, num_heads, dk, dv,
+                            dtype, 0u, stream);
 }

@@ -258,13 +258,16 @@ struct PrepParams {
   int64_t E;          // entries per segment
   char* rec;          // record buffer of the segment
   int64_t rec_bytes;
+  uint32_t opts;      // input option bits (OPT_*)
 };
 
 // One workgroup of 4 waves per (chunk, head); wave w owns sub-block w (tokens 16w .. 16w+15).
 // Lane (m, g) = (lane % 16, lane / 16) holds token 16w + m and the channels 16u + 4g .. +3,
 // u = 0 .. K/16-1, which is exactly that token's MFMA fragment over the channels. Phases are
 // separated by LDS-only barriers; record stores stay in flight.
-template <int K, typename MT>
+// OPTS = false compiles the kernel without the input-option code (options == 0), which keeps
+// that path's register allocation and schedule free of it.
+template <int K, typename MT, bool OPTS>
 __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   using L = PrepLayout<K, MT>;
   using R = Rec<K, MT>;
@@ -320,7 +323,10 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   };
   // Rows past the chunk's end load the last valid row again; they are zeroed after conversion
   // (q = k = 0, log alpha = 0, beta = 0 there), so every load is unconditional.
-  // part 0: q; part 1: k; part 2: log alpha and beta; part -1: everything
+  // part 0: q; part 1: k; part 2: log alpha and beta; part -1: everything. A scalar gate (one
+  // value per token and head) is loaded into element 0 of r.g[0].
+  const uint32_t opts = OPTS ? p.opts : 0u;
+  const bool scalar_gate = (opts & OPT_SCALAR_GATE) != 0;
   auto load_raw = [&](Raw& r, TaskPos tp, int task, int part) {
     const int hh = task % H;
     const int64_t tl = tp.tok + min(t0, tp.len - 1);
@@ -329,8 +335,10 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     for (int u = 0; u < NG; ++u) {
       if (part < 0 || part == 0) r.q[u] = *reinterpret_cast<const raw4*>(gq_ + row + 16 * u);
       if (part < 0 || part == 1) r.k[u] = *reinterpret_cast<const raw4*>(gk_ + row + 16 * u);
-      if (part < 0 || part == 2) r.g[u] = *reinterpret_cast<const raw4*>(gg_ + row + 16 * u);
+      if ((part < 0 || part == 2) && !scalar_gate)
+        r.g[u] = *reinterpret_cast<const raw4*>(gg_ + row + 16 * u);
     }
+    if ((part < 0 || part == 2) && scalar_gate) r.g[0][0] = gg_[tl * H + hh];
     if (part < 0 || part == 2) r.b = gb_[tl * H + hh];
   };
   int task = blockIdx.x;
@@ -363,15 +371,42 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     // their rows of W and Delta (their columns of P meet only those zero rows of Delta) -- while
     // log alpha = 0 keeps the decay products of the valid tokens.
     float qv[NG][4], kv[NG][4], lv[NG][4];
+    const bool gate_logits = (opts & OPT_GATE_LOGITS) != 0;
+    auto log2_alpha = [&](float z) { return gate_logits ? log2_sigmoid(z) : z * LOG2E; };
+    const float l0 = valid ? log2_alpha(to_f32(cur.g[0][0])) : 0.f;  // the scalar gate
   #pragma unroll
     for (int u = 0; u < NG; ++u)
   #pragma unroll
       for (int r = 0; r < 4; ++r) {
         qv[u][r] = to_f32(cur.q[u][r]);
         kv[u][r] = to_f32(cur.k[u][r]);
-        lv[u][r] = valid ? to_f32(cur.g[u][r]) * LOG2E : 0.f;
+        lv[u][r] = scalar_gate ? l0 : valid ? log2_alpha(to_f32(cur.g[u][r])) : 0.f;
       }
-    const float bval = to_f32(cur.b);
+    if (opts & OPT_L2NORM_QK) {
+      // the token's K channels sit in the four lanes m, m + 16, m + 32, m + 48
+      float sq = 0.f, sk = 0.f;
+  #pragma unroll
+      for (int u = 0; u < NG; ++u)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sq += qv[u][r] * qv[u][r];
+          sk += kv[u][r] * kv[u][r];
+        }
+      sq += __shfl_xor(sq, 16);
+      sk += __shfl_xor(sk, 16);
+      sq += __shfl_xor(sq, 32);
+      sk += __shfl_xor(sk, 32);
+      const float nq = 1.f / sqrtf(sq + L2NORM_EPS), nk = 1.f / sqrtf(sk + L2NORM_EPS);
+  #pragma unroll
+      for (int u = 0; u < NG; ++u)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          qv[u][r] *= nq;
+          kv[u][r] *= nk;
+        }
+    }
+    float bval = to_f32(cur.b);
+    if (opts & OPT_BETA_LOGITS) bval = sigmoid_f(bval);
     if (g == 0) sBeta[t] = valid ? bval : 0.f;
     // inclusive cumsum of log2 alpha over the 16 tokens of the sub-block (one 16-lane row):
     // lv becomes b_t - e_{w-1}; dI = e_w - e_{w-1} is the row's last value (log2 units)
@@ -1129,8 +1164,11 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
   auto prep = [&](int64_t s, hipStream_t q) {
     char* rec = ws + pl.off_rec;
     PrepParams pp{a.q, a.k, a.g, a.beta, entries, header, a.num_heads, s * pl.seg_entries,
-                  pl.seg_entries, rec, pl.rec_bytes};
-    hipLaunchKernelGGL((prep_kernel<K, MT>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+                  pl.seg_entries, rec, pl.rec_bytes, a.options};
+    if (a.options == 0)
+      hipLaunchKernelGGL((prep_kernel<K, MT, false>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+    else
+      hipLaunchKernelGGL((prep_kernel<K, MT, true>), pgrid, dim3(PREP_THREADS), 0, q, pp);
   };
   auto state = [&](int64_t s, hipStream_t q) -> bool {
     const char* rec = ws + pl.off_rec;

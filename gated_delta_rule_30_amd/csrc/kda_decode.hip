@@ -9,6 +9,9 @@
 // HBM once into registers, reduces u and S'^T q across row groups through LDS, and writes
 // the updated state back once. The state is touched exactly once per step, so loads and
 // stores are non-temporal. The kernel is HBM-bound: 2*K*V*4 bytes of state traffic per head.
+// Input options: a scalar gate per head, alpha = sigmoid(z) from gate logits, beta from
+// logits, and unit-norm q and k. Since u, S'^T q and k.q are linear in k and q, the sums are
+// formed from the raw k and q and scaled by the inverse norms afterwards.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -55,7 +58,7 @@ template <int K, int V, typename TI>
 __global__ __launch_bounds__((DecodeShape<K, V>::TPB)) void decode_step_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const TI* __restrict__ g, const TI* __restrict__ beta, float* __restrict__ state,
-    TI* __restrict__ o) {
+    TI* __restrict__ o, uint32_t opts) {
   using DS = DecodeShape<K, V>;
   constexpr int CG = DS::CG;
   constexpr int RG = DS::RG;
@@ -72,20 +75,46 @@ __global__ __launch_bounds__((DecodeShape<K, V>::TPB)) void decode_step_kernel(
 
   const TI* qh = q + (size_t)head * K;
   const TI* kh = k + (size_t)head * K;
-  const TI* gh = g + (size_t)head * K;
+  const bool scalar_gate = (opts & OPT_SCALAR_GATE) != 0;
+  const bool gate_logits = (opts & OPT_GATE_LOGITS) != 0;
+  const TI* gh = g + (size_t)head * (scalar_gate ? 1 : K);
   float a[RPT], kk[RPT];
   f32x4 pu = {0.f, 0.f, 0.f, 0.f}, pw = {0.f, 0.f, 0.f, 0.f};
   float pkq = 0.f;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + RG * i;
-    a[i] = exp_f(to_f32(gh[r]));
+    const float z = to_f32(gh[scalar_gate ? 0 : r]);
+    a[i] = gate_logits ? sigmoid_f(z) : exp_f(z);
     kk[i] = to_f32(kh[r]);
     const float qq = to_f32(qh[r]);
     pu += (a[i] * kk[i]) * s[i];
     pw += (a[i] * qq) * s[i];
     pkq += kk[i] * qq;
   }
+
+  // unit-norm k and q: every wave sums the squares of the whole k and q (K <= 256 values),
+  // and the sums that are linear in k or q are scaled afterwards
+  float nk = 1.f, nq = 1.f;
+  if (opts & OPT_L2NORM_QK) {
+    const int lane = tid & 63;
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int c = lane; c < K; c += 64) {
+      const float x = to_f32(kh[c]), y = to_f32(qh[c]);
+      sk += x * x;
+      sq += y * y;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      sk += __shfl_xor(sk, off);
+      sq += __shfl_xor(sq, off);
+    }
+    nk = 1.f / sqrtf(sk + L2NORM_EPS);
+    nq = 1.f / sqrtf(sq + L2NORM_EPS);
+  }
+  float b = to_f32(beta[head]);
+  if (opts & OPT_BETA_LOGITS) b = sigmoid_f(b);
 
   __shared__ f32x4 red_u[RG][CG];
   __shared__ f32x4 red_w[RG][CG];
@@ -103,12 +132,14 @@ __global__ __launch_bounds__((DecodeShape<K, V>::TPB)) void decode_step_kernel(
     w += red_w[r][cg];
     kq += red_kq[r];
   }
+  u *= nk;
+  w *= nq;
+  kq *= nk * nq;
   const f32x4 vv = load4(v + (size_t)head * V + 4 * cg);
-  const float b = to_f32(beta[head]);
   const f32x4 d = b * (vv - u);
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    f32x4 ns = a[i] * s[i] + kk[i] * d;
+    f32x4 ns = a[i] * s[i] + (kk[i] * nk) * d;
     __builtin_nontemporal_store(ns, &S[(rg + RG * i) * CG + cg]);
   }
   if (rg == 0) store4(o + (size_t)head * V + 4 * cg, w + kq * d);
@@ -119,7 +150,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int heads = a.num_seqs * a.num_heads;
   hipLaunchKernelGGL((decode_step_kernel<K, V, TI>), dim3(heads), dim3(DecodeShape<K, V>::TPB), 0,
                      (hipStream_t)a.stream, (const TI*)a.q, (const TI*)a.k, (const TI*)a.v,
-                     (const TI*)a.g, (const TI*)a.beta, a.state, (TI*)a.o);
+                     (const TI*)a.g, (const TI*)a.beta, a.state, (TI*)a.o, a.options);
   return hipGetLastError();
 }
 
@@ -127,9 +158,10 @@ template <typename TI>
 static hipError_t launch_decode_dt(const DecodeArgs& a) {
 #define KDA_DEC_CASE(KK, VV) \
   if (a.dk == KK && a.dv == VV) return launch_decode_t<KK, VV, TI>(a);
-  KDA_DEC_CASE(32, 32) KDA_DEC_CASE(32, 64) KDA_DEC_CASE(32, 128)
-  KDA_DEC_CASE(64, 32) KDA_DEC_CASE(64, 64) KDA_DEC_CASE(64, 128)
-  KDA_DEC_CASE(128, 32) KDA_DEC_CASE(128, 64) KDA_DEC_CASE(128, 128)
+  KDA_DEC_CASE(32, 32) KDA_DEC_CASE(32, 64) KDA_DEC_CASE(32, 128) KDA_DEC_CASE(32, 256)
+  KDA_DEC_CASE(64, 32) KDA_DEC_CASE(64, 64) KDA_DEC_CASE(64, 128) KDA_DEC_CASE(64, 256)
+  KDA_DEC_CASE(128, 32) KDA_DEC_CASE(128, 64) KDA_DEC_CASE(128, 128) KDA_DEC_CASE(128, 256)
+  KDA_DEC_CASE(256, 32) KDA_DEC_CASE(256, 64) KDA_DEC_CASE(256, 128) KDA_DEC_CASE(256, 256)
 #undef KDA_DEC_CASE
   return hipErrorInvalidValue;
 }

@@ -28,6 +28,16 @@ __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Input prologue (the option bits of the C ABI). log2(sigmoid(z)) = -log2(1 + 2^{-z log2 e}),
+// evaluated as min(z, 0) log2 e - log2(1 + 2^{-|z| log2 e}) so that nothing overflows for any
+// finite z; v_log_f32 is the hardware base-2 logarithm.
+__device__ __forceinline__ float log2_sigmoid(float z) {
+  return fminf(z, 0.f) * LOG2E - __builtin_amdgcn_logf(1.f + exp2_f(-fabsf(z) * LOG2E));
+}
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return __builtin_amdgcn_rcpf(1.f + exp2_f(-x * LOG2E));  // 1 / inf = 0 for very negative x
+}
+
 // ------------------------------------------------------------------ MFMA 16x16 tiles
 // A "fragment" is what one lane feeds to one 16x16xKS reduction step: 16 bytes.
 // Lane l has row/column index m = l % 16 and group g = l / 16.

@@ -12,6 +12,12 @@ constexpr int SUBBLK = 16;    // sub-block edge = MFMA tile edge
 constexpr int NSUB = CHUNK / SUBBLK;
 constexpr int NTHREADS = 256;  // threads per workgroup of every chunk kernel
 
+// Input option bits (the KDA_OPT_* values of the C ABI).
+constexpr uint32_t OPT_SCALAR_GATE = 1u, OPT_GATE_LOGITS = 2u, OPT_BETA_LOGITS = 4u,
+                   OPT_L2NORM_QK = 8u;
+// Added to the sum of squares before the L2 normalisation of q and k.
+constexpr float L2NORM_EPS = 1e-6f;
+
 // Target number of (chunk, head) records per segment: the segment's record buffer (66 KB per
 // record at K=V=128 bf16, 135 MB) then stays resident in the 256 MB Infinity Cache.
 constexpr int64_t SEG_CHUNK_HEADS = 2048;
@@ -22,6 +28,7 @@ struct DecodeArgs {
   void* o;
   int num_seqs, num_heads, dk, dv;
   bool dtype_bf16;
+  uint32_t options;  // KDA_OPT_* bits
   void* stream;
 };
 
@@ -63,6 +70,7 @@ struct ChunkArgs {
   int64_t total_tokens;
   int num_heads, dk, dv;
   bool dtype_bf16;
+  uint32_t options;  // KDA_OPT_* bits
   void* o;
   float* final_state;
   void* workspace;

@@ -12,15 +12,19 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library never allocates
  *    or frees device memory and keeps no per-call state. Tensor pointers must be 16-byte
- *    aligned, except beta and cu_seqlens, which need only their element alignment.
+ *    aligned, except beta, cu_seqlens and a scalar gate (KDA_OPT_SCALAR_GATE), which need
+ *    only their element alignment.
  *  - Layouts are row-major and token-major. q, k, log_alpha: [rows][H][K]; v: [rows][H][V];
  *    beta: [rows][H]; o: [rows][H][V]; states: [N][H][K][V] fp32 (element (c, j) of S at
  *    c*V + j, c = key channel, j = value channel).
  *  - dtype selects the element type of q, k, v, log_alpha, beta and o (fp32 or bf16). States
  *    are always fp32. Outputs are rounded to nearest even when dtype is bf16.
  *  - log_alpha is the natural log of the per-channel decay alpha (expected <= 0); no query
- *    scale is applied and q, k are used as given (no normalisation inside).
- *  - Supported head dims: K, V in {32, 64, 128}. Other values give KDA_ERROR_NOT_SUPPORTED.
+ *    scale is applied and q, k are used as given (no normalisation inside). The _ex entry
+ *    points take options that change how these inputs are read (KDA_OPT_* below).
+ *  - Supported head dims: kda_chunk_fwd K in {32, 64, 128} (K = 128 only with bf16 inputs),
+ *    V in {32, 64, 128, 256}; kda_decode_step K, V in {32, 64, 128, 256}. Other values give
+ *    KDA_ERROR_NOT_SUPPORTED.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
  *    returns without waiting. Argument errors are reported synchronously before anything is
  *    enqueued; a failed launch gives KDA_ERROR_LAUNCH. Values are not checked on the device:
@@ -41,7 +45,7 @@ extern "C" {
 typedef enum {
   KDA_SUCCESS = 0,
   KDA_ERROR_INVALID_VALUE = 1,       /* NULL pointer, misaligned pointer, bad size/count */
-  KDA_ERROR_NOT_SUPPORTED = 2,       /* head dims outside {32, 64, 128}, unknown dtype */
+  KDA_ERROR_NOT_SUPPORTED = 2,       /* unsupported head dims, dtype or option bits */
   KDA_ERROR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below kda_chunk_fwd_workspace_size */
   KDA_ERROR_LAUNCH = 4               /* a kernel launch or stream operation failed */
 } kda_status;
@@ -50,6 +54,29 @@ typedef enum {
   KDA_DTYPE_F32 = 0,  /* IEEE fp32 */
   KDA_DTYPE_BF16 = 1  /* bfloat16 */
 } kda_dtype;
+
+/*
+ * Input options of kda_chunk_fwd_ex and kda_decode_step_ex: a bitwise OR of these values, 0 for
+ * the operator exactly as above. They fold the elementwise steps that produce the operator's
+ * inputs into the kernels, so that the raw tensors are read once. Unknown bits give
+ * KDA_ERROR_NOT_SUPPORTED.
+ *  KDA_OPT_SCALAR_GATE  log_alpha holds one value per token and head, [rows][H], and every key
+ *                       channel of the head decays by it: the gated delta rule, whose gate scales
+ *                       the whole memory ("A Technical Breakdown", section 3.2).
+ *  KDA_OPT_GATE_LOGITS  log_alpha holds the pre-activation z of alpha = sigmoid(z) (the gate of
+ *                       the "Kimi Linear" explainer, "Step 2: Per-Channel Decay"); the kernels
+ *                       form log alpha = -log(1 + e^{-z}) without overflow for any finite z.
+ *  KDA_OPT_BETA_LOGITS  beta holds x and the write strength is sigmoid(x).
+ *  KDA_OPT_L2NORM_QK    q and k are each scaled to unit L2 norm over the K key channels, per
+ *                       token and head: x / sqrt(sum_c x_c^2 + 1e-6).
+ * The options combine freely (e.g. SCALAR_GATE | GATE_LOGITS: one logit per token and head).
+ */
+enum {
+  KDA_OPT_SCALAR_GATE = 1u,
+  KDA_OPT_GATE_LOGITS = 2u,
+  KDA_OPT_BETA_LOGITS = 4u,
+  KDA_OPT_L2NORM_QK = 8u
+};
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kda_status_string(kda_status s);
@@ -96,6 +123,18 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_fwd with input options (KDA_OPT_*); options = 0 is kda_chunk_fwd. With
+ * KDA_OPT_SCALAR_GATE, log_alpha is [T_total][H]. The workspace size does not depend on the
+ * options.
+ */
+kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                            const void* beta, const float* init_state, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t dk,
+                            int32_t dv, kda_dtype dtype, uint32_t options, void* o,
+                            float* final_state, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * One recurrent KDA token step per (sequence, head), state updated in place (decode).
  * The decay, prediction u = (Diag(alpha) S)^T k, erase-and-write and read are fused into one
  * pass that streams each fp32 state once from HBM and writes it once.
@@ -107,6 +146,15 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
                            const void* beta, float* state, void* o, int32_t num_seqs,
                            int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype,
                            void* stream);
+
+/*
+ * kda_decode_step with input options (KDA_OPT_*); options = 0 is kda_decode_step. With
+ * KDA_OPT_SCALAR_GATE, log_alpha is [N][H].
+ */
+kda_status kda_decode_step_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                              const void* beta, float* state, void* o, int32_t num_seqs,
+                              int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype,
+                              uint32_t options, void* stream);
 
 #ifdef __cplusplus
 }

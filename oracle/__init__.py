@@ -4,16 +4,28 @@ TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the benchmark's CP
 baseline leg may import this package; the product path (the HIP library and its
 Python binding) never does, and shares no code with it.
 
-The arithmetic lives in ``kda_oracle.c`` (plain C, fp64, one token at a time, OpenMP over
-(sequence, head)). This module only builds/loads that file and marshals numpy arrays.
-Inputs are converted to float32 first, which is exact for bf16 and fp32 values, so the
-oracle consumes exactly the numbers the GPU received.
+The recurrence lives in ``kda_oracle.c`` (plain C, fp64, one token at a time, OpenMP over
+(sequence, head)). This module builds/loads that file, marshals numpy arrays, and applies
+the optional input prologue (``apply_options``) in fp64 numpy before the recurrence.
+Inputs are converted to float64, which is exact for bf16 and fp32 values, so the oracle
+consumes exactly the numbers the GPU received.
 
 The definition it follows is the KDA update of "Kimi Linear's Hybrid Linear Attention
 Architecture: A Technical Breakdown" section 3.3 (decay, then erase along k, then write),
 with the orientation of the update-rule code block of "Kimi Linear: How Moonshot AI Built
 a Hybrid Attention Architecture That Beats Full Attention" (S is K x V, write k v^T), and
 the output read after the write ("Kimi Linear" explainer, "Step 4: Query").
+
+Input options (the bit values of the library's public option flags):
+  OPT_SCALAR_GATE  one gate value per token and head, shared by every key channel: the gated
+                   delta rule of "A Technical Breakdown", section 3.2 (the whole memory decays
+                   by one scalar before the erase and write).
+  OPT_GATE_LOGITS  the gate input is z with alpha = sigmoid(z) ("Kimi Linear" explainer,
+                   "Step 2: Per-Channel Decay"), so log alpha = log sigmoid(z).
+  OPT_BETA_LOGITS  the beta input is x with beta = sigmoid(x) (a reading: the pages call beta
+                   a learned write strength in (0, 1) without fixing its activation).
+  OPT_L2NORM_QK    q and k are scaled to unit L2 norm per token and head (a reading of the
+                   L2-normalised q and k of the workloads), x / sqrt(sum x^2 + 1e-6).
 """
 from __future__ import annotations
 
@@ -29,6 +41,12 @@ _SRC = os.path.join(_HERE, "kda_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "_kda_oracle.so")
 _lock = threading.Lock()
 _lib = None
+
+OPT_SCALAR_GATE = 1
+OPT_GATE_LOGITS = 2
+OPT_BETA_LOGITS = 4
+OPT_L2NORM_QK = 8
+L2NORM_EPS = 1e-6
 
 
 def build(force: bool = False) -> str:
@@ -66,8 +84,44 @@ def max_threads() -> int:
     return int(_load().kda_oracle_max_threads())
 
 
-def _f32(a) -> np.ndarray:
-    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def log_sigmoid(z):
+    """log(1 / (1 + e^{-z})) in fp64, as -log(e^0 + e^{-z}) through numpy's logaddexp, which
+    does not overflow for any finite z."""
+    return -np.logaddexp(0.0, -np.asarray(z, dtype=np.float64))
+
+
+def sigmoid(x):
+    """1 / (1 + e^{-x}) in fp64, as exp(log_sigmoid(x))."""
+    return np.exp(log_sigmoid(x))
+
+
+def l2_normalize(x, eps: float = L2NORM_EPS):
+    """x / sqrt(sum of squares over the last axis + eps), fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def apply_options(q, k, gate, beta, options: int):
+    """The input prologue selected by ``options`` (OPT_* bits), in fp64.
+
+    q, k: [..., K]; gate: [..., K], or [...] with OPT_SCALAR_GATE; beta: [...].
+    Returns (q, k, log_alpha [..., K], beta) ready for the recurrence.
+    """
+    q, k, g, b = _f64(q), _f64(k), _f64(gate), _f64(beta)
+    K = q.shape[-1]
+    if options & OPT_L2NORM_QK:
+        q, k = l2_normalize(q), l2_normalize(k)
+    if options & OPT_GATE_LOGITS:
+        g = log_sigmoid(g)
+    if options & OPT_SCALAR_GATE:
+        g = np.repeat(g[..., None], K, axis=-1)
+    if options & OPT_BETA_LOGITS:
+        b = sigmoid(b)
+    return q, k, np.ascontiguousarray(g), b
 
 
 def _ptr(a: np.ndarray):
@@ -75,17 +129,19 @@ def _ptr(a: np.ndarray):
 
 
 def kda_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, heads=None,
-            threads: int = 0):
+            threads: int = 0, options: int = 0):
     """Token-by-token fp64 KDA forward.
 
     q, k, log_alpha: [T, H, K]; v: [T, H, V]; beta: [T, H] (any float dtype numpy arrays).
+    options: OPT_* bits (log_alpha is [T, H] with OPT_SCALAR_GATE); see apply_options.
     cu_seqlens: [N+1] int (None = one sequence of length T).
     init_state: [N, H, K, V] (None = zeros).
     heads: optional list of head indices to compute (outputs then hold only those heads).
     Returns (o [T, Hs, V] float64, final_state [N, Hs, K, V] float64).
     """
     lib = _load()
-    q, k, v, g, b = _f32(q), _f32(k), _f32(v), _f32(log_alpha), _f32(beta)
+    q, k, g, b = apply_options(q, k, log_alpha, beta, options)
+    v = _f64(v)
     T, H, K = q.shape
     V = v.shape[2]
     assert k.shape == (T, H, K) and g.shape == (T, H, K) and v.shape[:2] == (T, H)
@@ -117,11 +173,13 @@ def kda_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, init_state=None, heads=No
     return o, fin
 
 
-def kda_step(q, k, v, log_alpha, beta, state: np.ndarray, threads: int = 0):
+def kda_step(q, k, v, log_alpha, beta, state: np.ndarray, threads: int = 0, options: int = 0):
     """One fp64 recurrent step for N x H heads; ``state`` [N, H, K, V] float64 is updated
-    in place. q, k, log_alpha: [N, H, K]; v: [N, H, V]; beta: [N, H]. Returns o [N, H, V]."""
+    in place. q, k, log_alpha: [N, H, K] (log_alpha [N, H] with OPT_SCALAR_GATE);
+    v: [N, H, V]; beta: [N, H]. Returns o [N, H, V]."""
     lib = _load()
-    q, k, v, g, b = _f32(q), _f32(k), _f32(v), _f32(log_alpha), _f32(beta)
+    q, k, g, b = apply_options(q, k, log_alpha, beta, options)
+    v = _f64(v)
     N, H, K = q.shape
     V = v.shape[2]
     assert state.dtype == np.float64 and state.flags["C_CONTIGUOUS"]

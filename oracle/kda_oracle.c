@@ -19,7 +19,9 @@
  *
  * Readings (see the design notes): alpha = exp(log_alpha) per key channel; beta is one
  * scalar per token and head; no query scaling; no normalisation of q or k; o_t = S_t^T q_t
- * with S_t the state after token t; state never crosses a sequence boundary.
+ * with S_t the state after token t; state never crosses a sequence boundary. Inputs arrive
+ * in fp64: the exact values the GPU received, or the fp64 result of the input options
+ * (gate and beta activations, q/k normalisation), which the Python wrapper applies first.
  *
  * Step for one token (all in fp64):
  *   1. S[c][:] *= exp(g[c])                   decay first            [TB] 3.3
@@ -37,32 +39,32 @@
 #endif
 
 /* One token of one (sequence, head). S is K x V row-major, fp64. */
-static void oracle_token(double* S, int K, int V, const float* q, const float* k,
-                         const float* v, const float* g, double beta, double* o,
+static void oracle_token(double* S, int K, int V, const double* q, const double* k,
+                         const double* v, const double* g, double beta, double* o,
                          double* u /* scratch, V */) {
   /* 1. per-channel decay of the old memory */
   for (int c = 0; c < K; ++c) {
-    const double a = exp((double)g[c]);
+    const double a = exp(g[c]);
     double* row = S + (size_t)c * V;
     for (int j = 0; j < V; ++j) row[j] *= a;
   }
   /* 2. prediction of the decayed memory along k */
   for (int j = 0; j < V; ++j) u[j] = 0.0;
   for (int c = 0; c < K; ++c) {
-    const double kc = (double)k[c];
+    const double kc = k[c];
     const double* row = S + (size_t)c * V;
     for (int j = 0; j < V; ++j) u[j] += row[j] * kc;
   }
   /* 3. erase along k and write v (delta correction) */
   for (int c = 0; c < K; ++c) {
-    const double bk = beta * (double)k[c];
+    const double bk = beta * k[c];
     double* row = S + (size_t)c * V;
-    for (int j = 0; j < V; ++j) row[j] += bk * ((double)v[j] - u[j]);
+    for (int j = 0; j < V; ++j) row[j] += bk * (v[j] - u[j]);
   }
   /* 4. read with the query after the write */
   for (int j = 0; j < V; ++j) o[j] = 0.0;
   for (int c = 0; c < K; ++c) {
-    const double qc = (double)q[c];
+    const double qc = q[c];
     const double* row = S + (size_t)c * V;
     for (int j = 0; j < V; ++j) o[j] += row[j] * qc;
   }
@@ -80,7 +82,7 @@ static int pick_threads(int32_t requested) {
 
 /*
  * Full forward over packed variable-length sequences.
- *   q, k, g : [T_total][H][K]  float (exact copies of the bf16 / fp32 inputs)
+ *   q, k, g : [T_total][H][K]  double
  *   v       : [T_total][H][V]
  *   beta    : [T_total][H]
  *   cu_seqlens : [N+1] int64, sequence n is tokens cu[n] .. cu[n+1]-1
@@ -90,8 +92,8 @@ static int pick_threads(int32_t requested) {
  *   final_state : [N][num_sel][K][V] fp64 out (may be NULL)
  * Returns 0, or -1 on a bad argument.
  */
-int kda_oracle_fwd(const float* q, const float* k, const float* v, const float* g,
-                   const float* beta, const int64_t* cu_seqlens, int32_t num_seqs,
+int kda_oracle_fwd(const double* q, const double* k, const double* v, const double* g,
+                   const double* beta, const int64_t* cu_seqlens, int32_t num_seqs,
                    int32_t num_heads, int32_t dk, int32_t dv, const double* init_state,
                    const int32_t* heads, int32_t num_sel, double* o, double* final_state,
                    int32_t num_threads) {
@@ -118,7 +120,7 @@ int kda_oracle_fwd(const float* q, const float* k, const float* v, const float* 
     for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
       const size_t th = (size_t)t * H + h;
       oracle_token(S, K, V, q + th * K, k + th * K, v + th * V, g + th * K,
-                   (double)beta[th], o + ((size_t)t * num_sel + hs) * V, u);
+                   beta[th], o + ((size_t)t * num_sel + hs) * V, u);
     }
     if (final_state)
       memcpy(final_state + ((size_t)n * num_sel + hs) * K * V, S, sizeof(double) * K * V);
@@ -129,12 +131,12 @@ int kda_oracle_fwd(const float* q, const float* k, const float* v, const float* 
 
 /*
  * One recurrent decode step for N sequences x H heads, state updated in place.
- *   q, k, g : [N][H][K], v : [N][H][V], beta : [N][H]  (float)
+ *   q, k, g : [N][H][K], v : [N][H][V], beta : [N][H]  (double)
  *   state   : [N][H][K][V] fp64, in/out
  *   o       : [N][H][V] fp64 out
  */
-int kda_oracle_step(const float* q, const float* k, const float* v, const float* g,
-                    const float* beta, int32_t num_seqs, int32_t num_heads, int32_t dk,
+int kda_oracle_step(const double* q, const double* k, const double* v, const double* g,
+                    const double* beta, int32_t num_seqs, int32_t num_heads, int32_t dk,
                     int32_t dv, double* state, double* o, int32_t num_threads) {
   if (!q || !k || !v || !g || !beta || !state || !o) return -1;
   if (num_seqs <= 0 || num_heads <= 0 || dk <= 0 || dv <= 0) return -1;
@@ -146,7 +148,7 @@ int kda_oracle_step(const float* q, const float* k, const float* v, const float*
     double* u = (double*)malloc(sizeof(double) * V);
     if (!u) { bad = 1; continue; }
     oracle_token(state + (size_t)p * K * V, K, V, q + (size_t)p * K, k + (size_t)p * K,
-                 v + (size_t)p * V, g + (size_t)p * K, (double)beta[p], o + (size_t)p * V, u);
+                 v + (size_t)p * V, g + (size_t)p * K, beta[p], o + (size_t)p * V, u);
     free(u);
   }
   return bad ? -1 : 0;

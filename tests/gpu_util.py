@@ -21,13 +21,14 @@ def rel_err(got, ref):
     return float(np.abs(got - ref).max()) / scale
 
 
-def oracle_fwd(inp, cu=None, heads=None):
+def oracle_fwd(inp, cu=None, heads=None, options=0):
     """Run the oracle on exactly the tensors the GPU received."""
     cu_np = None if cu is None else cu.cpu().numpy().astype(np.int64)
     init = inp.get("init_state")
     init_np = None if init is None else np64(init)
     return oracle.kda_fwd(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), np64(inp["log_alpha"]),
-                          np64(inp["beta"]), cu_seqlens=cu_np, init_state=init_np, heads=heads)
+                          np64(inp["beta"]), cu_seqlens=cu_np, init_state=init_np, heads=heads,
+                          options=options)
 
 
 def assert_close(got, ref, dtype, what):

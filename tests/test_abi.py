@@ -17,8 +17,8 @@ F32, BF16 = 0, 1
 
 def test_every_declared_symbol_is_exported():
     names = kda.declared_functions()
-    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_decode_step",
-                          "kda_status_string"}
+    assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_fwd_workspace_size",
+                          "kda_decode_step", "kda_decode_step_ex", "kda_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
@@ -67,12 +67,16 @@ A = 1 << 20
 
 def _chunk(L, **kw):
     a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, init=None, cu=None, N=1, T=64, H=2,
-             dk=32, dv=32, dtype=BF16, o=6 * A, fin=7 * A, ws=8 * A, wsb=1 << 40, stream=None)
+             dk=32, dv=32, dtype=BF16, o=6 * A, fin=7 * A, ws=8 * A, wsb=1 << 40, stream=None,
+             opts=None)
     a.update(kw)
     vp = ctypes.c_void_p
-    return L.kda_chunk_fwd(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]),
-                           vp(a["init"]), vp(a["cu"]), a["N"], a["T"], a["H"], a["dk"], a["dv"],
-                           a["dtype"], vp(a["o"]), vp(a["fin"]), vp(a["ws"]), a["wsb"], vp(a["stream"]))
+    head = (vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]), vp(a["init"]),
+            vp(a["cu"]), a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"])
+    tail = (vp(a["o"]), vp(a["fin"]), vp(a["ws"]), a["wsb"], vp(a["stream"]))
+    if a["opts"] is None:
+        return L.kda_chunk_fwd(*head, *tail)
+    return L.kda_chunk_fwd_ex(*head, a["opts"], *tail)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -81,7 +85,12 @@ def _chunk(L, **kw):
     (dict(T=-5), INVALID),
     (dict(T=1 << 31), INVALID),
     (dict(dk=48), NOT_SUPPORTED),
-    (dict(dv=256), NOT_SUPPORTED),
+    (dict(dk=256), NOT_SUPPORTED),         # the chunk path takes K <= 128
+    (dict(dv=512), NOT_SUPPORTED),
+    (dict(opts=16), NOT_SUPPORTED),        # unknown option bit
+    (dict(opts=1 << 31), NOT_SUPPORTED),
+    (dict(opts=15, q=None), INVALID),
+    (dict(opts=0, dk=48), NOT_SUPPORTED),
     (dict(dtype=7), NOT_SUPPORTED),
     (dict(dtype=F32, dk=128), NOT_SUPPORTED),
     (dict(N=3, T=64), INVALID),            # equal lengths need T % N == 0
@@ -96,6 +105,13 @@ def _chunk(L, **kw):
     (dict(wsb=1024), WS_SMALL),
     (dict(init=9 * A, fin=9 * A + 256), INVALID),   # partial overlap of init and final
     (dict(o=A), INVALID),                  # o overlaps q
+    # o = [64 x 2 x 32] bf16 = 8 KB; a per-channel gate [64 x 2 x 32] at o - 6 KB overlaps it,
+    # a scalar gate [64 x 2] there (256 B) does not, so only the check itself can fail then
+    (dict(g=6 * A - 6144), INVALID),
+    (dict(g=6 * A - 6144, opts=1, wsb=1024), WS_SMALL),
+    (dict(g=4 * A + 2), INVALID),          # a per-channel gate needs 16 bytes
+    (dict(g=4 * A + 2, opts=1, wsb=1024), WS_SMALL),   # a scalar gate its element
+    (dict(g=4 * A + 1, opts=1), INVALID),
 ])
 def test_chunk_fwd_argument_errors(kw, expect):
     assert _chunk(kda.lib(), **kw) == expect
@@ -103,24 +119,31 @@ def test_chunk_fwd_argument_errors(kw, expect):
 
 def _decode(L, **kw):
     a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, state=6 * A, o=7 * A, N=2, H=2, dk=32,
-             dv=32, dtype=BF16, stream=None)
+             dv=32, dtype=BF16, stream=None, opts=None)
     a.update(kw)
     vp = ctypes.c_void_p
-    return L.kda_decode_step(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]),
-                             vp(a["state"]), vp(a["o"]), a["N"], a["H"], a["dk"], a["dv"],
-                             a["dtype"], vp(a["stream"]))
+    head = (vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]), vp(a["state"]),
+            vp(a["o"]), a["N"], a["H"], a["dk"], a["dv"], a["dtype"])
+    if a["opts"] is None:
+        return L.kda_decode_step(*head, vp(a["stream"]))
+    return L.kda_decode_step_ex(*head, a["opts"], vp(a["stream"]))
 
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(N=0), INVALID),
     (dict(H=-1), INVALID),
     (dict(dk=100), NOT_SUPPORTED),
+    (dict(dv=512), NOT_SUPPORTED),
+    (dict(opts=32), NOT_SUPPORTED),
+    (dict(opts=15, q=None), INVALID),
     (dict(dtype=3), NOT_SUPPORTED),
     (dict(state=None), INVALID),
     (dict(o=None), INVALID),
     (dict(k=2 * A + 2), INVALID),
     (dict(beta=5 * A + 1), INVALID),
     (dict(o=6 * A), INVALID),              # o overlaps the state
+    (dict(g=4 * A + 2), INVALID),
+    (dict(g=4 * A + 1, opts=1), INVALID),
 ])
 def test_decode_step_argument_errors(kw, expect):
     assert _decode(kda.lib(), **kw) == expect

@@ -9,6 +9,7 @@ import shutil
 import subprocess
 import tempfile
 
+import numpy as np
 import pytest
 
 import oracle
@@ -18,7 +19,7 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "kda_oracle.c")
 
 DECAY_BLOCK = """  /* 1. per-channel decay of the old memory */
   for (int c = 0; c < K; ++c) {
-    const double a = exp((double)g[c]);
+    const double a = exp(g[c]);
     double* row = S + (size_t)c * V;
     for (int j = 0; j < V; ++j) row[j] *= a;
   }
@@ -27,14 +28,14 @@ READ_BLOCK_HEAD = "  /* 4. read with the query after the write */\n"
 
 MUTATIONS = {
     "no_decay": [("row[j] *= a;", "row[j] *= 1.0;")],
-    "gate_sign": [("exp((double)g[c])", "exp(-(double)g[c])")],
-    "no_beta": [("const double bk = beta * (double)k[c];", "const double bk = (double)k[c];")],
-    "no_erase": [("row[j] += bk * ((double)v[j] - u[j]);", "row[j] += bk * ((double)v[j]);")],
-    "erase_sign": [("row[j] += bk * ((double)v[j] - u[j]);", "row[j] += bk * ((double)v[j] + u[j]);")],
+    "gate_sign": [("const double a = exp(g[c]);", "const double a = exp(-g[c]);")],
+    "no_beta": [("const double bk = beta * k[c];", "const double bk = k[c];")],
+    "no_erase": [("row[j] += bk * (v[j] - u[j]);", "row[j] += bk * (v[j]);")],
+    "erase_sign": [("row[j] += bk * (v[j] - u[j]);", "row[j] += bk * (v[j] + u[j]);")],
     "transposed_read": [("for (int j = 0; j < V; ++j) o[j] += row[j] * qc;",
-                         "for (int j = 0; j < V; ++j) o[c < V ? c : 0] += row[j] * (double)q[j < K ? j : 0] * (c < V);")],
+                         "for (int j = 0; j < V; ++j) o[c < V ? c : 0] += row[j] * q[j < K ? j : 0] * (c < V);")],
     "decay_after_write": [(DECAY_BLOCK, ""), (READ_BLOCK_HEAD, DECAY_BLOCK + READ_BLOCK_HEAD)],
-    "transposed_key_in_prediction": [("u[j] += row[j] * kc;", "u[j] += row[j] * (double)k[j < K ? j : 0] * (c == 0);")],
+    "transposed_key_in_prediction": [("u[j] += row[j] * kc;", "u[j] += row[j] * k[j < K ? j : 0] * (c == 0);")],
 }
 
 PIN_TESTS = [
@@ -102,3 +103,46 @@ def test_unmutated_copy_passes_every_pin():
     finally:
         oracle._lib = real
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+# ---------------------------------------------------------------- the input prologue (numpy)
+OPTION_PINS = [
+    lambda: pins.test_log_sigmoid_values(),
+    lambda: pins.test_sigmoid_values(),
+    lambda: pins.test_l2_normalize_values(),
+    lambda: pins.test_scalar_gate_option_is_gated_delta_rule(),
+    lambda: pins.test_gate_logits_with_tiny_beta_is_pure_decay(),
+    lambda: pins.test_l2norm_and_saturated_beta_recall_values(),
+    lambda: pins.test_l2norm_option_is_scale_invariant_and_matches_numpy_norm(),
+]
+
+_real_apply = oracle.apply_options
+
+
+def _apply_ignoring(bit):
+    return lambda q, k, g, b, options: _real_apply(q, k, g, b, options & ~bit)
+
+
+PROLOGUE_MUTATIONS = {
+    "log_sigmoid_sign": ("log_sigmoid", lambda z: np.logaddexp(0.0, -np.asarray(z, dtype=np.float64))),
+    "log_sigmoid_of_minus_z": ("log_sigmoid", lambda z: -np.logaddexp(0.0, np.asarray(z, dtype=np.float64))),
+    "sigmoid_of_minus_x": ("sigmoid", lambda x: 1.0 / (1.0 + np.exp(np.asarray(x, dtype=np.float64)))),
+    "l2_without_sqrt": ("l2_normalize", lambda x, eps=1e-6: np.asarray(x) / (np.sum(np.asarray(x) ** 2, axis=-1, keepdims=True) + eps)),
+    "l2_over_wrong_axis": ("l2_normalize", lambda x, eps=1e-6: np.asarray(x) / np.sqrt(np.sum(np.asarray(x) ** 2, axis=0, keepdims=True) + eps)),
+    "gate_logits_ignored": ("apply_options", _apply_ignoring(oracle.OPT_GATE_LOGITS)),
+    "beta_logits_ignored": ("apply_options", _apply_ignoring(oracle.OPT_BETA_LOGITS)),
+    "l2norm_ignored": ("apply_options", _apply_ignoring(oracle.OPT_L2NORM_QK)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PROLOGUE_MUTATIONS))
+def test_option_pins_catch_prologue_mutation(name, monkeypatch):
+    attr, fn = PROLOGUE_MUTATIONS[name]
+    monkeypatch.setattr(oracle, attr, fn)
+    caught = []
+    for i, t in enumerate(OPTION_PINS):
+        try:
+            t()
+        except (AssertionError, ValueError):
+            caught.append(i)
+    assert caught, "mutation %s survived every option pin" % name

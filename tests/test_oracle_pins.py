@@ -278,3 +278,130 @@ def test_head_subset_matches_full():
     os_, fs = oracle.kda_fwd(q, k, v, g, beta, heads=[3, 1])
     np.testing.assert_array_equal(os_, o[:, [3, 1]])
     np.testing.assert_array_equal(fs, fin[:, [3, 1]])
+
+
+# ---------------------------------------------------------------- input options
+# The prologue the option bits select: the gated delta rule's scalar gate ("A Technical
+# Breakdown" 3.2), alpha = sigmoid(z) ("Kimi Linear" explainer, Step 2), beta = sigmoid(x) and
+# unit-norm q, k (readings). Pinned by textbook values and identities of the activations and by
+# closed forms of the recurrence reached through the option path.
+def test_log_sigmoid_values():
+    ls = oracle.log_sigmoid
+    assert ls(0.0) == pytest.approx(-np.log(2.0), rel=0, abs=1e-15)
+    z = np.linspace(-30, 30, 121)
+    np.testing.assert_allclose(ls(z) - ls(-z), z, rtol=0, atol=1e-12)  # log(s(z)/s(-z)) = z
+    assert np.all(np.diff(ls(z)) > 0) and np.all(ls(z) < 0)
+    assert ls(40.0) == pytest.approx(-np.exp(-40.0), rel=1e-12)
+    assert ls(-800.0) == pytest.approx(-800.0, rel=1e-15)  # no overflow
+    np.testing.assert_allclose(ls(np.log(3.0)), np.log(0.75), rtol=1e-15)
+
+
+def test_sigmoid_values():
+    s = oracle.sigmoid
+    assert s(0.0) == 0.5
+    x = np.linspace(-20, 20, 81)
+    np.testing.assert_allclose(s(x) + s(-x), 1.0, rtol=0, atol=1e-15)
+    assert s(np.log(3.0)) == pytest.approx(0.75, rel=1e-15)
+    assert s(-800.0) == 0.0 and s(800.0) == 1.0
+
+
+def test_l2_normalize_values():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((7, 3, 16)) * rng.uniform(0.1, 10.0, (7, 3, 1))
+    y = oracle.l2_normalize(x)
+    n2 = np.sum(x * x, axis=-1)
+    np.testing.assert_allclose(np.sum(y * y, axis=-1), n2 / (n2 + oracle.L2NORM_EPS), rtol=1e-13)
+    cos = np.sum(x * y, axis=-1) / np.linalg.norm(x, axis=-1) / np.linalg.norm(y, axis=-1)
+    np.testing.assert_allclose(cos, 1.0, rtol=1e-14)
+    assert np.all(oracle.l2_normalize(np.zeros((2, 5))) == 0.0)
+
+
+def test_scalar_gate_option_is_gated_delta_rule():
+    """OPT_SCALAR_GATE with gate logits: S_t = a_t (I - beta k k^T) S_{t-1} + beta k v^T with
+    a_t = 1 / (1 + e^{-z_t}), written out per token."""
+    rng = np.random.default_rng(8)
+    T, H, K, V = 13, 2, 5, 4
+    q, k, v, _, beta = _rand_inputs(rng, T, H, K, V)
+    z = rng.uniform(-1.0, 4.0, (T, H))
+    S0 = rng.standard_normal((1, H, K, V))
+    opts = oracle.OPT_SCALAR_GATE | oracle.OPT_GATE_LOGITS
+    o, fin = oracle.kda_fwd(q, k, v, z, beta, init_state=S0, options=opts)
+    for h in range(H):
+        S = S0[0, h].copy()
+        for t in range(T):
+            a = 1.0 / (1.0 + np.exp(-z[t, h]))
+            kt = k[t, h]
+            S = a * ((np.eye(K) - beta[t, h] * np.outer(kt, kt)) @ S) + beta[t, h] * np.outer(kt, v[t, h])
+            np.testing.assert_allclose(o[t, h], S.T @ q[t, h], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(fin[0, h], S, rtol=1e-11, atol=1e-12)
+
+
+def test_gate_logits_with_tiny_beta_is_pure_decay():
+    """OPT_GATE_LOGITS | OPT_BETA_LOGITS, beta logits -60 (beta ~ 1e-26): nothing is written,
+    so S_t = Diag(prod_s sigmoid(z_s)) S_0 and o_t = S_t^T q_t."""
+    rng = np.random.default_rng(9)
+    T, K, V = 9, 6, 3
+    q = rng.standard_normal((T, 1, K))
+    k = rng.standard_normal((T, 1, K))
+    v = rng.standard_normal((T, 1, V))
+    z = rng.uniform(-2.0, 5.0, (T, 1, K))
+    x = np.full((T, 1), -60.0)
+    S0 = rng.standard_normal((1, 1, K, V))
+    opts = oracle.OPT_GATE_LOGITS | oracle.OPT_BETA_LOGITS
+    o, fin = oracle.kda_fwd(q, k, v, z, x, init_state=S0, options=opts)
+    dec = np.cumprod(1.0 / (1.0 + np.exp(-z[:, 0, :])), axis=0)  # [T, K]
+    for t in range(T):
+        np.testing.assert_allclose(o[t, 0], (dec[t][:, None] * S0[0, 0]).T @ q[t, 0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(fin[0, 0], dec[-1][:, None] * S0[0, 0], rtol=1e-12, atol=1e-12)
+
+
+def test_l2norm_and_saturated_beta_recall_values():
+    """OPT_L2NORM_QK | OPT_BETA_LOGITS with beta logits +40 (beta = 1 in fp64): the keys are
+    unit vectors up to the 1e-6 in the norm, so each token's write is recalled exactly along
+    its own key, k_t^T S_t = v_t^T, whatever the decay ("A Technical Breakdown" 3.1: the old
+    content along k is erased before v is written)."""
+    rng = np.random.default_rng(10)
+    T, K, V = 11, 8, 5
+    q = rng.standard_normal((T, 1, K))
+    k = rng.standard_normal((T, 1, K)) * rng.uniform(0.5, 20.0, (T, 1, 1))
+    v = rng.standard_normal((T, 1, V))
+    g = np.log(rng.uniform(0.3, 1.0, (T, 1, K)))
+    x = np.full((T, 1), 40.0)
+    opts = oracle.OPT_L2NORM_QK | oracle.OPT_BETA_LOGITS
+    for t_end in (4, T):
+        _, fin = oracle.kda_fwd(q[:t_end], k[:t_end], v[:t_end], g[:t_end], x[:t_end], options=opts)
+        kt = k[t_end - 1, 0] / np.linalg.norm(k[t_end - 1, 0])
+        np.testing.assert_allclose(kt @ fin[0, 0], v[t_end - 1, 0], rtol=0, atol=1e-7)
+
+
+def test_l2norm_option_is_scale_invariant_and_matches_numpy_norm():
+    """Scaling raw q and k by positive factors changes nothing beyond the 1e-6 in the norm, and
+    the result equals the plain recurrence on q / |q|, k / |k| (numpy's norm) to that level."""
+    rng = np.random.default_rng(11)
+    T, H, K, V = 10, 2, 6, 4
+    q, k, v, g, beta = _rand_inputs(rng, T, H, K, V, unit_k=False)
+    o1, f1 = oracle.kda_fwd(q, k, v, g, beta, options=oracle.OPT_L2NORM_QK)
+    c = rng.uniform(2.0, 9.0, (T, H, 1))
+    o2, f2 = oracle.kda_fwd(q * c, k / c, v, g, beta, options=oracle.OPT_L2NORM_QK)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-5 * np.abs(o1).max())
+    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    o3, f3 = oracle.kda_fwd(qn, kn, v, g, beta)
+    np.testing.assert_allclose(o1, o3, rtol=0, atol=1e-5 * np.abs(o3).max())
+    np.testing.assert_allclose(f1, f3, rtol=0, atol=1e-5 * np.abs(f3).max())
+
+
+def test_decode_step_options_match_fwd():
+    """The decode oracle applies the same prologue: one step per token equals kda_fwd."""
+    rng = np.random.default_rng(12)
+    T, H, K, V = 6, 3, 4, 5
+    q, k, v, _, _ = _rand_inputs(rng, T, H, K, V, unit_k=False)
+    z = rng.uniform(-1.0, 3.0, (T, H))
+    x = rng.uniform(-3.0, 3.0, (T, H))
+    opts = 15
+    o, fin = oracle.kda_fwd(q, k, v, z, x, options=opts)
+    S = np.zeros((1, H, K, V))
+    for t in range(T):
+        ot = oracle.kda_step(q[t:t + 1], k[t:t + 1], v[t:t + 1], z[t:t + 1], x[t:t + 1], S, options=opts)
+        np.testing.assert_allclose(ot[0], o[t], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(S, fin, rtol=1e-13, atol=1e-13)

@@ -118,6 +118,48 @@ def gen_forward(T_total: int, H: int, K: int, V: int, *, gates: str = "uniform",
     return out
 
 
+# option bits of the operator's input prologue (the public KDA_OPT_* values)
+OPT_SCALAR_GATE, OPT_GATE_LOGITS, OPT_BETA_LOGITS, OPT_L2NORM_QK = 1, 2, 4, 8
+
+
+def gen_raw(T_total: int, H: int, K: int, V: int, options: int, *, dtype=None, device="cpu",
+            seed: int = 0, num_seqs: int = 1, init_std: float | None = None):
+    """Seeded raw inputs for the option bits, token-major:
+    q, k ~ N(0,1), times U(0.5, 4) per token and head with OPT_L2NORM_QK (left for the kernel
+    to normalise), else L2-normalised here; v ~ N(0,1); the gate [T, H, K] or, with
+    OPT_SCALAR_GATE, [T, H]: logits z ~ U(2, 7) with OPT_GATE_LOGITS (alpha = sigmoid(z) in
+    [0.88, 0.999]), else log alpha = log U[0.9, 1); beta logits ~ 1.5 N(0,1) with
+    OPT_BETA_LOGITS, else beta ~ U(0, 1). Every tensor is cast to ``dtype``."""
+    torch = _torch()
+    dtype = dtype or torch.bfloat16
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    f = dict(generator=gen, device=device, dtype=torch.float32)
+    out = {}
+    for name in ("q", "k"):
+        x = torch.randn((T_total, H, K), **f)
+        if options & OPT_L2NORM_QK:
+            x = x * (0.5 + 3.5 * torch.rand((T_total, H, 1), **f))
+        else:
+            x = x / x.norm(dim=-1, keepdim=True)
+        out[name] = x.to(dtype)
+    out["v"] = torch.randn((T_total, H, V), **f).to(dtype)
+    gshape = (T_total, H) if options & OPT_SCALAR_GATE else (T_total, H, K)
+    if options & OPT_GATE_LOGITS:
+        g = 2.0 + 5.0 * torch.rand(gshape, **f)
+    else:
+        g = torch.log(0.9 + 0.1 * torch.rand(gshape, **f))
+    out["log_alpha"] = g.to(dtype)
+    if options & OPT_BETA_LOGITS:
+        b = 1.5 * torch.randn((T_total, H), **f)
+    else:
+        b = torch.rand((T_total, H), **f)
+    out["beta"] = b.to(dtype)
+    out["init_state"] = (None if init_std is None else
+                         init_std * torch.randn((num_seqs, H, K, V), **f))
+    return out
+
+
 def gen_decode_inputs(N: int, H: int, K: int, V: int, *, dtype=None, device="cpu",
                       gen=None, seed: int = 0):
     """One decode step's inputs [N, H, .] drawn as in the 'tiny' workload."""
