@@ -1091,6 +1091,309 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
   }
 }
 
+// ---------------------------------------------------------------------- two-wave state kernel
+// The chain of one (sequence run, head, 16-column slice) split by key channels over the two
+// waves of a workgroup: wave w holds rows [w K/2, (w+1) K/2) of S and streams only the record
+// fragments of its half -- -W and Qe over its reduction steps, Ktilde^T over its rows -- plus
+// T' of the next chunk (wave 0) or P (wave 1). Per chunk:
+//   Delta_w = [U] + (-W_w) S_w       partial over this wave's half of K (wave 0 starts from U)
+//   exchange Delta_w through LDS, Delta = Delta_0 + Delta_1 (fp32), one barrier
+//   S_w' = Diag(gamma_w) S_w + Ktilde_w^T Delta
+//   O^T = S_0^T Qe_0^T + S_1^T Qe_1^T + Delta^T P^T     (partials; summed at the next exchange)
+// Each wave issues half of the chunk's matrix-core and vector work and keeps two chunks of its
+// fragments in flight (a ring of 2 NF registers; the loop handles chunks in pairs so that every
+// ring slot has a fixed register). The two halves of the output meet at the next chunk's
+// exchange: each wave keeps half of the token tiles of O and receives the partner's partial
+// for them. Exchange buffers alternate by chunk parity, so a write never meets the partner's
+// read of the previous chunk. Measured on the long prefill this is a few percent faster than
+// one wave per chain: the chain stays bound by the fragments' round trips through L2 (the
+// CU's L1 reports stalls on pending L2 data for about 40% of the kernel's time either way).
+template <int K, typename MT>
+struct SplitShape {
+  using SH = StateShape<K, MT>;
+  static constexpr int KS = SH::KS, NKT = SH::NKT, NKS = SH::NKS, NTT = SH::NTT, NTS = SH::NTS;
+  static constexpr int NTRI = SH::NTRI;
+  static constexpr bool OK = NKS % 2 == 0 && NTT % 2 == 0;
+  static constexpr int HKS = NKS / 2;  // reduction steps over K per wave
+  static constexpr int HKT = NKT / 2;  // key-channel tiles of S per wave
+  static constexpr int HT = NTT / 2;   // output token tiles each wave stores
+  static constexpr int NA = 2 * NTT * HKS;      // -W and Qe, interleaved per step
+  static constexpr int NB = HKT * NTS;          // Ktilde^T over this wave's rows
+  static constexpr int NF = NA + NB + NTRI;     // + T' (wave 0) or P (wave 1)
+};
+constexpr int SPLIT_THREADS = 128;
+
+template <int K, typename MT>
+__global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_split_kernel(StateParams p) {
+  using SH = StateShape<K, MT>;
+  using SS = SplitShape<K, MT>;
+  using R = Rec<K, MT>;
+  using M = Mma<MT>;
+  using frag = typename M::frag;
+  constexpr int KS = SS::KS, NKS = SS::NKS, NTT = SS::NTT, NTS = SS::NTS, NTRI = SS::NTRI;
+  constexpr int HKS = SS::HKS, HKT = SS::HKT, HT = SS::HT, NA = SS::NA, NB = SS::NB, NF = SS::NF;
+  constexpr int LDV = SH::LDV;
+  constexpr int VL = 16 / (int)sizeof(MT);
+  constexpr int NVL = 16 / VL;
+  using vload = typename VecN<MT, VL>::vec;
+  static_assert(SS::OK, "two-wave split needs an even number of K steps and token tiles");
+  static_assert(HKT == HKS * (KS / 16), "a wave's K steps cover its key tiles");
+  __shared__ __align__(16) f32x4 sX[2][2][NTT][64];  // [parity][wave][token tile][lane]: Delta partials
+  __shared__ __align__(16) f32x4 sO[2][2][HT][64];   // [parity][wave][tile][lane]: O partials for the partner
+  __shared__ __align__(16) MT sV[CHUNK * LDV];       // wave 0: V of the next chunk
+  __shared__ int32_t sRun[SEG_CHUNK_HEADS + 16];
+  __shared__ int32_t sLen;
+
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int rr = bid >> 3;
+  const int slice = rr % p.n_slices;
+  const int64_t chain = (int64_t)(rr / p.n_slices) * 8 + xcd;
+  if (chain >= p.chains) return;
+  const int H = p.H, V = p.V;
+  const int64_t slot = chain / H;
+  const int h = (int)(chain % H);
+  if (slot >= p.seg_count[0]) return;
+  const int64_t total = p.header[0];
+  const int64_t seg_end = min(p.seg_begin + p.E, total);
+  const int64_t e0 = p.seg_first[slot];
+  const Entry en = p.entries[e0];
+  const int col0 = slice * 16;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int m = lane & 15;
+  const int g = lane >> 4;
+
+  const int seq_start = en.tok - CHUNK * en.depth;
+  const int nc = (en.end - seq_start + CHUNK - 1) / CHUNK;
+  const int64_t rank = e0 - p.basetab[en.depth];
+  const int kmax = (int)min((int64_t)(nc - en.depth), p.E);
+  if (tid == 0) sLen = kmax;
+  __syncthreads();
+  for (int k = tid; k < kmax; k += SPLIT_THREADS) {
+    const int64_t ek = p.basetab[en.depth + k] + rank;
+    sRun[k] = (int32_t)(ek - p.seg_begin);
+    if (ek >= seg_end) atomicMin(&sLen, k);
+  }
+  __syncthreads();
+  const int run = sLen;
+
+  const size_t sbase = ((size_t)en.seq * H + h) * (size_t)K * V + col0;
+  const float* src = (en.depth == 0) ? p.init_state : p.state;
+  const uint32_t rowb = (uint32_t)(H * V * (int)sizeof(MT));
+  const MT* gv = reinterpret_cast<const MT*>(p.v) + (int64_t)h * V + col0;
+  MT* go = reinterpret_cast<MT*>(p.o) + (int64_t)h * V + col0;
+  auto tok_of = [&](int k) { return seq_start + CHUNK * (en.depth + k); };
+  auto len_of = [&](int k) { return min(CHUNK, en.end - tok_of(k)); };
+  auto rows_rsrc = [&](const MT* base, int k) {
+    const int kk = min(k, run - 1);
+    return make_rsrc(base + (int64_t)tok_of(kk) * (H * V), (uint32_t)len_of(kk) * rowb);
+  };
+  const uint32_t v_voff = (uint32_t)lane * rowb;
+  const uint32_t o_voff = (uint32_t)m * rowb + 4u * g * (uint32_t)sizeof(MT);
+  const rsrc_t rrec = make_rsrc(p.rec, p.rec_buf_bytes);
+  const uint32_t rec_h = (uint32_t)h * p.rec_bytes;
+  const uint32_t rec_stride = (uint32_t)H * p.rec_bytes;
+  auto rec_off = [&](int ri) { return rec_h + (uint32_t)ri * rec_stride; };
+  const uint32_t lo = 16u * (uint32_t)lane;
+  auto ldf = [&](uint32_t rc, uint32_t off) -> frag {
+    return buf_load16<frag>(rrec, lo + (off & 4095u), rc + (off & ~4095u));
+  };
+  auto rec_index = [&](int k) { return __builtin_amdgcn_readfirstlane(sRun[min(k, run - 1)]); };
+
+  auto body = [&](auto WVc) {
+    constexpr int WV = decltype(WVc)::value;
+    // operation j of this wave's stream reads the next chunk's record (wave 0's T') or this one's
+    auto next_rec = [](int j) constexpr { return WV == 0 && j >= NA + NB; };
+    auto frag_off = [](auto J) constexpr -> uint32_t {
+      constexpr int j = decltype(J)::value;
+      constexpr uint32_t SLOT = 64 * 16;
+      if constexpr (j < NA) {
+        constexpr int s = WV * HKS + j / (2 * NTT), r = j % (2 * NTT), tt = r % NTT;
+        constexpr size_t base = (r < NTT ? R::oW : R::oQ) * sizeof(MT);
+        return (uint32_t)(base + (size_t)(tt * NKS + s) * SLOT);
+      } else if constexpr (j < NA + NB) {
+        constexpr int jj = j - NA, s = jj / HKT, kt = WV * HKT + jj % HKT;
+        return (uint32_t)(R::oKt * sizeof(MT) + (size_t)(kt * NTS + s) * SLOT);
+      } else {
+        constexpr int i = j - NA - NB;
+        constexpr size_t base = (WV == 0 ? R::oTb : R::oPb) * sizeof(MT);
+        return (uint32_t)(base + (size_t)(SH::tri_t(i) * NTS + SH::tri_s(i)) * SLOT);
+      }
+    };
+    // gamma of this wave's rows: lane (m, g) needs rows 16 kt + 4g .. +3 of its tiles
+    auto load_gam = [&](uint32_t rc, f32x4 (&x)[HKT]) {
+#pragma unroll
+      for (int i = 0; i < HKT; ++i) {
+        const uint32_t off = (uint32_t)R::oGamBytes + 64u * (uint32_t)(WV * HKT + i);
+        x[i] = buf_load16<f32x4>(rrec, 16u * (uint32_t)g + (off & 4095u), rc + (off & ~4095u));
+      }
+    };
+    auto load_v = [&](int k, vload (&x)[NVL]) {
+      const rsrc_t r = rows_rsrc(gv, k);
+#pragma unroll
+      for (int i = 0; i < NVL; ++i) x[i] = buf_load16<vload>(r, v_voff + 16u * i, 0);
+    };
+    auto stage_v = [&](const vload (&x)[NVL]) {
+#pragma unroll
+      for (int i = 0; i < NVL; ++i) *reinterpret_cast<vload*>(sV + lane * LDV + VL * i) = x[i];
+    };
+
+    // this wave's rows of S: local tile i is key tile WV * HKT + i
+    f32x4 S[HKT];
+#pragma unroll
+    for (int i = 0; i < HKT; ++i) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (src != nullptr) {
+        const float* ps = src + sbase + (size_t)(16 * (WV * HKT + i) + 4 * g) * V + m;
+        x = f32x4{ps[0], ps[V], ps[2 * V], ps[3 * V]};
+      }
+      S[i] = x;
+    }
+
+    uint32_t rc0 = rec_off(rec_index(0));
+    uint32_t rc1 = rec_off(rec_index(1));
+    uint32_t rc2 = rec_off(rec_index(2));
+    f32x4 U[NTT], O[NTT], Okeep[HT];
+    frag Vf[NTS];
+    vload vx[NVL];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) U[tt] = O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (WV == 0) {
+      load_v(0, vx);
+      stage_v(vx);
+#pragma unroll
+      for (int s = 0; s < NTS; ++s) Vf[s] = frag_t(sV, LDV, 0, s, lane);
+      static_for<0, NTRI>([&](auto I) {
+        constexpr int i = decltype(I)::value, tt = SH::tri_t(i), s = SH::tri_s(i);
+        constexpr uint32_t off = (uint32_t)(R::oTb * sizeof(MT) + (size_t)(tt * NTS + s) * 64 * 16);
+        U[tt] = M::mma(ldf(rc0, off), Vf[s], U[tt]);
+      });
+    }
+    f32x4 gnext[HKT], gcur[HKT];
+    load_gam(rc0, gnext);
+    __builtin_amdgcn_sched_barrier(0);
+    // ring slot P * NF + j holds operation j of the next chunk of parity P (chunks k, k + 1)
+    frag ring[2 * NF];
+    static_for<0, NF>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      ring[j] = ldf(next_rec(j) ? rc1 : rc0, frag_off(J));
+    });
+    static_for<0, NF>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      ring[NF + j] = ldf(next_rec(j) ? rc2 : rc1, frag_off(J));
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t rc3 = rec_off(rec_index(3));
+    int ri_pre = sRun[min(4, run - 1)];  // record index of chunk k + 4, read a chunk ahead
+    if constexpr (WV == 0) load_v(1, vx);
+    rsrc_t ro_prev = rows_rsrc(go, 0);
+
+    // one chunk; PAR = k & 1 selects the ring half and the exchange buffers
+    auto chunk = [&](auto PARc, const int k) {
+      constexpr int par = decltype(PARc)::value;
+      const rsrc_t ro = rows_rsrc(go, k);
+#pragma unroll
+      for (int i = 0; i < HKT; ++i) gcur[i] = gnext[i];
+      load_gam(rc1, gnext);
+      __builtin_amdgcn_sched_barrier(0);
+
+      frag Sb[HKS], Db[NTS];
+      static_for<0, NF>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if constexpr (j < NA && j % (2 * NTT) == 0) {
+          constexpr int s = j / (2 * NTT);
+          if constexpr (KS == 32) Sb[s] = frag_from_acc(S[2 * s], S[2 * s + 1], MT());
+          else Sb[s] = S[s];
+        }
+        if constexpr (j == NA) {
+          // exchange the Delta partials (and the previous chunk's output partials)
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt) sX[par][WV][tt][lane] = U[tt];
+          lds_barrier();
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt) U[tt] += sX[par][1 - WV][tt][lane];
+#pragma unroll
+          for (int s = 0; s < NTS; ++s) {
+            if constexpr (KS == 32) Db[s] = frag_from_acc(U[2 * s], U[2 * s + 1], MT());
+            else Db[s] = U[s];
+          }
+          if (k > 0) {
+#pragma unroll
+            for (int i = 0; i < HT; ++i) {
+              const f32x4 o = Okeep[i] + sO[par][1 - WV][i][lane];
+              buf_store(ro_prev, o_voff, (uint32_t)(16 * (WV * HT + i)) * rowb, to_mt4<MT>(o));
+            }
+          }
+        }
+        if constexpr (j >= NA && j < NA + HKT) S[j - NA] *= gcur[j - NA];
+        if constexpr (WV == 0 && j == NA + NB / 2) {
+          stage_v(vx);
+#pragma unroll
+          for (int s = 0; s < NTS; ++s) Vf[s] = frag_t(sV, LDV, 0, s, lane);
+        }
+        if constexpr (j == NA + NB) {
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt) U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (WV == 0) load_v(k + 2, vx);
+        }
+        const frag f = ring[par * NF + j];
+        if constexpr (j < NA) {
+          constexpr int s = j / (2 * NTT), r = j % (2 * NTT), tt = r % NTT;
+          if constexpr (r < NTT) U[tt] = M::mma(f, Sb[s], U[tt]);  // [U] - W S, this half
+          else O[tt] = M::mma(Sb[s], f, O[tt]);                    // S^T Qe^T, this half
+        } else if constexpr (j < NA + NB) {
+          constexpr int jj = j - NA, s = jj / HKT, i = jj % HKT;
+          S[i] = M::mma(f, Db[s], S[i]);  // + Ktilde^T Delta, this wave's rows
+        } else {
+          constexpr int i = j - NA - NB;
+          if constexpr (WV == 0) U[SH::tri_t(i)] = M::mma(f, Vf[SH::tri_s(i)], U[SH::tri_t(i)]);  // T'V, next chunk
+          else O[SH::tri_t(i)] = M::mma(Db[SH::tri_s(i)], f, O[SH::tri_t(i)]);               // + Delta^T P^T
+        }
+        // refill: the same operation two chunks on
+        ring[par * NF + j] = ldf(next_rec(j) ? rc3 : rc2, frag_off(J));
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // output partials: keep this wave's tiles, hand the partner its tiles
+#pragma unroll
+      for (int i = 0; i < HT; ++i) {
+        Okeep[i] = O[WV * HT + i];
+        sO[par ^ 1][WV][i][lane] = O[(1 - WV) * HT + i];
+      }
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ro_prev = ro;
+      // records of chunks k + 1 .. k + 4 for the next chunk
+      rc0 = rc1;
+      rc1 = rc2;
+      rc2 = rc3;
+      rc3 = rec_off(__builtin_amdgcn_readfirstlane(ri_pre));
+      ri_pre = sRun[min(k + 5, run - 1)];
+    };
+    for (int k = 0; k < run; k += 2) {
+      chunk(std::integral_constant<int, 0>(), k);
+      if (k + 1 < run) chunk(std::integral_constant<int, 1>(), k + 1);
+    }
+    // the last chunk's output
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < HT; ++i) {
+      const f32x4 o = Okeep[i] + sO[run & 1][1 - WV][i][lane];
+      buf_store(ro_prev, o_voff, (uint32_t)(16 * (WV * HT + i)) * rowb, to_mt4<MT>(o));
+    }
+#pragma unroll
+    for (int i = 0; i < HKT; ++i) {
+      float* ps = p.state + sbase + (size_t)(16 * (WV * HKT + i) + 4 * g) * V + m;
+      ps[0] = S[i][0];
+      ps[V] = S[i][1];
+      ps[2 * V] = S[i][2];
+      ps[3 * V] = S[i][3];
+    }
+  };
+  if (__builtin_amdgcn_readfirstlane(wave_id()) == 0) body(std::integral_constant<int, 0>());
+  else body(std::integral_constant<int, 1>());
+}
+
 // ====================================================================== host side
 bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan* p) {
   if (N <= 0 || H <= 0 || T < 0 || K <= 0 || V <= 0) return false;
@@ -1177,7 +1480,10 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
                    a.num_heads, a.dv, pl.n_slices, chains, rec, (uint32_t)pl.rec_bytes,
                    (uint32_t)pl.rec_buf_bytes};
     if (pl.vs != 16) return false;
-    hipLaunchKernelGGL((state_kernel<K, MT>), sgrid, dim3(STATE_THREADS), 0, q, sp);
+    if constexpr (SplitShape<K, MT>::OK)
+      hipLaunchKernelGGL((state_split_kernel<K, MT>), sgrid, dim3(SPLIT_THREADS), 0, q, sp);
+    else
+      hipLaunchKernelGGL((state_kernel<K, MT>), sgrid, dim3(STATE_THREADS), 0, q, sp);
     return true;
   };
 
