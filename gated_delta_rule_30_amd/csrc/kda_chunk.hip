@@ -1100,9 +1100,9 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
 //   exchange Delta_w through LDS, Delta = Delta_0 + Delta_1 (fp32), one barrier
 //   S_w' = Diag(gamma_w) S_w + Ktilde_w^T Delta
 //   O^T = S_0^T Qe_0^T + S_1^T Qe_1^T + Delta^T P^T     (partials; summed at the next exchange)
-// Each wave issues half of the chunk's matrix-core and vector work and keeps two chunks of its
-// fragments in flight (a ring of 2 NF registers; the loop handles chunks in pairs so that every
-// ring slot has a fixed register). The two halves of the output meet at the next chunk's
+// Each wave issues half of the chunk's matrix-core and vector work and keeps one chunk (or two:
+// a ring of 2 NF registers, for which the loop handles chunks in pairs so that every ring slot
+// has a fixed register) of its fragments in flight. The two halves of the output meet at the next chunk's
 // exchange: each wave keeps half of the token tiles of O and receives the partner's partial
 // for them. Exchange buffers alternate by chunk parity, so a write never meets the partner's
 // read of the previous chunk. Measured on the long prefill this is a few percent faster than
@@ -1120,6 +1120,9 @@ struct SplitShape {
   static constexpr int NA = 2 * NTT * HKS;      // -W and Qe, interleaved per step
   static constexpr int NB = HKT * NTS;          // Ktilde^T over this wave's rows
   static constexpr int NF = NA + NB + NTRI;     // + T' (wave 0) or P (wave 1)
+  // chunks of fragments in flight (1 or 2): the same time on the long prefill (2.24 ms per
+  // call), and one chunk needs 120 fewer registers
+  static constexpr int RING_CHUNKS = 1;
 };
 constexpr int SPLIT_THREADS = 128;
 
@@ -1273,16 +1276,20 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
     f32x4 gnext[HKT], gcur[HKT];
     load_gam(rc0, gnext);
     __builtin_amdgcn_sched_barrier(0);
-    // ring slot P * NF + j holds operation j of the next chunk of parity P (chunks k, k + 1)
-    frag ring[2 * NF];
+    // ring slot P * NF + j holds operation j of the next chunk of parity P (two chunks in
+    // flight), or slot j operation j of the next chunk (one chunk in flight)
+    constexpr int RC = SS::RING_CHUNKS;
+    static_assert(RC == 1 || RC == 2, "ring depth");
+    frag ring[RC * NF];
     static_for<0, NF>([&](auto J) {
       constexpr int j = decltype(J)::value;
       ring[j] = ldf(next_rec(j) ? rc1 : rc0, frag_off(J));
     });
-    static_for<0, NF>([&](auto J) {
-      constexpr int j = decltype(J)::value;
-      ring[NF + j] = ldf(next_rec(j) ? rc2 : rc1, frag_off(J));
-    });
+    if constexpr (RC == 2)
+      static_for<0, NF>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        ring[NF + j] = ldf(next_rec(j) ? rc2 : rc1, frag_off(J));
+      });
     __builtin_amdgcn_sched_barrier(0);
     uint32_t rc3 = rec_off(rec_index(3));
     int ri_pre = sRun[min(4, run - 1)];  // record index of chunk k + 4, read a chunk ahead
@@ -1337,7 +1344,8 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
           for (int tt = 0; tt < NTT; ++tt) U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
           if constexpr (WV == 0) load_v(k + 2, vx);
         }
-        const frag f = ring[par * NF + j];
+        constexpr int slot = (RC == 2 ? par * NF : 0) + j;
+        const frag f = ring[slot];
         if constexpr (j < NA) {
           constexpr int s = j / (2 * NTT), r = j % (2 * NTT), tt = r % NTT;
           if constexpr (r < NTT) U[tt] = M::mma(f, Sb[s], U[tt]);  // [U] - W S, this half
@@ -1350,8 +1358,9 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
           if constexpr (WV == 0) U[SH::tri_t(i)] = M::mma(f, Vf[SH::tri_s(i)], U[SH::tri_t(i)]);  // T'V, next chunk
           else O[SH::tri_t(i)] = M::mma(Db[SH::tri_s(i)], f, O[SH::tri_t(i)]);               // + Delta^T P^T
         }
-        // refill: the same operation two chunks on
-        ring[par * NF + j] = ldf(next_rec(j) ? rc3 : rc2, frag_off(J));
+        // refill: the same operation RC chunks on
+        if constexpr (RC == 2) ring[slot] = ldf(next_rec(j) ? rc3 : rc2, frag_off(J));
+        else ring[slot] = ldf(next_rec(j) ? rc2 : rc1, frag_off(J));
         __builtin_amdgcn_sched_barrier(0);
       });
       // output partials: keep this wave's tiles, hand the partner its tiles

@@ -74,6 +74,10 @@ def _load():
             s.restype = ctypes.c_int
             s.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 4 + [
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+            b = lib.kda_oracle_bwd
+            b.restype = ctypes.c_int
+            b.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 9 + [
+                ctypes.c_int32]
             lib.kda_oracle_max_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -190,3 +194,38 @@ def kda_step(q, k, v, log_alpha, beta, state: np.ndarray, threads: int = 0, opti
     if rc != 0:
         raise RuntimeError("kda_oracle_step failed (%d)" % rc)
     return o
+
+
+def kda_bwd(q, k, v, log_alpha, beta, dout, dfinal=None, cu_seqlens=None, init_state=None,
+            threads: int = 0):
+    """Gradients of kda_fwd for the loss sum(dout * o) + sum(dfinal * final_state), fp64.
+
+    Shapes as in kda_fwd; dout [T, H, V], dfinal [N, H, K, V] or None (zero).
+    Returns (dq, dk, dv, dlog_alpha, dbeta, dinit_state) as float64 arrays.
+    """
+    lib = _load()
+    q, k, v, g, b = _f64(q), _f64(k), _f64(v), _f64(log_alpha), _f64(beta)
+    do = _f64(dout)
+    T, H, K = q.shape
+    V = v.shape[2]
+    assert k.shape == (T, H, K) and g.shape == (T, H, K) and v.shape == (T, H, V)
+    assert b.shape == (T, H) and do.shape == (T, H, V)
+    cu = (np.array([0, T], dtype=np.int64) if cu_seqlens is None else
+          np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64)))
+    N = cu.shape[0] - 1
+    assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    init = None if init_state is None else _f64(init_state)
+    dfin = None if dfinal is None else _f64(dfinal)
+    for a in (init, dfin):
+        assert a is None or a.shape == (N, H, K, V)
+    dq, dk, dg = (np.zeros((T, H, K)) for _ in range(3))
+    dv = np.zeros((T, H, V))
+    db = np.zeros((T, H))
+    dinit = np.zeros((N, H, K, V))
+    P = lambda a: None if a is None else _ptr(a)
+    rc = lib.kda_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(cu), N, H, K, V,
+                            P(init), _ptr(do), P(dfin), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                            _ptr(db), _ptr(dinit), int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_bwd failed (%d)" % rc)
+    return dq, dk, dv, dg, db, dinit

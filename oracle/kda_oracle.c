@@ -154,4 +154,121 @@ int kda_oracle_step(const double* q, const double* k, const double* v, const dou
   return bad ? -1 : 0;
 }
 
+/*
+ * Gradients of the forward above (reverse mode, written from the four steps of one token).
+ * With the loss L = sum(do * o) + sum(dfinal * S_final), L_t = dL/dS_t accumulates backwards
+ * from dfinal. For token t, with S' = Diag(a) S_{t-1}, u = S'^T k, r = v - u:
+ *   L_t  += q do^T                       (o = S_t^T q)
+ *   dq    = S_t do
+ *   dbeta = k^T L_t r,   dk = beta L_t r,   dv = beta L_t^T k,   du = -dv
+ *   dS'   = L_t + k du^T,   dk += S' du  (u = S'^T k)
+ *   dlog_a[c] = a[c] sum_j S_{t-1}[c][j] dS'[c][j],   L_{t-1} = Diag(a) dS'
+ * and d init_state = L before the sequence's first token. The states S_t are recomputed by a
+ * forward pass over the sequence and kept (one K x V matrix per token).
+ *   dout  : [T_total][H][V]      dfinal : [N][H][K][V] or NULL (zero)
+ *   dq, dk, dg : [T_total][H][K]   dv : [T_total][H][V]   dbeta : [T_total][H]
+ *   dinit : [N][H][K][V] (may be NULL)
+ */
+int kda_oracle_bwd(const double* q, const double* k, const double* v, const double* g,
+                   const double* beta, const int64_t* cu_seqlens, int32_t num_seqs,
+                   int32_t num_heads, int32_t dk_, int32_t dv_, const double* init_state,
+                   const double* dout, const double* dfinal, double* dq, double* dk, double* dv,
+                   double* dg, double* dbeta, double* dinit, int32_t num_threads) {
+  if (!q || !k || !v || !g || !beta || !cu_seqlens || !dout || !dq || !dk || !dv || !dg || !dbeta)
+    return -1;
+  if (num_seqs <= 0 || num_heads <= 0 || dk_ <= 0 || dv_ <= 0) return -1;
+  const int K = dk_, V = dv_, H = num_heads;
+  const int64_t pairs = (int64_t)num_seqs * H;
+  const size_t KV = (size_t)K * V;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(pick_threads(num_threads)) reduction(| : bad)
+  for (int64_t p = 0; p < pairs; ++p) {
+    const int n = (int)(p / H), h = (int)(p % H);
+    const int64_t t0 = cu_seqlens[n], t1 = cu_seqlens[n + 1], L = t1 - t0;
+    double* St = (double*)malloc(sizeof(double) * ((size_t)(L + 1) * KV + 2 * KV + 4 * (size_t)(K + V)));
+    if (!St) { bad = 1; continue; }
+    double* Lam = St + (size_t)(L + 1) * KV;  /* dL/dS_t */
+    double* dS1 = Lam + KV;
+    double* u = dS1 + KV;
+    double* r = u + V;
+    double* dr = r + V;
+    double* tmpk = dr + V;
+    /* forward: St[i] = state after token t0 + i - 1 (St[0] = initial state) */
+    if (init_state) memcpy(St, init_state + ((size_t)n * H + h) * KV, sizeof(double) * KV);
+    else memset(St, 0, sizeof(double) * KV);
+    for (int64_t i = 0; i < L; ++i) {
+      const size_t th = (size_t)(t0 + i) * H + h;
+      double* S = St + (size_t)(i + 1) * KV;
+      memcpy(S, St + (size_t)i * KV, sizeof(double) * KV);
+      double* o_unused = tmpk;  /* the forward output is not needed here */
+      oracle_token(S, K, V, q + th * K, k + th * K, v + th * V, g + th * K, beta[th], o_unused, u);
+    }
+    /* backward */
+    if (dfinal) memcpy(Lam, dfinal + ((size_t)n * H + h) * KV, sizeof(double) * KV);
+    else memset(Lam, 0, sizeof(double) * KV);
+    for (int64_t i = L - 1; i >= 0; --i) {
+      const size_t th = (size_t)(t0 + i) * H + h;
+      const double* qt = q + th * K;
+      const double* kt = k + th * K;
+      const double* vt = v + th * V;
+      const double* gt = g + th * K;
+      const double* dot = dout + th * V;
+      const double b = beta[th];
+      const double* Sprev = St + (size_t)i * KV;
+      const double* Scur = St + (size_t)(i + 1) * KV;
+      /* L_t += q do^T; dq = S_t do */
+      for (int c = 0; c < K; ++c)
+        for (int j = 0; j < V; ++j) Lam[(size_t)c * V + j] += qt[c] * dot[j];
+      for (int c = 0; c < K; ++c) {
+        double acc = 0.0;
+        for (int j = 0; j < V; ++j) acc += Scur[(size_t)c * V + j] * dot[j];
+        dq[th * K + c] = acc;
+      }
+      /* u = (Diag(a) S_{t-1})^T k, r = v - u */
+      for (int j = 0; j < V; ++j) u[j] = 0.0;
+      for (int c = 0; c < K; ++c) {
+        const double a = exp(gt[c]);
+        for (int j = 0; j < V; ++j) u[j] += a * Sprev[(size_t)c * V + j] * kt[c];
+      }
+      for (int j = 0; j < V; ++j) r[j] = vt[j] - u[j];
+      /* dbeta = k^T L r; dk = beta L r; dr = beta L^T k */
+      double db = 0.0;
+      for (int c = 0; c < K; ++c) {
+        double lr = 0.0;
+        for (int j = 0; j < V; ++j) lr += Lam[(size_t)c * V + j] * r[j];
+        db += kt[c] * lr;
+        dk[th * K + c] = b * lr;
+      }
+      dbeta[th] = db;
+      for (int j = 0; j < V; ++j) {
+        double acc = 0.0;
+        for (int c = 0; c < K; ++c) acc += Lam[(size_t)c * V + j] * kt[c];
+        dr[j] = b * acc;
+        dv[th * V + j] = dr[j];
+      }
+      /* dS' = L + k du^T with du = -dr; dk += S' du */
+      for (int c = 0; c < K; ++c) {
+        const double a = exp(gt[c]);
+        double acc = 0.0;
+        for (int j = 0; j < V; ++j) {
+          dS1[(size_t)c * V + j] = Lam[(size_t)c * V + j] - kt[c] * dr[j];
+          acc -= a * Sprev[(size_t)c * V + j] * dr[j];
+        }
+        dk[th * K + c] += acc;
+      }
+      /* dlog a and L_{t-1} = Diag(a) dS' */
+      for (int c = 0; c < K; ++c) {
+        const double a = exp(gt[c]);
+        double acc = 0.0;
+        for (int j = 0; j < V; ++j) acc += Sprev[(size_t)c * V + j] * dS1[(size_t)c * V + j];
+        dg[th * K + c] = a * acc;
+        for (int j = 0; j < V; ++j) Lam[(size_t)c * V + j] = a * dS1[(size_t)c * V + j];
+      }
+    }
+    if (dinit) memcpy(dinit + ((size_t)n * H + h) * KV, Lam, sizeof(double) * KV);
+    free(St);
+  }
+  return bad ? -1 : 0;
+}
+
 int kda_oracle_max_threads(void) { return pick_threads(0); }

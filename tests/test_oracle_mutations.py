@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+import test_oracle_bwd_pins as bwd_pins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "kda_oracle.c")
@@ -36,7 +37,26 @@ MUTATIONS = {
                          "for (int j = 0; j < V; ++j) o[c < V ? c : 0] += row[j] * q[j < K ? j : 0] * (c < V);")],
     "decay_after_write": [(DECAY_BLOCK, ""), (READ_BLOCK_HEAD, DECAY_BLOCK + READ_BLOCK_HEAD)],
     "transposed_key_in_prediction": [("u[j] += row[j] * kc;", "u[j] += row[j] * k[j < K ? j : 0] * (c == 0);")],
+    # planted in the gradients
+    "bwd_du_sign": [("dS1[(size_t)c * V + j] = Lam[(size_t)c * V + j] - kt[c] * dr[j];",
+                     "dS1[(size_t)c * V + j] = Lam[(size_t)c * V + j] + kt[c] * dr[j];")],
+    "bwd_no_decay_on_adjoint": [("Lam[(size_t)c * V + j] = a * dS1[(size_t)c * V + j];",
+                                 "Lam[(size_t)c * V + j] = dS1[(size_t)c * V + j];")],
+    "bwd_dlog_alpha_without_alpha": [("dg[th * K + c] = a * acc;", "dg[th * K + c] = acc;")],
+    "bwd_dq_from_previous_state": [("acc += Scur[(size_t)c * V + j] * dot[j];",
+                                    "acc += Sprev[(size_t)c * V + j] * dot[j];")],
+    "bwd_output_grad_added_after_use": [
+        ("      for (int c = 0; c < K; ++c)\n        for (int j = 0; j < V; ++j) Lam[(size_t)c * V + j] += qt[c] * dot[j];\n", ""),
+        ("      /* dlog a and L_{t-1} = Diag(a) dS' */\n",
+         "      for (int c = 0; c < K; ++c)\n        for (int j = 0; j < V; ++j) dS1[(size_t)c * V + j] += qt[c] * dot[j];\n      /* dlog a and L_{t-1} = Diag(a) dS' */\n")],
+    "bwd_missing_prediction_term_in_dk": [("        dk[th * K + c] += acc;\n", "")],
 }
+
+BWD_PIN_TESTS = [
+    lambda: bwd_pins.test_gradients_match_central_differences([7], 2, 3, 4),
+    lambda: bwd_pins.test_gradients_match_central_differences([4, 0, 6], 1, 4, 3),
+    lambda: bwd_pins.test_zero_beta_closed_forms(),
+]
 
 PIN_TESTS = [
     lambda: pins.test_hand_example(),
@@ -70,13 +90,13 @@ def test_pins_catch_mutation(name):
     tmp = tempfile.mkdtemp()
     try:
         lib = ctypes.CDLL(_build_mutant(MUTATIONS[name], tmp))
-        for fn in ("kda_oracle_fwd", "kda_oracle_step"):
+        for fn in ("kda_oracle_fwd", "kda_oracle_step", "kda_oracle_bwd"):
             getattr(lib, fn).argtypes = getattr(real, fn).argtypes
             getattr(lib, fn).restype = ctypes.c_int
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         oracle._lib = lib
         caught = []
-        for i, t in enumerate(PIN_TESTS):
+        for i, t in enumerate(BWD_PIN_TESTS if name.startswith("bwd_") else PIN_TESTS):
             try:
                 t()
             except AssertionError:
@@ -94,11 +114,11 @@ def test_unmutated_copy_passes_every_pin():
     tmp = tempfile.mkdtemp()
     try:
         lib = ctypes.CDLL(_build_mutant([], tmp))
-        for fn in ("kda_oracle_fwd", "kda_oracle_step"):
+        for fn in ("kda_oracle_fwd", "kda_oracle_step", "kda_oracle_bwd"):
             getattr(lib, fn).argtypes = getattr(real, fn).argtypes
             getattr(lib, fn).restype = ctypes.c_int
         oracle._lib = lib
-        for t in PIN_TESTS:
+        for t in PIN_TESTS + BWD_PIN_TESTS:
             t()
     finally:
         oracle._lib = real
