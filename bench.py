@@ -57,7 +57,7 @@ def decode_alg_bytes(N, H, K, V, es, gate_dim=None):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_long_prefill_and_decode.json")
 SOURCES = [os.path.join(ROOT, "gated_delta_rule_30_amd", "csrc", f)
            for f in ("kda_chunk.hip", "kda_decode.hip", "kda_device.h", "kda_internal.h")]
-CHUNK_KERNELS = ("table_kernel", "segment_kernel", "prep_kernel", "state_kernel")
+CHUNK_KERNELS = ("table_kernel", "segment_kernel", "prep_kernel", "state_kernel", "state_split_kernel")
 DECODE_KERNEL = "decode_step_kernel"
 CALIB_KERNEL = "neg_kernel"
 
