@@ -51,6 +51,10 @@ struct Rec {
   static constexpr size_t nMat = oPb + (size_t)CHUNK * CHUNK;
   static constexpr size_t oGamBytes = nMat * sizeof(MT);         // K fp32
   static constexpr size_t bytes = (oGamBytes + K * 4 + 1023) / 1024 * 1024;  // whole 1 KB slots
+  // then V of the chunk, slice-major: slice c (value columns 16c .. 16c+15) is CHUNK rows of 16
+  // values, 16 * CHUNK * sizeof(MT) bytes, at oVBytes + c * 16 * CHUNK * sizeof(MT)
+  static constexpr size_t oVBytes = bytes;
+  static constexpr size_t vslice_bytes = (size_t)16 * CHUNK * sizeof(MT);
 };
 
 template <typename MT>
@@ -259,6 +263,8 @@ struct PrepParams {
   char* rec;          // record buffer of the segment
   int64_t rec_bytes;
   uint32_t opts;      // input option bits (OPT_*)
+  const void* v;      // V [T][H][V], copied into the records slice-major
+  int V;
 };
 
 // One workgroup of 4 waves per (chunk, head); wave w owns sub-block w (tokens 16w .. 16w+15).
@@ -266,8 +272,10 @@ struct PrepParams {
 // u = 0 .. K/16-1, which is exactly that token's MFMA fragment over the channels. Phases are
 // separated by LDS-only barriers; record stores stay in flight.
 // OPTS = false compiles the kernel without the input-option code (options == 0), which keeps
-// that path's register allocation and schedule free of it.
-template <int K, typename MT, bool OPTS>
+// that path's register allocation and schedule free of it. V256 = true fixes a token row of V
+// at 256 bytes (bf16 V = 128, fp32 V = 64): the V copy is then one branch-free batch (at the
+// join points of the generic copy's batch branches the compiler waits for all memory traffic).
+template <int K, typename MT, bool OPTS, bool V256>
 __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   using L = PrepLayout<K, MT>;
   using R = Rec<K, MT>;
@@ -341,10 +349,50 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     if ((part < 0 || part == 2) && scalar_gate) r.g[0][0] = gg_[tl * H + hh];
     if (part < 0 || part == 2) r.b = gb_[tl * H + hh];
   };
+  // V of the current task into its record, slice-major (the state kernel then reads a slice's
+  // CHUNK x 16 values as one contiguous block instead of gathering 16 values from each of CHUNK
+  // token rows). A token row is vpr 16-byte pieces; each thread copies vpt pieces in up to four
+  // batches of four, spread over phases 2-5: a batch is loaded one phase before it is stored.
+  // Rows past the chunk's end repeat the last valid row (finite; T' is zero in those columns).
+  typedef __attribute__((ext_vector_type(4))) unsigned u4;
+  const MT* gv_ = reinterpret_cast<const MT*>(p.v);
+  const int vpr = V256 ? 16 : p.V * (int)sizeof(MT) / 16;  // a power of two
+  const int vsh = V256 ? 4 : __builtin_ctz((unsigned)vpr);
+  const int vpt = V256 ? 4 : CHUNK * vpr / PREP_THREADS;  // 1 .. 16
+  constexpr int VB = V256 ? 1 : 4;  // pieces per batch
+  u4 vbuf[VB];
+  // (tid: the loop's opaque copy of threadIdx.x, so that no address is hoisted and kept live)
+  auto v_load = [&](int tid, TaskPos tp, int task, int batch) {
+    const int hh = task % H;
+#pragma unroll
+    for (int i = 0; i < VB; ++i) {
+      const int pi = batch * VB + i;
+      if (pi < vpt) {
+        const int id = tid + PREP_THREADS * pi;
+        const int row = id >> vsh, c = id & (vpr - 1);
+        const int64_t tl = tp.tok + min(row, tp.len - 1);
+        vbuf[i] = *reinterpret_cast<const u4*>(gv_ + (tl * H + hh) * (int64_t)p.V + c * (16 / (int)sizeof(MT)));
+      }
+    }
+  };
+  auto v_store = [&](int tid, char* rec, int batch) {
+#pragma unroll
+    for (int i = 0; i < VB; ++i) {
+      const int pi = batch * VB + i;
+      if (pi < vpt) {
+        const int id = tid + PREP_THREADS * pi;
+        const int row = id >> vsh, c = id & (vpr - 1);
+        const int slice = c / (int)sizeof(MT), sub = c % (int)sizeof(MT);  // sizeof(MT) pieces per slice row
+        *reinterpret_cast<u4*>(rec + R::oVBytes + (size_t)slice * R::vslice_bytes +
+                               (size_t)row * 16 * sizeof(MT) + 16 * sub) = vbuf[i];
+      }
+    }
+  };
   int task = blockIdx.x;
   if (task >= ntask) return;
+  TaskPos pcur = task_pos(task);  // the current task's chunk position
   Raw raw;  // raw inputs of one task: filled one task ahead, consumed by phase 1
-  load_raw(raw, task_pos(task), task, -1);
+  load_raw(raw, pcur, task, -1);
   float kc[NG][4];  // phase 1 -> phase 2: this wave's column operand
 
   // Phase 1 of a task: its raw inputs become the LDS operands, the per-channel tables, kc and
@@ -510,7 +558,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     }
 
   };
-  front(task, task_pos(task), raw);
+  front(task, pcur, raw);
 
   // Each iteration runs phases 2-5 of one task and then phase 1 of the next, so the waits for
   // the prefetched inputs come after the record stores in straight-line code.
@@ -530,6 +578,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   // the next task's inputs load during phases 2-5 (phase 1's fp32 copies are dead by now)
   // (in three parts, so that the loads enter the memory pipeline in smaller bursts)
   load_raw(raw, pn, ntsk, 0);
+  v_load(tid, pcur, task, 0);
 
   // ---------------- phase 2: blocks (I, w), I >= w, of A and P. The column operand (token
   // block w, scaled per channel by D_{Iw}) is this wave's own kc; the row operands are read as
@@ -585,6 +634,8 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   }
 
   load_raw(raw, pn, ntsk, 1);
+  v_store(tid, reinterpret_cast<char*>(recM), 0);
+  if (vpt > VB) v_load(tid, pcur, task, 1);
 
   // ---------------- phase 3: T = (I + A)^{-1}
   // (a) Diagonal 16x16 block of wave w by right-looking forward substitution: lane c keeps
@@ -662,6 +713,8 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   lds_barrier();
 
   load_raw(raw, pn, ntsk, 2);
+  if (vpt > VB) v_store(tid, reinterpret_cast<char*>(recM), 1);
+  if (vpt > 2 * VB) v_load(tid, pcur, task, 2);
 
   // ---------------- phase 4: T' = T diag(beta) -> LDS (row-major)
 #pragma unroll
@@ -680,6 +733,8 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     st4(sTb + i * L::LC + j0, tv);
   }
   lds_barrier();
+  if (vpt > 2 * VB) v_store(tid, reinterpret_cast<char*>(recM), 2);
+  if (vpt > 3 * VB) v_load(tid, pcur, task, 3);
 
   // ---------------- phase 5: T' fragments to the record (whole 16-byte lane slots), then
   // W^T = Ka^T T'^T -> record (as -W fragments)
@@ -719,9 +774,11 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     }
   }
 
+  if (vpt > 3 * VB) v_store(tid, reinterpret_cast<char*>(recM), 3);
   lds_barrier();  // the next task reuses every LDS region
   task += gridDim.x;
   if (task >= ntask) break;
+  pcur = pn;
   front(task, pn, raw);
   }
 }
@@ -897,7 +954,6 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
   // Per-chunk descriptors cover the chunk's valid rows of V and of the output, so rows past
   // the end load as zero (T' is zero in those columns anyway) and are never stored.
   const uint32_t rowb = (uint32_t)(H * V * (int)sizeof(MT));  // bytes between token rows
-  const MT* gv = reinterpret_cast<const MT*>(p.v) + (int64_t)h * V + col0;
   MT* go = reinterpret_cast<MT*>(p.o) + (int64_t)h * V + col0;
   auto tok_of = [&](int k) { return seq_start + CHUNK * (en.depth + k); };
   auto len_of = [&](int k) { return min(CHUNK, en.end - tok_of(k)); };
@@ -905,7 +961,6 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
     const int kk = min(k, run - 1);
     return make_rsrc(base + (int64_t)tok_of(kk) * (H * V), (uint32_t)len_of(kk) * rowb);
   };
-  const uint32_t v_voff = (uint32_t)lane * rowb;                          // lane = token
   const uint32_t o_voff = (uint32_t)m * rowb + 4u * g * (uint32_t)sizeof(MT);  // token m of a tile
 
   // records: one descriptor over the buffer, 32-bit offsets; chunk k of the run (clamped to the
@@ -939,11 +994,12 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
     }
   };
 
-  // V rows of chunk k (lane = token) and gamma of chunk k
-  auto load_v = [&](int k, vload (&x)[NVL]) {
-    const rsrc_t r = rows_rsrc(gv, k);
+  // this slice's V rows of the chunk whose record starts at rc (lane = token), and gamma
+  const uint32_t vslice_off = (uint32_t)(R::oVBytes + (size_t)slice * R::vslice_bytes);
+  auto load_v = [&](uint32_t rc, vload (&x)[NVL]) {
 #pragma unroll
-    for (int i = 0; i < NVL; ++i) x[i] = buf_load16<vload>(r, v_voff + 16u * i, 0);
+    for (int i = 0; i < NVL; ++i)
+      x[i] = buf_load16<vload>(rrec, (uint32_t)lane * 16u * sizeof(MT) + 16u * i, rc + vslice_off);
   };
   auto stage_v = [&](const vload (&x)[NVL]) {
 #pragma unroll
@@ -971,7 +1027,7 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
   frag Vf[NTS];
   {
     vload vx[NVL];
-    load_v(0, vx);
+    load_v(rc0, vx);
     stage_v(vx);
 #pragma unroll
     for (int s = 0; s < NTS; ++s) Vf[s] = frag_t(sV, LDV, 0, s, lane);
@@ -993,7 +1049,7 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
   __builtin_amdgcn_sched_barrier(0);
   int ri_pre = sRun[min(3, run - 1)];  // record index of chunk k + 3, read one chunk ahead
   vload vx[NVL];                         // V rows of chunk k + 1, loaded a chunk ahead
-  load_v(1, vx);
+  load_v(rc1, vx);
 
   for (int k = 0; k < run; ++k) {
     // records of chunks k, k+1, k+2 (rc0 .. rc2 on entry), and k+3 for the next iteration
@@ -1040,7 +1096,7 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
       if constexpr (j == NA + NB) {
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        load_v(k + 2, vx);
+        load_v(rc2, vx);
       }
       // --- operation j
       const frag f = ring[j % D];
@@ -1184,7 +1240,6 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
   const size_t sbase = ((size_t)en.seq * H + h) * (size_t)K * V + col0;
   const float* src = (en.depth == 0) ? p.init_state : p.state;
   const uint32_t rowb = (uint32_t)(H * V * (int)sizeof(MT));
-  const MT* gv = reinterpret_cast<const MT*>(p.v) + (int64_t)h * V + col0;
   MT* go = reinterpret_cast<MT*>(p.o) + (int64_t)h * V + col0;
   auto tok_of = [&](int k) { return seq_start + CHUNK * (en.depth + k); };
   auto len_of = [&](int k) { return min(CHUNK, en.end - tok_of(k)); };
@@ -1192,7 +1247,6 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
     const int kk = min(k, run - 1);
     return make_rsrc(base + (int64_t)tok_of(kk) * (H * V), (uint32_t)len_of(kk) * rowb);
   };
-  const uint32_t v_voff = (uint32_t)lane * rowb;
   const uint32_t o_voff = (uint32_t)m * rowb + 4u * g * (uint32_t)sizeof(MT);
   const rsrc_t rrec = make_rsrc(p.rec, p.rec_buf_bytes);
   const uint32_t rec_h = (uint32_t)h * p.rec_bytes;
@@ -1232,10 +1286,12 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
         x[i] = buf_load16<f32x4>(rrec, 16u * (uint32_t)g + (off & 4095u), rc + (off & ~4095u));
       }
     };
-    auto load_v = [&](int k, vload (&x)[NVL]) {
-      const rsrc_t r = rows_rsrc(gv, k);
+    // this slice's V rows of the chunk whose record starts at rc (lane = token)
+    const uint32_t vslice_off = (uint32_t)(R::oVBytes + (size_t)slice * R::vslice_bytes);
+    auto load_v = [&](uint32_t rc, vload (&x)[NVL]) {
 #pragma unroll
-      for (int i = 0; i < NVL; ++i) x[i] = buf_load16<vload>(r, v_voff + 16u * i, 0);
+      for (int i = 0; i < NVL; ++i)
+        x[i] = buf_load16<vload>(rrec, (uint32_t)lane * 16u * sizeof(MT) + 16u * i, rc + vslice_off);
     };
     auto stage_v = [&](const vload (&x)[NVL]) {
 #pragma unroll
@@ -1263,7 +1319,7 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) U[tt] = O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (WV == 0) {
-      load_v(0, vx);
+      load_v(rc0, vx);
       stage_v(vx);
 #pragma unroll
       for (int s = 0; s < NTS; ++s) Vf[s] = frag_t(sV, LDV, 0, s, lane);
@@ -1293,7 +1349,7 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
     __builtin_amdgcn_sched_barrier(0);
     uint32_t rc3 = rec_off(rec_index(3));
     int ri_pre = sRun[min(4, run - 1)];  // record index of chunk k + 4, read a chunk ahead
-    if constexpr (WV == 0) load_v(1, vx);
+    if constexpr (WV == 0) load_v(rc1, vx);
     rsrc_t ro_prev = rows_rsrc(go, 0);
 
     // one chunk; PAR = k & 1 selects the ring half and the exchange buffers
@@ -1342,7 +1398,7 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
         if constexpr (j == NA + NB) {
 #pragma unroll
           for (int tt = 0; tt < NTT; ++tt) U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if constexpr (WV == 0) load_v(k + 2, vx);
+          if constexpr (WV == 0) load_v(rc2, vx);
         }
         constexpr int slot = (RC == 2 ? par * NF : 0) + j;
         const frag f = ring[slot];
@@ -1416,7 +1472,9 @@ bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan
   p->seg_entries = E;
   p->num_segs = ub > 0 ? (ub + E - 1) / E : 0;
   p->slots = N < E ? N : E;
-  p->rec_bytes = ((3LL * CHUNK * K + 2LL * CHUNK * CHUNK) * es + 4LL * K + 1023) / 1024 * 1024;
+  // the fixed part (a multiple of 1 KB), then the chunk's V (CHUNK x V, a multiple of 1 KB)
+  p->rec_bytes = ((3LL * CHUNK * K + 2LL * CHUNK * CHUNK) * es + 4LL * K + 1023) / 1024 * 1024 +
+                 (int64_t)CHUNK * V * es;
   // V split: slices of 16 columns, one wave each
   p->n_slices = V / 16;
   p->vs = 16;
@@ -1453,7 +1511,8 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
   int32_t* seg_first = reinterpret_cast<int32_t*>(ws + pl.off_seg_first);
   int32_t* seg_count = reinterpret_cast<int32_t*>(ws + pl.off_seg_count);
   float* run_state = a.final_state ? a.final_state : reinterpret_cast<float*>(ws + pl.off_state);
-  if ((int64_t)Rec<K, MT>::bytes != pl.rec_bytes) return hipErrorInvalidValue;
+  if ((int64_t)(Rec<K, MT>::bytes + (size_t)CHUNK * a.dv * sizeof(MT)) != pl.rec_bytes)
+    return hipErrorInvalidValue;
 
   SeqView sv{a.cu_seqlens, a.num_seqs, a.total_tokens};
   hipLaunchKernelGGL(table_kernel, dim3(a.num_seqs), dim3(256), 0, st, sv, a.num_heads,
@@ -1476,11 +1535,16 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
   auto prep = [&](int64_t s, hipStream_t q) {
     char* rec = ws + pl.off_rec;
     PrepParams pp{a.q, a.k, a.g, a.beta, entries, header, a.num_heads, s * pl.seg_entries,
-                  pl.seg_entries, rec, pl.rec_bytes, a.options};
-    if (a.options == 0)
-      hipLaunchKernelGGL((prep_kernel<K, MT, false>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+                  pl.seg_entries, rec, pl.rec_bytes, a.options, a.v, a.dv};
+    const bool v256 = (size_t)a.dv * sizeof(MT) == 256;
+    if (a.options == 0 && v256)
+      hipLaunchKernelGGL((prep_kernel<K, MT, false, true>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+    else if (a.options == 0)
+      hipLaunchKernelGGL((prep_kernel<K, MT, false, false>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+    else if (v256)
+      hipLaunchKernelGGL((prep_kernel<K, MT, true, true>), pgrid, dim3(PREP_THREADS), 0, q, pp);
     else
-      hipLaunchKernelGGL((prep_kernel<K, MT, true>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+      hipLaunchKernelGGL((prep_kernel<K, MT, true, false>), pgrid, dim3(PREP_THREADS), 0, q, pp);
   };
   auto state = [&](int64_t s, hipStream_t q) -> bool {
     const char* rec = ws + pl.off_rec;

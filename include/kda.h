@@ -84,7 +84,7 @@ const char* kda_status_string(kda_status s);
 /*
  * Workspace bytes kda_chunk_fwd needs for this shape (0 if the arguments are invalid).
  * The value depends only on the arguments; it covers the device chunk table, a running state
- * and one chunk-record buffer, and is bounded (about 140 MB at H=32, K=V=128, bf16) plus
+ * and one chunk-record buffer, and is bounded (about 170 MB at H=32, K=V=128, bf16) plus
  * 32 bytes per chunk and 4*N*H*K*V bytes, whatever the sequence length.
  */
 size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,

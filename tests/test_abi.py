@@ -51,7 +51,7 @@ def test_workspace_size_is_bounded_and_valid():
     long_ = ws(1, 65536, 32, 128, 128, torch.bfloat16)
     # bounded by the two segment record buffers, not by the sequence length
     assert big - long_ < 1 << 20
-    assert big < 160 * (1 << 20)
+    assert big < 200 * (1 << 20)
     # invalid shapes give 0
     assert ws(0, 10, 1, 32, 32, torch.float32) == 0
     assert ws(1, 10, 1, 48, 32, torch.float32) == 0
