@@ -113,6 +113,36 @@ def measured_traffic():
     return t.get("chunk_bytes_per_call"), t.get("decode_bytes_per_call")
 
 
+def stream_reference():
+    """Bytes read + written per second by torch's elementwise kernels (neg out of place, add_ in
+    place: the decode step's pattern, copy_) over fp32 buffers of 0.5, 1 and 4 GiB."""
+    import torch
+    dev = torch.device("cuda:0")
+
+    def timed(fn, n=20):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e-3
+
+    out = {}
+    for mib in (512, 1024, 4096):
+        n = mib * (1 << 18)
+        x = torch.ones(n, device=dev)
+        y = torch.empty_like(x)
+        b = 2 * n * 4
+        out[str(mib) + "MiB"] = {"neg_TBps": b / timed(lambda: torch.neg(x, out=y)) / 1e12,
+                                 "add_inplace_TBps": b / timed(lambda: x.add_(1.0)) / 1e12,
+                                 "copy_TBps": b / timed(lambda: y.copy_(x)) / 1e12}
+        del x, y
+    print(json.dumps({"stream_reference": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,10 +158,16 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the per-call HBM traffic record from two counter runs and exit")
     ap.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
+    ap.add_argument("--stream-reference", action="store_true",
+                    help="time torch's elementwise kernels over 0.5-4 GiB of fp32 (bytes read + "
+                         "written per second) as a practical HBM reference, and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_calibration_mib,
                       args.pmc_command)
+        return
+    if args.stream_reference:
+        stream_reference()
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void segment_kernel(const Entry* __restrict__ 
   scan[threadIdx.x] = cnt;
   __syncthreads();
   for (int off = 1; off < 256; off <<= 1) {
-    int x = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+    int x = (int)threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
     __syncthreads();
     scan[threadIdx.x] += x;
     __syncthreads();
@@ -571,7 +571,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   const int g = lane >> 4;
   const int j = task / H;
   const int h = task - j * H;
-  const int ntsk = task + gridDim.x < ntask ? task + gridDim.x : task;
+  const int ntsk = task + (int)gridDim.x < ntask ? task + (int)gridDim.x : task;
   const TaskPos pn = task_pos(ntsk);
   MT* recM = reinterpret_cast<MT*>(p.rec + (j * H + h) * p.rec_bytes);
 
