@@ -5,8 +5,8 @@ include/kda.h); this package is its thin Python binding.
 """
 from ._binding import (KDA_DTYPE_BF16, KDA_DTYPE_F32, LIB_PATH, OPT_BETA_LOGITS,
                        OPT_GATE_LOGITS, OPT_L2NORM_QK, OPT_SCALAR_GATE, KdaError, chunk_fwd,
-                       decode_step, declared_functions, lib, workspace_size)
+                       chunk_fwd_scan, decode_step, declared_functions, lib, workspace_size)
 
-__all__ = ["chunk_fwd", "decode_step", "workspace_size", "KdaError", "lib", "LIB_PATH",
+__all__ = ["chunk_fwd", "chunk_fwd_scan", "decode_step", "workspace_size", "KdaError", "lib", "LIB_PATH",
            "declared_functions", "KDA_DTYPE_BF16", "KDA_DTYPE_F32", "OPT_SCALAR_GATE",
            "OPT_GATE_LOGITS", "OPT_BETA_LOGITS", "OPT_L2NORM_QK"]

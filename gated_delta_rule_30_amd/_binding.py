@@ -58,6 +58,11 @@ def _lib():
         lib.kda_chunk_fwd_ex.restype = ctypes.c_int
         lib.kda_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                          ctypes.c_int, u32, vp, vp, vp, sz, vp]
+        lib.kda_chunk_fwd_scan_workspace_size.restype = sz
+        lib.kda_chunk_fwd_scan_workspace_size.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int, i32]
+        lib.kda_chunk_fwd_scan.restype = ctypes.c_int
+        lib.kda_chunk_fwd_scan.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                           ctypes.c_int, u32, i32, vp, vp, vp, sz, vp]
         lib.kda_decode_step_ex.restype = ctypes.c_int
         lib.kda_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                            ctypes.c_int, u32, vp]
@@ -157,6 +162,42 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, num_se
                                  workspace.numel() * workspace.element_size(), _stream(device))
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd")
+    return o, final_state
+
+
+def chunk_fwd_scan(q, k, v, log_alpha, beta, init_state=None, num_seqs=1, num_groups=8,
+                   output_final_state=True, o=None, final_state=None, workspace=None, options=0):
+    """kda_chunk_fwd_scan on torch tensors: num_seqs equal-length sequences packed token-major
+    ([T, H, .]), each split into num_groups groups whose states are combined by a scan (see
+    include/kda.h). Returns (o, final_state) as chunk_fwd does."""
+    device = q.device
+    T, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    N = int(num_seqs)
+    gshape = (T, H) if options & OPT_SCALAR_GATE else (T, H, K)
+    for name, t, shp in (("q", q, (T, H, K)), ("k", k, (T, H, K)), ("v", v, (T, H, V)),
+                         ("log_alpha", log_alpha, gshape), ("beta", beta, (T, H))):
+        _check(t, name, shp, dt, device)
+    if init_state is not None:
+        _check(init_state, "init_state", (N, H, K, V), torch.float32, device)
+    if o is None:
+        o = torch.empty((T, H, V), dtype=dt, device=device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, K, V), dtype=torch.float32, device=device)
+    need = int(_lib().kda_chunk_fwd_scan_workspace_size(N, T, H, K, V, code, int(num_groups)))
+    if need == 0:
+        raise KdaError(2 if K != V or K not in (32, 64, 128) else 1,
+                       "kda_chunk_fwd_scan_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    st = _lib().kda_chunk_fwd_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                   _ptr(init_state), N, T, H, K, V, code, int(options),
+                                   int(num_groups), _ptr(o), _ptr(final_state), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(device))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_scan")
     return o, final_state
 
 

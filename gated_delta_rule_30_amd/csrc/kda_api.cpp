@@ -138,6 +138,87 @@ extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                           workspace_bytes, stream);
 }
 
+static kda_status check_scan_shape(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                   int32_t dk, int32_t dv, kda_dtype dtype, int32_t num_groups) {
+  kda_status st = check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
+  if (st != KDA_SUCCESS) return st;
+  if (dk != dv) return KDA_ERROR_NOT_SUPPORTED;  // the first pass needs V + K columns (<= 256)
+  if (num_groups <= 0 || total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
+  return KDA_SUCCESS;
+}
+
+extern "C" size_t kda_chunk_fwd_scan_workspace_size(int32_t num_seqs, int64_t total_tokens,
+                                                    int32_t num_heads, int32_t dk, int32_t dv,
+                                                    kda_dtype dtype, int32_t num_groups) {
+  if (check_scan_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype, num_groups) != KDA_SUCCESS)
+    return 0;
+  kda::ScanPlan sp;
+  if (!kda::make_scan_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16,
+                           num_groups, &sp))
+    return 0;
+  return sp.total_bytes;
+}
+
+extern "C" kda_status kda_chunk_fwd_scan(const void* q, const void* k, const void* v,
+                                         const void* log_alpha, const void* beta,
+                                         const float* init_state, int32_t num_seqs,
+                                         int64_t total_tokens, int32_t num_heads, int32_t dk,
+                                         int32_t dv, kda_dtype dtype, uint32_t options,
+                                         int32_t num_groups, void* o, float* final_state,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  kda_status st = check_scan_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype, num_groups);
+  if (st != KDA_SUCCESS) return st;
+  if (options & ~kAllOptions) return KDA_ERROR_NOT_SUPPORTED;
+  if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERROR_INVALID_VALUE;
+  if (!workspace) return KDA_ERROR_INVALID_VALUE;
+  const bool scalar_gate = (options & KDA_OPT_SCALAR_GATE) != 0;
+  const void* ptrs[] = {q, k, v, scalar_gate ? nullptr : log_alpha, init_state, o, final_state};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
+  if ((beta && !aligned_to(beta, esize(dtype))) || (log_alpha && !aligned_to(log_alpha, esize(dtype))))
+    return KDA_ERROR_INVALID_VALUE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERROR_INVALID_VALUE;
+  const size_t sbytes = (size_t)num_seqs * num_heads * dk * dv * sizeof(float);
+  if (init_state && final_state && init_state != final_state &&
+      overlap(init_state, sbytes, final_state, sbytes))
+    return KDA_ERROR_INVALID_VALUE;
+  if (total_tokens > 0) {
+    const int32_t gdim = scalar_gate ? 1 : dk;
+    const size_t obytes = (size_t)total_tokens * num_heads * dv * esize(dtype);
+    const size_t ibytes = (size_t)total_tokens * num_heads * dk * esize(dtype);
+    const size_t gbytes = (size_t)total_tokens * num_heads * gdim * esize(dtype);
+    if (overlap(o, obytes, q, ibytes) || overlap(o, obytes, k, ibytes) ||
+        overlap(o, obytes, log_alpha, gbytes) || overlap(o, obytes, v, obytes))
+      return KDA_ERROR_INVALID_VALUE;
+  }
+  kda::ScanPlan sp;
+  if (!kda::make_scan_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16,
+                           num_groups, &sp))
+    return KDA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < sp.total_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+  kda::ChunkArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = log_alpha;
+  a.beta = beta;
+  a.init_state = init_state;
+  a.cu_seqlens = nullptr;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.num_heads = num_heads;
+  a.dk = dk;
+  a.dv = dv;
+  a.dtype_bf16 = dtype == KDA_DTYPE_BF16;
+  a.options = options;
+  a.o = o;
+  a.final_state = final_state;
+  a.workspace = workspace;
+  a.stream = stream;
+  hipError_t e = kda::launch_chunk_fwd_scan(a, num_groups, sp);
+  return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+}
+
 extern "C" kda_status kda_decode_step_ex(const void* q, const void* k, const void* v,
                                          const void* log_alpha, const void* beta, float* state,
                                          void* o, int32_t num_seqs, int32_t num_heads,

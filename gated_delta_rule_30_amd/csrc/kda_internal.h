@@ -80,4 +80,17 @@ struct ChunkArgs {
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkPlan& p);
 
+// Chunk-parallel scan over equal-length sequences split into G groups of whole chunks: a pass
+// over the groups with V + K state columns, a combine, and a pass from the groups' initial
+// states. Workspace: the chunk workspace of the larger pass, [v | 0], its scratch output,
+// [0 | I], the groups' [B | M], their initial states and the group boundaries.
+struct ScanPlan {
+  int64_t L, Lg;       // tokens per sequence and per group
+  ChunkPlan p1, p3;    // the two chunk passes (N * G sequences; V + K and V columns)
+  size_t off_ws, off_vaug, off_oaug, off_init1, off_fin1, off_sin, off_cu, total_bytes;
+};
+bool make_scan_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv, bool bf16,
+                    int groups, ScanPlan* p);
+hipError_t launch_chunk_fwd_scan(const ChunkArgs& a, int groups, const ScanPlan& p);
+
 }  // namespace kda

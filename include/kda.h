@@ -135,6 +135,32 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
                             void* stream);
 
 /*
+ * Chunk-parallel scan variant of kda_chunk_fwd_ex for long sequences over few heads. Each of the
+ * num_seqs sequences (equal lengths total_tokens / num_seqs, no cu_seqlens) splits into
+ * num_groups groups of whole 64-token chunks; one chunked pass over all groups with the values
+ * [v | 0] and the initial state [0 | I] yields each group's end state from zero, B_g, and its
+ * state transition, M_g (K x K); a combine forms every group's initial state
+ * S_in(g + 1) = M_g S_in(g) + B_g; a second pass runs all groups from those states ("Kimi Linear"
+ * explainer, "DPLR Chunked Parallel"). Results equal kda_chunk_fwd_ex's up to rounding. It
+ * doubles the chunk work and pays off when num_seqs * num_heads * dv / 16 is far below the
+ * GPU's 256 CUs (e.g. one sequence of 64k tokens over 4 heads with num_groups = 8).
+ * Requires dk == dv in {32, 64, 128}; other shapes give KDA_ERROR_NOT_SUPPORTED.
+ * total_tokens must be divisible by num_seqs and num_groups >= 1 (else
+ * KDA_ERROR_INVALID_VALUE). The workspace needs kda_chunk_fwd_scan_workspace_size bytes
+ * (it holds [v | 0], a scratch output and the groups' states: about 4 * T * H * K bytes for
+ * bf16 beyond the chunk workspace). Other arguments as for kda_chunk_fwd_ex.
+ */
+size_t kda_chunk_fwd_scan_workspace_size(int32_t num_seqs, int64_t total_tokens,
+                                         int32_t num_heads, int32_t dk, int32_t dv,
+                                         kda_dtype dtype, int32_t num_groups);
+kda_status kda_chunk_fwd_scan(const void* q, const void* k, const void* v, const void* log_alpha,
+                              const void* beta, const float* init_state, int32_t num_seqs,
+                              int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                              kda_dtype dtype, uint32_t options, int32_t num_groups, void* o,
+                              float* final_state, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * One recurrent KDA token step per (sequence, head), state updated in place (decode).
  * The decay, prediction u = (Diag(alpha) S)^T k, erase-and-write and read are fused into one
  * pass that streams each fp32 state once from HBM and writes it once.

@@ -18,6 +18,7 @@ F32, BF16 = 0, 1
 def test_every_declared_symbol_is_exported():
     names = kda.declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_fwd_workspace_size",
+                          "kda_chunk_fwd_scan", "kda_chunk_fwd_scan_workspace_size",
                           "kda_decode_step", "kda_decode_step_ex", "kda_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -147,3 +148,40 @@ def _decode(L, **kw):
 ])
 def test_decode_step_argument_errors(kw, expect):
     assert _decode(kda.lib(), **kw) == expect
+
+
+def _scan(L, **kw):
+    a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, init=None, N=1, T=128, H=2, dk=32, dv=32,
+             dtype=BF16, opts=0, G=4, o=6 * A, fin=7 * A, ws=8 * A, wsb=1 << 40, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kda_chunk_fwd_scan(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]),
+                                vp(a["init"]), a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"],
+                                a["opts"], a["G"], vp(a["o"]), vp(a["fin"]), vp(a["ws"]), a["wsb"],
+                                vp(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(G=0), INVALID),
+    (dict(G=-3), INVALID),
+    (dict(N=3, T=128), INVALID),           # equal lengths only
+    (dict(dk=32, dv=64), NOT_SUPPORTED),   # K == V only
+    (dict(dk=256, dv=256), NOT_SUPPORTED),
+    (dict(opts=64), NOT_SUPPORTED),
+    (dict(q=None), INVALID),
+    (dict(q=A + 4), INVALID),
+    (dict(ws=8 * A + 64), INVALID),
+    (dict(wsb=4096), WS_SMALL),
+    (dict(o=A), INVALID),
+])
+def test_chunk_fwd_scan_argument_errors(kw, expect):
+    assert _scan(kda.lib(), **kw) == expect
+
+
+def test_scan_workspace_size():
+    import torch
+    ws = lambda *a: int(kda.lib().kda_chunk_fwd_scan_workspace_size(*a))
+    assert ws(1, 65536, 4, 128, 128, 1, 8) > kda.workspace_size(1, 65536, 4, 128, 128, torch.bfloat16)
+    assert ws(1, 65536, 4, 128, 64, 1, 8) == 0
+    assert ws(1, 65536, 4, 128, 128, 1, 0) == 0
+    assert ws(3, 100, 4, 64, 64, 0, 2) == 0

@@ -1,0 +1,65 @@
+"""kda_chunk_fwd_scan (the chunk-parallel scan over groups of chunks) on the GPU against the
+oracle and against kda_chunk_fwd, through the C ABI."""
+import pytest
+import torch
+
+import gated_delta_rule_30_amd as kda
+import workloads
+from gpu_util import TOL, assert_close, np64, oracle_fwd, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ORDER = ("q", "k", "v", "log_alpha", "beta")
+
+
+def _cu(N, T):
+    return torch.tensor([n * (T // N) for n in range(N + 1)], dtype=torch.int32, device=DEV)
+
+
+@pytest.mark.parametrize("N,T,H,K,dtype,G", [
+    (2, 6000, 2, 64, torch.bfloat16, 5),
+    (1, 2000, 2, 32, torch.float32, 4),
+    (1, 100, 2, 32, torch.bfloat16, 5),    # more groups than chunks: empty groups
+    (3, 900, 1, 128, torch.bfloat16, 1),   # one group
+    (1, 5000, 2, 128, torch.bfloat16, 7),
+])
+def test_scan_matches_oracle(N, T, H, K, dtype, G):
+    print("scan", N, T, H, K, dtype, G, flush=True)
+    inp = workloads.gen_forward(T, H, K, K, dtype=dtype, device=DEV, seed=T + G, num_seqs=N,
+                                init_std=0.1)
+    o, fin = kda.chunk_fwd_scan(*(inp[x] for x in ORDER), init_state=inp["init_state"],
+                                num_seqs=N, num_groups=G)
+    o_ref, f_ref = oracle_fwd(inp, cu=_cu(N, T))
+    assert_close(np64(o), o_ref, dtype, "o")
+    assert_close(np64(fin), f_ref, dtype, "final")
+
+
+def test_scan_equals_chunk_fwd_long():
+    """One 20000-token sequence over 3 heads, K=V=128 bf16, 8 groups: the scan and the plain
+    chunk path agree."""
+    print("scan vs chunk_fwd", flush=True)
+    T, H, K = 20000, 3, 128
+    inp = workloads.gen_forward(T, H, K, K, dtype=torch.bfloat16, device=DEV, seed=11, init_std=0.1)
+    o1, f1 = kda.chunk_fwd(*(inp[x] for x in ORDER), init_state=inp["init_state"])
+    o2, f2 = kda.chunk_fwd_scan(*(inp[x] for x in ORDER), init_state=inp["init_state"], num_groups=8)
+    tol = TOL[torch.bfloat16]
+    assert rel_err(np64(o2), np64(o1)) <= tol
+    assert rel_err(np64(f2), np64(f1)) <= tol
+    o_ref, f_ref = oracle_fwd(inp, heads=[1])
+    assert_close(np64(o2[:, 1:2]), o_ref, torch.bfloat16, "o head 1")
+    assert_close(np64(f2[:, 1:2]), f_ref, torch.bfloat16, "final head 1")
+
+
+def test_scan_with_options_and_in_place_state():
+    print("scan with options", flush=True)
+    T, H, K = 3000, 2, 128
+    opts = kda.OPT_SCALAR_GATE | kda.OPT_GATE_LOGITS | kda.OPT_BETA_LOGITS | kda.OPT_L2NORM_QK
+    inp = workloads.gen_raw(T, H, K, K, opts, dtype=torch.bfloat16, device=DEV, seed=12,
+                            init_std=0.1)
+    o_ref, f_ref = oracle_fwd(inp, options=opts)
+    st = inp["init_state"].clone()
+    o, fin = kda.chunk_fwd_scan(*(inp[x] for x in ORDER), init_state=st, final_state=st,
+                                num_groups=3, options=opts)
+    assert fin.data_ptr() == st.data_ptr()
+    assert_close(np64(o), o_ref, torch.bfloat16, "o")
+    assert_close(np64(st), f_ref, torch.bfloat16, "final in place")
