@@ -153,6 +153,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-options-bench", action="store_true",
                     help="skip the timing of the input-option entry points (counter runs)")
+    ap.add_argument("--no-scan-bench", action="store_true",
+                    help="skip the few-head long-sequence comparison of kda_chunk_fwd and "
+                         "kda_chunk_fwd_scan")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run torch.neg over this many MiB of fp32 (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -317,6 +320,49 @@ def main():
         }
         del raw, draw, o2, fin2, od2, state2
 
+    # ---------------- one long sequence with few heads, where the chunk chains alone cannot fill
+    # the device: the plain chunked call against the chunk-parallel scan over groups of chunks
+    scan = None
+    if not args.no_scan_bench:
+        Hs, Gs = 2, 16
+        sinp = workloads.gen_forward(T, Hs, K, V, dtype=torch.bfloat16, device=dev,
+                                     seed=wl["seed"] + 7, init_std=wl["init_std"])
+        os_p, os_s = (torch.empty((T, Hs, V), dtype=torch.bfloat16, device=dev) for _ in range(2))
+        fs_p, fs_s = (torch.empty((1, Hs, K, V), dtype=torch.float32, device=dev) for _ in range(2))
+        ws_p = torch.empty(kda.workspace_size(1, T, Hs, K, V, torch.bfloat16), dtype=torch.uint8,
+                           device=dev)
+        ws_s = torch.empty(int(kda.lib().kda_chunk_fwd_scan_workspace_size(1, T, Hs, K, V, 1, Gs)),
+                           dtype=torch.uint8, device=dev)
+
+        def plain_few():
+            kda.chunk_fwd(*(sinp[x] for x in names), init_state=sinp["init_state"], o=os_p,
+                          final_state=fs_p, workspace=ws_p)
+
+        def scan_few():
+            kda.chunk_fwd_scan(*(sinp[x] for x in names), init_state=sinp["init_state"],
+                               num_groups=Gs, o=os_s, final_state=fs_s, workspace=ws_s)
+
+        for _ in range(args.warmup):
+            plain_few()
+            scan_few()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for s in range(args.steps):
+            evs[s][0].record()
+            plain_few()
+            evs[s][1].record()
+            scan_few()
+            evs[s][2].record()
+        torch.cuda.synchronize()
+        pms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        sms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        rel = lambda a, b: float((a.float() - b.float()).abs().max() / b.float().abs().max())
+        scan = {"workload": "B=1 H=%d T=%d K=V=%d bf16, init state 0.1*N(0,1)" % (Hs, T, K),
+                "groups": Gs, "plain_ms": pms, "scan_ms": sms,
+                "plain_tokens_per_s": T / (pms * 1e-3), "scan_tokens_per_s": T / (sms * 1e-3),
+                "speedup": pms / sms,
+                "o_max_rel_diff": rel(os_s, os_p), "final_state_max_rel_diff": rel(fs_s, fs_p)}
+        del sinp, os_p, os_s, fs_p, fs_s, ws_p, ws_s
+
     # ---------------- parity spot check and CPU baseline (oracle on the same inputs)
     cpu = None
     parity = None
@@ -358,6 +404,7 @@ def main():
         "decode_step": decode,
         "roofline_decode": roofline_decode,
         "input_options": options,
+        "few_head_scan": scan,
         "parity_sample_max_rel_err": parity,
     }
     print(json.dumps(out), flush=True)

@@ -1502,7 +1502,7 @@ bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan
 }
 
 template <int K, typename MT>
-static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
+static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl, const RecordRegion* rr) {
   hipStream_t st = (hipStream_t)a.stream;
   char* ws = reinterpret_cast<char*>(a.workspace);
   Entry* entries = reinterpret_cast<Entry*>(ws + pl.off_entries);
@@ -1511,8 +1511,18 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
   int32_t* seg_first = reinterpret_cast<int32_t*>(ws + pl.off_seg_first);
   int32_t* seg_count = reinterpret_cast<int32_t*>(ws + pl.off_seg_count);
   float* run_state = a.final_state ? a.final_state : reinterpret_cast<float*>(ws + pl.off_state);
-  if ((int64_t)(Rec<K, MT>::bytes + (size_t)CHUNK * a.dv * sizeof(MT)) != pl.rec_bytes)
+  // records: the plan's buffer, reused by every segment, or the caller's region with one slot
+  // per segment; a region filled by an earlier call with more value columns serves a call
+  // with fewer (the value slices lead the record's V part, the rest is never read)
+  const int64_t need = (int64_t)(Rec<K, MT>::bytes + (size_t)CHUNK * a.dv * sizeof(MT));
+  const int64_t rb = rr ? rr->rec_bytes : pl.rec_bytes;
+  if (rr ? (rb < need || (rr->prep && rb != need) || rb % 1024 != 0) : rb != need)
     return hipErrorInvalidValue;
+  const size_t seg_buf = (size_t)pl.seg_entries * a.num_heads * rb;
+  if (seg_buf >= (1ull << 31)) return hipErrorInvalidValue;
+  auto seg_rec = [&](int64_t s) -> char* {
+    return rr ? rr->base + (size_t)s * seg_buf : ws + pl.off_rec;
+  };
 
   SeqView sv{a.cu_seqlens, a.num_seqs, a.total_tokens};
   hipLaunchKernelGGL(table_kernel, dim3(a.num_seqs), dim3(256), 0, st, sv, a.num_heads,
@@ -1533,9 +1543,8 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
   const int64_t ptasks = pl.seg_entries * a.num_heads;
   const dim3 pgrid((unsigned)min(ptasks, (int64_t)2 * ncu));
   auto prep = [&](int64_t s, hipStream_t q) {
-    char* rec = ws + pl.off_rec;
     PrepParams pp{a.q, a.k, a.g, a.beta, entries, header, a.num_heads, s * pl.seg_entries,
-                  pl.seg_entries, rec, pl.rec_bytes, a.options, a.v, a.dv};
+                  pl.seg_entries, seg_rec(s), rb, a.options, a.v, a.dv};
     const bool v256 = (size_t)a.dv * sizeof(MT) == 256;
     if (a.options == 0 && v256)
       hipLaunchKernelGGL((prep_kernel<K, MT, false, true>), pgrid, dim3(PREP_THREADS), 0, q, pp);
@@ -1547,11 +1556,10 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
       hipLaunchKernelGGL((prep_kernel<K, MT, true, false>), pgrid, dim3(PREP_THREADS), 0, q, pp);
   };
   auto state = [&](int64_t s, hipStream_t q) -> bool {
-    const char* rec = ws + pl.off_rec;
     StateParams sp{a.v, a.o, a.init_state, run_state, entries, header, basetab,
                    seg_first + s * pl.slots, seg_count + s, s * pl.seg_entries, pl.seg_entries,
-                   a.num_heads, a.dv, pl.n_slices, chains, rec, (uint32_t)pl.rec_bytes,
-                   (uint32_t)pl.rec_buf_bytes};
+                   a.num_heads, a.dv, pl.n_slices, chains, seg_rec(s), (uint32_t)rb,
+                   (uint32_t)seg_buf};
     if (pl.vs != 16) return false;
     if constexpr (SplitShape<K, MT>::OK)
       hipLaunchKernelGGL((state_split_kernel<K, MT>), sgrid, dim3(SPLIT_THREADS), 0, q, sp);
@@ -1562,21 +1570,22 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl) {
 
   // Segments run in order on the caller's stream, each kernel with the whole device: the
   // prep kernel fills the record buffer, then the state kernel consumes it.
+  const bool run_prep = !rr || rr->prep;
   for (int64_t s = 0; s < pl.num_segs; ++s) {
-    prep(s, st);
+    if (run_prep) prep(s, st);
     if (!state(s, st)) return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkPlan& pl) {
+hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkPlan& pl, const RecordRegion* rr) {
   if (a.dtype_bf16) {
-    if (a.dk == 32) return launch_chunk_t<32, bf16>(a, pl);
-    if (a.dk == 64) return launch_chunk_t<64, bf16>(a, pl);
-    if (a.dk == 128) return launch_chunk_t<128, bf16>(a, pl);
+    if (a.dk == 32) return launch_chunk_t<32, bf16>(a, pl, rr);
+    if (a.dk == 64) return launch_chunk_t<64, bf16>(a, pl, rr);
+    if (a.dk == 128) return launch_chunk_t<128, bf16>(a, pl, rr);
   } else {
-    if (a.dk == 32) return launch_chunk_t<32, float>(a, pl);
-    if (a.dk == 64) return launch_chunk_t<64, float>(a, pl);
+    if (a.dk == 32) return launch_chunk_t<32, float>(a, pl, rr);
+    if (a.dk == 64) return launch_chunk_t<64, float>(a, pl, rr);
   }
   return hipErrorInvalidValue;
 }

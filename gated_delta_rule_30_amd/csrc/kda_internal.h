@@ -78,16 +78,29 @@ struct ChunkArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
-hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkPlan& p);
+// Where a chunked pass keeps its (chunk, head) records when the caller wants them to outlive
+// it: base holds one slot of seg_entries * num_heads * rec_bytes per segment; prep = false
+// skips the record-building kernel because an earlier pass over the same chunks (with at
+// least as many value columns) left them there.
+struct RecordRegion {
+  char* base;
+  int64_t rec_bytes;
+  bool prep;
+};
+hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkPlan& p,
+                            const RecordRegion* records = nullptr);
 
 // Chunk-parallel scan over equal-length sequences split into G groups of whole chunks: a pass
 // over the groups with V + K state columns, a combine, and a pass from the groups' initial
-// states. Workspace: the chunk workspace of the larger pass, [v | 0], its scratch output,
-// [0 | I], the groups' [B | M], their initial states and the group boundaries.
+// states that reuses the first pass's records. Workspace: the chunk workspace of the larger
+// pass with every segment's records, [v | 0], its scratch output, [0 | I], the groups'
+// [B | M], their initial states and the group boundaries.
 struct ScanPlan {
   int64_t L, Lg;       // tokens per sequence and per group
   ChunkPlan p1, p3;    // the two chunk passes (N * G sequences; V + K and V columns)
-  size_t off_ws, off_vaug, off_oaug, off_init1, off_fin1, off_sin, off_cu, total_bytes;
+  size_t rec_region_bytes;  // every segment's records of the first pass, kept for the second
+  size_t off_ws, off_vaug, off_oaug, off_init1, off_fin1, off_sin, off_cu, off_dummy,
+      total_bytes;
 };
 bool make_scan_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv, bool bf16,
                     int groups, ScanPlan* p);

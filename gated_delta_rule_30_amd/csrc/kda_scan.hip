@@ -14,9 +14,11 @@
 // groups' end states; the last group's end state is the sequence's final state.
 //
 // Both passes are the chunk path of kda_chunk.hip on the packed groups (a group is a sequence
-// of the pass); this file holds the glue: the group boundaries, [v | 0] and [0 | I], the
-// combine and the final copy. It pays a second pass and K more state columns in the first, so
-// it helps when few (sequence, head) chains leave most CUs idle (e.g. one sequence, 4 heads).
+// of the pass); the second reuses the (chunk, head) records the first built, so only the
+// state recurrence runs twice. This file holds the glue: the group boundaries, [v | 0] and
+// [0 | I], the combine and the final copy. It pays a second state sweep and K more state
+// columns in the first, so it helps when few (sequence, head) chains leave most CUs idle
+// (one long sequence with a few heads).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -55,72 +57,95 @@ __global__ void scan_init_kernel(float* __restrict__ init, int64_t heads, int K,
   }
 }
 
-// S_in of every group. One workgroup per (sequence, head, 16 value columns): the column block
-// of S (K x 16) and, per group, M_g (read once, coalesced) sit in LDS; thread (r, half) owns
-// row r and 8 of the 16 columns of S, and forms them as K outer-product steps
-// acc += M_g[r][c] * S[c][cols] (one LDS read of M, two 16-byte reads of S, 8 FMAs per step),
-// plus B_g. fin1 rows are V + K wide.
-constexpr int SCAN_THREADS = 256;
-__global__ __launch_bounds__(SCAN_THREADS) void scan_combine_kernel(
+// S_in of every group. One workgroup of 4K threads per (sequence, head, 4 value columns):
+// thread (r, q) holds a quarter of row r of M_g in registers (columns 16 i + 4 q .. + 3, so the
+// four threads of a row read 64 contiguous bytes per load) and forms that quarter's share of
+// row r of M_g S_in(g) from the K x 4 column block of S_in(g) in LDS (broadcast reads, the
+// four quarters in four bank groups); the shares meet through two quad permutes, and the sum
+// plus row r of B_g is row r of S_in(g + 1). The half rows and B of the next two groups are in flight
+// while the current product runs. fin1 rows are V + K wide: B_g, then M_g.
+constexpr int SCAN_COLS = 4;
+
+__device__ __forceinline__ float quad_xor(float x, int m) {
+  // DPP quad_perm: lane i of each 4-lane group reads lane i ^ m (m = 1: [1,0,3,2], 2: [2,3,0,1])
+  return m == 1 ? __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, true))
+                : __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, true));
+}
+
+template <int K>
+__global__ __launch_bounds__(4 * K) void scan_combine_kernel(
     const float* __restrict__ fin1, const float* __restrict__ init, float* __restrict__ sin,
-    int G, int H, int K, int V) {
-  __shared__ __align__(16) float sS[128 * 16];        // K <= 128
-  __shared__ __align__(16) float sM[128 * (128 + 4)];  // M_g, rows padded by 4
-  const int blocks = V / 16;
+    float* __restrict__ dummy, int G, int H, int V) {
+  constexpr int KQ = K / 4;  // this thread's share of a row
+  __shared__ __align__(16) f32x4 sS[K];  // S_in(g)'s column block
+  const int blocks = V / SCAN_COLS;
   const int cb = blockIdx.x % blocks;
   const int nh = blockIdx.x / blocks;
   const int n = nh / H, h = nh % H;
-  const int W = V + K, c0 = 16 * cb, LM = K + 4;
+  const int W = V + K, c0 = SCAN_COLS * cb;
   const int tid = threadIdx.x;
-  const int r = tid >> 1, half = tid & 1;  // threads past 2K idle in the product
-  for (int e = tid; e < K * 16; e += SCAN_THREADS) {
-    const int rr = e >> 4, j = e & 15;
-    sS[e] = init ? init[((size_t)nh * K + rr) * V + c0 + j] : 0.f;
-  }
+  const int r = tid >> 2, q = tid & 3;
+  // three register sets in rotation: the current group's quarter row, the next group's (in
+  // flight since the step before) and the one after (issued now)
+  f32x4 m0[KQ / 4], m1[KQ / 4], m2[KQ / 4];
+  f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0, b2 = b0;
+  auto load = [&](int g, f32x4* m, f32x4& bv) {
+    const float* F = fin1 + ((((size_t)n * G + g) * H + h) * K + r) * (size_t)W;
+#pragma unroll
+    for (int i = 0; i < KQ / 4; ++i)
+      m[i] = *reinterpret_cast<const f32x4*>(F + V + 16 * i + 4 * q);
+    bv = *reinterpret_cast<const f32x4*>(F + c0);
+  };
+  // The loop body has no branch: the steps run in threes, to a multiple of 3; a group past
+  // the last is read as the last (in bounds), and a step past the last group stores its unused
+  // values to a dummy slot. The four threads of a row hold the same values; each stores one
+  // column. (A branch between a load and its use lets the compiler sink the load to the use,
+  // and one around the loads makes it wait for every load in flight at the join.)
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  if (init) s = *reinterpret_cast<const f32x4*>(init + ((size_t)nh * K + r) * V + c0);
+  sS[r] = s;
+  load(0, m0, b0);
+  load(min(1, G - 1), m1, b1);
   __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const size_t gi = ((size_t)n * G + g) * H + h;
-    for (int e = tid; e < K * 16; e += SCAN_THREADS)
-      sin[(gi * K + (e >> 4)) * V + c0 + (e & 15)] = sS[e];
-    if (g == G - 1) break;
-    const float* F = fin1 + gi * (size_t)K * W;
-    // M_g: K * K / 4 16-byte pieces, at most 16 per thread, all loads issued before the stores
-    {
-      constexpr int MAXP = 128 * 128 / 4 / SCAN_THREADS;
-      const int ppr = K / 4, np = K * ppr;  // pieces per row, pieces
-      f32x4 mp[MAXP];
+  float* srow = sin + ((size_t)n * G * H + h) * K * V + (size_t)r * V + c0 + q;
+  const size_t gstride = (size_t)H * K * V;
+  // step g: store S_in(g), start loading group g + 2, form S_in(g + 1) = M_g S_in(g) + B_g
+  auto step = [&](int g, const f32x4* cur, const f32x4& bcur, f32x4* nxt, f32x4& bnxt) {
+    const float mine = q == 0 ? s[0] : q == 1 ? s[1] : q == 2 ? s[2] : s[3];
+    *(g < G ? srow + (size_t)g * gstride : dummy) = mine;
+    load(min(g + 2, G - 1), nxt, bnxt);
+    // the quarter's rows of S_in(g) in batches of up to 16 LDS reads, each batch issued whole
+    // before its FMAs (the scheduler would otherwise wait on every read or two)
+    constexpr int BI = KQ / 4 < 4 ? KQ / 4 : 4;  // 4-row pieces per batch
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < MAXP; ++i) {
-        const int e = tid + SCAN_THREADS * i;
-        if (e < np) mp[i] = *reinterpret_cast<const f32x4*>(F + (size_t)(e / ppr) * W + V + 4 * (e % ppr));
-      }
+    for (int b = 0; b < KQ / 4; b += BI) {
+      f32x4 sv[4 * BI];
 #pragma unroll
-      for (int i = 0; i < MAXP; ++i) {
-        const int e = tid + SCAN_THREADS * i;
-        if (e < np) *reinterpret_cast<f32x4*>(sM + (e / ppr) * LM + 4 * (e % ppr)) = mp[i];
-      }
+      for (int i = 0; i < BI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sv[4 * i + j] = sS[16 * (b + i) + 4 * q + j];
+#pragma unroll
+      for (int i = 0; i < BI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc += cur[b + i][j] * sv[4 * i + j];
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * BI, 0);   // the batch's LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 16 * BI, 0);  // then its FMAs
     }
-    __syncthreads();
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-    if (r < K) {
-      const float* brow = F + (size_t)r * W + c0 + 8 * half;
-      a0 = *reinterpret_cast<const f32x4*>(brow);
-      a1 = *reinterpret_cast<const f32x4*>(brow + 4);
-      const float* mrow = sM + r * LM;
-      for (int c = 0; c < K; ++c) {
-        const float mv = mrow[c];
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(sS + c * 16 + 8 * half);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(sS + c * 16 + 8 * half + 4);
-        a0 += mv * s0;
-        a1 += mv * s1;
-      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j] += quad_xor(acc[j], 1);
+      acc[j] += quad_xor(acc[j], 2);
     }
+    s = acc + bcur;
+    __syncthreads();  // every read of sS done
+    sS[r] = s;
     __syncthreads();
-    if (r < K) {
-      *reinterpret_cast<f32x4*>(sS + r * 16 + 8 * half) = a0;
-      *reinterpret_cast<f32x4*>(sS + r * 16 + 8 * half + 4) = a1;
-    }
-    __syncthreads();
+  };
+  for (int g = 0; g < G; g += 3) {
+    step(g, m0, b0, m2, b2);
+    step(g + 1, m1, b1, m0, b0);
+    step(g + 2, m2, b2, m1, b1);
   }
 }
 
@@ -149,8 +174,12 @@ bool make_scan_plan(int N, int64_t T, int H, int K, int V, bool bf16, int G, Sca
   if (!make_chunk_plan((int)N1, T, H, K, V + K, bf16, &sp->p1)) return false;
   if (!make_chunk_plan((int)N1, T, H, K, V, bf16, &sp->p3)) return false;
   size_t off = 0;
+  // the first pass keeps every segment's records (one slot each, from its record buffer on)
+  // and the second pass reads them: same chunks, and its value columns lead the first's
   sp->off_ws = off;
-  off += al256(sp->p1.total_bytes > sp->p3.total_bytes ? sp->p1.total_bytes : sp->p3.total_bytes);
+  sp->rec_region_bytes = (size_t)sp->p1.num_segs * sp->p1.rec_buf_bytes;
+  const size_t ws1 = sp->p1.off_rec + sp->rec_region_bytes;
+  off += al256(ws1 > sp->p3.total_bytes ? ws1 : sp->p3.total_bytes);
   sp->off_vaug = off;
   off += al256((size_t)T * H * (V + K) * es);
   sp->off_oaug = off;
@@ -163,6 +192,8 @@ bool make_scan_plan(int N, int64_t T, int H, int K, int V, bool bf16, int G, Sca
   off += al256((size_t)N1 * H * K * V * 4);
   sp->off_cu = off;
   off += al256((size_t)(N1 + 1) * 4);
+  sp->off_dummy = off;
+  off += 256;
   sp->total_bytes = off;
   return true;
 }
@@ -178,6 +209,7 @@ hipError_t launch_chunk_fwd_scan(const ChunkArgs& a, int G, const ScanPlan& sp) 
   float* init1 = reinterpret_cast<float*>(ws + sp.off_init1);
   float* fin1 = reinterpret_cast<float*>(ws + sp.off_fin1);
   float* sin = reinterpret_cast<float*>(ws + sp.off_sin);
+  float* dummy = reinterpret_cast<float*>(ws + sp.off_dummy);
   const int64_t cu_n = N1 + 1;
   hipLaunchKernelGGL(scan_cu_kernel, dim3((unsigned)((cu_n + 255) / 256)), dim3(256), 0, st, cu, N,
                      G, sp.L, sp.Lg);
@@ -201,11 +233,17 @@ hipError_t launch_chunk_fwd_scan(const ChunkArgs& a, int G, const ScanPlan& sp) 
   a1.o = oaug;
   a1.final_state = fin1;
   a1.workspace = ws + sp.off_ws;
-  hipError_t e = launch_chunk_fwd(a1, sp.p1);
+  const RecordRegion rr1{ws + sp.off_ws + sp.p1.off_rec, sp.p1.rec_bytes, true};
+  hipError_t e = launch_chunk_fwd(a1, sp.p1, &rr1);
   if (e != hipSuccess) return e;
   // the groups' initial states
-  hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((int64_t)N * H * (V / 16))),
-                     dim3(SCAN_THREADS), 0, st, fin1, a.init_state, sin, G, H, K, V);
+  const dim3 cgrid((unsigned)((int64_t)N * H * (V / SCAN_COLS)));
+  if (K == 32)
+    hipLaunchKernelGGL(scan_combine_kernel<32>, cgrid, dim3(4 * 32), 0, st, fin1, a.init_state, sin, dummy, G, H, V);
+  else if (K == 64)
+    hipLaunchKernelGGL(scan_combine_kernel<64>, cgrid, dim3(4 * 64), 0, st, fin1, a.init_state, sin, dummy, G, H, V);
+  else
+    hipLaunchKernelGGL(scan_combine_kernel<128>, cgrid, dim3(4 * 128), 0, st, fin1, a.init_state, sin, dummy, G, H, V);
   // pass 3: every group from its initial state; the end states overwrite them
   ChunkArgs a3 = a;
   a3.init_state = sin;
@@ -213,7 +251,8 @@ hipError_t launch_chunk_fwd_scan(const ChunkArgs& a, int G, const ScanPlan& sp) 
   a3.num_seqs = (int)N1;
   a3.final_state = sin;
   a3.workspace = ws + sp.off_ws;
-  e = launch_chunk_fwd(a3, sp.p3);
+  const RecordRegion rr3{rr1.base, sp.p1.rec_bytes, false};
+  e = launch_chunk_fwd(a3, sp.p3, &rr3);
   if (e != hipSuccess) return e;
   if (a.final_state)
     hipLaunchKernelGGL(scan_final_kernel, dim3(fill_blocks), dim3(256), 0, st, sin, a.final_state,

@@ -141,14 +141,16 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
  * [v | 0] and the initial state [0 | I] yields each group's end state from zero, B_g, and its
  * state transition, M_g (K x K); a combine forms every group's initial state
  * S_in(g + 1) = M_g S_in(g) + B_g; a second pass runs all groups from those states ("Kimi Linear"
- * explainer, "DPLR Chunked Parallel"). Results equal kda_chunk_fwd_ex's up to rounding. It
- * doubles the chunk work and pays off when num_seqs * num_heads * dv / 16 is far below the
- * GPU's 256 CUs (e.g. one sequence of 64k tokens over 4 heads with num_groups = 8).
+ * explainer, "DPLR Chunked Parallel"); it reads the records the first pass built. Results
+ * equal kda_chunk_fwd_ex's up to rounding. It runs the sequential state sweep twice (the first
+ * time with dv + dk columns) and pays off when num_seqs * num_heads * dv / 16 is far below the
+ * GPU's 256 CUs (e.g. one sequence of 64k tokens over 1 to 4 heads with num_groups = 16).
  * Requires dk == dv in {32, 64, 128}; other shapes give KDA_ERROR_NOT_SUPPORTED.
  * total_tokens must be divisible by num_seqs and num_groups >= 1 (else
  * KDA_ERROR_INVALID_VALUE). The workspace needs kda_chunk_fwd_scan_workspace_size bytes
- * (it holds [v | 0], a scratch output and the groups' states: about 4 * T * H * K bytes for
- * bf16 beyond the chunk workspace). Other arguments as for kda_chunk_fwd_ex.
+ * (it holds every (chunk, head) record of the first pass, about 100 KB per 64 tokens and head
+ * at dk = dv = 128 bf16, plus [v | 0], a scratch output and the groups' states). Other
+ * arguments as for kda_chunk_fwd_ex.
  */
 size_t kda_chunk_fwd_scan_workspace_size(int32_t num_seqs, int64_t total_tokens,
                                          int32_t num_heads, int32_t dk, int32_t dv,

@@ -83,3 +83,38 @@ def test_chunk_gradients_match_oracle(C):
     got = chunk_bwd(q, k, v, g, beta, dO, C, dfinal=dfin, cu_seqlens=cu, init_state=S0)
     for name, a, b in zip(("dq", "dk", "dv", "dg", "dbeta", "dinit"), got, ref):
         np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-9 * max(1.0, np.abs(b).max()), err_msg=name)
+
+
+def test_group_scan_matches_oracle():
+    """The scan over groups of chunks, in fp64: one chunked pass per group from the zero state
+    with the values widened to [v | 0] and the initial state [0 | I] gives [B_g | M_g] (the
+    group's end state from zero and its K x K transition); S_in(g + 1) = M_g S_in(g) + B_g; a
+    second chunked pass from S_in(g) reproduces the token recurrence ("Kimi Linear" explainer,
+    "DPLR Chunked Parallel"). Slow decay and short groups keep M_g far from zero, so a wrong
+    transition would show."""
+    rng = np.random.default_rng(23)
+    T, H, K, V, C, Lg = 300, 2, 8, 6, 16, 48   # 7 groups, the last one partial
+    q, k, v, g, beta = _inputs(rng, T, H, K, V, alpha_lo=0.98)
+    S0 = rng.standard_normal((1, H, K, V))
+    o_ref, f_ref = oracle.kda_fwd(q, k, v, g, beta, init_state=S0)
+    starts = list(range(0, T, Lg))
+    o = np.zeros((T, H, V))
+    S_in = S0[0].copy()
+    mnorm = []
+    for s in starts:
+        e = min(s + Lg, T)
+        sl = slice(s, e)
+        vaug = np.concatenate([v[sl], np.zeros((e - s, H, K))], axis=2)
+        init1 = np.concatenate([np.zeros((1, H, K, V)), np.broadcast_to(np.eye(K), (1, H, K, K))],
+                               axis=3)
+        _, f1 = chunk_fwd(q[sl], k[sl], vaug, g[sl], beta[sl], C, init_state=init1)
+        B, M = f1[0, :, :, :V], f1[0, :, :, V:]
+        mnorm.append(np.abs(M).max())
+        og, fg = chunk_fwd(q[sl], k[sl], v[sl], g[sl], beta[sl], C, init_state=S_in[None])
+        o[sl] = og
+        S_next = np.einsum("hij,hjv->hiv", M, S_in) + B
+        np.testing.assert_allclose(S_next, fg[0], rtol=1e-10, atol=1e-10)
+        S_in = S_next
+    assert min(mnorm) > 1e-2
+    np.testing.assert_allclose(o, o_ref, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(S_in, f_ref[0], rtol=1e-10, atol=1e-10)

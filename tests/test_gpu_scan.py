@@ -5,6 +5,7 @@ import torch
 
 import gated_delta_rule_30_amd as kda
 import workloads
+import oracle
 from gpu_util import TOL, assert_close, np64, oracle_fwd, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -22,6 +23,8 @@ def _cu(N, T):
     (1, 100, 2, 32, torch.bfloat16, 5),    # more groups than chunks: empty groups
     (3, 900, 1, 128, torch.bfloat16, 1),   # one group
     (1, 5000, 2, 128, torch.bfloat16, 7),
+    (1, 8192, 1, 128, torch.bfloat16, 16),
+    (2, 4096, 1, 64, torch.float32, 6),
 ])
 def test_scan_matches_oracle(N, T, H, K, dtype, G):
     print("scan", N, T, H, K, dtype, G, flush=True)
@@ -32,6 +35,31 @@ def test_scan_matches_oracle(N, T, H, K, dtype, G):
     o_ref, f_ref = oracle_fwd(inp, cu=_cu(N, T))
     assert_close(np64(o), o_ref, dtype, "o")
     assert_close(np64(fin), f_ref, dtype, "final")
+
+
+@pytest.mark.parametrize("N,T,H,K,dtype,G", [
+    (1, 2048, 2, 128, torch.bfloat16, 8),
+    (1, 1500, 2, 64, torch.float32, 6),    # the last group partial
+    (2, 1024, 1, 32, torch.float32, 5),
+])
+def test_scan_slow_decay_short_groups(N, T, H, K, dtype, G):
+    """Slow decay (alpha in [0.999, 1)) over groups of a few chunks: each group's start state
+    carries much of the past, so the combine's transitions M_g shape the outputs (checked: the
+    oracle's outputs of the second group differ from that group's outputs from a zero state by
+    far more than the tolerance)."""
+    print("scan slow decay", N, T, H, K, dtype, G, flush=True)
+    inp = workloads.gen_forward(T, H, K, K, gates="slow", dtype=dtype, device=DEV, seed=T + 3 * G,
+                                num_seqs=N, init_std=0.1)
+    o, fin = kda.chunk_fwd_scan(*(inp[x] for x in ORDER), init_state=inp["init_state"],
+                                num_seqs=N, num_groups=G)
+    o_ref, f_ref = oracle_fwd(inp, cu=_cu(N, T))
+    assert_close(np64(o), o_ref, dtype, "o")
+    assert_close(np64(fin), f_ref, dtype, "final")
+    L = T // N
+    Lg = -(-(-(-L // G)) // 64) * 64  # tokens per group, whole chunks
+    g1 = slice(Lg, min(2 * Lg, L))
+    alone, _ = oracle.kda_fwd(*(np64(inp[x][g1]) for x in ORDER))
+    assert rel_err(alone, o_ref[g1]) > 10 * TOL[dtype]
 
 
 def test_scan_equals_chunk_fwd_long():
@@ -63,3 +91,19 @@ def test_scan_with_options_and_in_place_state():
     assert fin.data_ptr() == st.data_ptr()
     assert_close(np64(o), o_ref, torch.bfloat16, "o")
     assert_close(np64(st), f_ref, torch.bfloat16, "final in place")
+
+
+def test_scan_several_record_segments():
+    """8 heads over 20000 tokens in 4 groups: more (chunk, head) records than one segment of the
+    chunk path holds, so the first pass keeps several segments' records for the second."""
+    print("scan, several record segments", flush=True)
+    T, H, K = 20000, 8, 64
+    inp = workloads.gen_forward(T, H, K, K, dtype=torch.bfloat16, device=DEV, seed=13, init_std=0.1)
+    o1, f1 = kda.chunk_fwd(*(inp[x] for x in ORDER), init_state=inp["init_state"])
+    o2, f2 = kda.chunk_fwd_scan(*(inp[x] for x in ORDER), init_state=inp["init_state"], num_groups=4)
+    tol = TOL[torch.bfloat16]
+    assert rel_err(np64(o2), np64(o1)) <= tol
+    assert rel_err(np64(f2), np64(f1)) <= tol
+    o_ref, f_ref = oracle_fwd(inp, heads=[6])
+    assert_close(np64(o2[:, 6:7]), o_ref, torch.bfloat16, "o head 6")
+    assert_close(np64(f2[:, 6:7]), f_ref, torch.bfloat16, "final head 6")

@@ -74,8 +74,9 @@ def gen_forward(T_total: int, H: int, K: int, V: int, *, gates: str = "uniform",
                 init_std: float | None = None, block_tokens: int = 65536):
     """Seeded torch inputs for kda_chunk_fwd, laid out token-major [T, H, .].
 
-    gates: 'uniform' (alpha ~ U[0.9,1), beta ~ U(0,1)) or 'softplus'
-    (log alpha = -softplus(z)*0.1, beta = sigmoid(z')). q, k are drawn N(0,1) and
+    gates: 'uniform' (alpha ~ U[0.9,1), beta ~ U(0,1)), 'slow' (alpha ~ U[0.999,1), beta ~
+    U(0,1): the state keeps a visible share of its past over a few hundred tokens) or
+    'softplus' (log alpha = -softplus(z)*0.1, beta = sigmoid(z')). q, k are drawn N(0,1) and
     L2-normalised per token and head in fp32, then every tensor is cast to ``dtype``.
     Generated in token blocks to bound peak memory; init_state (fp32) only if init_std.
     """
@@ -96,14 +97,15 @@ def gen_forward(T_total: int, H: int, K: int, V: int, *, gates: str = "uniform",
             elif name == "v":
                 x = torch.randn(shp, generator=gen, device=device, dtype=torch.float32)
             elif name == "log_alpha":
-                if gates == "uniform":
-                    x = torch.log(0.9 + 0.1 * torch.rand(shp, generator=gen, device=device,
-                                                         dtype=torch.float32))
+                if gates in ("uniform", "slow"):
+                    lo = 0.9 if gates == "uniform" else 0.999
+                    x = torch.log(lo + (1.0 - lo) * torch.rand(shp, generator=gen, device=device,
+                                                               dtype=torch.float32))
                 else:
                     z = torch.randn(shp, generator=gen, device=device, dtype=torch.float32)
                     x = -torch.nn.functional.softplus(z) * 0.1
             else:
-                if gates == "uniform":
+                if gates in ("uniform", "slow"):
                     x = torch.rand(shp, generator=gen, device=device, dtype=torch.float32)
                 else:
                     z = torch.randn(shp, generator=gen, device=device, dtype=torch.float32)
