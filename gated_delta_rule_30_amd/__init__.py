@@ -1,12 +1,13 @@
-"""MI355X-native Kimi Delta Attention (KDA): chunkwise prefill and recurrent decode.
+"""MI355X-native Kimi Delta Attention (KDA): chunkwise prefill, its training backward and
+recurrent decode.
 
 The operator lives in libkda.so (hand-written HIP kernels for gfx950, C ABI in
 include/kda.h); this package is its thin Python binding.
 """
 from ._binding import (KDA_DTYPE_BF16, KDA_DTYPE_F32, LIB_PATH, OPT_BETA_LOGITS,
-                       OPT_GATE_LOGITS, OPT_L2NORM_QK, OPT_SCALAR_GATE, KdaError, chunk_fwd,
-                       chunk_fwd_scan, decode_step, declared_functions, lib, workspace_size)
+                       OPT_GATE_LOGITS, OPT_L2NORM_QK, OPT_SCALAR_GATE, KdaError, chunk_bwd,
+                       chunk_fwd, chunk_fwd_scan, decode_step, declared_functions, lib, workspace_size)
 
-__all__ = ["chunk_fwd", "chunk_fwd_scan", "decode_step", "workspace_size", "KdaError", "lib", "LIB_PATH",
+__all__ = ["chunk_fwd", "chunk_fwd_scan", "chunk_bwd", "decode_step", "workspace_size", "KdaError", "lib", "LIB_PATH",
            "declared_functions", "KDA_DTYPE_BF16", "KDA_DTYPE_F32", "OPT_SCALAR_GATE",
            "OPT_GATE_LOGITS", "OPT_BETA_LOGITS", "OPT_L2NORM_QK"]

@@ -63,6 +63,11 @@ def _lib():
         lib.kda_chunk_fwd_scan.restype = ctypes.c_int
         lib.kda_chunk_fwd_scan.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                            ctypes.c_int, u32, i32, vp, vp, vp, sz, vp]
+        lib.kda_chunk_bwd_workspace_size.restype = sz
+        lib.kda_chunk_bwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
+        lib.kda_chunk_bwd.restype = ctypes.c_int
+        lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                      ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.kda_decode_step_ex.restype = ctypes.c_int
         lib.kda_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                            ctypes.c_int, u32, vp]
@@ -199,6 +204,53 @@ def chunk_fwd_scan(q, k, v, log_alpha, beta, init_state=None, num_seqs=1, num_gr
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd_scan")
     return o, final_state
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final_state=None,
+              cu_seqlens=None, num_seqs=None, workspace=None):
+    """kda_chunk_bwd on torch tensors: the gradients of sum(d_o * o) + sum(d_final_state *
+    final_state) for chunk_fwd on the same inputs (no input options). d_o [T, H, V] in the input
+    dtype; d_final_state [N, H, K, V] fp32 or None (zero). Returns fp32 tensors
+    (dq [T, H, K], dk [T, H, K], dv [T, H, V], dlog_alpha [T, H, K], dbeta [T, H],
+    dinit_state [N, H, K, V])."""
+    device = q.device
+    T, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, device)
+        N = cu_seqlens.shape[0] - 1
+        if num_seqs is not None and num_seqs != N:
+            raise ValueError("num_seqs does not match cu_seqlens")
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
+    for name, t, shp in (("q", q, (T, H, K)), ("k", k, (T, H, K)), ("v", v, (T, H, V)),
+                         ("log_alpha", log_alpha, (T, H, K)), ("beta", beta, (T, H)),
+                         ("d_o", d_o, (T, H, V))):
+        _check(t, name, shp, dt, device)
+    for name, t in (("init_state", init_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _check(t, name, (N, H, K, V), torch.float32, device)
+    f32 = dict(dtype=torch.float32, device=device)
+    dq, dk, dg = (torch.empty((T, H, K), **f32) for _ in range(3))
+    dv = torch.empty((T, H, V), **f32)
+    db = torch.empty((T, H), **f32)
+    dinit = torch.empty((N, H, K, V), **f32)
+    need = int(_lib().kda_chunk_bwd_workspace_size(N, T, H, K, V, code))
+    if need == 0:
+        raise KdaError(2 if K not in (32, 64, 128) or V not in (32, 64, 128) else 1,
+                       "kda_chunk_bwd_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    st = _lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                              _ptr(init_state), _ptr(cu_seqlens), N, T, H, K, V, code, _ptr(d_o),
+                              _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                              _ptr(db), _ptr(dinit), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(device))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_bwd")
+    return dq, dk, dv, dg, db, dinit
 
 
 def decode_step(q, k, v, log_alpha, beta, state, o=None, options=0):

@@ -138,6 +138,98 @@ extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                           workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------- training backward
+static kda_status check_bwd_shape(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                  int32_t dk, int32_t dv, kda_dtype dtype) {
+  if (num_seqs <= 0 || num_heads <= 0 || total_tokens < 0 || total_tokens > kMaxTokens)
+    return KDA_ERROR_INVALID_VALUE;
+  // the gradient kernels hold up to three 64 x V fp32 blocks in LDS: V <= 128
+  if (!valid_dtype(dtype) || !supported_chunk_dk(dk) || !supported_chunk_dk(dv))
+    return KDA_ERROR_NOT_SUPPORTED;
+  return KDA_SUCCESS;
+}
+
+extern "C" size_t kda_chunk_bwd_workspace_size(int32_t num_seqs, int64_t total_tokens,
+                                               int32_t num_heads, int32_t dk, int32_t dv,
+                                               kda_dtype dtype) {
+  if (check_bwd_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype) != KDA_SUCCESS) return 0;
+  kda::BwdPlan p;
+  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, &p)) return 0;
+  return p.total_bytes;
+}
+
+extern "C" kda_status kda_chunk_bwd(const void* q, const void* k, const void* v,
+                                    const void* log_alpha, const void* beta,
+                                    const float* init_state, const int32_t* cu_seqlens,
+                                    int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                    int32_t dk, int32_t dv, kda_dtype dtype, const void* d_o,
+                                    const float* d_final_state, float* grad_q, float* grad_k,
+                                    float* grad_v, float* grad_log_alpha, float* grad_beta,
+                                    float* grad_init_state, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  kda_status st = check_bwd_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
+  if (st != KDA_SUCCESS) return st;
+  if (cu_seqlens == nullptr && total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
+  if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !d_o || !grad_q || !grad_k ||
+                           !grad_v || !grad_log_alpha || !grad_beta))
+    return KDA_ERROR_INVALID_VALUE;
+  if (!workspace) return KDA_ERROR_INVALID_VALUE;
+  const void* vec[] = {q, k, v, log_alpha, d_o, init_state, d_final_state, grad_q, grad_k,
+                       grad_v, grad_log_alpha, grad_init_state};
+  for (const void* p : vec)
+    if (p && !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
+  if ((beta && !aligned_to(beta, esize(dtype))) || (grad_beta && !aligned_to(grad_beta, 4)) ||
+      (cu_seqlens && !aligned_to(cu_seqlens, 4)))
+    return KDA_ERROR_INVALID_VALUE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERROR_INVALID_VALUE;
+  // every gradient buffer is written while the inputs are still read: none may overlap them
+  const size_t T = (size_t)total_tokens, H = (size_t)num_heads, es = esize(dtype);
+  const size_t sbytes = (size_t)num_seqs * H * dk * dv * sizeof(float);
+  const void* in_p[] = {q, k, v, log_alpha, beta, d_o, init_state, d_final_state};
+  const size_t in_n[] = {T * H * dk * es, T * H * dk * es, T * H * dv * es, T * H * dk * es,
+                         T * H * es, T * H * dv * es, sbytes, sbytes};
+  const void* out_p[] = {grad_q, grad_k, grad_v, grad_log_alpha, grad_beta, grad_init_state};
+  const size_t out_n[] = {T * H * dk * 4, T * H * dk * 4, T * H * dv * 4, T * H * dk * 4, T * H * 4,
+                          sbytes};
+  for (int o = 0; o < 6; ++o) {
+    if (!out_p[o] || out_n[o] == 0) continue;
+    for (int i = 0; i < 8; ++i)
+      if (in_p[i] && in_n[i] && overlap(out_p[o], out_n[o], in_p[i], in_n[i])) return KDA_ERROR_INVALID_VALUE;
+    for (int o2 = o + 1; o2 < 6; ++o2)
+      if (out_p[o2] && out_n[o2] && overlap(out_p[o], out_n[o], out_p[o2], out_n[o2]))
+        return KDA_ERROR_INVALID_VALUE;
+  }
+  kda::BwdPlan p;
+  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, &p)) return KDA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < p.total_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+  kda::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = log_alpha;
+  a.beta = beta;
+  a.init_state = init_state;
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.num_heads = num_heads;
+  a.dk = dk;
+  a.dv = dv;
+  a.dtype_bf16 = dtype == KDA_DTYPE_BF16;
+  a.dO = d_o;
+  a.dfinal = d_final_state;
+  a.grad_q = grad_q;
+  a.grad_k = grad_k;
+  a.grad_v = grad_v;
+  a.grad_g = grad_log_alpha;
+  a.grad_beta = grad_beta;
+  a.grad_init = grad_init_state;
+  a.workspace = workspace;
+  a.stream = stream;
+  hipError_t e = kda::launch_chunk_bwd(a, p);
+  return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+}
+
 static kda_status check_scan_shape(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                                    int32_t dk, int32_t dv, kda_dtype dtype, int32_t num_groups) {
   kda_status st = check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);

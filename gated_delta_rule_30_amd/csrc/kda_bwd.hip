@@ -1,0 +1,737 @@
+// Training backward of the chunked KDA forward: the gradients of
+//     L = sum(dO * o) + sum(dS_final * S_final)
+// with respect to q, k, v, log alpha, beta and the initial state, by reverse mode through the
+// chunk form ("A Technical Breakdown", section 4: state passing with the in-chunk cumulative
+// decay and the U / W matrices; "Kimi Linear" explainer, "WY Representation": the chunk's
+// rank-1 updates through a unit lower triangular inverse). With, per chunk of C = 64 tokens,
+// b = cumsum(log alpha) (per key channel), Qe = q e^b, Ke = k e^b, Kt = k e^{b_last - b},
+// gamma = e^{b_last}, A = strict_lower(diag(beta) (k k^T weighted by e^{b_i - b_j})),
+// T = (I + A)^{-1}, W = T diag(beta) Ke, U = T diag(beta) V, P = lower((q k^T weighted)),
+// the forward is  Delta = U - W S,  O = Qe S + P Delta,  S' = diag(gamma) S + Kt^T Delta,  and the
+// adjoints, with X = dL/dS' carried backwards over the chunks, are
+//     dDelta = P^T dO + Kt X,          dS = Qe^T dO + diag(gamma) X - W^T dDelta,
+//     dP = lower(dO Delta^T),          dW = -dDelta S^T,   dv = diag(beta) T^T dDelta,
+//     dT = dDelta (beta V)^T + dW (beta Ke)^T,              dA = strict_lower(-T^T dT T^T),
+// and the per-token gradients of q, k, beta and log alpha follow from dP, dA, T^T dW and
+// Delta X^T. Every product that carries in-chunk decay is formed pairwise as e^{b_i - b_j}
+// with j <= i (at most 1), so nothing overflows for any decay.
+//
+// Everything runs in fp32 (the chunk's inputs, bf16 or fp32, are exact in fp32). Kernels:
+//   bwd_seq_kernel, bwd_chunk_kernel   the chunk table (sequence boundaries from cu_seqlens)
+//   bwd_prep_kernel                    per (chunk, head): T, P, W, Kt, Qe, U, gamma -> record
+//   bwd_fstate_kernel                  per (sequence, head, 16 value columns), forward in
+//                                      time: S at every chunk start and Delta
+//   bwd_rstate_kernel                  the same chains backwards: X at every chunk end, dDelta,
+//                                      and the initial state's gradient
+//   bwd_ga_kernel, bwd_gb_kernel, bwd_gc_kernel
+//                                      per (chunk, head): the products with S and X, then the
+//                                      T-side adjoints, then the decay-weighted pairwise sums
+//                                      and the per-token gradients
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int BC = CHUNK;  // 64 tokens per chunk
+constexpr int NT = NTHREADS;
+
+// per-(chunk, head) fp32 record of the backward, row-major blocks
+template <int K, int V>
+struct BRec {
+  static constexpr int oT = 0;                 // T = (I + A)^{-1}        [64][64]
+  static constexpr int oP = oT + BC * BC;      // P (lower incl.)        [64][64]
+  static constexpr int oW = oP + BC * BC;      // W                       [64][K]
+  static constexpr int oKt = oW + BC * K;      // Kt = k e^{b_last - b}   [64][K]
+  static constexpr int oQe = oKt + BC * K;     // Qe = q e^b              [64][K]
+  static constexpr int oU = oQe + BC * K;      // U                       [64][V]
+  static constexpr int oGam = oU + BC * V;     // gamma = e^{b_last}      [K]
+  static constexpr int floats = (oGam + K + 63) / 64 * 64;
+};
+
+// per-(chunk, head) fp32 scratch between the three gradient kernels
+template <int K>
+struct GScr {
+  static constexpr int oDP = 0;                // dP (lower incl.)       [64][64]
+  static constexpr int oDA = oDP + BC * BC;    // dA (strict lower)      [64][64]
+  static constexpr int oR1 = oDA + BC * BC;    // dO S^T                 [64][K]
+  static constexpr int oDW = oR1 + BC * K;     // dW = -dDelta S^T       [64][K]
+  static constexpr int oDKt = oDW + BC * K;    // Delta X^T              [64][K]
+  static constexpr int oTDW = oDKt + BC * K;   // T^T dW                 [64][K]
+  static constexpr int oDG = oTDW + BC * K;    // rowsum(S * X)          [K]
+  static constexpr int oDB = oDG + K;          // dbeta, the T-side terms [64]
+  static constexpr int floats = (oDB + BC + 63) / 64 * 64;
+};
+
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
+  return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+}
+
+// out(r, c, x) for x = sum_j M(r, j) S[j][c], r < 64, c < N: M is 64 x 64 in LDS (row stride
+// LM), read as M[r][j], or as M[j][r] with TRANS; S is 64 x N in LDS (row stride LS). Thread t
+// owns column t % N and the rows (t / N) * RB .. + RB - 1, RB = N / 4, so the M reads of a
+// wave are broadcasts and the S reads consecutive words.
+template <int N, int LM, int LS, bool TRANS, typename F>
+__device__ __forceinline__ void mm64(const float* sM, const float* sS, F&& out) {
+  constexpr int NG = NT / N, RB = BC / NG;
+  const int c = threadIdx.x % N, r0 = (threadIdx.x / N) * RB;
+  float acc[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) acc[u] = 0.f;
+  if constexpr (!TRANS) {
+    for (int j = 0; j < BC; j += 4) {
+      const f32x4 x = {sS[(j + 0) * LS + c], sS[(j + 1) * LS + c], sS[(j + 2) * LS + c],
+                       sS[(j + 3) * LS + c]};
+#pragma unroll
+      for (int u = 0; u < RB; ++u)
+        acc[u] += dot4(*reinterpret_cast<const f32x4*>(sM + (r0 + u) * LM + j), x);
+    }
+  } else {
+    for (int j = 0; j < BC; ++j) {
+      const float x = sS[j * LS + c];
+#pragma unroll
+      for (int u = 0; u < RB; u += 4) {
+        const f32x4 m = *reinterpret_cast<const f32x4*>(sM + j * LM + r0 + u);
+        acc[u] += m[0] * x;
+        acc[u + 1] += m[1] * x;
+        acc[u + 2] += m[2] * x;
+        acc[u + 3] += m[3] * x;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < RB; ++u) out(r0 + u, c, acc[u]);
+}
+
+// out(i, j, x) for x = sum_c X[i][c] Y[j][c], i, j < 64, c < N; X, Y in LDS with row stride L
+// (L = N + 4: the 16 consecutive rows a wave reads at once fall in different banks). Thread t
+// owns rows 4 (t / 16) .. + 3 and columns t % 16 + 16 b, b < 4.
+template <int N, int L, typename F>
+__device__ __forceinline__ void rowdot64(const float* sX, const float* sY, F&& out) {
+  const int i0 = 4 * (threadIdx.x >> 4), jb = threadIdx.x & 15;
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+  for (int c = 0; c < N; c += 4) {
+    f32x4 x[4], y[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      x[a] = *reinterpret_cast<const f32x4*>(sX + (i0 + a) * L + c);
+      y[a] = *reinterpret_cast<const f32x4*>(sY + (jb + 16 * a) * L + c);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] += dot4(x[a], y[b]);
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) out(i0 + a, jb + 16 * b, acc[a][b]);
+}
+
+// rows r < len of a [T][H][N] tensor (token tok + r, head h) into LDS as fp32, zeros past len
+template <int N, int L, typename MT>
+__device__ __forceinline__ void load_rows(float* dst, const MT* src, int64_t tok, int len, int H,
+                                          int h) {
+  for (int e = threadIdx.x; e < BC * N; e += NT) {
+    const int r = e / N, c = e % N;
+    dst[r * L + c] = r < len ? to_f32(src[((tok + r) * H + h) * (int64_t)N + c]) : 0.f;
+  }
+}
+
+// 64 x N fp32 block of a record or scratch (row-major, stride N) into LDS
+template <int N, int L>
+__device__ __forceinline__ void load_block(float* dst, const float* src) {
+  for (int e = threadIdx.x; e < BC * N; e += NT) dst[(e / N) * L + e % N] = src[e];
+}
+
+// cumulative log2 decay: dst (64 x K, stride L) holds log alpha on entry, b * log2 e on exit
+template <int K, int L>
+__device__ __forceinline__ void cumsum_log2(float* sB) {
+  if (threadIdx.x < K) {
+    float acc = 0.f;
+    for (int r = 0; r < BC; ++r) {
+      acc += sB[r * L + threadIdx.x];
+      sB[r * L + threadIdx.x] = acc * LOG2E;
+    }
+  }
+}
+
+}  // namespace
+
+struct BwdChunk {
+  int32_t seq, tok, len, pad;
+};
+
+// seq_first[n] = the first chunk of sequence n, seq_first[N] = the number of chunks (one block)
+__global__ __launch_bounds__(NT) void bwd_seq_kernel(const int32_t* __restrict__ cu, int N,
+                                                     int64_t T, int32_t* __restrict__ seq_first) {
+  __shared__ int32_t part[NT];
+  int32_t carry = 0;
+  for (int base = 0; base < N; base += NT) {
+    const int n = base + threadIdx.x;
+    int32_t cnt = 0;
+    if (n < N) {
+      const int64_t a = cu ? cu[n] : (T / N) * n, b = cu ? cu[n + 1] : (T / N) * (n + 1);
+      cnt = (int32_t)((b - a + BC - 1) / BC);
+    }
+    part[threadIdx.x] = cnt;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {  // inclusive scan
+      const int32_t x = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+      __syncthreads();
+      part[threadIdx.x] += x;
+      __syncthreads();
+    }
+    if (n < N) seq_first[n] = carry + part[threadIdx.x] - cnt;
+    carry += part[NT - 1];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) seq_first[N] = carry;
+}
+
+// chunk c: its sequence (the last n with seq_first[n] <= c), first token and length
+__global__ __launch_bounds__(NT) void bwd_chunk_kernel(const int32_t* __restrict__ cu, int N,
+                                                       int64_t T, const int32_t* __restrict__ seq_first,
+                                                       int64_t ub, BwdChunk* __restrict__ chunks) {
+  const int64_t c = blockIdx.x * (int64_t)NT + threadIdx.x;
+  if (c >= ub || c >= seq_first[N]) return;
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (seq_first[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  const int64_t s1 = cu ? cu[lo + 1] : (T / N) * (lo + 1);
+  const int64_t s0 = cu ? cu[lo] : (T / N) * lo;
+  const int64_t tok = s0 + (c - seq_first[lo]) * BC;
+  chunks[c] = BwdChunk{lo, (int32_t)tok, (int32_t)min((int64_t)BC, s1 - tok), 0};
+}
+
+// ---------------------------------------------------------------- per-chunk record
+template <int K, int V, typename MT>
+__global__ __launch_bounds__(NT) void bwd_prep_kernel(
+    const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ v,
+    const MT* __restrict__ g, const MT* __restrict__ beta, int H,
+    const BwdChunk* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ rec) {
+  using R = BRec<K, V>;
+  constexpr int N1 = K > V ? K : V, L = N1 + 4, LK = K + 4;
+  __shared__ __align__(16) float sQ[BC * L];   // q, then beta v
+  __shared__ __align__(16) float sK[BC * LK];  // k, then beta k e^b
+  __shared__ __align__(16) float sB[BC * LK];  // b log2 e
+  __shared__ __align__(16) float sA[BC * 68];  // A (strict lower)
+  __shared__ __align__(16) float sT[BC * 68];  // T = (I + A)^{-1}
+  __shared__ float sBeta[BC];
+  const int c = blockIdx.x, h = blockIdx.y;
+  if (c >= *ntot) return;
+  const BwdChunk ch = chunks[c];
+  float* rc = rec + ((size_t)c * H + h) * R::floats;
+  load_rows<K, L>(sQ, q, ch.tok, ch.len, H, h);
+  load_rows<K, LK>(sK, k, ch.tok, ch.len, H, h);
+  load_rows<K, LK>(sB, g, ch.tok, ch.len, H, h);
+  if (threadIdx.x < BC)
+    sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
+  __syncthreads();
+  cumsum_log2<K, LK>(sB);
+  __syncthreads();
+  // Qe, Kt, gamma (rows past len hold q = k = 0, and b stays at its last value)
+  for (int e = threadIdx.x; e < BC * K; e += NT) {
+    const int r = e / K, cc = e % K;
+    const float br = sB[r * LK + cc], bl = sB[(BC - 1) * LK + cc];
+    rc[R::oQe + e] = sQ[r * L + cc] * exp2_f(br);
+    rc[R::oKt + e] = sK[r * LK + cc] * exp2_f(bl - br);
+  }
+  if (threadIdx.x < K) rc[R::oGam + threadIdx.x] = exp2_f(sB[(BC - 1) * LK + threadIdx.x]);
+  // A_ij = beta_i sum_c k_ic k_jc e^{b_ic - b_jc} (j < i) and P_ij = sum_c q_ic k_jc e^{..} (j <= i);
+  // thread (i, jq) forms j = jq + 4u, rows spread so that every wave has short and long rows
+  {
+    const int i = 4 * ((threadIdx.x >> 2) & 15) + (threadIdx.x >> 6), jq = threadIdx.x & 3;
+    float a[16], p[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) a[u] = p[u] = 0.f;
+    for (int c4 = 0; c4 < K; c4 += 4) {
+      const f32x4 qi = *reinterpret_cast<const f32x4*>(sQ + i * L + c4);
+      const f32x4 ki = *reinterpret_cast<const f32x4*>(sK + i * LK + c4);
+      const f32x4 bi = *reinterpret_cast<const f32x4*>(sB + i * LK + c4);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int j = jq + 4 * u;
+        if (j <= i) {
+          const f32x4 kj = *reinterpret_cast<const f32x4*>(sK + j * LK + c4);
+          const f32x4 bj = *reinterpret_cast<const f32x4*>(sB + j * LK + c4);
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = kj[e] * exp2_f(bi[e] - bj[e]);
+          a[u] += dot4(ki, w);
+          p[u] += dot4(qi, w);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = jq + 4 * u;
+      sA[i * 68 + j] = j < i ? sBeta[i] * a[u] : 0.f;
+      rc[R::oP + i * BC + j] = j <= i ? p[u] : 0.f;
+    }
+  }
+  __syncthreads();
+  // T = (I + A)^{-1} by forward substitution, one column per thread
+  if (threadIdx.x < BC) {
+    const int m = threadIdx.x;
+    float x[BC];
+#pragma unroll
+    for (int i = 0; i < BC; ++i) {
+      float s = i == m ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < i; ++j) s -= sA[i * 68 + j] * x[j];
+      x[i] = s;
+    }
+#pragma unroll
+    for (int i = 0; i < BC; ++i) {
+      sT[i * 68 + m] = x[i];
+      rc[R::oT + i * BC + m] = x[i];
+    }
+  }
+  // beta k e^b and beta v replace k and q
+  for (int e = threadIdx.x; e < BC * K; e += NT) {
+    const int r = e / K, cc = e % K;
+    sK[r * LK + cc] *= sBeta[r] * exp2_f(sB[r * LK + cc]);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < BC * V; e += NT) {
+    const int r = e / V, cc = e % V;
+    sQ[r * L + cc] = r < ch.len ? sBeta[r] * to_f32(v[((ch.tok + r) * H + h) * (int64_t)V + cc]) : 0.f;
+  }
+  __syncthreads();
+  mm64<K, 68, LK, false>(sT, sK, [&](int r, int cc, float x) { rc[R::oW + r * K + cc] = x; });
+  mm64<V, 68, L, false>(sT, sQ, [&](int r, int cc, float x) { rc[R::oU + r * V + cc] = x; });
+}
+
+// ---------------------------------------------------------------- the chains
+// One workgroup per (sequence, head, 16 value columns); the slices of one chain share
+// blockIdx % 8 (one XCD's L2) with blockIdx = slice * chains8 + chain.
+template <int K, int V>
+__global__ __launch_bounds__(NT) void bwd_fstate_kernel(
+    const float* __restrict__ rec, const float* __restrict__ init, const int32_t* __restrict__ seq_first,
+    int N, int H, int chains8, float* __restrict__ ckS, float* __restrict__ Dl) {
+  using R = BRec<K, V>;
+  constexpr int NC = K / 16;  // columns per thread in the state update
+  __shared__ __align__(16) float sS[K * 16];
+  __shared__ __align__(16) float sD[BC * 16];
+  const int nh = blockIdx.x % chains8, s = blockIdx.x / chains8;
+  if (nh >= N * H) return;
+  const int n = nh / H, h = nh % H, c0 = 16 * s;
+  for (int e = threadIdx.x; e < K * 16; e += NT)
+    sS[e] = init ? init[((size_t)nh * K + e / 16) * V + c0 + e % 16] : 0.f;
+  const int first = seq_first[n], last = seq_first[n + 1];
+  const int i = threadIdx.x >> 2, jj = 4 * (threadIdx.x & 3);
+  const int m = threadIdx.x % K, cg = (threadIdx.x / K) * NC;
+  for (int c = first; c < last; ++c) {
+    const float* rc = rec + ((size_t)c * H + h) * R::floats;
+    __syncthreads();
+    for (int e = threadIdx.x; e < K * 16; e += NT)
+      ckS[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sS[e];
+    // Delta = U - W S for row i, columns jj .. jj + 3
+    f32x4 d = *reinterpret_cast<const f32x4*>(rc + R::oU + i * V + c0 + jj);
+    for (int mm = 0; mm < K; mm += 4) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(rc + R::oW + i * K + mm);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d -= w[e] * *reinterpret_cast<const f32x4*>(sS + (mm + e) * 16 + jj);
+    }
+    *reinterpret_cast<f32x4*>(Dl + (((size_t)c * H + h) * BC + i) * V + c0 + jj) = d;
+    *reinterpret_cast<f32x4*>(sD + i * 16 + jj) = d;
+    __syncthreads();
+    // S' = diag(gamma) S + Kt^T Delta for row m, columns cg .. cg + NC - 1
+    const float gm = rc[R::oGam + m];
+    float acc[NC];
+#pragma unroll
+    for (int e = 0; e < NC; ++e) acc[e] = gm * sS[m * 16 + cg + e];
+    for (int r = 0; r < BC; ++r) {
+      const float kt = rc[R::oKt + r * K + m];
+#pragma unroll
+      for (int e = 0; e < NC; ++e) acc[e] += kt * sD[r * 16 + cg + e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < NC; ++e) sS[m * 16 + cg + e] = acc[e];
+  }
+}
+
+template <int K, int V, typename MT>
+__global__ __launch_bounds__(NT) void bwd_rstate_kernel(
+    const float* __restrict__ rec, const MT* __restrict__ dO, const float* __restrict__ dfin,
+    const BwdChunk* __restrict__ chunks, const int32_t* __restrict__ seq_first, int N, int H,
+    int chains8, float* __restrict__ ckX, float* __restrict__ dDl, float* __restrict__ dinit) {
+  using R = BRec<K, V>;
+  constexpr int NC = K / 16;
+  __shared__ __align__(16) float sX[K * 16];
+  __shared__ __align__(16) float sO[BC * 16];
+  __shared__ __align__(16) float sDD[BC * 16];
+  const int nh = blockIdx.x % chains8, s = blockIdx.x / chains8;
+  if (nh >= N * H) return;
+  const int n = nh / H, h = nh % H, c0 = 16 * s;
+  for (int e = threadIdx.x; e < K * 16; e += NT)
+    sX[e] = dfin ? dfin[((size_t)nh * K + e / 16) * V + c0 + e % 16] : 0.f;
+  const int first = seq_first[n], last = seq_first[n + 1];
+  const int i = threadIdx.x >> 2, jj = 4 * (threadIdx.x & 3);
+  const int m = threadIdx.x % K, cg = (threadIdx.x / K) * NC;
+  for (int c = last - 1; c >= first; --c) {
+    const float* rc = rec + ((size_t)c * H + h) * R::floats;
+    const BwdChunk ch = chunks[c];
+    __syncthreads();
+    for (int e = threadIdx.x; e < K * 16; e += NT)
+      ckX[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sX[e];
+    for (int e = threadIdx.x; e < BC * 16; e += NT) {
+      const int r = e / 16;
+      sO[e] = r < ch.len ? to_f32(dO[((ch.tok + r) * (int64_t)H + h) * V + c0 + e % 16]) : 0.f;
+    }
+    __syncthreads();
+    // dDelta = P^T dO + Kt X for row i, columns jj .. jj + 3
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+    for (int r = i; r < BC; ++r)
+      d += rc[R::oP + r * BC + i] * *reinterpret_cast<const f32x4*>(sO + r * 16 + jj);
+    for (int mm = 0; mm < K; mm += 4) {
+      const f32x4 kt = *reinterpret_cast<const f32x4*>(rc + R::oKt + i * K + mm);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d += kt[e] * *reinterpret_cast<const f32x4*>(sX + (mm + e) * 16 + jj);
+    }
+    *reinterpret_cast<f32x4*>(dDl + (((size_t)c * H + h) * BC + i) * V + c0 + jj) = d;
+    *reinterpret_cast<f32x4*>(sDD + i * 16 + jj) = d;
+    __syncthreads();
+    // X_prev = diag(gamma) X + Qe^T dO - W^T dDelta for row m, columns cg .. cg + NC - 1
+    const float gm = rc[R::oGam + m];
+    float acc[NC];
+#pragma unroll
+    for (int e = 0; e < NC; ++e) acc[e] = gm * sX[m * 16 + cg + e];
+    for (int r = 0; r < BC; ++r) {
+      const float qe = rc[R::oQe + r * K + m], w = rc[R::oW + r * K + m];
+#pragma unroll
+      for (int e = 0; e < NC; ++e) acc[e] += qe * sO[r * 16 + cg + e] - w * sDD[r * 16 + cg + e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < NC; ++e) sX[m * 16 + cg + e] = acc[e];
+  }
+  if (dinit) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < K * 16; e += NT)
+      dinit[((size_t)nh * K + e / 16) * V + c0 + e % 16] = sX[e];
+  }
+}
+
+// ---------------------------------------------------------------- per-chunk gradients
+// (a) dP = lower(dO Delta^T); with S (chunk start) and X (chunk end) streamed from HBM:
+//     dO S^T, dW = -dDelta S^T, Delta X^T and rowsum(S * X)
+template <int K, int V, typename MT>
+__global__ __launch_bounds__(NT) void bwd_ga_kernel(
+    const MT* __restrict__ dO, const float* __restrict__ ckS, const float* __restrict__ ckX,
+    const float* __restrict__ Dl, const float* __restrict__ dDl, int H,
+    const BwdChunk* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr) {
+  using G = GScr<K>;
+  constexpr int L = V + 4;
+  __shared__ __align__(16) float sO[BC * L];
+  __shared__ __align__(16) float sDl[BC * L];
+  __shared__ __align__(16) float sDD[BC * L];
+  const int c = blockIdx.x, h = blockIdx.y;
+  if (c >= *ntot) return;
+  const BwdChunk ch = chunks[c];
+  const size_t ch_h = (size_t)c * H + h;
+  float* sc = scr + ch_h * G::floats;
+  load_rows<V, L>(sO, dO, ch.tok, ch.len, H, h);
+  load_block<V, L>(sDl, Dl + ch_h * BC * V);
+  load_block<V, L>(sDD, dDl + ch_h * BC * V);
+  __syncthreads();
+  rowdot64<V, L>(sO, sDl, [&](int i, int j, float x) { sc[G::oDP + i * BC + j] = j <= i ? x : 0.f; });
+  // thread: key channel m, rows r0 .. r0 + RB - 1
+  constexpr int NG = NT / K, RB = BC / NG;
+  const int m = threadIdx.x % K, r0 = (threadIdx.x / K) * RB;
+  const float* Sm = ckS + (ch_h * K + m) * V;
+  const float* Xm = ckX + (ch_h * K + m) * V;
+  float r1[RB], dw[RB], dkt[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) r1[u] = dw[u] = dkt[u] = 0.f;
+  float dg = 0.f;
+  for (int vv = 0; vv < V; vv += 4) {
+    const f32x4 s4 = *reinterpret_cast<const f32x4*>(Sm + vv);
+    const f32x4 x4 = *reinterpret_cast<const f32x4*>(Xm + vv);
+    dg += dot4(s4, x4);
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      r1[u] += dot4(*reinterpret_cast<const f32x4*>(sO + (r0 + u) * L + vv), s4);
+      dw[u] -= dot4(*reinterpret_cast<const f32x4*>(sDD + (r0 + u) * L + vv), s4);
+      dkt[u] += dot4(*reinterpret_cast<const f32x4*>(sDl + (r0 + u) * L + vv), x4);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < RB; ++u) {
+    sc[G::oR1 + (r0 + u) * K + m] = r1[u];
+    sc[G::oDW + (r0 + u) * K + m] = dw[u];
+    sc[G::oDKt + (r0 + u) * K + m] = dkt[u];
+  }
+  if (r0 == 0) sc[G::oDG + m] = dg;
+}
+
+// (b) dv = diag(beta) T^T dDelta, T^T dW, dT = dDelta (beta V)^T + dW (beta Ke)^T,
+//     dA = strict_lower(-T^T dT T^T), and dbeta's terms rowsum(V * T^T dDelta) and
+//     rowsum(Ke * T^T dW)
+template <int K, int V, typename MT>
+__global__ __launch_bounds__(NT) void bwd_gb_kernel(
+    const MT* __restrict__ k, const MT* __restrict__ v, const MT* __restrict__ g,
+    const MT* __restrict__ beta, const float* __restrict__ rec, const float* __restrict__ dDl, int H,
+    const BwdChunk* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr,
+    float* __restrict__ grad_v) {
+  using R = BRec<K, V>;
+  using G = GScr<K>;
+  constexpr int N1 = K > V ? K : V, L = N1 + 4, LV = V + 4, LK = K + 4;
+  constexpr int LA = L > 68 ? L : 68;  // bufA also holds a 64 x 64 product (row stride 68)
+  __shared__ __align__(16) float sT[BC * 68];
+  __shared__ __align__(16) float sdT[BC * 68];
+  __shared__ __align__(16) float bufA[BC * LA];
+  __shared__ __align__(16) float bufB[BC * L];
+  __shared__ float sBeta[BC], sDb[BC];
+  const int c = blockIdx.x, h = blockIdx.y;
+  if (c >= *ntot) return;
+  const BwdChunk ch = chunks[c];
+  const size_t ch_h = (size_t)c * H + h;
+  const float* rc = rec + ch_h * R::floats;
+  float* sc = scr + ch_h * G::floats;
+  for (int e = threadIdx.x; e < BC * BC; e += NT) sT[(e / BC) * 68 + e % BC] = rc[R::oT + e];
+  load_block<V, LV>(bufA, dDl + ch_h * BC * V);
+  if (threadIdx.x < BC) {
+    sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
+    sDb[threadIdx.x] = 0.f;
+  }
+  __syncthreads();
+  load_rows<V, LV>(bufB, v, ch.tok, ch.len, H, h);
+  __syncthreads();
+  // T^T dDelta: dv = beta T^T dDelta, dbeta += rowsum(v * T^T dDelta)
+  mm64<V, 68, LV, true>(sT, bufA, [&](int r, int cc, float x) {
+    if (r < ch.len) grad_v[((ch.tok + r) * (int64_t)H + h) * V + cc] = sBeta[r] * x;
+    atomicAdd(&sDb[r], bufB[r * LV + cc] * x);
+  });
+  __syncthreads();
+  for (int e = threadIdx.x; e < BC * V; e += NT) bufB[(e / V) * LV + e % V] *= sBeta[e / V];
+  __syncthreads();
+  rowdot64<V, LV>(bufA, bufB, [&](int i, int j, float x) { sdT[i * 68 + j] = x; });
+  __syncthreads();
+  // dW and Ke = k e^b
+  load_block<K, LK>(bufA, sc + G::oDW);
+  load_rows<K, LK>(bufB, g, ch.tok, ch.len, H, h);
+  __syncthreads();
+  cumsum_log2<K, LK>(bufB);
+  __syncthreads();
+  for (int e = threadIdx.x; e < BC * K; e += NT) {
+    const int r = e / K, cc = e % K;
+    bufB[r * LK + cc] = r < ch.len ? to_f32(k[((ch.tok + r) * (int64_t)H + h) * K + cc]) *
+                                         exp2_f(bufB[r * LK + cc]) : 0.f;
+  }
+  __syncthreads();
+  // T^T dW; dbeta += rowsum(Ke * T^T dW)
+  mm64<K, 68, LK, true>(sT, bufA, [&](int r, int cc, float x) {
+    sc[G::oTDW + r * K + cc] = x;
+    atomicAdd(&sDb[r], bufB[r * LK + cc] * x);
+  });
+  // dT += dW (beta Ke)^T (each thread adds to the entries it owns)
+  rowdot64<K, LK>(bufA, bufB, [&](int i, int j, float x) { sdT[i * 68 + j] += sBeta[j] * x; });
+  __syncthreads();
+  // M1 = T^T dT into bufA, then dA = strict_lower(-M1 T^T)
+  mm64<BC, 68, 68, true>(sT, sdT, [&](int r, int cc, float x) { bufA[r * 68 + cc] = x; });
+  __syncthreads();
+  rowdot64<BC, 68>(bufA, sT, [&](int i, int j, float x) { sc[G::oDA + i * BC + j] = j < i ? -x : 0.f; });
+  if (threadIdx.x < BC) sc[G::oDB + threadIdx.x] = sDb[threadIdx.x];
+}
+
+// (c) the decay-weighted pairwise sums and the per-token gradients of q, k, log alpha, beta
+template <int K, int V, typename MT>
+__global__ __launch_bounds__(NT) void bwd_gc_kernel(
+    const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ g,
+    const MT* __restrict__ beta, int H, const BwdChunk* __restrict__ chunks,
+    const int32_t* __restrict__ ntot, const float* __restrict__ scr, float* __restrict__ grad_q,
+    float* __restrict__ grad_k, float* __restrict__ grad_g, float* __restrict__ grad_beta) {
+  using G = GScr<K>;
+  constexpr int LK = K + 4;
+  __shared__ __align__(16) float sQ[BC * LK];
+  __shared__ __align__(16) float sK[BC * LK];
+  __shared__ __align__(16) float sB[BC * LK];
+  __shared__ __align__(16) float sdP[BC * 68];
+  __shared__ __align__(16) float sdA[BC * 68];
+  __shared__ float sBeta[BC], sDb[BC], sRed[K];
+  const int c = blockIdx.x, h = blockIdx.y;
+  if (c >= *ntot) return;
+  const BwdChunk ch = chunks[c];
+  const size_t ch_h = (size_t)c * H + h;
+  const float* sc = scr + ch_h * G::floats;
+  load_rows<K, LK>(sQ, q, ch.tok, ch.len, H, h);
+  load_rows<K, LK>(sK, k, ch.tok, ch.len, H, h);
+  load_rows<K, LK>(sB, g, ch.tok, ch.len, H, h);
+  for (int e = threadIdx.x; e < BC * BC; e += NT) {
+    sdP[(e / BC) * 68 + e % BC] = sc[G::oDP + e];
+    sdA[(e / BC) * 68 + e % BC] = sc[G::oDA + e];
+  }
+  if (threadIdx.x < BC) {
+    sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
+    sDb[threadIdx.x] = 0.f;
+  }
+  if (threadIdx.x < K) sRed[threadIdx.x] = 0.f;
+  __syncthreads();
+  cumsum_log2<K, LK>(sB);
+  __syncthreads();
+  // thread: key channel m, rows i = i0 + NG u (interleaved: the pairwise sums grow with i)
+  constexpr int NG = NT / K, RB = BC / NG;
+  const int m = threadIdx.x % K, i0 = threadIdx.x / K;
+  const float bl = sB[(BC - 1) * LK + m];
+  float db[RB];
+  float red = 0.f;
+#pragma unroll
+  for (int u = 0; u < RB; ++u) {
+    const int i = i0 + NG * u;
+    const float bi = sB[i * LK + m], qi = sQ[i * LK + m], ki = sK[i * LK + m];
+    // sum_{j <= i} dP_ij k_j e^{b_i - b_j} and sum_{j < i} dA_ij k_j e^{b_i - b_j}
+    float s1 = 0.f, s2 = 0.f;
+    for (int j = 0; j <= i; ++j) {
+      const float w = sK[j * LK + m] * exp2_f(bi - sB[j * LK + m]);
+      s1 += sdP[i * 68 + j] * w;
+      s2 += sdA[i * 68 + j] * w;
+    }
+    // sum_{r >= i} (dA_ri beta_r k_r + dP_ri q_r) e^{b_r - b_i}
+    float s3 = 0.f;
+    for (int r = i; r < BC; ++r)
+      s3 += (sdA[r * 68 + i] * sBeta[r] * sK[r * LK + m] + sdP[r * 68 + i] * sQ[r * LK + m]) *
+            exp2_f(sB[r * LK + m] - bi);
+    const float eb = exp2_f(bi);
+    const float dq = sc[G::oR1 + i * K + m] * eb + s1;
+    const float dke = sBeta[i] * (sc[G::oTDW + i * K + m] * eb + s2);
+    const float dkt = sc[G::oDKt + i * K + m] * exp2_f(bl - bi);
+    const float dk = dke + s3 + dkt;
+    atomicAdd(&sDb[i], ki * s2);
+    red += ki * dkt;
+    db[u] = qi * dq + ki * (dke - s3 - dkt);
+    if (i < ch.len) {
+      const int64_t o = ((ch.tok + i) * (int64_t)H + h) * K + m;
+      grad_q[o] = dq;
+      grad_k[o] = dk;
+    }
+  }
+  atomicAdd(&sRed[m], red);
+  __syncthreads();  // every read of sQ done
+#pragma unroll
+  for (int u = 0; u < RB; ++u) sQ[(i0 + NG * u) * LK + m] = db[u];
+  __syncthreads();
+  // log alpha: reverse cumulative sum of db over the chunk, the last token also carrying
+  // sum_i k_i * dKt_i and gamma * rowsum(S * X)
+  if (threadIdx.x < K) {
+    float acc = sRed[m] + sc[G::oDG + m] * exp2_f(bl);
+    for (int r = BC - 1; r >= 0; --r) {
+      acc += sQ[r * LK + m];
+      if (r < ch.len) grad_g[((ch.tok + r) * (int64_t)H + h) * K + m] = acc;
+    }
+  }
+  if (threadIdx.x < ch.len)
+    grad_beta[(ch.tok + threadIdx.x) * (int64_t)H + h] = sc[G::oDB + threadIdx.x] + sDb[threadIdx.x];
+}
+
+// ---------------------------------------------------------------- host
+static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+template <int K, int V>
+static void bwd_sizes(int64_t ub, int H, size_t* rec_f, size_t* scr_f) {
+  *rec_f = (size_t)ub * H * BRec<K, V>::floats;
+  *scr_f = (size_t)ub * H * GScr<K>::floats;
+}
+
+bool make_bwd_plan(int N, int64_t T, int H, int K, int V, BwdPlan* p) {
+  if (N <= 0 || H <= 0 || T < 0) return false;
+  int64_t ub = (T + (int64_t)N * (BC - 1)) / BC;
+  if (ub > T) ub = T;
+  p->ub = ub;
+  size_t rec_f = 0, scr_f = 0;
+#define KDA_BWD_SIZES(KK, VV) \
+  if (K == KK && V == VV) bwd_sizes<KK, VV>(ub, H, &rec_f, &scr_f);
+  KDA_BWD_SIZES(32, 32) KDA_BWD_SIZES(32, 64) KDA_BWD_SIZES(32, 128)
+  KDA_BWD_SIZES(64, 32) KDA_BWD_SIZES(64, 64) KDA_BWD_SIZES(64, 128)
+  KDA_BWD_SIZES(128, 32) KDA_BWD_SIZES(128, 64) KDA_BWD_SIZES(128, 128)
+#undef KDA_BWD_SIZES
+  if (rec_f == 0 && ub > 0) return false;
+  const size_t chv = (size_t)ub * H;
+  size_t off = 0;
+  p->off_seq = off;
+  off += al256((size_t)(N + 1) * 4);
+  p->off_chunks = off;
+  off += al256((size_t)ub * sizeof(BwdChunk));
+  p->off_rec = off;
+  off += al256(rec_f * 4);
+  p->off_ckS = off;
+  off += al256(chv * K * V * 4);
+  p->off_ckX = off;
+  off += al256(chv * K * V * 4);
+  p->off_D = off;
+  off += al256(chv * BC * V * 4);
+  p->off_dD = off;
+  off += al256(chv * BC * V * 4);
+  p->off_scr = off;
+  off += al256(scr_f * 4);
+  p->total_bytes = off;
+  return true;
+}
+
+template <int K, int V, typename MT>
+static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
+  hipStream_t st = (hipStream_t)a.stream;
+  char* ws = reinterpret_cast<char*>(a.workspace);
+  int32_t* seq_first = reinterpret_cast<int32_t*>(ws + p.off_seq);
+  BwdChunk* chunks = reinterpret_cast<BwdChunk*>(ws + p.off_chunks);
+  float* rec = reinterpret_cast<float*>(ws + p.off_rec);
+  float* ckS = reinterpret_cast<float*>(ws + p.off_ckS);
+  float* ckX = reinterpret_cast<float*>(ws + p.off_ckX);
+  float* Dl = reinterpret_cast<float*>(ws + p.off_D);
+  float* dDl = reinterpret_cast<float*>(ws + p.off_dD);
+  float* scr = reinterpret_cast<float*>(ws + p.off_scr);
+  const int N = a.num_seqs, H = a.num_heads;
+  const int32_t* ntot = seq_first + N;
+  const MT *q = (const MT*)a.q, *k = (const MT*)a.k, *v = (const MT*)a.v, *g = (const MT*)a.g,
+           *beta = (const MT*)a.beta, *dO = (const MT*)a.dO;
+  hipLaunchKernelGGL(bwd_seq_kernel, dim3(1), dim3(NT), 0, st, a.cu_seqlens, N, a.total_tokens,
+                     seq_first);
+  if (p.ub > 0)
+    hipLaunchKernelGGL(bwd_chunk_kernel, dim3((unsigned)((p.ub + NT - 1) / NT)), dim3(NT), 0, st,
+                       a.cu_seqlens, N, a.total_tokens, (const int32_t*)seq_first, p.ub, chunks);
+  const dim3 cgrid((unsigned)(p.ub > 0 ? p.ub : 1), (unsigned)H);
+  if (p.ub > 0)
+    hipLaunchKernelGGL((bwd_prep_kernel<K, V, MT>), cgrid, dim3(NT), 0, st, q, k, v, g, beta, H,
+                       (const BwdChunk*)chunks, ntot, rec);
+  const int chains8 = (N * H + 7) / 8 * 8;
+  const dim3 sgrid((unsigned)(chains8 * (V / 16)));
+  hipLaunchKernelGGL((bwd_fstate_kernel<K, V>), sgrid, dim3(NT), 0, st, (const float*)rec,
+                     a.init_state, (const int32_t*)seq_first, N, H, chains8, ckS, Dl);
+  hipLaunchKernelGGL((bwd_rstate_kernel<K, V, MT>), sgrid, dim3(NT), 0, st, (const float*)rec, dO,
+                     a.dfinal, (const BwdChunk*)chunks, (const int32_t*)seq_first, N, H, chains8,
+                     ckX, dDl, a.grad_init);
+  if (p.ub > 0) {
+    hipLaunchKernelGGL((bwd_ga_kernel<K, V, MT>), cgrid, dim3(NT), 0, st, dO, (const float*)ckS,
+                       (const float*)ckX, (const float*)Dl, (const float*)dDl, H,
+                       (const BwdChunk*)chunks, ntot, scr);
+    hipLaunchKernelGGL((bwd_gb_kernel<K, V, MT>), cgrid, dim3(NT), 0, st, k, v, g, beta,
+                       (const float*)rec, (const float*)dDl, H, (const BwdChunk*)chunks, ntot, scr,
+                       a.grad_v);
+    hipLaunchKernelGGL((bwd_gc_kernel<K, V, MT>), cgrid, dim3(NT), 0, st, q, k, g, beta, H,
+                       (const BwdChunk*)chunks, ntot, (const float*)scr, a.grad_q, a.grad_k,
+                       a.grad_g, a.grad_beta);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a, const BwdPlan& p) {
+#define KDA_BWD_CASE(KK, VV)                                                     \
+  if (a.dk == KK && a.dv == VV)                                                  \
+    return a.dtype_bf16 ? launch_bwd_t<KK, VV, bf16>(a, p) : launch_bwd_t<KK, VV, float>(a, p);
+  KDA_BWD_CASE(32, 32) KDA_BWD_CASE(32, 64) KDA_BWD_CASE(32, 128)
+  KDA_BWD_CASE(64, 32) KDA_BWD_CASE(64, 64) KDA_BWD_CASE(64, 128)
+  KDA_BWD_CASE(128, 32) KDA_BWD_CASE(128, 64) KDA_BWD_CASE(128, 128)
+#undef KDA_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -106,4 +106,29 @@ bool make_scan_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, i
                     int groups, ScanPlan* p);
 hipError_t launch_chunk_fwd_scan(const ChunkArgs& a, int groups, const ScanPlan& p);
 
+// Training backward (kda_bwd.hip): per chunk and head an fp32 record, the chunk-start states,
+// the chunk-end state gradients, Delta, dDelta and the gradient kernels' scratch, for every
+// chunk at once.
+struct BwdPlan {
+  int64_t ub;  // upper bound of the number of chunks over all sequences
+  size_t off_seq, off_chunks, off_rec, off_ckS, off_ckX, off_D, off_dD, off_scr, total_bytes;
+};
+bool make_bwd_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv, BwdPlan* p);
+
+struct BwdArgs {
+  const void *q, *k, *v, *g, *beta;
+  const float* init_state;
+  const int32_t* cu_seqlens;
+  int num_seqs;
+  int64_t total_tokens;
+  int num_heads, dk, dv;
+  bool dtype_bf16;
+  const void* dO;
+  const float* dfinal;
+  float *grad_q, *grad_k, *grad_v, *grad_g, *grad_beta, *grad_init;
+  void* workspace;
+  void* stream;
+};
+hipError_t launch_chunk_bwd(const BwdArgs& a, const BwdPlan& p);
+
 }  // namespace kda

@@ -163,6 +163,39 @@ kda_status kda_chunk_fwd_scan(const void* q, const void* k, const void* v, const
                               void* stream);
 
 /*
+ * Training backward of kda_chunk_fwd (options = 0): the gradients of
+ *     L = sum(d_o * o) + sum(d_final_state * final_state)
+ * with respect to q, k, v, log_alpha, beta and init_state, for the forward on the same inputs
+ * (same q, k, v, log_alpha, beta, init_state, cu_seqlens and shapes), by reverse mode through
+ * the chunk form ("A Technical Breakdown", section 4; "Kimi Linear" explainer, "WY
+ * Representation"): the chunk-start states are recomputed, the state gradient is carried
+ * backwards chunk by chunk, and the per-token gradients of each chunk follow from it. All of
+ * it runs in fp32.
+ *   d_o            : [rows][H][V], dtype
+ *   d_final_state  : [N][H][K][V] fp32, or NULL (zero)
+ *   grad_q, grad_k, grad_log_alpha : [rows][H][K] fp32 (written)
+ *   grad_v         : [rows][H][V] fp32 (written)
+ *   grad_beta      : [rows][H] fp32 (written; 4-byte aligned)
+ *   grad_init_state: [N][H][K][V] fp32 (written), or NULL (not needed); with a NULL init_state
+ *                    it is still the gradient with respect to the zero initial state.
+ * Gradients of rows past the end of every sequence are not written (there are none: cu_seqlens
+ * covers all rows). No gradient buffer may overlap an input or another gradient
+ * (KDA_ERROR_INVALID_VALUE). Head dims K, V in {32, 64, 128}, both dtypes; others give
+ * KDA_ERROR_NOT_SUPPORTED. The workspace (kda_chunk_bwd_workspace_size bytes, 256-byte aligned)
+ * holds, for every (chunk, head), an fp32 record, the chunk-start state and the chunk-end state
+ * gradient and scratch: about 512 KB per 64 tokens and head at K = V = 128.
+ */
+size_t kda_chunk_bwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                    int32_t dk, int32_t dv, kda_dtype dtype);
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* beta, const float* init_state, const int32_t* cu_seqlens,
+                         int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t dk,
+                         int32_t dv, kda_dtype dtype, const void* d_o,
+                         const float* d_final_state, float* grad_q, float* grad_k, float* grad_v,
+                         float* grad_log_alpha, float* grad_beta, float* grad_init_state,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One recurrent KDA token step per (sequence, head), state updated in place (decode).
  * The decay, prediction u = (Diag(alpha) S)^T k, erase-and-write and read are fused into one
  * pass that streams each fp32 state once from HBM and writes it once.

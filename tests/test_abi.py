@@ -19,6 +19,7 @@ def test_every_declared_symbol_is_exported():
     names = kda.declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_fwd_workspace_size",
                           "kda_chunk_fwd_scan", "kda_chunk_fwd_scan_workspace_size",
+                          "kda_chunk_bwd", "kda_chunk_bwd_workspace_size",
                           "kda_decode_step", "kda_decode_step_ex", "kda_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -185,3 +186,53 @@ def test_scan_workspace_size():
     assert ws(1, 65536, 4, 128, 64, 1, 8) == 0
     assert ws(1, 65536, 4, 128, 128, 1, 0) == 0
     assert ws(3, 100, 4, 64, 64, 0, 2) == 0
+
+
+def _bwd(L, **kw):
+    a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, init=None, cu=None, N=1, T=128, H=2,
+             dk=32, dv=32, dtype=BF16, do=6 * A, dfin=None, gq=7 * A, gk=8 * A, gv=9 * A,
+             gg=10 * A, gb=11 * A, ginit=12 * A, ws=13 * A, wsb=1 << 40, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kda_chunk_bwd(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]),
+                           vp(a["init"]), vp(a["cu"]), a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                           a["dtype"], vp(a["do"]), vp(a["dfin"]), vp(a["gq"]), vp(a["gk"]),
+                           vp(a["gv"]), vp(a["gg"]), vp(a["gb"]), vp(a["ginit"]), vp(a["ws"]),
+                           a["wsb"], vp(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=0), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(N=3, T=128), INVALID),            # equal lengths need T % N == 0
+    (dict(dk=48), NOT_SUPPORTED),
+    (dict(dv=256), NOT_SUPPORTED),          # the gradient kernels hold V <= 128 in LDS
+    (dict(dtype=7), NOT_SUPPORTED),
+    (dict(q=None), INVALID),
+    (dict(do=None), INVALID),
+    (dict(gq=None), INVALID),
+    (dict(gb=None), INVALID),
+    (dict(k=2 * A + 8), INVALID),           # 16-byte alignment
+    (dict(gv=9 * A + 4), INVALID),
+    (dict(beta=5 * A + 1), INVALID),        # element alignment
+    (dict(ws=13 * A + 64), INVALID),        # 256-byte aligned workspace
+    (dict(ws=None), INVALID),
+    (dict(wsb=4096), WS_SMALL),
+    (dict(gq=A), INVALID),                  # a gradient over an input
+    (dict(gk=7 * A), INVALID),              # two gradients on one buffer
+    (dict(ginit=6 * A), INVALID),
+])
+def test_chunk_bwd_argument_errors(kw, expect):
+    assert _bwd(kda.lib(), **kw) == expect
+
+
+def test_bwd_workspace_size():
+    ws = lambda *a: int(kda.lib().kda_chunk_bwd_workspace_size(*a))
+    small = ws(1, 256, 1, 32, 32, 1)
+    assert small > 0
+    # every (chunk, head) keeps its record, states and scratch: linear in T * H
+    a, b = ws(1, 65536, 4, 128, 128, 1), ws(1, 2 * 65536, 4, 128, 128, 1)
+    assert 1.9 < b / a < 2.1
+    assert ws(1, 65536, 4, 128, 256, 1) == 0
+    assert ws(0, 100, 4, 64, 64, 1) == 0
+    assert ws(1, 0, 4, 64, 64, 0) > 0

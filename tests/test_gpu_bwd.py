@@ -1,0 +1,104 @@
+"""kda_chunk_bwd (the training backward) on the GPU against the oracle's fp64 gradients
+(oracle.kda_bwd, itself pinned to central differences of the forward oracle), through the
+C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_30_amd as kda
+import oracle
+import workloads
+from gpu_util import np64, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ORDER = ("q", "k", "v", "log_alpha", "beta")
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dinit")
+# max-abs error / max|ref| per gradient: the kernels compute in fp32 from the exact inputs
+TOL = 1e-4
+
+
+def _run(inp, cu=None, N=1, with_init=True, with_dfinal=True, seed=0, dtype=torch.bfloat16):
+    T, H, K = inp["q"].shape
+    V = inp["v"].shape[-1]
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    d_o = torch.randn((T, H, V), generator=gen, device=DEV).to(dtype)
+    dfin = torch.randn((N, H, K, V), generator=gen, device=DEV) if with_dfinal else None
+    init = inp["init_state"] if with_init else None
+    grads = kda.chunk_bwd(*(inp[x] for x in ORDER), d_o, init_state=init, d_final_state=dfin,
+                          cu_seqlens=cu, num_seqs=N)
+    ref = oracle.kda_bwd(*(np64(inp[x]) for x in ORDER), np64(d_o),
+                         dfinal=None if dfin is None else np64(dfin),
+                         cu_seqlens=None if cu is None else cu.cpu().numpy().astype(np.int64),
+                         init_state=None if init is None else np64(init))
+    for name, got, want in zip(NAMES, grads, ref):
+        g = np64(got)
+        assert np.all(np.isfinite(g)), name
+        err = rel_err(g, want)
+        print("  %-10s max|ref| %.3e  rel err %.2e" % (name, np.abs(want).max() if want.size else 0, err))
+        assert err <= TOL, "%s: %.3e > %.1e" % (name, err, TOL)
+    return grads
+
+
+@pytest.mark.parametrize("T,H,K,V,dtype", [
+    (200, 2, 32, 32, torch.float32),      # a partial last chunk
+    (64, 1, 64, 64, torch.float32),       # exactly one chunk
+    (1000, 1, 128, 128, torch.bfloat16),
+    (700, 2, 64, 128, torch.bfloat16),    # K != V
+    (333, 2, 128, 32, torch.bfloat16),
+])
+def test_bwd_matches_oracle(T, H, K, V, dtype):
+    print("bwd", T, H, K, V, dtype, flush=True)
+    inp = workloads.gen_forward(T, H, K, V, dtype=dtype, device=DEV, seed=T + K, init_std=0.1)
+    _run(inp, seed=T, dtype=dtype)
+
+
+def test_bwd_varlen_with_empty_sequence():
+    print("bwd varlen", flush=True)
+    lens = [70, 0, 230, 33, 64]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    T, H, K = int(cu[-1]), 2, 64
+    inp = workloads.gen_forward(T, H, K, K, dtype=torch.bfloat16, device=DEV, seed=5,
+                                num_seqs=len(lens), init_std=0.1)
+    _run(inp, cu=cu, N=len(lens), seed=5)
+
+
+def test_bwd_without_initial_state_or_final_gradient():
+    print("bwd, zero initial state and final gradient", flush=True)
+    T, H, K = 300, 2, 64
+    inp = workloads.gen_forward(T, H, K, K, dtype=torch.bfloat16, device=DEV, seed=6)
+    _run(inp, with_init=False, with_dfinal=False, seed=6)
+
+
+def test_bwd_slow_decay_long():
+    """Slow decay over 4096 tokens: the state gradient travels back across many chunks."""
+    print("bwd slow decay", flush=True)
+    T, H, K = 4096, 1, 128
+    inp = workloads.gen_forward(T, H, K, K, gates="slow", dtype=torch.bfloat16, device=DEV, seed=7,
+                                init_std=0.1)
+    _run(inp, seed=7)
+
+
+def test_bwd_strong_decay_no_overflow():
+    """alpha down to e^-6 per token: e^{-b} would overflow in fp32 within a chunk; the pairwise
+    in-chunk factors stay at most 1."""
+    print("bwd strong decay", flush=True)
+    T, H, K = 256, 2, 64
+    inp = workloads.gen_forward(T, H, K, K, dtype=torch.float32, device=DEV, seed=8, init_std=0.1)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(80)
+    inp["log_alpha"] = -6.0 * torch.rand((T, H, K), generator=gen, device=DEV)
+    _run(inp, seed=8, dtype=torch.float32)
+
+
+def test_bwd_empty_input():
+    """No tokens: the initial state's gradient is the final state's."""
+    print("bwd empty", flush=True)
+    H, K = 2, 32
+    z = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device=DEV)
+    dfin = torch.randn((1, H, K, K), device=DEV)
+    grads = kda.chunk_bwd(z(0, H, K), z(0, H, K), z(0, H, K), z(0, H, K), z(0, H), z(0, H, K),
+                          d_final_state=dfin)
+    assert torch.equal(grads[5], dfin)
+    assert all(g.numel() == 0 for g in grads[:5])
