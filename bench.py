@@ -7,7 +7,10 @@ the decode workload (256 sequences x 32 heads, K=V=128, fp32 state 0.1*N(0,1), b
 inputs). Inputs are synthetic, seeded and resident in HBM before timing starts.
 
 Prints one JSON line. `value` is whole-step throughput (prefill tokens + decode tokens per
-second); per-call figures, roofline fractions and the oracle's CPU rate are attached.
+second); per-call figures, roofline fractions and the oracle's CPU rate are attached. After the
+timed steps, the same line reports (each can be skipped by a flag): the input options on the
+same shapes, one long sequence over two heads through the plain call and through the
+chunk-parallel scan, and the training backward on the long-prefill shape.
 """
 import argparse
 import csv
@@ -24,6 +27,7 @@ if ROOT not in sys.path:
 METRIC = "KDA chunk_fwd tokens/s (H=32,d=128) + decode_step GB/s, % of roofline"
 PEAK_HBM = 8.0e12         # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15        # FLOP/s, dense bf16 MFMA
+PEAK_FP32 = 157.3e12      # FLOP/s, fp32 (vector FMA; fp32 MFMA has the same peak)
 CHUNK = 64
 
 
@@ -37,6 +41,15 @@ def chunk_alg_flops(T, H, K, V, C=CHUNK):
     # state GEMMs W.S, Q.S, Kt^T.Delta (6KV), triangular A, P, W (C*K each) and U, P.Delta
     # (C*V each), triangular solve (C^2/3), per token-head
     return T * H * (6 * K * V + C * (3 * K + 2 * V) + C * C / 3.0)
+
+
+def bwd_alg_flops(T, H, K, V, C=CHUNK):
+    # per token-head, counting multiply-adds twice: the states' products (W.S, Kt^T.Delta in
+    # the recomputation; P^T.dO, Kt.X, Qe^T.dO, W^T.dDelta in the reverse chain; dO.S^T,
+    # dDelta.S^T, Delta.X^T per chunk: 8KV), the chunk's C x C x K products (A, P, W, T^T.dW,
+    # dW.Ke^T and the four decay-weighted pairwise sums: 5CK), its C x C x V products (U,
+    # P^T.dO, dO.Delta^T, T^T.dDelta, dDelta.V^T: 3CV) and the C x C x C ones (T, T^T.dT, .T^T)
+    return T * H * (16 * K * V + 2 * C * (5 * K + 3 * V) + 7.0 * C * C / 3.0)
 
 
 def chunk_dense_flops(T, H, K, V, C=CHUNK):
@@ -156,6 +169,8 @@ def main():
     ap.add_argument("--no-scan-bench", action="store_true",
                     help="skip the few-head long-sequence comparison of kda_chunk_fwd and "
                          "kda_chunk_fwd_scan")
+    ap.add_argument("--no-bwd-bench", action="store_true",
+                    help="skip the training backward (kda_chunk_bwd) on the long-prefill shape")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run torch.neg over this many MiB of fp32 (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -363,6 +378,42 @@ def main():
                 "o_max_rel_diff": rel(os_s, os_p), "final_state_max_rel_diff": rel(fs_s, fs_p)}
         del sinp, os_p, os_s, fs_p, fs_s, ws_p, ws_s
 
+    # ---------------- the training backward on the long-prefill shape (gradients of
+    # sum(dO * o) + sum(dS * S_final) for every input and the initial state, fp32)
+    bwd = None
+    if not args.no_bwd_bench:
+        gen2 = torch.Generator(device=dev)
+        gen2.manual_seed(wl["seed"] + 11)
+        d_o = torch.randn((T, H, V), generator=gen2, device=dev).to(torch.bfloat16)
+        d_fin = torch.randn((1, H, K, V), generator=gen2, device=dev)
+        wsb = torch.empty(int(kda.lib().kda_chunk_bwd_workspace_size(1, T, H, K, V, 1)),
+                          dtype=torch.uint8, device=dev)
+
+        def bwd_call():
+            return kda.chunk_bwd(*(inp[x] for x in names), d_o, init_state=inp["init_state"],
+                                 d_final_state=d_fin, workspace=wsb)
+
+        bsteps = max(1, min(args.steps, 5))
+        for _ in range(max(1, min(args.warmup, 2))):
+            grads = bwd_call()
+        torch.cuda.synchronize()
+        eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        eb0.record()
+        for _ in range(bsteps):
+            grads = bwd_call()
+        eb1.record()
+        torch.cuda.synchronize()
+        bms = eb0.elapsed_time(eb1) / bsteps
+        bfl = bwd_alg_flops(T, H, K, V)
+        bwd = {"workload": "B=1 H=32 T=65536 K=V=128 bf16 inputs, fp32 gradients of q, k, v, "
+                           "log alpha, beta and the initial state",
+               "ms": bms, "calls": bsteps, "tokens_per_s": T / (bms * 1e-3),
+               "alg_flops": bfl, "fp32_TFLOPs": bfl / (bms * 1e-3) / 1e12,
+               "fp32_frac": bfl / (bms * 1e-3) / PEAK_FP32,
+               "workspace_GB": wsb.numel() / 1e9,
+               "finite": bool(all(torch.isfinite(g).all().item() for g in grads))}
+        del d_o, d_fin, wsb, grads
+
     # ---------------- parity spot check and CPU baseline (oracle on the same inputs)
     cpu = None
     parity = None
@@ -405,6 +456,7 @@ def main():
         "roofline_decode": roofline_decode,
         "input_options": options,
         "few_head_scan": scan,
+        "training_backward": bwd,
         "parity_sample_max_rel_err": parity,
     }
     print(json.dumps(out), flush=True)

@@ -35,7 +35,9 @@ namespace kda {
 namespace {
 
 constexpr int BC = CHUNK;  // 64 tokens per chunk
-constexpr int NT = NTHREADS;
+constexpr int NT = NTHREADS;  // the chains and the table kernels
+constexpr int NTP = 512;      // the record kernel: 8 waves per workgroup
+constexpr int NTG = 1024;     // the gradient kernels: 16 waves per workgroup
 
 // per-(chunk, head) fp32 record of the backward, row-major blocks
 template <int K, int V>
@@ -69,12 +71,12 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
 }
 
 // out(r, c, x) for x = sum_j M(r, j) S[j][c], r < 64, c < N: M is 64 x 64 in LDS (row stride
-// LM), read as M[r][j], or as M[j][r] with TRANS; S is 64 x N in LDS (row stride LS). Thread t
-// owns column t % N and the rows (t / N) * RB .. + RB - 1, RB = N / 4, so the M reads of a
-// wave are broadcasts and the S reads consecutive words.
-template <int N, int LM, int LS, bool TRANS, typename F>
+// LM), read as M[r][j], or as M[j][r] with TRANS; S is 64 x N in LDS (row stride LS). Of the
+// NTB threads, thread t owns column t % N and the rows (t / N) * RB .. + RB - 1,
+// RB = 64 N / NTB, so the M reads of a wave are broadcasts and the S reads consecutive words.
+template <int N, int LM, int LS, bool TRANS, int NTB, typename F>
 __device__ __forceinline__ void mm64(const float* sM, const float* sS, F&& out) {
-  constexpr int NG = NT / N, RB = BC / NG;
+  constexpr int NG = NTB / N, RB = BC / NG;
   const int c = threadIdx.x % N, r0 = (threadIdx.x / N) * RB;
   float acc[RB];
 #pragma unroll
@@ -87,7 +89,8 @@ __device__ __forceinline__ void mm64(const float* sM, const float* sS, F&& out) 
       for (int u = 0; u < RB; ++u)
         acc[u] += dot4(*reinterpret_cast<const f32x4*>(sM + (r0 + u) * LM + j), x);
     }
-  } else {
+  } else if constexpr (RB % 4 == 0) {
+#pragma unroll 4
     for (int j = 0; j < BC; ++j) {
       const float x = sS[j * LS + c];
 #pragma unroll
@@ -99,54 +102,62 @@ __device__ __forceinline__ void mm64(const float* sM, const float* sS, F&& out) 
         acc[u + 3] += m[3] * x;
       }
     }
+  } else {
+#pragma unroll 4
+    for (int j = 0; j < BC; ++j) {
+      const float x = sS[j * LS + c];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) acc[u] += sM[j * LM + r0 + u] * x;
+    }
   }
 #pragma unroll
   for (int u = 0; u < RB; ++u) out(r0 + u, c, acc[u]);
 }
 
 // out(i, j, x) for x = sum_c X[i][c] Y[j][c], i, j < 64, c < N; X, Y in LDS with row stride L
-// (L = N + 4: the 16 consecutive rows a wave reads at once fall in different banks). Thread t
-// owns rows 4 (t / 16) .. + 3 and columns t % 16 + 16 b, b < 4.
-template <int N, int L, typename F>
+// (L = N + 4: the 16 consecutive rows a wave reads at once fall in different banks). Of the
+// NTB threads, thread t owns rows IA (t / 16) .. + IA - 1, IA = 1024 / NTB, and the columns
+// t % 16 + 16 b, b < 4.
+template <int N, int L, int NTB, typename F>
 __device__ __forceinline__ void rowdot64(const float* sX, const float* sY, F&& out) {
-  const int i0 = 4 * (threadIdx.x >> 4), jb = threadIdx.x & 15;
-  float acc[4][4];
+  constexpr int IA = 1024 / NTB;
+  const int i0 = IA * (threadIdx.x >> 4), jb = threadIdx.x & 15;
+  float acc[IA][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < IA; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
   for (int c = 0; c < N; c += 4) {
-    f32x4 x[4], y[4];
+    f32x4 x[IA], y[4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      x[a] = *reinterpret_cast<const f32x4*>(sX + (i0 + a) * L + c);
-      y[a] = *reinterpret_cast<const f32x4*>(sY + (jb + 16 * a) * L + c);
-    }
+    for (int a = 0; a < IA; ++a) x[a] = *reinterpret_cast<const f32x4*>(sX + (i0 + a) * L + c);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int b = 0; b < 4; ++b) y[b] = *reinterpret_cast<const f32x4*>(sY + (jb + 16 * b) * L + c);
+#pragma unroll
+    for (int a = 0; a < IA; ++a)
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[a][b] += dot4(x[a], y[b]);
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < IA; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) out(i0 + a, jb + 16 * b, acc[a][b]);
 }
 
 // rows r < len of a [T][H][N] tensor (token tok + r, head h) into LDS as fp32, zeros past len
-template <int N, int L, typename MT>
+template <int N, int L, int NTB, typename MT>
 __device__ __forceinline__ void load_rows(float* dst, const MT* src, int64_t tok, int len, int H,
                                           int h) {
-  for (int e = threadIdx.x; e < BC * N; e += NT) {
+  for (int e = threadIdx.x; e < BC * N; e += NTB) {
     const int r = e / N, c = e % N;
     dst[r * L + c] = r < len ? to_f32(src[((tok + r) * H + h) * (int64_t)N + c]) : 0.f;
   }
 }
 
 // 64 x N fp32 block of a record or scratch (row-major, stride N) into LDS
-template <int N, int L>
+template <int N, int L, int NTB>
 __device__ __forceinline__ void load_block(float* dst, const float* src) {
-  for (int e = threadIdx.x; e < BC * N; e += NT) dst[(e / N) * L + e % N] = src[e];
+  for (int e = threadIdx.x; e < BC * N; e += NTB) dst[(e / N) * L + e % N] = src[e];
 }
 
 // cumulative log2 decay: dst (64 x K, stride L) holds log alpha on entry, b * log2 e on exit
@@ -213,7 +224,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(const int32_t* __restrict
 
 // ---------------------------------------------------------------- per-chunk record
 template <int K, int V, typename MT>
-__global__ __launch_bounds__(NT) void bwd_prep_kernel(
+__global__ __launch_bounds__(NTP) void bwd_prep_kernel(
     const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ v,
     const MT* __restrict__ g, const MT* __restrict__ beta, int H,
     const BwdChunk* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ rec) {
@@ -229,16 +240,16 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
   if (c >= *ntot) return;
   const BwdChunk ch = chunks[c];
   float* rc = rec + ((size_t)c * H + h) * R::floats;
-  load_rows<K, L>(sQ, q, ch.tok, ch.len, H, h);
-  load_rows<K, LK>(sK, k, ch.tok, ch.len, H, h);
-  load_rows<K, LK>(sB, g, ch.tok, ch.len, H, h);
+  load_rows<K, L, NTP>(sQ, q, ch.tok, ch.len, H, h);
+  load_rows<K, LK, NTP>(sK, k, ch.tok, ch.len, H, h);
+  load_rows<K, LK, NTP>(sB, g, ch.tok, ch.len, H, h);
   if (threadIdx.x < BC)
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
   __syncthreads();
   cumsum_log2<K, LK>(sB);
   __syncthreads();
   // Qe, Kt, gamma (rows past len hold q = k = 0, and b stays at its last value)
-  for (int e = threadIdx.x; e < BC * K; e += NT) {
+  for (int e = threadIdx.x; e < BC * K; e += NTP) {
     const int r = e / K, cc = e % K;
     const float br = sB[r * LK + cc], bl = sB[(BC - 1) * LK + cc];
     rc[R::oQe + e] = sQ[r * L + cc] * exp2_f(br);
@@ -246,19 +257,22 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
   }
   if (threadIdx.x < K) rc[R::oGam + threadIdx.x] = exp2_f(sB[(BC - 1) * LK + threadIdx.x]);
   // A_ij = beta_i sum_c k_ic k_jc e^{b_ic - b_jc} (j < i) and P_ij = sum_c q_ic k_jc e^{..} (j <= i);
-  // thread (i, jq) forms j = jq + 4u, rows spread so that every wave has short and long rows
+  // TPR threads per row, thread (i, jq) forms j = jq + TPR u, and the rows are spread so that
+  // every wave has short and long rows
   {
-    const int i = 4 * ((threadIdx.x >> 2) & 15) + (threadIdx.x >> 6), jq = threadIdx.x & 3;
-    float a[16], p[16];
+    constexpr int TPR = NTP / BC, JPT = BC / TPR, WAVES = NTP / 64;
+    const int jq = threadIdx.x % TPR;
+    const int i = WAVES * ((threadIdx.x % 64) / TPR) + threadIdx.x / 64;
+    float a[JPT], p[JPT];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) a[u] = p[u] = 0.f;
+    for (int u = 0; u < JPT; ++u) a[u] = p[u] = 0.f;
     for (int c4 = 0; c4 < K; c4 += 4) {
       const f32x4 qi = *reinterpret_cast<const f32x4*>(sQ + i * L + c4);
       const f32x4 ki = *reinterpret_cast<const f32x4*>(sK + i * LK + c4);
       const f32x4 bi = *reinterpret_cast<const f32x4*>(sB + i * LK + c4);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int j = jq + 4 * u;
+      for (int u = 0; u < JPT; ++u) {
+        const int j = jq + TPR * u;
         if (j <= i) {
           const f32x4 kj = *reinterpret_cast<const f32x4*>(sK + j * LK + c4);
           const f32x4 bj = *reinterpret_cast<const f32x4*>(sB + j * LK + c4);
@@ -271,8 +285,8 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
       }
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int j = jq + 4 * u;
+    for (int u = 0; u < JPT; ++u) {
+      const int j = jq + TPR * u;
       sA[i * 68 + j] = j < i ? sBeta[i] * a[u] : 0.f;
       rc[R::oP + i * BC + j] = j <= i ? p[u] : 0.f;
     }
@@ -296,48 +310,89 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
     }
   }
   // beta k e^b and beta v replace k and q
-  for (int e = threadIdx.x; e < BC * K; e += NT) {
+  for (int e = threadIdx.x; e < BC * K; e += NTP) {
     const int r = e / K, cc = e % K;
     sK[r * LK + cc] *= sBeta[r] * exp2_f(sB[r * LK + cc]);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < BC * V; e += NT) {
+  for (int e = threadIdx.x; e < BC * V; e += NTP) {
     const int r = e / V, cc = e % V;
     sQ[r * L + cc] = r < ch.len ? sBeta[r] * to_f32(v[((ch.tok + r) * H + h) * (int64_t)V + cc]) : 0.f;
   }
   __syncthreads();
-  mm64<K, 68, LK, false>(sT, sK, [&](int r, int cc, float x) { rc[R::oW + r * K + cc] = x; });
-  mm64<V, 68, L, false>(sT, sQ, [&](int r, int cc, float x) { rc[R::oU + r * V + cc] = x; });
+  mm64<K, 68, LK, false, NTP>(sT, sK, [&](int r, int cc, float x) { rc[R::oW + r * K + cc] = x; });
+  mm64<V, 68, L, false, NTP>(sT, sQ, [&](int r, int cc, float x) { rc[R::oU + r * V + cc] = x; });
 }
 
 // ---------------------------------------------------------------- the chains
 // One workgroup per (sequence, head, 16 value columns); the slices of one chain share
-// blockIdx % 8 (one XCD's L2) with blockIdx = slice * chains8 + chain.
+// blockIdx % 8 (one XCD's L2) with blockIdx = slice * chains8 + chain. A chunk's record
+// blocks are loaded whole into registers (16-byte pieces, all in flight) while the chunk
+// before is computed, then stored to LDS; the chunk's products read LDS only. The loop body
+// has no branch around those loads (the next chunk's index is clamped to the last), so the
+// compiler neither sinks them to their use nor waits for them early.
+
+// the token range of sequence n
+__device__ __forceinline__ void seq_range(const int32_t* cu, int N, int64_t T, int n, int64_t* s0,
+                                          int64_t* s1) {
+  *s0 = cu ? (int64_t)cu[n] : (T / N) * n;
+  *s1 = cu ? (int64_t)cu[n + 1] : (T / N) * (n + 1);
+}
+
 template <int K, int V>
 __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
     const float* __restrict__ rec, const float* __restrict__ init, const int32_t* __restrict__ seq_first,
     int N, int H, int chains8, float* __restrict__ ckS, float* __restrict__ Dl) {
   using R = BRec<K, V>;
-  constexpr int NC = K / 16;  // columns per thread in the state update
+  constexpr int NC = K / 16;          // columns per thread in the state update
+  constexpr int LW = K + 4;           // W rows are read whole: padded against bank conflicts
+  constexpr int PB = BC * K / 4 / NT;  // 16-byte pieces per thread of a 64 x K block
   __shared__ __align__(16) float sS[K * 16];
   __shared__ __align__(16) float sD[BC * 16];
+  __shared__ __align__(16) float sW[BC * LW];
+  __shared__ __align__(16) float sKt[BC * K];
+  __shared__ float sG[K];
   const int nh = blockIdx.x % chains8, s = blockIdx.x / chains8;
   if (nh >= N * H) return;
   const int n = nh / H, h = nh % H, c0 = 16 * s;
-  for (int e = threadIdx.x; e < K * 16; e += NT)
+  const int tid = threadIdx.x;
+  for (int e = tid; e < K * 16; e += NT)
     sS[e] = init ? init[((size_t)nh * K + e / 16) * V + c0 + e % 16] : 0.f;
   const int first = seq_first[n], last = seq_first[n + 1];
-  const int i = threadIdx.x >> 2, jj = 4 * (threadIdx.x & 3);
-  const int m = threadIdx.x % K, cg = (threadIdx.x / K) * NC;
-  for (int c = first; c < last; ++c) {
+  if (first == last) return;
+  const int i = tid >> 2, jj = 4 * (tid & 3);
+  const int m = tid % K, cg = (tid / K) * NC;
+  f32x4 rw[PB], rk[PB], ru;
+  float rg;
+  auto fetch = [&](int c) {
     const float* rc = rec + ((size_t)c * H + h) * R::floats;
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      rw[u] = reinterpret_cast<const f32x4*>(rc + R::oW)[tid + NT * u];
+      rk[u] = reinterpret_cast<const f32x4*>(rc + R::oKt)[tid + NT * u];
+    }
+    ru = *reinterpret_cast<const f32x4*>(rc + R::oU + i * V + c0 + jj);
+    rg = rc[R::oGam + m];
+  };
+  fetch(first);
+  for (int c = first; c < last; ++c) {
+    __syncthreads();  // the previous chunk's reads of LDS are done
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int e = tid + NT * u;
+      *reinterpret_cast<f32x4*>(sW + (e / (K / 4)) * LW + 4 * (e % (K / 4))) = rw[u];
+      reinterpret_cast<f32x4*>(sKt)[e] = rk[u];
+    }
+    sG[m] = rg;
+    f32x4 d = ru;
+    fetch(min(c + 1, last - 1));
     __syncthreads();
-    for (int e = threadIdx.x; e < K * 16; e += NT)
+    for (int e = tid; e < K * 16; e += NT)
       ckS[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sS[e];
     // Delta = U - W S for row i, columns jj .. jj + 3
-    f32x4 d = *reinterpret_cast<const f32x4*>(rc + R::oU + i * V + c0 + jj);
+#pragma unroll 4
     for (int mm = 0; mm < K; mm += 4) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(rc + R::oW + i * K + mm);
+      const f32x4 w = *reinterpret_cast<const f32x4*>(sW + i * LW + mm);
 #pragma unroll
       for (int e = 0; e < 4; ++e) d -= w[e] * *reinterpret_cast<const f32x4*>(sS + (mm + e) * 16 + jj);
     }
@@ -345,12 +400,12 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
     *reinterpret_cast<f32x4*>(sD + i * 16 + jj) = d;
     __syncthreads();
     // S' = diag(gamma) S + Kt^T Delta for row m, columns cg .. cg + NC - 1
-    const float gm = rc[R::oGam + m];
     float acc[NC];
 #pragma unroll
-    for (int e = 0; e < NC; ++e) acc[e] = gm * sS[m * 16 + cg + e];
+    for (int e = 0; e < NC; ++e) acc[e] = sG[m] * sS[m * 16 + cg + e];
+#pragma unroll 8
     for (int r = 0; r < BC; ++r) {
-      const float kt = rc[R::oKt + r * K + m];
+      const float kt = sKt[r * K + m];
 #pragma unroll
       for (int e = 0; e < NC; ++e) acc[e] += kt * sD[r * 16 + cg + e];
     }
@@ -363,38 +418,88 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
 template <int K, int V, typename MT>
 __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
     const float* __restrict__ rec, const MT* __restrict__ dO, const float* __restrict__ dfin,
-    const BwdChunk* __restrict__ chunks, const int32_t* __restrict__ seq_first, int N, int H,
+    const int32_t* __restrict__ cu, int64_t T, const int32_t* __restrict__ seq_first, int N, int H,
     int chains8, float* __restrict__ ckX, float* __restrict__ dDl, float* __restrict__ dinit) {
   using R = BRec<K, V>;
   constexpr int NC = K / 16;
+  constexpr int LKt = K + 4;           // Kt rows are read whole
+  constexpr int PB = BC * K / 4 / NT;  // 16-byte pieces per thread of a 64 x K block
+  constexpr int PP = BC * BC / 4 / NT;  // ... of the 64 x 64 P
+  constexpr int PO = BC * 16 / NT;      // dO values per thread (the chunk's 16 columns)
   __shared__ __align__(16) float sX[K * 16];
   __shared__ __align__(16) float sO[BC * 16];
   __shared__ __align__(16) float sDD[BC * 16];
+  __shared__ __align__(16) float sP[BC * BC];
+  __shared__ __align__(16) float sKt[BC * LKt];
+  __shared__ __align__(16) float sQe[BC * K];
+  __shared__ __align__(16) float sW[BC * K];
+  __shared__ float sG[K];
   const int nh = blockIdx.x % chains8, s = blockIdx.x / chains8;
   if (nh >= N * H) return;
   const int n = nh / H, h = nh % H, c0 = 16 * s;
-  for (int e = threadIdx.x; e < K * 16; e += NT)
+  const int tid = threadIdx.x;
+  for (int e = tid; e < K * 16; e += NT)
     sX[e] = dfin ? dfin[((size_t)nh * K + e / 16) * V + c0 + e % 16] : 0.f;
   const int first = seq_first[n], last = seq_first[n + 1];
-  const int i = threadIdx.x >> 2, jj = 4 * (threadIdx.x & 3);
-  const int m = threadIdx.x % K, cg = (threadIdx.x / K) * NC;
-  for (int c = last - 1; c >= first; --c) {
+  int64_t s0, s1;
+  seq_range(cu, N, T, n, &s0, &s1);
+  const int i = tid >> 2, jj = 4 * (tid & 3);
+  const int m = tid % K, cg = (tid / K) * NC;
+  f32x4 rp[PP], rk[PB], rq[PB], rw[PB];
+  MT ro[PO];
+  float rg;
+  // chunk c's rows are tokens s0 + 64 (c - first) + r; rows past the sequence read its last
+  // token (in bounds) and are zeroed when stored
+  auto fetch = [&](int c) {
     const float* rc = rec + ((size_t)c * H + h) * R::floats;
-    const BwdChunk ch = chunks[c];
-    __syncthreads();
-    for (int e = threadIdx.x; e < K * 16; e += NT)
-      ckX[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sX[e];
-    for (int e = threadIdx.x; e < BC * 16; e += NT) {
-      const int r = e / 16;
-      sO[e] = r < ch.len ? to_f32(dO[((ch.tok + r) * (int64_t)H + h) * V + c0 + e % 16]) : 0.f;
+#pragma unroll
+    for (int u = 0; u < PP; ++u) rp[u] = reinterpret_cast<const f32x4*>(rc + R::oP)[tid + NT * u];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      rk[u] = reinterpret_cast<const f32x4*>(rc + R::oKt)[tid + NT * u];
+      rq[u] = reinterpret_cast<const f32x4*>(rc + R::oQe)[tid + NT * u];
+      rw[u] = reinterpret_cast<const f32x4*>(rc + R::oW)[tid + NT * u];
     }
+    rg = rc[R::oGam + m];
+    const int64_t tok = s0 + (int64_t)(c - first) * BC;
+#pragma unroll
+    for (int u = 0; u < PO; ++u) {
+      const int e = tid + NT * u;
+      const int64_t t = min(tok + e / 16, s1 - 1);
+      ro[u] = dO[(t * H + h) * (int64_t)V + c0 + e % 16];
+    }
+  };
+  if (first < last) fetch(last - 1);
+  for (int c = last - 1; c >= first; --c) {
+    const int len = (int)min((int64_t)BC, s1 - (s0 + (int64_t)(c - first) * BC));
+    __syncthreads();  // the previous chunk's reads of LDS are done
+#pragma unroll
+    for (int u = 0; u < PP; ++u) reinterpret_cast<f32x4*>(sP)[tid + NT * u] = rp[u];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int e = tid + NT * u;
+      *reinterpret_cast<f32x4*>(sKt + (e / (K / 4)) * LKt + 4 * (e % (K / 4))) = rk[u];
+      reinterpret_cast<f32x4*>(sQe)[e] = rq[u];
+      reinterpret_cast<f32x4*>(sW)[e] = rw[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PO; ++u) {
+      const int e = tid + NT * u;
+      sO[e] = e / 16 < len ? to_f32(ro[u]) : 0.f;
+    }
+    sG[m] = rg;
+    fetch(max(c - 1, first));
     __syncthreads();
-    // dDelta = P^T dO + Kt X for row i, columns jj .. jj + 3
+    for (int e = tid; e < K * 16; e += NT)
+      ckX[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sX[e];
+    // dDelta = P^T dO + Kt X for row i, columns jj .. jj + 3 (P_ri = 0 for r < i: a uniform
+    // trip count)
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
-    for (int r = i; r < BC; ++r)
-      d += rc[R::oP + r * BC + i] * *reinterpret_cast<const f32x4*>(sO + r * 16 + jj);
+#pragma unroll 8
+    for (int r = 0; r < BC; ++r) d += sP[r * BC + i] * *reinterpret_cast<const f32x4*>(sO + r * 16 + jj);
+#pragma unroll 4
     for (int mm = 0; mm < K; mm += 4) {
-      const f32x4 kt = *reinterpret_cast<const f32x4*>(rc + R::oKt + i * K + mm);
+      const f32x4 kt = *reinterpret_cast<const f32x4*>(sKt + i * LKt + mm);
 #pragma unroll
       for (int e = 0; e < 4; ++e) d += kt[e] * *reinterpret_cast<const f32x4*>(sX + (mm + e) * 16 + jj);
     }
@@ -402,12 +507,12 @@ __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
     *reinterpret_cast<f32x4*>(sDD + i * 16 + jj) = d;
     __syncthreads();
     // X_prev = diag(gamma) X + Qe^T dO - W^T dDelta for row m, columns cg .. cg + NC - 1
-    const float gm = rc[R::oGam + m];
     float acc[NC];
 #pragma unroll
-    for (int e = 0; e < NC; ++e) acc[e] = gm * sX[m * 16 + cg + e];
+    for (int e = 0; e < NC; ++e) acc[e] = sG[m] * sX[m * 16 + cg + e];
+#pragma unroll 8
     for (int r = 0; r < BC; ++r) {
-      const float qe = rc[R::oQe + r * K + m], w = rc[R::oW + r * K + m];
+      const float qe = sQe[r * K + m], w = sW[r * K + m];
 #pragma unroll
       for (int e = 0; e < NC; ++e) acc[e] += qe * sO[r * 16 + cg + e] - w * sDD[r * 16 + cg + e];
     }
@@ -417,7 +522,7 @@ __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
   }
   if (dinit) {
     __syncthreads();
-    for (int e = threadIdx.x; e < K * 16; e += NT)
+    for (int e = tid; e < K * 16; e += NT)
       dinit[((size_t)nh * K + e / 16) * V + c0 + e % 16] = sX[e];
   }
 }
@@ -426,7 +531,7 @@ __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
 // (a) dP = lower(dO Delta^T); with S (chunk start) and X (chunk end) streamed from HBM:
 //     dO S^T, dW = -dDelta S^T, Delta X^T and rowsum(S * X)
 template <int K, int V, typename MT>
-__global__ __launch_bounds__(NT) void bwd_ga_kernel(
+__global__ __launch_bounds__(NTG) void bwd_ga_kernel(
     const MT* __restrict__ dO, const float* __restrict__ ckS, const float* __restrict__ ckX,
     const float* __restrict__ Dl, const float* __restrict__ dDl, int H,
     const BwdChunk* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr) {
@@ -440,13 +545,13 @@ __global__ __launch_bounds__(NT) void bwd_ga_kernel(
   const BwdChunk ch = chunks[c];
   const size_t ch_h = (size_t)c * H + h;
   float* sc = scr + ch_h * G::floats;
-  load_rows<V, L>(sO, dO, ch.tok, ch.len, H, h);
-  load_block<V, L>(sDl, Dl + ch_h * BC * V);
-  load_block<V, L>(sDD, dDl + ch_h * BC * V);
+  load_rows<V, L, NTG>(sO, dO, ch.tok, ch.len, H, h);
+  load_block<V, L, NTG>(sDl, Dl + ch_h * BC * V);
+  load_block<V, L, NTG>(sDD, dDl + ch_h * BC * V);
   __syncthreads();
-  rowdot64<V, L>(sO, sDl, [&](int i, int j, float x) { sc[G::oDP + i * BC + j] = j <= i ? x : 0.f; });
+  rowdot64<V, L, NTG>(sO, sDl, [&](int i, int j, float x) { sc[G::oDP + i * BC + j] = j <= i ? x : 0.f; });
   // thread: key channel m, rows r0 .. r0 + RB - 1
-  constexpr int NG = NT / K, RB = BC / NG;
+  constexpr int NG = NTG / K, RB = BC / NG;
   const int m = threadIdx.x % K, r0 = (threadIdx.x / K) * RB;
   const float* Sm = ckS + (ch_h * K + m) * V;
   const float* Xm = ckX + (ch_h * K + m) * V;
@@ -478,7 +583,7 @@ __global__ __launch_bounds__(NT) void bwd_ga_kernel(
 //     dA = strict_lower(-T^T dT T^T), and dbeta's terms rowsum(V * T^T dDelta) and
 //     rowsum(Ke * T^T dW)
 template <int K, int V, typename MT>
-__global__ __launch_bounds__(NT) void bwd_gb_kernel(
+__global__ __launch_bounds__(NTG) void bwd_gb_kernel(
     const MT* __restrict__ k, const MT* __restrict__ v, const MT* __restrict__ g,
     const MT* __restrict__ beta, const float* __restrict__ rec, const float* __restrict__ dDl, int H,
     const BwdChunk* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr,
@@ -498,55 +603,55 @@ __global__ __launch_bounds__(NT) void bwd_gb_kernel(
   const size_t ch_h = (size_t)c * H + h;
   const float* rc = rec + ch_h * R::floats;
   float* sc = scr + ch_h * G::floats;
-  for (int e = threadIdx.x; e < BC * BC; e += NT) sT[(e / BC) * 68 + e % BC] = rc[R::oT + e];
-  load_block<V, LV>(bufA, dDl + ch_h * BC * V);
+  for (int e = threadIdx.x; e < BC * BC; e += NTG) sT[(e / BC) * 68 + e % BC] = rc[R::oT + e];
+  load_block<V, LV, NTG>(bufA, dDl + ch_h * BC * V);
   if (threadIdx.x < BC) {
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
     sDb[threadIdx.x] = 0.f;
   }
   __syncthreads();
-  load_rows<V, LV>(bufB, v, ch.tok, ch.len, H, h);
+  load_rows<V, LV, NTG>(bufB, v, ch.tok, ch.len, H, h);
   __syncthreads();
   // T^T dDelta: dv = beta T^T dDelta, dbeta += rowsum(v * T^T dDelta)
-  mm64<V, 68, LV, true>(sT, bufA, [&](int r, int cc, float x) {
+  mm64<V, 68, LV, true, NTG>(sT, bufA, [&](int r, int cc, float x) {
     if (r < ch.len) grad_v[((ch.tok + r) * (int64_t)H + h) * V + cc] = sBeta[r] * x;
     atomicAdd(&sDb[r], bufB[r * LV + cc] * x);
   });
   __syncthreads();
-  for (int e = threadIdx.x; e < BC * V; e += NT) bufB[(e / V) * LV + e % V] *= sBeta[e / V];
+  for (int e = threadIdx.x; e < BC * V; e += NTG) bufB[(e / V) * LV + e % V] *= sBeta[e / V];
   __syncthreads();
-  rowdot64<V, LV>(bufA, bufB, [&](int i, int j, float x) { sdT[i * 68 + j] = x; });
+  rowdot64<V, LV, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * 68 + j] = x; });
   __syncthreads();
   // dW and Ke = k e^b
-  load_block<K, LK>(bufA, sc + G::oDW);
-  load_rows<K, LK>(bufB, g, ch.tok, ch.len, H, h);
+  load_block<K, LK, NTG>(bufA, sc + G::oDW);
+  load_rows<K, LK, NTG>(bufB, g, ch.tok, ch.len, H, h);
   __syncthreads();
   cumsum_log2<K, LK>(bufB);
   __syncthreads();
-  for (int e = threadIdx.x; e < BC * K; e += NT) {
+  for (int e = threadIdx.x; e < BC * K; e += NTG) {
     const int r = e / K, cc = e % K;
     bufB[r * LK + cc] = r < ch.len ? to_f32(k[((ch.tok + r) * (int64_t)H + h) * K + cc]) *
                                          exp2_f(bufB[r * LK + cc]) : 0.f;
   }
   __syncthreads();
   // T^T dW; dbeta += rowsum(Ke * T^T dW)
-  mm64<K, 68, LK, true>(sT, bufA, [&](int r, int cc, float x) {
+  mm64<K, 68, LK, true, NTG>(sT, bufA, [&](int r, int cc, float x) {
     sc[G::oTDW + r * K + cc] = x;
     atomicAdd(&sDb[r], bufB[r * LK + cc] * x);
   });
   // dT += dW (beta Ke)^T (each thread adds to the entries it owns)
-  rowdot64<K, LK>(bufA, bufB, [&](int i, int j, float x) { sdT[i * 68 + j] += sBeta[j] * x; });
+  rowdot64<K, LK, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * 68 + j] += sBeta[j] * x; });
   __syncthreads();
   // M1 = T^T dT into bufA, then dA = strict_lower(-M1 T^T)
-  mm64<BC, 68, 68, true>(sT, sdT, [&](int r, int cc, float x) { bufA[r * 68 + cc] = x; });
+  mm64<BC, 68, 68, true, NTG>(sT, sdT, [&](int r, int cc, float x) { bufA[r * 68 + cc] = x; });
   __syncthreads();
-  rowdot64<BC, 68>(bufA, sT, [&](int i, int j, float x) { sc[G::oDA + i * BC + j] = j < i ? -x : 0.f; });
+  rowdot64<BC, 68, NTG>(bufA, sT, [&](int i, int j, float x) { sc[G::oDA + i * BC + j] = j < i ? -x : 0.f; });
   if (threadIdx.x < BC) sc[G::oDB + threadIdx.x] = sDb[threadIdx.x];
 }
 
 // (c) the decay-weighted pairwise sums and the per-token gradients of q, k, log alpha, beta
 template <int K, int V, typename MT>
-__global__ __launch_bounds__(NT) void bwd_gc_kernel(
+__global__ __launch_bounds__(NTG) void bwd_gc_kernel(
     const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ g,
     const MT* __restrict__ beta, int H, const BwdChunk* __restrict__ chunks,
     const int32_t* __restrict__ ntot, const float* __restrict__ scr, float* __restrict__ grad_q,
@@ -564,10 +669,10 @@ __global__ __launch_bounds__(NT) void bwd_gc_kernel(
   const BwdChunk ch = chunks[c];
   const size_t ch_h = (size_t)c * H + h;
   const float* sc = scr + ch_h * G::floats;
-  load_rows<K, LK>(sQ, q, ch.tok, ch.len, H, h);
-  load_rows<K, LK>(sK, k, ch.tok, ch.len, H, h);
-  load_rows<K, LK>(sB, g, ch.tok, ch.len, H, h);
-  for (int e = threadIdx.x; e < BC * BC; e += NT) {
+  load_rows<K, LK, NTG>(sQ, q, ch.tok, ch.len, H, h);
+  load_rows<K, LK, NTG>(sK, k, ch.tok, ch.len, H, h);
+  load_rows<K, LK, NTG>(sB, g, ch.tok, ch.len, H, h);
+  for (int e = threadIdx.x; e < BC * BC; e += NTG) {
     sdP[(e / BC) * 68 + e % BC] = sc[G::oDP + e];
     sdA[(e / BC) * 68 + e % BC] = sc[G::oDA + e];
   }
@@ -580,7 +685,7 @@ __global__ __launch_bounds__(NT) void bwd_gc_kernel(
   cumsum_log2<K, LK>(sB);
   __syncthreads();
   // thread: key channel m, rows i = i0 + NG u (interleaved: the pairwise sums grow with i)
-  constexpr int NG = NT / K, RB = BC / NG;
+  constexpr int NG = NTG / K, RB = BC / NG;
   const int m = threadIdx.x % K, i0 = threadIdx.x / K;
   const float bl = sB[(BC - 1) * LK + m];
   float db[RB];
@@ -700,23 +805,23 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
                        a.cu_seqlens, N, a.total_tokens, (const int32_t*)seq_first, p.ub, chunks);
   const dim3 cgrid((unsigned)(p.ub > 0 ? p.ub : 1), (unsigned)H);
   if (p.ub > 0)
-    hipLaunchKernelGGL((bwd_prep_kernel<K, V, MT>), cgrid, dim3(NT), 0, st, q, k, v, g, beta, H,
+    hipLaunchKernelGGL((bwd_prep_kernel<K, V, MT>), cgrid, dim3(NTP), 0, st, q, k, v, g, beta, H,
                        (const BwdChunk*)chunks, ntot, rec);
   const int chains8 = (N * H + 7) / 8 * 8;
   const dim3 sgrid((unsigned)(chains8 * (V / 16)));
   hipLaunchKernelGGL((bwd_fstate_kernel<K, V>), sgrid, dim3(NT), 0, st, (const float*)rec,
                      a.init_state, (const int32_t*)seq_first, N, H, chains8, ckS, Dl);
   hipLaunchKernelGGL((bwd_rstate_kernel<K, V, MT>), sgrid, dim3(NT), 0, st, (const float*)rec, dO,
-                     a.dfinal, (const BwdChunk*)chunks, (const int32_t*)seq_first, N, H, chains8,
-                     ckX, dDl, a.grad_init);
+                     a.dfinal, a.cu_seqlens, a.total_tokens, (const int32_t*)seq_first, N, H,
+                     chains8, ckX, dDl, a.grad_init);
   if (p.ub > 0) {
-    hipLaunchKernelGGL((bwd_ga_kernel<K, V, MT>), cgrid, dim3(NT), 0, st, dO, (const float*)ckS,
+    hipLaunchKernelGGL((bwd_ga_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, dO, (const float*)ckS,
                        (const float*)ckX, (const float*)Dl, (const float*)dDl, H,
                        (const BwdChunk*)chunks, ntot, scr);
-    hipLaunchKernelGGL((bwd_gb_kernel<K, V, MT>), cgrid, dim3(NT), 0, st, k, v, g, beta,
+    hipLaunchKernelGGL((bwd_gb_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, k, v, g, beta,
                        (const float*)rec, (const float*)dDl, H, (const BwdChunk*)chunks, ntot, scr,
                        a.grad_v);
-    hipLaunchKernelGGL((bwd_gc_kernel<K, V, MT>), cgrid, dim3(NT), 0, st, q, k, g, beta, H,
+    hipLaunchKernelGGL((bwd_gc_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, q, k, g, beta, H,
                        (const BwdChunk*)chunks, ntot, (const float*)scr, a.grad_q, a.grad_k,
                        a.grad_g, a.grad_beta);
   }
