@@ -70,6 +70,36 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
   return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
 
+// fp32 16 x 16 x 4 matrix-core step: lane l = 16 g + m supplies A[m][g] and B[g][m]; the
+// 16 x 16 result has lane (m, g) holding rows 4 g + r (r = 0..3) of column m.
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// out(r, c, x) for x = sum_{k < R} A(r, k) B(k, c), r < 64, c < N, operands in LDS:
+// A(r, k) = A[r][k] (row stride LA) or, with TA, A[k][r]; B(k, c) = B[k][c] (row stride LB)
+// or, with TB, B[c][k]. The 4 N / 16 output tiles of 16 x 16 go round robin to the NTB / 64
+// waves, each formed by R / 4 fp32 matrix-core steps. A wave's 64 operand reads fall in 64
+// banks when an operand read along its rows (A, or B with TB) has a stride of 4 more than a
+// multiple of 64 floats, and one read down its columns a stride of 16 more.
+template <int N, int R, bool TA, bool TB, int LA, int LB, int NTB, typename F>
+__device__ __forceinline__ void mmf(const float* sA, const float* sB, F&& out) {
+  constexpr int TILES = 4 * (N / 16), WAVES = NTB / 64;
+  const int wv = threadIdx.x >> 6, lm = threadIdx.x & 15, lg = (threadIdx.x >> 4) & 3;
+  for (int t = wv; t < TILES; t += WAVES) {
+    const int r0 = 16 * (t & 3), c0 = 16 * (t >> 2);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int k = 0; k < R; k += 4) {
+      const float a = TA ? sA[(k + lg) * LA + r0 + lm] : sA[(r0 + lm) * LA + k + lg];
+      const float b = TB ? sB[(c0 + lm) * LB + k + lg] : sB[(k + lg) * LB + c0 + lm];
+      acc = mfma4(a, b, acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out(r0 + 4 * lg + r, c0 + lm, acc[r]);
+  }
+}
+
 // out(r, c, x) for x = sum_j M(r, j) S[j][c], r < 64, c < N: M is 64 x 64 in LDS (row stride
 // LM), read as M[r][j], or as M[j][r] with TRANS; S is 64 x N in LDS (row stride LS). Of the
 // NTB threads, thread t owns column t % N and the rows (t / N) * RB .. + RB - 1,
@@ -320,8 +350,8 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
     sQ[r * L + cc] = r < ch.len ? sBeta[r] * to_f32(v[((ch.tok + r) * H + h) * (int64_t)V + cc]) : 0.f;
   }
   __syncthreads();
-  mm64<K, 68, LK, false, NTP>(sT, sK, [&](int r, int cc, float x) { rc[R::oW + r * K + cc] = x; });
-  mm64<V, 68, L, false, NTP>(sT, sQ, [&](int r, int cc, float x) { rc[R::oU + r * V + cc] = x; });
+  mmf<K, BC, false, false, 68, LK, NTP>(sT, sK, [&](int r, int cc, float x) { rc[R::oW + r * K + cc] = x; });
+  mmf<V, BC, false, false, 68, L, NTP>(sT, sQ, [&](int r, int cc, float x) { rc[R::oU + r * V + cc] = x; });
 }
 
 // ---------------------------------------------------------------- the chains
@@ -339,31 +369,35 @@ __device__ __forceinline__ void seq_range(const int32_t* cu, int N, int64_t T, i
   *s1 = cu ? (int64_t)cu[n + 1] : (T / N) * (n + 1);
 }
 
+// Forward in time: S_c (chunk start) and Delta = U - W S per chunk, S' = diag(gamma) S + Kt^T
+// Delta. Wave w forms rows 16 w .. 16 w + 15 of Delta and the 16-row tiles w, w + 4, .. of S'
+// with matrix-core steps over LDS operands.
 template <int K, int V>
 __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
     const float* __restrict__ rec, const float* __restrict__ init, const int32_t* __restrict__ seq_first,
     int N, int H, int chains8, float* __restrict__ ckS, float* __restrict__ Dl) {
   using R = BRec<K, V>;
-  constexpr int NC = K / 16;          // columns per thread in the state update
-  constexpr int LW = K + 4;           // W rows are read whole: padded against bank conflicts
+  // LDS row strides: a block read as the A operand along its rows (lane m takes row m, the
+  // four lane groups consecutive columns) is padded by 4 floats, one read along its columns
+  // (lane group g takes row g) by 16, so a wave's 64 reads fall in 64 different banks
+  constexpr int LW = K + 4, LKT = K + 16;
   constexpr int PB = BC * K / 4 / NT;  // 16-byte pieces per thread of a 64 x K block
+  constexpr int TPW = (K / 16 + 3) / 4;  // S' tiles per wave
   __shared__ __align__(16) float sS[K * 16];
   __shared__ __align__(16) float sD[BC * 16];
   __shared__ __align__(16) float sW[BC * LW];
-  __shared__ __align__(16) float sKt[BC * K];
+  __shared__ __align__(16) float sKt[BC * LKT];
   __shared__ float sG[K];
   const int nh = blockIdx.x % chains8, s = blockIdx.x / chains8;
   if (nh >= N * H) return;
   const int n = nh / H, h = nh % H, c0 = 16 * s;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, lm = tid & 15, lg = (tid >> 4) & 3;
   for (int e = tid; e < K * 16; e += NT)
     sS[e] = init ? init[((size_t)nh * K + e / 16) * V + c0 + e % 16] : 0.f;
   const int first = seq_first[n], last = seq_first[n + 1];
   if (first == last) return;
-  const int i = tid >> 2, jj = 4 * (tid & 3);
-  const int m = tid % K, cg = (tid / K) * NC;
-  f32x4 rw[PB], rk[PB], ru;
-  float rg;
+  f32x4 rw[PB], rk[PB];
+  float ru[4], rg;
   auto fetch = [&](int c) {
     const float* rc = rec + ((size_t)c * H + h) * R::floats;
 #pragma unroll
@@ -371,8 +405,9 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
       rw[u] = reinterpret_cast<const f32x4*>(rc + R::oW)[tid + NT * u];
       rk[u] = reinterpret_cast<const f32x4*>(rc + R::oKt)[tid + NT * u];
     }
-    ru = *reinterpret_cast<const f32x4*>(rc + R::oU + i * V + c0 + jj);
-    rg = rc[R::oGam + m];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ru[r] = rc[R::oU + (16 * w + 4 * lg + r) * V + c0 + lm];
+    rg = rc[R::oGam + tid % K];
   };
   fetch(first);
   for (int c = first; c < last; ++c) {
@@ -381,70 +416,84 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
     for (int u = 0; u < PB; ++u) {
       const int e = tid + NT * u;
       *reinterpret_cast<f32x4*>(sW + (e / (K / 4)) * LW + 4 * (e % (K / 4))) = rw[u];
-      reinterpret_cast<f32x4*>(sKt)[e] = rk[u];
+      *reinterpret_cast<f32x4*>(sKt + (e / (K / 4)) * LKT + 4 * (e % (K / 4))) = rk[u];
     }
-    sG[m] = rg;
-    f32x4 d = ru;
+    sG[tid % K] = rg;
+    f32x4 d = {ru[0], ru[1], ru[2], ru[3]};
     fetch(min(c + 1, last - 1));
     __syncthreads();
     for (int e = tid; e < K * 16; e += NT)
       ckS[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sS[e];
-    // Delta = U - W S for row i, columns jj .. jj + 3
-#pragma unroll 4
-    for (int mm = 0; mm < K; mm += 4) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(sW + i * LW + mm);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) d -= w[e] * *reinterpret_cast<const f32x4*>(sS + (mm + e) * 16 + jj);
-    }
-    *reinterpret_cast<f32x4*>(Dl + (((size_t)c * H + h) * BC + i) * V + c0 + jj) = d;
-    *reinterpret_cast<f32x4*>(sD + i * 16 + jj) = d;
-    __syncthreads();
-    // S' = diag(gamma) S + Kt^T Delta for row m, columns cg .. cg + NC - 1
-    float acc[NC];
-#pragma unroll
-    for (int e = 0; e < NC; ++e) acc[e] = sG[m] * sS[m * 16 + cg + e];
+    // Delta rows 16 w .. : U - W S
 #pragma unroll 8
-    for (int r = 0; r < BC; ++r) {
-      const float kt = sKt[r * K + m];
+    for (int mm = 0; mm < K; mm += 4)
+      d = mfma4(-sW[(16 * w + lm) * LW + mm + lg], sS[(mm + lg) * 16 + lm], d);
 #pragma unroll
-      for (int e = 0; e < NC; ++e) acc[e] += kt * sD[r * 16 + cg + e];
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * w + 4 * lg + r;
+      sD[row * 16 + lm] = d[r];
+      Dl[(((size_t)c * H + h) * BC + row) * V + c0 + lm] = d[r];
+    }
+    __syncthreads();
+    // S' tiles: diag(gamma) S + Kt^T Delta
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      const int mt = w + 4 * q;
+      if (mt < K / 16) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * mt + 4 * lg + r;
+          acc[q][r] = sG[row] * sS[row * 16 + lm];
+        }
+#pragma unroll 8
+        for (int r0 = 0; r0 < BC; r0 += 4)
+          acc[q] = mfma4(sKt[(r0 + lg) * LKT + 16 * mt + lm], sD[(r0 + lg) * 16 + lm], acc[q]);
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < NC; ++e) sS[m * 16 + cg + e] = acc[e];
+    for (int q = 0; q < TPW; ++q) {
+      const int mt = w + 4 * q;
+      if (mt < K / 16)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sS[(16 * mt + 4 * lg + r) * 16 + lm] = acc[q][r];
+    }
   }
 }
 
+// Backwards in time: X_c (the gradient at the chunk's end), dDelta = P^T dO + Kt X per chunk,
+// X_prev = diag(gamma) X + Qe^T dO - W^T dDelta; at the end the initial state's gradient.
 template <int K, int V, typename MT>
 __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
     const float* __restrict__ rec, const MT* __restrict__ dO, const float* __restrict__ dfin,
     const int32_t* __restrict__ cu, int64_t T, const int32_t* __restrict__ seq_first, int N, int H,
     int chains8, float* __restrict__ ckX, float* __restrict__ dDl, float* __restrict__ dinit) {
   using R = BRec<K, V>;
-  constexpr int NC = K / 16;
-  constexpr int LKt = K + 4;           // Kt rows are read whole
-  constexpr int PB = BC * K / 4 / NT;  // 16-byte pieces per thread of a 64 x K block
+  // LDS row strides as in the forward chain: Kt is read along its rows (+4), P, Qe and W
+  // along their columns (+16)
+  constexpr int LKt = K + 4, LC = K + 16, LP = BC + 16;
+  constexpr int PB = BC * K / 4 / NT;   // 16-byte pieces per thread of a 64 x K block
   constexpr int PP = BC * BC / 4 / NT;  // ... of the 64 x 64 P
   constexpr int PO = BC * 16 / NT;      // dO values per thread (the chunk's 16 columns)
+  constexpr int TPW = (K / 16 + 3) / 4;
   __shared__ __align__(16) float sX[K * 16];
   __shared__ __align__(16) float sO[BC * 16];
   __shared__ __align__(16) float sDD[BC * 16];
-  __shared__ __align__(16) float sP[BC * BC];
+  __shared__ __align__(16) float sP[BC * LP];
   __shared__ __align__(16) float sKt[BC * LKt];
-  __shared__ __align__(16) float sQe[BC * K];
-  __shared__ __align__(16) float sW[BC * K];
+  __shared__ __align__(16) float sQe[BC * LC];
+  __shared__ __align__(16) float sW[BC * LC];
   __shared__ float sG[K];
   const int nh = blockIdx.x % chains8, s = blockIdx.x / chains8;
   if (nh >= N * H) return;
   const int n = nh / H, h = nh % H, c0 = 16 * s;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, lm = tid & 15, lg = (tid >> 4) & 3;
   for (int e = tid; e < K * 16; e += NT)
     sX[e] = dfin ? dfin[((size_t)nh * K + e / 16) * V + c0 + e % 16] : 0.f;
   const int first = seq_first[n], last = seq_first[n + 1];
   int64_t s0, s1;
   seq_range(cu, N, T, n, &s0, &s1);
-  const int i = tid >> 2, jj = 4 * (tid & 3);
-  const int m = tid % K, cg = (tid / K) * NC;
   f32x4 rp[PP], rk[PB], rq[PB], rw[PB];
   MT ro[PO];
   float rg;
@@ -460,7 +509,7 @@ __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
       rq[u] = reinterpret_cast<const f32x4*>(rc + R::oQe)[tid + NT * u];
       rw[u] = reinterpret_cast<const f32x4*>(rc + R::oW)[tid + NT * u];
     }
-    rg = rc[R::oGam + m];
+    rg = rc[R::oGam + tid % K];
     const int64_t tok = s0 + (int64_t)(c - first) * BC;
 #pragma unroll
     for (int u = 0; u < PO; ++u) {
@@ -474,51 +523,67 @@ __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
     const int len = (int)min((int64_t)BC, s1 - (s0 + (int64_t)(c - first) * BC));
     __syncthreads();  // the previous chunk's reads of LDS are done
 #pragma unroll
-    for (int u = 0; u < PP; ++u) reinterpret_cast<f32x4*>(sP)[tid + NT * u] = rp[u];
+    for (int u = 0; u < PP; ++u) {
+      const int e = tid + NT * u;
+      *reinterpret_cast<f32x4*>(sP + (e / (BC / 4)) * LP + 4 * (e % (BC / 4))) = rp[u];
+    }
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
-      const int e = tid + NT * u;
-      *reinterpret_cast<f32x4*>(sKt + (e / (K / 4)) * LKt + 4 * (e % (K / 4))) = rk[u];
-      reinterpret_cast<f32x4*>(sQe)[e] = rq[u];
-      reinterpret_cast<f32x4*>(sW)[e] = rw[u];
+      const int e = tid + NT * u, o = (e / (K / 4)), q4 = 4 * (e % (K / 4));
+      *reinterpret_cast<f32x4*>(sKt + o * LKt + q4) = rk[u];
+      *reinterpret_cast<f32x4*>(sQe + o * LC + q4) = rq[u];
+      *reinterpret_cast<f32x4*>(sW + o * LC + q4) = rw[u];
     }
 #pragma unroll
     for (int u = 0; u < PO; ++u) {
       const int e = tid + NT * u;
       sO[e] = e / 16 < len ? to_f32(ro[u]) : 0.f;
     }
-    sG[m] = rg;
+    sG[tid % K] = rg;
     fetch(max(c - 1, first));
     __syncthreads();
     for (int e = tid; e < K * 16; e += NT)
       ckX[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sX[e];
-    // dDelta = P^T dO + Kt X for row i, columns jj .. jj + 3 (P_ri = 0 for r < i: a uniform
-    // trip count)
+    // dDelta rows 16 w .. : P^T dO (P_ri = 0 for r < i, so the steps start at r = 16 w) + Kt X
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 16 * w; r0 < BC; r0 += 4)
+      d = mfma4(sP[(r0 + lg) * LP + 16 * w + lm], sO[(r0 + lg) * 16 + lm], d);
 #pragma unroll 8
-    for (int r = 0; r < BC; ++r) d += sP[r * BC + i] * *reinterpret_cast<const f32x4*>(sO + r * 16 + jj);
-#pragma unroll 4
-    for (int mm = 0; mm < K; mm += 4) {
-      const f32x4 kt = *reinterpret_cast<const f32x4*>(sKt + i * LKt + mm);
+    for (int mm = 0; mm < K; mm += 4)
+      d = mfma4(sKt[(16 * w + lm) * LKt + mm + lg], sX[(mm + lg) * 16 + lm], d);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) d += kt[e] * *reinterpret_cast<const f32x4*>(sX + (mm + e) * 16 + jj);
-    }
-    *reinterpret_cast<f32x4*>(dDl + (((size_t)c * H + h) * BC + i) * V + c0 + jj) = d;
-    *reinterpret_cast<f32x4*>(sDD + i * 16 + jj) = d;
-    __syncthreads();
-    // X_prev = diag(gamma) X + Qe^T dO - W^T dDelta for row m, columns cg .. cg + NC - 1
-    float acc[NC];
-#pragma unroll
-    for (int e = 0; e < NC; ++e) acc[e] = sG[m] * sX[m * 16 + cg + e];
-#pragma unroll 8
-    for (int r = 0; r < BC; ++r) {
-      const float qe = sQe[r * K + m], w = sW[r * K + m];
-#pragma unroll
-      for (int e = 0; e < NC; ++e) acc[e] += qe * sO[r * 16 + cg + e] - w * sDD[r * 16 + cg + e];
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * w + 4 * lg + r;
+      sDD[row * 16 + lm] = d[r];
+      dDl[(((size_t)c * H + h) * BC + row) * V + c0 + lm] = d[r];
     }
     __syncthreads();
+    // X_prev tiles: diag(gamma) X + Qe^T dO - W^T dDelta
+    f32x4 acc[TPW];
 #pragma unroll
-    for (int e = 0; e < NC; ++e) sX[m * 16 + cg + e] = acc[e];
+    for (int q = 0; q < TPW; ++q) {
+      const int mt = w + 4 * q;
+      if (mt < K / 16) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * mt + 4 * lg + r;
+          acc[q][r] = sG[row] * sX[row * 16 + lm];
+        }
+#pragma unroll 8
+        for (int r0 = 0; r0 < BC; r0 += 4) {
+          acc[q] = mfma4(sQe[(r0 + lg) * LC + 16 * mt + lm], sO[(r0 + lg) * 16 + lm], acc[q]);
+          acc[q] = mfma4(-sW[(r0 + lg) * LC + 16 * mt + lm], sDD[(r0 + lg) * 16 + lm], acc[q]);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      const int mt = w + 4 * q;
+      if (mt < K / 16)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * lg + r) * 16 + lm] = acc[q][r];
+    }
   }
   if (dinit) {
     __syncthreads();
@@ -536,47 +601,47 @@ __global__ __launch_bounds__(NTG) void bwd_ga_kernel(
     const float* __restrict__ Dl, const float* __restrict__ dDl, int H,
     const BwdChunk* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr) {
   using G = GScr<K>;
-  constexpr int L = V + 4;
+  constexpr int L = V + 4;  // every block here is read along its rows
   __shared__ __align__(16) float sO[BC * L];
-  __shared__ __align__(16) float sDl[BC * L];
-  __shared__ __align__(16) float sDD[BC * L];
+  __shared__ __align__(16) float sD[BC * L];  // dDelta, then Delta
+  __shared__ __align__(16) float sS[K * L];   // S, then X
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= *ntot) return;
   const BwdChunk ch = chunks[c];
   const size_t ch_h = (size_t)c * H + h;
   float* sc = scr + ch_h * G::floats;
-  load_rows<V, L, NTG>(sO, dO, ch.tok, ch.len, H, h);
-  load_block<V, L, NTG>(sDl, Dl + ch_h * BC * V);
-  load_block<V, L, NTG>(sDD, dDl + ch_h * BC * V);
-  __syncthreads();
-  rowdot64<V, L, NTG>(sO, sDl, [&](int i, int j, float x) { sc[G::oDP + i * BC + j] = j <= i ? x : 0.f; });
-  // thread: key channel m, rows r0 .. r0 + RB - 1
-  constexpr int NG = NTG / K, RB = BC / NG;
-  const int m = threadIdx.x % K, r0 = (threadIdx.x / K) * RB;
-  const float* Sm = ckS + (ch_h * K + m) * V;
-  const float* Xm = ckX + (ch_h * K + m) * V;
-  float r1[RB], dw[RB], dkt[RB];
+  const float* S = ckS + ch_h * K * V;
+  const float* X = ckX + ch_h * K * V;
+  // rowsum(S * X): NP neighbouring threads per key channel (K NP is a whole number of waves),
+  // then a shuffle reduction among them
+  {
+    constexpr int NP = NTG / K < V / 4 ? NTG / K : V / 4, VP = V / NP;
+    if (threadIdx.x < K * NP) {
+      const int m = threadIdx.x / NP, part = threadIdx.x % NP;
+      float dg = 0.f;
 #pragma unroll
-  for (int u = 0; u < RB; ++u) r1[u] = dw[u] = dkt[u] = 0.f;
-  float dg = 0.f;
-  for (int vv = 0; vv < V; vv += 4) {
-    const f32x4 s4 = *reinterpret_cast<const f32x4*>(Sm + vv);
-    const f32x4 x4 = *reinterpret_cast<const f32x4*>(Xm + vv);
-    dg += dot4(s4, x4);
+      for (int vv = 0; vv < VP; vv += 4)
+        dg += dot4(*reinterpret_cast<const f32x4*>(S + m * V + part * VP + vv),
+                   *reinterpret_cast<const f32x4*>(X + m * V + part * VP + vv));
 #pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      r1[u] += dot4(*reinterpret_cast<const f32x4*>(sO + (r0 + u) * L + vv), s4);
-      dw[u] -= dot4(*reinterpret_cast<const f32x4*>(sDD + (r0 + u) * L + vv), s4);
-      dkt[u] += dot4(*reinterpret_cast<const f32x4*>(sDl + (r0 + u) * L + vv), x4);
+      for (int o = 1; o < NP; o <<= 1) dg += __shfl_xor(dg, o);
+      if (part == 0) sc[G::oDG + m] = dg;
     }
   }
-#pragma unroll
-  for (int u = 0; u < RB; ++u) {
-    sc[G::oR1 + (r0 + u) * K + m] = r1[u];
-    sc[G::oDW + (r0 + u) * K + m] = dw[u];
-    sc[G::oDKt + (r0 + u) * K + m] = dkt[u];
-  }
-  if (r0 == 0) sc[G::oDG + m] = dg;
+  load_rows<V, L, NTG>(sO, dO, ch.tok, ch.len, H, h);
+  load_block<V, L, NTG>(sD, dDl + ch_h * BC * V);
+  for (int e = threadIdx.x; e < K * V; e += NTG) sS[(e / V) * L + e % V] = S[e];
+  __syncthreads();
+  // dO S^T and dW = -dDelta S^T
+  mmf<K, V, false, true, L, L, NTG>(sO, sS, [&](int r, int m, float x) { sc[G::oR1 + r * K + m] = x; });
+  mmf<K, V, false, true, L, L, NTG>(sD, sS, [&](int r, int m, float x) { sc[G::oDW + r * K + m] = -x; });
+  __syncthreads();
+  load_block<V, L, NTG>(sD, Dl + ch_h * BC * V);
+  for (int e = threadIdx.x; e < K * V; e += NTG) sS[(e / V) * L + e % V] = X[e];
+  __syncthreads();
+  // Delta X^T and dP = lower(dO Delta^T)
+  mmf<K, V, false, true, L, L, NTG>(sD, sS, [&](int r, int m, float x) { sc[G::oDKt + r * K + m] = x; });
+  mmf<BC, V, false, true, L, L, NTG>(sO, sD, [&](int i, int j, float x) { sc[G::oDP + i * BC + j] = j <= i ? x : 0.f; });
 }
 
 // (b) dv = diag(beta) T^T dDelta, T^T dW, dT = dDelta (beta V)^T + dW (beta Ke)^T,
@@ -590,12 +655,15 @@ __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
     float* __restrict__ grad_v) {
   using R = BRec<K, V>;
   using G = GScr<K>;
-  constexpr int N1 = K > V ? K : V, L = N1 + 4, LV = V + 4, LK = K + 4;
-  constexpr int LA = L > 68 ? L : 68;  // bufA also holds a 64 x 64 product (row stride 68)
-  __shared__ __align__(16) float sT[BC * 68];
-  __shared__ __align__(16) float sdT[BC * 68];
+  // row strides: T and dT (read down their columns by most products) 80; dDelta and dW
+  // (B operands read down their columns) V + 16 and K + 16; v and Ke (read along rows) + 4
+  constexpr int LT = BC + 16, LDD = V + 16, LDW = K + 16, LVV = V + 4, LKE = K + 4;
+  constexpr int LA = (LDD > LDW ? LDD : LDW) > LT ? (LDD > LDW ? LDD : LDW) : LT;
+  constexpr int LB = LVV > LKE ? LVV : LKE;
+  __shared__ __align__(16) float sT[BC * LT];
+  __shared__ __align__(16) float sdT[BC * LT];
   __shared__ __align__(16) float bufA[BC * LA];
-  __shared__ __align__(16) float bufB[BC * L];
+  __shared__ __align__(16) float bufB[BC * LB];
   __shared__ float sBeta[BC], sDb[BC];
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= *ntot) return;
@@ -603,49 +671,48 @@ __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
   const size_t ch_h = (size_t)c * H + h;
   const float* rc = rec + ch_h * R::floats;
   float* sc = scr + ch_h * G::floats;
-  for (int e = threadIdx.x; e < BC * BC; e += NTG) sT[(e / BC) * 68 + e % BC] = rc[R::oT + e];
-  load_block<V, LV, NTG>(bufA, dDl + ch_h * BC * V);
+  for (int e = threadIdx.x; e < BC * BC; e += NTG) sT[(e / BC) * LT + e % BC] = rc[R::oT + e];
+  load_block<V, LDD, NTG>(bufA, dDl + ch_h * BC * V);
+  load_rows<V, LVV, NTG>(bufB, v, ch.tok, ch.len, H, h);
   if (threadIdx.x < BC) {
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
     sDb[threadIdx.x] = 0.f;
   }
   __syncthreads();
-  load_rows<V, LV, NTG>(bufB, v, ch.tok, ch.len, H, h);
-  __syncthreads();
   // T^T dDelta: dv = beta T^T dDelta, dbeta += rowsum(v * T^T dDelta)
-  mm64<V, 68, LV, true, NTG>(sT, bufA, [&](int r, int cc, float x) {
+  mmf<V, BC, true, false, LT, LDD, NTG>(sT, bufA, [&](int r, int cc, float x) {
     if (r < ch.len) grad_v[((ch.tok + r) * (int64_t)H + h) * V + cc] = sBeta[r] * x;
-    atomicAdd(&sDb[r], bufB[r * LV + cc] * x);
+    atomicAdd(&sDb[r], bufB[r * LVV + cc] * x);
   });
   __syncthreads();
-  for (int e = threadIdx.x; e < BC * V; e += NTG) bufB[(e / V) * LV + e % V] *= sBeta[e / V];
+  for (int e = threadIdx.x; e < BC * V; e += NTG) bufB[(e / V) * LVV + e % V] *= sBeta[e / V];
   __syncthreads();
-  rowdot64<V, LV, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * 68 + j] = x; });
+  // dT = dDelta (beta V)^T
+  mmf<BC, V, false, true, LDD, LVV, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * LT + j] = x; });
   __syncthreads();
   // dW and Ke = k e^b
-  load_block<K, LK, NTG>(bufA, sc + G::oDW);
-  load_rows<K, LK, NTG>(bufB, g, ch.tok, ch.len, H, h);
+  load_block<K, LDW, NTG>(bufA, sc + G::oDW);
+  load_rows<K, LKE, NTG>(bufB, g, ch.tok, ch.len, H, h);
   __syncthreads();
-  cumsum_log2<K, LK>(bufB);
+  cumsum_log2<K, LKE>(bufB);
   __syncthreads();
   for (int e = threadIdx.x; e < BC * K; e += NTG) {
     const int r = e / K, cc = e % K;
-    bufB[r * LK + cc] = r < ch.len ? to_f32(k[((ch.tok + r) * (int64_t)H + h) * K + cc]) *
-                                         exp2_f(bufB[r * LK + cc]) : 0.f;
+    bufB[r * LKE + cc] = r < ch.len ? to_f32(k[((ch.tok + r) * (int64_t)H + h) * K + cc]) *
+                                          exp2_f(bufB[r * LKE + cc]) : 0.f;
   }
   __syncthreads();
-  // T^T dW; dbeta += rowsum(Ke * T^T dW)
-  mm64<K, 68, LK, true, NTG>(sT, bufA, [&](int r, int cc, float x) {
+  // T^T dW; dbeta += rowsum(Ke * T^T dW); dT += dW (beta Ke)^T
+  mmf<K, BC, true, false, LT, LDW, NTG>(sT, bufA, [&](int r, int cc, float x) {
     sc[G::oTDW + r * K + cc] = x;
-    atomicAdd(&sDb[r], bufB[r * LK + cc] * x);
+    atomicAdd(&sDb[r], bufB[r * LKE + cc] * x);
   });
-  // dT += dW (beta Ke)^T (each thread adds to the entries it owns)
-  rowdot64<K, LK, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * 68 + j] += sBeta[j] * x; });
+  mmf<BC, K, false, true, LDW, LKE, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * LT + j] += sBeta[j] * x; });
   __syncthreads();
-  // M1 = T^T dT into bufA, then dA = strict_lower(-M1 T^T)
-  mm64<BC, 68, 68, true, NTG>(sT, sdT, [&](int r, int cc, float x) { bufA[r * 68 + cc] = x; });
+  // M1 = T^T dT into bufA (row stride LT), then dA = strict_lower(-M1 T^T)
+  mmf<BC, BC, true, false, LT, LT, NTG>(sT, sdT, [&](int r, int cc, float x) { bufA[r * LT + cc] = x; });
   __syncthreads();
-  rowdot64<BC, 68, NTG>(bufA, sT, [&](int i, int j, float x) { sc[G::oDA + i * BC + j] = j < i ? -x : 0.f; });
+  mmf<BC, BC, false, true, LT, LT, NTG>(bufA, sT, [&](int i, int j, float x) { sc[G::oDA + i * BC + j] = j < i ? -x : 0.f; });
   if (threadIdx.x < BC) sc[G::oDB + threadIdx.x] = sDb[threadIdx.x];
 }
 
