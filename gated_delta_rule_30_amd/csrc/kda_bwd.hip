@@ -76,6 +76,15 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Sum of x over the 16 lanes of a DPP row (lanes 16 q .. 16 q + 15), in every lane.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror 8
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror 4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror 2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));  // row_ror 1
+  return x;
+}
+
 // out(r, c, x) for x = sum_{k < R} A(r, k) B(k, c), r < 64, c < N, operands in LDS:
 // A(r, k) = A[r][k] (row stride LA) or, with TA, A[k][r]; B(k, c) = B[k][c] (row stride LB)
 // or, with TB, B[c][k]. The 4 N / 16 output tiles of 16 x 16 go round robin to the NTB / 64
@@ -88,13 +97,17 @@ __device__ __forceinline__ void mmf(const float* sA, const float* sB, F&& out) {
   const int wv = threadIdx.x >> 6, lm = threadIdx.x & 15, lg = (threadIdx.x >> 4) & 3;
   for (int t = wv; t < TILES; t += WAVES) {
     const int r0 = 16 * (t & 3), c0 = 16 * (t >> 2);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;  // two chains of dependent steps
 #pragma unroll 8
-    for (int k = 0; k < R; k += 4) {
-      const float a = TA ? sA[(k + lg) * LA + r0 + lm] : sA[(r0 + lm) * LA + k + lg];
-      const float b = TB ? sB[(c0 + lm) * LB + k + lg] : sB[(k + lg) * LB + c0 + lm];
-      acc = mfma4(a, b, acc);
+    for (int k = 0; k < R; k += 8) {
+      const float a0 = TA ? sA[(k + lg) * LA + r0 + lm] : sA[(r0 + lm) * LA + k + lg];
+      const float b0 = TB ? sB[(c0 + lm) * LB + k + lg] : sB[(k + lg) * LB + c0 + lm];
+      const float a1 = TA ? sA[(k + 4 + lg) * LA + r0 + lm] : sA[(r0 + lm) * LA + k + 4 + lg];
+      const float b1 = TB ? sB[(c0 + lm) * LB + k + 4 + lg] : sB[(k + 4 + lg) * LB + c0 + lm];
+      acc0 = mfma4(a0, b0, acc0);
+      acc1 = mfma4(a1, b1, acc1);
     }
+    const f32x4 acc = acc0 + acc1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) out(r0 + 4 * lg + r, c0 + lm, acc[r]);
   }
@@ -174,32 +187,109 @@ __device__ __forceinline__ void rowdot64(const float* sX, const float* sY, F&& o
     for (int b = 0; b < 4; ++b) out(i0 + a, jb + 16 * b, acc[a][b]);
 }
 
-// rows r < len of a [T][H][N] tensor (token tok + r, head h) into LDS as fp32, zeros past len
+// Four consecutive elements as fp32.
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 load4(const bf16* p) {
+  return __builtin_convertvector(*reinterpret_cast<const bf16x4*>(p), f32x4);
+}
+
+// Rows r < len of a [T][H][N] tensor (token tok + r, head h) into LDS as fp32 (row stride L),
+// zeros past len. Four elements per load, every load of the thread issued before the first
+// store (rows past len read the last row, in bounds, and are dropped by a select).
 template <int N, int L, int NTB, typename MT>
 __device__ __forceinline__ void load_rows(float* dst, const MT* src, int64_t tok, int len, int H,
                                           int h) {
-  for (int e = threadIdx.x; e < BC * N; e += NTB) {
-    const int r = e / N, c = e % N;
-    dst[r * L + c] = r < len ? to_f32(src[((tok + r) * H + h) * (int64_t)N + c]) : 0.f;
+  constexpr int PIECES = BC * N / 4, PT = (PIECES + NTB - 1) / NTB;
+  f32x4 t[PT];
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = threadIdx.x + NTB * u;
+    const int r = e / (N / 4), c = 4 * (e % (N / 4));
+    if (PIECES % NTB == 0 || e < PIECES)
+      t[u] = load4(src + ((tok + min(r, len - 1)) * H + h) * (int64_t)N + c);
   }
-}
-
-// 64 x N fp32 block of a record or scratch (row-major, stride N) into LDS
-template <int N, int L, int NTB>
-__device__ __forceinline__ void load_block(float* dst, const float* src) {
-  for (int e = threadIdx.x; e < BC * N; e += NTB) dst[(e / N) * L + e % N] = src[e];
-}
-
-// cumulative log2 decay: dst (64 x K, stride L) holds log alpha on entry, b * log2 e on exit
-template <int K, int L>
-__device__ __forceinline__ void cumsum_log2(float* sB) {
-  if (threadIdx.x < K) {
-    float acc = 0.f;
-    for (int r = 0; r < BC; ++r) {
-      acc += sB[r * L + threadIdx.x];
-      sB[r * L + threadIdx.x] = acc * LOG2E;
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = threadIdx.x + NTB * u;
+    const int r = e / (N / 4), c = 4 * (e % (N / 4));
+    if (PIECES % NTB == 0 || e < PIECES) {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(dst + r * L + c) = r < len ? t[u] : z;
     }
   }
+}
+
+// dst[r][c] = src[r][c] * 2^{dst[r][c]} for rows r < len of a [T][H][N] tensor, 0 past len
+// (e.g. k e^b from b log2 e); the loads are issued first, as in load_rows.
+template <int N, int L, int NTB, typename MT>
+__device__ __forceinline__ void mul_rows_exp2(float* dst, const MT* src, int64_t tok, int len,
+                                              int H, int h) {
+  constexpr int PIECES = BC * N / 4, PT = (PIECES + NTB - 1) / NTB;
+  f32x4 t[PT];
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = threadIdx.x + NTB * u;
+    const int r = e / (N / 4), c = 4 * (e % (N / 4));
+    if (PIECES % NTB == 0 || e < PIECES)
+      t[u] = load4(src + ((tok + min(r, len - 1)) * H + h) * (int64_t)N + c);
+  }
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = threadIdx.x + NTB * u;
+    const int r = e / (N / 4), c = 4 * (e % (N / 4));
+    if (PIECES % NTB == 0 || e < PIECES) {
+      f32x4* d = reinterpret_cast<f32x4*>(dst + r * L + c);
+      const f32x4 b = *d;
+      f32x4 x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = r < len ? t[u][j] * exp2_f(b[j]) : 0.f;
+      *d = x;
+    }
+  }
+}
+
+// ROWS x N fp32 block (row-major, stride N) into LDS (row stride L), loads first.
+template <int N, int L, int NTB, int ROWS = BC>
+__device__ __forceinline__ void load_block(float* dst, const float* src) {
+  constexpr int PIECES = ROWS * N / 4, PT = (PIECES + NTB - 1) / NTB;
+  f32x4 t[PT];
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = threadIdx.x + NTB * u;
+    if (PIECES % NTB == 0 || e < PIECES) t[u] = load4(src + 4 * e);
+  }
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = threadIdx.x + NTB * u;
+    if (PIECES % NTB == 0 || e < PIECES)
+      *reinterpret_cast<f32x4*>(dst + (e / (N / 4)) * L + 4 * (e % (N / 4))) = t[u];
+  }
+}
+
+// Cumulative log2 decay: sB (64 x K, stride L) holds log alpha on entry, b * log2 e on exit.
+// P = NTB / K neighbouring threads share a channel: each sums its 64 / P consecutive rows, the
+// running totals of the P threads are scanned with shuffles, and each adds its prefix.
+template <int K, int L, int NTB>
+__device__ __forceinline__ void cumsum_log2(float* sB) {
+  constexpr int P = NTB / K, RP = BC / P;
+  static_assert(P >= 1 && P <= 32 && RP >= 1, "threads per channel");
+  const int c = threadIdx.x / P, part = threadIdx.x % P;
+  float x[RP];
+  float run = 0.f;
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    run += sB[(part * RP + r) * L + c];
+    x[r] = run;
+  }
+  float pre = run;
+#pragma unroll
+  for (int o = 1; o < P; o <<= 1) {
+    const float y = __shfl_up(pre, o, P);
+    if (part >= o) pre += y;
+  }
+  pre -= run;  // the rows before this thread's
+#pragma unroll
+  for (int r = 0; r < RP; ++r) sB[(part * RP + r) * L + c] = (x[r] + pre) * LOG2E;
 }
 
 }  // namespace
@@ -276,7 +366,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
   if (threadIdx.x < BC)
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
   __syncthreads();
-  cumsum_log2<K, LK>(sB);
+  cumsum_log2<K, LK, NTP>(sB);
   __syncthreads();
   // Qe, Kt, gamma (rows past len hold q = k = 0, and b stays at its last value)
   for (int e = threadIdx.x; e < BC * K; e += NTP) {
@@ -345,10 +435,9 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
     sK[r * LK + cc] *= sBeta[r] * exp2_f(sB[r * LK + cc]);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < BC * V; e += NTP) {
-    const int r = e / V, cc = e % V;
-    sQ[r * L + cc] = r < ch.len ? sBeta[r] * to_f32(v[((ch.tok + r) * H + h) * (int64_t)V + cc]) : 0.f;
-  }
+  load_rows<V, L, NTP>(sQ, v, ch.tok, ch.len, H, h);
+  __syncthreads();
+  for (int e = threadIdx.x; e < BC * V; e += NTP) sQ[(e / V) * L + e % V] *= sBeta[e / V];
   __syncthreads();
   mmf<K, BC, false, false, 68, LK, NTP>(sT, sK, [&](int r, int cc, float x) { rc[R::oW + r * K + cc] = x; });
   mmf<V, BC, false, false, 68, L, NTP>(sT, sQ, [&](int r, int cc, float x) { rc[R::oU + r * V + cc] = x; });
@@ -630,14 +719,14 @@ __global__ __launch_bounds__(NTG) void bwd_ga_kernel(
   }
   load_rows<V, L, NTG>(sO, dO, ch.tok, ch.len, H, h);
   load_block<V, L, NTG>(sD, dDl + ch_h * BC * V);
-  for (int e = threadIdx.x; e < K * V; e += NTG) sS[(e / V) * L + e % V] = S[e];
+  load_block<V, L, NTG, K>(sS, S);
   __syncthreads();
   // dO S^T and dW = -dDelta S^T
   mmf<K, V, false, true, L, L, NTG>(sO, sS, [&](int r, int m, float x) { sc[G::oR1 + r * K + m] = x; });
   mmf<K, V, false, true, L, L, NTG>(sD, sS, [&](int r, int m, float x) { sc[G::oDW + r * K + m] = -x; });
   __syncthreads();
   load_block<V, L, NTG>(sD, Dl + ch_h * BC * V);
-  for (int e = threadIdx.x; e < K * V; e += NTG) sS[(e / V) * L + e % V] = X[e];
+  load_block<V, L, NTG, K>(sS, X);
   __syncthreads();
   // Delta X^T and dP = lower(dO Delta^T)
   mmf<K, V, false, true, L, L, NTG>(sD, sS, [&](int r, int m, float x) { sc[G::oDKt + r * K + m] = x; });
@@ -655,13 +744,15 @@ __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
     float* __restrict__ grad_v) {
   using R = BRec<K, V>;
   using G = GScr<K>;
-  // row strides: T and dT (read down their columns by most products) 80; dDelta and dW
-  // (B operands read down their columns) V + 16 and K + 16; v and Ke (read along rows) + 4
-  constexpr int LT = BC + 16, LDD = V + 16, LDW = K + 16, LVV = V + 4, LKE = K + 4;
+  // row strides: blocks read both along and down their rows (T, dDelta, dW) 20 more than a
+  // multiple of 64 floats (no bank conflict along rows, at most two-way down columns); dT,
+  // read down its columns, 80; v and Ke, read along rows, + 4
+  constexpr int LT = BC + 20, LDT = BC + 16;
+  constexpr int LDD = V + ((84 - V) & 63), LDW = K + ((84 - K) & 63), LVV = V + 4, LKE = K + 4;
   constexpr int LA = (LDD > LDW ? LDD : LDW) > LT ? (LDD > LDW ? LDD : LDW) : LT;
   constexpr int LB = LVV > LKE ? LVV : LKE;
   __shared__ __align__(16) float sT[BC * LT];
-  __shared__ __align__(16) float sdT[BC * LT];
+  __shared__ __align__(16) float sdT[BC * LDT];
   __shared__ __align__(16) float bufA[BC * LA];
   __shared__ __align__(16) float bufB[BC * LB];
   __shared__ float sBeta[BC], sDb[BC];
@@ -671,7 +762,7 @@ __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
   const size_t ch_h = (size_t)c * H + h;
   const float* rc = rec + ch_h * R::floats;
   float* sc = scr + ch_h * G::floats;
-  for (int e = threadIdx.x; e < BC * BC; e += NTG) sT[(e / BC) * LT + e % BC] = rc[R::oT + e];
+  load_block<BC, LT, NTG>(sT, rc + R::oT);
   load_block<V, LDD, NTG>(bufA, dDl + ch_h * BC * V);
   load_rows<V, LVV, NTG>(bufB, v, ch.tok, ch.len, H, h);
   if (threadIdx.x < BC) {
@@ -682,35 +773,33 @@ __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
   // T^T dDelta: dv = beta T^T dDelta, dbeta += rowsum(v * T^T dDelta)
   mmf<V, BC, true, false, LT, LDD, NTG>(sT, bufA, [&](int r, int cc, float x) {
     if (r < ch.len) grad_v[((ch.tok + r) * (int64_t)H + h) * V + cc] = sBeta[r] * x;
-    atomicAdd(&sDb[r], bufB[r * LVV + cc] * x);
+    const float y = row16_sum(bufB[r * LVV + cc] * x);  // the 16 lanes of a row hold one r
+    if ((threadIdx.x & 15) == 0) atomicAdd(&sDb[r], y);
   });
   __syncthreads();
   for (int e = threadIdx.x; e < BC * V; e += NTG) bufB[(e / V) * LVV + e % V] *= sBeta[e / V];
   __syncthreads();
   // dT = dDelta (beta V)^T
-  mmf<BC, V, false, true, LDD, LVV, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * LT + j] = x; });
+  mmf<BC, V, false, true, LDD, LVV, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * LDT + j] = x; });
   __syncthreads();
   // dW and Ke = k e^b
   load_block<K, LDW, NTG>(bufA, sc + G::oDW);
   load_rows<K, LKE, NTG>(bufB, g, ch.tok, ch.len, H, h);
   __syncthreads();
-  cumsum_log2<K, LKE>(bufB);
+  cumsum_log2<K, LKE, NTG>(bufB);
   __syncthreads();
-  for (int e = threadIdx.x; e < BC * K; e += NTG) {
-    const int r = e / K, cc = e % K;
-    bufB[r * LKE + cc] = r < ch.len ? to_f32(k[((ch.tok + r) * (int64_t)H + h) * K + cc]) *
-                                          exp2_f(bufB[r * LKE + cc]) : 0.f;
-  }
+  mul_rows_exp2<K, LKE, NTG>(bufB, k, ch.tok, ch.len, H, h);
   __syncthreads();
   // T^T dW; dbeta += rowsum(Ke * T^T dW); dT += dW (beta Ke)^T
   mmf<K, BC, true, false, LT, LDW, NTG>(sT, bufA, [&](int r, int cc, float x) {
     sc[G::oTDW + r * K + cc] = x;
-    atomicAdd(&sDb[r], bufB[r * LKE + cc] * x);
+    const float y = row16_sum(bufB[r * LKE + cc] * x);
+    if ((threadIdx.x & 15) == 0) atomicAdd(&sDb[r], y);
   });
-  mmf<BC, K, false, true, LDW, LKE, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * LT + j] += sBeta[j] * x; });
+  mmf<BC, K, false, true, LDW, LKE, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * LDT + j] += sBeta[j] * x; });
   __syncthreads();
   // M1 = T^T dT into bufA (row stride LT), then dA = strict_lower(-M1 T^T)
-  mmf<BC, BC, true, false, LT, LT, NTG>(sT, sdT, [&](int r, int cc, float x) { bufA[r * LT + cc] = x; });
+  mmf<BC, BC, true, false, LT, LDT, NTG>(sT, sdT, [&](int r, int cc, float x) { bufA[r * LT + cc] = x; });
   __syncthreads();
   mmf<BC, BC, false, true, LT, LT, NTG>(bufA, sT, [&](int i, int j, float x) { sc[G::oDA + i * BC + j] = j < i ? -x : 0.f; });
   if (threadIdx.x < BC) sc[G::oDB + threadIdx.x] = sDb[threadIdx.x];
@@ -739,17 +828,15 @@ __global__ __launch_bounds__(NTG) void bwd_gc_kernel(
   load_rows<K, LK, NTG>(sQ, q, ch.tok, ch.len, H, h);
   load_rows<K, LK, NTG>(sK, k, ch.tok, ch.len, H, h);
   load_rows<K, LK, NTG>(sB, g, ch.tok, ch.len, H, h);
-  for (int e = threadIdx.x; e < BC * BC; e += NTG) {
-    sdP[(e / BC) * 68 + e % BC] = sc[G::oDP + e];
-    sdA[(e / BC) * 68 + e % BC] = sc[G::oDA + e];
-  }
+  load_block<BC, 68, NTG>(sdP, sc + G::oDP);
+  load_block<BC, 68, NTG>(sdA, sc + G::oDA);
   if (threadIdx.x < BC) {
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
     sDb[threadIdx.x] = 0.f;
   }
   if (threadIdx.x < K) sRed[threadIdx.x] = 0.f;
   __syncthreads();
-  cumsum_log2<K, LK>(sB);
+  cumsum_log2<K, LK, NTG>(sB);
   __syncthreads();
   // thread: key channel m, rows i = i0 + NG u (interleaved: the pairwise sums grow with i)
   constexpr int NG = NTG / K, RB = BC / NG;
@@ -793,12 +880,30 @@ __global__ __launch_bounds__(NTG) void bwd_gc_kernel(
   for (int u = 0; u < RB; ++u) sQ[(i0 + NG * u) * LK + m] = db[u];
   __syncthreads();
   // log alpha: reverse cumulative sum of db over the chunk, the last token also carrying
-  // sum_i k_i * dKt_i and gamma * rowsum(S * X)
-  if (threadIdx.x < K) {
-    float acc = sRed[m] + sc[G::oDG + m] * exp2_f(bl);
-    for (int r = BC - 1; r >= 0; --r) {
-      acc += sQ[r * LK + m];
-      if (r < ch.len) grad_g[((ch.tok + r) * (int64_t)H + h) * K + m] = acc;
+  // sum_i k_i * dKt_i and gamma * rowsum(S * X); NTG / K neighbouring threads per channel, as
+  // in cumsum_log2 but from the last row
+  {
+    constexpr int P = NTG / K, RP = BC / P;
+    const int cm = threadIdx.x / P, part = threadIdx.x % P;
+    float x[RP];
+    float run = 0.f;
+#pragma unroll
+    for (int r = RP - 1; r >= 0; --r) {
+      run += sQ[(part * RP + r) * LK + cm];
+      x[r] = run;
+    }
+    float post = run;  // rows from this thread's first to the last, after the scan
+#pragma unroll
+    for (int o = 1; o < P; o <<= 1) {
+      const float y = __shfl_down(post, o, P);
+      if (part + o < P) post += y;
+    }
+    post -= run;  // the rows after this thread's
+    post += sRed[cm] + sc[G::oDG + cm] * exp2_f(sB[(BC - 1) * LK + cm]);
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      const int row = part * RP + r;
+      if (row < ch.len) grad_g[((ch.tok + row) * (int64_t)H + h) * K + cm] = x[r] + post;
     }
   }
   if (threadIdx.x < ch.len)
