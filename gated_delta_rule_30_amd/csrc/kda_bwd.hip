@@ -449,7 +449,8 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
 // blocks are loaded whole into registers (16-byte pieces, all in flight) while the chunk
 // before is computed, then stored to LDS; the chunk's products read LDS only. The loop body
 // has no branch around those loads (the next chunk's index is clamped to the last), so the
-// compiler neither sinks them to their use nor waits for them early.
+// compiler neither sinks them to their use nor waits for them early, and its barriers order
+// LDS only (a full __syncthreads would also wait for the loads in flight).
 
 // the token range of sequence n
 __device__ __forceinline__ void seq_range(const int32_t* cu, int N, int64_t T, int n, int64_t* s0,
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
   };
   fetch(first);
   for (int c = first; c < last; ++c) {
-    __syncthreads();  // the previous chunk's reads of LDS are done
+    lds_barrier();  // the previous chunk's reads of LDS are done (the prefetch stays in flight)
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
       const int e = tid + NT * u;
@@ -510,20 +511,26 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
     sG[tid % K] = rg;
     f32x4 d = {ru[0], ru[1], ru[2], ru[3]};
     fetch(min(c + 1, last - 1));
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < K * 16; e += NT)
       ckS[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sS[e];
-    // Delta rows 16 w .. : U - W S
+    // Delta rows 16 w .. : U - W S (two chains of dependent steps)
+    {
+      f32x4 d1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-    for (int mm = 0; mm < K; mm += 4)
-      d = mfma4(-sW[(16 * w + lm) * LW + mm + lg], sS[(mm + lg) * 16 + lm], d);
+      for (int mm = 0; mm < K; mm += 8) {
+        d = mfma4(-sW[(16 * w + lm) * LW + mm + lg], sS[(mm + lg) * 16 + lm], d);
+        d1 = mfma4(-sW[(16 * w + lm) * LW + mm + 4 + lg], sS[(mm + 4 + lg) * 16 + lm], d1);
+      }
+      d += d1;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * w + 4 * lg + r;
       sD[row * 16 + lm] = d[r];
       Dl[(((size_t)c * H + h) * BC + row) * V + c0 + lm] = d[r];
     }
-    __syncthreads();
+    lds_barrier();
     // S' tiles: diag(gamma) S + Kt^T Delta
     f32x4 acc[TPW];
 #pragma unroll
@@ -535,12 +542,16 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
           const int row = 16 * mt + 4 * lg + r;
           acc[q][r] = sG[row] * sS[row * 16 + lm];
         }
+        f32x4 a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-        for (int r0 = 0; r0 < BC; r0 += 4)
+        for (int r0 = 0; r0 < BC; r0 += 8) {
           acc[q] = mfma4(sKt[(r0 + lg) * LKT + 16 * mt + lm], sD[(r0 + lg) * 16 + lm], acc[q]);
+          a1 = mfma4(sKt[(r0 + 4 + lg) * LKT + 16 * mt + lm], sD[(r0 + 4 + lg) * 16 + lm], a1);
+        }
+        acc[q] += a1;
       }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int q = 0; q < TPW; ++q) {
       const int mt = w + 4 * q;
@@ -610,7 +621,7 @@ __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
   if (first < last) fetch(last - 1);
   for (int c = last - 1; c >= first; --c) {
     const int len = (int)min((int64_t)BC, s1 - (s0 + (int64_t)(c - first) * BC));
-    __syncthreads();  // the previous chunk's reads of LDS are done
+    lds_barrier();  // the previous chunk's reads of LDS are done (the prefetch stays in flight)
 #pragma unroll
     for (int u = 0; u < PP; ++u) {
       const int e = tid + NT * u;
@@ -630,7 +641,7 @@ __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
     }
     sG[tid % K] = rg;
     fetch(max(c - 1, first));
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < K * 16; e += NT)
       ckX[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sX[e];
     // dDelta rows 16 w .. : P^T dO (P_ri = 0 for r < i, so the steps start at r = 16 w) + Kt X
@@ -646,7 +657,7 @@ __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
       sDD[row * 16 + lm] = d[r];
       dDl[(((size_t)c * H + h) * BC + row) * V + c0 + lm] = d[r];
     }
-    __syncthreads();
+    lds_barrier();
     // X_prev tiles: diag(gamma) X + Qe^T dO - W^T dDelta
     f32x4 acc[TPW];
 #pragma unroll
@@ -665,7 +676,7 @@ __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int q = 0; q < TPW; ++q) {
       const int mt = w + 4 * q;
