@@ -102,3 +102,27 @@ def test_bwd_empty_input():
                           d_final_state=dfin)
     assert torch.equal(grads[5], dfin)
     assert all(g.numel() == 0 for g in grads[:5])
+
+
+@pytest.mark.timeout(900)
+def test_bwd_long_prefill_sampled_head():
+    """The benchmarked shape (B=1, H=32, T=65536, K=V=128, bf16): every gradient of one sampled
+    head against the oracle, which runs that head alone (heads are independent)."""
+    print("bwd long prefill, head 7", flush=True)
+    inp = workloads.make_workload("long", device=DEV)
+    T, H, K = inp["q"].shape
+    V = inp["v"].shape[-1]
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(77)
+    d_o = torch.randn((T, H, V), generator=gen, device=DEV).to(torch.bfloat16)
+    dfin = torch.randn((1, H, K, V), generator=gen, device=DEV)
+    grads = kda.chunk_bwd(*(inp[x] for x in ORDER), d_o, init_state=inp["init_state"],
+                          d_final_state=dfin)
+    hs = slice(7, 8)
+    ref = oracle.kda_bwd(*(np64(inp[x][:, hs]) for x in ORDER), np64(d_o[:, hs]),
+                         dfinal=np64(dfin[:, hs]), init_state=np64(inp["init_state"][:, hs]))
+    for name, got, want in zip(NAMES, grads, ref):
+        g = np64(got[:, hs])
+        err = rel_err(g, want)
+        print("  %-10s rel err %.2e" % (name, err), flush=True)
+        assert np.all(np.isfinite(g)) and err <= TOL, "%s: %.3e" % (name, err)
