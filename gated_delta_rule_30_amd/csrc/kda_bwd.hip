@@ -847,11 +847,20 @@ __global__ __launch_bounds__(NTG) void bwd_gc_kernel(
   }
   if (threadIdx.x < K) sRed[threadIdx.x] = 0.f;
   __syncthreads();
-  cumsum_log2<K, LK, NTG>(sB);
-  __syncthreads();
-  // thread: key channel m, rows i = i0 + NG u (interleaved: the pairwise sums grow with i)
+  // thread: key channel m, rows i = i0 + NG u (interleaved: the pairwise sums grow with i);
+  // its rows of dO S^T, T^T dW and Delta X^T are loaded now, in flight through the scan
   constexpr int NG = NTG / K, RB = BC / NG;
   const int m = threadIdx.x % K, i0 = threadIdx.x / K;
+  float r1v[RB], tdw[RB], dkv[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) {
+    const int i = i0 + NG * u;
+    r1v[u] = sc[G::oR1 + i * K + m];
+    tdw[u] = sc[G::oTDW + i * K + m];
+    dkv[u] = sc[G::oDKt + i * K + m];
+  }
+  cumsum_log2<K, LK, NTG>(sB);
+  lds_barrier();  // LDS only: the loads above stay in flight
   const float bl = sB[(BC - 1) * LK + m];
   float db[RB];
   float red = 0.f;
@@ -872,11 +881,18 @@ __global__ __launch_bounds__(NTG) void bwd_gc_kernel(
       s3 += (sdA[r * 68 + i] * sBeta[r] * sK[r * LK + m] + sdP[r * 68 + i] * sQ[r * LK + m]) *
             exp2_f(sB[r * LK + m] - bi);
     const float eb = exp2_f(bi);
-    const float dq = sc[G::oR1 + i * K + m] * eb + s1;
-    const float dke = sBeta[i] * (sc[G::oTDW + i * K + m] * eb + s2);
-    const float dkt = sc[G::oDKt + i * K + m] * exp2_f(bl - bi);
+    const float dq = r1v[u] * eb + s1;
+    const float dke = sBeta[i] * (tdw[u] * eb + s2);
+    const float dkt = dkv[u] * exp2_f(bl - bi);
     const float dk = dke + s3 + dkt;
-    atomicAdd(&sDb[i], ki * s2);
+    {
+      // dbeta's sum over the key channels of row i: the lanes sharing i (a whole wave, or 32
+      // lanes at K = 32) reduce first, then one LDS atomic
+      float y = row16_sum(ki * s2);
+      y += __shfl_xor(y, 16);
+      if constexpr (K >= 64) y += __shfl_xor(y, 32);
+      if (threadIdx.x % (K >= 64 ? 64 : K) == 0) atomicAdd(&sDb[i], y);
+    }
     red += ki * dkt;
     db[u] = qi * dq + ki * (dke - s3 - dkt);
     if (i < ch.len) {
