@@ -365,9 +365,9 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
   load_rows<K, LK, NTP>(sB, g, ch.tok, ch.len, H, h);
   if (threadIdx.x < BC)
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
-  __syncthreads();
+  lds_barrier();
   cumsum_log2<K, LK, NTP>(sB);
-  __syncthreads();
+  lds_barrier();
   // Qe, Kt, gamma (rows past len hold q = k = 0, and b stays at its last value)
   for (int e = threadIdx.x; e < BC * K; e += NTP) {
     const int r = e / K, cc = e % K;
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
       rc[R::oP + i * BC + j] = j <= i ? p[u] : 0.f;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // T = (I + A)^{-1} by forward substitution, one column per thread
   if (threadIdx.x < BC) {
     const int m = threadIdx.x;
@@ -434,11 +434,11 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
     const int r = e / K, cc = e % K;
     sK[r * LK + cc] *= sBeta[r] * exp2_f(sB[r * LK + cc]);
   }
-  __syncthreads();
+  lds_barrier();
   load_rows<V, L, NTP>(sQ, v, ch.tok, ch.len, H, h);
-  __syncthreads();
+  lds_barrier();
   for (int e = threadIdx.x; e < BC * V; e += NTP) sQ[(e / V) * L + e % V] *= sBeta[e / V];
-  __syncthreads();
+  lds_barrier();
   mmf<K, BC, false, false, 68, LK, NTP>(sT, sK, [&](int r, int cc, float x) { rc[R::oW + r * K + cc] = x; });
   mmf<V, BC, false, false, 68, L, NTP>(sT, sQ, [&](int r, int cc, float x) { rc[R::oU + r * V + cc] = x; });
 }
@@ -693,6 +693,8 @@ __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
 }
 
 // ---------------------------------------------------------------- per-chunk gradients
+// As in the record kernel, the barriers order LDS only: no kernel here reads global memory that
+// it writes itself, so none waits for its stores (or for loads it has in flight) at a barrier.
 // (a) dP = lower(dO Delta^T); with S (chunk start) and X (chunk end) streamed from HBM:
 //     dO S^T, dW = -dDelta S^T, Delta X^T and rowsum(S * X)
 template <int K, int V, typename MT>
@@ -731,14 +733,14 @@ __global__ __launch_bounds__(NTG) void bwd_ga_kernel(
   load_rows<V, L, NTG>(sO, dO, ch.tok, ch.len, H, h);
   load_block<V, L, NTG>(sD, dDl + ch_h * BC * V);
   load_block<V, L, NTG, K>(sS, S);
-  __syncthreads();
+  lds_barrier();
   // dO S^T and dW = -dDelta S^T
   mmf<K, V, false, true, L, L, NTG>(sO, sS, [&](int r, int m, float x) { sc[G::oR1 + r * K + m] = x; });
   mmf<K, V, false, true, L, L, NTG>(sD, sS, [&](int r, int m, float x) { sc[G::oDW + r * K + m] = -x; });
-  __syncthreads();
+  lds_barrier();
   load_block<V, L, NTG>(sD, Dl + ch_h * BC * V);
   load_block<V, L, NTG, K>(sS, X);
-  __syncthreads();
+  lds_barrier();
   // Delta X^T and dP = lower(dO Delta^T)
   mmf<K, V, false, true, L, L, NTG>(sD, sS, [&](int r, int m, float x) { sc[G::oDKt + r * K + m] = x; });
   mmf<BC, V, false, true, L, L, NTG>(sO, sD, [&](int i, int j, float x) { sc[G::oDP + i * BC + j] = j <= i ? x : 0.f; });
@@ -780,27 +782,27 @@ __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
     sDb[threadIdx.x] = 0.f;
   }
-  __syncthreads();
+  lds_barrier();
   // T^T dDelta: dv = beta T^T dDelta, dbeta += rowsum(v * T^T dDelta)
   mmf<V, BC, true, false, LT, LDD, NTG>(sT, bufA, [&](int r, int cc, float x) {
     if (r < ch.len) grad_v[((ch.tok + r) * (int64_t)H + h) * V + cc] = sBeta[r] * x;
     const float y = row16_sum(bufB[r * LVV + cc] * x);  // the 16 lanes of a row hold one r
     if ((threadIdx.x & 15) == 0) atomicAdd(&sDb[r], y);
   });
-  __syncthreads();
+  lds_barrier();
   for (int e = threadIdx.x; e < BC * V; e += NTG) bufB[(e / V) * LVV + e % V] *= sBeta[e / V];
-  __syncthreads();
+  lds_barrier();
   // dT = dDelta (beta V)^T
   mmf<BC, V, false, true, LDD, LVV, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * LDT + j] = x; });
-  __syncthreads();
+  lds_barrier();
   // dW and Ke = k e^b
   load_block<K, LDW, NTG>(bufA, sc + G::oDW);
   load_rows<K, LKE, NTG>(bufB, g, ch.tok, ch.len, H, h);
-  __syncthreads();
+  lds_barrier();
   cumsum_log2<K, LKE, NTG>(bufB);
-  __syncthreads();
+  lds_barrier();
   mul_rows_exp2<K, LKE, NTG>(bufB, k, ch.tok, ch.len, H, h);
-  __syncthreads();
+  lds_barrier();
   // T^T dW; dbeta += rowsum(Ke * T^T dW); dT += dW (beta Ke)^T
   mmf<K, BC, true, false, LT, LDW, NTG>(sT, bufA, [&](int r, int cc, float x) {
     sc[G::oTDW + r * K + cc] = x;
@@ -808,10 +810,10 @@ __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
     if ((threadIdx.x & 15) == 0) atomicAdd(&sDb[r], y);
   });
   mmf<BC, K, false, true, LDW, LKE, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * LDT + j] += sBeta[j] * x; });
-  __syncthreads();
+  lds_barrier();
   // M1 = T^T dT into bufA (row stride LT), then dA = strict_lower(-M1 T^T)
   mmf<BC, BC, true, false, LT, LDT, NTG>(sT, sdT, [&](int r, int cc, float x) { bufA[r * LT + cc] = x; });
-  __syncthreads();
+  lds_barrier();
   mmf<BC, BC, false, true, LT, LT, NTG>(bufA, sT, [&](int i, int j, float x) { sc[G::oDA + i * BC + j] = j < i ? -x : 0.f; });
   if (threadIdx.x < BC) sc[G::oDB + threadIdx.x] = sDb[threadIdx.x];
 }
@@ -846,7 +848,7 @@ __global__ __launch_bounds__(NTG) void bwd_gc_kernel(
     sDb[threadIdx.x] = 0.f;
   }
   if (threadIdx.x < K) sRed[threadIdx.x] = 0.f;
-  __syncthreads();
+  lds_barrier();
   // thread: key channel m, rows i = i0 + NG u (interleaved: the pairwise sums grow with i);
   // its rows of dO S^T, T^T dW and Delta X^T are loaded now, in flight through the scan
   constexpr int NG = NTG / K, RB = BC / NG;
@@ -902,10 +904,10 @@ __global__ __launch_bounds__(NTG) void bwd_gc_kernel(
     }
   }
   atomicAdd(&sRed[m], red);
-  __syncthreads();  // every read of sQ done
+  lds_barrier();  // every read of sQ done
 #pragma unroll
   for (int u = 0; u < RB; ++u) sQ[(i0 + NG * u) * LK + m] = db[u];
-  __syncthreads();
+  lds_barrier();
   // log alpha: reverse cumulative sum of db over the chunk, the last token also carrying
   // sum_i k_i * dKt_i and gamma * rowsum(S * X); NTG / K neighbouring threads per channel, as
   // in cumsum_log2 but from the last row
