@@ -207,12 +207,13 @@ def chunk_fwd_scan(q, k, v, log_alpha, beta, init_state=None, num_seqs=1, num_gr
 
 
 def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final_state=None,
-              cu_seqlens=None, num_seqs=None, workspace=None):
+              cu_seqlens=None, num_seqs=None, workspace=None, grads=None):
     """kda_chunk_bwd on torch tensors: the gradients of sum(d_o * o) + sum(d_final_state *
     final_state) for chunk_fwd on the same inputs (no input options). d_o [T, H, V] in the input
     dtype; d_final_state [N, H, K, V] fp32 or None (zero). Returns fp32 tensors
     (dq [T, H, K], dk [T, H, K], dv [T, H, V], dlog_alpha [T, H, K], dbeta [T, H],
-    dinit_state [N, H, K, V])."""
+    dinit_state [N, H, K, V]). ``grads`` may pass those six tensors to be written in place
+    (e.g. under graph capture)."""
     device = q.device
     T, H, K = q.shape
     V = v.shape[-1]
@@ -233,10 +234,17 @@ def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final_state=None
         if t is not None:
             _check(t, name, (N, H, K, V), torch.float32, device)
     f32 = dict(dtype=torch.float32, device=device)
-    dq, dk, dg = (torch.empty((T, H, K), **f32) for _ in range(3))
-    dv = torch.empty((T, H, V), **f32)
-    db = torch.empty((T, H), **f32)
-    dinit = torch.empty((N, H, K, V), **f32)
+    if grads is None:
+        dq, dk, dg = (torch.empty((T, H, K), **f32) for _ in range(3))
+        dv = torch.empty((T, H, V), **f32)
+        db = torch.empty((T, H), **f32)
+        dinit = torch.empty((N, H, K, V), **f32)
+    else:
+        dq, dk, dv, dg, db, dinit = grads
+        for name, t, shp in (("dq", dq, (T, H, K)), ("dk", dk, (T, H, K)), ("dv", dv, (T, H, V)),
+                             ("dlog_alpha", dg, (T, H, K)), ("dbeta", db, (T, H)),
+                             ("dinit_state", dinit, (N, H, K, V))):
+            _check(t, name, shp, torch.float32, device)
     need = int(_lib().kda_chunk_bwd_workspace_size(N, T, H, K, V, code))
     if need == 0:
         raise KdaError(2 if K not in (32, 64, 128) or V not in (32, 64, 128) else 1,

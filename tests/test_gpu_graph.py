@@ -68,3 +68,64 @@ def test_graph_replay_equals_eager():
         # eager work between replays
         step()
         torch.cuda.synchronize()
+
+
+def test_graph_replay_scan_and_backward():
+    """kda_chunk_fwd_scan and kda_chunk_bwd captured together and replayed three times with
+    eager work between: the scan's outputs equal the eager ones bit for bit; the backward's
+    per-row beta and decay sums go through LDS atomics, whose order may vary, so its
+    gradients are compared to 1e-6 of their largest magnitude."""
+    print("graph capture of chunk_fwd_scan + chunk_bwd", flush=True)
+    T, H, K = 2048, 2, 64
+    inp = workloads.gen_forward(T, H, K, K, gates="slow", dtype=torch.bfloat16, device=DEV,
+                                seed=22, init_std=0.1)
+    G = 6
+    wss = torch.empty(int(kda.lib().kda_chunk_fwd_scan_workspace_size(1, T, H, K, K, 1, G)),
+                      dtype=torch.uint8, device=DEV)
+    wsb = torch.empty(int(kda.lib().kda_chunk_bwd_workspace_size(1, T, H, K, K, 1)),
+                      dtype=torch.uint8, device=DEV)
+    o = torch.empty((T, H, K), dtype=torch.bfloat16, device=DEV)
+    fin = torch.empty((1, H, K, K), device=DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(6)
+    d_o = torch.randn((T, H, K), generator=gen, device=DEV).to(torch.bfloat16)
+    dfin = torch.randn((1, H, K, K), generator=gen, device=DEV)
+    f32 = dict(dtype=torch.float32, device=DEV)
+    grads = (torch.empty((T, H, K), **f32), torch.empty((T, H, K), **f32),
+             torch.empty((T, H, K), **f32), torch.empty((T, H, K), **f32),
+             torch.empty((T, H), **f32), torch.empty((1, H, K, K), **f32))
+
+    def step():
+        kda.chunk_fwd_scan(*(inp[x] for x in ORDER), init_state=inp["init_state"], num_groups=G,
+                           o=o, final_state=fin, workspace=wss)
+        kda.chunk_bwd(*(inp[x] for x in ORDER), d_o, init_state=inp["init_state"],
+                      d_final_state=dfin, workspace=wsb, grads=grads)
+
+    step()
+    torch.cuda.synchronize()
+    o_ref, fin_ref = o.clone(), fin.clone()
+    g_ref = [g.clone() for g in grads]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        o.fill_(float("nan"))
+        fin.zero_()
+        for g in grads:
+            g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), "replay %d: o" % rep
+        assert torch.equal(fin, fin_ref), "replay %d: final state" % rep
+        for i, (g, r) in enumerate(zip(grads, g_ref)):
+            err = float((g - r).abs().max() / r.abs().max())
+            assert err <= 1e-6, "replay %d: gradient %d differs by %.2e" % (rep, i, err)
+        step()
+        torch.cuda.synchronize()
