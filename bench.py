@@ -10,7 +10,8 @@ Prints one JSON line. `value` is whole-step throughput (prefill tokens + decode 
 second); per-call figures, roofline fractions and the oracle's CPU rate are attached. After the
 timed steps, the same line reports (each can be skipped by a flag): the input options on the
 same shapes, one long sequence over two heads through the plain call and through the
-chunk-parallel scan, and the training backward on the long-prefill shape.
+chunk-parallel scan, the forward at 256 key channels and the training backward on the
+long-prefill shape.
 """
 import argparse
 import csv
@@ -72,6 +73,7 @@ SOURCES = [os.path.join(ROOT, "gated_delta_rule_30_amd", "csrc", f)
            for f in ("kda_chunk.hip", "kda_decode.hip", "kda_device.h", "kda_internal.h")]
 CHUNK_KERNELS = ("table_kernel", "segment_kernel", "prep_kernel", "state_kernel", "state_split_kernel")
 DECODE_KERNEL = "decode_step_kernel"
+OTHER_PATHS = ("wide_", "bwd_", "scan_")  # kernels of other entry points with similar names
 CALIB_KERNEL = "neg_kernel"
 
 
@@ -101,7 +103,8 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib, command):
             raise SystemExit("no calibration kernel in " + path)
         factor = copy_mib * 1024.0 / calib[-1]  # true KiB / counted KiB
         calls = sum(1 for n, _ in rows if "table_kernel" in n)
-        chunk_kib = sum(v for n, v in rows if any(k in n for k in CHUNK_KERNELS))
+        chunk_kib = sum(v for n, v in rows if any(k in n for k in CHUNK_KERNELS)
+                        and not any(x in n for x in OTHER_PATHS))
         dec = [v for n, v in rows if DECODE_KERNEL in n]
         res[key] = {"factor": factor, "chunk_calls": calls,
                     "chunk_bytes_per_call": chunk_kib * 1024.0 * factor / max(calls, 1),
@@ -169,6 +172,8 @@ def main():
     ap.add_argument("--no-scan-bench", action="store_true",
                     help="skip the few-head long-sequence comparison of kda_chunk_fwd and "
                          "kda_chunk_fwd_scan")
+    ap.add_argument("--no-wide-bench", action="store_true",
+                    help="skip kda_chunk_fwd at K = V = 256 (the wide-key path) on the long shape")
     ap.add_argument("--no-bwd-bench", action="store_true",
                     help="skip the training backward (kda_chunk_bwd) on the long-prefill shape")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -378,6 +383,39 @@ def main():
                 "o_max_rel_diff": rel(os_s, os_p), "final_state_max_rel_diff": rel(fs_s, fs_p)}
         del sinp, os_p, os_s, fs_p, fs_s, ws_p, ws_s
 
+    # ---------------- 256 key channels (the wide-key path) on the long-prefill shape
+    wide = None
+    if not args.no_wide_bench:
+        Kw = Vw = 256
+        winp = workloads.gen_forward(T, H, Kw, Vw, dtype=torch.bfloat16, device=dev,
+                                     seed=wl["seed"] + 13, init_std=wl["init_std"])
+        ow = torch.empty((T, H, Vw), dtype=torch.bfloat16, device=dev)
+        fw = torch.empty((1, H, Kw, Vw), dtype=torch.float32, device=dev)
+        wsw = torch.empty(kda.workspace_size(1, T, H, Kw, Vw, torch.bfloat16), dtype=torch.uint8,
+                          device=dev)
+
+        def wide_call():
+            kda.chunk_fwd(*(winp[x] for x in names), init_state=winp["init_state"], o=ow,
+                          final_state=fw, workspace=wsw)
+
+        wsteps = max(1, min(args.steps, 5))
+        for _ in range(max(1, min(args.warmup, 2))):
+            wide_call()
+        torch.cuda.synchronize()
+        ew0, ew1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ew0.record()
+        for _ in range(wsteps):
+            wide_call()
+        ew1.record()
+        torch.cuda.synchronize()
+        wms = ew0.elapsed_time(ew1) / wsteps
+        wfl = chunk_alg_flops(T, H, Kw, Vw)
+        wide = {"workload": "B=1 H=32 T=65536 K=V=256 bf16, init state 0.1*N(0,1)",
+                "ms": wms, "calls": wsteps, "tokens_per_s": T / (wms * 1e-3),
+                "alg_flops": wfl, "fp32_frac": wfl / (wms * 1e-3) / PEAK_FP32,
+                "workspace_GB": wsw.numel() / 1e9}
+        del winp, ow, fw, wsw
+
     # ---------------- the training backward on the long-prefill shape (gradients of
     # sum(dO * o) + sum(dS * S_final) for every input and the initial state, fp32)
     bwd = None
@@ -457,6 +495,7 @@ def main():
         "input_options": options,
         "few_head_scan": scan,
         "training_backward": bwd,
+        "wide_key": wide,
         "parity_sample_max_rel_err": parity,
     }
     print(json.dumps(out), flush=True)

@@ -157,7 +157,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, num_se
         _check(final_state, "final_state", (N, H, K, V), torch.float32, device)
     need = int(_lib().kda_chunk_fwd_workspace_size(N, T, H, K, V, code))
     if need == 0:
-        raise KdaError(2 if K not in (32, 64, 128) or V not in (32, 64, 128, 256) else 1,
+        raise KdaError(2 if K not in (32, 64, 128, 256) or V not in (32, 64, 128, 256) else 1,
                        "kda_chunk_fwd_workspace_size")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)

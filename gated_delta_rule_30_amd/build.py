@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_scan.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_scan.hip", "kda_bwd.hip", "kda_wide.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

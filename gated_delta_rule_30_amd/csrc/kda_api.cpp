@@ -9,8 +9,10 @@
 namespace {
 
 bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128 || d == 256; }
-// the chunk path's prep kernel holds K-wide operand tiles in LDS: K <= 128
+// the chunk path's prep kernel holds K-wide operand tiles in LDS: K <= 128; K = 256 takes the
+// wide-key path (fp32 records, key channels in two halves)
 bool supported_chunk_dk(int32_t d) { return d == 32 || d == 64 || d == 128; }
+constexpr int32_t kWideDk = 256;
 constexpr uint32_t kAllOptions =
     KDA_OPT_SCALAR_GATE | KDA_OPT_GATE_LOGITS | KDA_OPT_BETA_LOGITS | KDA_OPT_L2NORM_QK;
 static_assert(KDA_OPT_SCALAR_GATE == kda::OPT_SCALAR_GATE && KDA_OPT_GATE_LOGITS == kda::OPT_GATE_LOGITS &&
@@ -47,7 +49,8 @@ static kda_status check_chunk_shape(int32_t num_seqs, int64_t total_tokens, int3
                                     int32_t dk, int32_t dv, kda_dtype dtype) {
   if (num_seqs <= 0 || num_heads <= 0 || total_tokens < 0 || total_tokens > kMaxTokens)
     return KDA_ERROR_INVALID_VALUE;
-  if (!valid_dtype(dtype) || !supported_chunk_dk(dk) || !supported_dim(dv)) return KDA_ERROR_NOT_SUPPORTED;
+  if (!valid_dtype(dtype) || !(supported_chunk_dk(dk) || dk == kWideDk) || !supported_dim(dv))
+    return KDA_ERROR_NOT_SUPPORTED;
   // fp32 operands at K = 128 exceed the prep kernel's LDS budget
   if (dtype == KDA_DTYPE_F32 && dk == 128) return KDA_ERROR_NOT_SUPPORTED;
   return KDA_SUCCESS;
@@ -57,6 +60,10 @@ extern "C" size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_t
                                                int32_t num_heads, int32_t dk, int32_t dv,
                                                kda_dtype dtype) {
   if (check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype) != KDA_SUCCESS) return 0;
+  if (dk == kWideDk) {
+    kda::WidePlan wp;
+    return kda::make_wide_plan(num_seqs, total_tokens, num_heads, dv, &wp) ? wp.total_bytes : 0;
+  }
   kda::ChunkPlan pl;
   if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16, &pl))
     return 0;
@@ -73,6 +80,7 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
   kda_status st = check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_SUCCESS) return st;
   if (options & ~kAllOptions) return KDA_ERROR_NOT_SUPPORTED;
+  if (dk == kWideDk && options != 0) return KDA_ERROR_NOT_SUPPORTED;  // the wide-key path: plain inputs
   const int32_t gdim = (options & KDA_OPT_SCALAR_GATE) ? 1 : dk;  // gate values per token and head
   if (cu_seqlens == nullptr && total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
   if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERROR_INVALID_VALUE;
@@ -99,9 +107,15 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
       return KDA_ERROR_INVALID_VALUE;
   }
   kda::ChunkPlan pl;
-  if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16, &pl))
-    return KDA_ERROR_INVALID_VALUE;
-  if (workspace_bytes < pl.total_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+  kda::WidePlan wp;
+  if (dk == kWideDk) {
+    if (!kda::make_wide_plan(num_seqs, total_tokens, num_heads, dv, &wp)) return KDA_ERROR_INVALID_VALUE;
+    if (workspace_bytes < wp.total_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+  } else {
+    if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16, &pl))
+      return KDA_ERROR_INVALID_VALUE;
+    if (workspace_bytes < pl.total_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+  }
 
   kda::ChunkArgs a;
   a.q = q;
@@ -122,7 +136,7 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
   a.final_state = final_state;
   a.workspace = workspace;
   a.stream = stream;
-  hipError_t e = kda::launch_chunk_fwd(a, pl);
+  hipError_t e = dk == kWideDk ? kda::launch_chunk_fwd_wide(a, wp) : kda::launch_chunk_fwd(a, pl);
   return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
 }
 
@@ -234,7 +248,8 @@ static kda_status check_scan_shape(int32_t num_seqs, int64_t total_tokens, int32
                                    int32_t dk, int32_t dv, kda_dtype dtype, int32_t num_groups) {
   kda_status st = check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_SUCCESS) return st;
-  if (dk != dv) return KDA_ERROR_NOT_SUPPORTED;  // the first pass needs V + K columns (<= 256)
+  // the first pass needs V + K columns (<= 256) and the K <= 128 chunk path
+  if (dk != dv || dk == kWideDk) return KDA_ERROR_NOT_SUPPORTED;
   if (num_groups <= 0 || total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
   return KDA_SUCCESS;
 }

@@ -27,17 +27,13 @@
 //                                      per (chunk, head): the products with S and X, then the
 //                                      T-side adjoints, then the decay-weighted pairwise sums
 //                                      and the per-token gradients
-#include "kda_device.h"
-#include "kda_internal.h"
+#include "kda_fp32.h"
 
 namespace kda {
 
-namespace {
+using namespace fp32;
 
-constexpr int BC = CHUNK;  // 64 tokens per chunk
-constexpr int NT = NTHREADS;  // the chains and the table kernels
-constexpr int NTP = 512;      // the record kernel: 8 waves per workgroup
-constexpr int NTG = 1024;     // the gradient kernels: 16 waves per workgroup
+namespace {
 
 // per-(chunk, head) fp32 record of the backward, row-major blocks
 template <int K, int V>
@@ -66,237 +62,7 @@ struct GScr {
   static constexpr int floats = (oDB + BC + 63) / 64 * 64;
 };
 
-__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
-  return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
-}
-
-// fp32 16 x 16 x 4 matrix-core step: lane l = 16 g + m supplies A[m][g] and B[g][m]; the
-// 16 x 16 result has lane (m, g) holding rows 4 g + r (r = 0..3) of column m.
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Sum of x over the 16 lanes of a DPP row (lanes 16 q .. 16 q + 15), in every lane.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror 8
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror 4
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror 2
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));  // row_ror 1
-  return x;
-}
-
-// out(r, c, x) for x = sum_{k < R} A(r, k) B(k, c), r < 64, c < N, operands in LDS:
-// A(r, k) = A[r][k] (row stride LA) or, with TA, A[k][r]; B(k, c) = B[k][c] (row stride LB)
-// or, with TB, B[c][k]. The 4 N / 16 output tiles of 16 x 16 go round robin to the NTB / 64
-// waves, each formed by R / 4 fp32 matrix-core steps. A wave's 64 operand reads fall in 64
-// banks when an operand read along its rows (A, or B with TB) has a stride of 4 more than a
-// multiple of 64 floats, and one read down its columns a stride of 16 more.
-template <int N, int R, bool TA, bool TB, int LA, int LB, int NTB, typename F>
-__device__ __forceinline__ void mmf(const float* sA, const float* sB, F&& out) {
-  constexpr int TILES = 4 * (N / 16), WAVES = NTB / 64;
-  const int wv = threadIdx.x >> 6, lm = threadIdx.x & 15, lg = (threadIdx.x >> 4) & 3;
-  for (int t = wv; t < TILES; t += WAVES) {
-    const int r0 = 16 * (t & 3), c0 = 16 * (t >> 2);
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;  // two chains of dependent steps
-#pragma unroll 8
-    for (int k = 0; k < R; k += 8) {
-      const float a0 = TA ? sA[(k + lg) * LA + r0 + lm] : sA[(r0 + lm) * LA + k + lg];
-      const float b0 = TB ? sB[(c0 + lm) * LB + k + lg] : sB[(k + lg) * LB + c0 + lm];
-      const float a1 = TA ? sA[(k + 4 + lg) * LA + r0 + lm] : sA[(r0 + lm) * LA + k + 4 + lg];
-      const float b1 = TB ? sB[(c0 + lm) * LB + k + 4 + lg] : sB[(k + 4 + lg) * LB + c0 + lm];
-      acc0 = mfma4(a0, b0, acc0);
-      acc1 = mfma4(a1, b1, acc1);
-    }
-    const f32x4 acc = acc0 + acc1;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) out(r0 + 4 * lg + r, c0 + lm, acc[r]);
-  }
-}
-
-// out(r, c, x) for x = sum_j M(r, j) S[j][c], r < 64, c < N: M is 64 x 64 in LDS (row stride
-// LM), read as M[r][j], or as M[j][r] with TRANS; S is 64 x N in LDS (row stride LS). Of the
-// NTB threads, thread t owns column t % N and the rows (t / N) * RB .. + RB - 1,
-// RB = 64 N / NTB, so the M reads of a wave are broadcasts and the S reads consecutive words.
-template <int N, int LM, int LS, bool TRANS, int NTB, typename F>
-__device__ __forceinline__ void mm64(const float* sM, const float* sS, F&& out) {
-  constexpr int NG = NTB / N, RB = BC / NG;
-  const int c = threadIdx.x % N, r0 = (threadIdx.x / N) * RB;
-  float acc[RB];
-#pragma unroll
-  for (int u = 0; u < RB; ++u) acc[u] = 0.f;
-  if constexpr (!TRANS) {
-    for (int j = 0; j < BC; j += 4) {
-      const f32x4 x = {sS[(j + 0) * LS + c], sS[(j + 1) * LS + c], sS[(j + 2) * LS + c],
-                       sS[(j + 3) * LS + c]};
-#pragma unroll
-      for (int u = 0; u < RB; ++u)
-        acc[u] += dot4(*reinterpret_cast<const f32x4*>(sM + (r0 + u) * LM + j), x);
-    }
-  } else if constexpr (RB % 4 == 0) {
-#pragma unroll 4
-    for (int j = 0; j < BC; ++j) {
-      const float x = sS[j * LS + c];
-#pragma unroll
-      for (int u = 0; u < RB; u += 4) {
-        const f32x4 m = *reinterpret_cast<const f32x4*>(sM + j * LM + r0 + u);
-        acc[u] += m[0] * x;
-        acc[u + 1] += m[1] * x;
-        acc[u + 2] += m[2] * x;
-        acc[u + 3] += m[3] * x;
-      }
-    }
-  } else {
-#pragma unroll 4
-    for (int j = 0; j < BC; ++j) {
-      const float x = sS[j * LS + c];
-#pragma unroll
-      for (int u = 0; u < RB; ++u) acc[u] += sM[j * LM + r0 + u] * x;
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < RB; ++u) out(r0 + u, c, acc[u]);
-}
-
-// out(i, j, x) for x = sum_c X[i][c] Y[j][c], i, j < 64, c < N; X, Y in LDS with row stride L
-// (L = N + 4: the 16 consecutive rows a wave reads at once fall in different banks). Of the
-// NTB threads, thread t owns rows IA (t / 16) .. + IA - 1, IA = 1024 / NTB, and the columns
-// t % 16 + 16 b, b < 4.
-template <int N, int L, int NTB, typename F>
-__device__ __forceinline__ void rowdot64(const float* sX, const float* sY, F&& out) {
-  constexpr int IA = 1024 / NTB;
-  const int i0 = IA * (threadIdx.x >> 4), jb = threadIdx.x & 15;
-  float acc[IA][4];
-#pragma unroll
-  for (int a = 0; a < IA; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
-  for (int c = 0; c < N; c += 4) {
-    f32x4 x[IA], y[4];
-#pragma unroll
-    for (int a = 0; a < IA; ++a) x[a] = *reinterpret_cast<const f32x4*>(sX + (i0 + a) * L + c);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) y[b] = *reinterpret_cast<const f32x4*>(sY + (jb + 16 * b) * L + c);
-#pragma unroll
-    for (int a = 0; a < IA; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] += dot4(x[a], y[b]);
-  }
-#pragma unroll
-  for (int a = 0; a < IA; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) out(i0 + a, jb + 16 * b, acc[a][b]);
-}
-
-// Four consecutive elements as fp32.
-__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ f32x4 load4(const bf16* p) {
-  return __builtin_convertvector(*reinterpret_cast<const bf16x4*>(p), f32x4);
-}
-
-// Rows r < len of a [T][H][N] tensor (token tok + r, head h) into LDS as fp32 (row stride L),
-// zeros past len. Four elements per load, every load of the thread issued before the first
-// store (rows past len read the last row, in bounds, and are dropped by a select).
-template <int N, int L, int NTB, typename MT>
-__device__ __forceinline__ void load_rows(float* dst, const MT* src, int64_t tok, int len, int H,
-                                          int h) {
-  constexpr int PIECES = BC * N / 4, PT = (PIECES + NTB - 1) / NTB;
-  f32x4 t[PT];
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    const int e = threadIdx.x + NTB * u;
-    const int r = e / (N / 4), c = 4 * (e % (N / 4));
-    if (PIECES % NTB == 0 || e < PIECES)
-      t[u] = load4(src + ((tok + min(r, len - 1)) * H + h) * (int64_t)N + c);
-  }
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    const int e = threadIdx.x + NTB * u;
-    const int r = e / (N / 4), c = 4 * (e % (N / 4));
-    if (PIECES % NTB == 0 || e < PIECES) {
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4*>(dst + r * L + c) = r < len ? t[u] : z;
-    }
-  }
-}
-
-// dst[r][c] = src[r][c] * 2^{dst[r][c]} for rows r < len of a [T][H][N] tensor, 0 past len
-// (e.g. k e^b from b log2 e); the loads are issued first, as in load_rows.
-template <int N, int L, int NTB, typename MT>
-__device__ __forceinline__ void mul_rows_exp2(float* dst, const MT* src, int64_t tok, int len,
-                                              int H, int h) {
-  constexpr int PIECES = BC * N / 4, PT = (PIECES + NTB - 1) / NTB;
-  f32x4 t[PT];
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    const int e = threadIdx.x + NTB * u;
-    const int r = e / (N / 4), c = 4 * (e % (N / 4));
-    if (PIECES % NTB == 0 || e < PIECES)
-      t[u] = load4(src + ((tok + min(r, len - 1)) * H + h) * (int64_t)N + c);
-  }
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    const int e = threadIdx.x + NTB * u;
-    const int r = e / (N / 4), c = 4 * (e % (N / 4));
-    if (PIECES % NTB == 0 || e < PIECES) {
-      f32x4* d = reinterpret_cast<f32x4*>(dst + r * L + c);
-      const f32x4 b = *d;
-      f32x4 x;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = r < len ? t[u][j] * exp2_f(b[j]) : 0.f;
-      *d = x;
-    }
-  }
-}
-
-// ROWS x N fp32 block (row-major, stride N) into LDS (row stride L), loads first.
-template <int N, int L, int NTB, int ROWS = BC>
-__device__ __forceinline__ void load_block(float* dst, const float* src) {
-  constexpr int PIECES = ROWS * N / 4, PT = (PIECES + NTB - 1) / NTB;
-  f32x4 t[PT];
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    const int e = threadIdx.x + NTB * u;
-    if (PIECES % NTB == 0 || e < PIECES) t[u] = load4(src + 4 * e);
-  }
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    const int e = threadIdx.x + NTB * u;
-    if (PIECES % NTB == 0 || e < PIECES)
-      *reinterpret_cast<f32x4*>(dst + (e / (N / 4)) * L + 4 * (e % (N / 4))) = t[u];
-  }
-}
-
-// Cumulative log2 decay: sB (64 x K, stride L) holds log alpha on entry, b * log2 e on exit.
-// P = NTB / K neighbouring threads share a channel: each sums its 64 / P consecutive rows, the
-// running totals of the P threads are scanned with shuffles, and each adds its prefix.
-template <int K, int L, int NTB>
-__device__ __forceinline__ void cumsum_log2(float* sB) {
-  constexpr int P = NTB / K, RP = BC / P;
-  static_assert(P >= 1 && P <= 32 && RP >= 1, "threads per channel");
-  const int c = threadIdx.x / P, part = threadIdx.x % P;
-  float x[RP];
-  float run = 0.f;
-#pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    run += sB[(part * RP + r) * L + c];
-    x[r] = run;
-  }
-  float pre = run;
-#pragma unroll
-  for (int o = 1; o < P; o <<= 1) {
-    const float y = __shfl_up(pre, o, P);
-    if (part >= o) pre += y;
-  }
-  pre -= run;  // the rows before this thread's
-#pragma unroll
-  for (int r = 0; r < RP; ++r) sB[(part * RP + r) * L + c] = (x[r] + pre) * LOG2E;
-}
-
 }  // namespace
-
-struct BwdChunk {
-  int32_t seq, tok, len, pad;
-};
 
 // seq_first[n] = the first chunk of sequence n, seq_first[N] = the number of chunks (one block)
 __global__ __launch_bounds__(NT) void bwd_seq_kernel(const int32_t* __restrict__ cu, int N,
@@ -328,7 +94,7 @@ __global__ __launch_bounds__(NT) void bwd_seq_kernel(const int32_t* __restrict__
 // chunk c: its sequence (the last n with seq_first[n] <= c), first token and length
 __global__ __launch_bounds__(NT) void bwd_chunk_kernel(const int32_t* __restrict__ cu, int N,
                                                        int64_t T, const int32_t* __restrict__ seq_first,
-                                                       int64_t ub, BwdChunk* __restrict__ chunks) {
+                                                       int64_t ub, ChunkRow* __restrict__ chunks) {
   const int64_t c = blockIdx.x * (int64_t)NT + threadIdx.x;
   if (c >= ub || c >= seq_first[N]) return;
   int lo = 0, hi = N - 1;
@@ -339,7 +105,7 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(const int32_t* __restrict
   const int64_t s1 = cu ? cu[lo + 1] : (T / N) * (lo + 1);
   const int64_t s0 = cu ? cu[lo] : (T / N) * lo;
   const int64_t tok = s0 + (c - seq_first[lo]) * BC;
-  chunks[c] = BwdChunk{lo, (int32_t)tok, (int32_t)min((int64_t)BC, s1 - tok), 0};
+  chunks[c] = ChunkRow{lo, (int32_t)tok, (int32_t)min((int64_t)BC, s1 - tok), 0};
 }
 
 // ---------------------------------------------------------------- per-chunk record
@@ -347,7 +113,7 @@ template <int K, int V, typename MT>
 __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
     const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ v,
     const MT* __restrict__ g, const MT* __restrict__ beta, int H,
-    const BwdChunk* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ rec) {
+    const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ rec) {
   using R = BRec<K, V>;
   constexpr int N1 = K > V ? K : V, L = N1 + 4, LK = K + 4;
   __shared__ __align__(16) float sQ[BC * L];   // q, then beta v
@@ -358,7 +124,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
   __shared__ float sBeta[BC];
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= *ntot) return;
-  const BwdChunk ch = chunks[c];
+  const ChunkRow ch = chunks[c];
   float* rc = rec + ((size_t)c * H + h) * R::floats;
   load_rows<K, L, NTP>(sQ, q, ch.tok, ch.len, H, h);
   load_rows<K, LK, NTP>(sK, k, ch.tok, ch.len, H, h);
@@ -452,12 +218,6 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
 // compiler neither sinks them to their use nor waits for them early, and its barriers order
 // LDS only (a full __syncthreads would also wait for the loads in flight).
 
-// the token range of sequence n
-__device__ __forceinline__ void seq_range(const int32_t* cu, int N, int64_t T, int n, int64_t* s0,
-                                          int64_t* s1) {
-  *s0 = cu ? (int64_t)cu[n] : (T / N) * n;
-  *s1 = cu ? (int64_t)cu[n + 1] : (T / N) * (n + 1);
-}
 
 // Forward in time: S_c (chunk start) and Delta = U - W S per chunk, S' = diag(gamma) S + Kt^T
 // Delta. Wave w forms rows 16 w .. 16 w + 15 of Delta and the 16-row tiles w, w + 4, .. of S'
@@ -701,7 +461,7 @@ template <int K, int V, typename MT>
 __global__ __launch_bounds__(NTG) void bwd_ga_kernel(
     const MT* __restrict__ dO, const float* __restrict__ ckS, const float* __restrict__ ckX,
     const float* __restrict__ Dl, const float* __restrict__ dDl, int H,
-    const BwdChunk* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr) {
+    const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr) {
   using G = GScr<K>;
   constexpr int L = V + 4;  // every block here is read along its rows
   __shared__ __align__(16) float sO[BC * L];
@@ -709,7 +469,7 @@ __global__ __launch_bounds__(NTG) void bwd_ga_kernel(
   __shared__ __align__(16) float sS[K * L];   // S, then X
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= *ntot) return;
-  const BwdChunk ch = chunks[c];
+  const ChunkRow ch = chunks[c];
   const size_t ch_h = (size_t)c * H + h;
   float* sc = scr + ch_h * G::floats;
   const float* S = ckS + ch_h * K * V;
@@ -753,7 +513,7 @@ template <int K, int V, typename MT>
 __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
     const MT* __restrict__ k, const MT* __restrict__ v, const MT* __restrict__ g,
     const MT* __restrict__ beta, const float* __restrict__ rec, const float* __restrict__ dDl, int H,
-    const BwdChunk* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr,
+    const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr,
     float* __restrict__ grad_v) {
   using R = BRec<K, V>;
   using G = GScr<K>;
@@ -771,7 +531,7 @@ __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
   __shared__ float sBeta[BC], sDb[BC];
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= *ntot) return;
-  const BwdChunk ch = chunks[c];
+  const ChunkRow ch = chunks[c];
   const size_t ch_h = (size_t)c * H + h;
   const float* rc = rec + ch_h * R::floats;
   float* sc = scr + ch_h * G::floats;
@@ -822,7 +582,7 @@ __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
 template <int K, int V, typename MT>
 __global__ __launch_bounds__(NTG) void bwd_gc_kernel(
     const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ g,
-    const MT* __restrict__ beta, int H, const BwdChunk* __restrict__ chunks,
+    const MT* __restrict__ beta, int H, const ChunkRow* __restrict__ chunks,
     const int32_t* __restrict__ ntot, const float* __restrict__ scr, float* __restrict__ grad_q,
     float* __restrict__ grad_k, float* __restrict__ grad_g, float* __restrict__ grad_beta) {
   using G = GScr<K>;
@@ -835,7 +595,7 @@ __global__ __launch_bounds__(NTG) void bwd_gc_kernel(
   __shared__ float sBeta[BC], sDb[BC], sRed[K];
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= *ntot) return;
-  const BwdChunk ch = chunks[c];
+  const ChunkRow ch = chunks[c];
   const size_t ch_h = (size_t)c * H + h;
   const float* sc = scr + ch_h * G::floats;
   load_rows<K, LK, NTG>(sQ, q, ch.tok, ch.len, H, h);
@@ -940,6 +700,15 @@ __global__ __launch_bounds__(NTG) void bwd_gc_kernel(
 }
 
 // ---------------------------------------------------------------- host
+hipError_t launch_chunk_rows(const int32_t* cu, int N, int64_t T, int64_t ub, int32_t* seq_first,
+                             ChunkRow* rows, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_seq_kernel, dim3(1), dim3(NT), 0, st, cu, N, T, seq_first);
+  if (ub > 0)
+    hipLaunchKernelGGL(bwd_chunk_kernel, dim3((unsigned)((ub + NT - 1) / NT)), dim3(NT), 0, st, cu,
+                       N, T, (const int32_t*)seq_first, ub, rows);
+  return hipGetLastError();
+}
+
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 template <int K, int V>
@@ -966,7 +735,7 @@ bool make_bwd_plan(int N, int64_t T, int H, int K, int V, BwdPlan* p) {
   p->off_seq = off;
   off += al256((size_t)(N + 1) * 4);
   p->off_chunks = off;
-  off += al256((size_t)ub * sizeof(BwdChunk));
+  off += al256((size_t)ub * sizeof(ChunkRow));
   p->off_rec = off;
   off += al256(rec_f * 4);
   p->off_ckS = off;
@@ -988,7 +757,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
   hipStream_t st = (hipStream_t)a.stream;
   char* ws = reinterpret_cast<char*>(a.workspace);
   int32_t* seq_first = reinterpret_cast<int32_t*>(ws + p.off_seq);
-  BwdChunk* chunks = reinterpret_cast<BwdChunk*>(ws + p.off_chunks);
+  ChunkRow* chunks = reinterpret_cast<ChunkRow*>(ws + p.off_chunks);
   float* rec = reinterpret_cast<float*>(ws + p.off_rec);
   float* ckS = reinterpret_cast<float*>(ws + p.off_ckS);
   float* ckX = reinterpret_cast<float*>(ws + p.off_ckX);
@@ -999,15 +768,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
   const int32_t* ntot = seq_first + N;
   const MT *q = (const MT*)a.q, *k = (const MT*)a.k, *v = (const MT*)a.v, *g = (const MT*)a.g,
            *beta = (const MT*)a.beta, *dO = (const MT*)a.dO;
-  hipLaunchKernelGGL(bwd_seq_kernel, dim3(1), dim3(NT), 0, st, a.cu_seqlens, N, a.total_tokens,
-                     seq_first);
-  if (p.ub > 0)
-    hipLaunchKernelGGL(bwd_chunk_kernel, dim3((unsigned)((p.ub + NT - 1) / NT)), dim3(NT), 0, st,
-                       a.cu_seqlens, N, a.total_tokens, (const int32_t*)seq_first, p.ub, chunks);
+  launch_chunk_rows(a.cu_seqlens, N, a.total_tokens, p.ub, seq_first, chunks, st);
   const dim3 cgrid((unsigned)(p.ub > 0 ? p.ub : 1), (unsigned)H);
   if (p.ub > 0)
     hipLaunchKernelGGL((bwd_prep_kernel<K, V, MT>), cgrid, dim3(NTP), 0, st, q, k, v, g, beta, H,
-                       (const BwdChunk*)chunks, ntot, rec);
+                       (const ChunkRow*)chunks, ntot, rec);
   const int chains8 = (N * H + 7) / 8 * 8;
   const dim3 sgrid((unsigned)(chains8 * (V / 16)));
   hipLaunchKernelGGL((bwd_fstate_kernel<K, V>), sgrid, dim3(NT), 0, st, (const float*)rec,
@@ -1018,12 +783,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
   if (p.ub > 0) {
     hipLaunchKernelGGL((bwd_ga_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, dO, (const float*)ckS,
                        (const float*)ckX, (const float*)Dl, (const float*)dDl, H,
-                       (const BwdChunk*)chunks, ntot, scr);
+                       (const ChunkRow*)chunks, ntot, scr);
     hipLaunchKernelGGL((bwd_gb_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, k, v, g, beta,
-                       (const float*)rec, (const float*)dDl, H, (const BwdChunk*)chunks, ntot, scr,
+                       (const float*)rec, (const float*)dDl, H, (const ChunkRow*)chunks, ntot, scr,
                        a.grad_v);
     hipLaunchKernelGGL((bwd_gc_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, q, k, g, beta, H,
-                       (const BwdChunk*)chunks, ntot, (const float*)scr, a.grad_q, a.grad_k,
+                       (const ChunkRow*)chunks, ntot, (const float*)scr, a.grad_q, a.grad_k,
                        a.grad_g, a.grad_beta);
   }
   return hipGetLastError();

@@ -106,6 +106,23 @@ bool make_scan_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, i
                     int groups, ScanPlan* p);
 hipError_t launch_chunk_fwd_scan(const ChunkArgs& a, int groups, const ScanPlan& p);
 
+// One chunk of the fp32 chunk machinery's table: its sequence, first token and length.
+struct ChunkRow {
+  int32_t seq, tok, len, pad;
+};
+// seq_first[n] = the first chunk of sequence n (seq_first[N] = the number of chunks) and the
+// rows of every chunk, for N sequences (cu_seqlens, or equal lengths T / N when cu is null).
+hipError_t launch_chunk_rows(const int32_t* cu, int N, int64_t T, int64_t ub, int32_t* seq_first,
+                             ChunkRow* rows, hipStream_t st);
+
+// Chunked forward at 256 key channels (kda_wide.hip): fp32 records for every chunk at once.
+struct WidePlan {
+  int64_t ub;  // upper bound of the number of chunks over all sequences
+  size_t off_seq, off_rows, off_rec, total_bytes;
+};
+bool make_wide_plan(int num_seqs, int64_t total_tokens, int num_heads, int dv, WidePlan* p);
+hipError_t launch_chunk_fwd_wide(const ChunkArgs& a, const WidePlan& p);
+
 // Training backward (kda_bwd.hip): per chunk and head an fp32 record, the chunk-start states,
 // the chunk-end state gradients, Delta, dDelta and the gradient kernels' scratch, for every
 // chunk at once.

@@ -87,7 +87,9 @@ def _chunk(L, **kw):
     (dict(T=-5), INVALID),
     (dict(T=1 << 31), INVALID),
     (dict(dk=48), NOT_SUPPORTED),
-    (dict(dk=256), NOT_SUPPORTED),         # the chunk path takes K <= 128
+    (dict(dk=256, opts=1), NOT_SUPPORTED),  # the wide-key path (K = 256) takes plain inputs
+    (dict(dk=256, wsb=4096), WS_SMALL),     # K = 256 is supported (the wide-key path)
+    (dict(dk=512), NOT_SUPPORTED),
     (dict(dv=512), NOT_SUPPORTED),
     (dict(opts=16), NOT_SUPPORTED),        # unknown option bit
     (dict(opts=1 << 31), NOT_SUPPORTED),
@@ -236,3 +238,15 @@ def test_bwd_workspace_size():
     assert ws(1, 65536, 4, 128, 256, 1) == 0
     assert ws(0, 100, 4, 64, 64, 1) == 0
     assert ws(1, 0, 4, 64, 64, 0) > 0
+
+
+def test_wide_key_workspace_size():
+    import torch
+    ws = lambda *a: kda.workspace_size(*a)
+    # K = 256 takes the wide-key path: fp32 records for every chunk (linear in T * H)
+    a, b = ws(1, 65536, 4, 256, 128, torch.bfloat16), ws(1, 2 * 65536, 4, 256, 128, torch.bfloat16)
+    assert a > 0 and 1.9 < b / a < 2.1
+    assert ws(1, 1000, 2, 256, 256, torch.float32) > 0
+    assert ws(1, 1000, 2, 256, 512, torch.bfloat16) == 0
+    # the scan keeps K = V <= 128
+    assert int(kda.lib().kda_chunk_fwd_scan_workspace_size(1, 4096, 2, 256, 256, 1, 4)) == 0
