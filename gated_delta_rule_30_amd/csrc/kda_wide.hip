@@ -9,9 +9,10 @@
 // over channels in A and P add up across the halves, and every other quantity is per channel),
 // in fp32 on the shared fp32 machinery of the training backward:
 //   wide_prep_kernel   per (chunk, head), 512 threads: P, W, Kt, Qe, U, gamma -> fp32 record
-//   wide_state_kernel  per (sequence, head, 16 value columns), 256 threads: the chain over the
-//                      sequence's chunks, S (256 x 16) in LDS, the record blocks staged
-//                      through LDS one after another (W, then Qe, then Kt), matrix-core steps
+//   wide_state_kernel  per (sequence, head, 16 or 32 value columns), 256 threads: the chain
+//                      over the sequence's chunks, S (256 x 16 or 32) in LDS, the record
+//                      blocks staged through LDS one after another (W, then Qe, then Kt),
+//                      matrix-core steps
 // Every product that carries in-chunk decay is formed pairwise, e^{b_i - b_j} with j <= i.
 #include "kda_fp32.h"
 
@@ -152,33 +153,36 @@ __global__ __launch_bounds__(NTP) void wide_prep_kernel(
   }
 }
 
-// The chain of one (sequence, head, 16 value columns); blockIdx = slice * chains8 + chain, so
+// The chain of one (sequence, head, CW value columns); blockIdx = slice * chains8 + chain, so
 // the slices of a chain share one XCD's L2. Per chunk: W staged, Delta = U - W S (wave w:
 // rows 16 w ..); Qe staged, O = Qe S + P Delta (wave w: rows 16 w ..); Kt staged,
-// S' = diag(gamma) S + Kt^T Delta (wave w: 16-row tiles w, w + 4, ..). The next block's loads
-// are issued before the current block's products.
-template <int V, typename MT>
+// S' = diag(gamma) S + Kt^T Delta (wave w: 16-row tiles w, w + 4, ..), each staged A operand
+// read once for the CW / 16 column blocks. The next block's loads are issued before the
+// current block's products. CW = 32 at V = 256 keeps the chains to one wave of workgroups.
+template <int V, int CW, typename MT>
 __global__ __launch_bounds__(NT) void wide_state_kernel(
     const float* __restrict__ rec, const float* __restrict__ init, const int32_t* __restrict__ cu,
     int64_t T, const int32_t* __restrict__ seq_first, int N, int H, int chains8, MT* __restrict__ o,
     float* __restrict__ fin) {
   using R = WRec<V>;
+  constexpr int NCB = CW / 16;           // 16-column blocks per workgroup
+  constexpr int LS = CW == 16 ? 16 : CW + 16;  // S and Delta rows, read down their columns
   constexpr int LR = KW + 4;    // W and Qe: read along rows (A operand rows)
   constexpr int LC = KW + 16;   // Kt: read down columns
   constexpr int PB = BC * KW / 4 / NT;   // 16-byte pieces per thread of a 64 x 256 block
   constexpr int PP = BC * BC / 4 / NT;   // ... of P
-  constexpr int TPW = KW / 16 / 4;       // S' tiles per wave
-  __shared__ __align__(16) float sS[KW * 16];
+  constexpr int TPW = KW / 16 / 4;       // S' row tiles per wave
+  __shared__ __align__(16) float sS[KW * LS];
   __shared__ __align__(16) float sOp[BC * LC];  // W, then Qe, then Kt
   __shared__ __align__(16) float sP[BC * 68];
-  __shared__ __align__(16) float sD[BC * 16];
+  __shared__ __align__(16) float sD[BC * LS];
   __shared__ float sG[KW];
   const int nh = blockIdx.x % chains8, s = blockIdx.x / chains8;
   if (nh >= N * H) return;
-  const int n = nh / H, h = nh % H, c0 = 16 * s;
+  const int n = nh / H, h = nh % H, c0 = CW * s;
   const int tid = threadIdx.x, w = tid >> 6, lm = tid & 15, lg = (tid >> 4) & 3;
-  for (int e = tid; e < KW * 16; e += NT)
-    sS[e] = init ? init[((size_t)nh * KW + e / 16) * V + c0 + e % 16] : 0.f;
+  for (int e = tid; e < KW * CW; e += NT)
+    sS[(e / CW) * LS + e % CW] = init ? init[((size_t)nh * KW + e / CW) * V + c0 + e % CW] : 0.f;
   const int first = seq_first[n], last = seq_first[n + 1];
   int64_t s0, s1;
   seq_range(cu, N, T, n, &s0, &s1);
@@ -202,9 +206,11 @@ __global__ __launch_bounds__(NT) void wide_state_kernel(
     f32x4 pp[PP];
 #pragma unroll
     for (int u = 0; u < PP; ++u) pp[u] = reinterpret_cast<const f32x4*>(rc + R::oP)[tid + NT * u];
-    float ru[4];
+    f32x4 d[NCB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ru[r] = rc[R::oU + (16 * w + 4 * lg + r) * V + c0 + lm];
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[cb][r] = rc[R::oU + (16 * w + 4 * lg + r) * V + c0 + 16 * cb + lm];
     const float rg = rc[R::oGam + tid];  // NT == KW
     lds_barrier();  // the previous chunk's reads of LDS are done
     stage(LR);
@@ -217,56 +223,80 @@ __global__ __launch_bounds__(NT) void wide_state_kernel(
     fetch(rc + R::oQe);  // in flight during Delta
     lds_barrier();
     // Delta rows 16 w .. : U - W S
-    f32x4 d = {ru[0], ru[1], ru[2], ru[3]};
-#pragma unroll 8
-    for (int mm = 0; mm < KW; mm += 4)
-      d = mfma4(-sOp[(16 * w + lm) * LR + mm + lg], sS[(mm + lg) * 16 + lm], d);
+#pragma unroll 4
+    for (int mm = 0; mm < KW; mm += 4) {
+      const float a = -sOp[(16 * w + lm) * LR + mm + lg];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sD[(16 * w + 4 * lg + r) * 16 + lm] = d[r];
+      for (int cb = 0; cb < NCB; ++cb) d[cb] = mfma4(a, sS[(mm + lg) * LS + 16 * cb + lm], d[cb]);
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sD[(16 * w + 4 * lg + r) * LS + 16 * cb + lm] = d[cb][r];
     lds_barrier();  // Delta complete, W no longer read
     stage(LR);
     fetch(rc + R::oKt);  // in flight during O
     lds_barrier();
     // O rows 16 w .. : Qe S + P Delta (P_ij = 0 for j > i: steps up to row 16 w + 15)
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int mm = 0; mm < KW; mm += 4)
-      acc = mfma4(sOp[(16 * w + lm) * LR + mm + lg], sS[(mm + lg) * 16 + lm], acc);
-    for (int j = 0; j < 16 * (w + 1); j += 4)
-      acc = mfma4(sP[(16 * w + lm) * 68 + j + lg], sD[(j + lg) * 16 + lm], acc);
+    f32x4 acc[NCB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * w + 4 * lg + r;
-      if (row < len) o[((tok + row) * H + h) * (int64_t)V + c0 + lm] = from_f32<MT>(acc[r]);
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int mm = 0; mm < KW; mm += 4) {
+      const float a = sOp[(16 * w + lm) * LR + mm + lg];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mfma4(a, sS[(mm + lg) * LS + 16 * cb + lm], acc[cb]);
     }
+    for (int j = 0; j < 16 * (w + 1); j += 4) {
+      const float a = sP[(16 * w + lm) * 68 + j + lg];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[cb] = mfma4(a, sD[(j + lg) * LS + 16 * cb + lm], acc[cb]);
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * w + 4 * lg + r;
+        if (row < len)
+          o[((tok + row) * H + h) * (int64_t)V + c0 + 16 * cb + lm] = from_f32<MT>(acc[cb][r]);
+      }
     lds_barrier();  // Qe no longer read
     stage(LC);
     lds_barrier();
     // S' tiles: diag(gamma) S + Kt^T Delta
-    f32x4 sn[TPW];
+    f32x4 sn[TPW][NCB];
 #pragma unroll
     for (int qq = 0; qq < TPW; ++qq) {
       const int mt = w + 4 * qq;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mt + 4 * lg + r;
-        sn[qq][r] = sG[row] * sS[row * 16 + lm];
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * mt + 4 * lg + r;
+          sn[qq][cb][r] = sG[row] * sS[row * LS + 16 * cb + lm];
+        }
+#pragma unroll 4
+      for (int r0 = 0; r0 < BC; r0 += 4) {
+        const float a = sOp[(r0 + lg) * LC + 16 * mt + lm];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          sn[qq][cb] = mfma4(a, sD[(r0 + lg) * LS + 16 * cb + lm], sn[qq][cb]);
       }
-#pragma unroll 8
-      for (int r0 = 0; r0 < BC; r0 += 4)
-        sn[qq] = mfma4(sOp[(r0 + lg) * LC + 16 * mt + lm], sD[(r0 + lg) * 16 + lm], sn[qq]);
     }
     lds_barrier();  // every read of S done
 #pragma unroll
     for (int qq = 0; qq < TPW; ++qq) {
       const int mt = w + 4 * qq;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sS[(16 * mt + 4 * lg + r) * 16 + lm] = sn[qq][r];
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sS[(16 * mt + 4 * lg + r) * LS + 16 * cb + lm] = sn[qq][cb][r];
     }
   }
   if (fin) {
     __syncthreads();
-    for (int e = tid; e < KW * 16; e += NT) fin[((size_t)nh * KW + e / 16) * V + c0 + e % 16] = sS[e];
+    for (int e = tid; e < KW * CW; e += NT)
+      fin[((size_t)nh * KW + e / CW) * V + c0 + e % CW] = sS[(e / CW) * LS + e % CW];
   }
 }
 
@@ -311,8 +341,9 @@ static hipError_t launch_wide_t(const ChunkArgs& a, const WidePlan& p) {
                        (const MT*)a.beta, H, (const ChunkRow*)rows, (const int32_t*)(seq_first + N),
                        rec);
   const int chains8 = (N * H + 7) / 8 * 8;
-  hipLaunchKernelGGL((wide_state_kernel<V, MT>), dim3((unsigned)(chains8 * (V / 16))), dim3(NT), 0,
-                     st, (const float*)rec, a.init_state, a.cu_seqlens, a.total_tokens,
+  constexpr int CW = V == 256 ? 32 : 16;  // value columns per chain workgroup
+  hipLaunchKernelGGL((wide_state_kernel<V, CW, MT>), dim3((unsigned)(chains8 * (V / CW))), dim3(NT),
+                     0, st, (const float*)rec, a.init_state, a.cu_seqlens, a.total_tokens,
                      (const int32_t*)seq_first, N, H, chains8, (MT*)a.o, a.final_state);
   return hipGetLastError();
 }
