@@ -4,7 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "kda_internal.h"
+#include "kda_paths.h"
 
 namespace {
 

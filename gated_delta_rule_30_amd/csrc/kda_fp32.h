@@ -4,7 +4,7 @@
 #pragma once
 
 #include "kda_device.h"
-#include "kda_internal.h"
+#include "kda_paths.h"
 
 namespace kda {
 namespace fp32 {

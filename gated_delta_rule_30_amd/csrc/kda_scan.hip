@@ -20,7 +20,7 @@
 // columns in the first, so it helps when few (sequence, head) chains leave most CUs idle
 // (one long sequence with a few heads).
 #include "kda_device.h"
-#include "kda_internal.h"
+#include "kda_paths.h"
 
 namespace kda {
 
