@@ -324,8 +324,12 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
 
 // Backwards in time: X_c (the gradient at the chunk's end), dDelta = P^T dO + Kt X per chunk,
 // X_prev = diag(gamma) X + Qe^T dO - W^T dDelta; at the end the initial state's gradient.
+// NTR threads: waves 0-3 form the four 16-row tiles of dDelta, and wave w the 16-row tiles
+// w, w + 8, .. of X_prev. Two register sets hold the records of the next two chunks, so each
+// chunk's loads have two chunks of compute to arrive in.
+constexpr int NTR = 512;
 template <int K, int V, typename MT>
-__global__ __launch_bounds__(NT) void bwd_rstate_kernel(
+__global__ __launch_bounds__(NTR) void bwd_rstate_kernel(
     const float* __restrict__ rec, const MT* __restrict__ dO, const float* __restrict__ dfin,
     const int32_t* __restrict__ cu, int64_t T, const int32_t* __restrict__ seq_first, int N, int H,
     int chains8, float* __restrict__ ckX, float* __restrict__ dDl, float* __restrict__ dinit) {
@@ -333,10 +337,12 @@ __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
   // LDS row strides as in the forward chain: Kt is read along its rows (+4), P, Qe and W
   // along their columns (+16)
   constexpr int LKt = K + 4, LC = K + 16, LP = BC + 16;
-  constexpr int PB = BC * K / 4 / NT;   // 16-byte pieces per thread of a 64 x K block
-  constexpr int PP = BC * BC / 4 / NT;  // ... of the 64 x 64 P
-  constexpr int PO = BC * 16 / NT;      // dO values per thread (the chunk's 16 columns)
-  constexpr int TPW = (K / 16 + 3) / 4;
+  constexpr int PB = BC * K / 4 / NTR;   // 16-byte pieces per thread of a 64 x K block
+  constexpr int PP = BC * BC / 4 / NTR;  // ... of the 64 x 64 P
+  constexpr int PO = BC * 16 / NTR;      // dO values per thread (the chunk's 16 columns)
+  constexpr int WV = NTR / 64;           // waves
+  constexpr int TPW = (K / 16 + WV - 1) / WV;
+  static_assert(PB >= 1 && PP >= 1 && PO >= 1, "pieces per thread");
   __shared__ __align__(16) float sX[K * 16];
   __shared__ __align__(16) float sO[BC * 16];
   __shared__ __align__(16) float sDD[BC * 16];
@@ -349,105 +355,120 @@ __global__ __launch_bounds__(NT) void bwd_rstate_kernel(
   if (nh >= N * H) return;
   const int n = nh / H, h = nh % H, c0 = 16 * s;
   const int tid = threadIdx.x, w = tid >> 6, lm = tid & 15, lg = (tid >> 4) & 3;
-  for (int e = tid; e < K * 16; e += NT)
+  for (int e = tid; e < K * 16; e += NTR)
     sX[e] = dfin ? dfin[((size_t)nh * K + e / 16) * V + c0 + e % 16] : 0.f;
   const int first = seq_first[n], last = seq_first[n + 1];
   int64_t s0, s1;
   seq_range(cu, N, T, n, &s0, &s1);
-  f32x4 rp[PP], rk[PB], rq[PB], rw[PB];
-  MT ro[PO];
-  float rg;
+  struct Regs {
+    f32x4 p[PP], k[PB], q[PB], w[PB];
+    MT o[PO];
+    float g;
+  };
+  Regs ra, rb;
   // chunk c's rows are tokens s0 + 64 (c - first) + r; rows past the sequence read its last
   // token (in bounds) and are zeroed when stored
-  auto fetch = [&](int c) {
+  auto fetch = [&](Regs& x, int c) {
     const float* rc = rec + ((size_t)c * H + h) * R::floats;
 #pragma unroll
-    for (int u = 0; u < PP; ++u) rp[u] = reinterpret_cast<const f32x4*>(rc + R::oP)[tid + NT * u];
+    for (int u = 0; u < PP; ++u) x.p[u] = reinterpret_cast<const f32x4*>(rc + R::oP)[tid + NTR * u];
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
-      rk[u] = reinterpret_cast<const f32x4*>(rc + R::oKt)[tid + NT * u];
-      rq[u] = reinterpret_cast<const f32x4*>(rc + R::oQe)[tid + NT * u];
-      rw[u] = reinterpret_cast<const f32x4*>(rc + R::oW)[tid + NT * u];
+      x.k[u] = reinterpret_cast<const f32x4*>(rc + R::oKt)[tid + NTR * u];
+      x.q[u] = reinterpret_cast<const f32x4*>(rc + R::oQe)[tid + NTR * u];
+      x.w[u] = reinterpret_cast<const f32x4*>(rc + R::oW)[tid + NTR * u];
     }
-    rg = rc[R::oGam + tid % K];
+    x.g = rc[R::oGam + tid % K];
     const int64_t tok = s0 + (int64_t)(c - first) * BC;
 #pragma unroll
     for (int u = 0; u < PO; ++u) {
-      const int e = tid + NT * u;
+      const int e = tid + NTR * u;
       const int64_t t = min(tok + e / 16, s1 - 1);
-      ro[u] = dO[(t * H + h) * (int64_t)V + c0 + e % 16];
+      x.o[u] = dO[(t * H + h) * (int64_t)V + c0 + e % 16];
     }
   };
-  if (first < last) fetch(last - 1);
-  for (int c = last - 1; c >= first; --c) {
+  // one chunk: stage its registers, start loading chunk c - 2 into them, then its products
+  auto step = [&](Regs& x, int c) {
     const int len = (int)min((int64_t)BC, s1 - (s0 + (int64_t)(c - first) * BC));
-    lds_barrier();  // the previous chunk's reads of LDS are done (the prefetch stays in flight)
+    lds_barrier();  // the previous chunk's reads of LDS are done
 #pragma unroll
     for (int u = 0; u < PP; ++u) {
-      const int e = tid + NT * u;
-      *reinterpret_cast<f32x4*>(sP + (e / (BC / 4)) * LP + 4 * (e % (BC / 4))) = rp[u];
+      const int e = tid + NTR * u;
+      *reinterpret_cast<f32x4*>(sP + (e / (BC / 4)) * LP + 4 * (e % (BC / 4))) = x.p[u];
     }
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
-      const int e = tid + NT * u, o = (e / (K / 4)), q4 = 4 * (e % (K / 4));
-      *reinterpret_cast<f32x4*>(sKt + o * LKt + q4) = rk[u];
-      *reinterpret_cast<f32x4*>(sQe + o * LC + q4) = rq[u];
-      *reinterpret_cast<f32x4*>(sW + o * LC + q4) = rw[u];
+      const int e = tid + NTR * u, o = (e / (K / 4)), q4 = 4 * (e % (K / 4));
+      *reinterpret_cast<f32x4*>(sKt + o * LKt + q4) = x.k[u];
+      *reinterpret_cast<f32x4*>(sQe + o * LC + q4) = x.q[u];
+      *reinterpret_cast<f32x4*>(sW + o * LC + q4) = x.w[u];
     }
 #pragma unroll
     for (int u = 0; u < PO; ++u) {
-      const int e = tid + NT * u;
-      sO[e] = e / 16 < len ? to_f32(ro[u]) : 0.f;
+      const int e = tid + NTR * u;
+      sO[e] = e / 16 < len ? to_f32(x.o[u]) : 0.f;
     }
-    sG[tid % K] = rg;
-    fetch(max(c - 1, first));
+    if (tid < K) sG[tid] = x.g;
+    fetch(x, max(c - 2, first));
     lds_barrier();
-    for (int e = tid; e < K * 16; e += NT)
+    for (int e = tid; e < K * 16; e += NTR)
       ckX[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sX[e];
-    // dDelta rows 16 w .. : P^T dO (P_ri = 0 for r < i, so the steps start at r = 16 w) + Kt X
-    f32x4 d = {0.f, 0.f, 0.f, 0.f};
-    for (int r0 = 16 * w; r0 < BC; r0 += 4)
-      d = mfma4(sP[(r0 + lg) * LP + 16 * w + lm], sO[(r0 + lg) * 16 + lm], d);
+    // dDelta rows 16 w .. (waves 0-3): P^T dO (P_ri = 0 for r < i, so the steps start at
+    // r = 16 w) + Kt X
+    if (w < 4) {
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      for (int r0 = 16 * w; r0 < BC; r0 += 4)
+        d = mfma4(sP[(r0 + lg) * LP + 16 * w + lm], sO[(r0 + lg) * 16 + lm], d);
 #pragma unroll 8
-    for (int mm = 0; mm < K; mm += 4)
-      d = mfma4(sKt[(16 * w + lm) * LKt + mm + lg], sX[(mm + lg) * 16 + lm], d);
+      for (int mm = 0; mm < K; mm += 4)
+        d = mfma4(sKt[(16 * w + lm) * LKt + mm + lg], sX[(mm + lg) * 16 + lm], d);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * w + 4 * lg + r;
-      sDD[row * 16 + lm] = d[r];
-      dDl[(((size_t)c * H + h) * BC + row) * V + c0 + lm] = d[r];
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * w + 4 * lg + r;
+        sDD[row * 16 + lm] = d[r];
+        dDl[(((size_t)c * H + h) * BC + row) * V + c0 + lm] = d[r];
+      }
     }
     lds_barrier();
     // X_prev tiles: diag(gamma) X + Qe^T dO - W^T dDelta
     f32x4 acc[TPW];
 #pragma unroll
-    for (int q = 0; q < TPW; ++q) {
-      const int mt = w + 4 * q;
+    for (int qq = 0; qq < TPW; ++qq) {
+      const int mt = w + WV * qq;
       if (mt < K / 16) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * mt + 4 * lg + r;
-          acc[q][r] = sG[row] * sX[row * 16 + lm];
+          acc[qq][r] = sG[row] * sX[row * 16 + lm];
         }
 #pragma unroll 8
         for (int r0 = 0; r0 < BC; r0 += 4) {
-          acc[q] = mfma4(sQe[(r0 + lg) * LC + 16 * mt + lm], sO[(r0 + lg) * 16 + lm], acc[q]);
-          acc[q] = mfma4(-sW[(r0 + lg) * LC + 16 * mt + lm], sDD[(r0 + lg) * 16 + lm], acc[q]);
+          acc[qq] = mfma4(sQe[(r0 + lg) * LC + 16 * mt + lm], sO[(r0 + lg) * 16 + lm], acc[qq]);
+          acc[qq] = mfma4(-sW[(r0 + lg) * LC + 16 * mt + lm], sDD[(r0 + lg) * 16 + lm], acc[qq]);
         }
       }
     }
     lds_barrier();
 #pragma unroll
-    for (int q = 0; q < TPW; ++q) {
-      const int mt = w + 4 * q;
+    for (int qq = 0; qq < TPW; ++qq) {
+      const int mt = w + WV * qq;
       if (mt < K / 16)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * lg + r) * 16 + lm] = acc[q][r];
+        for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * lg + r) * 16 + lm] = acc[qq][r];
     }
+  };
+  if (first < last) {
+    fetch(ra, last - 1);
+    fetch(rb, max(last - 2, first));
+  }
+  for (int c = last - 1; c >= first; c -= 2) {
+    step(ra, c);
+    if (c - 1 < first) break;
+    step(rb, c - 1);
   }
   if (dinit) {
     __syncthreads();
-    for (int e = tid; e < K * 16; e += NT)
+    for (int e = tid; e < K * 16; e += NTR)
       dinit[((size_t)nh * K + e / 16) * V + c0 + e % 16] = sX[e];
   }
 }
@@ -777,7 +798,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
   const dim3 sgrid((unsigned)(chains8 * (V / 16)));
   hipLaunchKernelGGL((bwd_fstate_kernel<K, V>), sgrid, dim3(NT), 0, st, (const float*)rec,
                      a.init_state, (const int32_t*)seq_first, N, H, chains8, ckS, Dl);
-  hipLaunchKernelGGL((bwd_rstate_kernel<K, V, MT>), sgrid, dim3(NT), 0, st, (const float*)rec, dO,
+  hipLaunchKernelGGL((bwd_rstate_kernel<K, V, MT>), sgrid, dim3(NTR), 0, st, (const float*)rec, dO,
                      a.dfinal, a.cu_seqlens, a.total_tokens, (const int32_t*)seq_first, N, H,
                      chains8, ckX, dDl, a.grad_init);
   if (p.ub > 0) {
