@@ -210,6 +210,7 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
 }
 
 // ---------------------------------------------------------------- the chains
+constexpr int NTR = 512;  // threads of a chain workgroup: 8 waves
 // One workgroup per (sequence, head, 16 value columns); the slices of one chain share
 // blockIdx % 8 (one XCD's L2) with blockIdx = slice * chains8 + chain. A chunk's record
 // blocks are loaded whole into registers (16-byte pieces, all in flight) while the chunk
@@ -220,10 +221,11 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
 
 
 // Forward in time: S_c (chunk start) and Delta = U - W S per chunk, S' = diag(gamma) S + Kt^T
-// Delta. Wave w forms rows 16 w .. 16 w + 15 of Delta and the 16-row tiles w, w + 4, .. of S'
-// with matrix-core steps over LDS operands.
+// Delta. NTR threads: waves 0-3 form the four 16-row tiles of Delta, wave w the 16-row tiles
+// w, w + 8, .. of S', with matrix-core steps over LDS operands; two register sets hold the
+// records of the next two chunks.
 template <int K, int V>
-__global__ __launch_bounds__(NT) void bwd_fstate_kernel(
+__global__ __launch_bounds__(NTR) void bwd_fstate_kernel(
     const float* __restrict__ rec, const float* __restrict__ init, const int32_t* __restrict__ seq_first,
     int N, int H, int chains8, float* __restrict__ ckS, float* __restrict__ Dl) {
   using R = BRec<K, V>;
@@ -231,8 +233,9 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
   // four lane groups consecutive columns) is padded by 4 floats, one read along its columns
   // (lane group g takes row g) by 16, so a wave's 64 reads fall in 64 different banks
   constexpr int LW = K + 4, LKT = K + 16;
-  constexpr int PB = BC * K / 4 / NT;  // 16-byte pieces per thread of a 64 x K block
-  constexpr int TPW = (K / 16 + 3) / 4;  // S' tiles per wave
+  constexpr int PB = BC * K / 4 / NTR;  // 16-byte pieces per thread of a 64 x K block
+  constexpr int WV = NTR / 64;
+  constexpr int TPW = (K / 16 + WV - 1) / WV;  // S' tiles per wave
   __shared__ __align__(16) float sS[K * 16];
   __shared__ __align__(16) float sD[BC * 16];
   __shared__ __align__(16) float sW[BC * LW];
@@ -242,40 +245,43 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
   if (nh >= N * H) return;
   const int n = nh / H, h = nh % H, c0 = 16 * s;
   const int tid = threadIdx.x, w = tid >> 6, lm = tid & 15, lg = (tid >> 4) & 3;
-  for (int e = tid; e < K * 16; e += NT)
+  for (int e = tid; e < K * 16; e += NTR)
     sS[e] = init ? init[((size_t)nh * K + e / 16) * V + c0 + e % 16] : 0.f;
   const int first = seq_first[n], last = seq_first[n + 1];
   if (first == last) return;
-  f32x4 rw[PB], rk[PB];
-  float ru[4], rg;
-  auto fetch = [&](int c) {
+  struct Regs {
+    f32x4 w[PB], k[PB];
+    float u[4], g;
+  };
+  Regs ra, rb;
+  auto fetch = [&](Regs& x, int c) {
     const float* rc = rec + ((size_t)c * H + h) * R::floats;
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
-      rw[u] = reinterpret_cast<const f32x4*>(rc + R::oW)[tid + NT * u];
-      rk[u] = reinterpret_cast<const f32x4*>(rc + R::oKt)[tid + NT * u];
+      x.w[u] = reinterpret_cast<const f32x4*>(rc + R::oW)[tid + NTR * u];
+      x.k[u] = reinterpret_cast<const f32x4*>(rc + R::oKt)[tid + NTR * u];
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ru[r] = rc[R::oU + (16 * w + 4 * lg + r) * V + c0 + lm];
-    rg = rc[R::oGam + tid % K];
+    for (int r = 0; r < 4; ++r) x.u[r] = rc[R::oU + (16 * (w & 3) + 4 * lg + r) * V + c0 + lm];
+    x.g = rc[R::oGam + tid % K];
   };
-  fetch(first);
-  for (int c = first; c < last; ++c) {
-    lds_barrier();  // the previous chunk's reads of LDS are done (the prefetch stays in flight)
+  // one chunk: stage its registers, start loading chunk c + 2 into them, then its products
+  auto step = [&](Regs& x, int c) {
+    lds_barrier();  // the previous chunk's reads of LDS are done
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
-      const int e = tid + NT * u;
-      *reinterpret_cast<f32x4*>(sW + (e / (K / 4)) * LW + 4 * (e % (K / 4))) = rw[u];
-      *reinterpret_cast<f32x4*>(sKt + (e / (K / 4)) * LKT + 4 * (e % (K / 4))) = rk[u];
+      const int e = tid + NTR * u;
+      *reinterpret_cast<f32x4*>(sW + (e / (K / 4)) * LW + 4 * (e % (K / 4))) = x.w[u];
+      *reinterpret_cast<f32x4*>(sKt + (e / (K / 4)) * LKT + 4 * (e % (K / 4))) = x.k[u];
     }
-    sG[tid % K] = rg;
-    f32x4 d = {ru[0], ru[1], ru[2], ru[3]};
-    fetch(min(c + 1, last - 1));
+    if (tid < K) sG[tid] = x.g;
+    f32x4 d = {x.u[0], x.u[1], x.u[2], x.u[3]};
+    fetch(x, min(c + 2, last - 1));
     lds_barrier();
-    for (int e = tid; e < K * 16; e += NT)
+    for (int e = tid; e < K * 16; e += NTR)
       ckS[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sS[e];
-    // Delta rows 16 w .. : U - W S (two chains of dependent steps)
-    {
+    // Delta rows 16 w .. (waves 0-3): U - W S (two chains of dependent steps)
+    if (w < 4) {
       f32x4 d1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
       for (int mm = 0; mm < K; mm += 8) {
@@ -283,19 +289,19 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
         d1 = mfma4(-sW[(16 * w + lm) * LW + mm + 4 + lg], sS[(mm + 4 + lg) * 16 + lm], d1);
       }
       d += d1;
-    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * w + 4 * lg + r;
-      sD[row * 16 + lm] = d[r];
-      Dl[(((size_t)c * H + h) * BC + row) * V + c0 + lm] = d[r];
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * w + 4 * lg + r;
+        sD[row * 16 + lm] = d[r];
+        Dl[(((size_t)c * H + h) * BC + row) * V + c0 + lm] = d[r];
+      }
     }
     lds_barrier();
     // S' tiles: diag(gamma) S + Kt^T Delta
     f32x4 acc[TPW];
 #pragma unroll
     for (int q = 0; q < TPW; ++q) {
-      const int mt = w + 4 * q;
+      const int mt = w + WV * q;
       if (mt < K / 16) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -314,11 +320,18 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
     lds_barrier();
 #pragma unroll
     for (int q = 0; q < TPW; ++q) {
-      const int mt = w + 4 * q;
+      const int mt = w + WV * q;
       if (mt < K / 16)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sS[(16 * mt + 4 * lg + r) * 16 + lm] = acc[q][r];
     }
+  };
+  fetch(ra, first);
+  fetch(rb, min(first + 1, last - 1));
+  for (int c = first; c < last; c += 2) {
+    step(ra, c);
+    if (c + 1 >= last) break;
+    step(rb, c + 1);
   }
 }
 
@@ -327,7 +340,6 @@ __global__ __launch_bounds__(NT) void bwd_fstate_kernel(
 // NTR threads: waves 0-3 form the four 16-row tiles of dDelta, and wave w the 16-row tiles
 // w, w + 8, .. of X_prev. Two register sets hold the records of the next two chunks, so each
 // chunk's loads have two chunks of compute to arrive in.
-constexpr int NTR = 512;
 template <int K, int V, typename MT>
 __global__ __launch_bounds__(NTR) void bwd_rstate_kernel(
     const float* __restrict__ rec, const MT* __restrict__ dO, const float* __restrict__ dfin,
@@ -796,7 +808,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
                        (const ChunkRow*)chunks, ntot, rec);
   const int chains8 = (N * H + 7) / 8 * 8;
   const dim3 sgrid((unsigned)(chains8 * (V / 16)));
-  hipLaunchKernelGGL((bwd_fstate_kernel<K, V>), sgrid, dim3(NT), 0, st, (const float*)rec,
+  hipLaunchKernelGGL((bwd_fstate_kernel<K, V>), sgrid, dim3(NTR), 0, st, (const float*)rec,
                      a.init_state, (const int32_t*)seq_first, N, H, chains8, ckS, Dl);
   hipLaunchKernelGGL((bwd_rstate_kernel<K, V, MT>), sgrid, dim3(NTR), 0, st, (const float*)rec, dO,
                      a.dfinal, a.cu_seqlens, a.total_tokens, (const int32_t*)seq_first, N, H,
