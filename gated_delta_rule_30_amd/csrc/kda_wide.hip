@@ -59,13 +59,14 @@ __global__ __launch_bounds__(NTP) void wide_prep_kernel(
   float* rc = rec + ((size_t)c * H + h) * R::floats;
   if (threadIdx.x < BC)
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
-  // A and P: TPR threads per row, thread (i, jq) forms j = jq + TPR u; sums over both halves
-  constexpr int TPR = NTP / BC, JPT = BC / TPR, WAVES = NTP / 64;
-  const int jq = threadIdx.x % TPR;
-  const int i = WAVES * ((threadIdx.x % 64) / TPR) + threadIdx.x / 64;
-  float a[JPT], p[JPT];
+  // A and P, summed over both halves: rows pi and 63 - pi form a pair with 65 entries j <= i;
+  // TPP threads share a pair, thread jq taking v = jq + TPP u (v <= pi: row pi, j = v; else
+  // row 63 - pi, j = v - pi - 1), so every thread has the same work
+  constexpr int TPP = NTP / (BC / 2), VPT = (BC + 1 + TPP - 1) / TPP;
+  const int pi = threadIdx.x / TPP, jq = threadIdx.x % TPP, i2 = BC - 1 - pi;
+  float a[VPT], p[VPT];
 #pragma unroll
-  for (int u = 0; u < JPT; ++u) a[u] = p[u] = 0.f;
+  for (int u = 0; u < VPT; ++u) a[u] = p[u] = 0.f;
   for (int hh = 0; hh < 2; ++hh) {
     const int c0 = hh * KH;
     load_rows<KH, LK, NTP, MT, KW>(sQ, q, ch.tok, ch.len, H, h, c0);
@@ -83,13 +84,19 @@ __global__ __launch_bounds__(NTP) void wide_prep_kernel(
     }
     if (threadIdx.x < KH) rc[R::oGam + c0 + threadIdx.x] = exp2_f(sB[(BC - 1) * LK + threadIdx.x]);
     for (int c4 = 0; c4 < KH; c4 += 4) {
-      const f32x4 qi = *reinterpret_cast<const f32x4*>(sQ + i * LK + c4);
-      const f32x4 ki = *reinterpret_cast<const f32x4*>(sK + i * LK + c4);
-      const f32x4 bi = *reinterpret_cast<const f32x4*>(sB + i * LK + c4);
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(sQ + pi * LK + c4);
+      const f32x4 k1 = *reinterpret_cast<const f32x4*>(sK + pi * LK + c4);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(sB + pi * LK + c4);
+      const f32x4 q2 = *reinterpret_cast<const f32x4*>(sQ + i2 * LK + c4);
+      const f32x4 k2 = *reinterpret_cast<const f32x4*>(sK + i2 * LK + c4);
+      const f32x4 b2 = *reinterpret_cast<const f32x4*>(sB + i2 * LK + c4);
 #pragma unroll
-      for (int u = 0; u < JPT; ++u) {
-        const int j = jq + TPR * u;
-        if (j <= i) {
+      for (int u = 0; u < VPT; ++u) {
+        const int v = jq + TPP * u;
+        if (v <= BC) {
+          const bool lo = v <= pi;
+          const int j = lo ? v : v - pi - 1;
+          const f32x4 qi = lo ? q1 : q2, ki = lo ? k1 : k2, bi = lo ? b1 : b2;
           const f32x4 kj = *reinterpret_cast<const f32x4*>(sK + j * LK + c4);
           const f32x4 bj = *reinterpret_cast<const f32x4*>(sB + j * LK + c4);
           f32x4 w;
@@ -103,11 +110,17 @@ __global__ __launch_bounds__(NTP) void wide_prep_kernel(
     lds_barrier();  // the half's reads done before the next half overwrites it
   }
 #pragma unroll
-  for (int u = 0; u < JPT; ++u) {
-    const int j = jq + TPR * u;
-    sA[i * 68 + j] = j < i ? sBeta[i] * a[u] : 0.f;
-    rc[R::oP + i * BC + j] = j <= i ? p[u] : 0.f;
+  for (int u = 0; u < VPT; ++u) {
+    const int v = jq + TPP * u;
+    if (v <= BC) {
+      const bool lo = v <= pi;
+      const int i = lo ? pi : i2, j = lo ? v : v - pi - 1;
+      sA[i * 68 + j] = j < i ? sBeta[i] * a[u] : 0.f;
+      rc[R::oP + i * BC + j] = p[u];
+    }
   }
+  for (int e = threadIdx.x; e < BC * BC; e += NTP)  // P's upper triangle
+    if (e % BC > e / BC) rc[R::oP + e] = 0.f;
   lds_barrier();
   // T = (I + A)^{-1} by forward substitution, one column per thread
   if (threadIdx.x < BC) {
