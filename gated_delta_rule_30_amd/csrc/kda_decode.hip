@@ -5,9 +5,9 @@
 //   u  = S'^T k                                (prediction of the decayed memory along k)
 //   S  = S' + beta k (v - u)^T                 (erase along k and write v)
 //   o  = S^T q = S'^T q + beta (k.q) (v - u)   (read after the write; explainer "Step 4")
-// All four are fused into one pass: each workgroup streams its 64 KB state (K=V=128) from
-// HBM once into registers, reduces u and S'^T q across row groups through LDS, and writes
-// the updated state back once. The state is touched exactly once per step, so loads and
+// All four are fused into one pass: each workgroup streams its slice of the state from HBM
+// once into registers, reduces u and S'^T q across the key channels, and writes the updated
+// slice back once. The state is touched exactly once per step, so loads and
 // stores are non-temporal. The kernel is HBM-bound: 2*K*V*4 bytes of state traffic per head.
 // Input options: a scalar gate per head, alpha = sigmoid(z) from gate logits, beta from
 // logits, and unit-norm q and k. Since u, S'^T q and k.q are linear in k and q, the sums are
@@ -40,20 +40,44 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, f32x4 x) {
   *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
 }
 
-// Threads per head: up to 1024, one per 16-byte state vector (K*V/4) where that is fewer. With
-// K=V=128 each thread holds four vectors of one column group; measured on MI355X the whole
-// 8192-head step streams at about 6.1 TB/s with 1024 threads, 5.7 with 512 and 5.6 with 256 (the
-// barrier between the loads and the stores idles a smaller workgroup's share of the CU).
+// A workgroup takes one (sequence, head) and a slice of VS value columns (the columns of S evolve
+// independently, and u, S'^T q and k.q are sums over the key channels only). Thread (rg, cg)
+// holds the 4 columns of column group cg in rows rg, rg + RG, rg + 2 RG, ... The partial sums
+// meet in two steps: across the row groups of one wave by lane exchanges, then across the waves
+// through LDS, so a thread adds one partial per wave, not one per row group.
+// (VS, TPB) per shape were measured on MI355X with 512 MB of state per step: every shape then
+// streams at 76-82% of the HBM peak. Two rows per thread and 512-1024 threads are best almost
+// everywhere; a whole 128 x 128 head in one workgroup with 4 rows per thread ran 2% slower than
+// two slices of 64 columns, and a 256 x 256 head in one workgroup (16 rows per thread) spilled.
+constexpr int decode_vs(int K, int V) {
+  return V == 32 ? 32 : V == 64 ? 64 : V == 128 ? (K == 128 ? 64 : K == 256 ? 32 : 128) : 128;
+}
+constexpr int decode_tpb(int K, int V) {
+  return K == 32    ? (V == 32 ? 128 : V == 64 ? 256 : 512)
+         : K == 64  ? (V == 32 ? 256 : V == 64 ? 512 : V == 128 ? 1024 : 512)
+         : K == 128 ? (V == 32 ? 512 : 1024)
+                    : 1024;
+}
+
 template <int K, int V>
 struct DecodeShape {
-  static constexpr int TPB = K * V / 4 < 1024 ? K * V / 4 : 1024;
-  static constexpr int CG = V / 4;      // column groups of 4 value columns
-  static constexpr int RG = TPB / CG;   // row groups
-  static constexpr int RPT = K / RG;    // rows per thread
-  static_assert(RPT >= 1 && RG * CG == TPB, "decode shape");
+  static constexpr int VS = decode_vs(K, V);   // value columns per workgroup
+  static constexpr int NSL = V / VS;           // workgroups per head
+  static constexpr int TPB = decode_tpb(K, V);
+  static constexpr int CG = VS / 4;            // column groups of 4 value columns
+  static constexpr int RG = TPB / CG;          // row groups
+  static constexpr int RPT = K / RG;           // rows per thread
+  static constexpr int RGW = CG < 64 ? 64 / CG : 1;  // row groups per wave
+  static constexpr int NW = RG / RGW;          // partials per column group after the lane step
+  static_assert(NSL * VS == V && RG * CG == TPB && RPT * RG == K && RPT >= 1 && NW >= 1,
+                "decode shape");
 };
 
-// Column group cg holds 4 value columns; row group rg holds rows rg, rg + RG, rg + 2 RG, ...
+__device__ __forceinline__ f32x4 shfl_xor4(f32x4 x, int off) {
+  return f32x4{__shfl_xor(x[0], off), __shfl_xor(x[1], off), __shfl_xor(x[2], off),
+               __shfl_xor(x[3], off)};
+}
+
 template <int K, int V, typename TI>
 __global__ __launch_bounds__((DecodeShape<K, V>::TPB)) void decode_step_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
@@ -63,15 +87,18 @@ __global__ __launch_bounds__((DecodeShape<K, V>::TPB)) void decode_step_kernel(
   constexpr int CG = DS::CG;
   constexpr int RG = DS::RG;
   constexpr int RPT = DS::RPT;
-  const int head = blockIdx.x;
+  constexpr int RGW = DS::RGW;
+  const int head = blockIdx.x / DS::NSL;
+  const int col0 = (blockIdx.x % DS::NSL) * DS::VS;
   const int tid = threadIdx.x;
   const int cg = tid % CG;
   const int rg = tid / CG;
 
-  f32x4* S = reinterpret_cast<f32x4*>(state + (size_t)head * K * V);
+  // column group cg of this slice, row 0; row r is V / 4 vectors further
+  f32x4* S = reinterpret_cast<f32x4*>(state + (size_t)head * K * V + col0) + cg;
   f32x4 s[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(&S[(rg + RG * i) * CG + cg]);
+  for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(&S[(rg + RG * i) * (V / 4)]);
 
   const TI* qh = q + (size_t)head * K;
   const TI* kh = k + (size_t)head * K;
@@ -116,18 +143,27 @@ __global__ __launch_bounds__((DecodeShape<K, V>::TPB)) void decode_step_kernel(
   float b = to_f32(beta[head]);
   if (opts & OPT_BETA_LOGITS) b = sigmoid_f(b);
 
-  __shared__ f32x4 red_u[RG][CG];
-  __shared__ f32x4 red_w[RG][CG];
-  __shared__ float red_kq[RG];
-  red_u[rg][cg] = pu;
-  red_w[rg][cg] = pw;
-  if (cg == 0) red_kq[rg] = pkq;
+  // row groups of one wave are the lanes cg + CG j: add them up by lane exchanges
+#pragma unroll
+  for (int off = CG; off < 64; off <<= 1) {
+    pu += shfl_xor4(pu, off);
+    pw += shfl_xor4(pw, off);
+    pkq += __shfl_xor(pkq, off);
+  }
+  __shared__ f32x4 red_u[DS::NW][CG];
+  __shared__ f32x4 red_w[DS::NW][CG];
+  __shared__ float red_kq[DS::NW];
+  if (rg % RGW == 0) {
+    red_u[rg / RGW][cg] = pu;
+    red_w[rg / RGW][cg] = pw;
+    if (cg == 0) red_kq[rg / RGW] = pkq;
+  }
   __syncthreads();
 
   f32x4 u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
   float kq = 0.f;
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
+  for (int r = 0; r < DS::NW; ++r) {
     u += red_u[r][cg];
     w += red_w[r][cg];
     kq += red_kq[r];
@@ -135,20 +171,21 @@ __global__ __launch_bounds__((DecodeShape<K, V>::TPB)) void decode_step_kernel(
   u *= nk;
   w *= nq;
   kq *= nk * nq;
-  const f32x4 vv = load4(v + (size_t)head * V + 4 * cg);
+  const f32x4 vv = load4(v + (size_t)head * V + col0 + 4 * cg);
   const f32x4 d = b * (vv - u);
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     f32x4 ns = a[i] * s[i] + (kk[i] * nk) * d;
-    __builtin_nontemporal_store(ns, &S[(rg + RG * i) * CG + cg]);
+    __builtin_nontemporal_store(ns, &S[(rg + RG * i) * (V / 4)]);
   }
-  if (rg == 0) store4(o + (size_t)head * V + 4 * cg, w + kq * d);
+  if (rg == 0) store4(o + (size_t)head * V + col0 + 4 * cg, w + kq * d);
 }
 
 template <int K, int V, typename TI>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int heads = a.num_seqs * a.num_heads;
-  hipLaunchKernelGGL((decode_step_kernel<K, V, TI>), dim3(heads), dim3(DecodeShape<K, V>::TPB), 0,
+  hipLaunchKernelGGL((decode_step_kernel<K, V, TI>), dim3(heads * DecodeShape<K, V>::NSL),
+                     dim3(DecodeShape<K, V>::TPB), 0,
                      (hipStream_t)a.stream, (const TI*)a.q, (const TI*)a.k, (const TI*)a.v,
                      (const TI*)a.g, (const TI*)a.beta, a.state, (TI*)a.o, a.options);
   return hipGetLastError();

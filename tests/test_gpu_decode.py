@@ -43,6 +43,16 @@ def test_decode_matches_oracle(dtype, K, V, N, H, steps):
     _run_steps(N, H, K, V, dtype, steps, seed=K + V + N)
 
 
+@pytest.mark.parametrize("K", [32, 64, 128, 256])
+@pytest.mark.parametrize("V", [32, 64, 128, 256])
+def test_decode_every_head_shape(K, V):
+    """Every (K, V) the library dispatches: each has its own workgroup shape and value-column
+    slicing, so each is checked on its own (two steps, bf16 and fp32 alternating)."""
+    dtype = torch.bfloat16 if (K + V) % 64 == 0 and K != V else torch.float32
+    print("decode shape", K, V, dtype, flush=True)
+    _run_steps(2, 3, K, V, dtype, 2, seed=7 * K + V)
+
+
 def test_decode_full_size_256x32():
     """The serving shape: 256 sequences x 32 heads, K=V=128, fp32 state ~ 0.1 N(0,1), bf16
     step inputs; four consecutive steps checked on every head."""
