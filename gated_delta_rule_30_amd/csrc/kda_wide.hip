@@ -5,8 +5,8 @@
 // e^{b_last}, A = strict_lower(diag(beta) (k k^T weighted by e^{b_i - b_j})), T = (I + A)^{-1},
 // W = T diag(beta) (k e^b), U = T diag(beta) V and P = lower(q k^T weighted by e^{b_i - b_j}).
 // kda_chunk.hip's prep kernel keeps K-wide operand tiles in LDS, which at K = 256 would not
-// fit; here the per-chunk kernel works over the key channels in two halves of 128 (the sums
-// over channels in A and P add up across the halves, and every other quantity is per channel),
+// fit; here the per-chunk kernel works over the key channels in four quarters of 64 (the sums
+// over channels in A and P add up across the quarters, and every other quantity is per channel),
 // in fp32 on the shared fp32 machinery of the training backward:
 //   wide_prep_kernel   per (chunk, head), 512 threads: P, W, Kt, Qe, U, gamma -> fp32 record
 //   wide_state_kernel  per (sequence, head, 16 or 32 value columns), 256 threads: the chain
@@ -23,7 +23,7 @@ using namespace fp32;
 namespace {
 
 constexpr int KW = 256;     // key channels
-constexpr int KH = KW / 2;  // channels per half
+constexpr int KQ = KW / 4;  // channels per quarter (the record kernel's LDS tiles)
 
 // per-(chunk, head) fp32 record, row-major blocks
 template <int V>
@@ -40,18 +40,19 @@ struct WRec {
 }  // namespace
 
 template <int V, typename MT>
-__global__ __launch_bounds__(NTP) void wide_prep_kernel(
+__global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
     const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ v,
     const MT* __restrict__ g, const MT* __restrict__ beta, int H,
     const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ rec) {
   using R = WRec<V>;
-  constexpr int LK = KH + 4;                 // rows of a channel half
-  constexpr int VH = V > KH ? KH : V, LV = VH + 4;
-  __shared__ __align__(16) float sQ[BC * LK];  // q (half), then beta v (half)
-  __shared__ __align__(16) float sK[BC * LK];  // k (half), then beta k e^b (half)
-  __shared__ __align__(16) float sB[BC * LK];  // b log2 e (half)
-  __shared__ __align__(16) float sA[BC * 68];  // A (strict lower)
-  __shared__ __align__(16) float sT[BC * 68];  // T = (I + A)^{-1}
+  constexpr int LK = KQ + 4;                 // rows of a channel quarter
+  constexpr int VH = V > KQ ? KQ : V, LV = VH + 4;
+  // 70 KB in all and at most 128 VGPRs (4 waves per SIMD), so that two workgroups share a CU
+  __shared__ __align__(16) float sQ[BC * LK];  // q (quarter), then beta v (quarter)
+  __shared__ __align__(16) float sK[BC * LK];  // k (quarter)
+  __shared__ __align__(16) float sB[BC * LK];  // b log2 e (quarter), then beta k e^b (quarter)
+  __shared__ __align__(16) float sA[BC * 68];  // A (strict lower), then T = (I + A)^{-1}
+  float* sT = sA;
   __shared__ float sBeta[BC];
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= *ntot) return;
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(NTP) void wide_prep_kernel(
   float* rc = rec + ((size_t)c * H + h) * R::floats;
   if (threadIdx.x < BC)
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
-  // A and P, summed over both halves: rows pi and 63 - pi form a pair with 65 entries j <= i;
+  // A and P, summed over the four quarters: rows pi and 63 - pi form a pair with 65 entries j <= i;
   // TPP threads share a pair, thread jq taking v = jq + TPP u (v <= pi: row pi, j = v; else
   // row 63 - pi, j = v - pi - 1), so every thread has the same work
   constexpr int TPP = NTP / (BC / 2), VPT = (BC + 1 + TPP - 1) / TPP;
@@ -67,23 +68,23 @@ __global__ __launch_bounds__(NTP) void wide_prep_kernel(
   float a[VPT], p[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) a[u] = p[u] = 0.f;
-  for (int hh = 0; hh < 2; ++hh) {
-    const int c0 = hh * KH;
-    load_rows<KH, LK, NTP, MT, KW>(sQ, q, ch.tok, ch.len, H, h, c0);
-    load_rows<KH, LK, NTP, MT, KW>(sK, k, ch.tok, ch.len, H, h, c0);
-    load_rows<KH, LK, NTP, MT, KW>(sB, g, ch.tok, ch.len, H, h, c0);
+  for (int hh = 0; hh < KW / KQ; ++hh) {
+    const int c0 = hh * KQ;
+    load_rows<KQ, LK, NTP, MT, KW>(sQ, q, ch.tok, ch.len, H, h, c0);
+    load_rows<KQ, LK, NTP, MT, KW>(sK, k, ch.tok, ch.len, H, h, c0);
+    load_rows<KQ, LK, NTP, MT, KW>(sB, g, ch.tok, ch.len, H, h, c0);
     lds_barrier();
-    cumsum_log2<KH, LK, NTP>(sB);
+    cumsum_log2<KQ, LK, NTP>(sB);
     lds_barrier();
-    // Qe, Kt, gamma of the half (rows past len hold q = k = 0, and b stays at its last value)
-    for (int e = threadIdx.x; e < BC * KH; e += NTP) {
-      const int r = e / KH, cc = e % KH;
+    // Qe, Kt, gamma of the quarter (rows past len hold q = k = 0, and b stays at its last value)
+    for (int e = threadIdx.x; e < BC * KQ; e += NTP) {
+      const int r = e / KQ, cc = e % KQ;
       const float br = sB[r * LK + cc], bl = sB[(BC - 1) * LK + cc];
       rc[R::oQe + r * KW + c0 + cc] = sQ[r * LK + cc] * exp2_f(br);
       rc[R::oKt + r * KW + c0 + cc] = sK[r * LK + cc] * exp2_f(bl - br);
     }
-    if (threadIdx.x < KH) rc[R::oGam + c0 + threadIdx.x] = exp2_f(sB[(BC - 1) * LK + threadIdx.x]);
-    for (int c4 = 0; c4 < KH; c4 += 4) {
+    if (threadIdx.x < KQ) rc[R::oGam + c0 + threadIdx.x] = exp2_f(sB[(BC - 1) * LK + threadIdx.x]);
+    for (int c4 = 0; c4 < KQ; c4 += 4) {
       const f32x4 q1 = *reinterpret_cast<const f32x4*>(sQ + pi * LK + c4);
       const f32x4 k1 = *reinterpret_cast<const f32x4*>(sK + pi * LK + c4);
       const f32x4 b1 = *reinterpret_cast<const f32x4*>(sB + pi * LK + c4);
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(NTP) void wide_prep_kernel(
         }
       }
     }
-    lds_barrier();  // the half's reads done before the next half overwrites it
+    lds_barrier();  // the quarter's reads done before the next quarter overwrites it
   }
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
@@ -122,7 +123,8 @@ __global__ __launch_bounds__(NTP) void wide_prep_kernel(
   for (int e = threadIdx.x; e < BC * BC; e += NTP)  // P's upper triangle
     if (e % BC > e / BC) rc[R::oP + e] = 0.f;
   lds_barrier();
-  // T = (I + A)^{-1} by forward substitution, one column per thread
+  // T = (I + A)^{-1} by forward substitution, one column per thread of wave 0; T overwrites A
+  // after the wave's last read of it (a wave's LDS accesses take effect in program order)
   if (threadIdx.x < BC) {
     const int m = threadIdx.x;
     float x[BC];
@@ -137,18 +139,18 @@ __global__ __launch_bounds__(NTP) void wide_prep_kernel(
     for (int r = 0; r < BC; ++r) sT[r * 68 + m] = x[r];
   }
   lds_barrier();
-  // W = T diag(beta) (k e^b), half by half
-  for (int hh = 0; hh < 2; ++hh) {
-    const int c0 = hh * KH;
-    load_rows<KH, LK, NTP, MT, KW>(sB, g, ch.tok, ch.len, H, h, c0);
+  // W = T diag(beta) (k e^b), quarter by quarter
+  for (int hh = 0; hh < KW / KQ; ++hh) {
+    const int c0 = hh * KQ;
+    load_rows<KQ, LK, NTP, MT, KW>(sB, g, ch.tok, ch.len, H, h, c0);
     lds_barrier();
-    cumsum_log2<KH, LK, NTP>(sB);
+    cumsum_log2<KQ, LK, NTP>(sB);
     lds_barrier();
-    mul_rows_exp2<KH, LK, NTP, MT, KW>(sB, k, ch.tok, ch.len, H, h, c0);
+    mul_rows_exp2<KQ, LK, NTP, MT, KW>(sB, k, ch.tok, ch.len, H, h, c0);
     lds_barrier();
-    for (int e = threadIdx.x; e < BC * KH; e += NTP) sB[(e / KH) * LK + e % KH] *= sBeta[e / KH];
+    for (int e = threadIdx.x; e < BC * KQ; e += NTP) sB[(e / KQ) * LK + e % KQ] *= sBeta[e / KQ];
     lds_barrier();
-    mmf<KH, BC, false, false, 68, LK, NTP>(sT, sB, [&](int r, int cc, float x) {
+    mmf<KQ, BC, false, false, 68, LK, NTP>(sT, sB, [&](int r, int cc, float x) {
       rc[R::oW + r * KW + c0 + cc] = x;
     });
     lds_barrier();
