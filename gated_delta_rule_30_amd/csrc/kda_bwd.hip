@@ -110,53 +110,58 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(const int32_t* __restrict
 
 // ---------------------------------------------------------------- per-chunk record
 template <int K, int V, typename MT>
-__global__ __launch_bounds__(NTP) void bwd_prep_kernel(
+__global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
     const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ v,
     const MT* __restrict__ g, const MT* __restrict__ beta, int H,
     const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ rec) {
   using R = BRec<K, V>;
-  constexpr int N1 = K > V ? K : V, L = N1 + 4, LK = K + 4;
-  __shared__ __align__(16) float sQ[BC * L];   // q, then beta v
-  __shared__ __align__(16) float sK[BC * LK];  // k, then beta k e^b
-  __shared__ __align__(16) float sB[BC * LK];  // b log2 e
-  __shared__ __align__(16) float sA[BC * 68];  // A (strict lower)
-  __shared__ __align__(16) float sT[BC * 68];  // T = (I + A)^{-1}
+  // The key channels are taken in parts of KC and the value columns in parts of VC (at most
+  // 64 each): the sums over channels in A and P add up across the parts, and every other
+  // quantity is per channel or per column. With T written over A the LDS stays at 70 KB and
+  // the kernel at 128 VGPRs, so two workgroups (16 waves) share a CU.
+  constexpr int KC = K > 64 ? 64 : K, VC = V > 64 ? 64 : V;
+  constexpr int LK = KC + 4, LV = VC + 4, LQ = LK > LV ? LK : LV;
+  __shared__ __align__(16) float sQ[BC * LQ];  // q (part), then beta v (part)
+  __shared__ __align__(16) float sK[BC * LK];  // k (part)
+  __shared__ __align__(16) float sB[BC * LK];  // b log2 e (part), then beta k e^b (part)
+  __shared__ __align__(16) float sA[BC * 68];  // A (strict lower), then T = (I + A)^{-1}
   __shared__ float sBeta[BC];
+  float* sT = sA;
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= *ntot) return;
   const ChunkRow ch = chunks[c];
   float* rc = rec + ((size_t)c * H + h) * R::floats;
-  load_rows<K, L, NTP>(sQ, q, ch.tok, ch.len, H, h);
-  load_rows<K, LK, NTP>(sK, k, ch.tok, ch.len, H, h);
-  load_rows<K, LK, NTP>(sB, g, ch.tok, ch.len, H, h);
   if (threadIdx.x < BC)
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
-  lds_barrier();
-  cumsum_log2<K, LK, NTP>(sB);
-  lds_barrier();
-  // Qe, Kt, gamma (rows past len hold q = k = 0, and b stays at its last value)
-  for (int e = threadIdx.x; e < BC * K; e += NTP) {
-    const int r = e / K, cc = e % K;
-    const float br = sB[r * LK + cc], bl = sB[(BC - 1) * LK + cc];
-    rc[R::oQe + e] = sQ[r * L + cc] * exp2_f(br);
-    rc[R::oKt + e] = sK[r * LK + cc] * exp2_f(bl - br);
-  }
-  if (threadIdx.x < K) rc[R::oGam + threadIdx.x] = exp2_f(sB[(BC - 1) * LK + threadIdx.x]);
   // A_ij = beta_i sum_c k_ic k_jc e^{b_ic - b_jc} (j < i) and P_ij = sum_c q_ic k_jc e^{..} (j <= i).
   // Rows pi and 63 - pi form a pair with 65 entries j <= i between them; TPP threads share a
   // pair, thread jq taking the entries v = jq + TPP u (v <= pi: row pi, j = v; else row
   // 63 - pi, j = v - pi - 1), so every thread has the same work and no entry is masked off.
-  {
-    constexpr int TPP = NTP / (BC / 2), VPT = (BC + 1 + TPP - 1) / TPP;
-    const int pi = threadIdx.x / TPP, jq = threadIdx.x % TPP, i2 = BC - 1 - pi;
-    float a[VPT], p[VPT];
+  constexpr int TPP = NTP / (BC / 2), VPT = (BC + 1 + TPP - 1) / TPP;
+  const int pi = threadIdx.x / TPP, jq = threadIdx.x % TPP, i2 = BC - 1 - pi;
+  float a[VPT], p[VPT];
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) a[u] = p[u] = 0.f;
-    for (int c4 = 0; c4 < K; c4 += 4) {
-      const f32x4 q1 = *reinterpret_cast<const f32x4*>(sQ + pi * L + c4);
+  for (int u = 0; u < VPT; ++u) a[u] = p[u] = 0.f;
+  for (int c0 = 0; c0 < K; c0 += KC) {
+    load_rows<KC, LQ, NTP, MT, K>(sQ, q, ch.tok, ch.len, H, h, c0);
+    load_rows<KC, LK, NTP, MT, K>(sK, k, ch.tok, ch.len, H, h, c0);
+    load_rows<KC, LK, NTP, MT, K>(sB, g, ch.tok, ch.len, H, h, c0);
+    lds_barrier();
+    cumsum_log2<KC, LK, NTP>(sB);
+    lds_barrier();
+    // Qe, Kt, gamma of the part (rows past len hold q = k = 0, and b stays at its last value)
+    for (int e = threadIdx.x; e < BC * KC; e += NTP) {
+      const int r = e / KC, cc = e % KC;
+      const float br = sB[r * LK + cc], bl = sB[(BC - 1) * LK + cc];
+      rc[R::oQe + r * K + c0 + cc] = sQ[r * LQ + cc] * exp2_f(br);
+      rc[R::oKt + r * K + c0 + cc] = sK[r * LK + cc] * exp2_f(bl - br);
+    }
+    if (threadIdx.x < KC) rc[R::oGam + c0 + threadIdx.x] = exp2_f(sB[(BC - 1) * LK + threadIdx.x]);
+    for (int c4 = 0; c4 < KC; c4 += 4) {
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(sQ + pi * LQ + c4);
       const f32x4 k1 = *reinterpret_cast<const f32x4*>(sK + pi * LK + c4);
       const f32x4 b1 = *reinterpret_cast<const f32x4*>(sB + pi * LK + c4);
-      const f32x4 q2 = *reinterpret_cast<const f32x4*>(sQ + i2 * L + c4);
+      const f32x4 q2 = *reinterpret_cast<const f32x4*>(sQ + i2 * LQ + c4);
       const f32x4 k2 = *reinterpret_cast<const f32x4*>(sK + i2 * LK + c4);
       const f32x4 b2 = *reinterpret_cast<const f32x4*>(sB + i2 * LK + c4);
 #pragma unroll
@@ -176,21 +181,23 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int v = jq + TPP * u;
-      if (v <= BC) {
-        const bool lo = v <= pi;
-        const int i = lo ? pi : i2, j = lo ? v : v - pi - 1;
-        sA[i * 68 + j] = j < i ? sBeta[i] * a[u] : 0.f;
-        rc[R::oP + i * BC + j] = p[u];
-      }
-    }
-    for (int e = threadIdx.x; e < BC * BC; e += NTP)  // P's upper triangle
-      if (e % BC > e / BC) rc[R::oP + e] = 0.f;
+    lds_barrier();  // the part's reads done before the next part overwrites it
   }
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int v = jq + TPP * u;
+    if (v <= BC) {
+      const bool lo = v <= pi;
+      const int i = lo ? pi : i2, j = lo ? v : v - pi - 1;
+      sA[i * 68 + j] = j < i ? sBeta[i] * a[u] : 0.f;
+      rc[R::oP + i * BC + j] = p[u];
+    }
+  }
+  for (int e = threadIdx.x; e < BC * BC; e += NTP)  // P's upper triangle
+    if (e % BC > e / BC) rc[R::oP + e] = 0.f;
   lds_barrier();
-  // T = (I + A)^{-1} by forward substitution, one column per thread
+  // T = (I + A)^{-1} by forward substitution, one column per thread of wave 0; T overwrites A
+  // after the wave's last read of it (a wave's LDS accesses take effect in program order)
   if (threadIdx.x < BC) {
     const int m = threadIdx.x;
     float x[BC];
@@ -207,18 +214,33 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(
       rc[R::oT + i * BC + m] = x[i];
     }
   }
-  // beta k e^b and beta v replace k and q
-  for (int e = threadIdx.x; e < BC * K; e += NTP) {
-    const int r = e / K, cc = e % K;
-    sK[r * LK + cc] *= sBeta[r] * exp2_f(sB[r * LK + cc]);
+  lds_barrier();
+  // W = T diag(beta) (k e^b), part by part
+  for (int c0 = 0; c0 < K; c0 += KC) {
+    load_rows<KC, LK, NTP, MT, K>(sB, g, ch.tok, ch.len, H, h, c0);
+    lds_barrier();
+    cumsum_log2<KC, LK, NTP>(sB);
+    lds_barrier();
+    mul_rows_exp2<KC, LK, NTP, MT, K>(sB, k, ch.tok, ch.len, H, h, c0);
+    lds_barrier();
+    for (int e = threadIdx.x; e < BC * KC; e += NTP) sB[(e / KC) * LK + e % KC] *= sBeta[e / KC];
+    lds_barrier();
+    mmf<KC, BC, false, false, 68, LK, NTP>(sT, sB, [&](int r, int cc, float x) {
+      rc[R::oW + r * K + c0 + cc] = x;
+    });
+    lds_barrier();
   }
-  lds_barrier();
-  load_rows<V, L, NTP>(sQ, v, ch.tok, ch.len, H, h);
-  lds_barrier();
-  for (int e = threadIdx.x; e < BC * V; e += NTP) sQ[(e / V) * L + e % V] *= sBeta[e / V];
-  lds_barrier();
-  mmf<K, BC, false, false, 68, LK, NTP>(sT, sK, [&](int r, int cc, float x) { rc[R::oW + r * K + cc] = x; });
-  mmf<V, BC, false, false, 68, L, NTP>(sT, sQ, [&](int r, int cc, float x) { rc[R::oU + r * V + cc] = x; });
+  // U = T diag(beta) V, part by part
+  for (int c0 = 0; c0 < V; c0 += VC) {
+    load_rows<VC, LV, NTP, MT, V>(sQ, v, ch.tok, ch.len, H, h, c0);
+    lds_barrier();
+    for (int e = threadIdx.x; e < BC * VC; e += NTP) sQ[(e / VC) * LV + e % VC] *= sBeta[e / VC];
+    lds_barrier();
+    mmf<VC, BC, false, false, 68, LV, NTP>(sT, sQ, [&](int r, int cc, float x) {
+      rc[R::oU + r * V + c0 + cc] = x;
+    });
+    lds_barrier();
+  }
 }
 
 // ---------------------------------------------------------------- the chains
