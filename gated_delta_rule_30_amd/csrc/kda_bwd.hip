@@ -525,12 +525,17 @@ __global__ __launch_bounds__(NTR) void bwd_rstate_kernel(
 // (a) dP = lower(dO Delta^T); with S (chunk start) and X (chunk end) streamed from HBM:
 //     dO S^T, dW = -dDelta S^T, Delta X^T and rowsum(S * X)
 template <int K, int V, typename MT>
-__global__ __launch_bounds__(NTG) void bwd_ga_kernel(
+__global__ __launch_bounds__(NTGA, 8) void bwd_ga_kernel(
     const MT* __restrict__ dO, const float* __restrict__ ckS, const float* __restrict__ ckX,
     const float* __restrict__ Dl, const float* __restrict__ dDl, int H,
     const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr) {
   using G = GScr<K>;
-  constexpr int L = V + 4;  // every block here is read along its rows
+  // Every product here sums over the value columns; they run over parts of VC columns with
+  // the partial tiles kept in registers, so LDS holds 64 x VC and K x VC blocks (70 KB at
+  // K = V = 128) and two workgroups share a CU.
+  constexpr int VC = V > 64 ? 64 : V;
+  constexpr int L = VC + 4;  // every block here is read along its rows
+  constexpr int TK = mmf_tiles<K, NTGA>(), TC = mmf_tiles<BC, NTGA>();
   __shared__ __align__(16) float sO[BC * L];
   __shared__ __align__(16) float sD[BC * L];  // dDelta, then Delta
   __shared__ __align__(16) float sS[K * L];   // S, then X
@@ -544,7 +549,7 @@ __global__ __launch_bounds__(NTG) void bwd_ga_kernel(
   // rowsum(S * X): NP neighbouring threads per key channel (K NP is a whole number of waves),
   // then a shuffle reduction among them
   {
-    constexpr int NP = NTG / K < V / 4 ? NTG / K : V / 4, VP = V / NP;
+    constexpr int NP = NTGA / K < V / 4 ? NTGA / K : V / 4, VP = V / NP;
     if (threadIdx.x < K * NP) {
       const int m = threadIdx.x / NP, part = threadIdx.x % NP;
       float dg = 0.f;
@@ -557,20 +562,43 @@ __global__ __launch_bounds__(NTG) void bwd_ga_kernel(
       if (part == 0) sc[G::oDG + m] = dg;
     }
   }
-  load_rows<V, L, NTG>(sO, dO, ch.tok, ch.len, H, h);
-  load_block<V, L, NTG>(sD, dDl + ch_h * BC * V);
-  load_block<V, L, NTG, K>(sS, S);
-  lds_barrier();
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   // dO S^T and dW = -dDelta S^T
-  mmf<K, V, false, true, L, L, NTG>(sO, sS, [&](int r, int m, float x) { sc[G::oR1 + r * K + m] = x; });
-  mmf<K, V, false, true, L, L, NTG>(sD, sS, [&](int r, int m, float x) { sc[G::oDW + r * K + m] = -x; });
-  lds_barrier();
-  load_block<V, L, NTG>(sD, Dl + ch_h * BC * V);
-  load_block<V, L, NTG, K>(sS, X);
-  lds_barrier();
+  {
+    f32x4 r1[TK], dw[TK];
+#pragma unroll
+    for (int i = 0; i < TK; ++i) r1[i] = dw[i] = z;
+    for (int c0 = 0; c0 < V; c0 += VC) {
+      load_rows<VC, L, NTGA, MT, V>(sO, dO, ch.tok, ch.len, H, h, c0);
+      load_block<VC, L, NTGA, BC, V>(sD, dDl + ch_h * BC * V + c0);
+      load_block<VC, L, NTGA, K, V>(sS, S + c0);
+      lds_barrier();
+      mmf_acc<K, VC, false, true, L, L, NTGA>(sO, sS, r1);
+      mmf_acc<K, VC, false, true, L, L, NTGA>(sD, sS, dw);
+      lds_barrier();
+    }
+    mmf_out<K, NTGA>(r1, [&](int r, int m, float x) { sc[G::oR1 + r * K + m] = x; });
+    mmf_out<K, NTGA>(dw, [&](int r, int m, float x) { sc[G::oDW + r * K + m] = -x; });
+  }
   // Delta X^T and dP = lower(dO Delta^T)
-  mmf<K, V, false, true, L, L, NTG>(sD, sS, [&](int r, int m, float x) { sc[G::oDKt + r * K + m] = x; });
-  mmf<BC, V, false, true, L, L, NTG>(sO, sD, [&](int i, int j, float x) { sc[G::oDP + i * BC + j] = j <= i ? x : 0.f; });
+  {
+    f32x4 dk[TK], dp[TC];
+#pragma unroll
+    for (int i = 0; i < TK; ++i) dk[i] = z;
+#pragma unroll
+    for (int i = 0; i < TC; ++i) dp[i] = z;
+    for (int c0 = 0; c0 < V; c0 += VC) {
+      if (V > VC) load_rows<VC, L, NTGA, MT, V>(sO, dO, ch.tok, ch.len, H, h, c0);
+      load_block<VC, L, NTGA, BC, V>(sD, Dl + ch_h * BC * V + c0);
+      load_block<VC, L, NTGA, K, V>(sS, X + c0);
+      lds_barrier();
+      mmf_acc<K, VC, false, true, L, L, NTGA>(sD, sS, dk);
+      mmf_acc<BC, VC, false, true, L, L, NTGA>(sO, sD, dp);
+      lds_barrier();
+    }
+    mmf_out<K, NTGA>(dk, [&](int r, int m, float x) { sc[G::oDKt + r * K + m] = x; });
+    mmf_out<BC, NTGA>(dp, [&](int i, int j, float x) { sc[G::oDP + i * BC + j] = j <= i ? x : 0.f; });
+  }
 }
 
 // (b) dv = diag(beta) T^T dDelta, T^T dW, dT = dDelta (beta V)^T + dW (beta Ke)^T,
@@ -848,7 +876,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
                      a.dfinal, a.cu_seqlens, a.total_tokens, (const int32_t*)seq_first, N, H,
                      chains8, ckX, dDl, a.grad_init);
   if (p.ub > 0) {
-    hipLaunchKernelGGL((bwd_ga_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, dO, (const float*)ckS,
+    hipLaunchKernelGGL((bwd_ga_kernel<K, V, MT>), cgrid, dim3(NTGA), 0, st, dO, (const float*)ckS,
                        (const float*)ckX, (const float*)Dl, (const float*)dDl, H,
                        (const ChunkRow*)chunks, ntot, scr);
     hipLaunchKernelGGL((bwd_gb_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, k, v, g, beta,

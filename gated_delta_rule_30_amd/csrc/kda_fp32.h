@@ -13,6 +13,7 @@ constexpr int BC = CHUNK;  // 64 tokens per chunk
 constexpr int NT = NTHREADS;  // the chains and the table kernels
 constexpr int NTP = 512;      // the record kernel: 8 waves per workgroup
 constexpr int NTG = 1024;     // the gradient kernels: 16 waves per workgroup
+constexpr int NTGA = 1024;    // the S/X product kernel: 16 waves, two workgroups per CU
 
 __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
   return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
@@ -58,6 +59,50 @@ __device__ __forceinline__ void mmf(const float* sA, const float* sB, F&& out) {
     const f32x4 acc = acc0 + acc1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) out(r0 + 4 * lg + r, c0 + lm, acc[r]);
+  }
+}
+
+// mmf split over the reduction index: acc[i] += the partial product of the wave's i-th tile
+// (tiles t = wave, wave + NTB / 64, ...; mmf_tiles<N, NTB>() per wave, the last ones skipped
+// by waves past the tile count), and mmf_out hands the finished tiles to out(r, c, x).
+template <int N, int NTB>
+__host__ __device__ constexpr int mmf_tiles() {
+  return (4 * (N / 16) + NTB / 64 - 1) / (NTB / 64);
+}
+template <int N, int R, bool TA, bool TB, int LA, int LB, int NTB>
+__device__ __forceinline__ void mmf_acc(const float* sA, const float* sB, f32x4* acc) {
+  constexpr int TILES = 4 * (N / 16), WAVES = NTB / 64;
+  static_assert(R % 8 == 0, "reduction steps of 8");
+  const int wv = threadIdx.x >> 6, lm = threadIdx.x & 15, lg = (threadIdx.x >> 4) & 3;
+#pragma unroll
+  for (int i = 0; i < mmf_tiles<N, NTB>(); ++i) {
+    const int t = wv + WAVES * i;
+    if (TILES % WAVES != 0 && t >= TILES) break;  // uniform per wave
+    const int r0 = 16 * (t & 3), c0 = 16 * (t >> 2);
+    f32x4 acc0 = acc[i], acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int k = 0; k < R; k += 8) {
+      const float a0 = TA ? sA[(k + lg) * LA + r0 + lm] : sA[(r0 + lm) * LA + k + lg];
+      const float b0 = TB ? sB[(c0 + lm) * LB + k + lg] : sB[(k + lg) * LB + c0 + lm];
+      const float a1 = TA ? sA[(k + 4 + lg) * LA + r0 + lm] : sA[(r0 + lm) * LA + k + 4 + lg];
+      const float b1 = TB ? sB[(c0 + lm) * LB + k + 4 + lg] : sB[(k + 4 + lg) * LB + c0 + lm];
+      acc0 = mfma4(a0, b0, acc0);
+      acc1 = mfma4(a1, b1, acc1);
+    }
+    acc[i] = acc0 + acc1;
+  }
+}
+template <int N, int NTB, typename F>
+__device__ __forceinline__ void mmf_out(const f32x4* acc, F&& out) {
+  constexpr int TILES = 4 * (N / 16), WAVES = NTB / 64;
+  const int wv = threadIdx.x >> 6, lm = threadIdx.x & 15, lg = (threadIdx.x >> 4) & 3;
+#pragma unroll
+  for (int i = 0; i < mmf_tiles<N, NTB>(); ++i) {
+    const int t = wv + WAVES * i;
+    if (TILES % WAVES != 0 && t >= TILES) break;  // uniform per wave
+    const int r0 = 16 * (t & 3), c0 = 16 * (t >> 2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out(r0 + 4 * lg + r, c0 + lm, acc[i][r]);
   }
 }
 
@@ -123,15 +168,15 @@ __device__ __forceinline__ void mul_rows_exp2(float* dst, const MT* src, int64_t
   }
 }
 
-// ROWS x N fp32 block (row-major, stride N) into LDS (row stride L), loads first.
-template <int N, int L, int NTB, int ROWS = BC>
+// ROWS x N fp32 block (row-major, stride SRCN) into LDS (row stride L), loads first.
+template <int N, int L, int NTB, int ROWS = BC, int SRCN = N>
 __device__ __forceinline__ void load_block(float* dst, const float* src) {
   constexpr int PIECES = ROWS * N / 4, PT = (PIECES + NTB - 1) / NTB;
   f32x4 t[PT];
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
     const int e = threadIdx.x + NTB * u;
-    if (PIECES % NTB == 0 || e < PIECES) t[u] = load4(src + 4 * e);
+    if (PIECES % NTB == 0 || e < PIECES) t[u] = load4(src + (e / (N / 4)) * SRCN + 4 * (e % (N / 4)));
   }
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
