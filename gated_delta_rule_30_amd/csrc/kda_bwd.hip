@@ -51,15 +51,15 @@ struct BRec {
 // per-(chunk, head) fp32 scratch between the three gradient kernels
 template <int K>
 struct GScr {
-  static constexpr int oDP = 0;                // dP (lower incl.)       [64][64]
-  static constexpr int oDA = oDP + BC * BC;    // dA (strict lower)      [64][64]
-  static constexpr int oR1 = oDA + BC * BC;    // dO S^T                 [64][K]
+  // [i][j] = dP_ij for j <= i (written by the S/X product kernel) and [j][i] = dA_ij for
+  // j < i (dA's strict lower triangle, transposed, written by the T-side kernel)
+  static constexpr int oDPA = 0;               // dP and dA^T            [64][64]
+  static constexpr int oR1 = oDPA + BC * BC;   // dO S^T                 [64][K]
   static constexpr int oDW = oR1 + BC * K;     // dW = -dDelta S^T       [64][K]
   static constexpr int oDKt = oDW + BC * K;    // Delta X^T              [64][K]
   static constexpr int oTDW = oDKt + BC * K;   // T^T dW                 [64][K]
   static constexpr int oDG = oTDW + BC * K;    // rowsum(S * X)          [K]
-  static constexpr int oDB = oDG + K;          // dbeta, the T-side terms [64]
-  static constexpr int floats = (oDB + BC + 63) / 64 * 64;
+  static constexpr int floats = (oDG + K + 63) / 64 * 64;
 };
 
 }  // namespace
@@ -597,7 +597,9 @@ __global__ __launch_bounds__(NTGA, 8) void bwd_ga_kernel(
       lds_barrier();
     }
     mmf_out<K, NTGA>(dk, [&](int r, int m, float x) { sc[G::oDKt + r * K + m] = x; });
-    mmf_out<BC, NTGA>(dp, [&](int i, int j, float x) { sc[G::oDP + i * BC + j] = j <= i ? x : 0.f; });
+    mmf_out<BC, NTGA>(dp, [&](int i, int j, float x) {
+      if (j <= i) sc[G::oDPA + i * BC + j] = x;
+    });
   }
 }
 
@@ -609,7 +611,7 @@ __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
     const MT* __restrict__ k, const MT* __restrict__ v, const MT* __restrict__ g,
     const MT* __restrict__ beta, const float* __restrict__ rec, const float* __restrict__ dDl, int H,
     const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr,
-    float* __restrict__ grad_v) {
+    float* __restrict__ grad_v, float* __restrict__ grad_beta) {
   using R = BRec<K, V>;
   using G = GScr<K>;
   // row strides: blocks read both along and down their rows (T, dDelta, dW) 20 more than a
@@ -669,129 +671,140 @@ __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
   // M1 = T^T dT into bufA (row stride LT), then dA = strict_lower(-M1 T^T)
   mmf<BC, BC, true, false, LT, LDT, NTG>(sT, sdT, [&](int r, int cc, float x) { bufA[r * LT + cc] = x; });
   lds_barrier();
-  mmf<BC, BC, false, true, LT, LT, NTG>(bufA, sT, [&](int i, int j, float x) { sc[G::oDA + i * BC + j] = j < i ? -x : 0.f; });
-  if (threadIdx.x < BC) sc[G::oDB + threadIdx.x] = sDb[threadIdx.x];
+  mmf<BC, BC, false, true, LT, LT, NTG>(bufA, sT, [&](int i, int j, float x) {
+    if (j < i) sc[G::oDPA + j * BC + i] = -x;  // dA_ij, transposed above dP
+  });
+  // dbeta's T-side terms; the gradient kernel adds the rest (one part of the key channels
+  // per workgroup) with atomics
+  if (threadIdx.x < ch.len) grad_beta[(ch.tok + threadIdx.x) * (int64_t)H + h] = sDb[threadIdx.x];
 }
 
 // (c) the decay-weighted pairwise sums and the per-token gradients of q, k, log alpha, beta
 template <int K, int V, typename MT>
-__global__ __launch_bounds__(NTG) void bwd_gc_kernel(
+__global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
     const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ g,
     const MT* __restrict__ beta, int H, const ChunkRow* __restrict__ chunks,
     const int32_t* __restrict__ ntot, const float* __restrict__ scr, float* __restrict__ grad_q,
     float* __restrict__ grad_k, float* __restrict__ grad_g, float* __restrict__ grad_beta) {
   using G = GScr<K>;
-  constexpr int LK = K + 4;
-  __shared__ __align__(16) float sQ[BC * LK];
+  // Everything here is per key channel except dbeta's sum over the channels, so each
+  // workgroup takes one part of KC channels (blockIdx.z) and adds its share of dbeta to
+  // grad_beta atomically. dP and dA share one 64 x 64 block (dP on and below the diagonal,
+  // dA transposed above it): 70 KB of LDS, and at 64 VGPRs two workgroups share a CU.
+  constexpr int KC = K > 64 ? 64 : K;
+  constexpr int LK = KC + 4;
+  __shared__ __align__(16) float sQ[BC * LK];  // q (part), then the per-token decay gradient
   __shared__ __align__(16) float sK[BC * LK];
   __shared__ __align__(16) float sB[BC * LK];
-  __shared__ __align__(16) float sdP[BC * 68];
-  __shared__ __align__(16) float sdA[BC * 68];
-  __shared__ float sBeta[BC], sDb[BC], sRed[K];
+  __shared__ __align__(16) float sM[BC * 68];  // [i][j] = dP_ij (j <= i), [j][i] = dA_ij (j < i)
+  __shared__ float sBeta[BC], sDb[BC], sRed[KC];
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= *ntot) return;
   const ChunkRow ch = chunks[c];
   const size_t ch_h = (size_t)c * H + h;
   const float* sc = scr + ch_h * G::floats;
-  load_rows<K, LK, NTG>(sQ, q, ch.tok, ch.len, H, h);
-  load_rows<K, LK, NTG>(sK, k, ch.tok, ch.len, H, h);
-  load_rows<K, LK, NTG>(sB, g, ch.tok, ch.len, H, h);
-  load_block<BC, 68, NTG>(sdP, sc + G::oDP);
-  load_block<BC, 68, NTG>(sdA, sc + G::oDA);
+  load_block<BC, 68, NTG>(sM, sc + G::oDPA);
   if (threadIdx.x < BC) {
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
     sDb[threadIdx.x] = 0.f;
   }
-  if (threadIdx.x < K) sRed[threadIdx.x] = 0.f;
-  lds_barrier();
-  // thread: key channel m, rows i = i0 + NG u (interleaved: the pairwise sums grow with i);
-  // its rows of dO S^T, T^T dW and Delta X^T are loaded now, in flight through the scan
-  constexpr int NG = NTG / K, RB = BC / NG;
-  const int m = threadIdx.x % K, i0 = threadIdx.x / K;
-  float r1v[RB], tdw[RB], dkv[RB];
-#pragma unroll
-  for (int u = 0; u < RB; ++u) {
-    const int i = i0 + NG * u;
-    r1v[u] = sc[G::oR1 + i * K + m];
-    tdw[u] = sc[G::oTDW + i * K + m];
-    dkv[u] = sc[G::oDKt + i * K + m];
-  }
-  cumsum_log2<K, LK, NTG>(sB);
-  lds_barrier();  // LDS only: the loads above stay in flight
-  const float bl = sB[(BC - 1) * LK + m];
-  float db[RB];
-  float red = 0.f;
-#pragma unroll
-  for (int u = 0; u < RB; ++u) {
-    const int i = i0 + NG * u;
-    const float bi = sB[i * LK + m], qi = sQ[i * LK + m], ki = sK[i * LK + m];
-    // sum_{j <= i} dP_ij k_j e^{b_i - b_j} and sum_{j < i} dA_ij k_j e^{b_i - b_j}
-    float s1 = 0.f, s2 = 0.f;
-    for (int j = 0; j <= i; ++j) {
-      const float w = sK[j * LK + m] * exp2_f(bi - sB[j * LK + m]);
-      s1 += sdP[i * 68 + j] * w;
-      s2 += sdA[i * 68 + j] * w;
-    }
-    // sum_{r >= i} (dA_ri beta_r k_r + dP_ri q_r) e^{b_r - b_i}
-    float s3 = 0.f;
-    for (int r = i; r < BC; ++r)
-      s3 += (sdA[r * 68 + i] * sBeta[r] * sK[r * LK + m] + sdP[r * 68 + i] * sQ[r * LK + m]) *
-            exp2_f(sB[r * LK + m] - bi);
-    const float eb = exp2_f(bi);
-    const float dq = r1v[u] * eb + s1;
-    const float dke = sBeta[i] * (tdw[u] * eb + s2);
-    const float dkt = dkv[u] * exp2_f(bl - bi);
-    const float dk = dke + s3 + dkt;
-    {
-      // dbeta's sum over the key channels of row i: the lanes sharing i (a whole wave, or 32
-      // lanes at K = 32) reduce first, then one LDS atomic
-      float y = row16_sum(ki * s2);
-      y += __shfl_xor(y, 16);
-      if constexpr (K >= 64) y += __shfl_xor(y, 32);
-      if (threadIdx.x % (K >= 64 ? 64 : K) == 0) atomicAdd(&sDb[i], y);
-    }
-    red += ki * dkt;
-    db[u] = qi * dq + ki * (dke - s3 - dkt);
-    if (i < ch.len) {
-      const int64_t o = ((ch.tok + i) * (int64_t)H + h) * K + m;
-      grad_q[o] = dq;
-      grad_k[o] = dk;
-    }
-  }
-  atomicAdd(&sRed[m], red);
-  lds_barrier();  // every read of sQ done
-#pragma unroll
-  for (int u = 0; u < RB; ++u) sQ[(i0 + NG * u) * LK + m] = db[u];
-  lds_barrier();
-  // log alpha: reverse cumulative sum of db over the chunk, the last token also carrying
-  // sum_i k_i * dKt_i and gamma * rowsum(S * X); NTG / K neighbouring threads per channel, as
-  // in cumsum_log2 but from the last row
+  // thread: key channel c0 + m, rows i = i0 + NG u (interleaved; a row's two pairwise sums
+  // have 65 terms together, so every thread has the same work)
+  constexpr int NG = NTG / KC, RB = BC / NG;
+  const int m = threadIdx.x % KC, i0 = threadIdx.x / KC;
+  const int c0 = blockIdx.z * KC;
   {
-    constexpr int P = NTG / K, RP = BC / P;
-    const int cm = threadIdx.x / P, part = threadIdx.x % P;
-    float x[RP];
-    float run = 0.f;
+    load_rows<KC, LK, NTG, MT, K>(sQ, q, ch.tok, ch.len, H, h, c0);
+    load_rows<KC, LK, NTG, MT, K>(sK, k, ch.tok, ch.len, H, h, c0);
+    load_rows<KC, LK, NTG, MT, K>(sB, g, ch.tok, ch.len, H, h, c0);
+    if (threadIdx.x < KC) sRed[threadIdx.x] = 0.f;
+    // this thread's rows of dO S^T, T^T dW and Delta X^T, in flight through the scan
+    float r1v[RB], tdw[RB], dkv[RB];
 #pragma unroll
-    for (int r = RP - 1; r >= 0; --r) {
-      run += sQ[(part * RP + r) * LK + cm];
-      x[r] = run;
+    for (int u = 0; u < RB; ++u) {
+      const int i = i0 + NG * u;
+      r1v[u] = sc[G::oR1 + i * K + c0 + m];
+      tdw[u] = sc[G::oTDW + i * K + c0 + m];
+      dkv[u] = sc[G::oDKt + i * K + c0 + m];
     }
-    float post = run;  // rows from this thread's first to the last, after the scan
+    lds_barrier();
+    cumsum_log2<KC, LK, NTG>(sB);
+    lds_barrier();  // LDS only: the loads above stay in flight
+    const float bl = sB[(BC - 1) * LK + m];
+    float db[RB];
+    float red = 0.f;
 #pragma unroll
-    for (int o = 1; o < P; o <<= 1) {
-      const float y = __shfl_down(post, o, P);
-      if (part + o < P) post += y;
+    for (int u = 0; u < RB; ++u) {
+      const int i = i0 + NG * u;
+      const float bi = sB[i * LK + m], qi = sQ[i * LK + m], ki = sK[i * LK + m];
+      const float dpii = sM[i * 68 + i];
+      // sum_{j <= i} dP_ij k_j e^{b_i - b_j} and sum_{j < i} dA_ij k_j e^{b_i - b_j}
+      float s1 = dpii * ki, s2 = 0.f;
+      for (int j = 0; j < i; ++j) {
+        const float w = sK[j * LK + m] * exp2_f(bi - sB[j * LK + m]);
+        s1 += sM[i * 68 + j] * w;
+        s2 += sM[j * 68 + i] * w;
+      }
+      // sum_{r >= i} (dA_ri beta_r k_r + dP_ri q_r) e^{b_r - b_i}  (dA_ii = 0)
+      float s3 = dpii * qi;
+      for (int r = i + 1; r < BC; ++r)
+        s3 += (sM[i * 68 + r] * sBeta[r] * sK[r * LK + m] + sM[r * 68 + i] * sQ[r * LK + m]) *
+              exp2_f(sB[r * LK + m] - bi);
+      const float eb = exp2_f(bi);
+      const float dq = r1v[u] * eb + s1;
+      const float dke = sBeta[i] * (tdw[u] * eb + s2);
+      const float dkt = dkv[u] * exp2_f(bl - bi);
+      const float dk = dke + s3 + dkt;
+      {
+        // dbeta's sum over the part's key channels of row i: the lanes sharing i (a whole
+        // wave, or 32 lanes at K = 32) reduce first, then one LDS atomic
+        float y = row16_sum(ki * s2);
+        y += __shfl_xor(y, 16);
+        if constexpr (KC >= 64) y += __shfl_xor(y, 32);
+        if (threadIdx.x % (KC >= 64 ? 64 : KC) == 0) atomicAdd(&sDb[i], y);
+      }
+      red += ki * dkt;
+      db[u] = qi * dq + ki * (dke - s3 - dkt);
+      if (i < ch.len) {
+        const int64_t o = ((ch.tok + i) * (int64_t)H + h) * K + c0 + m;
+        grad_q[o] = dq;
+        grad_k[o] = dk;
+      }
     }
-    post -= run;  // the rows after this thread's
-    post += sRed[cm] + sc[G::oDG + cm] * exp2_f(sB[(BC - 1) * LK + cm]);
+    atomicAdd(&sRed[m], red);
+    lds_barrier();  // every read of sQ done
 #pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      const int row = part * RP + r;
-      if (row < ch.len) grad_g[((ch.tok + row) * (int64_t)H + h) * K + cm] = x[r] + post;
+    for (int u = 0; u < RB; ++u) sQ[(i0 + NG * u) * LK + m] = db[u];
+    lds_barrier();
+    // log alpha: reverse cumulative sum of db over the chunk, the last token also carrying
+    // sum_i k_i * dKt_i and gamma * rowsum(S * X); NTG / KC neighbouring threads per channel,
+    // as in cumsum_log2 but from the last row
+    {
+      constexpr int P = NTG / KC, RP = BC / P;
+      const int cm = threadIdx.x / P, part = threadIdx.x % P;
+      float x[RP];
+      float run = 0.f;
+#pragma unroll
+      for (int r = RP - 1; r >= 0; --r) {
+        run += sQ[(part * RP + r) * LK + cm];
+        x[r] = run;
+      }
+      float post = run;  // rows from this thread's first to the last, after the scan
+#pragma unroll
+      for (int o = 1; o < P; o <<= 1) {
+        const float y = __shfl_down(post, o, P);
+        if (part + o < P) post += y;
+      }
+      post -= run;  // the rows after this thread's
+      post += sRed[cm] + sc[G::oDG + c0 + cm] * exp2_f(sB[(BC - 1) * LK + cm]);
+#pragma unroll
+      for (int r = 0; r < RP; ++r) {
+        const int row = part * RP + r;
+        if (row < ch.len) grad_g[((ch.tok + row) * (int64_t)H + h) * K + c0 + cm] = x[r] + post;
+      }
     }
   }
-  if (threadIdx.x < ch.len)
-    grad_beta[(ch.tok + threadIdx.x) * (int64_t)H + h] = sc[G::oDB + threadIdx.x] + sDb[threadIdx.x];
+  if (threadIdx.x < ch.len) atomicAdd(&grad_beta[(ch.tok + threadIdx.x) * (int64_t)H + h], sDb[threadIdx.x]);
 }
 
 // ---------------------------------------------------------------- host
@@ -881,8 +894,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
                        (const ChunkRow*)chunks, ntot, scr);
     hipLaunchKernelGGL((bwd_gb_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, k, v, g, beta,
                        (const float*)rec, (const float*)dDl, H, (const ChunkRow*)chunks, ntot, scr,
-                       a.grad_v);
-    hipLaunchKernelGGL((bwd_gc_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, q, k, g, beta, H,
+                       a.grad_v, a.grad_beta);
+    const dim3 pgrid(cgrid.x, cgrid.y, (unsigned)(K > 64 ? K / 64 : 1));  // key-channel parts
+    hipLaunchKernelGGL((bwd_gc_kernel<K, V, MT>), pgrid, dim3(NTG), 0, st, q, k, g, beta, H,
                        (const ChunkRow*)chunks, ntot, (const float*)scr, a.grad_q, a.grad_k,
                        a.grad_g, a.grad_beta);
   }

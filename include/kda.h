@@ -188,7 +188,7 @@ kda_status kda_chunk_fwd_scan(const void* q, const void* k, const void* v, const
  * (KDA_ERROR_INVALID_VALUE). Head dims K, V in {32, 64, 128}, both dtypes; others give
  * KDA_ERROR_NOT_SUPPORTED. The workspace (kda_chunk_bwd_workspace_size bytes, 256-byte aligned)
  * holds, for every (chunk, head), an fp32 record, the chunk-start state and the chunk-end state
- * gradient and scratch: about 512 KB per 64 tokens and head at K = V = 128.
+ * gradient and scratch: about 500 KB per 64 tokens and head at K = V = 128.
  */
 size_t kda_chunk_bwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                                     int32_t dk, int32_t dv, kda_dtype dtype);
