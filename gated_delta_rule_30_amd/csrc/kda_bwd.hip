@@ -607,24 +607,26 @@ __global__ __launch_bounds__(NTGA, 8) void bwd_ga_kernel(
 //     dA = strict_lower(-T^T dT T^T), and dbeta's terms rowsum(V * T^T dDelta) and
 //     rowsum(Ke * T^T dW)
 template <int K, int V, typename MT>
-__global__ __launch_bounds__(NTG) void bwd_gb_kernel(
+__global__ __launch_bounds__(NTG, 8) void bwd_gb_kernel(
     const MT* __restrict__ k, const MT* __restrict__ v, const MT* __restrict__ g,
     const MT* __restrict__ beta, const float* __restrict__ rec, const float* __restrict__ dDl, int H,
     const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr,
     float* __restrict__ grad_v, float* __restrict__ grad_beta) {
   using R = BRec<K, V>;
   using G = GScr<K>;
+  // The value columns and the key channels run in parts of at most 64; dT's partial tiles stay
+  // in registers until both sums are done. 64 KB of LDS and 64 VGPRs: two workgroups per CU.
+  constexpr int VC = V > 64 ? 64 : V, KC = K > 64 ? 64 : K;
   // row strides: blocks read both along and down their rows (T, dDelta, dW) 20 more than a
   // multiple of 64 floats (no bank conflict along rows, at most two-way down columns); dT,
   // read down its columns, 80; v and Ke, read along rows, + 4
   constexpr int LT = BC + 20, LDT = BC + 16;
-  constexpr int LDD = V + ((84 - V) & 63), LDW = K + ((84 - K) & 63), LVV = V + 4, LKE = K + 4;
+  constexpr int LDD = VC + ((84 - VC) & 63), LDW = KC + ((84 - KC) & 63), LVV = VC + 4, LKE = KC + 4;
   constexpr int LA = (LDD > LDW ? LDD : LDW) > LT ? (LDD > LDW ? LDD : LDW) : LT;
-  constexpr int LB = LVV > LKE ? LVV : LKE;
+  constexpr int LB0 = LVV > LKE ? LVV : LKE, LB = LB0 > LDT ? LB0 : LDT;
   __shared__ __align__(16) float sT[BC * LT];
-  __shared__ __align__(16) float sdT[BC * LDT];
-  __shared__ __align__(16) float bufA[BC * LA];
-  __shared__ __align__(16) float bufB[BC * LB];
+  __shared__ __align__(16) float bufA[BC * LA];  // dDelta (part), dW (part), then M1 = T^T dT
+  __shared__ __align__(16) float bufB[BC * LB];  // v (part), Ke (part), then dT
   __shared__ float sBeta[BC], sDb[BC];
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= *ntot) return;
@@ -633,43 +635,59 @@ __global__ __launch_bounds__(NTG) void bwd_gb_kernel(
   const float* rc = rec + ch_h * R::floats;
   float* sc = scr + ch_h * G::floats;
   load_block<BC, LT, NTG>(sT, rc + R::oT);
-  load_block<V, LDD, NTG>(bufA, dDl + ch_h * BC * V);
-  load_rows<V, LVV, NTG>(bufB, v, ch.tok, ch.len, H, h);
   if (threadIdx.x < BC) {
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
     sDb[threadIdx.x] = 0.f;
   }
-  lds_barrier();
-  // T^T dDelta: dv = beta T^T dDelta, dbeta += rowsum(v * T^T dDelta)
-  mmf<V, BC, true, false, LT, LDD, NTG>(sT, bufA, [&](int r, int cc, float x) {
-    if (r < ch.len) grad_v[((ch.tok + r) * (int64_t)H + h) * V + cc] = sBeta[r] * x;
-    const float y = row16_sum(bufB[r * LVV + cc] * x);  // the 16 lanes of a row hold one r
-    if ((threadIdx.x & 15) == 0) atomicAdd(&sDb[r], y);
-  });
-  lds_barrier();
-  for (int e = threadIdx.x; e < BC * V; e += NTG) bufB[(e / V) * LVV + e % V] *= sBeta[e / V];
-  lds_barrier();
-  // dT = dDelta (beta V)^T
-  mmf<BC, V, false, true, LDD, LVV, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * LDT + j] = x; });
-  lds_barrier();
-  // dW and Ke = k e^b
-  load_block<K, LDW, NTG>(bufA, sc + G::oDW);
-  load_rows<K, LKE, NTG>(bufB, g, ch.tok, ch.len, H, h);
-  lds_barrier();
-  cumsum_log2<K, LKE, NTG>(bufB);
-  lds_barrier();
-  mul_rows_exp2<K, LKE, NTG>(bufB, k, ch.tok, ch.len, H, h);
-  lds_barrier();
-  // T^T dW; dbeta += rowsum(Ke * T^T dW); dT += dW (beta Ke)^T
-  mmf<K, BC, true, false, LT, LDW, NTG>(sT, bufA, [&](int r, int cc, float x) {
-    sc[G::oTDW + r * K + cc] = x;
-    const float y = row16_sum(bufB[r * LKE + cc] * x);
-    if ((threadIdx.x & 15) == 0) atomicAdd(&sDb[r], y);
-  });
-  mmf<BC, K, false, true, LDW, LKE, NTG>(bufA, bufB, [&](int i, int j, float x) { sdT[i * LDT + j] += sBeta[j] * x; });
+  constexpr int TC = mmf_tiles<BC, NTG>();
+  f32x4 dT[TC];
+#pragma unroll
+  for (int i = 0; i < TC; ++i) dT[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int c0 = 0; c0 < V; c0 += VC) {
+    load_block<VC, LDD, NTG, BC, V>(bufA, dDl + ch_h * BC * V + c0);
+    load_rows<VC, LVV, NTG, MT, V>(bufB, v, ch.tok, ch.len, H, h, c0);
+    lds_barrier();
+    // T^T dDelta: dv = beta T^T dDelta, dbeta += rowsum(v * T^T dDelta)
+    mmf<VC, BC, true, false, LT, LDD, NTG>(sT, bufA, [&](int r, int cc, float x) {
+      if (r < ch.len) grad_v[((ch.tok + r) * (int64_t)H + h) * V + c0 + cc] = sBeta[r] * x;
+      const float y = row16_sum(bufB[r * LVV + cc] * x);  // the 16 lanes of a row hold one r
+      if ((threadIdx.x & 15) == 0) atomicAdd(&sDb[r], y);
+    });
+    lds_barrier();
+    for (int e = threadIdx.x; e < BC * VC; e += NTG) bufB[(e / VC) * LVV + e % VC] *= sBeta[e / VC];
+    lds_barrier();
+    // dT += dDelta (beta V)^T over the part's columns
+    mmf_acc<BC, VC, false, true, LDD, LVV, NTG>(bufA, bufB, dT);
+    lds_barrier();
+  }
+#pragma unroll 1
+  for (int c0 = 0; c0 < K; c0 += KC) {
+    // dW and Ke = k e^b (the decay is per channel, so a part's cumulative sum is its own)
+    load_block<KC, LDW, NTG, BC, K>(bufA, sc + G::oDW + c0);
+    load_rows<KC, LKE, NTG, MT, K>(bufB, g, ch.tok, ch.len, H, h, c0);
+    lds_barrier();
+    cumsum_log2<KC, LKE, NTG>(bufB);
+    lds_barrier();
+    mul_rows_exp2<KC, LKE, NTG, MT, K>(bufB, k, ch.tok, ch.len, H, h, c0);
+    lds_barrier();
+    // T^T dW; dbeta += rowsum(Ke * T^T dW)
+    mmf<KC, BC, true, false, LT, LDW, NTG>(sT, bufA, [&](int r, int cc, float x) {
+      sc[G::oTDW + r * K + c0 + cc] = x;
+      const float y = row16_sum(bufB[r * LKE + cc] * x);
+      if ((threadIdx.x & 15) == 0) atomicAdd(&sDb[r], y);
+    });
+    lds_barrier();
+    for (int e = threadIdx.x; e < BC * KC; e += NTG) bufB[(e / KC) * LKE + e % KC] *= sBeta[e / KC];
+    lds_barrier();
+    // dT += dW (beta Ke)^T over the part's channels
+    mmf_acc<BC, KC, false, true, LDW, LKE, NTG>(bufA, bufB, dT);
+    lds_barrier();
+  }
+  mmf_out<BC, NTG>(dT, [&](int i, int j, float x) { bufB[i * LDT + j] = x; });
   lds_barrier();
   // M1 = T^T dT into bufA (row stride LT), then dA = strict_lower(-M1 T^T)
-  mmf<BC, BC, true, false, LT, LDT, NTG>(sT, sdT, [&](int r, int cc, float x) { bufA[r * LT + cc] = x; });
+  mmf<BC, BC, true, false, LT, LDT, NTG>(sT, bufB, [&](int r, int cc, float x) { bufA[r * LT + cc] = x; });
   lds_barrier();
   mmf<BC, BC, false, true, LT, LT, NTG>(bufA, sT, [&](int i, int j, float x) {
     if (j < i) sc[G::oDPA + j * BC + i] = -x;  // dA_ij, transposed above dP
