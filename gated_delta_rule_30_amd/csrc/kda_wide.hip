@@ -213,20 +213,25 @@ __global__ __launch_bounds__(NT) void wide_state_kernel(
       *reinterpret_cast<f32x4*>(sOp + (e / (KW / 4)) * ld + 4 * (e % (KW / 4))) = rb[u];
     }
   };
-  for (int c = first; c < last; ++c) {
-    const float* rc = rec + ((size_t)c * H + h) * R::floats;
-    const int64_t tok = s0 + (int64_t)(c - first) * BC;
-    const int len = (int)min((int64_t)BC, s1 - tok);
+  // W, P, this slice of U and gamma of a chunk; a chunk's are loaded while the chunk before
+  // forms S' (the last chunk loads its own again)
+  f32x4 pp[PP], d[NCB];
+  float rg;
+  auto fetch_head = [&](const float* rc) {
     fetch(rc + R::oW);
-    f32x4 pp[PP];
 #pragma unroll
     for (int u = 0; u < PP; ++u) pp[u] = reinterpret_cast<const f32x4*>(rc + R::oP)[tid + NT * u];
-    f32x4 d[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) d[cb][r] = rc[R::oU + (16 * w + 4 * lg + r) * V + c0 + 16 * cb + lm];
-    const float rg = rc[R::oGam + tid];  // NT == KW
+    rg = rc[R::oGam + tid];  // NT == KW
+  };
+  if (first < last) fetch_head(rec + ((size_t)first * H + h) * R::floats);
+  for (int c = first; c < last; ++c) {
+    const float* rc = rec + ((size_t)c * H + h) * R::floats;
+    const int64_t tok = s0 + (int64_t)(c - first) * BC;
+    const int len = (int)min((int64_t)BC, s1 - tok);
     lds_barrier();  // the previous chunk's reads of LDS are done
     stage(LR);
 #pragma unroll
@@ -277,6 +282,7 @@ __global__ __launch_bounds__(NT) void wide_state_kernel(
       }
     lds_barrier();  // Qe no longer read
     stage(LC);
+    fetch_head(rec + ((size_t)(c + 1 < last ? c + 1 : c) * H + h) * R::floats);
     lds_barrier();
     // S' tiles: diag(gamma) S + Kt^T Delta
     f32x4 sn[TPW][NCB];
