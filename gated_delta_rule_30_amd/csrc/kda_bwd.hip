@@ -203,10 +203,11 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
     float x[BC];
 #pragma unroll
     for (int i = 0; i < BC; ++i) {
-      float s = i == m ? 1.f : 0.f;
+      // four partial sums: the row's dot product is not one chain of dependent FMAs
+      float ps[4] = {i == m ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < i; ++j) s -= sA[i * 68 + j] * x[j];
-      x[i] = s;
+      for (int j = 0; j < i; ++j) ps[j & 3] -= sA[i * 68 + j] * x[j];
+      x[i] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
     }
 #pragma unroll
     for (int i = 0; i < BC; ++i) {

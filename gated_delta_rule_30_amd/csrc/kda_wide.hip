@@ -130,10 +130,11 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
     float x[BC];
 #pragma unroll
     for (int r = 0; r < BC; ++r) {
-      float s = r == m ? 1.f : 0.f;
+      // four partial sums: the row's dot product is not one chain of dependent FMAs
+      float ps[4] = {r == m ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < r; ++j) s -= sA[r * 68 + j] * x[j];
-      x[r] = s;
+      for (int j = 0; j < r; ++j) ps[j & 3] -= sA[r * 68 + j] * x[j];
+      x[r] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
     }
 #pragma unroll
     for (int r = 0; r < BC; ++r) sT[r * 68 + m] = x[r];
