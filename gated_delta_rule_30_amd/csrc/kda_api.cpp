@@ -10,9 +10,14 @@ namespace {
 
 bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 // the chunk path's prep kernel holds K-wide operand tiles in LDS: K <= 128; K = 256 takes the
-// wide-key path (fp32 records, key channels in two halves)
+// wide-key path (fp32 records, key channels in parts of 64), as do fp32 inputs at K = 128
 bool supported_chunk_dk(int32_t d) { return d == 32 || d == 64 || d == 128; }
 constexpr int32_t kWideDk = 256;
+// the chunk forward's wide-key path: K = 256, and fp32 inputs at K = 128 (whose fp32 operand
+// tiles exceed the chunk path's prep kernel LDS budget)
+bool wide_path(int32_t dk, kda_dtype dtype) {
+  return dk == kWideDk || (dk == 128 && dtype == KDA_DTYPE_F32);
+}
 constexpr uint32_t kAllOptions =
     KDA_OPT_SCALAR_GATE | KDA_OPT_GATE_LOGITS | KDA_OPT_BETA_LOGITS | KDA_OPT_L2NORM_QK;
 static_assert(KDA_OPT_SCALAR_GATE == kda::OPT_SCALAR_GATE && KDA_OPT_GATE_LOGITS == kda::OPT_GATE_LOGITS &&
@@ -51,8 +56,6 @@ static kda_status check_chunk_shape(int32_t num_seqs, int64_t total_tokens, int3
     return KDA_ERROR_INVALID_VALUE;
   if (!valid_dtype(dtype) || !(supported_chunk_dk(dk) || dk == kWideDk) || !supported_dim(dv))
     return KDA_ERROR_NOT_SUPPORTED;
-  // fp32 operands at K = 128 exceed the prep kernel's LDS budget
-  if (dtype == KDA_DTYPE_F32 && dk == 128) return KDA_ERROR_NOT_SUPPORTED;
   return KDA_SUCCESS;
 }
 
@@ -60,9 +63,9 @@ extern "C" size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_t
                                                int32_t num_heads, int32_t dk, int32_t dv,
                                                kda_dtype dtype) {
   if (check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype) != KDA_SUCCESS) return 0;
-  if (dk == kWideDk) {
+  if (wide_path(dk, dtype)) {
     kda::WidePlan wp;
-    return kda::make_wide_plan(num_seqs, total_tokens, num_heads, dv, &wp) ? wp.total_bytes : 0;
+    return kda::make_wide_plan(num_seqs, total_tokens, num_heads, dk, dv, &wp) ? wp.total_bytes : 0;
   }
   kda::ChunkPlan pl;
   if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16, &pl))
@@ -80,7 +83,7 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
   kda_status st = check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_SUCCESS) return st;
   if (options & ~kAllOptions) return KDA_ERROR_NOT_SUPPORTED;
-  if (dk == kWideDk && options != 0) return KDA_ERROR_NOT_SUPPORTED;  // the wide-key path: plain inputs
+  if (wide_path(dk, dtype) && options != 0) return KDA_ERROR_NOT_SUPPORTED;  // the wide-key path: plain inputs
   const int32_t gdim = (options & KDA_OPT_SCALAR_GATE) ? 1 : dk;  // gate values per token and head
   if (cu_seqlens == nullptr && total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
   if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERROR_INVALID_VALUE;
@@ -108,8 +111,8 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
   }
   kda::ChunkPlan pl;
   kda::WidePlan wp;
-  if (dk == kWideDk) {
-    if (!kda::make_wide_plan(num_seqs, total_tokens, num_heads, dv, &wp)) return KDA_ERROR_INVALID_VALUE;
+  if (wide_path(dk, dtype)) {
+    if (!kda::make_wide_plan(num_seqs, total_tokens, num_heads, dk, dv, &wp)) return KDA_ERROR_INVALID_VALUE;
     if (workspace_bytes < wp.total_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
   } else {
     if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16, &pl))
@@ -136,7 +139,7 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
   a.final_state = final_state;
   a.workspace = workspace;
   a.stream = stream;
-  hipError_t e = dk == kWideDk ? kda::launch_chunk_fwd_wide(a, wp) : kda::launch_chunk_fwd(a, pl);
+  hipError_t e = wide_path(dk, dtype) ? kda::launch_chunk_fwd_wide(a, wp) : kda::launch_chunk_fwd(a, pl);
   return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
 }
 
@@ -248,8 +251,8 @@ static kda_status check_scan_shape(int32_t num_seqs, int64_t total_tokens, int32
                                    int32_t dk, int32_t dv, kda_dtype dtype, int32_t num_groups) {
   kda_status st = check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_SUCCESS) return st;
-  // the first pass needs V + K columns (<= 256) and the K <= 128 chunk path
-  if (dk != dv || dk == kWideDk) return KDA_ERROR_NOT_SUPPORTED;
+  // the first pass needs V + K columns (<= 256) and the chunk path (K <= 128; fp32 at K <= 64)
+  if (dk != dv || wide_path(dk, dtype)) return KDA_ERROR_NOT_SUPPORTED;
   if (num_groups <= 0 || total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
   return KDA_SUCCESS;
 }

@@ -37,7 +37,8 @@ struct WidePlan {
   int64_t ub;  // upper bound of the number of chunks over all sequences
   size_t off_seq, off_rows, off_rec, total_bytes;
 };
-bool make_wide_plan(int num_seqs, int64_t total_tokens, int num_heads, int dv, WidePlan* p);
+bool make_wide_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv,
+                    WidePlan* p);
 hipError_t launch_chunk_fwd_wide(const ChunkArgs& a, const WidePlan& p);
 
 // Training backward (kda_bwd.hip): per chunk and head an fp32 record, the chunk-start states,

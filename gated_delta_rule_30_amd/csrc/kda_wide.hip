@@ -1,12 +1,14 @@
-// Chunked forward at 256 key channels. The same chunk form as kda_chunk.hip ("A Technical
-// Breakdown", section 4; "Kimi Linear" explainer, "WY Representation"):
+// Chunked forward at 256 key channels (and at 128 for fp32 inputs). The same chunk form as
+// kda_chunk.hip ("A Technical Breakdown", section 4; "Kimi Linear" explainer, "WY
+// Representation"):
 //     Delta = U - W S,   O = Qe S + P Delta,   S' = diag(gamma) S + Kt^T Delta,
 // with b = cumsum(log alpha) per key channel, Qe = q e^b, Kt = k e^{b_last - b}, gamma =
 // e^{b_last}, A = strict_lower(diag(beta) (k k^T weighted by e^{b_i - b_j})), T = (I + A)^{-1},
 // W = T diag(beta) (k e^b), U = T diag(beta) V and P = lower(q k^T weighted by e^{b_i - b_j}).
-// kda_chunk.hip's prep kernel keeps K-wide operand tiles in LDS, which at K = 256 would not
-// fit; here the per-chunk kernel works over the key channels in four quarters of 64 (the sums
-// over channels in A and P add up across the quarters, and every other quantity is per channel),
+// kda_chunk.hip's prep kernel keeps K-wide operand tiles in LDS, which at K = 256 (or fp32 at
+// K = 128) would not fit; here the per-chunk kernel works over the key channels in parts of 64
+// (the sums over channels in A and P add up across the parts, and every other quantity is per
+// channel),
 // in fp32 on the shared fp32 machinery of the training backward:
 //   wide_prep_kernel   per (chunk, head), 512 threads: P, W, Kt, Qe, U, gamma -> fp32 record
 //   wide_state_kernel  per (sequence, head, 16 or 32 value columns), 256 threads: the chain
@@ -22,11 +24,10 @@ using namespace fp32;
 
 namespace {
 
-constexpr int KW = 256;     // key channels
-constexpr int KQ = KW / 4;  // channels per quarter (the record kernel's LDS tiles)
+constexpr int KQ = 64;  // key channels per part (the record kernel's LDS tiles)
 
 // per-(chunk, head) fp32 record, row-major blocks
-template <int V>
+template <int KW, int V>
 struct WRec {
   static constexpr int oP = 0;               // P (lower incl.)     [64][64]
   static constexpr int oW = oP + BC * BC;    // W                   [64][256]
@@ -39,12 +40,12 @@ struct WRec {
 
 }  // namespace
 
-template <int V, typename MT>
+template <int KW, int V, typename MT>
 __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
     const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ v,
     const MT* __restrict__ g, const MT* __restrict__ beta, int H,
     const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ rec) {
-  using R = WRec<V>;
+  using R = WRec<KW, V>;
   constexpr int LK = KQ + 4;                 // rows of a channel quarter
   constexpr int VH = V > KQ ? KQ : V, LV = VH + 4;
   // 70 KB in all and at most 128 VGPRs (4 waves per SIMD), so that two workgroups share a CU
@@ -175,12 +176,13 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
 // S' = diag(gamma) S + Kt^T Delta (wave w: 16-row tiles w, w + 4, ..), each staged A operand
 // read once for the CW / 16 column blocks. The next block's loads are issued before the
 // current block's products. CW = 32 at V = 256 keeps the chains to one wave of workgroups.
-template <int V, int CW, typename MT>
+template <int KW, int V, int CW, typename MT>
 __global__ __launch_bounds__(NT) void wide_state_kernel(
     const float* __restrict__ rec, const float* __restrict__ init, const int32_t* __restrict__ cu,
     int64_t T, const int32_t* __restrict__ seq_first, int N, int H, int chains8, MT* __restrict__ o,
     float* __restrict__ fin) {
-  using R = WRec<V>;
+  using R = WRec<KW, V>;
+  static_assert(KW <= NT && KW % 64 == 0, "one thread per key channel for gamma");
   constexpr int NCB = CW / 16;           // 16-column blocks per workgroup
   constexpr int LS = CW == 16 ? 16 : CW + 16;  // S and Delta rows, read down their columns
   constexpr int LR = KW + 4;    // W and Qe: read along rows (A operand rows)
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(NT) void wide_state_kernel(
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) d[cb][r] = rc[R::oU + (16 * w + 4 * lg + r) * V + c0 + 16 * cb + lm];
-    rg = rc[R::oGam + tid];  // NT == KW
+    rg = tid < KW ? rc[R::oGam + tid] : 0.f;
   };
   if (first < last) fetch_head(rec + ((size_t)first * H + h) * R::floats);
   for (int c = first; c < last; ++c) {
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(NT) void wide_state_kernel(
       const int e = tid + NT * u;
       *reinterpret_cast<f32x4*>(sP + (e / (BC / 4)) * 68 + 4 * (e % (BC / 4))) = pp[u];
     }
-    sG[tid] = rg;
+    if (tid < KW) sG[tid] = rg;
     fetch(rc + R::oQe);  // in flight during Delta
     lds_barrier();
     // Delta rows 16 w .. : U - W S
@@ -325,14 +327,15 @@ __global__ __launch_bounds__(NT) void wide_state_kernel(
 // ---------------------------------------------------------------- host
 static size_t al256w(size_t x) { return (x + 255) / 256 * 256; }
 
-bool make_wide_plan(int N, int64_t T, int H, int V, WidePlan* p) {
+bool make_wide_plan(int N, int64_t T, int H, int K, int V, WidePlan* p) {
   if (N <= 0 || H <= 0 || T < 0) return false;
   size_t rec_floats = 0;
-  if (V == 32) rec_floats = WRec<32>::floats;
-  else if (V == 64) rec_floats = WRec<64>::floats;
-  else if (V == 128) rec_floats = WRec<128>::floats;
-  else if (V == 256) rec_floats = WRec<256>::floats;
-  else return false;
+#define KDA_WREC(KK, VV) \
+  if (K == KK && V == VV) rec_floats = WRec<KK, VV>::floats;
+  KDA_WREC(128, 32) KDA_WREC(128, 64) KDA_WREC(128, 128) KDA_WREC(128, 256)
+  KDA_WREC(256, 32) KDA_WREC(256, 64) KDA_WREC(256, 128) KDA_WREC(256, 256)
+#undef KDA_WREC
+  if (rec_floats == 0) return false;
   int64_t ub = (T + (int64_t)N * (BC - 1)) / BC;
   if (ub > T) ub = T;
   p->ub = ub;
@@ -347,7 +350,7 @@ bool make_wide_plan(int N, int64_t T, int H, int V, WidePlan* p) {
   return true;
 }
 
-template <int V, typename MT>
+template <int K, int V, typename MT>
 static hipError_t launch_wide_t(const ChunkArgs& a, const WidePlan& p) {
   hipStream_t st = (hipStream_t)a.stream;
   char* ws = reinterpret_cast<char*>(a.workspace);
@@ -358,23 +361,27 @@ static hipError_t launch_wide_t(const ChunkArgs& a, const WidePlan& p) {
   hipError_t e = launch_chunk_rows(a.cu_seqlens, N, a.total_tokens, p.ub, seq_first, rows, st);
   if (e != hipSuccess) return e;
   if (p.ub > 0)
-    hipLaunchKernelGGL((wide_prep_kernel<V, MT>), dim3((unsigned)p.ub, (unsigned)H), dim3(NTP), 0,
+    hipLaunchKernelGGL((wide_prep_kernel<K, V, MT>), dim3((unsigned)p.ub, (unsigned)H), dim3(NTP), 0,
                        st, (const MT*)a.q, (const MT*)a.k, (const MT*)a.v, (const MT*)a.g,
                        (const MT*)a.beta, H, (const ChunkRow*)rows, (const int32_t*)(seq_first + N),
                        rec);
   const int chains8 = (N * H + 7) / 8 * 8;
   constexpr int CW = V == 256 ? 32 : 16;  // value columns per chain workgroup
-  hipLaunchKernelGGL((wide_state_kernel<V, CW, MT>), dim3((unsigned)(chains8 * (V / CW))), dim3(NT),
+  hipLaunchKernelGGL((wide_state_kernel<K, V, CW, MT>), dim3((unsigned)(chains8 * (V / CW))), dim3(NT),
                      0, st, (const float*)rec, a.init_state, a.cu_seqlens, a.total_tokens,
                      (const int32_t*)seq_first, N, H, chains8, (MT*)a.o, a.final_state);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_fwd_wide(const ChunkArgs& a, const WidePlan& p) {
-  if (a.dk != KW) return hipErrorInvalidValue;
-#define KDA_WIDE_CASE(VV)                                                                    \
-  if (a.dv == VV)                                                                            \
-    return a.dtype_bf16 ? launch_wide_t<VV, bf16>(a, p) : launch_wide_t<VV, float>(a, p);
+#define KDA_WIDE_CASE(KK, VV)                                                                  \
+  if (a.dk == KK && a.dv == VV)                                                                \
+    return a.dtype_bf16 ? launch_wide_t<KK, VV, bf16>(a, p) : launch_wide_t<KK, VV, float>(a, p);
+  KDA_WIDE_CASE(256, 32) KDA_WIDE_CASE(256, 64) KDA_WIDE_CASE(256, 128) KDA_WIDE_CASE(256, 256)
+#undef KDA_WIDE_CASE
+  // K = 128 comes here for fp32 inputs only (bf16 takes the chunk path)
+#define KDA_WIDE_CASE(VV) \
+  if (a.dk == 128 && a.dv == VV && !a.dtype_bf16) return launch_wide_t<128, VV, float>(a, p);
   KDA_WIDE_CASE(32) KDA_WIDE_CASE(64) KDA_WIDE_CASE(128) KDA_WIDE_CASE(256)
 #undef KDA_WIDE_CASE
   return hipErrorInvalidValue;

@@ -22,8 +22,8 @@
  *  - log_alpha is the natural log of the per-channel decay alpha (expected <= 0); no query
  *    scale is applied and q, k are used as given (no normalisation inside). The _ex entry
  *    points take options that change how these inputs are read (KDA_OPT_* below).
- *  - Supported head dims: kda_chunk_fwd K in {32, 64, 128} (K = 128 only with bf16 inputs) or
- *    K = 256 (the wide-key path below: both dtypes, no input options), V in {32, 64, 128, 256};
+ *  - Supported head dims: kda_chunk_fwd K in {32, 64, 128, 256}, V in {32, 64, 128, 256};
+ *    K = 256, and fp32 inputs at K = 128, run the wide-key path below (no input options);
  *    kda_decode_step K, V in {32, 64, 128, 256}. Other values give KDA_ERROR_NOT_SUPPORTED.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
  *    returns without waiting. Argument errors are reported synchronously before anything is
@@ -85,8 +85,8 @@ const char* kda_status_string(kda_status s);
  * Workspace bytes kda_chunk_fwd needs for this shape (0 if the arguments are invalid).
  * The value depends only on the arguments; it covers the device chunk table, a running state
  * and one chunk-record buffer, and is bounded (about 170 MB at H=32, K=V=128, bf16) plus
- * 32 bytes per chunk and 4*N*H*K*V bytes, whatever the sequence length. At K = 256 (the
- * wide-key path) it holds an fp32 record for every chunk and head instead: 214 KB + 256 V
+ * 32 bytes per chunk and 4*N*H*K*V bytes, whatever the sequence length. On the wide-key path
+ * (K = 256) it holds an fp32 record for every chunk and head instead: 214 KB + 256 V
  * bytes per 64 tokens and head (e.g. 9.2 GB at H = 32, V = 256 and 65,536 tokens).
  */
 size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
@@ -117,9 +117,9 @@ size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int3
  * Numerical domain: the in-chunk factorisation keeps every factor within fp32 range when the
  * decay of any key channel over 16 consecutive tokens is at most e^80 (e.g. log_alpha >= -5
  * everywhere); stronger decays can overflow to Inf/NaN.
- * K = 256 runs a separate path in fp32 (the chunk's products over the key channels in two
- * halves of 128, every decay factor formed pairwise within the chunk, so any decay is in
- * range); it takes options = 0 only (other options give KDA_ERROR_NOT_SUPPORTED).
+ * K = 256, and fp32 inputs at K = 128, run a separate path in fp32 (the chunk's products over
+ * the key channels in parts of 64, every decay factor formed pairwise within the chunk, so any
+ * decay is in range); it takes options = 0 only (other options give KDA_ERROR_NOT_SUPPORTED).
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* beta, const float* init_state, const int32_t* cu_seqlens,

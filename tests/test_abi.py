@@ -96,7 +96,7 @@ def _chunk(L, **kw):
     (dict(opts=15, q=None), INVALID),
     (dict(opts=0, dk=48), NOT_SUPPORTED),
     (dict(dtype=7), NOT_SUPPORTED),
-    (dict(dtype=F32, dk=128), NOT_SUPPORTED),
+    (dict(dtype=F32, dk=128, opts=1), NOT_SUPPORTED),   # fp32 at K = 128: the wide-key path, plain inputs
     (dict(N=3, T=64), INVALID),            # equal lengths need T % N == 0
     (dict(q=None), INVALID),
     (dict(beta=None), INVALID),
@@ -248,5 +248,9 @@ def test_wide_key_workspace_size():
     assert a > 0 and 1.9 < b / a < 2.1
     assert ws(1, 1000, 2, 256, 256, torch.float32) > 0
     assert ws(1, 1000, 2, 256, 512, torch.bfloat16) == 0
+    # fp32 inputs at K = 128 take the same path; the scan (chunk path only) refuses them
+    assert ws(1, 1000, 2, 128, 128, torch.float32) > 0
+    assert int(kda.lib().kda_chunk_fwd_scan_workspace_size(1, 1024, 2, 128, 128, 0, 4)) == 0
+    assert int(kda.lib().kda_chunk_fwd_scan_workspace_size(1, 1024, 2, 128, 128, 1, 4)) > 0
     # the scan keeps K = V <= 128
     assert int(kda.lib().kda_chunk_fwd_scan_workspace_size(1, 4096, 2, 256, 256, 1, 4)) == 0

@@ -1,5 +1,5 @@
-"""kda_chunk_fwd at 256 key channels (the wide-key path: fp32 records, key channels in two
-halves) against the fp64 oracle, through the C ABI."""
+"""kda_chunk_fwd on the wide-key path (fp32 records, key channels in parts of 64): K = 256, and
+fp32 inputs at K = 128, against the fp64 oracle, through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -27,6 +27,36 @@ def test_wide_matches_oracle(T, H, V, dtype, with_init):
     o_ref, f_ref = oracle_fwd(inp)
     assert_close(np64(o), o_ref, dtype, "o")
     assert_close(np64(fin), f_ref, dtype, "final")
+
+
+@pytest.mark.parametrize("T,H,V", [
+    (300, 2, 128),   # a partial last chunk
+    (256, 3, 64),
+    (130, 1, 256),
+])
+def test_fp32_k128_matches_oracle(T, H, V):
+    """fp32 inputs at K = 128 take the wide-key path (the chunk path's fp32 tiles at K = 128
+    exceed its LDS budget)."""
+    print("fp32 K=128", T, H, V, flush=True)
+    inp = workloads.gen_forward(T, H, 128, V, dtype=torch.float32, device=DEV, seed=T + V + 1,
+                                init_std=0.1)
+    o, fin = kda.chunk_fwd(*(inp[x] for x in ORDER), init_state=inp["init_state"])
+    o_ref, f_ref = oracle_fwd(inp)
+    assert_close(np64(o), o_ref, torch.float32, "o")
+    assert_close(np64(fin), f_ref, torch.float32, "final")
+
+
+def test_fp32_k128_varlen():
+    print("fp32 K=128 varlen", flush=True)
+    lengths = [65, 0, 130, 1]
+    cu = torch.tensor(workloads.cu_from_lengths(lengths), dtype=torch.int32, device=DEV)
+    T, H = sum(lengths), 2
+    inp = workloads.gen_forward(T, H, 128, 128, dtype=torch.float32, device=DEV, seed=21,
+                                num_seqs=len(lengths), init_std=0.1)
+    o, fin = kda.chunk_fwd(*(inp[x] for x in ORDER), init_state=inp["init_state"], cu_seqlens=cu)
+    o_ref, f_ref = oracle_fwd(inp, cu=cu)
+    assert_close(np64(o), o_ref, torch.float32, "o")
+    assert_close(np64(fin), f_ref, torch.float32, "final")
 
 
 def test_wide_varlen_with_empty_sequence():
