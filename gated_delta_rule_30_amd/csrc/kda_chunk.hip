@@ -25,10 +25,14 @@
 //
 // Numerics. Inside a chunk every decay factor is formed relative to a 16-token sub-block
 // reference so it stays in fp32 range: row factors e^{b_i - e_{I-1}} <= 1, column factors
-// e^{e_J - b_j} <= 1 and per-channel block factors e^{e_{I-1} - e_J} <= 1 (J < I), with only
-// the diagonal sub-block using e^{-(block decay)} >= 1 (the renormalisation the Technical
-// Breakdown asks for in section 4's numerical-stability note). The solve runs in fp32 on
-// VALU (diagonal 16x16 blocks) and fp32 MFMA (off-diagonal blocks). The state stays fp32.
+// e^{e_J - b_j} <= 1 and per-channel block factors e^{e_{I-1} - e_J} <= 1 (J < I) (the
+// renormalisation the Technical Breakdown asks for in section 4's numerical-stability note).
+// A diagonal sub-block uses the column factor e^{-(block decay)} >= 1 only while every
+// channel's decay over its 16 tokens stays within 2^96; a stronger decay forms that block from
+// running products of the per-token decays instead, so any log alpha <= 0 gives finite
+// results. The solve runs in fp32 on VALU (diagonal 16x16 blocks) and fp32 MFMA (off-diagonal
+// blocks). The state stays fp32.
+#include <atomic>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -208,6 +212,9 @@ __global__ __launch_bounds__(256) void segment_kernel(const Entry* __restrict__ 
 
 // ====================================================================== PREP kernel
 constexpr int PREP_THREADS = 256;
+// Largest decay (log2 units) of a key channel over one 16-token sub-block for which the
+// diagonal sub-block is formed on the matrix cores (its column factor is at most 2^this).
+constexpr float DIAG_MAX_LOG2 = 96.f;
 
 // Sub-block pairs (I, J), J <= I, in the order (0,0) (1,0) (1,1) (2,0) ... (3,3).
 __host__ __device__ constexpr int pair_index(int I, int J) { return I * (I + 1) / 2 + J; }
@@ -394,6 +401,8 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   Raw raw;  // raw inputs of one task: filled one task ahead, consumed by phase 1
   load_raw(raw, pcur, task, -1);
   float kc[NG][4];  // phase 1 -> phase 2: this wave's column operand
+  bool diag_exact = false;     // phase 1 -> phase 2: this wave's diagonal block is formed
+  f32x4 adiag_x, pdiag_x;      // without the MFMA (strong decay): its A and P entries
 
   // Phase 1 of a task: its raw inputs become the LDS operands, the per-channel tables, kc and
   // the record parts that need nothing else (Qe, gamma, Ktilde^T).
@@ -474,6 +483,64 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     for (int u = 0; u < NG; ++u)
   #pragma unroll
       for (int r = 0; r < 4; ++r) dI[u][r] = __shfl(lv[u][r], lane | 15);
+    // Diagonal sub-block of this wave. Its MFMA form scales the column operand by the block's
+    // inverse decay 2^{-dI} >= 1, which is exact up to rounding while no channel decays by more
+    // than 2^DIAG_MAX_LOG2 over the sub-block. Beyond that, the block's A and P entries are
+    // formed without any factor above 1: for the token shift s, lane t carries
+    // Z_s(t) = k_{t-s} * alpha_{t-s+1} * ... * alpha_t (one DPP row shift and one product per
+    // step), so A_{t,t-s} = k_t . Z_s(t) and P_{t,t-s} = q_t . Z_s(t) over this lane's channels,
+    // summed over the four lanes that hold the token's channels. Decays then only underflow.
+    bool any_big = false;
+  #pragma unroll
+    for (int u = 0; u < NG; ++u)
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) any_big |= dI[u][r] < -DIAG_MAX_LOG2;
+    diag_exact = __any(any_big);
+    if (diag_exact) {
+      float* scr = sA + w * 2 * SUBBLK * SUBBLK;  // this wave's two 16 x 16 tiles (R1, free here)
+      float z[NG][4], al[NG][4];
+  #pragma unroll
+      for (int u = 0; u < NG; ++u)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          z[u][r] = kv[u][r];
+          al[u][r] = exp2_f(lv[u][r] - row_shr<1>(lv[u][r]));  // the token's own decay
+        }
+  #pragma unroll
+      for (int s = 0; s < SUBBLK; ++s) {
+        float a = 0.f, pq = 0.f;
+  #pragma unroll
+        for (int u = 0; u < NG; ++u)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            a += kv[u][r] * z[u][r];
+            pq += qv[u][r] * z[u][r];
+          }
+        a += __shfl_xor(a, 16);
+        pq += __shfl_xor(pq, 16);
+        a += __shfl_xor(a, 32);
+        pq += __shfl_xor(pq, 32);
+        // row t = m, column t - s (lanes m < s hold zero: the shift brought nothing in)
+        if (g == (s >> 2) && m >= s) {
+          scr[m * SUBBLK + (m - s)] = a;
+          scr[SUBBLK * SUBBLK + m * SUBBLK + (m - s)] = pq;
+        }
+        if (s + 1 < SUBBLK) {
+  #pragma unroll
+          for (int u = 0; u < NG; ++u)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) z[u][r] = row_shr<1>(z[u][r]) * al[u][r];
+        }
+      }
+      // back in the accumulator layout of the MFMA tile: lane (m, g) holds rows 4g .. 4g+3 of
+      // column m; entries above the diagonal are never written here and are masked later
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g + r;
+        adiag_x[r] = (m <= i) ? scr[i * SUBBLK + m] : 0.f;
+        pdiag_x[r] = (m <= i) ? scr[SUBBLK * SUBBLK + i * SUBBLK + m] : 0.f;
+      }
+    }
     if (m == 0) {
   #pragma unroll
       for (int u = 0; u < NG; ++u)
@@ -589,6 +656,11 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     tA[I] = f32x4{0.f, 0.f, 0.f, 0.f};
     tP[I] = tA[I];
     if (I < w) continue;
+    if (I == w && diag_exact) {
+      tA[I] = adiag_x;
+      tP[I] = pdiag_x;
+      continue;
+    }
     const float* drow = sD + pair_index(I, w) * K + 4 * g;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -1460,6 +1532,20 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
 }
 
 // ====================================================================== host side
+// Compute units of the current device, queried once per device and cached (256 if the query
+// fails).
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan* p) {
   if (N <= 0 || H <= 0 || T < 0 || K <= 0 || V <= 0) return false;
   const int64_t es = bf16 ? 2 : 4;
@@ -1536,10 +1622,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl, const 
   const int64_t chains8 = (chains + 7) / 8 * 8;
   const dim3 sgrid((unsigned)(chains8 * pl.n_slices));
   // prep: persistent workgroups, two per CU (its LDS and register budget), looping over tasks
-  int dev = 0, ncu = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
-    ncu = 256;
+  const int ncu = device_cu_count();
   const int64_t ptasks = pl.seg_entries * a.num_heads;
   const dim3 pgrid((unsigned)min(ptasks, (int64_t)2 * ncu));
   auto prep = [&](int64_t s, hipStream_t q) {

@@ -78,6 +78,8 @@ struct ChunkArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
+// Compute units of the current device (queried once per device, then cached).
+int device_cu_count();
 // Where a chunked pass keeps its (chunk, head) records when the caller wants them to outlive
 // it: base holds one slot of seg_entries * num_heads * rec_bytes per segment; prep = false
 // skips the record-building kernel because an earlier pass over the same chunks (with at

@@ -83,11 +83,15 @@ const char* kda_status_string(kda_status s);
 
 /*
  * Workspace bytes kda_chunk_fwd needs for this shape (0 if the arguments are invalid).
- * The value depends only on the arguments; it covers the device chunk table, a running state
- * and one chunk-record buffer, and is bounded (about 170 MB at H=32, K=V=128, bf16) plus
- * 32 bytes per chunk and 4*N*H*K*V bytes, whatever the sequence length. On the wide-key path
- * (K = 256) it holds an fp32 record for every chunk and head instead: 214 KB + 256 V
- * bytes per 64 tokens and head (e.g. 9.2 GB at H = 32, V = 256 and 65,536 tokens).
+ * The value depends only on the arguments. On the main path (K <= 128 with bf16 inputs,
+ * K <= 64 with fp32 inputs) it covers the device chunk table, a running state and one
+ * chunk-record buffer reused by every segment of the call: about 170 MB at H=32, K=V=128,
+ * bf16, plus 32 bytes per chunk and 4*N*H*K*V bytes, whatever the sequence length.
+ * The wide-key path (K = 256, and fp32 inputs at K = 128) holds an fp32 record for every
+ * chunk and head instead, so its workspace grows with the sequence length: per 64 tokens and
+ * head 214 KB + 256 V bytes at K = 256 (e.g. 9.2 GB at H = 32, V = 256 and 65,536 tokens) and
+ * 115 KB + 256 V bytes for fp32 inputs at K = 128 (e.g. 4.8 GB at H = 32, V = 128 and 65,536
+ * tokens).
  */
 size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                                     int32_t dk, int32_t dv, kda_dtype dtype);
@@ -114,9 +118,11 @@ size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int3
  *                     the call's stream work.
  * A sequence of length 0 gets final = init (or zero). T_total = 0 is a no-op apart from that.
  * States never cross sequence boundaries.
- * Numerical domain: the in-chunk factorisation keeps every factor within fp32 range when the
- * decay of any key channel over 16 consecutive tokens is at most e^80 (e.g. log_alpha >= -5
- * everywhere); stronger decays can overflow to Inf/NaN.
+ * Numerical domain: every log_alpha <= 0 gives finite results. In-chunk decay factors are
+ * formed relative to 16-token sub-block references so that each is at most 1; a diagonal
+ * sub-block whose decay exceeds 2^96 on some channel is formed from running products of the
+ * per-token decays instead (exact up to rounding; vanishing terms underflow to zero).
+ * Positive log_alpha values are accepted but lie outside this guarantee.
  * K = 256, and fp32 inputs at K = 128, run a separate path in fp32 (the chunk's products over
  * the key channels in parts of 64, every decay factor formed pairwise within the chunk, so any
  * decay is in range); it takes options = 0 only (other options give KDA_ERROR_NOT_SUPPORTED).

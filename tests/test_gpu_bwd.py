@@ -92,6 +92,19 @@ def test_bwd_strong_decay_no_overflow():
     _run(inp, seed=8, dtype=torch.float32)
 
 
+def test_bwd_extreme_decay():
+    """log alpha = -30 on a third of the key channels (those forget almost everything at each
+    token), bf16 inputs at K = V = 128 over a partial last chunk: every gradient finite and
+    equal to the oracle's."""
+    print("bwd extreme decay", flush=True)
+    T, H, K = 300, 2, 128
+    inp = workloads.gen_forward(T, H, K, K, dtype=torch.bfloat16, device=DEV, seed=9, init_std=0.1)
+    g = inp["log_alpha"].float()
+    g[..., ::3] = -30.0
+    inp["log_alpha"] = g.to(torch.bfloat16)
+    _run(inp, seed=9)
+
+
 def test_bwd_empty_input():
     """No tokens: the initial state's gradient is the final state's."""
     print("bwd empty", flush=True)

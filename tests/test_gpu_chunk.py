@@ -122,17 +122,53 @@ def test_head_dims_ragged_varlen(dtype, K, V):
     assert torch.equal(fin[4], inp["init_state"][4])
 
 
-def test_strong_decay_within_domain():
-    """log alpha = -5 on a third of the channels (the documented limit), random elsewhere."""
-    T, H, K, V = 300, 2, 128, 64
-    inp = _gen(T, H, K, V, torch.bfloat16, seed=9)
+@pytest.mark.parametrize("dtype,K,V,lg,every", [
+    (torch.bfloat16, 128, 64, -8.0, 3),
+    (torch.bfloat16, 128, 128, -30.0, 3),
+    (torch.bfloat16, 64, 64, -8.0, 3),
+    (torch.bfloat16, 64, 128, -30.0, 3),
+    (torch.bfloat16, 32, 32, -30.0, 1),
+    (torch.bfloat16, 128, 128, -5.0, 3),
+    (torch.float32, 32, 32, -30.0, 3),
+    (torch.float32, 64, 64, -8.0, 1),
+])
+def test_strong_decay(dtype, K, V, lg, every):
+    """log alpha = lg on every `every`-th key channel (random elsewhere): decays far beyond the
+    range where a 16-token sub-block's inverse decay fits in fp32 (-8 and -30 per token); the
+    outputs and final states stay finite and match the oracle. Ragged lengths put the strong
+    decays in full and partial chunks."""
+    print("strong decay", dtype, K, V, lg, every, flush=True)
+    lengths = [300, 1, 64, 77]
+    T, H = sum(lengths), 2
+    inp = _gen(T, H, K, V, dtype, seed=int(-lg) + K, N=len(lengths))
     g = inp["log_alpha"].float()
-    g[..., ::3] = -5.0
+    g[..., ::every] = lg
+    inp["log_alpha"] = g.to(dtype)
+    cu = _cu(lengths)
+    o, fin = _fwd(inp, cu=cu)
+    o_ref, f_ref = oracle_fwd(inp, cu=cu)
+    assert_close(np64(o), o_ref, dtype, "o")
+    assert_close(np64(fin), f_ref, dtype, "final")
+
+
+def test_strong_decay_chunk_matches_recurrent():
+    """Chunked and recurrent paths agree when a third of the channels forget almost entirely
+    at every token (log alpha = -30) and the others decay at log alpha ~ -6."""
+    print("strong decay chunk vs recurrent", flush=True)
+    T, H, K, V = 200, 2, 128, 128
+    inp = _gen(T, H, K, V, torch.bfloat16, seed=41)
+    g = inp["log_alpha"].float() * 60.0
+    g[..., ::3] = -30.0
     inp["log_alpha"] = g.to(torch.bfloat16)
     o, fin = _fwd(inp)
-    o_ref, f_ref = oracle_fwd(inp)
-    assert_close(np64(o), o_ref, torch.bfloat16, "o")
-    assert_close(np64(fin), f_ref, torch.bfloat16, "final")
+    st = inp["init_state"].clone()
+    od = torch.empty_like(o)
+    for t in range(T):
+        od[t] = kda.decode_step(*(inp[x][t:t + 1] for x in ORDER), state=st)[0]
+    tol = TOL[torch.bfloat16]
+    assert torch.isfinite(o.float()).all() and torch.isfinite(fin).all()
+    assert rel_err(np64(o), np64(od)) <= tol
+    assert rel_err(np64(fin), np64(st)) <= tol
 
 
 def test_no_init_and_no_final():

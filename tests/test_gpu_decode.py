@@ -61,6 +61,32 @@ def test_decode_full_size_256x32():
     _run_steps(w["num_seqs"], w["H"], w["K"], w["V"], torch.bfloat16, 4, seed=w["seed"])
 
 
+@pytest.mark.timeout(900)
+def test_decode_full_size_512_steps():
+    """The whole serving loop: 256 sequences x 32 heads, K=V=128, fp32 state ~ 0.1 N(0,1),
+    512 sequential kda_decode_step calls with fresh bf16 inputs drawn as in the tiny workload.
+    The output of every step on all 8,192 heads, and the state after steps 256 and 512,
+    against the fp64 oracle stepping from the same state."""
+    w = workloads.WORKLOADS["decode"]
+    N, H, K, V, steps = w["num_seqs"], w["H"], w["K"], w["V"], w["steps"]
+    print("decode full size, %d steps" % steps, flush=True)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(w["seed"])
+    state = w["state_std"] * torch.randn((N, H, K, V), generator=gen, device=DEV)
+    ref = np64(state).copy()
+    o = torch.empty((N, H, V), dtype=torch.bfloat16, device=DEV)
+    worst = 0.0
+    for s in range(steps):
+        inp = workloads.gen_decode_inputs(N, H, K, V, dtype=torch.bfloat16, device=DEV, gen=gen)
+        kda.decode_step(*(inp[x] for x in ORDER), state=state, o=o)
+        o_ref = oracle.kda_step(*(np64(inp[x]) for x in ORDER), ref)
+        worst = max(worst, assert_close(np64(o), o_ref, torch.bfloat16, "o step %d" % s))
+        if s + 1 in (steps // 2, steps):
+            worst = max(worst, assert_close(np64(state), ref, torch.bfloat16, "state after %d" % (s + 1)))
+        if (s + 1) % 64 == 0:
+            print("  step %d: worst rel err so far %.3e" % (s + 1, worst), flush=True)
+
+
 def test_decode_is_deterministic_and_in_place():
     N, H, K, V = 8, 4, 128, 128
     gen = torch.Generator(device=DEV)

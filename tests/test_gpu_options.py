@@ -45,6 +45,29 @@ def test_chunk_options_ragged_varlen(opts, dtype, K, V):
     assert_close(np64(fin), f_ref, dtype, "final")
 
 
+@pytest.mark.parametrize("opts,dtype,K,V", [
+    (GL, torch.bfloat16, 128, 128),
+    (GL, torch.bfloat16, 64, 64),
+    (GL | BL | L2, torch.bfloat16, 128, 64),
+    (SG | GL, torch.bfloat16, 128, 128),
+    (SG | GL, torch.float32, 32, 32),
+])
+def test_chunk_strong_gate_logits(opts, dtype, K, V):
+    """Gate logits z ~ U(-12, -6): alpha = sigmoid(z) between e^{-12} and e^{-6} per token, the
+    range trained gates reach; the in-chunk decays over 16 tokens leave fp32 range by far."""
+    print("chunk strong gate logits", opts, dtype, K, V, flush=True)
+    H = 2
+    T = sum(LENGTHS)
+    inp = workloads.gen_raw(T, H, K, V, opts, dtype=dtype, device=DEV, seed=opts + K + 3,
+                            num_seqs=len(LENGTHS), init_std=0.1, gate_logit_range=(-12.0, -6.0))
+    cu = _cu(LENGTHS)
+    o, fin = kda.chunk_fwd(*(inp[x] for x in ORDER), init_state=inp["init_state"], cu_seqlens=cu,
+                           options=opts)
+    o_ref, f_ref = oracle_fwd(inp, cu=cu, options=opts)
+    assert_close(np64(o), o_ref, dtype, "o")
+    assert_close(np64(fin), f_ref, dtype, "final")
+
+
 def test_chunk_all_options_long_sampled_heads():
     """Every option on the long-prefill shape (T=65536, H=32, K=V=128, bf16): the gated delta
     rule with gate and beta logits and unit-norm q, k; two heads against the oracle."""

@@ -62,6 +62,22 @@ def test_scan_slow_decay_short_groups(N, T, H, K, dtype, G):
     assert rel_err(alone, o_ref[g1]) > 10 * TOL[dtype]
 
 
+def test_scan_strong_decay():
+    """log alpha = -30 on a third of the channels: the group transitions M_g are nearly
+    singular along those channels and the in-chunk blocks take the exact strong-decay form."""
+    print("scan strong decay", flush=True)
+    N, T, H, K, G = 1, 3000, 2, 128, 6
+    inp = workloads.gen_forward(T, H, K, K, dtype=torch.bfloat16, device=DEV, seed=13, init_std=0.1)
+    g = inp["log_alpha"].float()
+    g[..., ::3] = -30.0
+    inp["log_alpha"] = g.to(torch.bfloat16)
+    o, fin = kda.chunk_fwd_scan(*(inp[x] for x in ORDER), init_state=inp["init_state"],
+                                num_seqs=N, num_groups=G)
+    o_ref, f_ref = oracle_fwd(inp, cu=_cu(N, T))
+    assert_close(np64(o), o_ref, torch.bfloat16, "o")
+    assert_close(np64(fin), f_ref, torch.bfloat16, "final")
+
+
 def test_scan_equals_chunk_fwd_long():
     """One 20000-token sequence over 3 heads, K=V=128 bf16, 8 groups: the scan and the plain
     chunk path agree."""

@@ -125,12 +125,14 @@ OPT_SCALAR_GATE, OPT_GATE_LOGITS, OPT_BETA_LOGITS, OPT_L2NORM_QK = 1, 2, 4, 8
 
 
 def gen_raw(T_total: int, H: int, K: int, V: int, options: int, *, dtype=None, device="cpu",
-            seed: int = 0, num_seqs: int = 1, init_std: float | None = None):
+            seed: int = 0, num_seqs: int = 1, init_std: float | None = None,
+            gate_logit_range=(2.0, 7.0)):
     """Seeded raw inputs for the option bits, token-major:
     q, k ~ N(0,1), times U(0.5, 4) per token and head with OPT_L2NORM_QK (left for the kernel
     to normalise), else L2-normalised here; v ~ N(0,1); the gate [T, H, K] or, with
-    OPT_SCALAR_GATE, [T, H]: logits z ~ U(2, 7) with OPT_GATE_LOGITS (alpha = sigmoid(z) in
-    [0.88, 0.999]), else log alpha = log U[0.9, 1); beta logits ~ 1.5 N(0,1) with
+    OPT_SCALAR_GATE, [T, H]: logits z ~ U(gate_logit_range), by default U(2, 7), with
+    OPT_GATE_LOGITS (alpha = sigmoid(z) in [0.88, 0.999]; U(-12, -6) gives the strong decays
+    alpha ~ e^{-6} .. e^{-12}), else log alpha = log U[0.9, 1); beta logits ~ 1.5 N(0,1) with
     OPT_BETA_LOGITS, else beta ~ U(0, 1). Every tensor is cast to ``dtype``."""
     torch = _torch()
     dtype = dtype or torch.bfloat16
@@ -148,7 +150,8 @@ def gen_raw(T_total: int, H: int, K: int, V: int, options: int, *, dtype=None, d
     out["v"] = torch.randn((T_total, H, V), **f).to(dtype)
     gshape = (T_total, H) if options & OPT_SCALAR_GATE else (T_total, H, K)
     if options & OPT_GATE_LOGITS:
-        g = 2.0 + 5.0 * torch.rand(gshape, **f)
+        lo, hi = gate_logit_range
+        g = lo + (hi - lo) * torch.rand(gshape, **f)
     else:
         g = torch.log(0.9 + 0.1 * torch.rand(gshape, **f))
     out["log_alpha"] = g.to(dtype)
