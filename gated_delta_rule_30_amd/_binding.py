@@ -58,6 +58,9 @@ def _lib():
         lib.kda_chunk_fwd_ex.restype = ctypes.c_int
         lib.kda_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                          ctypes.c_int, u32, vp, vp, vp, sz, vp]
+        lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+        lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                              i32, ctypes.c_int, u32, vp, vp, vp]
         lib.kda_chunk_fwd_scan_workspace_size.restype = sz
         lib.kda_chunk_fwd_scan_workspace_size.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int, i32]
         lib.kda_chunk_fwd_scan.restype = ctypes.c_int
@@ -167,6 +170,45 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, num_se
                                  workspace.numel() * workspace.element_size(), _stream(device))
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd")
+    return o, final_state
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None,
+                      num_seqs=None, o=None, final_state=None, options=0):
+    """kda_chunk_fwd_noalloc on torch tensors: chunk_fwd without a workspace (the library's
+    fixed scratch serves it). final_state is always produced; ``o`` and ``final_state`` may be
+    passed preallocated (then nothing is allocated here either). Returns (o, final_state)."""
+    device = q.device
+    T, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, device)
+        N = cu_seqlens.shape[0] - 1
+        if num_seqs is not None and num_seqs != N:
+            raise ValueError("num_seqs does not match cu_seqlens")
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
+    gshape = (T, H) if options & OPT_SCALAR_GATE else (T, H, K)
+    for name, t, shp in (("q", q, (T, H, K)), ("k", k, (T, H, K)), ("v", v, (T, H, V)),
+                         ("log_alpha", log_alpha, gshape), ("beta", beta, (T, H))):
+        _check(t, name, shp, dt, device)
+    if init_state is not None:
+        _check(init_state, "init_state", (N, H, K, V), torch.float32, device)
+    if o is None:
+        o = torch.empty((T, H, V), dtype=dt, device=device)
+    else:
+        _check(o, "o", (T, H, V), dt, device)
+    if final_state is None:
+        final_state = torch.empty((N, H, K, V), dtype=torch.float32, device=device)
+    else:
+        _check(final_state, "final_state", (N, H, K, V), torch.float32, device)
+    st = _lib().kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                      _ptr(init_state), _ptr(cu_seqlens), N, T, H, K, V, code,
+                                      int(options), _ptr(o), _ptr(final_state), _stream(device))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_noalloc")
     return o, final_state
 
 

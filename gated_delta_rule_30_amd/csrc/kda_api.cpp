@@ -73,13 +73,14 @@ extern "C" size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_t
   return pl.total_bytes;
 }
 
-extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v,
-                                       const void* log_alpha, const void* beta,
-                                       const float* init_state, const int32_t* cu_seqlens,
-                                       int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
-                                       int32_t dk, int32_t dv, kda_dtype dtype, uint32_t options,
-                                       void* o, float* final_state, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
+// Everything kda_chunk_fwd_ex checks before it looks at the workspace; fills the launch
+// arguments (all but the workspace).
+kda_status kda::prepare_chunk_fwd(const void* q, const void* k, const void* v,
+                                  const void* log_alpha, const void* beta,
+                                  const float* init_state, const int32_t* cu_seqlens,
+                                  int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                  int32_t dk, int32_t dv, kda_dtype dtype, uint32_t options,
+                                  void* o, float* final_state, void* stream, ChunkArgs* a) {
   kda_status st = check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_SUCCESS) return st;
   if (options & ~kAllOptions) return KDA_ERROR_NOT_SUPPORTED;
@@ -87,7 +88,6 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
   const int32_t gdim = (options & KDA_OPT_SCALAR_GATE) ? 1 : dk;  // gate values per token and head
   if (cu_seqlens == nullptr && total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
   if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERROR_INVALID_VALUE;
-  if (!workspace) return KDA_ERROR_INVALID_VALUE;
   // vectors of K or V elements need 16 bytes; per-token scalars (beta, a scalar gate) their element
   const bool scalar_gate = (options & KDA_OPT_SCALAR_GATE) != 0;
   const void* ptrs[] = {q, k, v, scalar_gate ? nullptr : log_alpha, init_state, o, final_state};
@@ -96,7 +96,6 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
   if ((beta && !aligned_to(beta, esize(dtype))) || (cu_seqlens && !aligned_to(cu_seqlens, 4)) ||
       (log_alpha && !aligned_to(log_alpha, esize(dtype))))
     return KDA_ERROR_INVALID_VALUE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERROR_INVALID_VALUE;
   const size_t sbytes = (size_t)num_seqs * num_heads * dk * dv * sizeof(float);
   if (init_state && final_state && init_state != final_state &&
       overlap(init_state, sbytes, final_state, sbytes))
@@ -109,6 +108,43 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
         overlap(o, obytes, log_alpha, gbytes) || overlap(o, obytes, v, obytes))
       return KDA_ERROR_INVALID_VALUE;
   }
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->g = log_alpha;
+  a->beta = beta;
+  a->init_state = init_state;
+  a->cu_seqlens = cu_seqlens;
+  a->num_seqs = num_seqs;
+  a->total_tokens = total_tokens;
+  a->num_heads = num_heads;
+  a->dk = dk;
+  a->dv = dv;
+  a->dtype_bf16 = dtype == KDA_DTYPE_BF16;
+  a->options = options;
+  a->o = o;
+  a->final_state = final_state;
+  a->workspace = nullptr;
+  a->stream = stream;
+  return KDA_SUCCESS;
+}
+
+bool kda::is_wide_path(int32_t dk, kda_dtype dtype) { return wide_path(dk, dtype); }
+
+extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v,
+                                       const void* log_alpha, const void* beta,
+                                       const float* init_state, const int32_t* cu_seqlens,
+                                       int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                       int32_t dk, int32_t dv, kda_dtype dtype, uint32_t options,
+                                       void* o, float* final_state, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  kda::ChunkArgs a;
+  kda_status st = kda::prepare_chunk_fwd(q, k, v, log_alpha, beta, init_state, cu_seqlens,
+                                         num_seqs, total_tokens, num_heads, dk, dv, dtype, options,
+                                         o, final_state, stream, &a);
+  if (st != KDA_SUCCESS) return st;
+  if (!workspace) return KDA_ERROR_INVALID_VALUE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERROR_INVALID_VALUE;
   kda::ChunkPlan pl;
   kda::WidePlan wp;
   if (wide_path(dk, dtype)) {
@@ -119,26 +155,7 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
       return KDA_ERROR_INVALID_VALUE;
     if (workspace_bytes < pl.total_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
   }
-
-  kda::ChunkArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.g = log_alpha;
-  a.beta = beta;
-  a.init_state = init_state;
-  a.cu_seqlens = cu_seqlens;
-  a.num_seqs = num_seqs;
-  a.total_tokens = total_tokens;
-  a.num_heads = num_heads;
-  a.dk = dk;
-  a.dv = dv;
-  a.dtype_bf16 = dtype == KDA_DTYPE_BF16;
-  a.options = options;
-  a.o = o;
-  a.final_state = final_state;
   a.workspace = workspace;
-  a.stream = stream;
   hipError_t e = wide_path(dk, dtype) ? kda::launch_chunk_fwd_wide(a, wp) : kda::launch_chunk_fwd(a, pl);
   return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
 }

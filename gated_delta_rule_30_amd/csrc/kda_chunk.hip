@@ -1546,21 +1546,27 @@ int device_cu_count() {
   return n;
 }
 
-bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan* p) {
+bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan* p,
+                     size_t max_rec_buf_bytes, bool running_state) {
   if (N <= 0 || H <= 0 || T < 0 || K <= 0 || V <= 0) return false;
   const int64_t es = bf16 ? 2 : 4;
   int64_t ub = (T + (int64_t)N * (CHUNK - 1)) / CHUNK;
   if (ub > T) ub = T;
   p->ub_entries = ub;
+  // the fixed part (a multiple of 1 KB), then the chunk's V (CHUNK x V, a multiple of 1 KB)
+  p->rec_bytes = ((3LL * CHUNK * K + 2LL * CHUNK * CHUNK) * es + 4LL * K + 1023) / 1024 * 1024 +
+                 (int64_t)CHUNK * V * es;
   int64_t E = SEG_CHUNK_HEADS / H;
+  if (max_rec_buf_bytes > 0) {  // a cap on the record buffer: fewer chunks per segment
+    const int64_t cap = (int64_t)(max_rec_buf_bytes / ((size_t)H * p->rec_bytes));
+    if (cap < E) E = cap;
+    if (E < 1) return false;
+  }
   if (E < 1) E = 1;
   if (ub > 0 && E > ub) E = ub;
   p->seg_entries = E;
   p->num_segs = ub > 0 ? (ub + E - 1) / E : 0;
   p->slots = N < E ? N : E;
-  // the fixed part (a multiple of 1 KB), then the chunk's V (CHUNK x V, a multiple of 1 KB)
-  p->rec_bytes = ((3LL * CHUNK * K + 2LL * CHUNK * CHUNK) * es + 4LL * K + 1023) / 1024 * 1024 +
-                 (int64_t)CHUNK * V * es;
   // V split: slices of 16 columns, one wave each
   p->n_slices = V / 16;
   p->vs = 16;
@@ -1577,7 +1583,7 @@ bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan
   p->off_seg_count = off;
   off += al((size_t)p->num_segs * 4);
   p->off_state = off;
-  off += al((size_t)N * H * K * V * 4);
+  if (running_state) off += al((size_t)N * H * K * V * 4);
   p->off_rec = off;
   p->rec_buf_bytes = (size_t)E * H * p->rec_bytes;
   off += p->rec_buf_bytes;

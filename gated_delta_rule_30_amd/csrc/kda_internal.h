@@ -59,8 +59,12 @@ struct ChunkPlan {
   size_t total_bytes;
 };
 
+// max_rec_buf_bytes > 0 caps the record buffer (fewer chunks per segment; false if not even
+// one chunk of every head fits); running_state = false leaves out the running state, which a
+// call with a final_state buffer does not use.
 bool make_chunk_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv,
-                     bool bf16, ChunkPlan* p);
+                     bool bf16, ChunkPlan* p, size_t max_rec_buf_bytes = 0,
+                     bool running_state = true);
 
 struct ChunkArgs {
   const void *q, *k, *v, *g, *beta;

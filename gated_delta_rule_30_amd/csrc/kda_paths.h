@@ -3,9 +3,20 @@
 // backward. Kept apart from kda_internal.h, which describes the main forward and decode.
 #pragma once
 
+#include "../../include/kda.h"
 #include "kda_internal.h"
 
 namespace kda {
+
+// The argument checks of kda_chunk_fwd_ex that do not involve the workspace; on success *a
+// holds the launch arguments with workspace = nullptr.
+kda_status prepare_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                             const void* beta, const float* init_state, const int32_t* cu_seqlens,
+                             int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t dk,
+                             int32_t dv, kda_dtype dtype, uint32_t options, void* o,
+                             float* final_state, void* stream, ChunkArgs* a);
+// Whether kda_chunk_fwd runs this head dim and dtype on the wide-key path (kda_wide.hip).
+bool is_wide_path(int32_t dk, kda_dtype dtype);
 
 // Chunk-parallel scan over equal-length sequences split into G groups of whole chunks: a pass
 // over the groups with V + K state columns, a combine, and a pass from the groups' initial

@@ -146,6 +146,29 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
                             void* stream);
 
 /*
+ * kda_chunk_fwd_ex without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It calls no allocating routine. Its scratch is one fixed array of 128 MiB inside the library,
+ * held on each device the entry point runs on until the process ends; it holds the chunk
+ * table and one record buffer, which is capped to fit, so a call runs in more (shorter)
+ * segments than kda_chunk_fwd_ex. Results are the same as kda_chunk_fwd_ex's.
+ * Differences from kda_chunk_fwd_ex:
+ *  - final_state is required (KDA_ERROR_INVALID_VALUE if NULL): it carries the running state;
+ *  - shapes on the wide-key path (K = 256, fp32 at K = 128) give KDA_ERROR_NOT_SUPPORTED;
+ *  - a shape whose chunk table plus one chunk record per head exceeds the scratch gives
+ *    KDA_ERROR_WORKSPACE_TOO_SMALL (e.g. more than about 2^24 chunks in total);
+ *  - every call on a device shares that device's scratch: calls that overlap in time on one
+ *    device (different streams, or different host threads without ordering) race and must be
+ *    serialised by the caller.
+ * Other arguments, layouts and errors as for kda_chunk_fwd_ex.
+ */
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 const void* log_alpha, const void* beta, const float* init_state,
+                                 const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                 int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype,
+                                 uint32_t options, void* o, float* final_state, void* stream);
+
+/*
  * Chunk-parallel scan variant of kda_chunk_fwd_ex for long sequences over few heads. Each of the
  * num_seqs sequences (equal lengths total_tokens / num_seqs, no cu_seqlens) splits into
  * num_groups groups of whole 64-token chunks; one chunked pass over all groups with the values

@@ -18,6 +18,7 @@ F32, BF16 = 0, 1
 def test_every_declared_symbol_is_exported():
     names = kda.declared_functions()
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_fwd_workspace_size",
+                          "kda_chunk_fwd_noalloc",
                           "kda_chunk_fwd_scan", "kda_chunk_fwd_scan_workspace_size",
                           "kda_chunk_bwd", "kda_chunk_bwd_workspace_size",
                           "kda_decode_step", "kda_decode_step_ex", "kda_status_string"}
@@ -119,6 +120,38 @@ def _chunk(L, **kw):
 ])
 def test_chunk_fwd_argument_errors(kw, expect):
     assert _chunk(kda.lib(), **kw) == expect
+
+
+def _noalloc(L, **kw):
+    a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, init=None, cu=None, N=1, T=64, H=2,
+             dk=32, dv=32, dtype=BF16, opts=0, o=6 * A, fin=7 * A, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kda_chunk_fwd_noalloc(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]),
+                                   vp(a["init"]), vp(a["cu"]), a["N"], a["T"], a["H"], a["dk"],
+                                   a["dv"], a["dtype"], a["opts"], vp(a["o"]), vp(a["fin"]),
+                                   vp(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(fin=None), INVALID),             # the running state lives in final_state
+    (dict(N=0), INVALID),
+    (dict(dk=48), NOT_SUPPORTED),
+    (dict(dk=256), NOT_SUPPORTED),         # the wide-key path is not served from the scratch
+    (dict(dtype=F32, dk=128), NOT_SUPPORTED),
+    (dict(opts=16), NOT_SUPPORTED),
+    (dict(q=A + 8), INVALID),
+    (dict(o=A), INVALID),
+    (dict(N=3, T=64), INVALID),
+    # 2^24 chunks: the chunk table alone exceeds the scratch (tensors 2^40 bytes apart)
+    (dict(T=1 << 30, q=1 << 40, k=2 << 40, v=3 << 40, g=4 << 40, beta=5 << 40, o=6 << 40,
+          fin=7 << 40), WS_SMALL),
+])
+def test_chunk_fwd_noalloc_argument_errors(kw, expect):
+    """The no-allocation forward rejects what kda_chunk_fwd_ex rejects, plus a missing
+    final_state, the wide-key shapes and problems whose tables exceed its fixed scratch; all
+    before anything is enqueued."""
+    assert _noalloc(kda.lib(), **kw) == expect
 
 
 def _decode(L, **kw):
