@@ -118,6 +118,41 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib, command):
     print(json.dumps(res))
 
 
+# bf16 matrix-core work of one kda_chunk_fwd call from the SQ_INSTS_VALU_MFMA_MOPS_BF16 counter
+# (one unit = 512 flops) of a `rocprofv3 --pmc` run of this script, stored with the source hash.
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_ops_long_prefill.json")
+MOPS_FLOPS = 512
+
+
+def summarize_mfma(csv_path, command):
+    rows = _per_kernel(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    busy = _per_kernel(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES")
+    calls = sum(1 for n, _ in _per_kernel(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16") if "table_kernel" in n)
+    pick = lambda rs: sum(v for n, v in rs if any(k in n for k in CHUNK_KERNELS)
+                          and not any(x in n for x in OTHER_PATHS))
+    per_kernel = {}
+    for n, v in rows:
+        if any(k in n for k in CHUNK_KERNELS) and not any(x in n for x in OTHER_PATHS):
+            short = n.split("(")[0].replace("void ", "")
+            per_kernel[short] = per_kernel.get(short, 0.0) + v * MOPS_FLOPS / max(calls, 1)
+    res = {"source_sha256": source_hash(), "command": command, "chunk_calls": calls,
+           "bf16_flops_per_call": pick(rows) * MOPS_FLOPS / max(calls, 1),
+           "mfma_busy_cycles_per_call": pick(busy) / max(calls, 1),
+           "bf16_flops_per_call_by_kernel": per_kernel}
+    with open(MFMA_FILE, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res))
+
+
+def measured_mfma_flops():
+    try:
+        with open(MFMA_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    return t.get("bf16_flops_per_call") if t.get("source_sha256") == source_hash() else None
+
+
 def measured_traffic():
     try:
         with open(TRAFFIC_FILE) as fh:
@@ -127,6 +162,19 @@ def measured_traffic():
     if t.get("source_sha256") != source_hash():
         return None, None
     return t.get("chunk_bytes_per_call"), t.get("decode_bytes_per_call")
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def stream_reference():
@@ -176,11 +224,23 @@ def main():
                     help="skip kda_chunk_fwd at K = V = 256 (the wide-key path) on the long shape")
     ap.add_argument("--no-bwd-bench", action="store_true",
                     help="skip the training backward (kda_chunk_bwd) on the long-prefill shape")
+    ap.add_argument("--no-varlen-bench", action="store_true",
+                    help="skip the 16-sequence varlen prefill (129,148 tokens, H=32)")
+    ap.add_argument("--no-prefill1m-bench", action="store_true",
+                    help="skip the 1,048,576-token prefill (H=32)")
+    ap.add_argument("--no-decode-loop-bench", action="store_true",
+                    help="skip the 512-call decode loop (256 sequences x 32 heads)")
+    ap.add_argument("--cpu-single-tokens", type=int, default=2048,
+                    help="tokens (all 32 heads) of the prefill workload the oracle is timed on "
+                         "with one thread")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run torch.neg over this many MiB of fp32 (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the per-call HBM traffic record from two counter runs and exit")
     ap.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
+    ap.add_argument("--summarize-mfma", metavar="CSV",
+                    help="write the per-call bf16 matrix-core record from a counter run "
+                         "(SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES) and exit")
     ap.add_argument("--stream-reference", action="store_true",
                     help="time torch's elementwise kernels over 0.5-4 GiB of fp32 (bytes read + "
                          "written per second) as a practical HBM reference, and exit")
@@ -188,6 +248,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_calibration_mib,
                       args.pmc_command)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.pmc_command)
         return
     if args.stream_reference:
         stream_reference()
@@ -275,6 +338,10 @@ def main():
         "mfma_frac_alg": cf / chunk_s / PEAK_BF16,
         "mfma_frac_dense": cfd / chunk_s / PEAK_BF16,
     }
+    mf = measured_mfma_flops()
+    if mf is not None:  # bf16 flops the matrix cores executed per call, by counter
+        chunk["mfma_bf16_flops_counter"] = mf
+        chunk["mfma_frac_counter"] = mf / chunk_s / PEAK_BF16
     decode = {
         "workload": "256 seqs x 32 heads, K=V=128, fp32 state, bf16 inputs",
         "ms": decode_ms,
@@ -416,6 +483,81 @@ def main():
                 "workspace_GB": wsw.numel() / 1e9}
         del winp, ow, fw, wsw
 
+    # ---------------- the other prefill workloads: 16 packed sequences of log-uniform lengths
+    # (129,148 tokens, per-sequence initial states) and one 1,048,576-token sequence
+    def time_calls(fn, calls, warm):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(calls):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / calls
+
+    def prefill_entry(name, desc, calls):
+        w = workloads.WORKLOADS[name]
+        pin = workloads.make_workload(name, device=dev)
+        Tt = int(pin["q"].shape[0])
+        N = int(pin["num_seqs"])
+        po = torch.empty((Tt, H, V), dtype=torch.bfloat16, device=dev)
+        pf = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+        pws = torch.empty(kda.workspace_size(N, Tt, H, K, V, torch.bfloat16), dtype=torch.uint8,
+                          device=dev)
+
+        def call():
+            kda.chunk_fwd(*(pin[x] for x in names), init_state=pin["init_state"],
+                          cu_seqlens=pin["cu_seqlens"], num_seqs=N, o=po, final_state=pf,
+                          workspace=pws)
+
+        ms = time_calls(call, calls, 1)
+        pb = chunk_alg_bytes(Tt, H, K, V, 2, N, pin["init_state"] is not None, True)
+        pfl = chunk_alg_flops(Tt, H, K, V)
+        res = {"workload": desc, "ms": ms, "calls": calls, "tokens": Tt,
+               "tokens_per_s": Tt / (ms * 1e-3), "alg_bytes": pb,
+               "hbm_frac": pb / (ms * 1e-3) / PEAK_HBM,
+               "mfma_frac_alg": pfl / (ms * 1e-3) / PEAK_BF16}
+        del pin, po, pf, pws
+        torch.cuda.empty_cache()
+        return res
+
+    varlen = None
+    if not args.no_varlen_bench:
+        varlen = prefill_entry("varlen", "16 packed sequences, lengths log-uniform in [1024, "
+                               "32768] (129,148 tokens), H=32, K=V=128 bf16, per-sequence init "
+                               "states 0.1*N(0,1)", max(1, min(args.steps, 10)))
+    prefill1m = None
+    if not args.no_prefill1m_bench:
+        prefill1m = prefill_entry("prefill1m", "B=1 H=32 T=1048576 K=V=128 bf16, zero init",
+                                  max(1, min(args.steps, 3)))
+
+    # ---------------- the serving loop: 512 sequential kda_decode_step calls over 256 sequences x
+    # 32 heads, fresh bf16 inputs at every step (generated beforehand), timed back to back
+    decode_loop = None
+    if not args.no_decode_loop_bench:
+        steps_d = wd["steps"]
+        gl = torch.Generator(device=dev)
+        gl.manual_seed(wd["seed"] + 3)
+        st_l = wd["state_std"] * torch.randn((Nd, Hd, K, V), generator=gl, device=dev)
+        step_inp = [workloads.gen_decode_inputs(Nd, Hd, K, V, dtype=torch.bfloat16, device=dev,
+                                                gen=gl) for _ in range(steps_d)]
+        od_l = torch.empty((Nd, Hd, V), dtype=torch.bfloat16, device=dev)
+
+        def loop():
+            for si in step_inp:
+                kda.decode_step(*(si[x] for x in names), state=st_l, o=od_l)
+
+        lms = time_calls(loop, 1, 1)
+        decode_loop = {"workload": "256 seqs x 32 heads, K=V=128, fp32 state, %d sequential "
+                                   "steps with fresh bf16 inputs" % steps_d,
+                       "ms": lms, "steps": steps_d, "ms_per_step": lms / steps_d,
+                       "tokens_per_s": Nd * steps_d / (lms * 1e-3),
+                       "GB_per_s": db * steps_d / (lms * 1e-3) / 1e9,
+                       "hbm_frac": db * steps_d / (lms * 1e-3) / PEAK_HBM}
+        del step_inp, st_l, od_l
+
     # ---------------- the training backward on the long-prefill shape (gradients of
     # sum(dO * o) + sum(dS * S_final) for every input and the initial state, fp32)
     bwd = None
@@ -464,10 +606,17 @@ def main():
         ta = time.perf_counter()
         o_ref, _ = oracle.kda_fwd(*sample, init_state=init_np)
         tb = time.perf_counter()
+        S1 = min(args.cpu_single_tokens, S)
+        tc = time.perf_counter()
+        oracle.kda_fwd(*(x[:S1] for x in sample), init_state=init_np, threads=1)
+        td = time.perf_counter()
         cpu = {"value": S / (tb - ta), "unit": "tokens/s", "cores": oracle.max_threads(),
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model(),
                "sample": "first %d tokens x all %d heads of the prefill workload (fp64 token "
-                         "recurrence, %.1f s wall)" % (S, H, tb - ta)}
+                         "recurrence, %.1f s wall)" % (S, H, tb - ta),
+               "single_thread": {"value": S1 / (td - tc), "unit": "tokens/s",
+                                 "sample": "first %d tokens x all %d heads, one thread "
+                                           "(%.1f s wall)" % (S1, H, td - tc)}}
         got = o[:S].float().cpu().numpy().astype(np.float64)
         parity = float(np.abs(got - o_ref).max() / np.abs(o_ref).max())
 
@@ -496,6 +645,9 @@ def main():
         "few_head_scan": scan,
         "training_backward": bwd,
         "wide_key": wide,
+        "varlen_prefill": varlen,
+        "prefill_1m": prefill1m,
+        "decode_loop": decode_loop,
         "parity_sample_max_rel_err": parity,
     }
     print(json.dumps(out), flush=True)
