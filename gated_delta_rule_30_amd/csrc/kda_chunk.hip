@@ -358,15 +358,18 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   };
   // V of the current task into its record, slice-major (the state kernel then reads a slice's
   // CHUNK x 16 values as one contiguous block instead of gathering 16 values from each of CHUNK
-  // token rows). A token row is vpr 16-byte pieces; each thread copies vpt pieces in up to four
-  // batches of four, spread over phases 2-5: a batch is loaded one phase before it is stored.
+  // token rows). A token row is vpr 16-byte pieces; each thread copies vpt pieces.
   // Rows past the chunk's end repeat the last valid row (finite; T' is zero in those columns).
   typedef __attribute__((ext_vector_type(4))) unsigned u4;
   const MT* gv_ = reinterpret_cast<const MT*>(p.v);
   const int vpr = V256 ? 16 : p.V * (int)sizeof(MT) / 16;  // a power of two
   const int vsh = V256 ? 4 : __builtin_ctz((unsigned)vpr);
   const int vpt = V256 ? 4 : CHUNK * vpr / PREP_THREADS;  // 1 .. 16
-  constexpr int VB = V256 ? 1 : 4;  // pieces per batch
+  // pieces per batch. With 256-byte rows a thread's 4 pieces load together when the task starts
+  // (ahead of the next task's prefetch) and are stored after phase 5, so that no store has to
+  // wait for a load issued just after another store; otherwise up to four batches of four, each
+  // loaded a phase before it is stored.
+  constexpr int VB = 4;
   u4 vbuf[VB];
   // (tid: the loop's opaque copy of threadIdx.x, so that no address is hoisted and kept live)
   auto v_load = [&](int tid, TaskPos tp, int task, int batch) {
@@ -397,7 +400,11 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   };
   int task = blockIdx.x;
   if (task >= ntask) return;
-  TaskPos pcur = task_pos(task);  // the current task's chunk position
+  // chunk positions of the current and the next task; the one after is read a task ahead. (A
+  // load issued right after the record stores would be counted behind them: reading the
+  // position one task ahead made the loop wait for every store of the task before.)
+  TaskPos pcur = task_pos(task);
+  TaskPos pnext = task_pos(task + (int)gridDim.x < ntask ? task + (int)gridDim.x : task);
   Raw raw;  // raw inputs of one task: filled one task ahead, consumed by phase 1
   load_raw(raw, pcur, task, -1);
   float kc[NG][4];  // phase 1 -> phase 2: this wave's column operand
@@ -639,13 +646,15 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   const int j = task / H;
   const int h = task - j * H;
   const int ntsk = task + (int)gridDim.x < ntask ? task + (int)gridDim.x : task;
-  const TaskPos pn = task_pos(ntsk);
+  const TaskPos pn = pnext;
+  const int nntsk = ntsk + (int)gridDim.x < ntask ? ntsk + (int)gridDim.x : ntsk;
+  pnext = task_pos(nntsk);
   MT* recM = reinterpret_cast<MT*>(p.rec + (j * H + h) * p.rec_bytes);
 
   // the next task's inputs load during phases 2-5 (phase 1's fp32 copies are dead by now)
   // (in three parts, so that the loads enter the memory pipeline in smaller bursts)
-  load_raw(raw, pn, ntsk, 0);
   v_load(tid, pcur, task, 0);
+  load_raw(raw, pn, ntsk, 0);
 
   // ---------------- phase 2: blocks (I, w), I >= w, of A and P. The column operand (token
   // block w, scaled per channel by D_{Iw}) is this wave's own kc; the row operands are read as
@@ -706,7 +715,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   }
 
   load_raw(raw, pn, ntsk, 1);
-  v_store(tid, reinterpret_cast<char*>(recM), 0);
+  if (!V256) v_store(tid, reinterpret_cast<char*>(recM), 0);
   if (vpt > VB) v_load(tid, pcur, task, 1);
 
   // ---------------- phase 3: T = (I + A)^{-1}
@@ -847,6 +856,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   }
 
   if (vpt > 3 * VB) v_store(tid, reinterpret_cast<char*>(recM), 3);
+  if (V256) v_store(tid, reinterpret_cast<char*>(recM), 0);
   lds_barrier();  // the next task reuses every LDS region
   task += gridDim.x;
   if (task >= ntask) break;
