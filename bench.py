@@ -566,33 +566,51 @@ def main():
         gen2.manual_seed(wl["seed"] + 11)
         d_o = torch.randn((T, H, V), generator=gen2, device=dev).to(torch.bfloat16)
         d_fin = torch.randn((1, H, K, V), generator=gen2, device=dev)
-        wsb = torch.empty(int(kda.lib().kda_chunk_bwd_workspace_size(1, T, H, K, V, 1)),
-                          dtype=torch.uint8, device=dev)
+        L = kda.lib()
 
-        def bwd_call():
-            return kda.chunk_bwd(*(inp[x] for x in names), d_o, init_state=inp["init_state"],
-                                 d_final_state=d_fin, workspace=wsb)
+        def time_bwd(wsbytes):
+            wsb = torch.empty(int(wsbytes), dtype=torch.uint8, device=dev)
 
-        bsteps = max(1, min(args.steps, 5))
-        for _ in range(max(1, min(args.warmup, 2))):
-            grads = bwd_call()
-        torch.cuda.synchronize()
-        eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        eb0.record()
-        for _ in range(bsteps):
-            grads = bwd_call()
-        eb1.record()
-        torch.cuda.synchronize()
-        bms = eb0.elapsed_time(eb1) / bsteps
+            def bwd_call():
+                return kda.chunk_bwd(*(inp[x] for x in names), d_o, init_state=inp["init_state"],
+                                     d_final_state=d_fin, workspace=wsb)
+
+            bsteps = max(1, min(args.steps, 5))
+            for _ in range(max(1, min(args.warmup, 2))):
+                grads = bwd_call()
+            torch.cuda.synchronize()
+            eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            eb0.record()
+            for _ in range(bsteps):
+                grads = bwd_call()
+            eb1.record()
+            torch.cuda.synchronize()
+            again = bwd_call()
+            same = all(torch.equal(x, y) for x, y in zip(grads, again))
+            return eb0.elapsed_time(eb1) / bsteps, bsteps, grads, same
+
+        # the default workspace (segments of about 4 GiB, a second pass over the records for
+        # the states at the segment boundaries), then one segment over every chunk
+        ws_def = int(L.kda_chunk_bwd_workspace_size(1, T, H, K, V, 1))
+        ws_one = int(L.kda_chunk_bwd_workspace_size_ex(1, T, H, K, V, 1, 0))
+        bms, bsteps, grads, same = time_bwd(ws_def)
+        finite = bool(all(torch.isfinite(g).all().item() for g in grads))
+        del grads
+        bms1, _, grads1, same1 = time_bwd(ws_one)
+        del grads1
         bfl = bwd_alg_flops(T, H, K, V)
         bwd = {"workload": "B=1 H=32 T=65536 K=V=128 bf16 inputs, fp32 gradients of q, k, v, "
                            "log alpha, beta and the initial state",
                "ms": bms, "calls": bsteps, "tokens_per_s": T / (bms * 1e-3),
                "alg_flops": bfl, "fp32_TFLOPs": bfl / (bms * 1e-3) / 1e12,
                "fp32_frac": bfl / (bms * 1e-3) / PEAK_FP32,
-               "workspace_GB": wsb.numel() / 1e9,
-               "finite": bool(all(torch.isfinite(g).all().item() for g in grads))}
-        del d_o, d_fin, wsb, grads
+               "workspace_GB": ws_def / 1e9,
+               "segments": "of about 4 GiB of per-chunk arrays (default workspace)",
+               "single_segment": {"ms": bms1, "workspace_GB": ws_one / 1e9,
+                                  "tokens_per_s": T / (bms1 * 1e-3)},
+               "bitwise_repeatable": bool(same and same1),
+               "finite": finite}
+        del d_o, d_fin
 
     # ---------------- parity spot check and CPU baseline (oracle on the same inputs)
     cpu = None

@@ -68,6 +68,8 @@ def _lib():
                                            ctypes.c_int, u32, i32, vp, vp, vp, sz, vp]
         lib.kda_chunk_bwd_workspace_size.restype = sz
         lib.kda_chunk_bwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
+        lib.kda_chunk_bwd_workspace_size_ex.restype = sz
+        lib.kda_chunk_bwd_workspace_size_ex.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int, i64]
         lib.kda_chunk_bwd.restype = ctypes.c_int
         lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                       ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -122,6 +124,16 @@ def _check(t, name, shape, dtype, device):
 def workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype) -> int:
     code = KDA_DTYPE_BF16 if dtype == torch.bfloat16 else KDA_DTYPE_F32
     return int(_lib().kda_chunk_fwd_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, code))
+
+
+def bwd_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype, segment_tokens=None) -> int:
+    """Workspace bytes of chunk_bwd: the default segments, or segments of ``segment_tokens``
+    tokens (0: one segment over every chunk)."""
+    code = KDA_DTYPE_BF16 if dtype == torch.bfloat16 else KDA_DTYPE_F32
+    if segment_tokens is None:
+        return int(_lib().kda_chunk_bwd_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, code))
+    return int(_lib().kda_chunk_bwd_workspace_size_ex(num_seqs, total_tokens, num_heads, dk, dv,
+                                                      code, int(segment_tokens)))
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, num_seqs=None,
@@ -249,13 +261,14 @@ def chunk_fwd_scan(q, k, v, log_alpha, beta, init_state=None, num_seqs=1, num_gr
 
 
 def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final_state=None,
-              cu_seqlens=None, num_seqs=None, workspace=None, grads=None):
+              cu_seqlens=None, num_seqs=None, workspace=None, grads=None, segment_tokens=None):
     """kda_chunk_bwd on torch tensors: the gradients of sum(d_o * o) + sum(d_final_state *
     final_state) for chunk_fwd on the same inputs (no input options). d_o [T, H, V] in the input
     dtype; d_final_state [N, H, K, V] fp32 or None (zero). Returns fp32 tensors
     (dq [T, H, K], dk [T, H, K], dv [T, H, V], dlog_alpha [T, H, K], dbeta [T, H],
     dinit_state [N, H, K, V]). ``grads`` may pass those six tensors to be written in place
-    (e.g. under graph capture)."""
+    (e.g. under graph capture). Without ``workspace``, one of the default size is allocated, or,
+    with ``segment_tokens``, one sized for segments of that many tokens (0: one segment)."""
     device = q.device
     T, H, K = q.shape
     V = v.shape[-1]
@@ -287,7 +300,8 @@ def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final_state=None
                              ("dlog_alpha", dg, (T, H, K)), ("dbeta", db, (T, H)),
                              ("dinit_state", dinit, (N, H, K, V))):
             _check(t, name, shp, torch.float32, device)
-    need = int(_lib().kda_chunk_bwd_workspace_size(N, T, H, K, V, code))
+    need = int(_lib().kda_chunk_bwd_workspace_size(N, T, H, K, V, code) if segment_tokens is None
+               else _lib().kda_chunk_bwd_workspace_size_ex(N, T, H, K, V, code, int(segment_tokens)))
     if need == 0:
         raise KdaError(2 if K not in (32, 64, 128) or V not in (32, 64, 128) else 1,
                        "kda_chunk_bwd_workspace_size")

@@ -183,12 +183,24 @@ static kda_status check_bwd_shape(int32_t num_seqs, int64_t total_tokens, int32_
   return KDA_SUCCESS;
 }
 
+extern "C" size_t kda_chunk_bwd_workspace_size_ex(int32_t num_seqs, int64_t total_tokens,
+                                                  int32_t num_heads, int32_t dk, int32_t dv,
+                                                  kda_dtype dtype, int64_t segment_tokens) {
+  if (check_bwd_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype) != KDA_SUCCESS) return 0;
+  kda::BwdPlan p;
+  const int64_t seg = segment_tokens <= 0 ? 0 : (segment_tokens + kda::CHUNK - 1) / kda::CHUNK;
+  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, seg, &p)) return 0;
+  return p.total_bytes;
+}
+
 extern "C" size_t kda_chunk_bwd_workspace_size(int32_t num_seqs, int64_t total_tokens,
                                                int32_t num_heads, int32_t dk, int32_t dv,
                                                kda_dtype dtype) {
   if (check_bwd_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype) != KDA_SUCCESS) return 0;
   kda::BwdPlan p;
-  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, &p)) return 0;
+  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv,
+                          kda::default_bwd_segment(num_heads, dk, dv), &p))
+    return 0;
   return p.total_bytes;
 }
 
@@ -233,9 +245,11 @@ extern "C" kda_status kda_chunk_bwd(const void* q, const void* k, const void* v,
       if (out_p[o2] && out_n[o2] && overlap(out_p[o], out_n[o], out_p[o2], out_n[o2]))
         return KDA_ERROR_INVALID_VALUE;
   }
+  // the longest segments the caller's workspace holds (one segment when it holds them all)
   kda::BwdPlan p;
-  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, &p)) return KDA_ERROR_INVALID_VALUE;
-  if (workspace_bytes < p.total_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, 0, &p)) return KDA_ERROR_INVALID_VALUE;
+  if (!kda::fit_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, workspace_bytes, &p))
+    return KDA_ERROR_WORKSPACE_TOO_SMALL;
   kda::BwdArgs a;
   a.q = q;
   a.k = k;

@@ -59,7 +59,9 @@ struct GScr {
   static constexpr int oDKt = oDW + BC * K;    // Delta X^T              [64][K]
   static constexpr int oTDW = oDKt + BC * K;   // T^T dW                 [64][K]
   static constexpr int oDG = oTDW + BC * K;    // rowsum(S * X)          [K]
-  static constexpr int floats = (oDG + K + 63) / 64 * 64;
+  static constexpr int KP = K > 64 ? K / 64 : 1;  // key-channel parts of the gradient kernel
+  static constexpr int oDB = oDG + K;          // dbeta per part          [KP][64]
+  static constexpr int floats = (oDB + KP * BC + 63) / 64 * 64;
 };
 
 }  // namespace
@@ -113,7 +115,8 @@ template <int K, int V, typename MT>
 __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
     const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ v,
     const MT* __restrict__ g, const MT* __restrict__ beta, int H,
-    const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ rec) {
+    const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, int cb,
+    float* __restrict__ rec) {
   using R = BRec<K, V>;
   // The key channels are taken in parts of KC and the value columns in parts of VC (at most
   // 64 each): the sums over channels in A and P add up across the parts, and every other
@@ -127,10 +130,10 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
   __shared__ __align__(16) float sA[BC * 68];  // A (strict lower), then T = (I + A)^{-1}
   __shared__ float sBeta[BC];
   float* sT = sA;
-  const int c = blockIdx.x, h = blockIdx.y;
+  const int lc = blockIdx.x, c = cb + lc, h = blockIdx.y;  // chunk of the segment, of the call
   if (c >= *ntot) return;
   const ChunkRow ch = chunks[c];
-  float* rc = rec + ((size_t)c * H + h) * R::floats;
+  float* rc = rec + ((size_t)lc * H + h) * R::floats;
   if (threadIdx.x < BC)
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
   // A_ij = beta_i sum_c k_ic k_jc e^{b_ic - b_jc} (j < i) and P_ij = sum_c q_ic k_jc e^{..} (j <= i).
@@ -259,10 +262,15 @@ constexpr int NTR = 512;  // threads of a chain workgroup: 8 waves
 // Delta. NTR threads: waves 0-3 form the four 16-row tiles of Delta, wave w the 16-row tiles
 // w, w + 8, .. of S', with matrix-core steps over LDS operands; two register sets hold the
 // records of the next two chunks.
-template <int K, int V>
+// The chunks [cb, ce) of one segment (records, S_c and Delta indexed from cb). A sequence that
+// began before the segment starts from ck_in (its state at chunk cb, [H][K][V]); one that goes
+// on past it leaves its state at chunk ce in ck_out (when given). STORE = false runs the chain
+// for that state alone.
+template <int K, int V, bool STORE>
 __global__ __launch_bounds__(NTR) void bwd_fstate_kernel(
     const float* __restrict__ rec, const float* __restrict__ init, const int32_t* __restrict__ seq_first,
-    int N, int H, int chains8, float* __restrict__ ckS, float* __restrict__ Dl) {
+    int N, int H, int chains8, int cb, int ce, const float* __restrict__ ck_in,
+    float* __restrict__ ck_out, float* __restrict__ ckS, float* __restrict__ Dl) {
   using R = BRec<K, V>;
   // LDS row strides: a block read as the A operand along its rows (lane m takes row m, the
   // four lane groups consecutive columns) is padded by 4 floats, one read along its columns
@@ -280,17 +288,18 @@ __global__ __launch_bounds__(NTR) void bwd_fstate_kernel(
   if (nh >= N * H) return;
   const int n = nh / H, h = nh % H, c0 = 16 * s;
   const int tid = threadIdx.x, w = tid >> 6, lm = tid & 15, lg = (tid >> 4) & 3;
-  for (int e = tid; e < K * 16; e += NTR)
-    sS[e] = init ? init[((size_t)nh * K + e / 16) * V + c0 + e % 16] : 0.f;
-  const int first = seq_first[n], last = seq_first[n + 1];
-  if (first == last) return;
+  const int sfirst = seq_first[n], slast = seq_first[n + 1];
+  const int first = max(sfirst, cb), last = min(slast, ce);  // the sequence's chunks here
+  if (first >= last) return;
+  const float* src = sfirst < cb ? ck_in + (size_t)h * K * V : (init ? init + (size_t)nh * K * V : nullptr);
+  for (int e = tid; e < K * 16; e += NTR) sS[e] = src ? src[(e / 16) * V + c0 + e % 16] : 0.f;
   struct Regs {
     f32x4 w[PB], k[PB];
     float u[4], g;
   };
   Regs ra, rb;
   auto fetch = [&](Regs& x, int c) {
-    const float* rc = rec + ((size_t)c * H + h) * R::floats;
+    const float* rc = rec + ((size_t)(c - cb) * H + h) * R::floats;
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
       x.w[u] = reinterpret_cast<const f32x4*>(rc + R::oW)[tid + NTR * u];
@@ -313,8 +322,9 @@ __global__ __launch_bounds__(NTR) void bwd_fstate_kernel(
     f32x4 d = {x.u[0], x.u[1], x.u[2], x.u[3]};
     fetch(x, min(c + 2, last - 1));
     lds_barrier();
-    for (int e = tid; e < K * 16; e += NTR)
-      ckS[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sS[e];
+    if constexpr (STORE)
+      for (int e = tid; e < K * 16; e += NTR)
+        ckS[(((size_t)(c - cb) * H + h) * K + e / 16) * V + c0 + e % 16] = sS[e];
     // Delta rows 16 w .. (waves 0-3): U - W S (two chains of dependent steps)
     if (w < 4) {
       f32x4 d1 = {0.f, 0.f, 0.f, 0.f};
@@ -328,7 +338,7 @@ __global__ __launch_bounds__(NTR) void bwd_fstate_kernel(
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * w + 4 * lg + r;
         sD[row * 16 + lm] = d[r];
-        Dl[(((size_t)c * H + h) * BC + row) * V + c0 + lm] = d[r];
+        if constexpr (STORE) Dl[(((size_t)(c - cb) * H + h) * BC + row) * V + c0 + lm] = d[r];
       }
     }
     lds_barrier();
@@ -368,6 +378,10 @@ __global__ __launch_bounds__(NTR) void bwd_fstate_kernel(
     if (c + 1 >= last) break;
     step(rb, c + 1);
   }
+  if (ck_out != nullptr && slast > ce) {
+    lds_barrier();
+    for (int e = tid; e < K * 16; e += NTR) ck_out[((size_t)h * K + e / 16) * V + c0 + e % 16] = sS[e];
+  }
 }
 
 // Backwards in time: X_c (the gradient at the chunk's end), dDelta = P^T dO + Kt X per chunk,
@@ -375,11 +389,16 @@ __global__ __launch_bounds__(NTR) void bwd_fstate_kernel(
 // NTR threads: waves 0-3 form the four 16-row tiles of dDelta, and wave w the 16-row tiles
 // w, w + 8, .. of X_prev. Two register sets hold the records of the next two chunks, so each
 // chunk's loads have two chunks of compute to arrive in.
+// The chunks [cb, ce) of one segment, as in the forward chain: a sequence that goes on past
+// the segment starts from x_in (its X at chunk ce - 1, [H][K][V]), and one that began before it
+// leaves its X at chunk cb - 1 in x_out instead of writing the initial state's gradient.
+// Empty sequences (initial state = final state) are handled by the segment at chunk 0.
 template <int K, int V, typename MT>
 __global__ __launch_bounds__(NTR) void bwd_rstate_kernel(
     const float* __restrict__ rec, const MT* __restrict__ dO, const float* __restrict__ dfin,
     const int32_t* __restrict__ cu, int64_t T, const int32_t* __restrict__ seq_first, int N, int H,
-    int chains8, float* __restrict__ ckX, float* __restrict__ dDl, float* __restrict__ dinit) {
+    int chains8, int cb, int ce, const float* __restrict__ x_in, float* __restrict__ x_out,
+    float* __restrict__ ckX, float* __restrict__ dDl, float* __restrict__ dinit) {
   using R = BRec<K, V>;
   // LDS row strides as in the forward chain: Kt is read along its rows (+4), P, Qe and W
   // along their columns (+16)
@@ -402,9 +421,12 @@ __global__ __launch_bounds__(NTR) void bwd_rstate_kernel(
   if (nh >= N * H) return;
   const int n = nh / H, h = nh % H, c0 = 16 * s;
   const int tid = threadIdx.x, w = tid >> 6, lm = tid & 15, lg = (tid >> 4) & 3;
-  for (int e = tid; e < K * 16; e += NTR)
-    sX[e] = dfin ? dfin[((size_t)nh * K + e / 16) * V + c0 + e % 16] : 0.f;
-  const int first = seq_first[n], last = seq_first[n + 1];
+  const int sfirst = seq_first[n], slast = seq_first[n + 1];
+  const int first = max(sfirst, cb), last = min(slast, ce);  // the sequence's chunks here
+  if (sfirst < slast ? first >= last : cb != 0) return;
+  const bool carried = sfirst < slast && slast > ce;  // X comes from the next segment
+  const float* src = carried ? x_in + (size_t)h * K * V : (dfin ? dfin + (size_t)nh * K * V : nullptr);
+  for (int e = tid; e < K * 16; e += NTR) sX[e] = src ? src[(e / 16) * V + c0 + e % 16] : 0.f;
   int64_t s0, s1;
   seq_range(cu, N, T, n, &s0, &s1);
   struct Regs {
@@ -416,7 +438,7 @@ __global__ __launch_bounds__(NTR) void bwd_rstate_kernel(
   // chunk c's rows are tokens s0 + 64 (c - first) + r; rows past the sequence read its last
   // token (in bounds) and are zeroed when stored
   auto fetch = [&](Regs& x, int c) {
-    const float* rc = rec + ((size_t)c * H + h) * R::floats;
+    const float* rc = rec + ((size_t)(c - cb) * H + h) * R::floats;
 #pragma unroll
     for (int u = 0; u < PP; ++u) x.p[u] = reinterpret_cast<const f32x4*>(rc + R::oP)[tid + NTR * u];
 #pragma unroll
@@ -426,7 +448,7 @@ __global__ __launch_bounds__(NTR) void bwd_rstate_kernel(
       x.w[u] = reinterpret_cast<const f32x4*>(rc + R::oW)[tid + NTR * u];
     }
     x.g = rc[R::oGam + tid % K];
-    const int64_t tok = s0 + (int64_t)(c - first) * BC;
+    const int64_t tok = s0 + (int64_t)(c - sfirst) * BC;
 #pragma unroll
     for (int u = 0; u < PO; ++u) {
       const int e = tid + NTR * u;
@@ -436,7 +458,7 @@ __global__ __launch_bounds__(NTR) void bwd_rstate_kernel(
   };
   // one chunk: stage its registers, start loading chunk c - 2 into them, then its products
   auto step = [&](Regs& x, int c) {
-    const int len = (int)min((int64_t)BC, s1 - (s0 + (int64_t)(c - first) * BC));
+    const int len = (int)min((int64_t)BC, s1 - (s0 + (int64_t)(c - sfirst) * BC));
     lds_barrier();  // the previous chunk's reads of LDS are done
 #pragma unroll
     for (int u = 0; u < PP; ++u) {
@@ -459,7 +481,7 @@ __global__ __launch_bounds__(NTR) void bwd_rstate_kernel(
     fetch(x, max(c - 2, first));
     lds_barrier();
     for (int e = tid; e < K * 16; e += NTR)
-      ckX[(((size_t)c * H + h) * K + e / 16) * V + c0 + e % 16] = sX[e];
+      ckX[(((size_t)(c - cb) * H + h) * K + e / 16) * V + c0 + e % 16] = sX[e];
     // dDelta rows 16 w .. (waves 0-3): P^T dO (P_ri = 0 for r < i, so the steps start at
     // r = 16 w) + Kt X
     if (w < 4) {
@@ -473,7 +495,7 @@ __global__ __launch_bounds__(NTR) void bwd_rstate_kernel(
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * w + 4 * lg + r;
         sDD[row * 16 + lm] = d[r];
-        dDl[(((size_t)c * H + h) * BC + row) * V + c0 + lm] = d[r];
+        dDl[(((size_t)(c - cb) * H + h) * BC + row) * V + c0 + lm] = d[r];
       }
     }
     lds_barrier();
@@ -513,7 +535,10 @@ __global__ __launch_bounds__(NTR) void bwd_rstate_kernel(
     if (c - 1 < first) break;
     step(rb, c - 1);
   }
-  if (dinit) {
+  if (sfirst < cb) {
+    __syncthreads();
+    for (int e = tid; e < K * 16; e += NTR) x_out[((size_t)h * K + e / 16) * V + c0 + e % 16] = sX[e];
+  } else if (dinit) {
     __syncthreads();
     for (int e = tid; e < K * 16; e += NTR)
       dinit[((size_t)nh * K + e / 16) * V + c0 + e % 16] = sX[e];
@@ -529,7 +554,8 @@ template <int K, int V, typename MT>
 __global__ __launch_bounds__(NTGA, 8) void bwd_ga_kernel(
     const MT* __restrict__ dO, const float* __restrict__ ckS, const float* __restrict__ ckX,
     const float* __restrict__ Dl, const float* __restrict__ dDl, int H,
-    const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr) {
+    const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, int cb,
+    float* __restrict__ scr) {
   using G = GScr<K>;
   // Every product here sums over the value columns; they run over parts of VC columns with
   // the partial tiles kept in registers, so LDS holds 64 x VC and K x VC blocks (70 KB at
@@ -540,10 +566,10 @@ __global__ __launch_bounds__(NTGA, 8) void bwd_ga_kernel(
   __shared__ __align__(16) float sO[BC * L];
   __shared__ __align__(16) float sD[BC * L];  // dDelta, then Delta
   __shared__ __align__(16) float sS[K * L];   // S, then X
-  const int c = blockIdx.x, h = blockIdx.y;
+  const int lc = blockIdx.x, c = cb + lc, h = blockIdx.y;  // chunk of the segment, of the call
   if (c >= *ntot) return;
   const ChunkRow ch = chunks[c];
-  const size_t ch_h = (size_t)c * H + h;
+  const size_t ch_h = (size_t)lc * H + h;
   float* sc = scr + ch_h * G::floats;
   const float* S = ckS + ch_h * K * V;
   const float* X = ckX + ch_h * K * V;
@@ -611,8 +637,8 @@ template <int K, int V, typename MT>
 __global__ __launch_bounds__(NTG, 8) void bwd_gb_kernel(
     const MT* __restrict__ k, const MT* __restrict__ v, const MT* __restrict__ g,
     const MT* __restrict__ beta, const float* __restrict__ rec, const float* __restrict__ dDl, int H,
-    const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ scr,
-    float* __restrict__ grad_v, float* __restrict__ grad_beta) {
+    const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, int cb,
+    float* __restrict__ scr, float* __restrict__ grad_v, float* __restrict__ grad_beta) {
   using R = BRec<K, V>;
   using G = GScr<K>;
   // The value columns and the key channels run in parts of at most 64; dT's partial tiles stay
@@ -629,10 +655,13 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gb_kernel(
   __shared__ __align__(16) float bufA[BC * LA];  // dDelta (part), dW (part), then M1 = T^T dT
   __shared__ __align__(16) float bufB[BC * LB];  // v (part), Ke (part), then dT
   __shared__ float sBeta[BC], sDb[BC];
-  const int c = blockIdx.x, h = blockIdx.y;
+  // dbeta's row sums per 16-column tile of a part, added to sDb in tile order (no atomics: the
+  // gradients are the same bit for bit on every run)
+  __shared__ float sDbp[BC][4];
+  const int lc = blockIdx.x, c = cb + lc, h = blockIdx.y;  // chunk of the segment, of the call
   if (c >= *ntot) return;
   const ChunkRow ch = chunks[c];
-  const size_t ch_h = (size_t)c * H + h;
+  const size_t ch_h = (size_t)lc * H + h;
   const float* rc = rec + ch_h * R::floats;
   float* sc = scr + ch_h * G::floats;
   load_block<BC, LT, NTG>(sT, rc + R::oT);
@@ -653,9 +682,15 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gb_kernel(
     mmf<VC, BC, true, false, LT, LDD, NTG>(sT, bufA, [&](int r, int cc, float x) {
       if (r < ch.len) grad_v[((ch.tok + r) * (int64_t)H + h) * V + c0 + cc] = sBeta[r] * x;
       const float y = row16_sum(bufB[r * LVV + cc] * x);  // the 16 lanes of a row hold one r
-      if ((threadIdx.x & 15) == 0) atomicAdd(&sDb[r], y);
+      if ((threadIdx.x & 15) == 0) sDbp[r][cc >> 4] = y;
     });
     lds_barrier();
+    if (threadIdx.x < BC) {
+      float y = sDb[threadIdx.x];
+#pragma unroll
+      for (int t = 0; t < VC / 16; ++t) y += sDbp[threadIdx.x][t];
+      sDb[threadIdx.x] = y;
+    }
     for (int e = threadIdx.x; e < BC * VC; e += NTG) bufB[(e / VC) * LVV + e % VC] *= sBeta[e / VC];
     lds_barrier();
     // dT += dDelta (beta V)^T over the part's columns
@@ -676,9 +711,15 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gb_kernel(
     mmf<KC, BC, true, false, LT, LDW, NTG>(sT, bufA, [&](int r, int cc, float x) {
       sc[G::oTDW + r * K + c0 + cc] = x;
       const float y = row16_sum(bufB[r * LKE + cc] * x);
-      if ((threadIdx.x & 15) == 0) atomicAdd(&sDb[r], y);
+      if ((threadIdx.x & 15) == 0) sDbp[r][cc >> 4] = y;
     });
     lds_barrier();
+    if (threadIdx.x < BC) {
+      float y = sDb[threadIdx.x];
+#pragma unroll
+      for (int t = 0; t < KC / 16; ++t) y += sDbp[threadIdx.x][t];
+      sDb[threadIdx.x] = y;
+    }
     for (int e = threadIdx.x; e < BC * KC; e += NTG) bufB[(e / KC) * LKE + e % KC] *= sBeta[e / KC];
     lds_barrier();
     // dT += dW (beta Ke)^T over the part's channels
@@ -693,8 +734,7 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gb_kernel(
   mmf<BC, BC, false, true, LT, LT, NTG>(bufA, sT, [&](int i, int j, float x) {
     if (j < i) sc[G::oDPA + j * BC + i] = -x;  // dA_ij, transposed above dP
   });
-  // dbeta's T-side terms; the gradient kernel adds the rest (one part of the key channels
-  // per workgroup) with atomics
+  // dbeta's T-side terms; the per-part sums of the gradient kernel are added after it
   if (threadIdx.x < ch.len) grad_beta[(ch.tok + threadIdx.x) * (int64_t)H + h] = sDb[threadIdx.x];
 }
 
@@ -703,12 +743,12 @@ template <int K, int V, typename MT>
 __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
     const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ g,
     const MT* __restrict__ beta, int H, const ChunkRow* __restrict__ chunks,
-    const int32_t* __restrict__ ntot, const float* __restrict__ scr, float* __restrict__ grad_q,
-    float* __restrict__ grad_k, float* __restrict__ grad_g, float* __restrict__ grad_beta) {
+    const int32_t* __restrict__ ntot, int cb, float* __restrict__ scr, float* __restrict__ grad_q,
+    float* __restrict__ grad_k, float* __restrict__ grad_g) {
   using G = GScr<K>;
   // Everything here is per key channel except dbeta's sum over the channels, so each
-  // workgroup takes one part of KC channels (blockIdx.z) and adds its share of dbeta to
-  // grad_beta atomically. dP and dA share one 64 x 64 block (dP on and below the diagonal,
+  // workgroup takes one part of KC channels (blockIdx.z) and leaves its share of dbeta in the
+  // scratch (bwd_beta_kernel adds the parts in order). dP and dA share one 64 x 64 block (dP on and below the diagonal,
   // dA transposed above it): 70 KB of LDS, and at 64 VGPRs two workgroups share a CU.
   constexpr int KC = K > 64 ? 64 : K;
   constexpr int LK = KC + 4;
@@ -716,12 +756,12 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
   __shared__ __align__(16) float sK[BC * LK];
   __shared__ __align__(16) float sB[BC * LK];
   __shared__ __align__(16) float sM[BC * 68];  // [i][j] = dP_ij (j <= i), [j][i] = dA_ij (j < i)
-  __shared__ float sBeta[BC], sDb[BC], sRed[KC];
-  const int c = blockIdx.x, h = blockIdx.y;
+  __shared__ float sBeta[BC], sDb[BC];
+  const int lc = blockIdx.x, c = cb + lc, h = blockIdx.y;  // chunk of the segment, of the call
   if (c >= *ntot) return;
   const ChunkRow ch = chunks[c];
-  const size_t ch_h = (size_t)c * H + h;
-  const float* sc = scr + ch_h * G::floats;
+  const size_t ch_h = (size_t)lc * H + h;
+  float* sc = scr + ch_h * G::floats;
   load_block<BC, 68, NTG>(sM, sc + G::oDPA);
   if (threadIdx.x < BC) {
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
@@ -736,7 +776,6 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
     load_rows<KC, LK, NTG, MT, K>(sQ, q, ch.tok, ch.len, H, h, c0);
     load_rows<KC, LK, NTG, MT, K>(sK, k, ch.tok, ch.len, H, h, c0);
     load_rows<KC, LK, NTG, MT, K>(sB, g, ch.tok, ch.len, H, h, c0);
-    if (threadIdx.x < KC) sRed[threadIdx.x] = 0.f;
     // this thread's rows of dO S^T, T^T dW and Delta X^T, in flight through the scan
     float r1v[RB], tdw[RB], dkv[RB];
 #pragma unroll
@@ -776,11 +815,11 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
       const float dk = dke + s3 + dkt;
       {
         // dbeta's sum over the part's key channels of row i: the lanes sharing i (a whole
-        // wave, or 32 lanes at K = 32) reduce first, then one LDS atomic
+        // wave, or 32 lanes at K = 32) are the only ones holding row i
         float y = row16_sum(ki * s2);
         y += __shfl_xor(y, 16);
         if constexpr (KC >= 64) y += __shfl_xor(y, 32);
-        if (threadIdx.x % (KC >= 64 ? 64 : KC) == 0) atomicAdd(&sDb[i], y);
+        if (threadIdx.x % (KC >= 64 ? 64 : KC) == 0) sDb[i] = y;
       }
       red += ki * dkt;
       db[u] = qi * dq + ki * (dke - s3 - dkt);
@@ -790,10 +829,10 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
         grad_k[o] = dk;
       }
     }
-    atomicAdd(&sRed[m], red);
-    lds_barrier();  // every read of sQ done
+    lds_barrier();  // every read of sQ and sK done
 #pragma unroll
     for (int u = 0; u < RB; ++u) sQ[(i0 + NG * u) * LK + m] = db[u];
+    sK[i0 * LK + m] = red;  // this thread's rows' share of sum_i k_i dKt_i, summed below in order
     lds_barrier();
     // log alpha: reverse cumulative sum of db over the chunk, the last token also carrying
     // sum_i k_i * dKt_i and gamma * rowsum(S * X); NTG / KC neighbouring threads per channel,
@@ -815,7 +854,10 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
         if (part + o < P) post += y;
       }
       post -= run;  // the rows after this thread's
-      post += sRed[cm] + sc[G::oDG + c0 + cm] * exp2_f(sB[(BC - 1) * LK + cm]);
+      float red = 0.f;
+#pragma unroll
+      for (int u = 0; u < NG; ++u) red += sK[u * LK + cm];
+      post += red + sc[G::oDG + c0 + cm] * exp2_f(sB[(BC - 1) * LK + cm]);
 #pragma unroll
       for (int r = 0; r < RP; ++r) {
         const int row = part * RP + r;
@@ -823,7 +865,27 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
       }
     }
   }
-  if (threadIdx.x < ch.len) atomicAdd(&grad_beta[(ch.tok + threadIdx.x) * (int64_t)H + h], sDb[threadIdx.x]);
+  if (threadIdx.x < BC) sc[G::oDB + blockIdx.z * BC + threadIdx.x] = sDb[threadIdx.x];
+}
+
+// dbeta = the T-side terms (already in grad_beta) + the gradient kernel's parts, in part order
+template <int K>
+__global__ __launch_bounds__(BC) void bwd_beta_kernel(int H, const ChunkRow* __restrict__ chunks,
+                                                      const int32_t* __restrict__ ntot, int cb,
+                                                      const float* __restrict__ scr,
+                                                      float* __restrict__ grad_beta) {
+  using G = GScr<K>;
+  const int lc = blockIdx.x, c = cb + lc, h = blockIdx.y;
+  if (c >= *ntot) return;
+  const ChunkRow ch = chunks[c];
+  const int i = threadIdx.x;
+  if (i >= ch.len) return;
+  const float* sc = scr + ((size_t)lc * H + h) * G::floats + G::oDB;
+  float* gb = grad_beta + (ch.tok + i) * (int64_t)H + h;
+  float y = *gb;
+#pragma unroll
+  for (int p = 0; p < G::KP; ++p) y += sc[p * BC + i];
+  *gb = y;
 }
 
 // ---------------------------------------------------------------- host
@@ -838,33 +900,48 @@ hipError_t launch_chunk_rows(const int32_t* cu, int N, int64_t T, int64_t ub, in
 
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
-template <int K, int V>
-static void bwd_sizes(int64_t ub, int H, size_t* rec_f, size_t* scr_f) {
-  *rec_f = (size_t)ub * H * BRec<K, V>::floats;
-  *scr_f = (size_t)ub * H * GScr<K>::floats;
+// fp32 values the backward keeps per (chunk, head) of a segment: the record, the gradient
+// kernels' scratch, and (see make_bwd_plan) the chunk-start state S, the chunk-end gradient X,
+// Delta and dDelta. Zero sizes for unsupported head dims.
+struct BwdFloats {
+  size_t rec, scr, all;
+};
+static BwdFloats bwd_floats(int K, int V) {
+#define KDA_BWD_FLOATS(KK, VV)                                                           \
+  if (K == KK && V == VV)                                                                \
+    return BwdFloats{(size_t)BRec<KK, VV>::floats, (size_t)GScr<KK>::floats,             \
+                     (size_t)BRec<KK, VV>::floats + GScr<KK>::floats + 2 * (size_t)KK * VV + \
+                         2 * (size_t)BC * VV};
+  KDA_BWD_FLOATS(32, 32) KDA_BWD_FLOATS(32, 64) KDA_BWD_FLOATS(32, 128)
+  KDA_BWD_FLOATS(64, 32) KDA_BWD_FLOATS(64, 64) KDA_BWD_FLOATS(64, 128)
+  KDA_BWD_FLOATS(128, 32) KDA_BWD_FLOATS(128, 64) KDA_BWD_FLOATS(128, 128)
+#undef KDA_BWD_FLOATS
+  return BwdFloats{0, 0, 0};
 }
 
-bool make_bwd_plan(int N, int64_t T, int H, int K, int V, BwdPlan* p) {
+bool make_bwd_plan(int N, int64_t T, int H, int K, int V, int64_t seg_chunks, BwdPlan* p) {
   if (N <= 0 || H <= 0 || T < 0) return false;
+  const BwdFloats fl = bwd_floats(K, V);
+  if (fl.all == 0) return false;
   int64_t ub = (T + (int64_t)N * (BC - 1)) / BC;
   if (ub > T) ub = T;
   p->ub = ub;
-  size_t rec_f = 0, scr_f = 0;
-#define KDA_BWD_SIZES(KK, VV) \
-  if (K == KK && V == VV) bwd_sizes<KK, VV>(ub, H, &rec_f, &scr_f);
-  KDA_BWD_SIZES(32, 32) KDA_BWD_SIZES(32, 64) KDA_BWD_SIZES(32, 128)
-  KDA_BWD_SIZES(64, 32) KDA_BWD_SIZES(64, 64) KDA_BWD_SIZES(64, 128)
-  KDA_BWD_SIZES(128, 32) KDA_BWD_SIZES(128, 64) KDA_BWD_SIZES(128, 128)
-#undef KDA_BWD_SIZES
-  if (rec_f == 0 && ub > 0) return false;
-  const size_t chv = (size_t)ub * H;
+  p->seg = (seg_chunks <= 0 || seg_chunks >= ub) ? (ub > 0 ? ub : 1) : seg_chunks;
+  p->nseg = ub > 0 ? (ub + p->seg - 1) / p->seg : 1;
+  // the per-chunk arrays are indexed with 32-bit chunk numbers
+  if (ub >= (1LL << 31)) return false;
+  const size_t chv = (size_t)p->seg * H;
   size_t off = 0;
   p->off_seq = off;
   off += al256((size_t)(N + 1) * 4);
   p->off_chunks = off;
   off += al256((size_t)ub * sizeof(ChunkRow));
+  // one [H][K][V] state per segment boundary: S of the sequence that spans it (forward pass),
+  // then its X (reverse pass); none with a single segment
+  p->off_ck = off;
+  if (p->nseg > 1) off += al256((size_t)p->nseg * H * K * V * 4);
   p->off_rec = off;
-  off += al256(rec_f * 4);
+  off += al256(chv * fl.rec * 4);
   p->off_ckS = off;
   off += al256(chv * K * V * 4);
   p->off_ckX = off;
@@ -874,9 +951,30 @@ bool make_bwd_plan(int N, int64_t T, int H, int K, int V, BwdPlan* p) {
   p->off_dD = off;
   off += al256(chv * BC * V * 4);
   p->off_scr = off;
-  off += al256(scr_f * 4);
+  off += al256(chv * fl.scr * 4);
   p->total_bytes = off;
   return true;
+}
+
+bool fit_bwd_plan(int N, int64_t T, int H, int K, int V, size_t bytes, BwdPlan* p) {
+  if (!make_bwd_plan(N, T, H, K, V, 0, p)) return false;
+  if (p->total_bytes <= bytes) return true;
+  // the longest segments that fit: from the per-chunk bytes down, shorter until it fits
+  const size_t per_chunk = (size_t)H * bwd_floats(K, V).all * 4;
+  int64_t e = (int64_t)min(bytes / per_chunk, (size_t)p->ub - 1);
+  while (e >= 1) {
+    if (!make_bwd_plan(N, T, H, K, V, e, p)) return false;
+    if (p->total_bytes <= bytes) return true;
+    e = e > 64 ? e - e / 32 : e - 1;
+  }
+  return false;
+}
+
+int64_t default_bwd_segment(int H, int K, int V) {
+  const size_t per_chunk = (size_t)H * bwd_floats(K, V).all * 4;
+  if (per_chunk == 0) return 1;
+  const int64_t e = (int64_t)(BWD_SEGMENT_BYTES / per_chunk);
+  return e > 1 ? e : 1;
 }
 
 template <int K, int V, typename MT>
@@ -885,6 +983,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
   char* ws = reinterpret_cast<char*>(a.workspace);
   int32_t* seq_first = reinterpret_cast<int32_t*>(ws + p.off_seq);
   ChunkRow* chunks = reinterpret_cast<ChunkRow*>(ws + p.off_chunks);
+  float* ck = reinterpret_cast<float*>(ws + p.off_ck);
   float* rec = reinterpret_cast<float*>(ws + p.off_rec);
   float* ckS = reinterpret_cast<float*>(ws + p.off_ckS);
   float* ckX = reinterpret_cast<float*>(ws + p.off_ckX);
@@ -896,28 +995,61 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
   const MT *q = (const MT*)a.q, *k = (const MT*)a.k, *v = (const MT*)a.v, *g = (const MT*)a.g,
            *beta = (const MT*)a.beta, *dO = (const MT*)a.dO;
   launch_chunk_rows(a.cu_seqlens, N, a.total_tokens, p.ub, seq_first, chunks, st);
-  const dim3 cgrid((unsigned)(p.ub > 0 ? p.ub : 1), (unsigned)H);
-  if (p.ub > 0)
-    hipLaunchKernelGGL((bwd_prep_kernel<K, V, MT>), cgrid, dim3(NTP), 0, st, q, k, v, g, beta, H,
-                       (const ChunkRow*)chunks, ntot, rec);
   const int chains8 = (N * H + 7) / 8 * 8;
   const dim3 sgrid((unsigned)(chains8 * (V / 16)));
-  hipLaunchKernelGGL((bwd_fstate_kernel<K, V>), sgrid, dim3(NTR), 0, st, (const float*)rec,
-                     a.init_state, (const int32_t*)seq_first, N, H, chains8, ckS, Dl);
-  hipLaunchKernelGGL((bwd_rstate_kernel<K, V, MT>), sgrid, dim3(NTR), 0, st, (const float*)rec, dO,
-                     a.dfinal, a.cu_seqlens, a.total_tokens, (const int32_t*)seq_first, N, H,
-                     chains8, ckX, dDl, a.grad_init);
-  if (p.ub > 0) {
-    hipLaunchKernelGGL((bwd_ga_kernel<K, V, MT>), cgrid, dim3(NTGA), 0, st, dO, (const float*)ckS,
-                       (const float*)ckX, (const float*)Dl, (const float*)dDl, H,
-                       (const ChunkRow*)chunks, ntot, scr);
-    hipLaunchKernelGGL((bwd_gb_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, k, v, g, beta,
-                       (const float*)rec, (const float*)dDl, H, (const ChunkRow*)chunks, ntot, scr,
-                       a.grad_v, a.grad_beta);
-    const dim3 pgrid(cgrid.x, cgrid.y, (unsigned)(K > 64 ? K / 64 : 1));  // key-channel parts
-    hipLaunchKernelGGL((bwd_gc_kernel<K, V, MT>), pgrid, dim3(NTG), 0, st, q, k, g, beta, H,
-                       (const ChunkRow*)chunks, ntot, (const float*)scr, a.grad_q, a.grad_k,
-                       a.grad_g, a.grad_beta);
+  const size_t ckb = (size_t)H * K * V;  // one boundary's state
+  auto bound = [&](int64_t s) { return ck + (size_t)s * ckb; };
+  // segment s: chunks [cb, ce) of the call
+  auto range = [&](int64_t s, int* cb, int* ce) {
+    *cb = (int)(s * p.seg);
+    *ce = (int)min((s + 1) * p.seg, p.ub);
+  };
+  auto prep = [&](int cb, int ce) {
+    if (ce > cb)
+      hipLaunchKernelGGL((bwd_prep_kernel<K, V, MT>), dim3((unsigned)(ce - cb), (unsigned)H),
+                         dim3(NTP), 0, st, q, k, v, g, beta, H, (const ChunkRow*)chunks, ntot, cb,
+                         rec);
+  };
+  // Forward through the segments but the last: each one's state at its end, for the sequence
+  // that goes on into the next
+  for (int64_t s = 0; s + 1 < p.nseg; ++s) {
+    int cb, ce;
+    range(s, &cb, &ce);
+    prep(cb, ce);
+    hipLaunchKernelGGL((bwd_fstate_kernel<K, V, false>), sgrid, dim3(NTR), 0, st,
+                       (const float*)rec, a.init_state, (const int32_t*)seq_first, N, H, chains8,
+                       cb, ce, (const float*)(s > 0 ? bound(s) : nullptr), bound(s + 1),
+                       (float*)nullptr, (float*)nullptr);
+  }
+  // Backwards through the segments: the record again, S_c and Delta from the segment's start
+  // state, X_c and dDelta from its end gradient (X of the next segment, kept at the boundary),
+  // then the chunks' gradients
+  for (int64_t s = p.nseg - 1; s >= 0; --s) {
+    int cb, ce;
+    range(s, &cb, &ce);
+    prep(cb, ce);
+    hipLaunchKernelGGL((bwd_fstate_kernel<K, V, true>), sgrid, dim3(NTR), 0, st,
+                       (const float*)rec, a.init_state, (const int32_t*)seq_first, N, H, chains8,
+                       cb, ce, (const float*)(s > 0 ? bound(s) : nullptr), (float*)nullptr, ckS,
+                       Dl);
+    hipLaunchKernelGGL((bwd_rstate_kernel<K, V, MT>), sgrid, dim3(NTR), 0, st, (const float*)rec,
+                       dO, a.dfinal, a.cu_seqlens, a.total_tokens, (const int32_t*)seq_first, N, H,
+                       chains8, cb, ce, (const float*)(s + 1 < p.nseg ? bound(s + 1) : nullptr),
+                       s > 0 ? bound(s) : (float*)nullptr, ckX, dDl, a.grad_init);
+    if (ce > cb) {
+      const dim3 cgrid((unsigned)(ce - cb), (unsigned)H);
+      hipLaunchKernelGGL((bwd_ga_kernel<K, V, MT>), cgrid, dim3(NTGA), 0, st, dO,
+                         (const float*)ckS, (const float*)ckX, (const float*)Dl,
+                         (const float*)dDl, H, (const ChunkRow*)chunks, ntot, cb, scr);
+      hipLaunchKernelGGL((bwd_gb_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, k, v, g, beta,
+                         (const float*)rec, (const float*)dDl, H, (const ChunkRow*)chunks, ntot,
+                         cb, scr, a.grad_v, a.grad_beta);
+      const dim3 pgrid(cgrid.x, cgrid.y, (unsigned)GScr<K>::KP);  // key-channel parts
+      hipLaunchKernelGGL((bwd_gc_kernel<K, V, MT>), pgrid, dim3(NTG), 0, st, q, k, g, beta, H,
+                         (const ChunkRow*)chunks, ntot, cb, scr, a.grad_q, a.grad_k, a.grad_g);
+      hipLaunchKernelGGL((bwd_beta_kernel<K>), cgrid, dim3(BC), 0, st, H,
+                         (const ChunkRow*)chunks, ntot, cb, (const float*)scr, a.grad_beta);
+    }
   }
   return hipGetLastError();
 }

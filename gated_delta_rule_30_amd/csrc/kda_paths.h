@@ -52,14 +52,28 @@ bool make_wide_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, i
                     WidePlan* p);
 hipError_t launch_chunk_fwd_wide(const ChunkArgs& a, const WidePlan& p);
 
-// Training backward (kda_bwd.hip): per chunk and head an fp32 record, the chunk-start states,
-// the chunk-end state gradients, Delta, dDelta and the gradient kernels' scratch, for every
-// chunk at once.
+// Training backward (kda_bwd.hip): per chunk and head of a segment an fp32 record, the
+// chunk-start state, the chunk-end state gradient, Delta, dDelta and the gradient kernels'
+// scratch, plus one [H][K][V] state per segment boundary. Segments of `seg` chunks run
+// backwards; with more than one, a forward pass over the records first leaves the state at
+// every boundary.
 struct BwdPlan {
-  int64_t ub;  // upper bound of the number of chunks over all sequences
-  size_t off_seq, off_chunks, off_rec, off_ckS, off_ckX, off_D, off_dD, off_scr, total_bytes;
+  int64_t ub;    // upper bound of the number of chunks over all sequences
+  int64_t seg;   // chunks per segment
+  int64_t nseg;  // segments (at least one)
+  size_t off_seq, off_chunks, off_ck, off_rec, off_ckS, off_ckX, off_D, off_dD, off_scr,
+      total_bytes;
 };
-bool make_bwd_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv, BwdPlan* p);
+// Per-segment bytes of the default plan (kda_chunk_bwd_workspace_size).
+constexpr size_t BWD_SEGMENT_BYTES = (size_t)4 << 30;
+// seg_chunks <= 0 (or >= the chunk count): one segment
+bool make_bwd_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv,
+                   int64_t seg_chunks, BwdPlan* p);
+// The plan with the longest segments whose workspace fits in `bytes` (false if none does).
+bool fit_bwd_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv, size_t bytes,
+                  BwdPlan* p);
+// Chunks per segment of the default plan.
+int64_t default_bwd_segment(int num_heads, int dk, int dv);
 
 struct BwdArgs {
   const void *q, *k, *v, *g, *beta;

@@ -215,12 +215,28 @@ kda_status kda_chunk_fwd_scan(const void* q, const void* k, const void* v, const
  * Gradients of rows past the end of every sequence are not written (there are none: cu_seqlens
  * covers all rows). No gradient buffer may overlap an input or another gradient
  * (KDA_ERROR_INVALID_VALUE). Head dims K, V in {32, 64, 128}, both dtypes; others give
- * KDA_ERROR_NOT_SUPPORTED. The workspace (kda_chunk_bwd_workspace_size bytes, 256-byte aligned)
- * holds, for every (chunk, head), an fp32 record, the chunk-start state and the chunk-end state
- * gradient and scratch: about 500 KB per 64 tokens and head at K = V = 128.
+ * KDA_ERROR_NOT_SUPPORTED. Every gradient is the same bit for bit on every run (no atomics;
+ * sums in a fixed order).
+ *
+ * Workspace (256-byte aligned): the chunks are taken in segments, processed from the last
+ * backwards; each segment holds, per (chunk, head), an fp32 record, the chunk-start state, the
+ * chunk-end state gradient and scratch (about 500 KB per 64 tokens and head at K = V = 128).
+ * With more than one segment, a forward pass over the records first keeps the state at every
+ * segment boundary (H * K * V fp32 each), and each segment's record and states are formed again
+ * on the way back: the workspace stays near one segment's size for any T, at the cost of that
+ * second pass. kda_chunk_bwd takes the longest segments that workspace_bytes holds (one segment,
+ * no second pass, when it holds every chunk) and returns KDA_ERROR_WORKSPACE_TOO_SMALL when not
+ * even one chunk per segment fits. The gradients do not depend on the segment length.
+ *   kda_chunk_bwd_workspace_size    : the default, segments of about 4 GiB
+ *   kda_chunk_bwd_workspace_size_ex : segments of segment_tokens tokens (rounded up to 64;
+ *                                     <= 0: one segment over every chunk)
+ * Both return 0 for shapes the backward does not support.
  */
 size_t kda_chunk_bwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                                     int32_t dk, int32_t dv, kda_dtype dtype);
+size_t kda_chunk_bwd_workspace_size_ex(int32_t num_seqs, int64_t total_tokens,
+                                       int32_t num_heads, int32_t dk, int32_t dv,
+                                       kda_dtype dtype, int64_t segment_tokens);
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* beta, const float* init_state, const int32_t* cu_seqlens,
                          int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t dk,

@@ -21,6 +21,7 @@ def test_every_declared_symbol_is_exported():
                           "kda_chunk_fwd_noalloc",
                           "kda_chunk_fwd_scan", "kda_chunk_fwd_scan_workspace_size",
                           "kda_chunk_bwd", "kda_chunk_bwd_workspace_size",
+                          "kda_chunk_bwd_workspace_size_ex",
                           "kda_decode_step", "kda_decode_step_ex", "kda_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -271,6 +272,28 @@ def test_bwd_workspace_size():
     assert ws(1, 65536, 4, 128, 256, 1) == 0
     assert ws(0, 100, 4, 64, 64, 1) == 0
     assert ws(1, 0, 4, 64, 64, 0) > 0
+
+
+
+def test_bwd_workspace_is_bounded():
+    L = kda.lib()
+    ws = lambda *a: int(L.kda_chunk_bwd_workspace_size(*a))
+    ex = lambda *a: int(L.kda_chunk_bwd_workspace_size_ex(*a))
+    # default: segments of about 4 GiB, so past one segment only the per-boundary states
+    # (H K V fp32 each) and the chunk table grow with T
+    a, b = ws(1, 1 << 20, 32, 128, 128, 1), ws(1, 1 << 21, 32, 128, 128, 1)
+    assert a < 5 << 30 and b - a < 700 << 20
+    # one segment over every chunk: about 500 KB per 64 tokens and head
+    one = ex(1, 65536, 32, 128, 128, 1, 0)
+    assert 15 << 30 < one < 17 << 30
+    assert ex(1, 2 * 65536, 32, 128, 128, 1, 0) > 1.9 * one
+    # segments of one chunk: 16 MB of per-chunk arrays, and a boundary state (2 MB) per chunk
+    small = ex(1, 65536, 32, 128, 128, 1, 64)
+    assert 2 << 30 < small < 2.1 * (1 << 30)
+    # segments of three chunks: a third of the boundary states
+    assert ex(1, 65536, 32, 128, 128, 1, 192) < 0.4 * small
+    assert ex(1, 65536, 32, 128, 128, 1, 1) == small  # rounded up to whole chunks
+    assert ex(1, 65536, 32, 128, 256, 1, 64) == 0
 
 
 def test_wide_key_workspace_size():

@@ -18,7 +18,8 @@ NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dinit")
 TOL = 1e-4
 
 
-def _run(inp, cu=None, N=1, with_init=True, with_dfinal=True, seed=0, dtype=torch.bfloat16):
+def _run(inp, cu=None, N=1, with_init=True, with_dfinal=True, seed=0, dtype=torch.bfloat16,
+         segment_tokens=None):
     T, H, K = inp["q"].shape
     V = inp["v"].shape[-1]
     gen = torch.Generator(device=DEV)
@@ -27,7 +28,7 @@ def _run(inp, cu=None, N=1, with_init=True, with_dfinal=True, seed=0, dtype=torc
     dfin = torch.randn((N, H, K, V), generator=gen, device=DEV) if with_dfinal else None
     init = inp["init_state"] if with_init else None
     grads = kda.chunk_bwd(*(inp[x] for x in ORDER), d_o, init_state=init, d_final_state=dfin,
-                          cu_seqlens=cu, num_seqs=N)
+                          cu_seqlens=cu, num_seqs=N, segment_tokens=segment_tokens)
     ref = oracle.kda_bwd(*(np64(inp[x]) for x in ORDER), np64(d_o),
                          dfinal=None if dfin is None else np64(dfin),
                          cu_seqlens=None if cu is None else cu.cpu().numpy().astype(np.int64),
@@ -62,6 +63,66 @@ def test_bwd_varlen_with_empty_sequence():
     inp = workloads.gen_forward(T, H, K, K, dtype=torch.bfloat16, device=DEV, seed=5,
                                 num_seqs=len(lens), init_std=0.1)
     _run(inp, cu=cu, N=len(lens), seed=5)
+
+
+def _grads(inp, d_o, dfin, cu=None, N=1, segment_tokens=None, init=True):
+    return kda.chunk_bwd(*(inp[x] for x in ORDER), d_o,
+                         init_state=inp["init_state"] if init else None, d_final_state=dfin,
+                         cu_seqlens=cu, num_seqs=N, segment_tokens=segment_tokens)
+
+
+def test_bwd_segmented_against_oracle():
+    """Segments of 3 chunks (the chunks are processed from the last segment backwards, each
+    segment's chunk-start states formed again from the state kept at its first chunk): every
+    gradient against the oracle, varlen with sequences across segment boundaries."""
+    print("bwd segments of 192 tokens, varlen", flush=True)
+    lens = [400, 0, 530, 64, 191]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    T, H, K = int(cu[-1]), 2, 128
+    inp = workloads.gen_forward(T, H, K, K, dtype=torch.bfloat16, device=DEV, seed=15,
+                                num_seqs=len(lens), init_std=0.1)
+    _run(inp, cu=cu, N=len(lens), seed=15, segment_tokens=192)
+
+
+@pytest.mark.parametrize("K,V,dtype,with_init", [
+    (128, 128, torch.bfloat16, True),
+    (64, 32, torch.float32, False),
+])
+def test_bwd_segment_length_does_not_change_gradients(K, V, dtype, with_init):
+    """The gradients are the same bit for bit for one segment, the default and segments of 1, 2
+    and 5 chunks (sequences starting, ending and empty inside and across segments)."""
+    lens = [333, 64, 0, 1, 700, 0, 130]
+    print("bwd segment lengths", K, V, dtype, flush=True)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    T, H, N = int(cu[-1]), 2, len(lens)
+    inp = workloads.gen_forward(T, H, K, V, dtype=dtype, device=DEV, seed=16, num_seqs=N,
+                                init_std=0.1)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(16)
+    d_o = torch.randn((T, H, V), generator=gen, device=DEV).to(dtype)
+    dfin = torch.randn((N, H, K, V), generator=gen, device=DEV)
+    one = _grads(inp, d_o, dfin, cu, N, segment_tokens=0, init=with_init)
+    for seg in (None, 64, 128, 320):
+        got = _grads(inp, d_o, dfin, cu, N, segment_tokens=seg, init=with_init)
+        for name, a, b in zip(NAMES, one, got):
+            assert torch.equal(a, b), "%s differs with segments of %s tokens" % (name, seg)
+
+
+def test_bwd_deterministic():
+    """Two runs give the same gradients bit for bit (fixed-order sums, no atomics), at
+    K = V = 128 (two key-channel parts in the gradient kernel) and at K = 32."""
+    for K, V, T, H in ((128, 128, 2048, 4), (32, 64, 1000, 3)):
+        print("bwd twice", K, V, T, H, flush=True)
+        inp = workloads.gen_forward(T, H, K, V, dtype=torch.bfloat16, device=DEV, seed=17,
+                                    init_std=0.1)
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(17)
+        d_o = torch.randn((T, H, V), generator=gen, device=DEV).to(torch.bfloat16)
+        dfin = torch.randn((1, H, K, V), generator=gen, device=DEV)
+        a = _grads(inp, d_o, dfin)
+        b = _grads(inp, d_o, dfin)
+        for name, x, y in zip(NAMES, a, b):
+            assert torch.equal(x, y), name
 
 
 def test_bwd_without_initial_state_or_final_gradient():
