@@ -592,7 +592,7 @@ def main():
         # the default workspace (segments of about 4 GiB, a second pass over the records for
         # the states at the segment boundaries), then one segment over every chunk
         ws_def = int(L.kda_chunk_bwd_workspace_size(1, T, H, K, V, 1))
-        ws_one = int(L.kda_chunk_bwd_workspace_size_ex(1, T, H, K, V, 1, 0))
+        ws_one = int(L.kda_chunk_bwd_workspace_size_ex(1, T, H, K, V, 1, 0, 0))
         bms, bsteps, grads, same = time_bwd(ws_def)
         finite = bool(all(torch.isfinite(g).all().item() for g in grads))
         del grads

@@ -69,10 +69,15 @@ def _lib():
         lib.kda_chunk_bwd_workspace_size.restype = sz
         lib.kda_chunk_bwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
         lib.kda_chunk_bwd_workspace_size_ex.restype = sz
-        lib.kda_chunk_bwd_workspace_size_ex.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int, i64]
+        lib.kda_chunk_bwd_workspace_size_ex.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int,
+                                                        ctypes.c_uint32, i64]
         lib.kda_chunk_bwd.restype = ctypes.c_int
         lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                       ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.kda_chunk_bwd_ex.restype = ctypes.c_int
+        lib.kda_chunk_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                         ctypes.c_int, ctypes.c_uint32, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, vp, sz, vp]
         lib.kda_decode_step_ex.restype = ctypes.c_int
         lib.kda_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                            ctypes.c_int, u32, vp]
@@ -126,14 +131,14 @@ def workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype) -> int:
     return int(_lib().kda_chunk_fwd_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, code))
 
 
-def bwd_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype, segment_tokens=None) -> int:
-    """Workspace bytes of chunk_bwd: the default segments, or segments of ``segment_tokens``
-    tokens (0: one segment over every chunk)."""
+def bwd_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype, segment_tokens=None,
+                       options=0) -> int:
+    """Workspace bytes of chunk_bwd with these input options (OPT_* bits): the default
+    segments (``segment_tokens`` None), or segments of that many tokens (0: one segment)."""
     code = KDA_DTYPE_BF16 if dtype == torch.bfloat16 else KDA_DTYPE_F32
-    if segment_tokens is None:
-        return int(_lib().kda_chunk_bwd_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, code))
+    seg = -1 if segment_tokens is None else int(segment_tokens)
     return int(_lib().kda_chunk_bwd_workspace_size_ex(num_seqs, total_tokens, num_heads, dk, dv,
-                                                      code, int(segment_tokens)))
+                                                      code, int(options), seg))
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, num_seqs=None,
@@ -261,14 +266,16 @@ def chunk_fwd_scan(q, k, v, log_alpha, beta, init_state=None, num_seqs=1, num_gr
 
 
 def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final_state=None,
-              cu_seqlens=None, num_seqs=None, workspace=None, grads=None, segment_tokens=None):
-    """kda_chunk_bwd on torch tensors: the gradients of sum(d_o * o) + sum(d_final_state *
-    final_state) for chunk_fwd on the same inputs (no input options). d_o [T, H, V] in the input
-    dtype; d_final_state [N, H, K, V] fp32 or None (zero). Returns fp32 tensors
-    (dq [T, H, K], dk [T, H, K], dv [T, H, V], dlog_alpha [T, H, K], dbeta [T, H],
-    dinit_state [N, H, K, V]). ``grads`` may pass those six tensors to be written in place
-    (e.g. under graph capture). Without ``workspace``, one of the default size is allocated, or,
-    with ``segment_tokens``, one sized for segments of that many tokens (0: one segment)."""
+              cu_seqlens=None, num_seqs=None, workspace=None, grads=None, segment_tokens=None,
+              options=0):
+    """kda_chunk_bwd_ex on torch tensors: the gradients of sum(d_o * o) + sum(d_final_state *
+    final_state) for chunk_fwd on the same inputs and options (OPT_* bits; with OPT_SCALAR_GATE
+    log_alpha and its gradient are [T, H]). d_o [T, H, V] in the input dtype; d_final_state
+    [N, H, K, V] fp32 or None (zero). Returns fp32 tensors (dq [T, H, K], dk [T, H, K],
+    dv [T, H, V], dlog_alpha, dbeta [T, H], dinit_state [N, H, K, V]). ``grads`` may pass those
+    six tensors to be written in place (e.g. under graph capture). Without ``workspace``, one of
+    the default size is allocated, or, with ``segment_tokens``, one sized for segments of that
+    many tokens (0: one segment)."""
     device = q.device
     T, H, K = q.shape
     V = v.shape[-1]
@@ -281,8 +288,9 @@ def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final_state=None
             raise ValueError("num_seqs does not match cu_seqlens")
     else:
         N = 1 if num_seqs is None else int(num_seqs)
+    gshape = (T, H) if options & OPT_SCALAR_GATE else (T, H, K)
     for name, t, shp in (("q", q, (T, H, K)), ("k", k, (T, H, K)), ("v", v, (T, H, V)),
-                         ("log_alpha", log_alpha, (T, H, K)), ("beta", beta, (T, H)),
+                         ("log_alpha", log_alpha, gshape), ("beta", beta, (T, H)),
                          ("d_o", d_o, (T, H, V))):
         _check(t, name, shp, dt, device)
     for name, t in (("init_state", init_state), ("d_final_state", d_final_state)):
@@ -290,30 +298,30 @@ def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final_state=None
             _check(t, name, (N, H, K, V), torch.float32, device)
     f32 = dict(dtype=torch.float32, device=device)
     if grads is None:
-        dq, dk, dg = (torch.empty((T, H, K), **f32) for _ in range(3))
+        dq, dk = (torch.empty((T, H, K), **f32) for _ in range(2))
+        dg = torch.empty(gshape, **f32)
         dv = torch.empty((T, H, V), **f32)
         db = torch.empty((T, H), **f32)
         dinit = torch.empty((N, H, K, V), **f32)
     else:
         dq, dk, dv, dg, db, dinit = grads
         for name, t, shp in (("dq", dq, (T, H, K)), ("dk", dk, (T, H, K)), ("dv", dv, (T, H, V)),
-                             ("dlog_alpha", dg, (T, H, K)), ("dbeta", db, (T, H)),
+                             ("dlog_alpha", dg, gshape), ("dbeta", db, (T, H)),
                              ("dinit_state", dinit, (N, H, K, V))):
             _check(t, name, shp, torch.float32, device)
-    need = int(_lib().kda_chunk_bwd_workspace_size(N, T, H, K, V, code) if segment_tokens is None
-               else _lib().kda_chunk_bwd_workspace_size_ex(N, T, H, K, V, code, int(segment_tokens)))
-    if need == 0:
-        raise KdaError(2 if K not in (32, 64, 128) or V not in (32, 64, 128) else 1,
-                       "kda_chunk_bwd_workspace_size")
     if workspace is None:
+        need = bwd_workspace_size(N, T, H, K, V, dt, segment_tokens, options)
+        if need == 0:
+            raise KdaError(2 if K not in (32, 64, 128) or V not in (32, 64, 128) else 1,
+                           "kda_chunk_bwd_workspace_size_ex")
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
-    st = _lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                              _ptr(init_state), _ptr(cu_seqlens), N, T, H, K, V, code, _ptr(d_o),
-                              _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
-                              _ptr(db), _ptr(dinit), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _stream(device))
+    st = _lib().kda_chunk_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                 _ptr(init_state), _ptr(cu_seqlens), N, T, H, K, V, code,
+                                 int(options), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(dg), _ptr(db), _ptr(dinit), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(device))
     if st != 0:
-        raise KdaError(st, "kda_chunk_bwd")
+        raise KdaError(st, "kda_chunk_bwd_ex")
     return dq, dk, dv, dg, db, dinit
 
 

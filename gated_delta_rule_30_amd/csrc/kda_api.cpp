@@ -185,11 +185,15 @@ static kda_status check_bwd_shape(int32_t num_seqs, int64_t total_tokens, int32_
 
 extern "C" size_t kda_chunk_bwd_workspace_size_ex(int32_t num_seqs, int64_t total_tokens,
                                                   int32_t num_heads, int32_t dk, int32_t dv,
-                                                  kda_dtype dtype, int64_t segment_tokens) {
+                                                  kda_dtype dtype, uint32_t options,
+                                                  int64_t segment_tokens) {
   if (check_bwd_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype) != KDA_SUCCESS) return 0;
+  if (options & ~kAllOptions) return 0;
   kda::BwdPlan p;
-  const int64_t seg = segment_tokens <= 0 ? 0 : (segment_tokens + kda::CHUNK - 1) / kda::CHUNK;
-  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, seg, &p)) return 0;
+  const int64_t seg = segment_tokens < 0    ? kda::default_bwd_segment(num_heads, dk, dv)
+                      : segment_tokens == 0 ? 0
+                                            : (segment_tokens + kda::CHUNK - 1) / kda::CHUNK;
+  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, options, seg, &p)) return 0;
   return p.total_bytes;
 }
 
@@ -198,44 +202,51 @@ extern "C" size_t kda_chunk_bwd_workspace_size(int32_t num_seqs, int64_t total_t
                                                kda_dtype dtype) {
   if (check_bwd_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype) != KDA_SUCCESS) return 0;
   kda::BwdPlan p;
-  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv,
+  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, 0u,
                           kda::default_bwd_segment(num_heads, dk, dv), &p))
     return 0;
   return p.total_bytes;
 }
 
-extern "C" kda_status kda_chunk_bwd(const void* q, const void* k, const void* v,
-                                    const void* log_alpha, const void* beta,
-                                    const float* init_state, const int32_t* cu_seqlens,
-                                    int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
-                                    int32_t dk, int32_t dv, kda_dtype dtype, const void* d_o,
-                                    const float* d_final_state, float* grad_q, float* grad_k,
-                                    float* grad_v, float* grad_log_alpha, float* grad_beta,
-                                    float* grad_init_state, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+extern "C" kda_status kda_chunk_bwd_ex(const void* q, const void* k, const void* v,
+                                       const void* log_alpha, const void* beta,
+                                       const float* init_state, const int32_t* cu_seqlens,
+                                       int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                       int32_t dk, int32_t dv, kda_dtype dtype, uint32_t options,
+                                       const void* d_o, const float* d_final_state, float* grad_q,
+                                       float* grad_k, float* grad_v, float* grad_log_alpha,
+                                       float* grad_beta, float* grad_init_state, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
   kda_status st = check_bwd_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_SUCCESS) return st;
+  if (options & ~kAllOptions) return KDA_ERROR_NOT_SUPPORTED;
+  const bool scalar = (options & KDA_OPT_SCALAR_GATE) != 0;
   if (cu_seqlens == nullptr && total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
   if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !d_o || !grad_q || !grad_k ||
                            !grad_v || !grad_log_alpha || !grad_beta))
     return KDA_ERROR_INVALID_VALUE;
   if (!workspace) return KDA_ERROR_INVALID_VALUE;
-  const void* vec[] = {q, k, v, log_alpha, d_o, init_state, d_final_state, grad_q, grad_k,
-                       grad_v, grad_log_alpha, grad_init_state};
+  // the scalar gate and its gradient ([rows][H]) need only their element alignment
+  const void* vec[] = {q, k, v, d_o, init_state, d_final_state, grad_q, grad_k, grad_v,
+                       grad_init_state, scalar ? nullptr : log_alpha,
+                       scalar ? nullptr : grad_log_alpha};
   for (const void* p : vec)
     if (p && !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
   if ((beta && !aligned_to(beta, esize(dtype))) || (grad_beta && !aligned_to(grad_beta, 4)) ||
-      (cu_seqlens && !aligned_to(cu_seqlens, 4)))
+      (cu_seqlens && !aligned_to(cu_seqlens, 4)) ||
+      (scalar && log_alpha && !aligned_to(log_alpha, esize(dtype))) ||
+      (scalar && grad_log_alpha && !aligned_to(grad_log_alpha, 4)))
     return KDA_ERROR_INVALID_VALUE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERROR_INVALID_VALUE;
   // every gradient buffer is written while the inputs are still read: none may overlap them
   const size_t T = (size_t)total_tokens, H = (size_t)num_heads, es = esize(dtype);
   const size_t sbytes = (size_t)num_seqs * H * dk * dv * sizeof(float);
   const void* in_p[] = {q, k, v, log_alpha, beta, d_o, init_state, d_final_state};
-  const size_t in_n[] = {T * H * dk * es, T * H * dk * es, T * H * dv * es, T * H * dk * es,
+  const size_t gd = scalar ? 1 : (size_t)dk;  // gate values per token and head
+  const size_t in_n[] = {T * H * dk * es, T * H * dk * es, T * H * dv * es, T * H * gd * es,
                          T * H * es, T * H * dv * es, sbytes, sbytes};
   const void* out_p[] = {grad_q, grad_k, grad_v, grad_log_alpha, grad_beta, grad_init_state};
-  const size_t out_n[] = {T * H * dk * 4, T * H * dk * 4, T * H * dv * 4, T * H * dk * 4, T * H * 4,
+  const size_t out_n[] = {T * H * dk * 4, T * H * dk * 4, T * H * dv * 4, T * H * gd * 4, T * H * 4,
                           sbytes};
   for (int o = 0; o < 6; ++o) {
     if (!out_p[o] || out_n[o] == 0) continue;
@@ -247,8 +258,9 @@ extern "C" kda_status kda_chunk_bwd(const void* q, const void* k, const void* v,
   }
   // the longest segments the caller's workspace holds (one segment when it holds them all)
   kda::BwdPlan p;
-  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, 0, &p)) return KDA_ERROR_INVALID_VALUE;
-  if (!kda::fit_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, workspace_bytes, &p))
+  if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, options, 0, &p))
+    return KDA_ERROR_INVALID_VALUE;
+  if (!kda::fit_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, options, workspace_bytes, &p))
     return KDA_ERROR_WORKSPACE_TOO_SMALL;
   kda::BwdArgs a;
   a.q = q;
@@ -272,10 +284,26 @@ extern "C" kda_status kda_chunk_bwd(const void* q, const void* k, const void* v,
   a.grad_g = grad_log_alpha;
   a.grad_beta = grad_beta;
   a.grad_init = grad_init_state;
+  a.options = options;
   a.workspace = workspace;
   a.stream = stream;
   hipError_t e = kda::launch_chunk_bwd(a, p);
   return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+}
+
+extern "C" kda_status kda_chunk_bwd(const void* q, const void* k, const void* v,
+                                    const void* log_alpha, const void* beta,
+                                    const float* init_state, const int32_t* cu_seqlens,
+                                    int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                    int32_t dk, int32_t dv, kda_dtype dtype, const void* d_o,
+                                    const float* d_final_state, float* grad_q, float* grad_k,
+                                    float* grad_v, float* grad_log_alpha, float* grad_beta,
+                                    float* grad_init_state, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return kda_chunk_bwd_ex(q, k, v, log_alpha, beta, init_state, cu_seqlens, num_seqs,
+                          total_tokens, num_heads, dk, dv, dtype, 0u, d_o, d_final_state, grad_q,
+                          grad_k, grad_v, grad_log_alpha, grad_beta, grad_init_state, workspace,
+                          workspace_bytes, stream);
 }
 
 static kda_status check_scan_shape(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,

@@ -111,10 +111,11 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------- per-chunk record
-template <int K, int V, typename MT>
+// MT: v; GT: q, k, log alpha and beta (fp32 when an input-option pass formed them)
+template <int K, int V, typename MT, typename GT>
 __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
-    const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ v,
-    const MT* __restrict__ g, const MT* __restrict__ beta, int H,
+    const GT* __restrict__ q, const GT* __restrict__ k, const MT* __restrict__ v,
+    const GT* __restrict__ g, const GT* __restrict__ beta, int H,
     const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, int cb,
     float* __restrict__ rec) {
   using R = BRec<K, V>;
@@ -146,9 +147,9 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
 #pragma unroll
   for (int u = 0; u < VPT; ++u) a[u] = p[u] = 0.f;
   for (int c0 = 0; c0 < K; c0 += KC) {
-    load_rows<KC, LQ, NTP, MT, K>(sQ, q, ch.tok, ch.len, H, h, c0);
-    load_rows<KC, LK, NTP, MT, K>(sK, k, ch.tok, ch.len, H, h, c0);
-    load_rows<KC, LK, NTP, MT, K>(sB, g, ch.tok, ch.len, H, h, c0);
+    load_rows<KC, LQ, NTP, GT, K>(sQ, q, ch.tok, ch.len, H, h, c0);
+    load_rows<KC, LK, NTP, GT, K>(sK, k, ch.tok, ch.len, H, h, c0);
+    load_rows<KC, LK, NTP, GT, K>(sB, g, ch.tok, ch.len, H, h, c0);
     lds_barrier();
     cumsum_log2<KC, LK, NTP>(sB);
     lds_barrier();
@@ -221,11 +222,11 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
   lds_barrier();
   // W = T diag(beta) (k e^b), part by part
   for (int c0 = 0; c0 < K; c0 += KC) {
-    load_rows<KC, LK, NTP, MT, K>(sB, g, ch.tok, ch.len, H, h, c0);
+    load_rows<KC, LK, NTP, GT, K>(sB, g, ch.tok, ch.len, H, h, c0);
     lds_barrier();
     cumsum_log2<KC, LK, NTP>(sB);
     lds_barrier();
-    mul_rows_exp2<KC, LK, NTP, MT, K>(sB, k, ch.tok, ch.len, H, h, c0);
+    mul_rows_exp2<KC, LK, NTP, GT, K>(sB, k, ch.tok, ch.len, H, h, c0);
     lds_barrier();
     for (int e = threadIdx.x; e < BC * KC; e += NTP) sB[(e / KC) * LK + e % KC] *= sBeta[e / KC];
     lds_barrier();
@@ -633,10 +634,10 @@ __global__ __launch_bounds__(NTGA, 8) void bwd_ga_kernel(
 // (b) dv = diag(beta) T^T dDelta, T^T dW, dT = dDelta (beta V)^T + dW (beta Ke)^T,
 //     dA = strict_lower(-T^T dT T^T), and dbeta's terms rowsum(V * T^T dDelta) and
 //     rowsum(Ke * T^T dW)
-template <int K, int V, typename MT>
+template <int K, int V, typename MT, typename GT>
 __global__ __launch_bounds__(NTG, 8) void bwd_gb_kernel(
-    const MT* __restrict__ k, const MT* __restrict__ v, const MT* __restrict__ g,
-    const MT* __restrict__ beta, const float* __restrict__ rec, const float* __restrict__ dDl, int H,
+    const GT* __restrict__ k, const MT* __restrict__ v, const GT* __restrict__ g,
+    const GT* __restrict__ beta, const float* __restrict__ rec, const float* __restrict__ dDl, int H,
     const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, int cb,
     float* __restrict__ scr, float* __restrict__ grad_v, float* __restrict__ grad_beta) {
   using R = BRec<K, V>;
@@ -701,11 +702,11 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gb_kernel(
   for (int c0 = 0; c0 < K; c0 += KC) {
     // dW and Ke = k e^b (the decay is per channel, so a part's cumulative sum is its own)
     load_block<KC, LDW, NTG, BC, K>(bufA, sc + G::oDW + c0);
-    load_rows<KC, LKE, NTG, MT, K>(bufB, g, ch.tok, ch.len, H, h, c0);
+    load_rows<KC, LKE, NTG, GT, K>(bufB, g, ch.tok, ch.len, H, h, c0);
     lds_barrier();
     cumsum_log2<KC, LKE, NTG>(bufB);
     lds_barrier();
-    mul_rows_exp2<KC, LKE, NTG, MT, K>(bufB, k, ch.tok, ch.len, H, h, c0);
+    mul_rows_exp2<KC, LKE, NTG, GT, K>(bufB, k, ch.tok, ch.len, H, h, c0);
     lds_barrier();
     // T^T dW; dbeta += rowsum(Ke * T^T dW)
     mmf<KC, BC, true, false, LT, LDW, NTG>(sT, bufA, [&](int r, int cc, float x) {
@@ -739,10 +740,10 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gb_kernel(
 }
 
 // (c) the decay-weighted pairwise sums and the per-token gradients of q, k, log alpha, beta
-template <int K, int V, typename MT>
+template <int K, int V, typename GT>
 __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
-    const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ g,
-    const MT* __restrict__ beta, int H, const ChunkRow* __restrict__ chunks,
+    const GT* __restrict__ q, const GT* __restrict__ k, const GT* __restrict__ g,
+    const GT* __restrict__ beta, int H, const ChunkRow* __restrict__ chunks,
     const int32_t* __restrict__ ntot, int cb, float* __restrict__ scr, float* __restrict__ grad_q,
     float* __restrict__ grad_k, float* __restrict__ grad_g) {
   using G = GScr<K>;
@@ -773,9 +774,9 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
   const int m = threadIdx.x % KC, i0 = threadIdx.x / KC;
   const int c0 = blockIdx.z * KC;
   {
-    load_rows<KC, LK, NTG, MT, K>(sQ, q, ch.tok, ch.len, H, h, c0);
-    load_rows<KC, LK, NTG, MT, K>(sK, k, ch.tok, ch.len, H, h, c0);
-    load_rows<KC, LK, NTG, MT, K>(sB, g, ch.tok, ch.len, H, h, c0);
+    load_rows<KC, LK, NTG, GT, K>(sQ, q, ch.tok, ch.len, H, h, c0);
+    load_rows<KC, LK, NTG, GT, K>(sK, k, ch.tok, ch.len, H, h, c0);
+    load_rows<KC, LK, NTG, GT, K>(sB, g, ch.tok, ch.len, H, h, c0);
     // this thread's rows of dO S^T, T^T dW and Delta X^T, in flight through the scan
     float r1v[RB], tdw[RB], dkv[RB];
 #pragma unroll
@@ -919,7 +920,8 @@ static BwdFloats bwd_floats(int K, int V) {
   return BwdFloats{0, 0, 0};
 }
 
-bool make_bwd_plan(int N, int64_t T, int H, int K, int V, int64_t seg_chunks, BwdPlan* p) {
+bool make_bwd_plan(int N, int64_t T, int H, int K, int V, uint32_t options, int64_t seg_chunks,
+                   BwdPlan* p) {
   if (N <= 0 || H <= 0 || T < 0) return false;
   const BwdFloats fl = bwd_floats(K, V);
   if (fl.all == 0) return false;
@@ -932,6 +934,21 @@ bool make_bwd_plan(int N, int64_t T, int H, int K, int V, int64_t seg_chunks, Bw
   if (ub >= (1LL << 31)) return false;
   const size_t chv = (size_t)p->seg * H;
   size_t off = 0;
+  // with input options: the processed q, k, log alpha and beta (fp32, every token), and with
+  // the scalar gate the per-channel gradient of log alpha before its sum over the channels
+  const size_t tk = al256((size_t)T * H * K * 4);
+  p->off_opt_q = p->off_opt_k = p->off_opt_g = p->off_opt_b = p->off_opt_dg = 0;
+  if (options != 0) {
+    p->off_opt_q = off;
+    p->off_opt_k = off + tk;
+    p->off_opt_g = off + 2 * tk;
+    p->off_opt_b = off + 3 * tk;
+    off += 3 * tk + al256((size_t)T * H * 4);
+    if (options & OPT_SCALAR_GATE) {
+      p->off_opt_dg = off;
+      off += tk;
+    }
+  }
   p->off_seq = off;
   off += al256((size_t)(N + 1) * 4);
   p->off_chunks = off;
@@ -956,14 +973,15 @@ bool make_bwd_plan(int N, int64_t T, int H, int K, int V, int64_t seg_chunks, Bw
   return true;
 }
 
-bool fit_bwd_plan(int N, int64_t T, int H, int K, int V, size_t bytes, BwdPlan* p) {
-  if (!make_bwd_plan(N, T, H, K, V, 0, p)) return false;
+bool fit_bwd_plan(int N, int64_t T, int H, int K, int V, uint32_t options, size_t bytes,
+                  BwdPlan* p) {
+  if (!make_bwd_plan(N, T, H, K, V, options, 0, p)) return false;
   if (p->total_bytes <= bytes) return true;
   // the longest segments that fit: from the per-chunk bytes down, shorter until it fits
   const size_t per_chunk = (size_t)H * bwd_floats(K, V).all * 4;
   int64_t e = (int64_t)min(bytes / per_chunk, (size_t)p->ub - 1);
   while (e >= 1) {
-    if (!make_bwd_plan(N, T, H, K, V, e, p)) return false;
+    if (!make_bwd_plan(N, T, H, K, V, options, e, p)) return false;
     if (p->total_bytes <= bytes) return true;
     e = e > 64 ? e - e / 32 : e - 1;
   }
@@ -977,7 +995,8 @@ int64_t default_bwd_segment(int H, int K, int V) {
   return e > 1 ? e : 1;
 }
 
-template <int K, int V, typename MT>
+// MT: v and dO; GT: q, k, log alpha and beta
+template <int K, int V, typename MT, typename GT>
 static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
   hipStream_t st = (hipStream_t)a.stream;
   char* ws = reinterpret_cast<char*>(a.workspace);
@@ -992,8 +1011,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
   float* scr = reinterpret_cast<float*>(ws + p.off_scr);
   const int N = a.num_seqs, H = a.num_heads;
   const int32_t* ntot = seq_first + N;
-  const MT *q = (const MT*)a.q, *k = (const MT*)a.k, *v = (const MT*)a.v, *g = (const MT*)a.g,
-           *beta = (const MT*)a.beta, *dO = (const MT*)a.dO;
+  const GT *q = (const GT*)a.q, *k = (const GT*)a.k, *g = (const GT*)a.g, *beta = (const GT*)a.beta;
+  const MT *v = (const MT*)a.v, *dO = (const MT*)a.dO;
   launch_chunk_rows(a.cu_seqlens, N, a.total_tokens, p.ub, seq_first, chunks, st);
   const int chains8 = (N * H + 7) / 8 * 8;
   const dim3 sgrid((unsigned)(chains8 * (V / 16)));
@@ -1006,7 +1025,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
   };
   auto prep = [&](int cb, int ce) {
     if (ce > cb)
-      hipLaunchKernelGGL((bwd_prep_kernel<K, V, MT>), dim3((unsigned)(ce - cb), (unsigned)H),
+      hipLaunchKernelGGL((bwd_prep_kernel<K, V, MT, GT>), dim3((unsigned)(ce - cb), (unsigned)H),
                          dim3(NTP), 0, st, q, k, v, g, beta, H, (const ChunkRow*)chunks, ntot, cb,
                          rec);
   };
@@ -1041,11 +1060,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
       hipLaunchKernelGGL((bwd_ga_kernel<K, V, MT>), cgrid, dim3(NTGA), 0, st, dO,
                          (const float*)ckS, (const float*)ckX, (const float*)Dl,
                          (const float*)dDl, H, (const ChunkRow*)chunks, ntot, cb, scr);
-      hipLaunchKernelGGL((bwd_gb_kernel<K, V, MT>), cgrid, dim3(NTG), 0, st, k, v, g, beta,
+      hipLaunchKernelGGL((bwd_gb_kernel<K, V, MT, GT>), cgrid, dim3(NTG), 0, st, k, v, g, beta,
                          (const float*)rec, (const float*)dDl, H, (const ChunkRow*)chunks, ntot,
                          cb, scr, a.grad_v, a.grad_beta);
       const dim3 pgrid(cgrid.x, cgrid.y, (unsigned)GScr<K>::KP);  // key-channel parts
-      hipLaunchKernelGGL((bwd_gc_kernel<K, V, MT>), pgrid, dim3(NTG), 0, st, q, k, g, beta, H,
+      hipLaunchKernelGGL((bwd_gc_kernel<K, V, GT>), pgrid, dim3(NTG), 0, st, q, k, g, beta, H,
                          (const ChunkRow*)chunks, ntot, cb, scr, a.grad_q, a.grad_k, a.grad_g);
       hipLaunchKernelGGL((bwd_beta_kernel<K>), cgrid, dim3(BC), 0, st, H,
                          (const ChunkRow*)chunks, ntot, cb, (const float*)scr, a.grad_beta);
@@ -1055,14 +1074,39 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a, const BwdPlan& p) {
-#define KDA_BWD_CASE(KK, VV)                                                     \
-  if (a.dk == KK && a.dv == VV)                                                  \
-    return a.dtype_bf16 ? launch_bwd_t<KK, VV, bf16>(a, p) : launch_bwd_t<KK, VV, float>(a, p);
+  hipStream_t st = (hipStream_t)a.stream;
+  BwdArgs b = a;
+  if (a.options != 0) {
+    // the processed inputs first (fp32, in the workspace's leading region), the backward on
+    // them, then the chain rule back to the raw inputs
+    char* ws = reinterpret_cast<char*>(a.workspace);
+    const OptBuffers ob{reinterpret_cast<float*>(ws + p.off_opt_q), reinterpret_cast<float*>(ws + p.off_opt_k),
+                        reinterpret_cast<float*>(ws + p.off_opt_g), reinterpret_cast<float*>(ws + p.off_opt_b)};
+    const OptInputs in{a.q, a.k, a.g, a.beta};
+    launch_prologue(in, a.dtype_bf16, a.total_tokens, a.num_heads, a.dk, a.options, nullptr,
+                    nullptr, 0, 0, ob, st, a.total_tokens);
+    b.q = ob.q;
+    b.k = ob.k;
+    b.g = ob.g;
+    b.beta = ob.beta;
+    if (a.options & OPT_SCALAR_GATE) b.grad_g = reinterpret_cast<float*>(ws + p.off_opt_dg);
+  }
+  hipError_t e = hipErrorInvalidValue;
+#define KDA_BWD_CASE(KK, VV)                                                                 \
+  if (a.dk == KK && a.dv == VV)                                                              \
+    e = a.options != 0 ? (a.dtype_bf16 ? launch_bwd_t<KK, VV, bf16, float>(b, p)              \
+                                       : launch_bwd_t<KK, VV, float, float>(b, p))            \
+                       : (a.dtype_bf16 ? launch_bwd_t<KK, VV, bf16, bf16>(b, p)               \
+                                       : launch_bwd_t<KK, VV, float, float>(b, p));
   KDA_BWD_CASE(32, 32) KDA_BWD_CASE(32, 64) KDA_BWD_CASE(32, 128)
   KDA_BWD_CASE(64, 32) KDA_BWD_CASE(64, 64) KDA_BWD_CASE(64, 128)
   KDA_BWD_CASE(128, 32) KDA_BWD_CASE(128, 64) KDA_BWD_CASE(128, 128)
 #undef KDA_BWD_CASE
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || a.options == 0) return e;
+  launch_bwd_epilogue(OptInputs{a.q, a.k, a.g, a.beta}, a.dtype_bf16, a.total_tokens,
+                      a.num_heads, a.dk, a.options, a.grad_q, a.grad_k, b.grad_g, a.grad_g,
+                      a.grad_beta, st);
+  return hipGetLastError();
 }
 
 }  // namespace kda

@@ -43,6 +43,26 @@ struct ChunkRow {
 hipError_t launch_chunk_rows(const int32_t* cu, int N, int64_t T, int64_t ub, int32_t* seq_first,
                              ChunkRow* rows, hipStream_t st);
 
+// Input options as a pass of their own (kda_prologue.hip), for the paths whose kernels read
+// plain inputs. launch_prologue writes the processed q, k, log alpha ([rows][H][K]) and beta
+// ([rows][H]) in fp32: every token of the call at its own row (chunks = nullptr), or the
+// tokens of chunks [cb, ce) from row 0 (max_rows bounds their number, for the grid).
+// launch_bwd_epilogue turns gradients with respect to the processed inputs into gradients
+// with respect to the raw ones (grad_q, grad_k, grad_beta in place; dg [T][H][K] into grad_g,
+// which is [T][H] with the scalar gate).
+struct OptInputs {
+  const void *q, *k, *g, *beta;
+};
+struct OptBuffers {
+  float *q, *k, *g, *beta;
+};
+void launch_prologue(const OptInputs& in, bool bf16, int64_t T, int H, int K, uint32_t options,
+                     const ChunkRow* chunks, const int32_t* ntot, int cb, int ce,
+                     const OptBuffers& out, hipStream_t st, int64_t max_rows);
+void launch_bwd_epilogue(const OptInputs& in, bool bf16, int64_t T, int H, int K,
+                         uint32_t options, float* grad_q, float* grad_k, const float* dg,
+                         float* grad_g, float* grad_beta, hipStream_t st);
+
 // Chunked forward at 256 key channels (kda_wide.hip): fp32 records for every chunk at once.
 struct WidePlan {
   int64_t ub;  // upper bound of the number of chunks over all sequences
@@ -61,6 +81,7 @@ struct BwdPlan {
   int64_t ub;    // upper bound of the number of chunks over all sequences
   int64_t seg;   // chunks per segment
   int64_t nseg;  // segments (at least one)
+  size_t off_opt_q, off_opt_k, off_opt_g, off_opt_b, off_opt_dg;  // input options only
   size_t off_seq, off_chunks, off_ck, off_rec, off_ckS, off_ckX, off_D, off_dD, off_scr,
       total_bytes;
 };
@@ -68,10 +89,10 @@ struct BwdPlan {
 constexpr size_t BWD_SEGMENT_BYTES = (size_t)4 << 30;
 // seg_chunks <= 0 (or >= the chunk count): one segment
 bool make_bwd_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv,
-                   int64_t seg_chunks, BwdPlan* p);
+                   uint32_t options, int64_t seg_chunks, BwdPlan* p);
 // The plan with the longest segments whose workspace fits in `bytes` (false if none does).
-bool fit_bwd_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv, size_t bytes,
-                  BwdPlan* p);
+bool fit_bwd_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv,
+                  uint32_t options, size_t bytes, BwdPlan* p);
 // Chunks per segment of the default plan.
 int64_t default_bwd_segment(int num_heads, int dk, int dv);
 
@@ -86,6 +107,7 @@ struct BwdArgs {
   const void* dO;
   const float* dfinal;
   float *grad_q, *grad_k, *grad_v, *grad_g, *grad_beta, *grad_init;
+  uint32_t options;  // KDA_OPT_* bits
   void* workspace;
   void* stream;
 };

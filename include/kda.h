@@ -197,7 +197,8 @@ kda_status kda_chunk_fwd_scan(const void* q, const void* k, const void* v, const
                               void* stream);
 
 /*
- * Training backward of kda_chunk_fwd (options = 0): the gradients of
+ * Training backward of kda_chunk_fwd (options = 0; kda_chunk_bwd_ex below takes input options):
+ * the gradients of
  *     L = sum(d_o * o) + sum(d_final_state * final_state)
  * with respect to q, k, v, log_alpha, beta and init_state, for the forward on the same inputs
  * (same q, k, v, log_alpha, beta, init_state, cu_seqlens and shapes), by reverse mode through
@@ -227,16 +228,17 @@ kda_status kda_chunk_fwd_scan(const void* q, const void* k, const void* v, const
  * second pass. kda_chunk_bwd takes the longest segments that workspace_bytes holds (one segment,
  * no second pass, when it holds every chunk) and returns KDA_ERROR_WORKSPACE_TOO_SMALL when not
  * even one chunk per segment fits. The gradients do not depend on the segment length.
- *   kda_chunk_bwd_workspace_size    : the default, segments of about 4 GiB
- *   kda_chunk_bwd_workspace_size_ex : segments of segment_tokens tokens (rounded up to 64;
- *                                     <= 0: one segment over every chunk)
- * Both return 0 for shapes the backward does not support.
+ *   kda_chunk_bwd_workspace_size    : the default, segments of about 4 GiB, no input options
+ *   kda_chunk_bwd_workspace_size_ex : for kda_chunk_bwd_ex with these options, segments of
+ *                                     segment_tokens tokens (rounded up to 64; 0: one segment
+ *                                     over every chunk; < 0: the default segments)
+ * Both return 0 for shapes (or option bits) the backward does not support.
  */
 size_t kda_chunk_bwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                                     int32_t dk, int32_t dv, kda_dtype dtype);
 size_t kda_chunk_bwd_workspace_size_ex(int32_t num_seqs, int64_t total_tokens,
                                        int32_t num_heads, int32_t dk, int32_t dv,
-                                       kda_dtype dtype, int64_t segment_tokens);
+                                       kda_dtype dtype, uint32_t options, int64_t segment_tokens);
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* beta, const float* init_state, const int32_t* cu_seqlens,
                          int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t dk,
@@ -244,6 +246,24 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
                          const float* d_final_state, float* grad_q, float* grad_k, float* grad_v,
                          float* grad_log_alpha, float* grad_beta, float* grad_init_state,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_bwd for kda_chunk_fwd_ex with input options (KDA_OPT_*; options = 0 is
+ * kda_chunk_bwd): the gradients are those of the raw inputs, through the options' prologue
+ * (unit-norm q and k, log alpha = log sigmoid(z), one gate per head, beta = sigmoid(x)). With
+ * KDA_OPT_SCALAR_GATE, log_alpha and grad_log_alpha are [rows][H] and need only their element
+ * alignment. The workspace (kda_chunk_bwd_workspace_size_ex with the same options) also holds
+ * the processed q, k, log alpha and beta in fp32 for every token (and, with the scalar gate,
+ * the per-channel gradient of log alpha): about 12 K + 4 bytes per token and head more.
+ */
+kda_status kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                            const void* beta, const float* init_state, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                            int32_t dk, int32_t dv, kda_dtype dtype, uint32_t options,
+                            const void* d_o, const float* d_final_state, float* grad_q,
+                            float* grad_k, float* grad_v, float* grad_log_alpha,
+                            float* grad_beta, float* grad_init_state, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * One recurrent KDA token step per (sequence, head), state updated in place (decode).

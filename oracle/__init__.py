@@ -229,3 +229,33 @@ def kda_bwd(q, k, v, log_alpha, beta, dout, dfinal=None, cu_seqlens=None, init_s
     if rc != 0:
         raise RuntimeError("kda_oracle_bwd failed (%d)" % rc)
     return dq, dk, dv, dg, db, dinit
+
+
+def kda_bwd_options(q, k, v, gate, beta, dout, options: int, dfinal=None, cu_seqlens=None,
+                    init_state=None, threads: int = 0):
+    """Gradients with respect to the raw inputs of kda_fwd on apply_options(q, k, gate, beta),
+    fp64: kda_bwd on the processed inputs, then the chain rule through each option.
+
+    gate is [T, H, K], or [T, H] with OPT_SCALAR_GATE (and so is its gradient). The options'
+    derivatives: unit norm y = x r, r = (|x|^2 + eps)^{-1/2}, gives dx = r dy - r^3 x (x . dy);
+    log alpha = log sigmoid(z) gives dz = dlog_alpha sigmoid(-z); one gate per head sums the
+    channels' gradients; beta = sigmoid(x) gives dx = dbeta sigmoid(x) sigmoid(-x).
+    Returns (dq, dk, dv, dgate, dbeta, dinit_state).
+    """
+    q0, k0, z0, b0 = _f64(q), _f64(k), _f64(gate), _f64(beta)
+    qp, kp, gp, bp = apply_options(q0, k0, z0, b0, options)
+    dq, dk, dv, dg, db, dinit = kda_bwd(qp, kp, v, gp, bp, dout, dfinal=dfinal,
+                                        cu_seqlens=cu_seqlens, init_state=init_state,
+                                        threads=threads)
+    if options & OPT_L2NORM_QK:
+        def back(x, dy):
+            r = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + L2NORM_EPS)
+            return r * dy - r ** 3 * x * np.sum(x * dy, axis=-1, keepdims=True)
+        dq, dk = back(q0, dq), back(k0, dk)
+    if options & OPT_SCALAR_GATE:
+        dg = np.sum(dg, axis=-1)
+    if options & OPT_GATE_LOGITS:
+        dg = dg * sigmoid(-z0)
+    if options & OPT_BETA_LOGITS:
+        db = db * sigmoid(b0) * sigmoid(-b0)
+    return dq, dk, dv, dg, db, dinit

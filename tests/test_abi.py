@@ -21,7 +21,7 @@ def test_every_declared_symbol_is_exported():
                           "kda_chunk_fwd_noalloc",
                           "kda_chunk_fwd_scan", "kda_chunk_fwd_scan_workspace_size",
                           "kda_chunk_bwd", "kda_chunk_bwd_workspace_size",
-                          "kda_chunk_bwd_workspace_size_ex",
+                          "kda_chunk_bwd_workspace_size_ex", "kda_chunk_bwd_ex",
                           "kda_decode_step", "kda_decode_step_ex", "kda_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -278,11 +278,12 @@ def test_bwd_workspace_size():
 def test_bwd_workspace_is_bounded():
     L = kda.lib()
     ws = lambda *a: int(L.kda_chunk_bwd_workspace_size(*a))
-    ex = lambda *a: int(L.kda_chunk_bwd_workspace_size_ex(*a))
+    ex = lambda *a, opts=0: int(L.kda_chunk_bwd_workspace_size_ex(*a[:6], opts, a[6]))
     # default: segments of about 4 GiB, so past one segment only the per-boundary states
     # (H K V fp32 each) and the chunk table grow with T
     a, b = ws(1, 1 << 20, 32, 128, 128, 1), ws(1, 1 << 21, 32, 128, 128, 1)
     assert a < 5 << 30 and b - a < 700 << 20
+    assert ex(1, 1 << 20, 32, 128, 128, 1, -1) == a  # < 0: the default segments
     # one segment over every chunk: about 500 KB per 64 tokens and head
     one = ex(1, 65536, 32, 128, 128, 1, 0)
     assert 15 << 30 < one < 17 << 30
@@ -294,7 +295,43 @@ def test_bwd_workspace_is_bounded():
     assert ex(1, 65536, 32, 128, 128, 1, 192) < 0.4 * small
     assert ex(1, 65536, 32, 128, 128, 1, 1) == small  # rounded up to whole chunks
     assert ex(1, 65536, 32, 128, 256, 1, 64) == 0
+    # input options add the processed q, k, log alpha (fp32) and beta for every token, and with
+    # the scalar gate the per-channel gradient of log alpha
+    T, H, K = 65536, 4, 128
+    extra = ex(1, T, H, K, 128, 1, 0, opts=kda.OPT_GATE_LOGITS) - ex(1, T, H, K, 128, 1, 0)
+    assert extra == 3 * T * H * K * 4 + T * H * 4
+    extra_sg = ex(1, T, H, K, 128, 1, 0, opts=kda.OPT_SCALAR_GATE) - ex(1, T, H, K, 128, 1, 0)
+    assert extra_sg == extra + T * H * K * 4
+    assert ex(1, T, H, K, 128, 1, 0, opts=16) == 0  # unknown option bit
 
+
+def _bwd_ex(L, opts, **kw):
+    a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, init=None, cu=None, N=1, T=128, H=2,
+             dk=32, dv=32, dtype=BF16, do=6 * A, dfin=None, gq=7 * A, gk=8 * A, gv=9 * A,
+             gg=10 * A, gb=11 * A, ginit=12 * A, ws=13 * A, wsb=1 << 40, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kda_chunk_bwd_ex(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]),
+                              vp(a["init"]), vp(a["cu"]), a["N"], a["T"], a["H"], a["dk"],
+                              a["dv"], a["dtype"], opts, vp(a["do"]), vp(a["dfin"]), vp(a["gq"]),
+                              vp(a["gk"]), vp(a["gv"]), vp(a["gg"]), vp(a["gb"]), vp(a["ginit"]),
+                              vp(a["ws"]), a["wsb"], vp(a["stream"]))
+
+
+@pytest.mark.parametrize("opts,kw,expect", [
+    (16, {}, NOT_SUPPORTED),                             # unknown option bit
+    (1 << 31, {}, NOT_SUPPORTED),
+    (2, dict(g=4 * A + 2), INVALID),                     # a per-channel gate is 16-byte aligned
+    (1, dict(g=4 * A + 2), WS_SMALL),                    # a scalar gate only element-aligned
+    (1, dict(g=4 * A + 1), INVALID),
+    (1, dict(gg=10 * A + 4, wsb=4096), WS_SMALL),        # its gradient 4-byte aligned
+    (1, dict(gg=10 * A + 2), INVALID),
+    (2, dict(gg=4 * A), INVALID),                        # a gradient over the gate input
+    (15, dict(wsb=4096), WS_SMALL),
+])
+def test_chunk_bwd_ex_argument_errors(opts, kw, expect):
+    kw.setdefault("wsb", 4096 if expect == WS_SMALL else 1 << 40)
+    assert _bwd_ex(kda.lib(), opts, **kw) == expect
 
 def test_wide_key_workspace_size():
     import torch

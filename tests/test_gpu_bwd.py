@@ -200,3 +200,59 @@ def test_bwd_long_prefill_sampled_head():
         err = rel_err(g, want)
         print("  %-10s rel err %.2e" % (name, err), flush=True)
         assert np.all(np.isfinite(g)) and err <= TOL, "%s: %.3e" % (name, err)
+
+
+SG, GL, BL, L2 = kda.OPT_SCALAR_GATE, kda.OPT_GATE_LOGITS, kda.OPT_BETA_LOGITS, kda.OPT_L2NORM_QK
+
+
+@pytest.mark.parametrize("opts,dtype,K,V,gates", [
+    (GL, torch.bfloat16, 128, 128, (2.0, 7.0)),
+    (GL, torch.bfloat16, 64, 64, (-12.0, -6.0)),   # strong decays through the gate logits (*)
+    (SG, torch.bfloat16, 128, 64, None),
+    (SG | GL, torch.float32, 64, 64, (-3.0, 5.0)),
+    (BL | L2, torch.bfloat16, 128, 128, None),
+    (SG | GL | BL | L2, torch.float32, 32, 32, (-2.0, 6.0)),
+    (GL | BL | L2, torch.bfloat16, 128, 128, (0.0, 6.0)),
+])
+def test_bwd_options_against_oracle(opts, dtype, K, V, gates):
+    """kda_chunk_bwd_ex: gradients with respect to the raw inputs (gate logits, one gate per
+    head, beta logits, q/k before normalisation) against the oracle's chain rule through the
+    same options (pinned to central differences), varlen with an empty sequence; one run with
+    segments of two chunks.
+
+    (*) With every channel decaying by e^-6 .. e^-12 per token, a chunk's cumulative log2 decay
+    reaches 64 * 12 * log2(e) ~ 1100, where an fp32 ulp is 1.2e-4: each in-chunk factor
+    2^{b_i - b_j} then carries a relative error up to about that, so those gradients are held
+    to 5e-4 (the others to 1e-4)."""
+    print("bwd options", opts, dtype, K, V, flush=True)
+    tol = 5e-4 if gates is not None and gates[1] <= -6.0 else TOL
+    lens = [70, 0, 230, 33, 64]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    T, H, N = int(cu[-1]), 2, len(lens)
+    kw = {} if gates is None else dict(gate_logit_range=gates)
+    inp = workloads.gen_raw(T, H, K, V, opts, dtype=dtype, device=DEV, seed=opts * 7 + K,
+                            num_seqs=N, init_std=0.1, **kw)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(opts + 3)
+    d_o = torch.randn((T, H, V), generator=gen, device=DEV).to(dtype)
+    dfin = torch.randn((N, H, K, V), generator=gen, device=DEV)
+    ref = oracle.kda_bwd_options(*(np64(inp[x]) for x in ORDER), np64(d_o), opts,
+                                 dfinal=np64(dfin), cu_seqlens=cu.cpu().numpy().astype(np.int64),
+                                 init_state=np64(inp["init_state"]))
+    one = None
+    for seg in (None, 128):
+        grads = kda.chunk_bwd(*(inp[x] for x in ORDER), d_o, init_state=inp["init_state"],
+                              d_final_state=dfin, cu_seqlens=cu, num_seqs=N, options=opts,
+                              segment_tokens=seg)
+        for name, got, want in zip(NAMES, grads, ref):
+            g = np64(got)
+            assert g.shape == want.shape, name
+            assert np.all(np.isfinite(g)), name
+            err = rel_err(g, want)
+            print("  %-10s seg %s rel err %.2e" % (name, seg, err))
+            assert err <= tol, "%s: %.3e > %.1e" % (name, err, tol)
+        if one is None:
+            one = grads
+        else:
+            for name, a, b in zip(NAMES, one, grads):
+                assert torch.equal(a, b), name

@@ -73,3 +73,55 @@ def test_zero_beta_closed_forms():
     fin_term = A[-1] * np.sum(S0[0, 0] * dfin[0, 0], axis=1)
     ref_dg = np.cumsum(term[::-1], axis=0)[::-1] + fin_term[None, :]
     np.testing.assert_allclose(dg[:, 0], ref_dg, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("options", [
+    oracle.OPT_L2NORM_QK | oracle.OPT_GATE_LOGITS | oracle.OPT_BETA_LOGITS,
+    oracle.OPT_SCALAR_GATE | oracle.OPT_GATE_LOGITS,
+    oracle.OPT_SCALAR_GATE | oracle.OPT_L2NORM_QK,
+])
+def test_option_gradients_match_central_differences(options):
+    """kda_bwd_options (the chain rule through the input options) against central differences
+    of the forward oracle run on apply_options of the raw inputs, for q, k, the gate and beta."""
+    rng = np.random.default_rng(options)
+    lengths, H, K, V = [5, 0, 4], 1, 3, 2
+    T, N = sum(lengths), len(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q = rng.standard_normal((T, H, K))
+    k = rng.standard_normal((T, H, K))
+    v = rng.standard_normal((T, H, V))
+    gshape = (T, H) if options & oracle.OPT_SCALAR_GATE else (T, H, K)
+    z = rng.uniform(-2.0, 3.0, gshape) if options & oracle.OPT_GATE_LOGITS else \
+        np.log(rng.uniform(0.4, 1.0, gshape))
+    b = rng.uniform(-2.0, 2.0, (T, H)) if options & oracle.OPT_BETA_LOGITS else \
+        rng.uniform(0.05, 1.0, (T, H))
+    S0 = rng.standard_normal((N, H, K, V))
+    do = rng.standard_normal((T, H, V))
+    dfin = rng.standard_normal((N, H, K, V))
+    grads = oracle.kda_bwd_options(q, k, v, z, b, do, options, dfinal=dfin, cu_seqlens=cu,
+                                   init_state=S0)
+    args = [q, k, v, z, b]
+
+    def loss():
+        qp, kp, gp, bp = oracle.apply_options(q, k, z, b, options)
+        o, fin = oracle.kda_fwd(qp, kp, v, gp, bp, cu_seqlens=cu, init_state=S0)
+        return float(np.sum(o * do) + np.sum(fin * dfin))
+
+    h = 1e-6
+    for which in (0, 1, 3, 4):
+        x = args[which]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            keep = x[idx]
+            x[idx] = keep + h
+            lp = loss()
+            x[idx] = keep - h
+            lm = loss()
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        scale = max(1.0, float(np.abs(fd).max()))
+        assert grads[which].shape == x.shape
+        np.testing.assert_allclose(grads[which], fd, rtol=0, atol=1e-7 * scale,
+                                   err_msg="gradient %d" % which)
