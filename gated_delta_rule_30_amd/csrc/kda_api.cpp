@@ -84,7 +84,6 @@ kda_status kda::prepare_chunk_fwd(const void* q, const void* k, const void* v,
   kda_status st = check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_SUCCESS) return st;
   if (options & ~kAllOptions) return KDA_ERROR_NOT_SUPPORTED;
-  if (wide_path(dk, dtype) && options != 0) return KDA_ERROR_NOT_SUPPORTED;  // the wide-key path: plain inputs
   const int32_t gdim = (options & KDA_OPT_SCALAR_GATE) ? 1 : dk;  // gate values per token and head
   if (cu_seqlens == nullptr && total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
   if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERROR_INVALID_VALUE;

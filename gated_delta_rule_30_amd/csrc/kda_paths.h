@@ -63,11 +63,18 @@ void launch_bwd_epilogue(const OptInputs& in, bool bf16, int64_t T, int H, int K
                          uint32_t options, float* grad_q, float* grad_k, const float* dg,
                          float* grad_g, float* grad_beta, hipStream_t st);
 
-// Chunked forward at 256 key channels (kda_wide.hip): fp32 records for every chunk at once.
+// Chunked forward at 256 key channels (kda_wide.hip): fp32 records for one segment of chunks
+// at a time (segments run in order, the state carried between them), and the input-option
+// pass's output for one segment's tokens.
 struct WidePlan {
-  int64_t ub;  // upper bound of the number of chunks over all sequences
-  size_t off_seq, off_rows, off_rec, total_bytes;
+  int64_t ub;    // upper bound of the number of chunks over all sequences
+  int64_t seg;   // chunks per segment
+  int64_t nseg;  // segments (at least one)
+  size_t off_seq, off_rows, off_rec, off_opt_q, off_opt_k, off_opt_g, off_opt_b, off_run,
+      total_bytes;
 };
+// Record bytes per segment.
+constexpr size_t WIDE_SEGMENT_BYTES = (size_t)512 << 20;
 bool make_wide_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv,
                     WidePlan* p);
 hipError_t launch_chunk_fwd_wide(const ChunkArgs& a, const WidePlan& p);

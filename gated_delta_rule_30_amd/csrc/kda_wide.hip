@@ -40,11 +40,15 @@ struct WRec {
 
 }  // namespace
 
-template <int KW, int V, typename MT>
+// The chunks [cb, ...) of one segment, records indexed from cb. MT: v; GT: q, k, log alpha and
+// beta, at the call's token positions, or (local) from the first token of chunk cb on (the
+// fp32 output of the input-option pass over the segment's tokens).
+template <int KW, int V, typename MT, typename GT>
 __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
-    const MT* __restrict__ q, const MT* __restrict__ k, const MT* __restrict__ v,
-    const MT* __restrict__ g, const MT* __restrict__ beta, int H,
-    const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, float* __restrict__ rec) {
+    const GT* __restrict__ q, const GT* __restrict__ k, const MT* __restrict__ v,
+    const GT* __restrict__ g, const GT* __restrict__ beta, int H,
+    const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, int cb, bool local,
+    float* __restrict__ rec) {
   using R = WRec<KW, V>;
   constexpr int LK = KQ + 4;                 // rows of a channel quarter
   constexpr int VH = V > KQ ? KQ : V, LV = VH + 4;
@@ -55,12 +59,13 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
   __shared__ __align__(16) float sA[BC * 68];  // A (strict lower), then T = (I + A)^{-1}
   float* sT = sA;
   __shared__ float sBeta[BC];
-  const int c = blockIdx.x, h = blockIdx.y;
+  const int lc = blockIdx.x, c = cb + lc, h = blockIdx.y;  // chunk of the segment, of the call
   if (c >= *ntot) return;
   const ChunkRow ch = chunks[c];
-  float* rc = rec + ((size_t)c * H + h) * R::floats;
+  const int64_t gtok = local ? (int64_t)ch.tok - chunks[cb].tok : ch.tok;  // q, k, g, beta row
+  float* rc = rec + ((size_t)lc * H + h) * R::floats;
   if (threadIdx.x < BC)
-    sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
+    sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(gtok + threadIdx.x) * (int64_t)H + h]) : 0.f;
   // A and P, summed over the four quarters: rows pi and 63 - pi form a pair with 65 entries j <= i;
   // TPP threads share a pair, thread jq taking v = jq + TPP u (v <= pi: row pi, j = v; else
   // row 63 - pi, j = v - pi - 1), so every thread has the same work
@@ -71,9 +76,9 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
   for (int u = 0; u < VPT; ++u) a[u] = p[u] = 0.f;
   for (int hh = 0; hh < KW / KQ; ++hh) {
     const int c0 = hh * KQ;
-    load_rows<KQ, LK, NTP, MT, KW>(sQ, q, ch.tok, ch.len, H, h, c0);
-    load_rows<KQ, LK, NTP, MT, KW>(sK, k, ch.tok, ch.len, H, h, c0);
-    load_rows<KQ, LK, NTP, MT, KW>(sB, g, ch.tok, ch.len, H, h, c0);
+    load_rows<KQ, LK, NTP, GT, KW>(sQ, q, gtok, ch.len, H, h, c0);
+    load_rows<KQ, LK, NTP, GT, KW>(sK, k, gtok, ch.len, H, h, c0);
+    load_rows<KQ, LK, NTP, GT, KW>(sB, g, gtok, ch.len, H, h, c0);
     lds_barrier();
     cumsum_log2<KQ, LK, NTP>(sB);
     lds_barrier();
@@ -144,11 +149,11 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
   // W = T diag(beta) (k e^b), quarter by quarter
   for (int hh = 0; hh < KW / KQ; ++hh) {
     const int c0 = hh * KQ;
-    load_rows<KQ, LK, NTP, MT, KW>(sB, g, ch.tok, ch.len, H, h, c0);
+    load_rows<KQ, LK, NTP, GT, KW>(sB, g, gtok, ch.len, H, h, c0);
     lds_barrier();
     cumsum_log2<KQ, LK, NTP>(sB);
     lds_barrier();
-    mul_rows_exp2<KQ, LK, NTP, MT, KW>(sB, k, ch.tok, ch.len, H, h, c0);
+    mul_rows_exp2<KQ, LK, NTP, GT, KW>(sB, k, gtok, ch.len, H, h, c0);
     lds_barrier();
     for (int e = threadIdx.x; e < BC * KQ; e += NTP) sB[(e / KQ) * LK + e % KQ] *= sBeta[e / KQ];
     lds_barrier();
@@ -176,11 +181,15 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
 // S' = diag(gamma) S + Kt^T Delta (wave w: 16-row tiles w, w + 4, ..), each staged A operand
 // read once for the CW / 16 column blocks. The next block's loads are issued before the
 // current block's products. CW = 32 at V = 256 keeps the chains to one wave of workgroups.
+// The chunks [cb, ce) of one segment (records indexed from cb): a sequence that began before
+// the segment starts from its state in `run`, and one that goes on past it leaves its state
+// there (run may be fin); empty sequences (final state = initial state) belong to the segment
+// at chunk 0.
 template <int KW, int V, int CW, typename MT>
 __global__ __launch_bounds__(NT) void wide_state_kernel(
     const float* __restrict__ rec, const float* __restrict__ init, const int32_t* __restrict__ cu,
-    int64_t T, const int32_t* __restrict__ seq_first, int N, int H, int chains8, MT* __restrict__ o,
-    float* __restrict__ fin) {
+    int64_t T, const int32_t* __restrict__ seq_first, int N, int H, int chains8, int cb, int ce,
+    float* run, MT* __restrict__ o, float* fin) {
   using R = WRec<KW, V>;
   static_assert(KW <= NT && KW % 64 == 0, "one thread per key channel for gamma");
   constexpr int NCB = CW / 16;           // 16-column blocks per workgroup
@@ -199,9 +208,13 @@ __global__ __launch_bounds__(NT) void wide_state_kernel(
   if (nh >= N * H) return;
   const int n = nh / H, h = nh % H, c0 = CW * s;
   const int tid = threadIdx.x, w = tid >> 6, lm = tid & 15, lg = (tid >> 4) & 3;
+  const int sfirst = seq_first[n], slast = seq_first[n + 1];
+  const int first = max(sfirst, cb), last = min(slast, ce);  // the sequence's chunks here
+  if (sfirst < slast ? first >= last : cb != 0) return;
+  const size_t sb = (size_t)nh * KW * V;
+  const float* src = sfirst < cb ? run + sb : (init ? init + sb : nullptr);
   for (int e = tid; e < KW * CW; e += NT)
-    sS[(e / CW) * LS + e % CW] = init ? init[((size_t)nh * KW + e / CW) * V + c0 + e % CW] : 0.f;
-  const int first = seq_first[n], last = seq_first[n + 1];
+    sS[(e / CW) * LS + e % CW] = src ? src[(e / CW) * V + c0 + e % CW] : 0.f;
   int64_t s0, s1;
   seq_range(cu, N, T, n, &s0, &s1);
   f32x4 rb[PB];
@@ -230,10 +243,10 @@ __global__ __launch_bounds__(NT) void wide_state_kernel(
       for (int r = 0; r < 4; ++r) d[cb][r] = rc[R::oU + (16 * w + 4 * lg + r) * V + c0 + 16 * cb + lm];
     rg = tid < KW ? rc[R::oGam + tid] : 0.f;
   };
-  if (first < last) fetch_head(rec + ((size_t)first * H + h) * R::floats);
+  if (first < last) fetch_head(rec + ((size_t)(first - cb) * H + h) * R::floats);
   for (int c = first; c < last; ++c) {
-    const float* rc = rec + ((size_t)c * H + h) * R::floats;
-    const int64_t tok = s0 + (int64_t)(c - first) * BC;
+    const float* rc = rec + ((size_t)(c - cb) * H + h) * R::floats;
+    const int64_t tok = s0 + (int64_t)(c - sfirst) * BC;
     const int len = (int)min((int64_t)BC, s1 - tok);
     lds_barrier();  // the previous chunk's reads of LDS are done
     stage(LR);
@@ -285,7 +298,7 @@ __global__ __launch_bounds__(NT) void wide_state_kernel(
       }
     lds_barrier();  // Qe no longer read
     stage(LC);
-    fetch_head(rec + ((size_t)(c + 1 < last ? c + 1 : c) * H + h) * R::floats);
+    fetch_head(rec + ((size_t)((c + 1 < last ? c + 1 : c) - cb) * H + h) * R::floats);
     lds_barrier();
     // S' tiles: diag(gamma) S + Kt^T Delta
     f32x4 sn[TPW][NCB];
@@ -317,71 +330,109 @@ __global__ __launch_bounds__(NT) void wide_state_kernel(
         for (int r = 0; r < 4; ++r) sS[(16 * mt + 4 * lg + r) * LS + 16 * cb + lm] = sn[qq][cb][r];
     }
   }
-  if (fin) {
+  float* dst = (sfirst < slast && slast > ce) ? run + sb : (fin ? fin + sb : nullptr);
+  if (dst) {
     __syncthreads();
-    for (int e = tid; e < KW * CW; e += NT)
-      fin[((size_t)nh * KW + e / CW) * V + c0 + e % CW] = sS[(e / CW) * LS + e % CW];
+    for (int e = tid; e < KW * CW; e += NT) dst[(e / CW) * V + c0 + e % CW] = sS[(e / CW) * LS + e % CW];
   }
 }
 
 // ---------------------------------------------------------------- host
 static size_t al256w(size_t x) { return (x + 255) / 256 * 256; }
 
-bool make_wide_plan(int N, int64_t T, int H, int K, int V, WidePlan* p) {
-  if (N <= 0 || H <= 0 || T < 0) return false;
-  size_t rec_floats = 0;
+// fp32 values of one (chunk, head) record (0 for unsupported head dims)
+static size_t wide_rec_floats(int K, int V) {
 #define KDA_WREC(KK, VV) \
-  if (K == KK && V == VV) rec_floats = WRec<KK, VV>::floats;
+  if (K == KK && V == VV) return WRec<KK, VV>::floats;
   KDA_WREC(128, 32) KDA_WREC(128, 64) KDA_WREC(128, 128) KDA_WREC(128, 256)
   KDA_WREC(256, 32) KDA_WREC(256, 64) KDA_WREC(256, 128) KDA_WREC(256, 256)
 #undef KDA_WREC
+  return 0;
+}
+
+bool make_wide_plan(int N, int64_t T, int H, int K, int V, WidePlan* p) {
+  if (N <= 0 || H <= 0 || T < 0) return false;
+  const size_t rec_floats = wide_rec_floats(K, V);
   if (rec_floats == 0) return false;
   int64_t ub = (T + (int64_t)N * (BC - 1)) / BC;
   if (ub > T) ub = T;
   p->ub = ub;
+  // segments of at most WIDE_SEGMENT_BYTES of records
+  int64_t e = (int64_t)(WIDE_SEGMENT_BYTES / ((size_t)H * rec_floats * 4));
+  if (e < 1) e = 1;
+  p->seg = ub > 0 && e > ub ? ub : e;
+  p->nseg = ub > 0 ? (ub + p->seg - 1) / p->seg : 1;
+  if (ub >= (1LL << 31)) return false;
   size_t off = 0;
   p->off_seq = off;
   off += al256w((size_t)(N + 1) * 4);
   p->off_rows = off;
   off += al256w((size_t)ub * sizeof(ChunkRow));
   p->off_rec = off;
-  off += al256w((size_t)ub * H * rec_floats * 4);
+  off += al256w((size_t)p->seg * H * rec_floats * 4);
+  // the input-option pass over one segment's tokens: q, k, log alpha, beta in fp32
+  const size_t tk = al256w((size_t)p->seg * BC * H * K * 4);
+  p->off_opt_q = off;
+  p->off_opt_k = off + tk;
+  p->off_opt_g = off + 2 * tk;
+  p->off_opt_b = off + 3 * tk;
+  off += 3 * tk + al256w((size_t)p->seg * BC * H * 4);
+  // the running state between segments when the caller keeps no final state
+  p->off_run = off;
+  if (p->nseg > 1) off += al256w((size_t)N * H * K * V * 4);
   p->total_bytes = off;
   return true;
 }
 
-template <int K, int V, typename MT>
+template <int K, int V, typename MT, typename GT>
 static hipError_t launch_wide_t(const ChunkArgs& a, const WidePlan& p) {
   hipStream_t st = (hipStream_t)a.stream;
   char* ws = reinterpret_cast<char*>(a.workspace);
   int32_t* seq_first = reinterpret_cast<int32_t*>(ws + p.off_seq);
   ChunkRow* rows = reinterpret_cast<ChunkRow*>(ws + p.off_rows);
   float* rec = reinterpret_cast<float*>(ws + p.off_rec);
+  float* run = a.final_state ? a.final_state : reinterpret_cast<float*>(ws + p.off_run);
   const int N = a.num_seqs, H = a.num_heads;
+  const int32_t* ntot = seq_first + N;
   hipError_t e = launch_chunk_rows(a.cu_seqlens, N, a.total_tokens, p.ub, seq_first, rows, st);
   if (e != hipSuccess) return e;
-  if (p.ub > 0)
-    hipLaunchKernelGGL((wide_prep_kernel<K, V, MT>), dim3((unsigned)p.ub, (unsigned)H), dim3(NTP), 0,
-                       st, (const MT*)a.q, (const MT*)a.k, (const MT*)a.v, (const MT*)a.g,
-                       (const MT*)a.beta, H, (const ChunkRow*)rows, (const int32_t*)(seq_first + N),
-                       rec);
+  const bool opts = a.options != 0;
+  const OptBuffers ob{reinterpret_cast<float*>(ws + p.off_opt_q), reinterpret_cast<float*>(ws + p.off_opt_k),
+                      reinterpret_cast<float*>(ws + p.off_opt_g), reinterpret_cast<float*>(ws + p.off_opt_b)};
+  const GT *q = opts ? (const GT*)ob.q : (const GT*)a.q, *k = opts ? (const GT*)ob.k : (const GT*)a.k,
+           *g = opts ? (const GT*)ob.g : (const GT*)a.g, *beta = opts ? (const GT*)ob.beta : (const GT*)a.beta;
   const int chains8 = (N * H + 7) / 8 * 8;
   constexpr int CW = V == 256 ? 32 : 16;  // value columns per chain workgroup
-  hipLaunchKernelGGL((wide_state_kernel<K, V, CW, MT>), dim3((unsigned)(chains8 * (V / CW))), dim3(NT),
-                     0, st, (const float*)rec, a.init_state, a.cu_seqlens, a.total_tokens,
-                     (const int32_t*)seq_first, N, H, chains8, (MT*)a.o, a.final_state);
+  for (int64_t s = 0; s < p.nseg; ++s) {
+    const int cb = (int)(s * p.seg), ce = (int)min((s + 1) * p.seg, p.ub);
+    if (ce > cb) {
+      if (opts)
+        launch_prologue(OptInputs{a.q, a.k, a.g, a.beta}, a.dtype_bf16, a.total_tokens, H, K,
+                        a.options, rows, ntot, cb, ce, ob, st, (int64_t)(ce - cb) * BC);
+      hipLaunchKernelGGL((wide_prep_kernel<K, V, MT, GT>), dim3((unsigned)(ce - cb), (unsigned)H),
+                         dim3(NTP), 0, st, q, k, (const MT*)a.v, g, beta, H, (const ChunkRow*)rows,
+                         ntot, cb, opts, rec);
+    }
+    hipLaunchKernelGGL((wide_state_kernel<K, V, CW, MT>), dim3((unsigned)(chains8 * (V / CW))),
+                       dim3(NT), 0, st, (const float*)rec, a.init_state, a.cu_seqlens,
+                       a.total_tokens, (const int32_t*)seq_first, N, H, chains8, cb, ce, run,
+                       (MT*)a.o, a.final_state);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_fwd_wide(const ChunkArgs& a, const WidePlan& p) {
-#define KDA_WIDE_CASE(KK, VV)                                                                  \
-  if (a.dk == KK && a.dv == VV)                                                                \
-    return a.dtype_bf16 ? launch_wide_t<KK, VV, bf16>(a, p) : launch_wide_t<KK, VV, float>(a, p);
+  const bool o = a.options != 0;
+#define KDA_WIDE_CASE(KK, VV)                                                               \
+  if (a.dk == KK && a.dv == VV)                                                             \
+    return a.dtype_bf16 ? (o ? launch_wide_t<KK, VV, bf16, float>(a, p)                     \
+                             : launch_wide_t<KK, VV, bf16, bf16>(a, p))                     \
+                        : launch_wide_t<KK, VV, float, float>(a, p);
   KDA_WIDE_CASE(256, 32) KDA_WIDE_CASE(256, 64) KDA_WIDE_CASE(256, 128) KDA_WIDE_CASE(256, 256)
 #undef KDA_WIDE_CASE
   // K = 128 comes here for fp32 inputs only (bf16 takes the chunk path)
 #define KDA_WIDE_CASE(VV) \
-  if (a.dk == 128 && a.dv == VV && !a.dtype_bf16) return launch_wide_t<128, VV, float>(a, p);
+  if (a.dk == 128 && a.dv == VV && !a.dtype_bf16) return launch_wide_t<128, VV, float, float>(a, p);
   KDA_WIDE_CASE(32) KDA_WIDE_CASE(64) KDA_WIDE_CASE(128) KDA_WIDE_CASE(256)
 #undef KDA_WIDE_CASE
   return hipErrorInvalidValue;

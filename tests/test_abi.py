@@ -89,7 +89,7 @@ def _chunk(L, **kw):
     (dict(T=-5), INVALID),
     (dict(T=1 << 31), INVALID),
     (dict(dk=48), NOT_SUPPORTED),
-    (dict(dk=256, opts=1), NOT_SUPPORTED),  # the wide-key path (K = 256) takes plain inputs
+    (dict(dk=256, opts=15, wsb=4096), WS_SMALL),  # the wide-key path (K = 256) takes options
     (dict(dk=256, wsb=4096), WS_SMALL),     # K = 256 is supported (the wide-key path)
     (dict(dk=512), NOT_SUPPORTED),
     (dict(dv=512), NOT_SUPPORTED),
@@ -98,7 +98,7 @@ def _chunk(L, **kw):
     (dict(opts=15, q=None), INVALID),
     (dict(opts=0, dk=48), NOT_SUPPORTED),
     (dict(dtype=7), NOT_SUPPORTED),
-    (dict(dtype=F32, dk=128, opts=1), NOT_SUPPORTED),   # fp32 at K = 128: the wide-key path, plain inputs
+    (dict(dtype=F32, dk=128, opts=1, wsb=4096), WS_SMALL),  # fp32 at K = 128: the wide-key path
     (dict(N=3, T=64), INVALID),            # equal lengths need T % N == 0
     (dict(q=None), INVALID),
     (dict(beta=None), INVALID),
@@ -336,9 +336,13 @@ def test_chunk_bwd_ex_argument_errors(opts, kw, expect):
 def test_wide_key_workspace_size():
     import torch
     ws = lambda *a: kda.workspace_size(*a)
-    # K = 256 takes the wide-key path: fp32 records for every chunk (linear in T * H)
-    a, b = ws(1, 65536, 4, 256, 128, torch.bfloat16), ws(1, 2 * 65536, 4, 256, 128, torch.bfloat16)
-    assert a > 0 and 1.9 < b / a < 2.1
+    # K = 256 takes the wide-key path: fp32 records for one segment of chunks at a time (512 MiB
+    # of records) and the option pass's output for its tokens, so past one segment only the
+    # chunk table and a running state grow with T
+    a, b = ws(1, 16384, 4, 256, 128, torch.bfloat16), ws(1, 32768, 4, 256, 128, torch.bfloat16)
+    assert a > 0 and 1.9 < b / a < 2.1                 # one segment each (256 and 512 chunks)
+    c, d = ws(1, 65536, 32, 256, 256, torch.bfloat16), ws(1, 1 << 20, 32, 256, 256, torch.bfloat16)
+    assert c < 1 << 30 and d - c < 8 << 20
     assert ws(1, 1000, 2, 256, 256, torch.float32) > 0
     assert ws(1, 1000, 2, 256, 512, torch.bfloat16) == 0
     # fp32 inputs at K = 128 take the same path; the scan (chunk path only) refuses them

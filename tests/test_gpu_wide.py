@@ -103,7 +103,55 @@ def test_wide_matches_recurrent_steps():
     assert float((fin - st).abs().max()) <= 1e-4 * float(st.abs().max())
 
 
-def test_wide_rejects_options():
-    inp = workloads.gen_forward(64, 1, 256, 64, dtype=torch.bfloat16, device=DEV, seed=13)
-    with pytest.raises(kda.KdaError):
-        kda.chunk_fwd(*(inp[x] for x in ORDER), options=kda.OPT_BETA_LOGITS)
+SG, GL, BL, L2 = kda.OPT_SCALAR_GATE, kda.OPT_GATE_LOGITS, kda.OPT_BETA_LOGITS, kda.OPT_L2NORM_QK
+
+
+@pytest.mark.parametrize("opts,dtype,K,V,gates", [
+    (SG, torch.bfloat16, 256, 64, None),
+    (GL, torch.bfloat16, 256, 256, None),
+    (GL, torch.float32, 256, 128, (-12.0, -6.0)),   # strong decays through the gate logits
+    (BL | L2, torch.bfloat16, 256, 128, None),
+    (SG | GL | BL | L2, torch.float32, 256, 32, None),
+    (SG | GL | BL | L2, torch.float32, 128, 128, None),  # fp32 at K = 128 takes this path too
+])
+def test_wide_options_ragged_varlen(opts, dtype, K, V, gates):
+    """The input options on the wide-key path (a pass that forms the processed q, k, log alpha
+    and beta for each segment's tokens) against the oracle running the same fp64 prologue."""
+    print("wide options", opts, dtype, K, V, flush=True)
+    lengths = [1, 63, 64, 65, 0, 127, 200]
+    cu = torch.tensor(workloads.cu_from_lengths(lengths), dtype=torch.int32, device=DEV)
+    T, H = sum(lengths), 2
+    kw = {} if gates is None else dict(gate_logit_range=gates)
+    inp = workloads.gen_raw(T, H, K, V, opts, dtype=dtype, device=DEV, seed=opts * 5 + V,
+                            num_seqs=len(lengths), init_std=0.1, **kw)
+    o, fin = kda.chunk_fwd(*(inp[x] for x in ORDER), init_state=inp["init_state"], cu_seqlens=cu,
+                           options=opts)
+    o_ref, f_ref = oracle_fwd(inp, cu=cu, options=opts)
+    assert_close(np64(o), o_ref, dtype, "o")
+    assert_close(np64(fin), f_ref, dtype, "final")
+
+
+@pytest.mark.parametrize("opts", [0, SG | GL | BL | L2])
+def test_wide_segments(opts):
+    """8192 tokens at H = 32, K = V = 256 (bf16): about 61 chunks per segment of records, so the
+    call runs three segments with sequences across their boundaries; two heads against the
+    oracle, and the same outputs bit for bit with the state updated in place or not kept."""
+    print("wide segments", opts, flush=True)
+    lengths = [3000, 0, 5000, 192]
+    cu = torch.tensor(workloads.cu_from_lengths(lengths), dtype=torch.int32, device=DEV)
+    T, H, K, V = sum(lengths), 32, 256, 256
+    assert kda.workspace_size(len(lengths), T, H, K, V, torch.bfloat16) < 1 << 30
+    inp = workloads.gen_raw(T, H, K, V, opts, dtype=torch.bfloat16, device=DEV, seed=31 + opts,
+                            num_seqs=len(lengths), init_std=0.1)
+    args = [inp[x] for x in ORDER]
+    o, fin = kda.chunk_fwd(*args, init_state=inp["init_state"], cu_seqlens=cu, options=opts)
+    heads = [3, 30]
+    o_ref, f_ref = oracle_fwd(inp, cu=cu, heads=heads, options=opts)
+    assert_close(np64(o[:, heads]), o_ref, torch.bfloat16, "o")
+    assert_close(np64(fin[:, heads]), f_ref, torch.bfloat16, "final")
+    st = inp["init_state"].clone()
+    o2, fin2 = kda.chunk_fwd(*args, init_state=st, final_state=st, cu_seqlens=cu, options=opts)
+    assert torch.equal(o2, o) and torch.equal(fin2, fin)
+    o3, none = kda.chunk_fwd(*args, init_state=inp["init_state"], cu_seqlens=cu, options=opts,
+                             output_final_state=False)
+    assert none is None and torch.equal(o3, o)
