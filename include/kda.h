@@ -23,7 +23,7 @@
  *    scale is applied and q, k are used as given (no normalisation inside). The _ex entry
  *    points take options that change how these inputs are read (KDA_OPT_* below).
  *  - Supported head dims: kda_chunk_fwd K in {32, 64, 128, 256}, V in {32, 64, 128, 256};
- *    K = 256, and fp32 inputs at K = 128, run the wide-key path below (no input options);
+ *    K = 256, and fp32 inputs at K = 128, run the wide-key path below;
  *    kda_decode_step K, V in {32, 64, 128, 256}. Other values give KDA_ERROR_NOT_SUPPORTED.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
  *    returns without waiting. Argument errors are reported synchronously before anything is
@@ -125,7 +125,10 @@ size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int3
  * Positive log_alpha values are accepted but lie outside this guarantee.
  * K = 256, and fp32 inputs at K = 128, run a separate path in fp32 (the chunk's products over
  * the key channels in parts of 64, every decay factor formed pairwise within the chunk, so any
- * decay is in range); it takes options = 0 only (other options give KDA_ERROR_NOT_SUPPORTED).
+ * decay is in range). It forms the chunks' records one segment of chunks at a time (512 MiB of
+ * records), so its workspace stays under about 1 GB at 32 heads whatever the length; with
+ * input options a separate pass forms the processed q, k, log alpha and beta of each segment's
+ * tokens in fp32 first.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* beta, const float* init_state, const int32_t* cu_seqlens,
