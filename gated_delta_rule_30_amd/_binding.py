@@ -66,6 +66,9 @@ def _lib():
         lib.kda_chunk_fwd_scan.restype = ctypes.c_int
         lib.kda_chunk_fwd_scan.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                            ctypes.c_int, u32, i32, vp, vp, vp, sz, vp]
+        lib.kda_chunk_fwd_scan_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                              ctypes.c_int, u32, i32, vp, vp, vp, sz, vp]
+        lib.kda_chunk_fwd_scan_ex.restype = ctypes.c_int
         lib.kda_chunk_bwd_workspace_size.restype = sz
         lib.kda_chunk_bwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
         lib.kda_chunk_bwd_workspace_size_ex.restype = sz
@@ -229,17 +232,25 @@ def chunk_fwd_noalloc(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None
     return o, final_state
 
 
-def chunk_fwd_scan(q, k, v, log_alpha, beta, init_state=None, num_seqs=1, num_groups=8,
-                   output_final_state=True, o=None, final_state=None, workspace=None, options=0):
-    """kda_chunk_fwd_scan on torch tensors: num_seqs equal-length sequences packed token-major
-    ([T, H, .]), each split into num_groups groups whose states are combined by a scan (see
-    include/kda.h). Returns (o, final_state) as chunk_fwd does."""
+def chunk_fwd_scan(q, k, v, log_alpha, beta, init_state=None, num_seqs=None, num_groups=8,
+                   output_final_state=True, o=None, final_state=None, workspace=None, options=0,
+                   cu_seqlens=None):
+    """kda_chunk_fwd_scan_ex on torch tensors: sequences packed token-major ([T, H, .]), equal
+    lengths (num_seqs of them, default 1) or given by cu_seqlens, each split into num_groups
+    groups whose states are combined by a scan (see include/kda.h). Returns (o, final_state) as
+    chunk_fwd does."""
     device = q.device
     T, H, K = q.shape
     V = v.shape[-1]
     dt = q.dtype
     code = _dtype_code(q)
-    N = int(num_seqs)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, device)
+        N = cu_seqlens.shape[0] - 1
+        if num_seqs is not None and num_seqs != N:
+            raise ValueError("num_seqs does not match cu_seqlens")
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
     gshape = (T, H) if options & OPT_SCALAR_GATE else (T, H, K)
     for name, t, shp in (("q", q, (T, H, K)), ("k", k, (T, H, K)), ("v", v, (T, H, V)),
                          ("log_alpha", log_alpha, gshape), ("beta", beta, (T, H))):
@@ -256,12 +267,13 @@ def chunk_fwd_scan(q, k, v, log_alpha, beta, init_state=None, num_seqs=1, num_gr
                        "kda_chunk_fwd_scan_workspace_size")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
-    st = _lib().kda_chunk_fwd_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                   _ptr(init_state), N, T, H, K, V, code, int(options),
-                                   int(num_groups), _ptr(o), _ptr(final_state), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(device))
+    st = _lib().kda_chunk_fwd_scan_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                      _ptr(init_state), _ptr(cu_seqlens), N, T, H, K, V, code,
+                                      int(options), int(num_groups), _ptr(o), _ptr(final_state),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(device))
     if st != 0:
-        raise KdaError(st, "kda_chunk_fwd_scan")
+        raise KdaError(st, "kda_chunk_fwd_scan_ex")
     return o, final_state
 
 

@@ -311,7 +311,7 @@ static kda_status check_scan_shape(int32_t num_seqs, int64_t total_tokens, int32
   if (st != KDA_SUCCESS) return st;
   // the first pass needs V + K columns (<= 256) and the chunk path (K <= 128; fp32 at K <= 64)
   if (dk != dv || wide_path(dk, dtype)) return KDA_ERROR_NOT_SUPPORTED;
-  if (num_groups <= 0 || total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
+  if (num_groups <= 0) return KDA_ERROR_INVALID_VALUE;
   return KDA_SUCCESS;
 }
 
@@ -327,15 +327,18 @@ extern "C" size_t kda_chunk_fwd_scan_workspace_size(int32_t num_seqs, int64_t to
   return sp.total_bytes;
 }
 
-extern "C" kda_status kda_chunk_fwd_scan(const void* q, const void* k, const void* v,
-                                         const void* log_alpha, const void* beta,
-                                         const float* init_state, int32_t num_seqs,
-                                         int64_t total_tokens, int32_t num_heads, int32_t dk,
-                                         int32_t dv, kda_dtype dtype, uint32_t options,
-                                         int32_t num_groups, void* o, float* final_state,
-                                         void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" kda_status kda_chunk_fwd_scan_ex(const void* q, const void* k, const void* v,
+                                            const void* log_alpha, const void* beta,
+                                            const float* init_state, const int32_t* cu_seqlens,
+                                            int32_t num_seqs, int64_t total_tokens,
+                                            int32_t num_heads, int32_t dk, int32_t dv,
+                                            kda_dtype dtype, uint32_t options, int32_t num_groups,
+                                            void* o, float* final_state, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
   kda_status st = check_scan_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype, num_groups);
   if (st != KDA_SUCCESS) return st;
+  if (cu_seqlens == nullptr && total_tokens % num_seqs != 0) return KDA_ERROR_INVALID_VALUE;
+  if (cu_seqlens && !aligned_to(cu_seqlens, 4)) return KDA_ERROR_INVALID_VALUE;
   if (options & ~kAllOptions) return KDA_ERROR_NOT_SUPPORTED;
   if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERROR_INVALID_VALUE;
   if (!workspace) return KDA_ERROR_INVALID_VALUE;
@@ -371,7 +374,7 @@ extern "C" kda_status kda_chunk_fwd_scan(const void* q, const void* k, const voi
   a.g = log_alpha;
   a.beta = beta;
   a.init_state = init_state;
-  a.cu_seqlens = nullptr;
+  a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
   a.total_tokens = total_tokens;
   a.num_heads = num_heads;
@@ -385,6 +388,18 @@ extern "C" kda_status kda_chunk_fwd_scan(const void* q, const void* k, const voi
   a.stream = stream;
   hipError_t e = kda::launch_chunk_fwd_scan(a, num_groups, sp);
   return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+}
+
+extern "C" kda_status kda_chunk_fwd_scan(const void* q, const void* k, const void* v,
+                                         const void* log_alpha, const void* beta,
+                                         const float* init_state, int32_t num_seqs,
+                                         int64_t total_tokens, int32_t num_heads, int32_t dk,
+                                         int32_t dv, kda_dtype dtype, uint32_t options,
+                                         int32_t num_groups, void* o, float* final_state,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  return kda_chunk_fwd_scan_ex(q, k, v, log_alpha, beta, init_state, nullptr, num_seqs,
+                               total_tokens, num_heads, dk, dv, dtype, options, num_groups, o,
+                               final_state, workspace, workspace_bytes, stream);
 }
 
 extern "C" kda_status kda_decode_step_ex(const void* q, const void* k, const void* v,

@@ -24,12 +24,22 @@
 
 namespace kda {
 
-// group g of sequence n: tokens [n L + min(g Lg, L), n L + min((g + 1) Lg, L))
-__global__ void scan_cu_kernel(int32_t* cu, int N, int G, int64_t L, int64_t Lg) {
+// group g of sequence n: tokens [s_n + min(g Lg_n, L_n), s_n + min((g + 1) Lg_n, L_n)), with
+// s_n, L_n the sequence's start and length (cu_in, or n L and L for equal lengths) and Lg_n
+// its length over G rounded up to whole chunks
+__global__ void scan_cu_kernel(int32_t* cu, const int32_t* __restrict__ cu_in, int N, int G,
+                               int64_t L) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i > (int64_t)N * G) return;
-  const int64_t n = i / G, g = i % G;
-  cu[i] = (int32_t)(n * L + min(g * Lg, L));
+  int64_t n = i / G, g = i % G;
+  if (n == N) {  // the end of the last sequence
+    n = N - 1;
+    g = G;
+  }
+  const int64_t s0 = cu_in ? cu_in[n] : n * L;
+  const int64_t len = cu_in ? cu_in[n + 1] - s0 : L;
+  const int64_t lg = ((len + G - 1) / G + CHUNK - 1) / CHUNK * CHUNK;
+  cu[i] = (int32_t)(s0 + min(g * lg, len));
 }
 
 // v' = [v | 0]: rows of V + K values, 16-byte pieces
@@ -164,10 +174,11 @@ __global__ void scan_final_kernel(const float* __restrict__ sin, float* __restri
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 bool make_scan_plan(int N, int64_t T, int H, int K, int V, bool bf16, int G, ScanPlan* sp) {
-  if (N <= 0 || G <= 0 || T < 0 || T % N != 0 || K != V || K > 128) return false;
+  if (N <= 0 || G <= 0 || T < 0 || K != V || K > 128) return false;
   const int64_t N1 = (int64_t)N * G;
   if (N1 > (1 << 30)) return false;
   const size_t es = bf16 ? 2 : 4;
+  // the sizes hold for any lengths: N G groups over T tokens (L: the equal-length split)
   const int64_t L = T / N;
   sp->L = L;
   sp->Lg = ((L + G - 1) / G + CHUNK - 1) / CHUNK * CHUNK;
@@ -211,8 +222,8 @@ hipError_t launch_chunk_fwd_scan(const ChunkArgs& a, int G, const ScanPlan& sp) 
   float* sin = reinterpret_cast<float*>(ws + sp.off_sin);
   float* dummy = reinterpret_cast<float*>(ws + sp.off_dummy);
   const int64_t cu_n = N1 + 1;
-  hipLaunchKernelGGL(scan_cu_kernel, dim3((unsigned)((cu_n + 255) / 256)), dim3(256), 0, st, cu, N,
-                     G, sp.L, sp.Lg);
+  hipLaunchKernelGGL(scan_cu_kernel, dim3((unsigned)((cu_n + 255) / 256)), dim3(256), 0, st, cu,
+                     a.cu_seqlens, N, G, sp.L);
   const unsigned fill_blocks = 1024;
   if (T > 0) {
     if (a.dtype_bf16)

@@ -173,8 +173,9 @@ kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
 
 /*
  * Chunk-parallel scan variant of kda_chunk_fwd_ex for long sequences over few heads. Each of the
- * num_seqs sequences (equal lengths total_tokens / num_seqs, no cu_seqlens) splits into
- * num_groups groups of whole 64-token chunks; one chunked pass over all groups with the values
+ * num_seqs sequences (equal lengths total_tokens / num_seqs; kda_chunk_fwd_scan_ex below takes
+ * cu_seqlens) splits into num_groups groups of whole 64-token chunks (its length over
+ * num_groups, rounded up to whole chunks, per group; trailing groups may be short or empty); one chunked pass over all groups with the values
  * [v | 0] and the initial state [0 | I] yields each group's end state from zero, B_g, and its
  * state transition, M_g (K x K); a combine forms every group's initial state
  * S_in(g + 1) = M_g S_in(g) + B_g; a second pass runs all groups from those states ("Kimi Linear"
@@ -184,7 +185,8 @@ kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
  * GPU's 256 CUs (e.g. one sequence of 64k tokens over 1 to 4 heads with num_groups = 16).
  * Requires dk == dv in {32, 64, 128}; other shapes give KDA_ERROR_NOT_SUPPORTED.
  * total_tokens must be divisible by num_seqs and num_groups >= 1 (else
- * KDA_ERROR_INVALID_VALUE). The workspace needs kda_chunk_fwd_scan_workspace_size bytes
+ * KDA_ERROR_INVALID_VALUE). The workspace needs kda_chunk_fwd_scan_workspace_size bytes (the
+ * same for any split of total_tokens into num_seqs sequences)
  * (it holds every (chunk, head) record of the first pass, about 100 KB per 64 tokens and head
  * at dk = dv = 128 bf16, plus [v | 0], a scratch output and the groups' states). Other
  * arguments as for kda_chunk_fwd_ex.
@@ -198,6 +200,20 @@ kda_status kda_chunk_fwd_scan(const void* q, const void* k, const void* v, const
                               kda_dtype dtype, uint32_t options, int32_t num_groups, void* o,
                               float* final_state, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * kda_chunk_fwd_scan over packed variable-length sequences: cu_seqlens ([num_seqs + 1] int32,
+ * device, 4-byte aligned, non-decreasing from 0 to total_tokens) gives each sequence's tokens,
+ * and each splits into num_groups groups of its own; NULL is kda_chunk_fwd_scan. The workspace
+ * size is kda_chunk_fwd_scan_workspace_size's.
+ */
+kda_status kda_chunk_fwd_scan_ex(const void* q, const void* k, const void* v,
+                                 const void* log_alpha, const void* beta, const float* init_state,
+                                 const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                                 kda_dtype dtype, uint32_t options, int32_t num_groups, void* o,
+                                 float* final_state, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /*
  * Training backward of kda_chunk_fwd (options = 0; kda_chunk_bwd_ex below takes input options):

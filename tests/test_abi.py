@@ -20,6 +20,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_chunk_fwd_workspace_size",
                           "kda_chunk_fwd_noalloc",
                           "kda_chunk_fwd_scan", "kda_chunk_fwd_scan_workspace_size",
+                          "kda_chunk_fwd_scan_ex",
                           "kda_chunk_bwd", "kda_chunk_bwd_workspace_size",
                           "kda_chunk_bwd_workspace_size_ex", "kda_chunk_bwd_ex",
                           "kda_decode_step", "kda_decode_step_ex", "kda_status_string"}
@@ -215,13 +216,35 @@ def test_chunk_fwd_scan_argument_errors(kw, expect):
     assert _scan(kda.lib(), **kw) == expect
 
 
+def _scan_ex(L, cu, **kw):
+    a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, init=None, N=3, T=128, H=2, dk=32, dv=32,
+             dtype=BF16, opts=0, G=4, o=6 * A, fin=7 * A, ws=8 * A, wsb=4096, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kda_chunk_fwd_scan_ex(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]),
+                                   vp(a["init"]), vp(cu), a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                                   a["dtype"], a["opts"], a["G"], vp(a["o"]), vp(a["fin"]),
+                                   vp(a["ws"]), a["wsb"], vp(a["stream"]))
+
+
+def test_chunk_fwd_scan_ex_argument_errors():
+    L = kda.lib()
+    # with cu_seqlens the lengths need not divide T (only the small workspace stops the call)
+    assert _scan_ex(L, 9 * A) == WS_SMALL
+    assert _scan_ex(L, None) == INVALID           # no cu_seqlens: equal lengths, 128 % 3 != 0
+    assert _scan_ex(L, 9 * A + 2) == INVALID      # cu_seqlens 4-byte aligned
+    assert _scan_ex(L, 9 * A, G=0) == INVALID
+    assert _scan_ex(L, 9 * A, dk=64) == NOT_SUPPORTED
+
+
 def test_scan_workspace_size():
     import torch
     ws = lambda *a: int(kda.lib().kda_chunk_fwd_scan_workspace_size(*a))
     assert ws(1, 65536, 4, 128, 128, 1, 8) > kda.workspace_size(1, 65536, 4, 128, 128, torch.bfloat16)
     assert ws(1, 65536, 4, 128, 64, 1, 8) == 0
     assert ws(1, 65536, 4, 128, 128, 1, 0) == 0
-    assert ws(3, 100, 4, 64, 64, 0, 2) == 0
+    # the size holds for any split of T into N sequences (varlen through kda_chunk_fwd_scan_ex)
+    assert ws(3, 100, 4, 64, 64, 0, 2) > 0
 
 
 def _bwd(L, **kw):

@@ -123,3 +123,29 @@ def test_scan_several_record_segments():
     o_ref, f_ref = oracle_fwd(inp, heads=[6])
     assert_close(np64(o2[:, 6:7]), o_ref, torch.bfloat16, "o head 6")
     assert_close(np64(f2[:, 6:7]), f_ref, torch.bfloat16, "final head 6")
+
+
+@pytest.mark.parametrize("lengths,H,K,dtype,G,gates", [
+    ([3000, 64, 0, 1, 5000, 700], 2, 64, torch.bfloat16, 4, "uniform"),
+    ([1500, 260, 2048], 1, 128, torch.bfloat16, 16, "uniform"),
+    ([700, 0, 1300, 65], 2, 32, torch.float32, 3, "slow"),
+    ([900, 2000], 1, 64, torch.float32, 1, "uniform"),   # one group per sequence
+])
+def test_scan_varlen(lengths, H, K, dtype, G, gates):
+    """kda_chunk_fwd_scan_ex over packed sequences of different lengths (empty and one-token
+    ones among them), each split into G groups of its own: against the oracle and against
+    kda_chunk_fwd on the same packing. The slow-decay case carries much of each group's start
+    state into its outputs."""
+    print("scan varlen", lengths, H, K, dtype, G, flush=True)
+    cu = torch.tensor(workloads.cu_from_lengths(lengths), dtype=torch.int32, device=DEV)
+    T, N = sum(lengths), len(lengths)
+    inp = workloads.gen_forward(T, H, K, K, gates=gates, dtype=dtype, device=DEV, seed=T + G,
+                                num_seqs=N, init_std=0.1)
+    o, fin = kda.chunk_fwd_scan(*(inp[x] for x in ORDER), init_state=inp["init_state"],
+                                cu_seqlens=cu, num_groups=G)
+    o_ref, f_ref = oracle_fwd(inp, cu=cu)
+    assert_close(np64(o), o_ref, dtype, "o")
+    assert_close(np64(fin), f_ref, dtype, "final")
+    o2, fin2 = kda.chunk_fwd(*(inp[x] for x in ORDER), init_state=inp["init_state"], cu_seqlens=cu)
+    assert rel_err(np64(o), np64(o2)) <= TOL[dtype]
+    assert rel_err(np64(fin), np64(fin2)) <= TOL[dtype]
