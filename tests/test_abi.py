@@ -370,6 +370,9 @@ def test_wide_key_workspace_size():
     assert ws(1, 1000, 2, 256, 512, torch.bfloat16) == 0
     # fp32 inputs at K = 128 take the same path; the scan (chunk path only) refuses them
     assert ws(1, 1000, 2, 128, 128, torch.float32) > 0
+    # ... with the same segmented records: bounded at any length
+    e, f = ws(1, 1 << 20, 32, 128, 128, torch.float32), ws(1, 1 << 21, 32, 128, 128, torch.float32)
+    assert e < 1 << 30 and f - e < 8 << 20
     assert int(kda.lib().kda_chunk_fwd_scan_workspace_size(1, 1024, 2, 128, 128, 0, 4)) == 0
     assert int(kda.lib().kda_chunk_fwd_scan_workspace_size(1, 1024, 2, 128, 128, 1, 4)) > 0
     # the scan keeps K = V <= 128
