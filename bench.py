@@ -70,7 +70,8 @@ def decode_alg_bytes(N, H, K, V, es, gate_dim=None):
 # JSON line carries it only while the sources are unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_long_prefill_and_decode.json")
 SOURCES = [os.path.join(ROOT, "gated_delta_rule_30_amd", "csrc", f)
-           for f in ("kda_chunk.hip", "kda_decode.hip", "kda_device.h", "kda_internal.h")]
+           for f in ("kda_chunk.hip", "kda_decode.hip", "kda_device.h", "kda_internal.h",
+                     "kda_record.h")]
 CHUNK_KERNELS = ("table_kernel", "segment_kernel", "prep_kernel", "state_kernel", "state_split_kernel")
 DECODE_KERNEL = "decode_step_kernel"
 OTHER_PATHS = ("wide_", "bwd_", "scan_")  # kernels of other entry points with similar names

@@ -9,14 +9,15 @@
 namespace {
 
 bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128 || d == 256; }
-// the chunk path's prep kernel holds K-wide operand tiles in LDS: K <= 128; K = 256 takes the
-// wide-key path (fp32 records, key channels in parts of 64), as do fp32 inputs at K = 128
+// the chunk path's prep kernel holds K-wide operand tiles in LDS: K <= 128 (K = 256 runs an
+// fp32 record kernel with the key channels in parts of 64 instead)
 bool supported_chunk_dk(int32_t d) { return d == 32 || d == 64 || d == 128; }
 constexpr int32_t kWideDk = 256;
-// the chunk forward's wide-key path: K = 256, and fp32 inputs at K = 128 (whose fp32 operand
-// tiles exceed the chunk path's prep kernel LDS budget)
-bool wide_path(int32_t dk, kda_dtype dtype) {
-  return dk == kWideDk || (dk == 128 && dtype == KDA_DTYPE_F32);
+// the fp32 wide-key path: fp32 inputs at K >= 128, and K = 256 with input options (bf16 inputs
+// at K = 256 without options run the chunk path: an fp32 record kernel and the bf16 chain)
+bool wide_path(int32_t dk, kda_dtype dtype, uint32_t options) {
+  return (dk == kWideDk && (dtype == KDA_DTYPE_F32 || options != 0)) ||
+         (dk == 128 && dtype == KDA_DTYPE_F32);
 }
 constexpr uint32_t kAllOptions =
     KDA_OPT_SCALAR_GATE | KDA_OPT_GATE_LOGITS | KDA_OPT_BETA_LOGITS | KDA_OPT_L2NORM_QK;
@@ -63,14 +64,20 @@ extern "C" size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_t
                                                int32_t num_heads, int32_t dk, int32_t dv,
                                                kda_dtype dtype) {
   if (check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype) != KDA_SUCCESS) return 0;
-  if (wide_path(dk, dtype)) {
+  // (the options are not known here: at K = 256 bf16 the larger of the two paths' needs)
+  size_t need = 0;
+  if (wide_path(dk, dtype, 0u) || (dk == kWideDk && dtype == KDA_DTYPE_BF16)) {
     kda::WidePlan wp;
-    return kda::make_wide_plan(num_seqs, total_tokens, num_heads, dk, dv, &wp) ? wp.total_bytes : 0;
+    if (!kda::make_wide_plan(num_seqs, total_tokens, num_heads, dk, dv, &wp)) return 0;
+    need = wp.total_bytes;
   }
-  kda::ChunkPlan pl;
-  if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16, &pl))
-    return 0;
-  return pl.total_bytes;
+  if (!wide_path(dk, dtype, 0u)) {
+    kda::ChunkPlan pl;
+    if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16, &pl))
+      return 0;
+    need = pl.total_bytes > need ? pl.total_bytes : need;
+  }
+  return need;
 }
 
 // Everything kda_chunk_fwd_ex checks before it looks at the workspace; fills the launch
@@ -128,7 +135,9 @@ kda_status kda::prepare_chunk_fwd(const void* q, const void* k, const void* v,
   return KDA_SUCCESS;
 }
 
-bool kda::is_wide_path(int32_t dk, kda_dtype dtype) { return wide_path(dk, dtype); }
+bool kda::is_wide_path(int32_t dk, kda_dtype dtype, uint32_t options) {
+  return wide_path(dk, dtype, options);
+}
 
 extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v,
                                        const void* log_alpha, const void* beta,
@@ -146,7 +155,8 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERROR_INVALID_VALUE;
   kda::ChunkPlan pl;
   kda::WidePlan wp;
-  if (wide_path(dk, dtype)) {
+  const bool wide = wide_path(dk, dtype, options);
+  if (wide) {
     if (!kda::make_wide_plan(num_seqs, total_tokens, num_heads, dk, dv, &wp)) return KDA_ERROR_INVALID_VALUE;
     if (workspace_bytes < wp.total_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
   } else {
@@ -155,7 +165,7 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
     if (workspace_bytes < pl.total_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
   }
   a.workspace = workspace;
-  hipError_t e = wide_path(dk, dtype) ? kda::launch_chunk_fwd_wide(a, wp) : kda::launch_chunk_fwd(a, pl);
+  hipError_t e = wide ? kda::launch_chunk_fwd_wide(a, wp) : kda::launch_chunk_fwd(a, pl);
   return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
 }
 
@@ -310,7 +320,7 @@ static kda_status check_scan_shape(int32_t num_seqs, int64_t total_tokens, int32
   kda_status st = check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_SUCCESS) return st;
   // the first pass needs V + K columns (<= 256) and the chunk path (K <= 128; fp32 at K <= 64)
-  if (dk != dv || wide_path(dk, dtype)) return KDA_ERROR_NOT_SUPPORTED;
+  if (dk != dv || dk > 128 || wide_path(dk, dtype, 0u)) return KDA_ERROR_NOT_SUPPORTED;
   if (num_groups <= 0) return KDA_ERROR_INVALID_VALUE;
   return KDA_SUCCESS;
 }

@@ -37,34 +37,9 @@
 
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_record.h"
 
 namespace kda {
-
-// ====================================================================== record layout
-// Matrices are stored as MFMA A-operand fragments: for a matrix with R rows and reduction
-// length L, the 16-byte slot of (row tile, reduction step, lane) is at element
-//     ((tile * (L / KS) + step) * 64 + lane) * EPL
-// and element e of the slot of lane (m, g) is (row 16*tile + m, index KS*step + kk(g, e)).
-template <int K, typename MT>
-struct Rec {
-  static constexpr size_t oW = 0;                                // [CHUNK rows][K]
-  static constexpr size_t oQ = oW + (size_t)CHUNK * K;           // [CHUNK rows][K]
-  static constexpr size_t oKt = oQ + (size_t)CHUNK * K;          // [K rows][CHUNK]
-  static constexpr size_t oTb = oKt + (size_t)K * CHUNK;         // [CHUNK rows][CHUNK]
-  static constexpr size_t oPb = oTb + (size_t)CHUNK * CHUNK;     // [CHUNK rows][CHUNK]
-  static constexpr size_t nMat = oPb + (size_t)CHUNK * CHUNK;
-  static constexpr size_t oGamBytes = nMat * sizeof(MT);         // K fp32
-  static constexpr size_t bytes = (oGamBytes + K * 4 + 1023) / 1024 * 1024;  // whole 1 KB slots
-  // then V of the chunk, slice-major: slice c (value columns 16c .. 16c+15) is CHUNK rows of 16
-  // values, 16 * CHUNK * sizeof(MT) bytes, at oVBytes + c * 16 * CHUNK * sizeof(MT)
-  static constexpr size_t oVBytes = bytes;
-  static constexpr size_t vslice_bytes = (size_t)16 * CHUNK * sizeof(MT);
-};
-
-template <typename MT>
-__device__ __forceinline__ size_t slot_elem(int tile, int step, int lane, int L) {
-  return ((size_t)(tile * (L / Mma<MT>::KS) + step) * 64 + lane) * Mma<MT>::EPL;
-}
 
 // four consecutive MT values from fp32
 __device__ __forceinline__ void st4(bf16* p, f32x4 x) {
@@ -1246,28 +1221,35 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
 // read of the previous chunk. Measured on the long prefill this is a few percent faster than
 // one wave per chain: the chain stays bound by the fragments' round trips through L2 (the
 // CU's L1 reports stalls on pending L2 data for about 40% of the kernel's time either way).
+// NW waves per slice, each holding K / NW key channels of S: two up to K = 128, four at
+// K = 256 (so that each wave's share of S and of the chunk's fragments stays that of K = 128)
+template <int K>
+constexpr int split_threads() { return K > 128 ? 256 : 128; }
 template <int K, typename MT>
 struct SplitShape {
   using SH = StateShape<K, MT>;
+  static constexpr int NW = K > 128 ? 4 : 2;
+  static constexpr int THREADS = 64 * NW;
   static constexpr int KS = SH::KS, NKT = SH::NKT, NKS = SH::NKS, NTT = SH::NTT, NTS = SH::NTS;
   static constexpr int NTRI = SH::NTRI;
-  static constexpr bool OK = NKS % 2 == 0 && NTT % 2 == 0;
-  static constexpr int HKS = NKS / 2;  // reduction steps over K per wave
-  static constexpr int HKT = NKT / 2;  // key-channel tiles of S per wave
-  static constexpr int HT = NTT / 2;   // output token tiles each wave stores
+  static constexpr bool OK = NKS % NW == 0 && NTT % NW == 0;
+  static constexpr int HKS = NKS / NW;  // reduction steps over K per wave
+  static constexpr int HKT = NKT / NW;  // key-channel tiles of S per wave
+  static constexpr int HT = NTT / NW;   // output token tiles each wave stores
   static constexpr int NA = 2 * NTT * HKS;      // -W and Qe, interleaved per step
   static constexpr int NB = HKT * NTS;          // Ktilde^T over this wave's rows
-  static constexpr int NF = NA + NB + NTRI;     // + T' (wave 0) or P (wave 1)
+  static constexpr int NF = NA + NB + NTRI;     // + T' (wave 0) or P (wave 1); NA + NB for the rest
   // chunks of fragments in flight (1 or 2): the same time on the long prefill (2.24 ms per
   // call), and one chunk needs 120 fewer registers
   static constexpr int RING_CHUNKS = 1;
+  static_assert(THREADS == split_threads<K>(), "one thread count per K");
 };
-constexpr int SPLIT_THREADS = 128;
 
 template <int K, typename MT>
-__global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_split_kernel(StateParams p) {
+__global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_split_kernel(StateParams p) {
   using SH = StateShape<K, MT>;
   using SS = SplitShape<K, MT>;
+  constexpr int NW = SS::NW;
   using R = Rec<K, MT>;
   using M = Mma<MT>;
   using frag = typename M::frag;
@@ -1279,8 +1261,8 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
   using vload = typename VecN<MT, VL>::vec;
   static_assert(SS::OK, "two-wave split needs an even number of K steps and token tiles");
   static_assert(HKT == HKS * (KS / 16), "a wave's K steps cover its key tiles");
-  __shared__ __align__(16) f32x4 sX[2][2][NTT][64];  // [parity][wave][token tile][lane]: Delta partials
-  __shared__ __align__(16) f32x4 sO[2][2][HT][64];   // [parity][wave][tile][lane]: O partials for the partner
+  __shared__ __align__(16) f32x4 sX[2][NW][NTT][64];  // [parity][wave][token tile][lane]: Delta partials
+  __shared__ __align__(16) f32x4 sO[2][NW][NTT][64];  // [parity][wave][tile][lane]: O partials for the tile's owner
   __shared__ __align__(16) MT sV[CHUNK * LDV];       // wave 0: V of the next chunk
   __shared__ int32_t sRun[SEG_CHUNK_HEADS + 16];
   __shared__ int32_t sLen;
@@ -1311,7 +1293,7 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
   const int kmax = (int)min((int64_t)(nc - en.depth), p.E);
   if (tid == 0) sLen = kmax;
   __syncthreads();
-  for (int k = tid; k < kmax; k += SPLIT_THREADS) {
+  for (int k = tid; k < kmax; k += SS::THREADS) {
     const int64_t ek = p.basetab[en.depth + k] + rank;
     sRun[k] = (int32_t)(ek - p.seg_begin);
     if (ek >= seg_end) atomicMin(&sLen, k);
@@ -1342,6 +1324,7 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
 
   auto body = [&](auto WVc) {
     constexpr int WV = decltype(WVc)::value;
+    constexpr int NFW = WV < 2 ? NF : NA + NB;  // this wave's operations per chunk
     // operation j of this wave's stream reads the next chunk's record (wave 0's T') or this one's
     auto next_rec = [](int j) constexpr { return WV == 0 && j >= NA + NB; };
     auto frag_off = [](auto J) constexpr -> uint32_t {
@@ -1418,15 +1401,15 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
     // flight), or slot j operation j of the next chunk (one chunk in flight)
     constexpr int RC = SS::RING_CHUNKS;
     static_assert(RC == 1 || RC == 2, "ring depth");
-    frag ring[RC * NF];
-    static_for<0, NF>([&](auto J) {
+    frag ring[RC * NFW];
+    static_for<0, NFW>([&](auto J) {
       constexpr int j = decltype(J)::value;
       ring[j] = ldf(next_rec(j) ? rc1 : rc0, frag_off(J));
     });
     if constexpr (RC == 2)
-      static_for<0, NF>([&](auto J) {
+      static_for<0, NFW>([&](auto J) {
         constexpr int j = decltype(J)::value;
-        ring[NF + j] = ldf(next_rec(j) ? rc2 : rc1, frag_off(J));
+        ring[NFW + j] = ldf(next_rec(j) ? rc2 : rc1, frag_off(J));
       });
     __builtin_amdgcn_sched_barrier(0);
     uint32_t rc3 = rec_off(rec_index(3));
@@ -1444,7 +1427,7 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
       __builtin_amdgcn_sched_barrier(0);
 
       frag Sb[HKS], Db[NTS];
-      static_for<0, NF>([&](auto J) {
+      static_for<0, NFW>([&](auto J) {
         constexpr int j = decltype(J)::value;
         if constexpr (j < NA && j % (2 * NTT) == 0) {
           constexpr int s = j / (2 * NTT);
@@ -1456,8 +1439,19 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
           for (int tt = 0; tt < NTT; ++tt) sX[par][WV][tt][lane] = U[tt];
           lds_barrier();
+          if constexpr (NW == 2) {
 #pragma unroll
-          for (int tt = 0; tt < NTT; ++tt) U[tt] += sX[par][1 - WV][tt][lane];
+            for (int tt = 0; tt < NTT; ++tt) U[tt] += sX[par][1 - WV][tt][lane];
+          } else {
+            // every wave sums the partials in wave order, so all hold the same Delta
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+              f32x4 x = sX[par][0][tt][lane];
+#pragma unroll
+              for (int v = 1; v < NW; ++v) x += sX[par][v][tt][lane];
+              U[tt] = x;
+            }
+          }
 #pragma unroll
           for (int s = 0; s < NTS; ++s) {
             if constexpr (KS == 32) Db[s] = frag_from_acc(U[2 * s], U[2 * s + 1], MT());
@@ -1466,7 +1460,10 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
           if (k > 0) {
 #pragma unroll
             for (int i = 0; i < HT; ++i) {
-              const f32x4 o = Okeep[i] + sO[par][1 - WV][i][lane];
+              f32x4 o = Okeep[i];
+#pragma unroll
+              for (int v = 0; v < NW; ++v)
+                if (v != WV) o += sO[par][v][WV * HT + i][lane];
               buf_store(ro_prev, o_voff, (uint32_t)(16 * (WV * HT + i)) * rowb, to_mt4<MT>(o));
             }
           }
@@ -1482,7 +1479,7 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
           for (int tt = 0; tt < NTT; ++tt) U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
           if constexpr (WV == 0) load_v(rc2, vx);
         }
-        constexpr int slot = (RC == 2 ? par * NF : 0) + j;
+        constexpr int slot = (RC == 2 ? par * NFW : 0) + j;
         const frag f = ring[slot];
         if constexpr (j < NA) {
           constexpr int s = j / (2 * NTT), r = j % (2 * NTT), tt = r % NTT;
@@ -1501,12 +1498,18 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
         else ring[slot] = ldf(next_rec(j) ? rc2 : rc1, frag_off(J));
         __builtin_amdgcn_sched_barrier(0);
       });
-      // output partials: keep this wave's tiles, hand the partner its tiles
+      // waves without the T'V / P Delta operations never reach the reset at NA + NB: their next
+      // Delta partial starts from zero here
+      if constexpr (NFW == NA + NB) {
 #pragma unroll
-      for (int i = 0; i < HT; ++i) {
-        Okeep[i] = O[WV * HT + i];
-        sO[par ^ 1][WV][i][lane] = O[(1 - WV) * HT + i];
+        for (int tt = 0; tt < NTT; ++tt) U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      // output partials: keep this wave's tiles, hand the other tiles to their owners
+#pragma unroll
+      for (int i = 0; i < HT; ++i) Okeep[i] = O[WV * HT + i];
+#pragma unroll
+      for (int t = 0; t < NTT; ++t)
+        if (t / HT != WV) sO[par ^ 1][WV][t][lane] = O[t];
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
       ro_prev = ro;
@@ -1525,7 +1528,10 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < HT; ++i) {
-      const f32x4 o = Okeep[i] + sO[run & 1][1 - WV][i][lane];
+      f32x4 o = Okeep[i];
+#pragma unroll
+      for (int v = 0; v < NW; ++v)
+        if (v != WV) o += sO[run & 1][v][WV * HT + i][lane];
       buf_store(ro_prev, o_voff, (uint32_t)(16 * (WV * HT + i)) * rowb, to_mt4<MT>(o));
     }
 #pragma unroll
@@ -1537,8 +1543,13 @@ __global__ __launch_bounds__(SPLIT_THREADS) __attribute__((amdgpu_waves_per_eu(1
       ps[3 * V] = S[i][3];
     }
   };
-  if (__builtin_amdgcn_readfirstlane(wave_id()) == 0) body(std::integral_constant<int, 0>());
-  else body(std::integral_constant<int, 1>());
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
+  if (wv == 0) body(std::integral_constant<int, 0>());
+  else if (wv == 1) body(std::integral_constant<int, 1>());
+  if constexpr (NW == 4) {
+    if (wv == 2) body(std::integral_constant<int, 2>());
+    else if (wv == 3) body(std::integral_constant<int, 3>());
+  }
 }
 
 // ====================================================================== host side
@@ -1642,17 +1653,23 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl, const 
   const int64_t ptasks = pl.seg_entries * a.num_heads;
   const dim3 pgrid((unsigned)min(ptasks, (int64_t)2 * ncu));
   auto prep = [&](int64_t s, hipStream_t q) {
-    PrepParams pp{a.q, a.k, a.g, a.beta, entries, header, a.num_heads, s * pl.seg_entries,
-                  pl.seg_entries, seg_rec(s), rb, a.options, a.v, a.dv};
-    const bool v256 = (size_t)a.dv * sizeof(MT) == 256;
-    if (a.options == 0 && v256)
-      hipLaunchKernelGGL((prep_kernel<K, MT, false, true>), pgrid, dim3(PREP_THREADS), 0, q, pp);
-    else if (a.options == 0)
-      hipLaunchKernelGGL((prep_kernel<K, MT, false, false>), pgrid, dim3(PREP_THREADS), 0, q, pp);
-    else if (v256)
-      hipLaunchKernelGGL((prep_kernel<K, MT, true, true>), pgrid, dim3(PREP_THREADS), 0, q, pp);
-    else
-      hipLaunchKernelGGL((prep_kernel<K, MT, true, false>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+    if constexpr (K == 256) {  // the fp32 record kernel of 256 key channels
+      const Rec256Params rp{a.q, a.k, a.v, a.g, a.beta, entries, header, a.num_heads, a.dv,
+                            s * pl.seg_entries, pl.seg_entries, seg_rec(s), rb};
+      launch_rec256(rp, q);
+    } else {
+      PrepParams pp{a.q, a.k, a.g, a.beta, entries, header, a.num_heads, s * pl.seg_entries,
+                    pl.seg_entries, seg_rec(s), rb, a.options, a.v, a.dv};
+      const bool v256 = (size_t)a.dv * sizeof(MT) == 256;
+      if (a.options == 0 && v256)
+        hipLaunchKernelGGL((prep_kernel<K, MT, false, true>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+      else if (a.options == 0)
+        hipLaunchKernelGGL((prep_kernel<K, MT, false, false>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+      else if (v256)
+        hipLaunchKernelGGL((prep_kernel<K, MT, true, true>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+      else
+        hipLaunchKernelGGL((prep_kernel<K, MT, true, false>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+    }
   };
   auto state = [&](int64_t s, hipStream_t q) -> bool {
     StateParams sp{a.v, a.o, a.init_state, run_state, entries, header, basetab,
@@ -1661,7 +1678,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl, const 
                    (uint32_t)seg_buf};
     if (pl.vs != 16) return false;
     if constexpr (SplitShape<K, MT>::OK)
-      hipLaunchKernelGGL((state_split_kernel<K, MT>), sgrid, dim3(SPLIT_THREADS), 0, q, sp);
+      hipLaunchKernelGGL((state_split_kernel<K, MT>), sgrid, dim3(SplitShape<K, MT>::THREADS), 0, q, sp);
     else
       hipLaunchKernelGGL((state_kernel<K, MT>), sgrid, dim3(STATE_THREADS), 0, q, sp);
     return true;
@@ -1682,6 +1699,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkPlan& pl, const Recor
     if (a.dk == 32) return launch_chunk_t<32, bf16>(a, pl, rr);
     if (a.dk == 64) return launch_chunk_t<64, bf16>(a, pl, rr);
     if (a.dk == 128) return launch_chunk_t<128, bf16>(a, pl, rr);
+    if (a.dk == 256 && a.options == 0) return launch_chunk_t<256, bf16>(a, pl, rr);
   } else {
     if (a.dk == 32) return launch_chunk_t<32, float>(a, pl, rr);
     if (a.dk == 64) return launch_chunk_t<64, float>(a, pl, rr);

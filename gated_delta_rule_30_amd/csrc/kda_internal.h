@@ -96,4 +96,18 @@ struct RecordRegion {
 hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkPlan& p,
                             const RecordRegion* records = nullptr);
 
+// The chunk records at 256 key channels (bf16 inputs, no input options), for entries
+// [seg_begin, seg_begin + E) of the chunk table, written by an fp32 record kernel
+// (kda_wide.hip) in the layout the state kernel reads.
+struct Rec256Params {
+  const void *q, *k, *v, *g, *beta;
+  const Entry* entries;
+  const int32_t* header;
+  int H, V;
+  int64_t seg_begin, E;
+  char* rec;
+  int64_t rec_bytes;
+};
+void launch_rec256(const Rec256Params& p, hipStream_t st);
+
 }  // namespace kda

@@ -65,7 +65,7 @@ extern "C" kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const 
   // the running state lives in the caller's final_state; the wide-key path's records grow
   // with the sequence length and are not served from the fixed scratch
   if (final_state == nullptr) return KDA_ERROR_INVALID_VALUE;
-  if (kda::is_wide_path(dk, dtype)) return KDA_ERROR_NOT_SUPPORTED;
+  if (kda::is_wide_path(dk, dtype, options)) return KDA_ERROR_NOT_SUPPORTED;
   // plan with the record buffer capped to what the scratch leaves after the tables; the
   // tables are largest with one chunk per segment, so that plan bounds them
   kda::ChunkPlan pl;

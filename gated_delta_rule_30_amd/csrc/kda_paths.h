@@ -15,8 +15,9 @@ kda_status prepare_chunk_fwd(const void* q, const void* k, const void* v, const 
                              int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t dk,
                              int32_t dv, kda_dtype dtype, uint32_t options, void* o,
                              float* final_state, void* stream, ChunkArgs* a);
-// Whether kda_chunk_fwd runs this head dim and dtype on the wide-key path (kda_wide.hip).
-bool is_wide_path(int32_t dk, kda_dtype dtype);
+// Whether kda_chunk_fwd_ex runs this head dim, dtype and options on the wide-key path
+// (kda_wide.hip).
+bool is_wide_path(int32_t dk, kda_dtype dtype, uint32_t options);
 
 // Chunk-parallel scan over equal-length sequences split into G groups of whole chunks: a pass
 // over the groups with V + K state columns, a combine, and a pass from the groups' initial

@@ -17,6 +17,7 @@
 //                      matrix-core steps
 // Every product that carries in-chunk decay is formed pairwise, e^{b_i - b_j} with j <= i.
 #include "kda_fp32.h"
+#include "kda_record.h"
 
 namespace kda {
 
@@ -37,6 +38,81 @@ struct WRec {
   static constexpr int oGam = oU + BC * V;   // gamma               [256]
   static constexpr int floats = (oGam + KW + 63) / 64 * 64;
 };
+
+// A and P of a chunk are summed over its key channels in parts of KQ: rows pi and 63 - pi form
+// a pair with 65 entries j <= i; TPP threads share a pair, thread jq taking v = jq + TPP u
+// (v <= pi: row pi, j = v; else row 63 - pi, j = v - pi - 1), so every thread has the same work
+constexpr int TPP = NTP / (BC / 2), VPT = (BC + 1 + TPP - 1) / TPP;
+constexpr int LKQ = KQ + 4;  // LDS row of a channel part
+
+// a[u] += sum_c k_ic k_jc e^{b_ic - b_jc} and p[u] += sum_c q_ic k_jc e^{b_ic - b_jc} over the
+// part's channels (sQ, sK: q and k; sB: b log2 e; all [64][LKQ]); every factor is at most 1
+__device__ __forceinline__ void pair_sums(const float* sQ, const float* sK, const float* sB,
+                                          float (&a)[VPT], float (&p)[VPT]) {
+  const int pi = threadIdx.x / TPP, jq = threadIdx.x % TPP, i2 = BC - 1 - pi;
+  for (int c4 = 0; c4 < KQ; c4 += 4) {
+    const f32x4 q1 = *reinterpret_cast<const f32x4*>(sQ + pi * LKQ + c4);
+    const f32x4 k1 = *reinterpret_cast<const f32x4*>(sK + pi * LKQ + c4);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(sB + pi * LKQ + c4);
+    const f32x4 q2 = *reinterpret_cast<const f32x4*>(sQ + i2 * LKQ + c4);
+    const f32x4 k2 = *reinterpret_cast<const f32x4*>(sK + i2 * LKQ + c4);
+    const f32x4 b2 = *reinterpret_cast<const f32x4*>(sB + i2 * LKQ + c4);
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int v = jq + TPP * u;
+      if (v <= BC) {
+        const bool lo = v <= pi;
+        const int j = lo ? v : v - pi - 1;
+        const f32x4 qi = lo ? q1 : q2, ki = lo ? k1 : k2, bi = lo ? b1 : b2;
+        const f32x4 kj = *reinterpret_cast<const f32x4*>(sK + j * LKQ + c4);
+        const f32x4 bj = *reinterpret_cast<const f32x4*>(sB + j * LKQ + c4);
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = kj[e] * exp2_f(bi[e] - bj[e]);
+        a[u] += dot4(ki, w);
+        p[u] += dot4(qi, w);
+      }
+    }
+  }
+}
+
+// The summed entries out: A (beta-scaled, strictly lower, zero elsewhere) into sA [64][68],
+// and P_ij (j <= i) to outp(i, j, x)
+template <typename F>
+__device__ __forceinline__ void pairs_out(float* sA, const float* sBeta, const float (&a)[VPT],
+                                          const float (&p)[VPT], F&& outp) {
+  const int pi = threadIdx.x / TPP, jq = threadIdx.x % TPP, i2 = BC - 1 - pi;
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int v = jq + TPP * u;
+    if (v <= BC) {
+      const bool lo = v <= pi;
+      const int i = lo ? pi : i2, j = lo ? v : v - pi - 1;
+      sA[i * 68 + j] = j < i ? sBeta[i] * a[u] : 0.f;
+      outp(i, j, p[u]);
+    }
+  }
+}
+
+// T = (I + A)^{-1} for the strictly lower A in sA [64][68], by forward substitution, one column
+// per thread of wave 0; T overwrites A after the wave's last read of it (a wave's LDS accesses
+// take effect in program order). The caller's barriers order it with the other waves.
+__device__ __forceinline__ void unit_lower_inverse(float* sA) {
+  if (threadIdx.x < BC) {
+    const int m = threadIdx.x;
+    float x[BC];
+#pragma unroll
+    for (int r = 0; r < BC; ++r) {
+      // four partial sums: the row's dot product is not one chain of dependent FMAs
+      float ps[4] = {r == m ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < r; ++j) ps[j & 3] -= sA[r * 68 + j] * x[j];
+      x[r] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
+#pragma unroll
+    for (int r = 0; r < BC; ++r) sA[r * 68 + m] = x[r];
+  }
+}
 
 }  // namespace
 
@@ -66,11 +142,7 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
   float* rc = rec + ((size_t)lc * H + h) * R::floats;
   if (threadIdx.x < BC)
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(gtok + threadIdx.x) * (int64_t)H + h]) : 0.f;
-  // A and P, summed over the four quarters: rows pi and 63 - pi form a pair with 65 entries j <= i;
-  // TPP threads share a pair, thread jq taking v = jq + TPP u (v <= pi: row pi, j = v; else
-  // row 63 - pi, j = v - pi - 1), so every thread has the same work
-  constexpr int TPP = NTP / (BC / 2), VPT = (BC + 1 + TPP - 1) / TPP;
-  const int pi = threadIdx.x / TPP, jq = threadIdx.x % TPP, i2 = BC - 1 - pi;
+  // A and P, summed over the four quarters
   float a[VPT], p[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) a[u] = p[u] = 0.f;
@@ -90,61 +162,14 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
       rc[R::oKt + r * KW + c0 + cc] = sK[r * LK + cc] * exp2_f(bl - br);
     }
     if (threadIdx.x < KQ) rc[R::oGam + c0 + threadIdx.x] = exp2_f(sB[(BC - 1) * LK + threadIdx.x]);
-    for (int c4 = 0; c4 < KQ; c4 += 4) {
-      const f32x4 q1 = *reinterpret_cast<const f32x4*>(sQ + pi * LK + c4);
-      const f32x4 k1 = *reinterpret_cast<const f32x4*>(sK + pi * LK + c4);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(sB + pi * LK + c4);
-      const f32x4 q2 = *reinterpret_cast<const f32x4*>(sQ + i2 * LK + c4);
-      const f32x4 k2 = *reinterpret_cast<const f32x4*>(sK + i2 * LK + c4);
-      const f32x4 b2 = *reinterpret_cast<const f32x4*>(sB + i2 * LK + c4);
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int v = jq + TPP * u;
-        if (v <= BC) {
-          const bool lo = v <= pi;
-          const int j = lo ? v : v - pi - 1;
-          const f32x4 qi = lo ? q1 : q2, ki = lo ? k1 : k2, bi = lo ? b1 : b2;
-          const f32x4 kj = *reinterpret_cast<const f32x4*>(sK + j * LK + c4);
-          const f32x4 bj = *reinterpret_cast<const f32x4*>(sB + j * LK + c4);
-          f32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = kj[e] * exp2_f(bi[e] - bj[e]);
-          a[u] += dot4(ki, w);
-          p[u] += dot4(qi, w);
-        }
-      }
-    }
+    pair_sums(sQ, sK, sB, a, p);
     lds_barrier();  // the quarter's reads done before the next quarter overwrites it
   }
-#pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-    const int v = jq + TPP * u;
-    if (v <= BC) {
-      const bool lo = v <= pi;
-      const int i = lo ? pi : i2, j = lo ? v : v - pi - 1;
-      sA[i * 68 + j] = j < i ? sBeta[i] * a[u] : 0.f;
-      rc[R::oP + i * BC + j] = p[u];
-    }
-  }
+  pairs_out(sA, sBeta, a, p, [&](int i, int j, float x) { rc[R::oP + i * BC + j] = x; });
   for (int e = threadIdx.x; e < BC * BC; e += NTP)  // P's upper triangle
     if (e % BC > e / BC) rc[R::oP + e] = 0.f;
   lds_barrier();
-  // T = (I + A)^{-1} by forward substitution, one column per thread of wave 0; T overwrites A
-  // after the wave's last read of it (a wave's LDS accesses take effect in program order)
-  if (threadIdx.x < BC) {
-    const int m = threadIdx.x;
-    float x[BC];
-#pragma unroll
-    for (int r = 0; r < BC; ++r) {
-      // four partial sums: the row's dot product is not one chain of dependent FMAs
-      float ps[4] = {r == m ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < r; ++j) ps[j & 3] -= sA[r * 68 + j] * x[j];
-      x[r] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    }
-#pragma unroll
-    for (int r = 0; r < BC; ++r) sT[r * 68 + m] = x[r];
-  }
+  unit_lower_inverse(sA);  // T = (I + A)^{-1} into sT (= sA)
   lds_barrier();
   // W = T diag(beta) (k e^b), quarter by quarter
   for (int hh = 0; hh < KW / KQ; ++hh) {
@@ -173,6 +198,130 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
     });
     lds_barrier();
   }
+}
+
+// Records of the chunk path at 256 key channels (bf16 inputs, no input options): the same
+// chunk form as wide_prep_kernel, in fp32 with the key channels in parts of 64, written as the
+// bf16 MFMA fragment records that prep_kernel writes for K <= 128 -- -W, Qe, Ktilde^T, T' =
+// T diag(beta), P, gamma and V slice-major -- so that state_split_kernel runs the chain on the
+// bf16 matrix cores. One workgroup of 512 threads per (chunk, head) of the segment: task j is
+// entry seg_begin + j of the chunk table. Each thread writes one 16-byte fragment slot of a
+// 4 x 2 block of slots (token or channel tile ft, reduction step fsl) per matrix part.
+__global__ __launch_bounds__(NTP, 4) void rec256_kernel(Rec256Params p) {
+  constexpr int KW = 256;
+  using R = Rec<KW, bf16>;
+  __shared__ __align__(16) float sQ[BC * LKQ];  // q (part), then P, then W (part)
+  __shared__ __align__(16) float sK[BC * LKQ];  // k (part)
+  __shared__ __align__(16) float sB[BC * LKQ];  // b log2 e (part), then beta k e^b (part)
+  __shared__ __align__(16) float sA[BC * 68];   // A (strict lower), then T = (I + A)^{-1}
+  __shared__ float sBeta[BC];
+  const int jj = blockIdx.x, h = blockIdx.y, H = p.H;
+  const int64_t e = p.seg_begin + jj;
+  if (jj >= p.E || e >= p.header[0]) return;
+  const Entry en = p.entries[e];
+  const int64_t tok = en.tok;
+  const int len = en.len;
+  const bf16 *q = (const bf16*)p.q, *k = (const bf16*)p.k, *g = (const bf16*)p.g,
+             *beta = (const bf16*)p.beta, *v = (const bf16*)p.v;
+  char* rc = p.rec + ((int64_t)jj * H + h) * p.rec_bytes;
+  bf16* recM = reinterpret_cast<bf16*>(rc);
+  float* recGam = reinterpret_cast<float*>(rc + R::oGamBytes);
+  const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, gg = lane >> 4;
+  const int ft = tid >> 7, fsl = (tid >> 6) & 1;
+  // element e of a slot covers reduction index 32 step + kk(e) of row 16 tile + m
+  auto kk = [&](int el) { return 16 * (el >> 2) + 4 * gg + (el & 3); };
+  auto put = [&](size_t elem, const float (&x)[8]) {
+    bf16x8 f;
+#pragma unroll
+    for (int el = 0; el < 8; ++el) f[el] = (bf16)x[el];
+    *reinterpret_cast<bf16x8*>(recM + elem) = f;
+  };
+  if (tid < BC) sBeta[tid] = tid < len ? to_f32(beta[(tok + tid) * H + h]) : 0.f;
+  float a[VPT], pp[VPT];
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) a[u] = pp[u] = 0.f;
+  for (int hh = 0; hh < KW / KQ; ++hh) {
+    const int c0 = hh * KQ;
+    load_rows<KQ, LKQ, NTP, bf16, KW>(sQ, q, tok, len, H, h, c0);
+    load_rows<KQ, LKQ, NTP, bf16, KW>(sK, k, tok, len, H, h, c0);
+    load_rows<KQ, LKQ, NTP, bf16, KW>(sB, g, tok, len, H, h, c0);
+    lds_barrier();
+    cumsum_log2<KQ, LKQ, NTP>(sB);
+    lds_barrier();
+    // Qe = q e^b (token tile ft, channel step 2 hh + fsl) and Ktilde^T = (k e^{b_last - b})^T
+    // (channel tile 4 hh + ft, token step fsl); rows past len hold q = k = 0
+    {
+      float x[8], y[8];
+      const int r = 16 * ft + m, c = 16 * ft + m;
+      const float bl = sB[(BC - 1) * LKQ + c];
+#pragma unroll
+      for (int el = 0; el < 8; ++el) {
+        const int cq = 32 * fsl + kk(el), rk = 32 * fsl + kk(el);
+        x[el] = sQ[r * LKQ + cq] * exp2_f(sB[r * LKQ + cq]);
+        y[el] = sK[rk * LKQ + c] * exp2_f(bl - sB[rk * LKQ + c]);
+      }
+      put(R::oQ + slot_elem<bf16>(ft, 2 * hh + fsl, lane, KW), x);
+      put(R::oKt + slot_elem<bf16>(4 * hh + ft, fsl, lane, CHUNK), y);
+    }
+    if (tid < KQ) recGam[c0 + tid] = exp2_f(sB[(BC - 1) * LKQ + tid]);
+    pair_sums(sQ, sK, sB, a, pp);
+    lds_barrier();  // the part's reads done before the next part overwrites it
+  }
+  // A into sA; P (zero above the diagonal) into sQ, then its fragments
+  for (int el = tid; el < BC * BC; el += NTP) sQ[(el / BC) * LKQ + el % BC] = 0.f;
+  lds_barrier();
+  pairs_out(sA, sBeta, a, pp, [&](int i, int j, float x) { sQ[i * LKQ + j] = x; });
+  lds_barrier();
+  {
+    float x[8];
+#pragma unroll
+    for (int el = 0; el < 8; ++el) x[el] = sQ[(16 * ft + m) * LKQ + 32 * fsl + kk(el)];
+    put(R::oPb + slot_elem<bf16>(ft, fsl, lane, CHUNK), x);
+  }
+  unit_lower_inverse(sA);  // T into sA
+  lds_barrier();
+  {  // T' = T diag(beta) (zero above the diagonal)
+    float x[8];
+#pragma unroll
+    for (int el = 0; el < 8; ++el) {
+      const int c = 32 * fsl + kk(el);
+      x[el] = sA[(16 * ft + m) * 68 + c] * sBeta[c];
+    }
+    put(R::oTb + slot_elem<bf16>(ft, fsl, lane, CHUNK), x);
+  }
+  // -W = -T diag(beta) (k e^b), part by part (token tile ft, channel step 2 hh + fsl)
+  for (int hh = 0; hh < KW / KQ; ++hh) {
+    const int c0 = hh * KQ;
+    load_rows<KQ, LKQ, NTP, bf16, KW>(sB, g, tok, len, H, h, c0);
+    lds_barrier();
+    cumsum_log2<KQ, LKQ, NTP>(sB);
+    lds_barrier();
+    mul_rows_exp2<KQ, LKQ, NTP, bf16, KW>(sB, k, tok, len, H, h, c0);
+    lds_barrier();
+    for (int el = tid; el < BC * KQ; el += NTP) sB[(el / KQ) * LKQ + el % KQ] *= sBeta[el / KQ];
+    lds_barrier();
+    mmf<KQ, BC, false, false, 68, LKQ, NTP>(sA, sB, [&](int r, int cc, float x) { sQ[r * LKQ + cc] = x; });
+    lds_barrier();
+    float x[8];
+#pragma unroll
+    for (int el = 0; el < 8; ++el) x[el] = -sQ[(16 * ft + m) * LKQ + 32 * fsl + kk(el)];
+    put(R::oW + slot_elem<bf16>(ft, 2 * hh + fsl, lane, KW), x);
+    lds_barrier();
+  }
+  // V slice-major: row r of slice c (value columns 16c .. 16c + 15) at oVBytes + c * vslice +
+  // 32 r bytes; rows past len repeat the last valid row (T' is zero in those columns)
+  const int ppr = p.V / 8;  // 16-byte pieces per row
+  for (int id = tid; id < BC * ppr; id += NTP) {
+    const int r = id / ppr, c = id % ppr;
+    const int64_t t = tok + min(r, len - 1);
+    const uint4 x = *reinterpret_cast<const uint4*>(v + (t * H + h) * (int64_t)p.V + 8 * c);
+    *reinterpret_cast<uint4*>(rc + R::oVBytes + (size_t)(c >> 1) * R::vslice_bytes +
+                              (size_t)r * 32 + 16 * (c & 1)) = x;
+  }
+}
+
+void launch_rec256(const Rec256Params& p, hipStream_t st) {
+  hipLaunchKernelGGL(rec256_kernel, dim3((unsigned)p.E, (unsigned)p.H), dim3(NTP), 0, st, p);
 }
 
 // The chain of one (sequence, head, CW value columns); blockIdx = slice * chains8 + chain, so

@@ -139,7 +139,7 @@ def _noalloc(L, **kw):
     (dict(fin=None), INVALID),             # the running state lives in final_state
     (dict(N=0), INVALID),
     (dict(dk=48), NOT_SUPPORTED),
-    (dict(dk=256), NOT_SUPPORTED),         # the wide-key path is not served from the scratch
+    (dict(dk=256, opts=4), NOT_SUPPORTED),  # the fp32 wide-key path is not served from the scratch
     (dict(dtype=F32, dk=128), NOT_SUPPORTED),
     (dict(opts=16), NOT_SUPPORTED),
     (dict(q=A + 8), INVALID),

@@ -63,8 +63,24 @@ def test_noalloc_matches_chunk_fwd_two_calls():
 
 
 def test_noalloc_rejects_wide_key():
-    """K = 256 runs on the wide-key path, whose records are not served from the scratch."""
-    T, H, K, V = 64, 1, 256, 64
-    inp = workloads.gen_forward(T, H, K, V, dtype=torch.bfloat16, device=DEV, seed=23)
-    with pytest.raises(kda.KdaError):
-        kda.chunk_fwd_noalloc(*(inp[x] for x in ORDER))
+    """The fp32 wide-key path (fp32 inputs at K >= 128, K = 256 with input options) keeps fp32
+    records that the scratch does not serve."""
+    for K, dt, opts in ((128, torch.float32, 0), (256, torch.bfloat16, kda.OPT_BETA_LOGITS)):
+        inp = workloads.gen_forward(64, 1, K, 64, dtype=dt, device=DEV, seed=23)
+        with pytest.raises(kda.KdaError):
+            kda.chunk_fwd_noalloc(*(inp[x] for x in ORDER), options=opts)
+
+
+def test_noalloc_k256_matches_chunk_fwd():
+    """bf16 inputs at K = 256 run the chunk path (an fp32 record kernel, the bf16 chain), which
+    the scratch serves: the same outputs and final states as kda_chunk_fwd, bit for bit, on two
+    calls in a row (the second smaller)."""
+    for lengths, V in (([700, 0, 300], 128), ([130], 256)):
+        cu = torch.tensor(workloads.cu_from_lengths(lengths), dtype=torch.int32, device=DEV)
+        T, H = sum(lengths), 3
+        inp = workloads.gen_forward(T, H, 256, V, dtype=torch.bfloat16, device=DEV, seed=T,
+                                    num_seqs=len(lengths), init_std=0.1)
+        args = [inp[x] for x in ORDER]
+        o, fin = kda.chunk_fwd(*args, init_state=inp["init_state"], cu_seqlens=cu)
+        o2, fin2 = kda.chunk_fwd_noalloc(*args, init_state=inp["init_state"], cu_seqlens=cu)
+        assert torch.equal(o, o2) and torch.equal(fin, fin2)
