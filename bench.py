@@ -478,9 +478,13 @@ def main():
         torch.cuda.synchronize()
         wms = ew0.elapsed_time(ew1) / wsteps
         wfl = chunk_alg_flops(T, H, Kw, Vw)
+        wb = chunk_alg_bytes(T, H, Kw, Vw, 2, 1, True, True)
+        # bf16 inputs, no options: the fp32 record kernel and the bf16 matrix-core chain
         wide = {"workload": "B=1 H=32 T=65536 K=V=256 bf16, init state 0.1*N(0,1)",
+                "path": "fp32 records (rec256_kernel), bf16 chain (state_split_kernel, 4 waves)",
                 "ms": wms, "calls": wsteps, "tokens_per_s": T / (wms * 1e-3),
-                "alg_flops": wfl, "fp32_frac": wfl / (wms * 1e-3) / PEAK_FP32,
+                "alg_bytes": wb, "hbm_frac": wb / (wms * 1e-3) / PEAK_HBM,
+                "alg_flops": wfl, "mfma_frac_alg": wfl / (wms * 1e-3) / PEAK_BF16,
                 "workspace_GB": wsw.numel() / 1e9}
         del winp, ow, fw, wsw
 

@@ -137,15 +137,10 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
   float* rc = rec + ((size_t)lc * H + h) * R::floats;
   if (threadIdx.x < BC)
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
-  // A_ij = beta_i sum_c k_ic k_jc e^{b_ic - b_jc} (j < i) and P_ij = sum_c q_ic k_jc e^{..} (j <= i).
-  // Rows pi and 63 - pi form a pair with 65 entries j <= i between them; TPP threads share a
-  // pair, thread jq taking the entries v = jq + TPP u (v <= pi: row pi, j = v; else row
-  // 63 - pi, j = v - pi - 1), so every thread has the same work and no entry is masked off.
-  constexpr int TPP = NTP / (BC / 2), VPT = (BC + 1 + TPP - 1) / TPP;
-  const int pi = threadIdx.x / TPP, jq = threadIdx.x % TPP, i2 = BC - 1 - pi;
-  float a[VPT], p[VPT];
-#pragma unroll
-  for (int u = 0; u < VPT; ++u) a[u] = p[u] = 0.f;
+  // A_ij = beta_i sum_c k_ic k_jc e^{b_ic - b_jc} (j < i) and P_ij = sum_c q_ic k_jc e^{..} (j <= i),
+  // summed over the parts (off-diagonal 16 x 16 blocks on the fp32 matrix cores)
+  PairAcc acc;
+  pair_acc_init<NTP>(acc);
   for (int c0 = 0; c0 < K; c0 += KC) {
     load_rows<KC, LQ, NTP, GT, K>(sQ, q, ch.tok, ch.len, H, h, c0);
     load_rows<KC, LK, NTP, GT, K>(sK, k, ch.tok, ch.len, H, h, c0);
@@ -161,42 +156,12 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
       rc[R::oKt + r * K + c0 + cc] = sK[r * LK + cc] * exp2_f(bl - br);
     }
     if (threadIdx.x < KC) rc[R::oGam + c0 + threadIdx.x] = exp2_f(sB[(BC - 1) * LK + threadIdx.x]);
-    for (int c4 = 0; c4 < KC; c4 += 4) {
-      const f32x4 q1 = *reinterpret_cast<const f32x4*>(sQ + pi * LQ + c4);
-      const f32x4 k1 = *reinterpret_cast<const f32x4*>(sK + pi * LK + c4);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(sB + pi * LK + c4);
-      const f32x4 q2 = *reinterpret_cast<const f32x4*>(sQ + i2 * LQ + c4);
-      const f32x4 k2 = *reinterpret_cast<const f32x4*>(sK + i2 * LK + c4);
-      const f32x4 b2 = *reinterpret_cast<const f32x4*>(sB + i2 * LK + c4);
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int v = jq + TPP * u;
-        if (v <= BC) {
-          const bool lo = v <= pi;
-          const int j = lo ? v : v - pi - 1;
-          const f32x4 qi = lo ? q1 : q2, ki = lo ? k1 : k2, bi = lo ? b1 : b2;
-          const f32x4 kj = *reinterpret_cast<const f32x4*>(sK + j * LK + c4);
-          const f32x4 bj = *reinterpret_cast<const f32x4*>(sB + j * LK + c4);
-          f32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = kj[e] * exp2_f(bi[e] - bj[e]);
-          a[u] += dot4(ki, w);
-          p[u] += dot4(qi, w);
-        }
-      }
-    }
+    pair_acc_part<KC, LK, LQ>(acc, sQ, sK, sB);
     lds_barrier();  // the part's reads done before the next part overwrites it
   }
-#pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-    const int v = jq + TPP * u;
-    if (v <= BC) {
-      const bool lo = v <= pi;
-      const int i = lo ? pi : i2, j = lo ? v : v - pi - 1;
-      sA[i * 68 + j] = j < i ? sBeta[i] * a[u] : 0.f;
-      rc[R::oP + i * BC + j] = p[u];
-    }
-  }
+  // (the solve reads A below the diagonal only)
+  pair_acc_out(acc, [&](int i, int j, float x) { sA[i * 68 + j] = sBeta[i] * x; },
+               [&](int i, int j, float x) { rc[R::oP + i * BC + j] = x; });
   for (int e = threadIdx.x; e < BC * BC; e += NTP)  // P's upper triangle
     if (e % BC > e / BC) rc[R::oP + e] = 0.f;
   lds_barrier();

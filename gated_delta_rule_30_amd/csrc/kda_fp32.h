@@ -213,6 +213,118 @@ __device__ __forceinline__ void cumsum_log2(float* sB) {
 }
 
 
+// A_ij = sum_c k_ic k_jc e^{b_ic - b_jc} (j < i) and P_ij = sum_c q_ic k_jc e^{b_ic - b_jc}
+// (j <= i) of a 64-token chunk, summed over the key channels part by part, with NTB = 512
+// threads. The six 16 x 16 blocks below the diagonal (I > J) run on the fp32 matrix cores, one
+// block per wave (waves 0-5), with the decay split at the end of token block I - 1:
+// e^{b_i - b_j} = e^{b_i - e} e^{e - b_j}, both factors at most 1 for log alpha <= 0 (rows of
+// block I follow that token, rows of block J precede it). The 4 x 136 entries of the diagonal
+// blocks are summed pairwise, e^{b_i - b_j} <= 1, one or two entries per thread.
+struct PairAcc {
+  f32x4 a, p;      // this wave's off-diagonal block: lane (m, g) holds rows 4g + r, column m
+  float da[2], dp[2];  // this thread's diagonal entries
+  int dI[2], di[2], dj[2];
+};
+
+// the off-diagonal block of wave w < 6: (I, J) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+__device__ __forceinline__ int pair_block_I(int w) { return w < 1 ? 1 : w < 3 ? 2 : 3; }
+__device__ __forceinline__ int pair_block_J(int w) { return w < 1 ? 0 : w < 3 ? w - 1 : w - 3; }
+
+template <int NTB>
+__device__ __forceinline__ void pair_acc_init(PairAcc& acc) {
+  static_assert(NTB == 512, "eight waves");
+  acc.a = acc.p = f32x4{0.f, 0.f, 0.f, 0.f};
+  // diagonal entry d in [0, 544): block d / 136, (i, j) the (d % 136)-th of j <= i < 16
+  const int tid = threadIdx.x;
+  const int d2 = (tid >= 384 && tid < 416) ? 512 + tid - 384 : -1;  // waves 6-7 take the rest
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int d = t == 0 ? tid : d2;
+    acc.da[t] = acc.dp[t] = 0.f;
+    acc.dI[t] = -1;
+    if (d >= 0) {
+      const int I = d / 136;
+      int r = d % 136, i = 0;
+      while (r > i) {
+        r -= i + 1;
+        ++i;
+      }
+      acc.dI[t] = I;
+      acc.di[t] = 16 * I + i;
+      acc.dj[t] = 16 * I + r;
+    }
+  }
+}
+
+// One part of KP channels: q in sQ ([64][LQ] fp32), k and b log2 e in sK, sB ([64][LK]); rows
+// past the chunk hold q = k = 0 and b at its last value.
+template <int KP, int LK, int LQ = LK>
+__device__ __forceinline__ void pair_acc_part(PairAcc& acc, const float* sQ, const float* sK,
+                                              const float* sB) {
+  const int w = threadIdx.x >> 6, m = threadIdx.x & 15, g = (threadIdx.x >> 4) & 3;
+  if (w < 6) {
+    const int I = pair_block_I(w), J = pair_block_J(w);
+    const float* rowI = sK + (16 * I + m) * LK;
+    const float* rowQ = sQ + (16 * I + m) * LQ;
+    const float* bI = sB + (16 * I + m) * LK;
+    const float* bE = sB + (16 * I - 1) * LK;
+    const float* rowJ = sK + (16 * J + m) * LK;
+    const float* bJ = sB + (16 * J + m) * LK;
+#pragma unroll 4
+    for (int c = g; c < KP; c += 4) {
+      const float e = bE[c];
+      const float fi = exp2_f(bI[c] - e), fj = exp2_f(e - bJ[c]);
+      const float kj = rowJ[c] * fj;
+      acc.a = mfma4(rowI[c] * fi, kj, acc.a);
+      acc.p = mfma4(rowQ[c] * fi, kj, acc.p);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (acc.dI[t] < 0) continue;
+    const float* ki = sK + acc.di[t] * LK;
+    const float* qi = sQ + acc.di[t] * LQ;
+    const float* bi = sB + acc.di[t] * LK;
+    const float* kj = sK + acc.dj[t] * LK;
+    const float* bj = sB + acc.dj[t] * LK;
+    float sa = 0.f, sp = 0.f;
+#pragma unroll 2
+    for (int c = 0; c < KP; c += 4) {
+      const f32x4 k1 = *reinterpret_cast<const f32x4*>(ki + c), q1 = *reinterpret_cast<const f32x4*>(qi + c);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(bi + c), k2 = *reinterpret_cast<const f32x4*>(kj + c);
+      const f32x4 b2 = *reinterpret_cast<const f32x4*>(bj + c);
+      f32x4 x;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = k2[u] * exp2_f(b1[u] - b2[u]);
+      sa += dot4(k1, x);
+      sp += dot4(q1, x);
+    }
+    acc.da[t] += sa;
+    acc.dp[t] += sp;
+  }
+}
+
+// The sums out: outA(i, j, x) for every j < i and outP(i, j, x) for every j <= i (each entry
+// once; entries above the diagonal are not visited).
+template <typename FA, typename FP>
+__device__ __forceinline__ void pair_acc_out(const PairAcc& acc, FA&& outA, FP&& outP) {
+  const int w = threadIdx.x >> 6, m = threadIdx.x & 15, g = (threadIdx.x >> 4) & 3;
+  if (w < 6) {
+    const int I = pair_block_I(w), J = pair_block_J(w);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      outA(16 * I + 4 * g + r, 16 * J + m, acc.a[r]);
+      outP(16 * I + 4 * g + r, 16 * J + m, acc.p[r]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (acc.dI[t] < 0) continue;
+    if (acc.dj[t] < acc.di[t]) outA(acc.di[t], acc.dj[t], acc.da[t]);
+    outP(acc.di[t], acc.dj[t], acc.dp[t]);
+  }
+}
+
 // the token range of sequence n
 __device__ __forceinline__ void seq_range(const int32_t* cu, int N, int64_t T, int n, int64_t* s0,
                                           int64_t* s1) {

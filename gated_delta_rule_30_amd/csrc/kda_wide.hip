@@ -39,60 +39,7 @@ struct WRec {
   static constexpr int floats = (oGam + KW + 63) / 64 * 64;
 };
 
-// A and P of a chunk are summed over its key channels in parts of KQ: rows pi and 63 - pi form
-// a pair with 65 entries j <= i; TPP threads share a pair, thread jq taking v = jq + TPP u
-// (v <= pi: row pi, j = v; else row 63 - pi, j = v - pi - 1), so every thread has the same work
-constexpr int TPP = NTP / (BC / 2), VPT = (BC + 1 + TPP - 1) / TPP;
 constexpr int LKQ = KQ + 4;  // LDS row of a channel part
-
-// a[u] += sum_c k_ic k_jc e^{b_ic - b_jc} and p[u] += sum_c q_ic k_jc e^{b_ic - b_jc} over the
-// part's channels (sQ, sK: q and k; sB: b log2 e; all [64][LKQ]); every factor is at most 1
-__device__ __forceinline__ void pair_sums(const float* sQ, const float* sK, const float* sB,
-                                          float (&a)[VPT], float (&p)[VPT]) {
-  const int pi = threadIdx.x / TPP, jq = threadIdx.x % TPP, i2 = BC - 1 - pi;
-  for (int c4 = 0; c4 < KQ; c4 += 4) {
-    const f32x4 q1 = *reinterpret_cast<const f32x4*>(sQ + pi * LKQ + c4);
-    const f32x4 k1 = *reinterpret_cast<const f32x4*>(sK + pi * LKQ + c4);
-    const f32x4 b1 = *reinterpret_cast<const f32x4*>(sB + pi * LKQ + c4);
-    const f32x4 q2 = *reinterpret_cast<const f32x4*>(sQ + i2 * LKQ + c4);
-    const f32x4 k2 = *reinterpret_cast<const f32x4*>(sK + i2 * LKQ + c4);
-    const f32x4 b2 = *reinterpret_cast<const f32x4*>(sB + i2 * LKQ + c4);
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int v = jq + TPP * u;
-      if (v <= BC) {
-        const bool lo = v <= pi;
-        const int j = lo ? v : v - pi - 1;
-        const f32x4 qi = lo ? q1 : q2, ki = lo ? k1 : k2, bi = lo ? b1 : b2;
-        const f32x4 kj = *reinterpret_cast<const f32x4*>(sK + j * LKQ + c4);
-        const f32x4 bj = *reinterpret_cast<const f32x4*>(sB + j * LKQ + c4);
-        f32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = kj[e] * exp2_f(bi[e] - bj[e]);
-        a[u] += dot4(ki, w);
-        p[u] += dot4(qi, w);
-      }
-    }
-  }
-}
-
-// The summed entries out: A (beta-scaled, strictly lower, zero elsewhere) into sA [64][68],
-// and P_ij (j <= i) to outp(i, j, x)
-template <typename F>
-__device__ __forceinline__ void pairs_out(float* sA, const float* sBeta, const float (&a)[VPT],
-                                          const float (&p)[VPT], F&& outp) {
-  const int pi = threadIdx.x / TPP, jq = threadIdx.x % TPP, i2 = BC - 1 - pi;
-#pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-    const int v = jq + TPP * u;
-    if (v <= BC) {
-      const bool lo = v <= pi;
-      const int i = lo ? pi : i2, j = lo ? v : v - pi - 1;
-      sA[i * 68 + j] = j < i ? sBeta[i] * a[u] : 0.f;
-      outp(i, j, p[u]);
-    }
-  }
-}
 
 // T = (I + A)^{-1} for the strictly lower A in sA [64][68], by forward substitution, one column
 // per thread of wave 0; T overwrites A after the wave's last read of it (a wave's LDS accesses
@@ -142,10 +89,9 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
   float* rc = rec + ((size_t)lc * H + h) * R::floats;
   if (threadIdx.x < BC)
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(gtok + threadIdx.x) * (int64_t)H + h]) : 0.f;
-  // A and P, summed over the four quarters
-  float a[VPT], p[VPT];
-#pragma unroll
-  for (int u = 0; u < VPT; ++u) a[u] = p[u] = 0.f;
+  // A and P, summed over the four quarters (off-diagonal 16 x 16 blocks on the matrix cores)
+  PairAcc acc;
+  pair_acc_init<NTP>(acc);
   for (int hh = 0; hh < KW / KQ; ++hh) {
     const int c0 = hh * KQ;
     load_rows<KQ, LK, NTP, GT, KW>(sQ, q, gtok, ch.len, H, h, c0);
@@ -162,10 +108,12 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
       rc[R::oKt + r * KW + c0 + cc] = sK[r * LK + cc] * exp2_f(bl - br);
     }
     if (threadIdx.x < KQ) rc[R::oGam + c0 + threadIdx.x] = exp2_f(sB[(BC - 1) * LK + threadIdx.x]);
-    pair_sums(sQ, sK, sB, a, p);
+    pair_acc_part<KQ, LK>(acc, sQ, sK, sB);
     lds_barrier();  // the quarter's reads done before the next quarter overwrites it
   }
-  pairs_out(sA, sBeta, a, p, [&](int i, int j, float x) { rc[R::oP + i * BC + j] = x; });
+  // (the solve reads A below the diagonal only)
+  pair_acc_out(acc, [&](int i, int j, float x) { sA[i * 68 + j] = sBeta[i] * x; },
+               [&](int i, int j, float x) { rc[R::oP + i * BC + j] = x; });
   for (int e = threadIdx.x; e < BC * BC; e += NTP)  // P's upper triangle
     if (e % BC > e / BC) rc[R::oP + e] = 0.f;
   lds_barrier();
@@ -237,9 +185,8 @@ __global__ __launch_bounds__(NTP, 4) void rec256_kernel(Rec256Params p) {
     *reinterpret_cast<bf16x8*>(recM + elem) = f;
   };
   if (tid < BC) sBeta[tid] = tid < len ? to_f32(beta[(tok + tid) * H + h]) : 0.f;
-  float a[VPT], pp[VPT];
-#pragma unroll
-  for (int u = 0; u < VPT; ++u) a[u] = pp[u] = 0.f;
+  PairAcc acc;
+  pair_acc_init<NTP>(acc);
   for (int hh = 0; hh < KW / KQ; ++hh) {
     const int c0 = hh * KQ;
     load_rows<KQ, LKQ, NTP, bf16, KW>(sQ, q, tok, len, H, h, c0);
@@ -264,13 +211,18 @@ __global__ __launch_bounds__(NTP, 4) void rec256_kernel(Rec256Params p) {
       put(R::oKt + slot_elem<bf16>(4 * hh + ft, fsl, lane, CHUNK), y);
     }
     if (tid < KQ) recGam[c0 + tid] = exp2_f(sB[(BC - 1) * LKQ + tid]);
-    pair_sums(sQ, sK, sB, a, pp);
+    pair_acc_part<KQ, LKQ>(acc, sQ, sK, sB);
     lds_barrier();  // the part's reads done before the next part overwrites it
   }
-  // A into sA; P (zero above the diagonal) into sQ, then its fragments
-  for (int el = tid; el < BC * BC; el += NTP) sQ[(el / BC) * LKQ + el % BC] = 0.f;
+  // A (beta-scaled, zero on and above the diagonal) into sA; P (zero above the diagonal) into
+  // sQ, then its fragments
+  for (int el = tid; el < BC * BC; el += NTP) {
+    sQ[(el / BC) * LKQ + el % BC] = 0.f;
+    sA[(el / BC) * 68 + el % BC] = 0.f;
+  }
   lds_barrier();
-  pairs_out(sA, sBeta, a, pp, [&](int i, int j, float x) { sQ[i * LKQ + j] = x; });
+  pair_acc_out(acc, [&](int i, int j, float x) { sA[i * 68 + j] = sBeta[i] * x; },
+               [&](int i, int j, float x) { sQ[i * LKQ + j] = x; });
   lds_barrier();
   {
     float x[8];
