@@ -165,26 +165,10 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
   for (int e = threadIdx.x; e < BC * BC; e += NTP)  // P's upper triangle
     if (e % BC > e / BC) rc[R::oP + e] = 0.f;
   lds_barrier();
-  // T = (I + A)^{-1} by forward substitution, one column per thread of wave 0; T overwrites A
-  // after the wave's last read of it (a wave's LDS accesses take effect in program order)
-  if (threadIdx.x < BC) {
-    const int m = threadIdx.x;
-    float x[BC];
-#pragma unroll
-    for (int i = 0; i < BC; ++i) {
-      // four partial sums: the row's dot product is not one chain of dependent FMAs
-      float ps[4] = {i == m ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < i; ++j) ps[j & 3] -= sA[i * 68 + j] * x[j];
-      x[i] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    }
-#pragma unroll
-    for (int i = 0; i < BC; ++i) {
-      sT[i * 68 + m] = x[i];
-      rc[R::oT + i * BC + m] = x[i];
-    }
-  }
-  lds_barrier();
+  // T = (I + A)^{-1} over A (blocked: diagonal blocks by substitution, the rest on the matrix
+  // cores), then to the record
+  unit_lower_inverse_blocked<NTP>(sT);
+  for (int e = threadIdx.x; e < BC * BC; e += NTP) rc[R::oT + e] = sT[(e / BC) * 68 + e % BC];
   // W = T diag(beta) (k e^b), part by part
   for (int c0 = 0; c0 < K; c0 += KC) {
     load_rows<KC, LK, NTP, GT, K>(sB, g, ch.tok, ch.len, H, h, c0);

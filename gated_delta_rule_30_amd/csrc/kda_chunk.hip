@@ -1246,7 +1246,7 @@ struct SplitShape {
 };
 
 template <int K, typename MT>
-__global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_split_kernel(StateParams p) {
+__global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per_eu(K > 128 ? 2 : 1, K > 128 ? 2 : 1))) void state_split_kernel(StateParams p) {
   using SH = StateShape<K, MT>;
   using SS = SplitShape<K, MT>;
   constexpr int NW = SS::NW;
@@ -1394,8 +1394,11 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
         U[tt] = M::mma(ldf(rc0, off), Vf[s], U[tt]);
       });
     }
-    f32x4 gnext[HKT], gcur[HKT];
-    load_gam(rc0, gnext);
+    // gamma of this wave's rows: a chunk ahead, or (four waves, whose registers are scarcer) at
+    // the chunk's start, NA operations before its first use
+    constexpr bool GAHEAD = NW == 2;
+    f32x4 gnext[GAHEAD ? HKT : 1], gcur[HKT];
+    if constexpr (GAHEAD) load_gam(rc0, gnext);
     __builtin_amdgcn_sched_barrier(0);
     // ring slot P * NF + j holds operation j of the next chunk of parity P (two chunks in
     // flight), or slot j operation j of the next chunk (one chunk in flight)
@@ -1421,9 +1424,13 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
     auto chunk = [&](auto PARc, const int k) {
       constexpr int par = decltype(PARc)::value;
       const rsrc_t ro = rows_rsrc(go, k);
+      if constexpr (GAHEAD) {
 #pragma unroll
-      for (int i = 0; i < HKT; ++i) gcur[i] = gnext[i];
-      load_gam(rc1, gnext);
+        for (int i = 0; i < HKT; ++i) gcur[i] = gnext[i];
+        load_gam(rc1, gnext);
+      } else {
+        load_gam(rc0, gcur);
+      }
       __builtin_amdgcn_sched_barrier(0);
 
       frag Sb[HKS], Db[NTS];

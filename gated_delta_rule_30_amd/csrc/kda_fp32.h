@@ -325,6 +325,68 @@ __device__ __forceinline__ void pair_acc_out(const PairAcc& acc, FA&& outA, FP&&
   }
 }
 
+// T = (I + A)^{-1} in place for the strictly lower 64 x 64 A in sA (row stride 68; on return
+// zero above the diagonal), with NTB = 512 threads: the four diagonal 16 x 16 blocks by forward
+// substitution (waves 0-3, one column per lane of the first 16), then the blocks below by
+// distance d = I - J, one block per wave, on the fp32 matrix cores:
+// T_IJ = -T_II (sum_{M=J}^{I-1} A_IM T_MJ). Until the end T_IJ (I > J) sits in the unused upper
+// block (J, I), so that T_MJ (M >= J) is always at rows 16J.., columns 16M.. and the A blocks
+// below stay intact; a last pass moves them down. LDS-only barriers between the steps.
+template <int NTB>
+__device__ __forceinline__ void unit_lower_inverse_blocked(float* sA) {
+  static_assert(NTB == 512, "eight waves");
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int m = lane & 15, g = lane >> 4;
+  if (w < 4 && lane < 16) {  // the wave's lanes run in step: every read of A_ww precedes the writes
+    float* a = sA + (16 * w) * 68 + 16 * w;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float ps = r == lane ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < r; ++j) ps -= a[r * 68 + j] * x[j];
+      x[r] = ps;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[r * 68 + lane] = x[r];
+  }
+  lds_barrier();
+  for (int d = 1; d < 4; ++d) {
+    if (w < 4 - d) {
+      const int J = w, I = w + d;
+      float* tij = sA + (16 * J) * 68 + 16 * I;  // T_IJ's slot: the upper block (J, I)
+      // X = sum_M A_IM T_MJ: lane (m, g) ends with rows 4g + r of column m
+      f32x4 X = {0.f, 0.f, 0.f, 0.f};
+      for (int M = J; M < I; ++M) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          X = mfma4(sA[(16 * I + m) * 68 + 16 * M + 4 * s + g],
+                    sA[(16 * J + 4 * s + g) * 68 + 16 * M + m], X);
+      }
+      // X through the slot (the wave's LDS accesses take effect in order), then T_IJ = -T_II X
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tij[(4 * g + r) * 68 + m] = X[r];
+      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        Y = mfma4(sA[(16 * I + m) * 68 + 16 * I + 4 * s + g], tij[(4 * s + g) * 68 + m], Y);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tij[(4 * g + r) * 68 + m] = -Y[r];
+    }
+    lds_barrier();
+  }
+  // T_IJ down to its place, zeros above the diagonal (each element moved by one thread)
+  for (int e = tid; e < BC * BC; e += NTB) {
+    const int r = e / BC, c = e % BC;
+    if ((c >> 4) > (r >> 4)) {
+      const int J = r >> 4, I = c >> 4;
+      sA[(16 * I + (r & 15)) * 68 + 16 * J + (c & 15)] = sA[r * 68 + c];
+      sA[r * 68 + c] = 0.f;
+    }
+  }
+  lds_barrier();
+}
+
 // the token range of sequence n
 __device__ __forceinline__ void seq_range(const int32_t* cu, int N, int64_t T, int n, int64_t* s0,
                                           int64_t* s1) {

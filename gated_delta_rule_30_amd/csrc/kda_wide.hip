@@ -41,26 +41,6 @@ struct WRec {
 
 constexpr int LKQ = KQ + 4;  // LDS row of a channel part
 
-// T = (I + A)^{-1} for the strictly lower A in sA [64][68], by forward substitution, one column
-// per thread of wave 0; T overwrites A after the wave's last read of it (a wave's LDS accesses
-// take effect in program order). The caller's barriers order it with the other waves.
-__device__ __forceinline__ void unit_lower_inverse(float* sA) {
-  if (threadIdx.x < BC) {
-    const int m = threadIdx.x;
-    float x[BC];
-#pragma unroll
-    for (int r = 0; r < BC; ++r) {
-      // four partial sums: the row's dot product is not one chain of dependent FMAs
-      float ps[4] = {r == m ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < r; ++j) ps[j & 3] -= sA[r * 68 + j] * x[j];
-      x[r] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    }
-#pragma unroll
-    for (int r = 0; r < BC; ++r) sA[r * 68 + m] = x[r];
-  }
-}
-
 }  // namespace
 
 // The chunks [cb, ...) of one segment, records indexed from cb. MT: v; GT: q, k, log alpha and
@@ -117,8 +97,7 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
   for (int e = threadIdx.x; e < BC * BC; e += NTP)  // P's upper triangle
     if (e % BC > e / BC) rc[R::oP + e] = 0.f;
   lds_barrier();
-  unit_lower_inverse(sA);  // T = (I + A)^{-1} into sT (= sA)
-  lds_barrier();
+  unit_lower_inverse_blocked<NTP>(sA);  // T = (I + A)^{-1} into sT (= sA)
   // W = T diag(beta) (k e^b), quarter by quarter
   for (int hh = 0; hh < KW / KQ; ++hh) {
     const int c0 = hh * KQ;
@@ -196,18 +175,30 @@ __global__ __launch_bounds__(NTP, 4) void rec256_kernel(Rec256Params p) {
     cumsum_log2<KQ, LKQ, NTP>(sB);
     lds_barrier();
     // Qe = q e^b (token tile ft, channel step 2 hh + fsl) and Ktilde^T = (k e^{b_last - b})^T
-    // (channel tile 4 hh + ft, token step fsl); rows past len hold q = k = 0
+    // (channel tile 4 hh + ft, token step fsl); rows past len hold q = k = 0. beta k e^b goes
+    // to the slot of W that this thread fills from it later (the W pass reads it back).
     {
       float x[8], y[8];
-      const int r = 16 * ft + m, c = 16 * ft + m;
+      const int r = 16 * ft + m;
+#pragma unroll
+      for (int el = 0; el < 8; ++el) {
+        const int cq = 32 * fsl + kk(el);
+        const float eb = exp2_f(sB[r * LKQ + cq]);
+        x[el] = sQ[r * LKQ + cq] * eb;
+        y[el] = sK[r * LKQ + cq] * eb * sBeta[r];
+      }
+      put(R::oQ + slot_elem<bf16>(ft, 2 * hh + fsl, lane, KW), x);
+      put(R::oW + slot_elem<bf16>(ft, 2 * hh + fsl, lane, KW), y);
+    }
+    {
+      float y[8];
+      const int c = 16 * ft + m;
       const float bl = sB[(BC - 1) * LKQ + c];
 #pragma unroll
       for (int el = 0; el < 8; ++el) {
-        const int cq = 32 * fsl + kk(el), rk = 32 * fsl + kk(el);
-        x[el] = sQ[r * LKQ + cq] * exp2_f(sB[r * LKQ + cq]);
+        const int rk = 32 * fsl + kk(el);
         y[el] = sK[rk * LKQ + c] * exp2_f(bl - sB[rk * LKQ + c]);
       }
-      put(R::oQ + slot_elem<bf16>(ft, 2 * hh + fsl, lane, KW), x);
       put(R::oKt + slot_elem<bf16>(4 * hh + ft, fsl, lane, CHUNK), y);
     }
     if (tid < KQ) recGam[c0 + tid] = exp2_f(sB[(BC - 1) * LKQ + tid]);
@@ -230,33 +221,33 @@ __global__ __launch_bounds__(NTP, 4) void rec256_kernel(Rec256Params p) {
     for (int el = 0; el < 8; ++el) x[el] = sQ[(16 * ft + m) * LKQ + 32 * fsl + kk(el)];
     put(R::oPb + slot_elem<bf16>(ft, fsl, lane, CHUNK), x);
   }
-  unit_lower_inverse(sA);  // T into sA
-  lds_barrier();
+  float* sT = sA;
+  unit_lower_inverse_blocked<NTP>(sT);  // T over A
   {  // T' = T diag(beta) (zero above the diagonal)
     float x[8];
 #pragma unroll
     for (int el = 0; el < 8; ++el) {
       const int c = 32 * fsl + kk(el);
-      x[el] = sA[(16 * ft + m) * 68 + c] * sBeta[c];
+      x[el] = sT[(16 * ft + m) * 68 + c] * sBeta[c];
     }
     put(R::oTb + slot_elem<bf16>(ft, fsl, lane, CHUNK), x);
   }
-  // -W = -T diag(beta) (k e^b), part by part (token tile ft, channel step 2 hh + fsl)
+  // -W = -T (beta k e^b), part by part (token tile ft, channel step 2 hh + fsl), from the
+  // part's beta k e^b this thread left in its W slot (and in sB through the other threads');
+  // the slot's store has completed before its load (all memory counters waited out)
+  __builtin_amdgcn_s_waitcnt(0);
   for (int hh = 0; hh < KW / KQ; ++hh) {
-    const int c0 = hh * KQ;
-    load_rows<KQ, LKQ, NTP, bf16, KW>(sB, g, tok, len, H, h, c0);
+    {
+      const bf16x8 f = *reinterpret_cast<const bf16x8*>(recM + R::oW + slot_elem<bf16>(ft, 2 * hh + fsl, lane, KW));
+#pragma unroll
+      for (int el = 0; el < 8; ++el) sB[(16 * ft + m) * LKQ + 32 * fsl + kk(el)] = (float)f[el];
+    }
     lds_barrier();
-    cumsum_log2<KQ, LKQ, NTP>(sB);
-    lds_barrier();
-    mul_rows_exp2<KQ, LKQ, NTP, bf16, KW>(sB, k, tok, len, H, h, c0);
-    lds_barrier();
-    for (int el = tid; el < BC * KQ; el += NTP) sB[(el / KQ) * LKQ + el % KQ] *= sBeta[el / KQ];
-    lds_barrier();
-    mmf<KQ, BC, false, false, 68, LKQ, NTP>(sA, sB, [&](int r, int cc, float x) { sQ[r * LKQ + cc] = x; });
+    mmf<KQ, BC, false, false, 68, LKQ, NTP>(sT, sB, [&](int r, int cc, float x) { sK[r * LKQ + cc] = x; });
     lds_barrier();
     float x[8];
 #pragma unroll
-    for (int el = 0; el < 8; ++el) x[el] = -sQ[(16 * ft + m) * LKQ + 32 * fsl + kk(el)];
+    for (int el = 0; el < 8; ++el) x[el] = -sK[(16 * ft + m) * LKQ + 32 * fsl + kk(el)];
     put(R::oW + slot_elem<bf16>(ft, 2 * hh + fsl, lane, KW), x);
     lds_barrier();
   }
