@@ -35,15 +35,18 @@ using namespace fp32;
 
 namespace {
 
+// Every per-(chunk, head) array of a segment (record, scratch, S_c, X_c, Delta, dDelta) is
+// head-major: entry h * (chunks of the segment) + chunk. A chain then walks through adjacent
+// entries, so its reads and writes stay within a few pages instead of one new page per chunk.
 // per-(chunk, head) fp32 record of the backward, row-major blocks
 template <int K, int V>
 struct BRec {
   static constexpr int oT = 0;                 // T = (I + A)^{-1}        [64][64]
-  static constexpr int oP = oT + BC * BC;      // P (lower incl.)        [64][64]
+  static constexpr int oP = oT + BC * BC;      // P^T (upper incl.)      [64][64]
   static constexpr int oW = oP + BC * BC;      // W                       [64][K]
   static constexpr int oKt = oW + BC * K;      // Kt = k e^{b_last - b}   [64][K]
-  static constexpr int oQe = oKt + BC * K;     // Qe = q e^b              [64][K]
-  static constexpr int oU = oQe + BC * K;      // U                       [64][V]
+  static constexpr int oQe = oKt + BC * K;     // Qe^T, Qe = q e^b        [K][64]
+  static constexpr int oU = oQe + BC * K;      // U^T                     [V][64]
   static constexpr int oGam = oU + BC * V;     // gamma = e^{b_last}      [K]
   static constexpr int floats = (oGam + K + 63) / 64 * 64;
 };
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
   const int lc = blockIdx.x, c = cb + lc, h = blockIdx.y;  // chunk of the segment, of the call
   if (c >= *ntot) return;
   const ChunkRow ch = chunks[c];
-  float* rc = rec + ((size_t)lc * H + h) * R::floats;
+  float* rc = rec + ((size_t)h * gridDim.x + lc) * R::floats;
   if (threadIdx.x < BC)
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
   // A_ij = beta_i sum_c k_ic k_jc e^{b_ic - b_jc} (j < i) and P_ij = sum_c q_ic k_jc e^{..} (j <= i),
@@ -152,8 +155,12 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
     for (int e = threadIdx.x; e < BC * KC; e += NTP) {
       const int r = e / KC, cc = e % KC;
       const float br = sB[r * LK + cc], bl = sB[(BC - 1) * LK + cc];
-      rc[R::oQe + r * K + c0 + cc] = sQ[r * LQ + cc] * exp2_f(br);
       rc[R::oKt + r * K + c0 + cc] = sK[r * LK + cc] * exp2_f(bl - br);
+    }
+    for (int e = threadIdx.x; e < BC * KC; e += NTP) {  // transposed: token index fastest
+      const int r = e % BC, cc = e / BC;
+      const float br = sB[r * LK + cc];
+      rc[R::oQe + (c0 + cc) * BC + r] = sQ[r * LQ + cc] * exp2_f(br);
     }
     if (threadIdx.x < KC) rc[R::oGam + c0 + threadIdx.x] = exp2_f(sB[(BC - 1) * LK + threadIdx.x]);
     pair_acc_part<KC, LK, LQ>(acc, sQ, sK, sB);
@@ -161,9 +168,9 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
   }
   // (the solve reads A below the diagonal only)
   pair_acc_out(acc, [&](int i, int j, float x) { sA[i * 68 + j] = sBeta[i] * x; },
-               [&](int i, int j, float x) { rc[R::oP + i * BC + j] = x; });
-  for (int e = threadIdx.x; e < BC * BC; e += NTP)  // P's upper triangle
-    if (e % BC > e / BC) rc[R::oP + e] = 0.f;
+               [&](int i, int j, float x) { rc[R::oP + j * BC + i] = x; });
+  for (int e = threadIdx.x; e < BC * BC; e += NTP)  // below P^T's diagonal
+    if (e / BC > e % BC) rc[R::oP + e] = 0.f;
   lds_barrier();
   // T = (I + A)^{-1} over A (blocked: diagonal blocks by substitution, the rest on the matrix
   // cores), then to the record
@@ -191,307 +198,390 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
     for (int e = threadIdx.x; e < BC * VC; e += NTP) sQ[(e / VC) * LV + e % VC] *= sBeta[e / VC];
     lds_barrier();
     mmf<VC, BC, false, false, 68, LV, NTP>(sT, sQ, [&](int r, int cc, float x) {
-      rc[R::oU + r * V + c0 + cc] = x;
+      rc[R::oU + (c0 + cc) * BC + r] = x;
     });
     lds_barrier();
   }
 }
 
 // ---------------------------------------------------------------- the chains
-constexpr int NTR = 512;  // threads of a chain workgroup: 8 waves
 // One workgroup per (sequence, head, 16 value columns); the slices of one chain share
-// blockIdx % 8 (one XCD's L2) with blockIdx = slice * chains8 + chain. A chunk's record
-// blocks are loaded whole into registers (16-byte pieces, all in flight) while the chunk
-// before is computed, then stored to LDS; the chunk's products read LDS only. The loop body
-// has no branch around those loads (the next chunk's index is clamped to the last), so the
-// compiler neither sinks them to their use nor waits for them early, and its barriers order
-// LDS only (a full __syncthreads would also wait for the loads in flight).
-
+// blockIdx % 8 (one XCD's L2) with blockIdx = slice * chains8 + chain.
+// Wave v of the chain_waves<K>() waves holds the key-channel rows [16 v HCT, 16 (v + 1) HCT)
+// of the chain's state (S forwards, X backwards) in registers, as 16 x 16 matrix-core result
+// tiles: lane (n, g) = (lane % 16, lane / 16) holds rows 16 t + 4 g + r (r = 0..3) of column
+// n. Such a tile is, unchanged, the B operand of four 16x16x4 steps in which lane group g
+// supplies the reduction index 16 t + 4 g + r at step r; the A operand of those steps for
+// output row i is then the four values at those indices: one 16-byte load along a row of a
+// row-major block, or four loads along a column. So the state and Delta (or dDelta) stay in
+// registers; the only exchange per chunk is that of the Delta partials (each wave sums over
+// its own rows of the state) through LDS, with one barrier. A chunk's record values load
+// while the chunk before is computed (two register sets, each refilled two chunks ahead).
+template <int K>
+constexpr int chain_waves() { return K >= 64 ? 4 : 2; }
+// A compiler-only fence: memory operations are not moved across it (no wait is issued).
+__device__ __forceinline__ void fence_compiler() { asm volatile("" ::: "memory"); }
 
 // Forward in time: S_c (chunk start) and Delta = U - W S per chunk, S' = diag(gamma) S + Kt^T
-// Delta. NTR threads: waves 0-3 form the four 16-row tiles of Delta, wave w the 16-row tiles
-// w, w + 8, .. of S', with matrix-core steps over LDS operands; two register sets hold the
-// records of the next two chunks.
-// The chunks [cb, ce) of one segment (records, S_c and Delta indexed from cb). A sequence that
-// began before the segment starts from ck_in (its state at chunk cb, [H][K][V]); one that goes
-// on past it leaves its state at chunk ce in ck_out (when given). STORE = false runs the chain
-// for that state alone.
+// Delta. The chunks [cb, ce) of one segment (records, S_c and Delta indexed from cb). A
+// sequence that began before the segment starts from ck_in (its state at chunk cb,
+// [H][K][V]); one that goes on past it leaves its state at chunk ce in ck_out (when given).
+// STORE = false runs the chain for that state alone.
 template <int K, int V, bool STORE>
-__global__ __launch_bounds__(NTR) void bwd_fstate_kernel(
-    const float* __restrict__ rec, const float* __restrict__ init, const int32_t* __restrict__ seq_first,
+__global__ __launch_bounds__(64 * chain_waves<K>()) void bwd_fstate_kernel(
+    const float* rec, const float* __restrict__ init, const int32_t* __restrict__ seq_first,
     int N, int H, int chains8, int cb, int ce, const float* __restrict__ ck_in,
     float* __restrict__ ck_out, float* __restrict__ ckS, float* __restrict__ Dl) {
   using R = BRec<K, V>;
-  // LDS row strides: a block read as the A operand along its rows (lane m takes row m, the
-  // four lane groups consecutive columns) is padded by 4 floats, one read along its columns
-  // (lane group g takes row g) by 16, so a wave's 64 reads fall in 64 different banks
-  constexpr int LW = K + 4, LKT = K + 16;
-  constexpr int PB = BC * K / 4 / NTR;  // 16-byte pieces per thread of a 64 x K block
-  constexpr int WV = NTR / 64;
-  constexpr int TPW = (K / 16 + WV - 1) / WV;  // S' tiles per wave
-  __shared__ __align__(16) float sS[K * 16];
-  __shared__ __align__(16) float sD[BC * 16];
-  __shared__ __align__(16) float sW[BC * LW];
-  __shared__ __align__(16) float sKt[BC * LKT];
-  __shared__ float sG[K];
+  constexpr int NW = chain_waves<K>(), HCT = K / 16 / NW, NTT = BC / 16, TPW = NTT / NW;
+  __shared__ __align__(16) f32x4 sX[2][NW][NTT][64];  // [parity][wave][token tile][lane]
   const int nh = blockIdx.x % chains8, s = blockIdx.x / chains8;
   if (nh >= N * H) return;
   const int n = nh / H, h = nh % H, c0 = 16 * s;
-  const int tid = threadIdx.x, w = tid >> 6, lm = tid & 15, lg = (tid >> 4) & 3;
+  const int lane = threadIdx.x & 63, v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lm = lane & 15, lg = lane >> 4;
+  const int r0 = 16 * v * HCT;  // this wave's first key channel
   const int sfirst = seq_first[n], slast = seq_first[n + 1];
   const int first = max(sfirst, cb), last = min(slast, ce);  // the sequence's chunks here
   if (first >= last) return;
   const float* src = sfirst < cb ? ck_in + (size_t)h * K * V : (init ? init + (size_t)nh * K * V : nullptr);
-  for (int e = tid; e < K * 16; e += NTR) sS[e] = src ? src[(e / 16) * V + c0 + e % 16] : 0.f;
-  struct Regs {
-    f32x4 w[PB], k[PB];
-    float u[4], g;
+  f32x4 S[HCT];
+#pragma unroll
+  for (int j = 0; j < HCT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[j][r] = src ? src[(r0 + 16 * j + 4 * lg + r) * V + c0 + lm] : 0.f;
+  struct Frags {
+    f32x4 w[NTT][HCT];   // W[16 t + lm][r0 + 16 j + 4 lg .. +3]
+    f32x4 kt[HCT][NTT];  // Kt[16 t + 4 lg + r][r0 + 16 j + lm], r = 0..3 (a column of Kt)
+    f32x4 u[TPW];        // U^T[c0 + lm][16 (v + NW i) + 4 lg .. +3]: the wave's own tiles of Delta
+    f32x4 gam[HCT];      // gamma[r0 + 16 j + 4 lg .. +3]
   };
-  Regs ra, rb;
-  auto fetch = [&](Regs& x, int c) {
-    const float* rc = rec + ((size_t)(c - cb) * H + h) * R::floats;
+  // The record pieces of chunk c, each loaded by its own helper so that a step can refill a
+  // register as soon as it has used it (the loads then trickle out between the matrix-core
+  // steps instead of queueing up at the end of the chunk, where a full memory pipeline would
+  // stall the wave). Each refill ends in a compiler fence that keeps it where it is.
+  auto rec_of = [&](int c) { return rec + ((size_t)h * (ce - cb) + (c - cb)) * R::floats; };
+  auto ld_w = [&](Frags& f, const float* rc, int j) {
 #pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      x.w[u] = reinterpret_cast<const f32x4*>(rc + R::oW)[tid + NTR * u];
-      x.k[u] = reinterpret_cast<const f32x4*>(rc + R::oKt)[tid + NTR * u];
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x.u[r] = rc[R::oU + (16 * (w & 3) + 4 * lg + r) * V + c0 + lm];
-    x.g = rc[R::oGam + tid % K];
+    for (int t = 0; t < NTT; ++t)
+      f.w[t][j] = *reinterpret_cast<const f32x4*>(rc + R::oW + (16 * t + lm) * K + r0 + 16 * j + 4 * lg);
   };
-  // one chunk: stage its registers, start loading chunk c + 2 into them, then its products
-  auto step = [&](Regs& x, int c) {
-    lds_barrier();  // the previous chunk's reads of LDS are done
+  auto ld_kt = [&](Frags& f, const float* rc, int t) {
 #pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      const int e = tid + NTR * u;
-      *reinterpret_cast<f32x4*>(sW + (e / (K / 4)) * LW + 4 * (e % (K / 4))) = x.w[u];
-      *reinterpret_cast<f32x4*>(sKt + (e / (K / 4)) * LKT + 4 * (e % (K / 4))) = x.k[u];
+    for (int j = 0; j < HCT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) f.kt[j][t][r] = rc[R::oKt + (16 * t + 4 * lg + r) * K + r0 + 16 * j + lm];
+  };
+  auto ld_u = [&](Frags& f, const float* rc) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+      f.u[i] = *reinterpret_cast<const f32x4*>(rc + R::oU + (c0 + lm) * BC + 16 * (v + NW * i) + 4 * lg);
+  };
+  auto ld_gam = [&](Frags& f, const float* rc) {
+#pragma unroll
+    for (int j = 0; j < HCT; ++j)
+      f.gam[j] = *reinterpret_cast<const f32x4*>(rc + R::oGam + r0 + 16 * j + 4 * lg);
+  };
+  auto fetch = [&](Frags& f, int c) {
+    const float* rc = rec_of(c);
+#pragma unroll
+    for (int j = 0; j < HCT; ++j) ld_w(f, rc, j);
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) ld_kt(f, rc, t);
+    ld_u(f, rc);
+    ld_gam(f, rc);
+  };
+  // live = false (the odd tail's second step) computes but stores nothing and keeps S. The
+  // set f is refilled with chunk c + 2 piece by piece.
+  auto step = [&](Frags& f, int c, bool live) {
+    const int par = (c - first) & 1;
+    const size_t ch_h = (size_t)h * (ce - cb) + (c - cb);
+    const float* rn = rec_of(min(c + 2, last - 1));
+    if (STORE && live) {
+#pragma unroll
+      for (int j = 0; j < HCT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ckS[(ch_h * K + r0 + 16 * j + 4 * lg + r) * V + c0 + lm] = S[j][r];
     }
-    if (tid < K) sG[tid] = x.g;
-    f32x4 d = {x.u[0], x.u[1], x.u[2], x.u[3]};
-    fetch(x, min(c + 2, last - 1));
-    lds_barrier();
-    if constexpr (STORE)
-      for (int e = tid; e < K * 16; e += NTR)
-        ckS[(((size_t)(c - cb) * H + h) * K + e / 16) * V + c0 + e % 16] = sS[e];
-    // Delta rows 16 w .. (waves 0-3): U - W S (two chains of dependent steps)
-    if (w < 4) {
-      f32x4 d1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int mm = 0; mm < K; mm += 8) {
-        d = mfma4(-sW[(16 * w + lm) * LW + mm + lg], sS[(mm + lg) * 16 + lm], d);
-        d1 = mfma4(-sW[(16 * w + lm) * LW + mm + 4 + lg], sS[(mm + 4 + lg) * 16 + lm], d1);
-      }
-      d += d1;
+    // this wave's part of -Delta: W S over its rows, minus U on its own tiles
+    f32x4 D[NTT];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * w + 4 * lg + r;
-        sD[row * 16 + lm] = d[r];
-        if constexpr (STORE) Dl[(((size_t)(c - cb) * H + h) * BC + row) * V + c0 + lm] = d[r];
-      }
+    for (int t = 0; t < NTT; ++t) D[t] = (t % NW == v) ? -f.u[t / NW] : f32x4{0.f, 0.f, 0.f, 0.f};
+    ld_u(f, rn);
+    fence_compiler();
+#pragma unroll
+    for (int j = 0; j < HCT; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < NTT; ++t) D[t] = mfma4(f.w[t][j][r], S[j][r], D[t]);
+      ld_w(f, rn, j);
+      fence_compiler();
     }
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) sX[par][v][t][lane] = D[t];
     lds_barrier();
-    // S' tiles: diag(gamma) S + Kt^T Delta
-    f32x4 acc[TPW];
+    // Delta, the partials summed in wave order (the same in every wave)
+    f32x4 Dd[NTT];
 #pragma unroll
-    for (int q = 0; q < TPW; ++q) {
-      const int mt = w + WV * q;
-      if (mt < K / 16) {
+    for (int t = 0; t < NTT; ++t) {
+      f32x4 x = sX[par][0][t][lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * mt + 4 * lg + r;
-          acc[q][r] = sG[row] * sS[row * 16 + lm];
+      for (int u = 1; u < NW; ++u) x += sX[par][u][t][lane];
+      Dd[t] = -x;
+    }
+    if (STORE && live) {
+#pragma unroll
+      for (int t = 0; t < NTT; ++t)
+        if (t % NW == v)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Dl[(ch_h * BC + 16 * t + 4 * lg + r) * V + c0 + lm] = Dd[t][r];
+    }
+    // S' = diag(gamma) S + Kt^T Delta (two accumulators per tile)
+    f32x4 A0[HCT], A1[HCT];
+#pragma unroll
+    for (int j = 0; j < HCT; ++j) {
+      A0[j] = f.gam[j] * S[j];
+      A1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    ld_gam(f, rn);
+    fence_compiler();
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < HCT; ++j) {
+          if (t < NTT / 2) A0[j] = mfma4(f.kt[j][t][r], Dd[t][r], A0[j]);
+          else A1[j] = mfma4(f.kt[j][t][r], Dd[t][r], A1[j]);
         }
-        f32x4 a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int r0 = 0; r0 < BC; r0 += 8) {
-          acc[q] = mfma4(sKt[(r0 + lg) * LKT + 16 * mt + lm], sD[(r0 + lg) * 16 + lm], acc[q]);
-          a1 = mfma4(sKt[(r0 + 4 + lg) * LKT + 16 * mt + lm], sD[(r0 + 4 + lg) * 16 + lm], a1);
-        }
-        acc[q] += a1;
-      }
+      ld_kt(f, rn, t);
+      fence_compiler();
     }
-    lds_barrier();
 #pragma unroll
-    for (int q = 0; q < TPW; ++q) {
-      const int mt = w + WV * q;
-      if (mt < K / 16)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sS[(16 * mt + 4 * lg + r) * 16 + lm] = acc[q][r];
-    }
+    for (int j = 0; j < HCT; ++j) S[j] = live ? A0[j] + A1[j] : S[j];
   };
-  fetch(ra, first);
-  fetch(rb, min(first + 1, last - 1));
+  // Two chunks per iteration and no branch between them: a branch there would let the compiler
+  // sink the second register set's loads to their use, which ends the prefetch.
+  Frags fa, fb;
+  fetch(fa, first);
+  fetch(fb, min(first + 1, last - 1));
   for (int c = first; c < last; c += 2) {
-    step(ra, c);
-    if (c + 1 >= last) break;
-    step(rb, c + 1);
+    step(fa, c, true);
+    step(fb, c + 1, c + 1 < last);
   }
   if (ck_out != nullptr && slast > ce) {
-    lds_barrier();
-    for (int e = tid; e < K * 16; e += NTR) ck_out[((size_t)h * K + e / 16) * V + c0 + e % 16] = sS[e];
+#pragma unroll
+    for (int j = 0; j < HCT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ck_out[((size_t)h * K + r0 + 16 * j + 4 * lg + r) * V + c0 + lm] = S[j][r];
   }
 }
 
 // Backwards in time: X_c (the gradient at the chunk's end), dDelta = P^T dO + Kt X per chunk,
 // X_prev = diag(gamma) X + Qe^T dO - W^T dDelta; at the end the initial state's gradient.
-// NTR threads: waves 0-3 form the four 16-row tiles of dDelta, and wave w the 16-row tiles
-// w, w + 8, .. of X_prev. Two register sets hold the records of the next two chunks, so each
-// chunk's loads have two chunks of compute to arrive in.
 // The chunks [cb, ce) of one segment, as in the forward chain: a sequence that goes on past
 // the segment starts from x_in (its X at chunk ce - 1, [H][K][V]), and one that began before it
 // leaves its X at chunk cb - 1 in x_out instead of writing the initial state's gradient.
 // Empty sequences (initial state = final state) are handled by the segment at chunk 0.
 template <int K, int V, typename MT>
-__global__ __launch_bounds__(NTR) void bwd_rstate_kernel(
-    const float* __restrict__ rec, const MT* __restrict__ dO, const float* __restrict__ dfin,
+__global__ __launch_bounds__(64 * chain_waves<K>()) void bwd_rstate_kernel(
+    const float* rec, const MT* dO, const float* __restrict__ dfin,
     const int32_t* __restrict__ cu, int64_t T, const int32_t* __restrict__ seq_first, int N, int H,
     int chains8, int cb, int ce, const float* __restrict__ x_in, float* __restrict__ x_out,
     float* __restrict__ ckX, float* __restrict__ dDl, float* __restrict__ dinit) {
   using R = BRec<K, V>;
-  // LDS row strides as in the forward chain: Kt is read along its rows (+4), P, Qe and W
-  // along their columns (+16)
-  constexpr int LKt = K + 4, LC = K + 16, LP = BC + 16;
-  constexpr int PB = BC * K / 4 / NTR;   // 16-byte pieces per thread of a 64 x K block
-  constexpr int PP = BC * BC / 4 / NTR;  // ... of the 64 x 64 P
-  constexpr int PO = BC * 16 / NTR;      // dO values per thread (the chunk's 16 columns)
-  constexpr int WV = NTR / 64;           // waves
-  constexpr int TPW = (K / 16 + WV - 1) / WV;
-  static_assert(PB >= 1 && PP >= 1 && PO >= 1, "pieces per thread");
-  __shared__ __align__(16) float sX[K * 16];
-  __shared__ __align__(16) float sO[BC * 16];
-  __shared__ __align__(16) float sDD[BC * 16];
-  __shared__ __align__(16) float sP[BC * LP];
-  __shared__ __align__(16) float sKt[BC * LKt];
-  __shared__ __align__(16) float sQe[BC * LC];
-  __shared__ __align__(16) float sW[BC * LC];
-  __shared__ float sG[K];
+  constexpr int NW = chain_waves<K>(), HCT = K / 16 / NW, NTT = BC / 16, TPW = NTT / NW;
+  __shared__ __align__(16) f32x4 sX[2][NW][NTT][64];  // [parity][wave][token tile][lane]
   const int nh = blockIdx.x % chains8, s = blockIdx.x / chains8;
   if (nh >= N * H) return;
   const int n = nh / H, h = nh % H, c0 = 16 * s;
-  const int tid = threadIdx.x, w = tid >> 6, lm = tid & 15, lg = (tid >> 4) & 3;
+  const int lane = threadIdx.x & 63, v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lm = lane & 15, lg = lane >> 4;
+  const int r0 = 16 * v * HCT;  // this wave's first key channel
   const int sfirst = seq_first[n], slast = seq_first[n + 1];
   const int first = max(sfirst, cb), last = min(slast, ce);  // the sequence's chunks here
   if (sfirst < slast ? first >= last : cb != 0) return;
   const bool carried = sfirst < slast && slast > ce;  // X comes from the next segment
   const float* src = carried ? x_in + (size_t)h * K * V : (dfin ? dfin + (size_t)nh * K * V : nullptr);
-  for (int e = tid; e < K * 16; e += NTR) sX[e] = src ? src[(e / 16) * V + c0 + e % 16] : 0.f;
+  f32x4 X[HCT];
+#pragma unroll
+  for (int j = 0; j < HCT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) X[j][r] = src ? src[(r0 + 16 * j + 4 * lg + r) * V + c0 + lm] : 0.f;
   int64_t s0, s1;
   seq_range(cu, N, T, n, &s0, &s1);
-  struct Regs {
-    f32x4 p[PP], k[PB], q[PB], w[PB];
-    MT o[PO];
-    float g;
+  struct Frags {
+    f32x4 kt[NTT][HCT];  // Kt[16 t + lm][r0 + 16 j + 4 lg .. +3]
+    f32x4 wt[HCT][NTT];  // W[16 t + 4 lg + r][r0 + 16 j + lm], r = 0..3 (a column of W)
+    f32x4 qt[HCT][NTT];  // Qe^T[r0 + 16 j + lm][16 t + 4 lg .. +3]
+    f32x4 pt[TPW][NTT];  // P^T[16 (v + NW i) + lm][16 t + 4 lg .. +3] (zero for t below the tile)
+    MT o[NTT][4];        // dO[token 16 t + 4 lg + r][c0 + lm]
+    f32x4 gam[HCT];
   };
-  Regs ra, rb;
-  // chunk c's rows are tokens s0 + 64 (c - first) + r; rows past the sequence read its last
-  // token (in bounds) and are zeroed when stored
-  auto fetch = [&](Regs& x, int c) {
-    const float* rc = rec + ((size_t)(c - cb) * H + h) * R::floats;
+  // chunk c's rows are tokens s0 + 64 (c - sfirst) + row; rows past the sequence read its last
+  // token (in bounds) and are zeroed when used. As in the forward chain, each piece has its own
+  // loader, so that a step refills a register right after its last use.
+  auto rec_of = [&](int c) { return rec + ((size_t)h * (ce - cb) + (c - cb)) * R::floats; };
+  auto ld_kt = [&](Frags& f, const float* rc, int j) {
 #pragma unroll
-    for (int u = 0; u < PP; ++u) x.p[u] = reinterpret_cast<const f32x4*>(rc + R::oP)[tid + NTR * u];
+    for (int t = 0; t < NTT; ++t)
+      f.kt[t][j] = *reinterpret_cast<const f32x4*>(rc + R::oKt + (16 * t + lm) * K + r0 + 16 * j + 4 * lg);
+  };
+  auto ld_wt = [&](Frags& f, const float* rc, int t) {
 #pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      x.k[u] = reinterpret_cast<const f32x4*>(rc + R::oKt)[tid + NTR * u];
-      x.q[u] = reinterpret_cast<const f32x4*>(rc + R::oQe)[tid + NTR * u];
-      x.w[u] = reinterpret_cast<const f32x4*>(rc + R::oW)[tid + NTR * u];
-    }
-    x.g = rc[R::oGam + tid % K];
+    for (int j = 0; j < HCT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) f.wt[j][t][r] = rc[R::oW + (16 * t + 4 * lg + r) * K + r0 + 16 * j + lm];
+  };
+  auto ld_qt = [&](Frags& f, const float* rc, int t) {
+#pragma unroll
+    for (int j = 0; j < HCT; ++j)
+      f.qt[j][t] = *reinterpret_cast<const f32x4*>(rc + R::oQe + (r0 + 16 * j + lm) * BC + 16 * t + 4 * lg);
+  };
+  auto ld_pt = [&](Frags& f, const float* rc) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int t = 0; t < NTT; ++t)
+        f.pt[i][t] = *reinterpret_cast<const f32x4*>(rc + R::oP + (16 * (v + NW * i) + lm) * BC + 16 * t + 4 * lg);
+  };
+  auto ld_o = [&](Frags& f, int c) {
     const int64_t tok = s0 + (int64_t)(c - sfirst) * BC;
 #pragma unroll
-    for (int u = 0; u < PO; ++u) {
-      const int e = tid + NTR * u;
-      const int64_t t = min(tok + e / 16, s1 - 1);
-      x.o[u] = dO[(t * H + h) * (int64_t)V + c0 + e % 16];
-    }
-  };
-  // one chunk: stage its registers, start loading chunk c - 2 into them, then its products
-  auto step = [&](Regs& x, int c) {
-    const int len = (int)min((int64_t)BC, s1 - (s0 + (int64_t)(c - sfirst) * BC));
-    lds_barrier();  // the previous chunk's reads of LDS are done
-#pragma unroll
-    for (int u = 0; u < PP; ++u) {
-      const int e = tid + NTR * u;
-      *reinterpret_cast<f32x4*>(sP + (e / (BC / 4)) * LP + 4 * (e % (BC / 4))) = x.p[u];
-    }
-#pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      const int e = tid + NTR * u, o = (e / (K / 4)), q4 = 4 * (e % (K / 4));
-      *reinterpret_cast<f32x4*>(sKt + o * LKt + q4) = x.k[u];
-      *reinterpret_cast<f32x4*>(sQe + o * LC + q4) = x.q[u];
-      *reinterpret_cast<f32x4*>(sW + o * LC + q4) = x.w[u];
-    }
-#pragma unroll
-    for (int u = 0; u < PO; ++u) {
-      const int e = tid + NTR * u;
-      sO[e] = e / 16 < len ? to_f32(x.o[u]) : 0.f;
-    }
-    if (tid < K) sG[tid] = x.g;
-    fetch(x, max(c - 2, first));
-    lds_barrier();
-    for (int e = tid; e < K * 16; e += NTR)
-      ckX[(((size_t)(c - cb) * H + h) * K + e / 16) * V + c0 + e % 16] = sX[e];
-    // dDelta rows 16 w .. (waves 0-3): P^T dO (P_ri = 0 for r < i, so the steps start at
-    // r = 16 w) + Kt X
-    if (w < 4) {
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
-      for (int r0 = 16 * w; r0 < BC; r0 += 4)
-        d = mfma4(sP[(r0 + lg) * LP + 16 * w + lm], sO[(r0 + lg) * 16 + lm], d);
-#pragma unroll 8
-      for (int mm = 0; mm < K; mm += 4)
-        d = mfma4(sKt[(16 * w + lm) * LKt + mm + lg], sX[(mm + lg) * 16 + lm], d);
+    for (int t = 0; t < NTT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 16 * w + 4 * lg + r;
-        sDD[row * 16 + lm] = d[r];
-        dDl[(((size_t)(c - cb) * H + h) * BC + row) * V + c0 + lm] = d[r];
+        const int64_t tt = min(tok + 16 * t + 4 * lg + r, s1 - 1);
+        f.o[t][r] = dO[(tt * H + h) * (int64_t)V + c0 + lm];
       }
+  };
+  auto ld_gam = [&](Frags& f, const float* rc) {
+#pragma unroll
+    for (int j = 0; j < HCT; ++j)
+      f.gam[j] = *reinterpret_cast<const f32x4*>(rc + R::oGam + r0 + 16 * j + 4 * lg);
+  };
+  auto fetch = [&](Frags& f, int c) {
+    const float* rc = rec_of(c);
+#pragma unroll
+    for (int j = 0; j < HCT; ++j) ld_kt(f, rc, j);
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+      ld_wt(f, rc, t);
+      ld_qt(f, rc, t);
+    }
+    ld_pt(f, rc);
+    ld_o(f, c);
+    ld_gam(f, rc);
+  };
+  // live = false (the odd tail's second step) computes but stores nothing and keeps X. The
+  // set f is refilled with chunk c - 2 piece by piece.
+  auto step = [&](Frags& f, int c, bool live) {
+    const int par = (last - 1 - c) & 1;
+    const size_t ch_h = (size_t)h * (ce - cb) + (c - cb);
+    const int len = (int)min((int64_t)BC, s1 - (s0 + (int64_t)(c - sfirst) * BC));
+    const int cn = max(c - 2, first);
+    const float* rn = rec_of(cn);
+    if (live) {
+#pragma unroll
+      for (int j = 0; j < HCT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ckX[(ch_h * K + r0 + 16 * j + 4 * lg + r) * V + c0 + lm] = X[j][r];
+    }
+    f32x4 od[NTT];
+#pragma unroll
+    for (int t = 0; t < NTT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) od[t][r] = 16 * t + 4 * lg + r < len ? to_f32(f.o[t][r]) : 0.f;
+    ld_o(f, cn);
+    fence_compiler();
+    // this wave's part of dDelta: Kt X over its rows, plus P^T dO on its own tiles
+    f32x4 D[NTT];
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) D[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < HCT; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < NTT; ++t) D[t] = mfma4(f.kt[t][j][r], X[j][r], D[t]);
+      ld_kt(f, rn, j);
+      fence_compiler();
+    }
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+      if (tt % NW == v)
+#pragma unroll
+        for (int t = tt; t < NTT; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) D[tt] = mfma4(f.pt[tt / NW][t][r], od[t][r], D[tt]);
+    ld_pt(f, rn);
+    fence_compiler();
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) sX[par][v][t][lane] = D[t];
+    // diag(gamma) X + Qe^T dO needs no dDelta: formed while the partials meet
+    f32x4 A0[HCT], A1[HCT];
+#pragma unroll
+    for (int j = 0; j < HCT; ++j) {
+      A0[j] = f.gam[j] * X[j];
+      A1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    ld_gam(f, rn);
+    fence_compiler();
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < HCT; ++j) A0[j] = mfma4(f.qt[j][t][r], od[t][r], A0[j]);
+      ld_qt(f, rn, t);
+      fence_compiler();
     }
     lds_barrier();
-    // X_prev tiles: diag(gamma) X + Qe^T dO - W^T dDelta
-    f32x4 acc[TPW];
+    f32x4 dD[NTT];
 #pragma unroll
-    for (int qq = 0; qq < TPW; ++qq) {
-      const int mt = w + WV * qq;
-      if (mt < K / 16) {
+    for (int t = 0; t < NTT; ++t) {
+      f32x4 x = sX[par][0][t][lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * mt + 4 * lg + r;
-          acc[qq][r] = sG[row] * sX[row * 16 + lm];
-        }
-#pragma unroll 8
-        for (int r0 = 0; r0 < BC; r0 += 4) {
-          acc[qq] = mfma4(sQe[(r0 + lg) * LC + 16 * mt + lm], sO[(r0 + lg) * 16 + lm], acc[qq]);
-          acc[qq] = mfma4(-sW[(r0 + lg) * LC + 16 * mt + lm], sDD[(r0 + lg) * 16 + lm], acc[qq]);
-        }
-      }
+      for (int u = 1; u < NW; ++u) x += sX[par][u][t][lane];
+      dD[t] = x;
     }
-    lds_barrier();
+    if (live) {
 #pragma unroll
-    for (int qq = 0; qq < TPW; ++qq) {
-      const int mt = w + WV * qq;
-      if (mt < K / 16)
+      for (int t = 0; t < NTT; ++t)
+        if (t % NW == v)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * lg + r) * 16 + lm] = acc[qq][r];
+          for (int r = 0; r < 4; ++r) dDl[(ch_h * BC + 16 * t + 4 * lg + r) * V + c0 + lm] = dD[t][r];
     }
+    // X_prev = diag(gamma) X + Qe^T dO - W^T dDelta
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < HCT; ++j) A1[j] = mfma4(f.wt[j][t][r], dD[t][r], A1[j]);
+      ld_wt(f, rn, t);
+      fence_compiler();
+    }
+#pragma unroll
+    for (int j = 0; j < HCT; ++j) X[j] = live ? A0[j] - A1[j] : X[j];
   };
   if (first < last) {
-    fetch(ra, last - 1);
-    fetch(rb, max(last - 2, first));
+    // two chunks per iteration, no branch between them (as in the forward chain)
+    Frags fa, fb;
+    fetch(fa, last - 1);
+    fetch(fb, max(last - 2, first));
+    for (int c = last - 1; c >= first; c -= 2) {
+      step(fa, c, true);
+      step(fb, c - 1, c - 1 >= first);
+    }
   }
-  for (int c = last - 1; c >= first; c -= 2) {
-    step(ra, c);
-    if (c - 1 < first) break;
-    step(rb, c - 1);
-  }
-  if (sfirst < cb) {
-    __syncthreads();
-    for (int e = tid; e < K * 16; e += NTR) x_out[((size_t)h * K + e / 16) * V + c0 + e % 16] = sX[e];
-  } else if (dinit) {
-    __syncthreads();
-    for (int e = tid; e < K * 16; e += NTR)
-      dinit[((size_t)nh * K + e / 16) * V + c0 + e % 16] = sX[e];
+  float* dst = sfirst < cb ? x_out + (size_t)h * K * V : (dinit ? dinit + (size_t)nh * K * V : nullptr);
+  if (dst != nullptr) {
+#pragma unroll
+    for (int j = 0; j < HCT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(r0 + 16 * j + 4 * lg + r) * V + c0 + lm] = X[j][r];
   }
 }
 
@@ -519,7 +609,7 @@ __global__ __launch_bounds__(NTGA, 8) void bwd_ga_kernel(
   const int lc = blockIdx.x, c = cb + lc, h = blockIdx.y;  // chunk of the segment, of the call
   if (c >= *ntot) return;
   const ChunkRow ch = chunks[c];
-  const size_t ch_h = (size_t)lc * H + h;
+  const size_t ch_h = (size_t)h * gridDim.x + lc;
   float* sc = scr + ch_h * G::floats;
   const float* S = ckS + ch_h * K * V;
   const float* X = ckX + ch_h * K * V;
@@ -611,7 +701,7 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gb_kernel(
   const int lc = blockIdx.x, c = cb + lc, h = blockIdx.y;  // chunk of the segment, of the call
   if (c >= *ntot) return;
   const ChunkRow ch = chunks[c];
-  const size_t ch_h = (size_t)lc * H + h;
+  const size_t ch_h = (size_t)h * gridDim.x + lc;
   const float* rc = rec + ch_h * R::floats;
   float* sc = scr + ch_h * G::floats;
   load_block<BC, LT, NTG>(sT, rc + R::oT);
@@ -710,7 +800,7 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
   const int lc = blockIdx.x, c = cb + lc, h = blockIdx.y;  // chunk of the segment, of the call
   if (c >= *ntot) return;
   const ChunkRow ch = chunks[c];
-  const size_t ch_h = (size_t)lc * H + h;
+  const size_t ch_h = (size_t)h * gridDim.x + lc;
   float* sc = scr + ch_h * G::floats;
   load_block<BC, 68, NTG>(sM, sc + G::oDPA);
   if (threadIdx.x < BC) {
@@ -830,7 +920,7 @@ __global__ __launch_bounds__(BC) void bwd_beta_kernel(int H, const ChunkRow* __r
   const ChunkRow ch = chunks[c];
   const int i = threadIdx.x;
   if (i >= ch.len) return;
-  const float* sc = scr + ((size_t)lc * H + h) * G::floats + G::oDB;
+  const float* sc = scr + ((size_t)h * gridDim.x + lc) * G::floats + G::oDB;
   float* gb = grad_beta + (ch.tok + i) * (int64_t)H + h;
   float y = *gb;
 #pragma unroll
@@ -984,7 +1074,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
     int cb, ce;
     range(s, &cb, &ce);
     prep(cb, ce);
-    hipLaunchKernelGGL((bwd_fstate_kernel<K, V, false>), sgrid, dim3(NTR), 0, st,
+    hipLaunchKernelGGL((bwd_fstate_kernel<K, V, false>), sgrid, dim3(64 * chain_waves<K>()), 0, st,
                        (const float*)rec, a.init_state, (const int32_t*)seq_first, N, H, chains8,
                        cb, ce, (const float*)(s > 0 ? bound(s) : nullptr), bound(s + 1),
                        (float*)nullptr, (float*)nullptr);
@@ -996,11 +1086,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
     int cb, ce;
     range(s, &cb, &ce);
     prep(cb, ce);
-    hipLaunchKernelGGL((bwd_fstate_kernel<K, V, true>), sgrid, dim3(NTR), 0, st,
+    hipLaunchKernelGGL((bwd_fstate_kernel<K, V, true>), sgrid, dim3(64 * chain_waves<K>()), 0, st,
                        (const float*)rec, a.init_state, (const int32_t*)seq_first, N, H, chains8,
                        cb, ce, (const float*)(s > 0 ? bound(s) : nullptr), (float*)nullptr, ckS,
                        Dl);
-    hipLaunchKernelGGL((bwd_rstate_kernel<K, V, MT>), sgrid, dim3(NTR), 0, st, (const float*)rec,
+    hipLaunchKernelGGL((bwd_rstate_kernel<K, V, MT>), sgrid, dim3(64 * chain_waves<K>()), 0, st, (const float*)rec,
                        dO, a.dfinal, a.cu_seqlens, a.total_tokens, (const int32_t*)seq_first, N, H,
                        chains8, cb, ce, (const float*)(s + 1 < p.nseg ? bound(s + 1) : nullptr),
                        s > 0 ? bound(s) : (float*)nullptr, ckX, dDl, a.grad_init);
