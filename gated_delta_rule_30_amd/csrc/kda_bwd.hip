@@ -816,7 +816,59 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
     load_rows<KC, LK, NTG, GT, K>(sQ, q, ch.tok, ch.len, H, h, c0);
     load_rows<KC, LK, NTG, GT, K>(sK, k, ch.tok, ch.len, H, h, c0);
     load_rows<KC, LK, NTG, GT, K>(sB, g, ch.tok, ch.len, H, h, c0);
-    // this thread's rows of dO S^T, T^T dW and Delta X^T, in flight through the scan
+    lds_barrier();
+    cumsum_log2<KC, LK, NTG>(sB);
+    lds_barrier();  // LDS only: the loads above stay in flight
+    const float bl = sB[(BC - 1) * LK + m];
+    float db[RB];
+    float red = 0.f;
+    // The pairwise sums of the thread's RB rows i_u = i0 + NG u, their loops fused so that
+    // every k_j, b_j (and q_r) read from LDS serves all the rows that need it; each row's
+    // terms are still added in ascending order.
+    //   s1_u = sum_{j <= i} dP_ij k_j e^{b_i - b_j},  s2_u = sum_{j < i} dA_ij k_j e^{b_i - b_j}
+    //   s3_u = sum_{r >= i} (dA_ri beta_r k_r + dP_ri q_r) e^{b_r - b_i}  (dA_ii = 0)
+    float bi[RB], s1[RB], s2[RB], s3[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int i = i0 + NG * u;
+      const float dpii = sM[i * 68 + i];
+      bi[u] = sB[i * LK + m];
+      s1[u] = dpii * sK[i * LK + m];
+      s2[u] = 0.f;
+      s3[u] = dpii * sQ[i * LK + m];
+    }
+    // j in [i_{q-1}, i_q) (from 0 for q = 0) belongs to the rows u >= q
+    static_for<0, RB>([&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      const int jb = q == 0 ? 0 : i0 + NG * (q - 1), je = i0 + NG * q;
+#pragma clang loop unroll(disable)
+      for (int j = jb; j < je; ++j) {
+        const float kj = sK[j * LK + m], bj = sB[j * LK + m];
+        static_for<q, RB>([&](auto U) {
+          constexpr int u = decltype(U)::value;
+          const int i = i0 + NG * u;
+          const float w = kj * exp2_f(bi[u] - bj);
+          s1[u] += sM[i * 68 + j] * w;
+          s2[u] += sM[j * 68 + i] * w;
+        });
+      }
+    });
+    // r in (i_q, i_{q+1}] (up to the chunk's end) belongs to the rows u <= q
+    static_for<0, RB>([&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      const int rb = i0 + NG * q + 1, re = min(i0 + NG * (q + 1) + 1, BC);
+#pragma clang loop unroll(disable)
+      for (int r = rb; r < re; ++r) {
+        const float kr = sK[r * LK + m], qr = sQ[r * LK + m], br = sB[r * LK + m], betar = sBeta[r];
+        static_for<0, q + 1>([&](auto U) {
+          constexpr int u = decltype(U)::value;
+          const int i = i0 + NG * u;
+          s3[u] += (sM[i * 68 + r] * betar * kr + sM[r * 68 + i] * qr) * exp2_f(br - bi[u]);
+        });
+      }
+    });
+    // this thread's rows of dO S^T, T^T dW and Delta X^T (loaded after the sums: through them
+    // the registers are all taken)
     float r1v[RB], tdw[RB], dkv[RB];
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
@@ -825,44 +877,25 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
       tdw[u] = sc[G::oTDW + i * K + c0 + m];
       dkv[u] = sc[G::oDKt + i * K + c0 + m];
     }
-    lds_barrier();
-    cumsum_log2<KC, LK, NTG>(sB);
-    lds_barrier();  // LDS only: the loads above stay in flight
-    const float bl = sB[(BC - 1) * LK + m];
-    float db[RB];
-    float red = 0.f;
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
       const int i = i0 + NG * u;
-      const float bi = sB[i * LK + m], qi = sQ[i * LK + m], ki = sK[i * LK + m];
-      const float dpii = sM[i * 68 + i];
-      // sum_{j <= i} dP_ij k_j e^{b_i - b_j} and sum_{j < i} dA_ij k_j e^{b_i - b_j}
-      float s1 = dpii * ki, s2 = 0.f;
-      for (int j = 0; j < i; ++j) {
-        const float w = sK[j * LK + m] * exp2_f(bi - sB[j * LK + m]);
-        s1 += sM[i * 68 + j] * w;
-        s2 += sM[j * 68 + i] * w;
-      }
-      // sum_{r >= i} (dA_ri beta_r k_r + dP_ri q_r) e^{b_r - b_i}  (dA_ii = 0)
-      float s3 = dpii * qi;
-      for (int r = i + 1; r < BC; ++r)
-        s3 += (sM[i * 68 + r] * sBeta[r] * sK[r * LK + m] + sM[r * 68 + i] * sQ[r * LK + m]) *
-              exp2_f(sB[r * LK + m] - bi);
-      const float eb = exp2_f(bi);
-      const float dq = r1v[u] * eb + s1;
-      const float dke = sBeta[i] * (tdw[u] * eb + s2);
-      const float dkt = dkv[u] * exp2_f(bl - bi);
-      const float dk = dke + s3 + dkt;
+      const float qi = sQ[i * LK + m], ki = sK[i * LK + m];
+      const float eb = exp2_f(bi[u]);
+      const float dq = r1v[u] * eb + s1[u];
+      const float dke = sBeta[i] * (tdw[u] * eb + s2[u]);
+      const float dkt = dkv[u] * exp2_f(bl - bi[u]);
+      const float dk = dke + s3[u] + dkt;
       {
         // dbeta's sum over the part's key channels of row i: the lanes sharing i (a whole
         // wave, or 32 lanes at K = 32) are the only ones holding row i
-        float y = row16_sum(ki * s2);
+        float y = row16_sum(ki * s2[u]);
         y += __shfl_xor(y, 16);
         if constexpr (KC >= 64) y += __shfl_xor(y, 32);
         if (threadIdx.x % (KC >= 64 ? 64 : KC) == 0) sDb[i] = y;
       }
       red += ki * dkt;
-      db[u] = qi * dq + ki * (dke - s3 - dkt);
+      db[u] = qi * dq + ki * (dke - s3[u] - dkt);
       if (i < ch.len) {
         const int64_t o = ((ch.tok + i) * (int64_t)H + h) * K + c0 + m;
         grad_q[o] = dq;

@@ -69,15 +69,6 @@ struct VecN {
   }
 };
 
-// Compile-time loop: f(std::integral_constant<int, I>()) for I = B .. E-1, in order.
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>());
-    static_for<B + 1, E>(f);
-  }
-}
-
 // ====================================================================== chunk table
 // Entries are ordered depth-major (chunk d of every sequence that has one, then chunk d+1),
 // so one segment advances many sequences at once and short sequences drop out early. Within a
