@@ -320,7 +320,7 @@ static kda_status check_scan_shape(int32_t num_seqs, int64_t total_tokens, int32
   kda_status st = check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_SUCCESS) return st;
   // the first pass needs V + K columns (<= 256) and the chunk path (K <= 128; fp32 at K <= 64)
-  if (dk != dv || dk > 128 || wide_path(dk, dtype, 0u)) return KDA_ERROR_NOT_SUPPORTED;
+  if (dk + dv > 256 || dk > 128 || wide_path(dk, dtype, 0u)) return KDA_ERROR_NOT_SUPPORTED;
   if (num_groups <= 0) return KDA_ERROR_INVALID_VALUE;
   return KDA_SUCCESS;
 }

@@ -26,7 +26,8 @@ bool is_wide_path(int32_t dk, kda_dtype dtype, uint32_t options);
 // [B | M], their initial states and the group boundaries.
 struct ScanPlan {
   int64_t L, Lg;       // tokens per sequence and per group
-  ChunkPlan p1, p3;    // the two chunk passes (N * G sequences; V + K and V columns)
+  int W;               // value columns of the first pass: V + K, rounded up to a power of two
+  ChunkPlan p1, p3;    // the two chunk passes (N * G sequences; W and V columns)
   size_t rec_region_bytes;  // every segment's records of the first pass, kept for the second
   size_t off_ws, off_vaug, off_oaug, off_init1, off_fin1, off_sin, off_cu, off_dummy,
       total_bytes;

@@ -8,7 +8,9 @@
 // M_g (K x K) is the product of the group's per-token transitions (I - beta k k^T) Diag(alpha)
 // and B_g (K x V) is the end state from S = 0. Since the columns of S evolve independently,
 // one chunked pass over the groups with the values [v | 0] and the initial state [0 | I]
-// (K x (V + K) per group) yields [B_g | M_g] at every group's end. Then, per sequence,
+// (K x (V + K) per group) yields [B_g | M_g] at every group's end. (The first pass takes W
+// columns, V + K rounded up to a power of two, the width the chunk path runs; the columns past
+// V + K hold zeros in the values and the initial state and are never read.) Then, per sequence,
 //   S_in(0) = initial state,   S_in(g + 1) = M_g S_in(g) + B_g      (a few K x K x V products)
 // and a second chunked pass runs all groups at once from S_in(g), writing the outputs and the
 // groups' end states; the last group's end state is the sequence's final state.
@@ -42,23 +44,22 @@ __global__ void scan_cu_kernel(int32_t* cu, const int32_t* __restrict__ cu_in, i
   cu[i] = (int32_t)(s0 + min(g * lg, len));
 }
 
-// v' = [v | 0]: rows of V + K values, 16-byte pieces
+// v' = [v | 0]: rows of W values, 16-byte pieces
 template <typename MT>
 __global__ void scan_vaug_kernel(const MT* __restrict__ v, MT* __restrict__ vaug, int64_t rows,
-                                 int V, int K) {
-  const int64_t ppr = (int64_t)(V + K) * sizeof(MT) / 16, vp = (int64_t)V * sizeof(MT) / 16;
+                                 int V, int W) {
+  const int64_t ppr = (int64_t)W * sizeof(MT) / 16, vp = (int64_t)V * sizeof(MT) / 16;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < rows * ppr;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = i / ppr, c = i - r * ppr;
     v4u32 x = {0u, 0u, 0u, 0u};
     if (c < vp) x = reinterpret_cast<const v4u32*>(v + r * V)[c];
-    reinterpret_cast<v4u32*>(vaug + r * (V + K))[c] = x;
+    reinterpret_cast<v4u32*>(vaug + r * W)[c] = x;
   }
 }
 
-// init' = [0 | I]: [groups * H][K][V + K] fp32
-__global__ void scan_init_kernel(float* __restrict__ init, int64_t heads, int K, int V) {
-  const int W = V + K;
+// init' = [0 | I | 0]: [groups * H][K][W] fp32, the identity in columns V .. V + K - 1
+__global__ void scan_init_kernel(float* __restrict__ init, int64_t heads, int K, int V, int W) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < heads * K * W;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int j = (int)(i % W);
@@ -73,7 +74,7 @@ __global__ void scan_init_kernel(float* __restrict__ init, int64_t heads, int K,
 // row r of M_g S_in(g) from the K x 4 column block of S_in(g) in LDS (broadcast reads, the
 // four quarters in four bank groups); the shares meet through two quad permutes, and the sum
 // plus row r of B_g is row r of S_in(g + 1). The half rows and B of the next two groups are in flight
-// while the current product runs. fin1 rows are V + K wide: B_g, then M_g.
+// while the current product runs. fin1 rows are W wide: B_g, then M_g (then unused columns).
 constexpr int SCAN_COLS = 4;
 
 __device__ __forceinline__ float quad_xor(float x, int m) {
@@ -85,14 +86,14 @@ __device__ __forceinline__ float quad_xor(float x, int m) {
 template <int K>
 __global__ __launch_bounds__(4 * K) void scan_combine_kernel(
     const float* __restrict__ fin1, const float* __restrict__ init, float* __restrict__ sin,
-    float* __restrict__ dummy, int G, int H, int V) {
+    float* __restrict__ dummy, int G, int H, int V, int W) {
   constexpr int KQ = K / 4;  // this thread's share of a row
   __shared__ __align__(16) f32x4 sS[K];  // S_in(g)'s column block
   const int blocks = V / SCAN_COLS;
   const int cb = blockIdx.x % blocks;
   const int nh = blockIdx.x / blocks;
   const int n = nh / H, h = nh % H;
-  const int W = V + K, c0 = SCAN_COLS * cb;
+  const int c0 = SCAN_COLS * cb;
   const int tid = threadIdx.x;
   const int r = tid >> 2, q = tid & 3;
   // three register sets in rotation: the current group's quarter row, the next group's (in
@@ -174,7 +175,7 @@ __global__ void scan_final_kernel(const float* __restrict__ sin, float* __restri
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 bool make_scan_plan(int N, int64_t T, int H, int K, int V, bool bf16, int G, ScanPlan* sp) {
-  if (N <= 0 || G <= 0 || T < 0 || K != V || K > 128) return false;
+  if (N <= 0 || G <= 0 || T < 0 || K > 128 || V + K > 256) return false;
   const int64_t N1 = (int64_t)N * G;
   if (N1 > (1 << 30)) return false;
   const size_t es = bf16 ? 2 : 4;
@@ -182,7 +183,9 @@ bool make_scan_plan(int N, int64_t T, int H, int K, int V, bool bf16, int G, Sca
   const int64_t L = T / N;
   sp->L = L;
   sp->Lg = ((L + G - 1) / G + CHUNK - 1) / CHUNK * CHUNK;
-  if (!make_chunk_plan((int)N1, T, H, K, V + K, bf16, &sp->p1)) return false;
+  sp->W = 32;
+  while (sp->W < V + K) sp->W *= 2;
+  if (!make_chunk_plan((int)N1, T, H, K, sp->W, bf16, &sp->p1)) return false;
   if (!make_chunk_plan((int)N1, T, H, K, V, bf16, &sp->p3)) return false;
   size_t off = 0;
   // the first pass keeps every segment's records (one slot each, from its record buffer on)
@@ -192,13 +195,13 @@ bool make_scan_plan(int N, int64_t T, int H, int K, int V, bool bf16, int G, Sca
   const size_t ws1 = sp->p1.off_rec + sp->rec_region_bytes;
   off += al256(ws1 > sp->p3.total_bytes ? ws1 : sp->p3.total_bytes);
   sp->off_vaug = off;
-  off += al256((size_t)T * H * (V + K) * es);
+  off += al256((size_t)T * H * sp->W * es);
   sp->off_oaug = off;
-  off += al256((size_t)T * H * (V + K) * es);
+  off += al256((size_t)T * H * sp->W * es);
   sp->off_init1 = off;
-  off += al256((size_t)N1 * H * K * (V + K) * 4);
+  off += al256((size_t)N1 * H * K * sp->W * 4);
   sp->off_fin1 = off;
-  off += al256((size_t)N1 * H * K * (V + K) * 4);
+  off += al256((size_t)N1 * H * K * sp->W * 4);
   sp->off_sin = off;
   off += al256((size_t)N1 * H * K * V * 4);
   sp->off_cu = off;
@@ -212,7 +215,7 @@ bool make_scan_plan(int N, int64_t T, int H, int K, int V, bool bf16, int G, Sca
 hipError_t launch_chunk_fwd_scan(const ChunkArgs& a, int G, const ScanPlan& sp) {
   hipStream_t st = (hipStream_t)a.stream;
   char* ws = reinterpret_cast<char*>(a.workspace);
-  const int N = a.num_seqs, H = a.num_heads, K = a.dk, V = a.dv;
+  const int N = a.num_seqs, H = a.num_heads, K = a.dk, V = a.dv, W = sp.W;
   const int64_t T = a.total_tokens, N1 = (int64_t)N * G;
   int32_t* cu = reinterpret_cast<int32_t*>(ws + sp.off_cu);
   void* vaug = ws + sp.off_vaug;
@@ -228,19 +231,19 @@ hipError_t launch_chunk_fwd_scan(const ChunkArgs& a, int G, const ScanPlan& sp) 
   if (T > 0) {
     if (a.dtype_bf16)
       hipLaunchKernelGGL(scan_vaug_kernel<bf16>, dim3(fill_blocks), dim3(256), 0, st,
-                         (const bf16*)a.v, (bf16*)vaug, T * H, V, K);
+                         (const bf16*)a.v, (bf16*)vaug, T * H, V, W);
     else
       hipLaunchKernelGGL(scan_vaug_kernel<float>, dim3(fill_blocks), dim3(256), 0, st,
-                         (const float*)a.v, (float*)vaug, T * H, V, K);
+                         (const float*)a.v, (float*)vaug, T * H, V, W);
   }
-  hipLaunchKernelGGL(scan_init_kernel, dim3(fill_blocks), dim3(256), 0, st, init1, N1 * H, K, V);
+  hipLaunchKernelGGL(scan_init_kernel, dim3(fill_blocks), dim3(256), 0, st, init1, N1 * H, K, V, W);
   // pass 1: [B_g | M_g] of every group
   ChunkArgs a1 = a;
   a1.v = vaug;
   a1.init_state = init1;
   a1.cu_seqlens = cu;
   a1.num_seqs = (int)N1;
-  a1.dv = V + K;
+  a1.dv = W;
   a1.o = oaug;
   a1.final_state = fin1;
   a1.workspace = ws + sp.off_ws;
@@ -250,11 +253,11 @@ hipError_t launch_chunk_fwd_scan(const ChunkArgs& a, int G, const ScanPlan& sp) 
   // the groups' initial states
   const dim3 cgrid((unsigned)((int64_t)N * H * (V / SCAN_COLS)));
   if (K == 32)
-    hipLaunchKernelGGL(scan_combine_kernel<32>, cgrid, dim3(4 * 32), 0, st, fin1, a.init_state, sin, dummy, G, H, V);
+    hipLaunchKernelGGL(scan_combine_kernel<32>, cgrid, dim3(4 * 32), 0, st, fin1, a.init_state, sin, dummy, G, H, V, W);
   else if (K == 64)
-    hipLaunchKernelGGL(scan_combine_kernel<64>, cgrid, dim3(4 * 64), 0, st, fin1, a.init_state, sin, dummy, G, H, V);
+    hipLaunchKernelGGL(scan_combine_kernel<64>, cgrid, dim3(4 * 64), 0, st, fin1, a.init_state, sin, dummy, G, H, V, W);
   else
-    hipLaunchKernelGGL(scan_combine_kernel<128>, cgrid, dim3(4 * 128), 0, st, fin1, a.init_state, sin, dummy, G, H, V);
+    hipLaunchKernelGGL(scan_combine_kernel<128>, cgrid, dim3(4 * 128), 0, st, fin1, a.init_state, sin, dummy, G, H, V, W);
   // pass 3: every group from its initial state; the end states overwrite them
   ChunkArgs a3 = a;
   a3.init_state = sin;

@@ -184,9 +184,10 @@ kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
  * S_in(g + 1) = M_g S_in(g) + B_g; a second pass runs all groups from those states ("Kimi Linear"
  * explainer, "DPLR Chunked Parallel"); it reads the records the first pass built. Results
  * equal kda_chunk_fwd_ex's up to rounding. It runs the sequential state sweep twice (the first
- * time with dv + dk columns) and pays off when num_seqs * num_heads * dv / 16 is far below the
- * GPU's 256 CUs (e.g. one sequence of 64k tokens over 1 to 4 heads with num_groups = 16).
- * Requires dk == dv in {32, 64, 128}; other shapes give KDA_ERROR_NOT_SUPPORTED.
+ * time with dv + dk columns, rounded up to a power of two) and pays off when
+ * num_seqs * num_heads * dv / 16 is far below the GPU's 256 CUs (e.g. one sequence of 64k
+ * tokens over 1 to 4 heads with num_groups = 16). Requires dk in {32, 64, 128} and
+ * dk + dv <= 256 (fp32 inputs: dk <= 64); other shapes give KDA_ERROR_NOT_SUPPORTED.
  * total_tokens must be divisible by num_seqs and num_groups >= 1 (else
  * KDA_ERROR_INVALID_VALUE). The workspace needs kda_chunk_fwd_scan_workspace_size bytes (the
  * same for any split of total_tokens into num_seqs sequences)

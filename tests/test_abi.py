@@ -203,7 +203,7 @@ def _scan(L, **kw):
     (dict(G=0), INVALID),
     (dict(G=-3), INVALID),
     (dict(N=3, T=128), INVALID),           # equal lengths only
-    (dict(dk=32, dv=64), NOT_SUPPORTED),   # K == V only
+    (dict(dk=128, dv=256), NOT_SUPPORTED),  # dk + dv <= 256 only
     (dict(dk=256, dv=256), NOT_SUPPORTED),
     (dict(opts=64), NOT_SUPPORTED),
     (dict(q=None), INVALID),
@@ -234,14 +234,16 @@ def test_chunk_fwd_scan_ex_argument_errors():
     assert _scan_ex(L, None) == INVALID           # no cu_seqlens: equal lengths, 128 % 3 != 0
     assert _scan_ex(L, 9 * A + 2) == INVALID      # cu_seqlens 4-byte aligned
     assert _scan_ex(L, 9 * A, G=0) == INVALID
-    assert _scan_ex(L, 9 * A, dk=64) == NOT_SUPPORTED
+    assert _scan_ex(L, 9 * A, dk=64) == WS_SMALL  # K != V: the first pass padded to 128 columns
+    assert _scan_ex(L, 9 * A, dk=128, dv=256) == NOT_SUPPORTED
 
 
 def test_scan_workspace_size():
     import torch
     ws = lambda *a: int(kda.lib().kda_chunk_fwd_scan_workspace_size(*a))
     assert ws(1, 65536, 4, 128, 128, 1, 8) > kda.workspace_size(1, 65536, 4, 128, 128, torch.bfloat16)
-    assert ws(1, 65536, 4, 128, 64, 1, 8) == 0
+    assert ws(1, 65536, 4, 128, 64, 1, 8) > 0      # K != V (first pass of 256 columns)
+    assert ws(1, 65536, 4, 128, 256, 1, 8) == 0     # dk + dv > 256
     assert ws(1, 65536, 4, 128, 128, 1, 0) == 0
     # the size holds for any split of T into N sequences (varlen through kda_chunk_fwd_scan_ex)
     assert ws(3, 100, 4, 64, 64, 0, 2) > 0

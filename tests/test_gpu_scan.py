@@ -37,6 +37,26 @@ def test_scan_matches_oracle(N, T, H, K, dtype, G):
     assert_close(np64(fin), f_ref, dtype, "final")
 
 
+@pytest.mark.parametrize("N,T,H,K,V,dtype,G", [
+    (1, 3000, 2, 64, 128, torch.bfloat16, 5),   # first pass of 256 columns
+    (2, 2048, 1, 128, 64, torch.bfloat16, 4),
+    (1, 1500, 2, 32, 64, torch.float32, 3),     # 96 -> 128 columns
+    (1, 2000, 2, 64, 32, torch.float32, 6),
+    (1, 1000, 1, 32, 128, torch.bfloat16, 4),   # 160 -> 256 columns
+])
+def test_scan_k_ne_v(N, T, H, K, V, dtype, G):
+    """K != V: the first pass runs [v | 0] with V + K columns rounded up to a power of two (the
+    padding columns stay zero and are never read)."""
+    print("scan K != V", N, T, H, K, V, dtype, G, flush=True)
+    inp = workloads.gen_forward(T, H, K, V, dtype=dtype, device=DEV, seed=T + K + 2 * V,
+                                num_seqs=N, init_std=0.1)
+    o, fin = kda.chunk_fwd_scan(*(inp[x] for x in ORDER), init_state=inp["init_state"],
+                                num_seqs=N, num_groups=G)
+    o_ref, f_ref = oracle_fwd(inp, cu=_cu(N, T))
+    assert_close(np64(o), o_ref, dtype, "o")
+    assert_close(np64(fin), f_ref, dtype, "final")
+
+
 @pytest.mark.parametrize("N,T,H,K,dtype,G", [
     (1, 2048, 2, 128, torch.bfloat16, 8),
     (1, 1500, 2, 64, torch.float32, 6),    # the last group partial
