@@ -114,8 +114,9 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------- per-chunk record
-// MT: v; GT: q, k, log alpha and beta (fp32 when an input-option pass formed them)
-template <int K, int V, typename MT, typename GT>
+// MT: v; GT: q, k, log alpha and beta (fp32 when an input-option pass formed them). LIGHT
+// writes only what the boundary pass's chain reads (W, Kt, U, gamma): no P, Qe or T.
+template <int K, int V, typename MT, typename GT, bool LIGHT = false>
 __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
     const GT* __restrict__ q, const GT* __restrict__ k, const MT* __restrict__ v,
     const GT* __restrict__ g, const GT* __restrict__ beta, int H,
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
   PairAcc acc;
   pair_acc_init<NTP>(acc);
   for (int c0 = 0; c0 < K; c0 += KC) {
-    load_rows<KC, LQ, NTP, GT, K>(sQ, q, ch.tok, ch.len, H, h, c0);
+    if constexpr (!LIGHT) load_rows<KC, LQ, NTP, GT, K>(sQ, q, ch.tok, ch.len, H, h, c0);
     load_rows<KC, LK, NTP, GT, K>(sK, k, ch.tok, ch.len, H, h, c0);
     load_rows<KC, LK, NTP, GT, K>(sB, g, ch.tok, ch.len, H, h, c0);
     lds_barrier();
@@ -157,25 +158,32 @@ __global__ __launch_bounds__(NTP, 4) void bwd_prep_kernel(
       const float br = sB[r * LK + cc], bl = sB[(BC - 1) * LK + cc];
       rc[R::oKt + r * K + c0 + cc] = sK[r * LK + cc] * exp2_f(bl - br);
     }
-    for (int e = threadIdx.x; e < BC * KC; e += NTP) {  // transposed: token index fastest
-      const int r = e % BC, cc = e / BC;
-      const float br = sB[r * LK + cc];
-      rc[R::oQe + (c0 + cc) * BC + r] = sQ[r * LQ + cc] * exp2_f(br);
+    if constexpr (!LIGHT) {
+      for (int e = threadIdx.x; e < BC * KC; e += NTP) {  // transposed: token index fastest
+        const int r = e % BC, cc = e / BC;
+        const float br = sB[r * LK + cc];
+        rc[R::oQe + (c0 + cc) * BC + r] = sQ[r * LQ + cc] * exp2_f(br);
+      }
     }
     if (threadIdx.x < KC) rc[R::oGam + c0 + threadIdx.x] = exp2_f(sB[(BC - 1) * LK + threadIdx.x]);
-    pair_acc_part<KC, LK, LQ>(acc, sQ, sK, sB);
+    pair_acc_part<KC, LK, LQ, !LIGHT>(acc, sQ, sK, sB);
     lds_barrier();  // the part's reads done before the next part overwrites it
   }
   // (the solve reads A below the diagonal only)
   pair_acc_out(acc, [&](int i, int j, float x) { sA[i * 68 + j] = sBeta[i] * x; },
-               [&](int i, int j, float x) { rc[R::oP + j * BC + i] = x; });
-  for (int e = threadIdx.x; e < BC * BC; e += NTP)  // below P^T's diagonal
-    if (e / BC > e % BC) rc[R::oP + e] = 0.f;
+               [&](int i, int j, float x) {
+                 if constexpr (!LIGHT) rc[R::oP + j * BC + i] = x;
+               });
+  if constexpr (!LIGHT) {
+    for (int e = threadIdx.x; e < BC * BC; e += NTP)  // below P^T's diagonal
+      if (e / BC > e % BC) rc[R::oP + e] = 0.f;
+  }
   lds_barrier();
   // T = (I + A)^{-1} over A (blocked: diagonal blocks by substitution, the rest on the matrix
   // cores), then to the record
   unit_lower_inverse_blocked<NTP>(sT);
-  for (int e = threadIdx.x; e < BC * BC; e += NTP) rc[R::oT + e] = sT[(e / BC) * 68 + e % BC];
+  if constexpr (!LIGHT)
+    for (int e = threadIdx.x; e < BC * BC; e += NTP) rc[R::oT + e] = sT[(e / BC) * 68 + e % BC];
   // W = T diag(beta) (k e^b), part by part
   for (int c0 = 0; c0 < K; c0 += KC) {
     load_rows<KC, LK, NTP, GT, K>(sB, g, ch.tok, ch.len, H, h, c0);
@@ -1095,18 +1103,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
     *cb = (int)(s * p.seg);
     *ce = (int)min((s + 1) * p.seg, p.ub);
   };
-  auto prep = [&](int cb, int ce) {
+  auto prep = [&](int cb, int ce, auto light) {
     if (ce > cb)
-      hipLaunchKernelGGL((bwd_prep_kernel<K, V, MT, GT>), dim3((unsigned)(ce - cb), (unsigned)H),
-                         dim3(NTP), 0, st, q, k, v, g, beta, H, (const ChunkRow*)chunks, ntot, cb,
-                         rec);
+      hipLaunchKernelGGL((bwd_prep_kernel<K, V, MT, GT, decltype(light)::value>),
+                         dim3((unsigned)(ce - cb), (unsigned)H), dim3(NTP), 0, st, q, k, v, g,
+                         beta, H, (const ChunkRow*)chunks, ntot, cb, rec);
   };
   // Forward through the segments but the last: each one's state at its end, for the sequence
   // that goes on into the next
   for (int64_t s = 0; s + 1 < p.nseg; ++s) {
     int cb, ce;
     range(s, &cb, &ce);
-    prep(cb, ce);
+    prep(cb, ce, std::true_type());
     hipLaunchKernelGGL((bwd_fstate_kernel<K, V, false>), sgrid, dim3(64 * chain_waves<K>()), 0, st,
                        (const float*)rec, a.init_state, (const int32_t*)seq_first, N, H, chains8,
                        cb, ce, (const float*)(s > 0 ? bound(s) : nullptr), bound(s + 1),
@@ -1118,7 +1126,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
   for (int64_t s = p.nseg - 1; s >= 0; --s) {
     int cb, ce;
     range(s, &cb, &ce);
-    prep(cb, ce);
+    prep(cb, ce, std::false_type());
     hipLaunchKernelGGL((bwd_fstate_kernel<K, V, true>), sgrid, dim3(64 * chain_waves<K>()), 0, st,
                        (const float*)rec, a.init_state, (const int32_t*)seq_first, N, H, chains8,
                        cb, ce, (const float*)(s > 0 ? bound(s) : nullptr), (float*)nullptr, ckS,

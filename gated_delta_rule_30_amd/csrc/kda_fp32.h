@@ -257,8 +257,9 @@ __device__ __forceinline__ void pair_acc_init(PairAcc& acc) {
 }
 
 // One part of KP channels: q in sQ ([64][LQ] fp32), k and b log2 e in sK, sB ([64][LK]); rows
-// past the chunk hold q = k = 0 and b at its last value.
-template <int KP, int LK, int LQ = LK>
+// past the chunk hold q = k = 0 and b at its last value. WITH_P = false forms A alone (sQ is
+// not read).
+template <int KP, int LK, int LQ = LK, bool WITH_P = true>
 __device__ __forceinline__ void pair_acc_part(PairAcc& acc, const float* sQ, const float* sK,
                                               const float* sB) {
   const int w = threadIdx.x >> 6, m = threadIdx.x & 15, g = (threadIdx.x >> 4) & 3;
@@ -276,7 +277,7 @@ __device__ __forceinline__ void pair_acc_part(PairAcc& acc, const float* sQ, con
       const float fi = exp2_f(bI[c] - e), fj = exp2_f(e - bJ[c]);
       const float kj = rowJ[c] * fj;
       acc.a = mfma4(rowI[c] * fi, kj, acc.a);
-      acc.p = mfma4(rowQ[c] * fi, kj, acc.p);
+      if constexpr (WITH_P) acc.p = mfma4(rowQ[c] * fi, kj, acc.p);
     }
   }
 #pragma unroll
@@ -290,14 +291,14 @@ __device__ __forceinline__ void pair_acc_part(PairAcc& acc, const float* sQ, con
     float sa = 0.f, sp = 0.f;
 #pragma unroll 2
     for (int c = 0; c < KP; c += 4) {
-      const f32x4 k1 = *reinterpret_cast<const f32x4*>(ki + c), q1 = *reinterpret_cast<const f32x4*>(qi + c);
+      const f32x4 k1 = *reinterpret_cast<const f32x4*>(ki + c);
       const f32x4 b1 = *reinterpret_cast<const f32x4*>(bi + c), k2 = *reinterpret_cast<const f32x4*>(kj + c);
       const f32x4 b2 = *reinterpret_cast<const f32x4*>(bj + c);
       f32x4 x;
 #pragma unroll
       for (int u = 0; u < 4; ++u) x[u] = k2[u] * exp2_f(b1[u] - b2[u]);
       sa += dot4(k1, x);
-      sp += dot4(q1, x);
+      if constexpr (WITH_P) sp += dot4(*reinterpret_cast<const f32x4*>(qi + c), x);
     }
     acc.da[t] += sa;
     acc.dp[t] += sp;
