@@ -815,105 +815,123 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
     sBeta[threadIdx.x] = threadIdx.x < ch.len ? to_f32(beta[(ch.tok + threadIdx.x) * (int64_t)H + h]) : 0.f;
     sDb[threadIdx.x] = 0.f;
   }
-  // thread: key channel c0 + m, rows i = i0 + NG u (interleaved; a row's two pairwise sums
-  // have 65 terms together, so every thread has the same work)
-  constexpr int NG = NTG / KC, RB = BC / NG;
-  const int m = threadIdx.x % KC, i0 = threadIdx.x / KC;
   const int c0 = blockIdx.z * KC;
+  // sDbp: dbeta's row sums per channel tile, added in tile order (no atomics)
+  constexpr int NCT = KC / 16;  // channel tiles of the part
+  __shared__ float sDbp[NCT][BC];
   {
     load_rows<KC, LK, NTG, GT, K>(sQ, q, ch.tok, ch.len, H, h, c0);
     load_rows<KC, LK, NTG, GT, K>(sK, k, ch.tok, ch.len, H, h, c0);
     load_rows<KC, LK, NTG, GT, K>(sB, g, ch.tok, ch.len, H, h, c0);
     lds_barrier();
     cumsum_log2<KC, LK, NTG>(sB);
-    lds_barrier();  // LDS only: the loads above stay in flight
-    const float bl = sB[(BC - 1) * LK + m];
-    float db[RB];
+    lds_barrier();
+    // Wave w takes row block X = w / NCT (rows 16 X ..) and channel tile ct = w % NCT; lane
+    // (n, lg) holds rows 16 X + 4 lg + r (r = 0..3) of channel m = 16 ct + n, as a matrix-core
+    // result tile. With b non-increasing along the chunk, the three decay-weighted sums
+    //   s1_i = sum_{j <= i} dP_ij k_j e^{b_i - b_j},  s2_i = sum_{j < i} dA_ij k_j e^{b_i - b_j},
+    //   s3_i = sum_{r >= i} (dA_ri beta_r k_r + dP_ri q_r) e^{b_r - b_i}          (dA_ii = 0)
+    // split into the blocks before (after) X, on the fp32 matrix cores with the decay split at
+    // the block boundary (e^{b_i - b_j} = e^{b_i - b_e} e^{b_e - b_j}, b_e the last token before
+    // block X; for s3 the last token of X; both factors at most 1), and the diagonal block X,
+    // pairwise. (The NCT * 4 waves cover the part; at 32 key channels the others idle here.)
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, lg = lane >> 4;
+    const int X = w / NCT, ct = w % NCT, m = 16 * ct + n;
+    const bool active = w < 4 * NCT;
+    f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = s1, s3 = s1;
+    float bi[4];
+    if (active) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bi[r] = sB[(16 * X + 4 * lg + r) * LK + m];
+      const int ia = 16 * X + n;  // the A operands' row
+      if (X >= 1) {
+        const float e = sB[(16 * X - 1) * LK + m];
+        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
+#pragma unroll 2
+        for (int j0 = 0; j0 < 16 * X; j0 += 4) {
+          const int jj = j0 + lg;
+          const float kh = sK[jj * LK + m] * exp2_f(e - sB[jj * LK + m]);
+          a1 = mfma4(sM[ia * 68 + jj], kh, a1);  // dP_ij
+          a2 = mfma4(sM[jj * 68 + ia], kh, a2);  // dA_ij (kept at [j][i])
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float f = exp2_f(bi[r] - e);
+          s1[r] = a1[r] * f;
+          s2[r] = a2[r] * f;
+        }
+      }
+      if (X <= 2) {
+        const float e = sB[(16 * X + 15) * LK + m];
+        f32x4 a3 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+        for (int r0 = 16 * X + 16; r0 < BC; r0 += 4) {
+          const int rr = r0 + lg;
+          const float f = exp2_f(sB[rr * LK + m] - e);
+          a3 = mfma4(sM[ia * 68 + rr], sBeta[rr] * sK[rr * LK + m] * f, a3);  // dA_ri (at [i][r])
+          a3 = mfma4(sM[rr * 68 + ia], sQ[rr * LK + m] * f, a3);                // dP_ri
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s3[r] = a3[r] * exp2_f(e - bi[r]);
+      }
+      // the diagonal block, pairwise: j <= i feeds s1 (and s2 for j < i), j >= i feeds s3
+#pragma clang loop unroll(disable)
+      for (int jj = 0; jj < 16; ++jj) {
+        const int j = 16 * X + jj;
+        const float kj = sK[j * LK + m], bj = sB[j * LK + m], qj = sQ[j * LK + m];
+        const float kbj = sBeta[j] * kj;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int il = 4 * lg + r, i = 16 * X + il;
+          const float xij = sM[i * 68 + j], xji = sM[j * 68 + i];
+          const float ex = exp2_f(jj <= il ? bi[r] - bj : bj - bi[r]);
+          s1[r] += jj <= il ? xij * kj * ex : 0.f;
+          s2[r] += jj < il ? xji * kj * ex : 0.f;
+          s3[r] += jj >= il ? ((jj > il ? xij * kbj : 0.f) + xji * qj) * ex : 0.f;
+        }
+      }
+    }
+    float db[4];
     float red = 0.f;
-    // The pairwise sums of the thread's RB rows i_u = i0 + NG u, their loops fused so that
-    // every k_j, b_j (and q_r) read from LDS serves all the rows that need it; each row's
-    // terms are still added in ascending order.
-    //   s1_u = sum_{j <= i} dP_ij k_j e^{b_i - b_j},  s2_u = sum_{j < i} dA_ij k_j e^{b_i - b_j}
-    //   s3_u = sum_{r >= i} (dA_ri beta_r k_r + dP_ri q_r) e^{b_r - b_i}  (dA_ii = 0)
-    float bi[RB], s1[RB], s2[RB], s3[RB];
+    if (active) {
+      const float bl = sB[(BC - 1) * LK + m];
 #pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int i = i0 + NG * u;
-      const float dpii = sM[i * 68 + i];
-      bi[u] = sB[i * LK + m];
-      s1[u] = dpii * sK[i * LK + m];
-      s2[u] = 0.f;
-      s3[u] = dpii * sQ[i * LK + m];
-    }
-    // j in [i_{q-1}, i_q) (from 0 for q = 0) belongs to the rows u >= q
-    static_for<0, RB>([&](auto Q) {
-      constexpr int q = decltype(Q)::value;
-      const int jb = q == 0 ? 0 : i0 + NG * (q - 1), je = i0 + NG * q;
-#pragma clang loop unroll(disable)
-      for (int j = jb; j < je; ++j) {
-        const float kj = sK[j * LK + m], bj = sB[j * LK + m];
-        static_for<q, RB>([&](auto U) {
-          constexpr int u = decltype(U)::value;
-          const int i = i0 + NG * u;
-          const float w = kj * exp2_f(bi[u] - bj);
-          s1[u] += sM[i * 68 + j] * w;
-          s2[u] += sM[j * 68 + i] * w;
-        });
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * X + 4 * lg + r;
+        const float r1v = sc[G::oR1 + i * K + c0 + m], tdw = sc[G::oTDW + i * K + c0 + m];
+        const float dkv = sc[G::oDKt + i * K + c0 + m];
+        const float qi = sQ[i * LK + m], ki = sK[i * LK + m];
+        const float eb = exp2_f(bi[r]);
+        const float dq = r1v * eb + s1[r];
+        const float dke = sBeta[i] * (tdw * eb + s2[r]);
+        const float dkt = dkv * exp2_f(bl - bi[r]);
+        const float dk = dke + s3[r] + dkt;
+        // dbeta's sum over the tile's 16 channels of row i (the 16 lanes of a lane group)
+        const float y = row16_sum(ki * s2[r]);
+        if (n == 0) sDbp[ct][i] = y;
+        red += ki * dkt;
+        db[r] = qi * dq + ki * (dke - s3[r] - dkt);
+        if (i < ch.len) {
+          const int64_t o = ((ch.tok + i) * (int64_t)H + h) * K + c0 + m;
+          grad_q[o] = dq;
+          grad_k[o] = dk;
+        }
       }
-    });
-    // r in (i_q, i_{q+1}] (up to the chunk's end) belongs to the rows u <= q
-    static_for<0, RB>([&](auto Q) {
-      constexpr int q = decltype(Q)::value;
-      const int rb = i0 + NG * q + 1, re = min(i0 + NG * (q + 1) + 1, BC);
-#pragma clang loop unroll(disable)
-      for (int r = rb; r < re; ++r) {
-        const float kr = sK[r * LK + m], qr = sQ[r * LK + m], br = sB[r * LK + m], betar = sBeta[r];
-        static_for<0, q + 1>([&](auto U) {
-          constexpr int u = decltype(U)::value;
-          const int i = i0 + NG * u;
-          s3[u] += (sM[i * 68 + r] * betar * kr + sM[r * 68 + i] * qr) * exp2_f(br - bi[u]);
-        });
-      }
-    });
-    // this thread's rows of dO S^T, T^T dW and Delta X^T (loaded after the sums: through them
-    // the registers are all taken)
-    float r1v[RB], tdw[RB], dkv[RB];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int i = i0 + NG * u;
-      r1v[u] = sc[G::oR1 + i * K + c0 + m];
-      tdw[u] = sc[G::oTDW + i * K + c0 + m];
-      dkv[u] = sc[G::oDKt + i * K + c0 + m];
-    }
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int i = i0 + NG * u;
-      const float qi = sQ[i * LK + m], ki = sK[i * LK + m];
-      const float eb = exp2_f(bi[u]);
-      const float dq = r1v[u] * eb + s1[u];
-      const float dke = sBeta[i] * (tdw[u] * eb + s2[u]);
-      const float dkt = dkv[u] * exp2_f(bl - bi[u]);
-      const float dk = dke + s3[u] + dkt;
-      {
-        // dbeta's sum over the part's key channels of row i: the lanes sharing i (a whole
-        // wave, or 32 lanes at K = 32) are the only ones holding row i
-        float y = row16_sum(ki * s2[u]);
-        y += __shfl_xor(y, 16);
-        if constexpr (KC >= 64) y += __shfl_xor(y, 32);
-        if (threadIdx.x % (KC >= 64 ? 64 : KC) == 0) sDb[i] = y;
-      }
-      red += ki * dkt;
-      db[u] = qi * dq + ki * (dke - s3[u] - dkt);
-      if (i < ch.len) {
-        const int64_t o = ((ch.tok + i) * (int64_t)H + h) * K + c0 + m;
-        grad_q[o] = dq;
-        grad_k[o] = dk;
-      }
+      red += __shfl_xor(red, 16);
+      red += __shfl_xor(red, 32);
     }
     lds_barrier();  // every read of sQ and sK done
+    if (active) {
 #pragma unroll
-    for (int u = 0; u < RB; ++u) sQ[(i0 + NG * u) * LK + m] = db[u];
-    sK[i0 * LK + m] = red;  // this thread's rows' share of sum_i k_i dKt_i, summed below in order
+      for (int r = 0; r < 4; ++r) sQ[(16 * X + 4 * lg + r) * LK + m] = db[r];
+      if (lg == 0) sK[X * LK + m] = red;  // this row block's share of sum_i k_i dKt_i
+    }
+    if (threadIdx.x < BC) {
+      float y = 0.f;
+#pragma unroll
+      for (int t = 0; t < NCT; ++t) y += sDbp[t][threadIdx.x];
+      sDb[threadIdx.x] = y;
+    }
     lds_barrier();
     // log alpha: reverse cumulative sum of db over the chunk, the last token also carrying
     // sum_i k_i * dKt_i and gamma * rowsum(S * X); NTG / KC neighbouring threads per channel,
@@ -937,7 +955,7 @@ __global__ __launch_bounds__(NTG, 8) void bwd_gc_kernel(
       post -= run;  // the rows after this thread's
       float red = 0.f;
 #pragma unroll
-      for (int u = 0; u < NG; ++u) red += sK[u * LK + cm];
+      for (int u = 0; u < 4; ++u) red += sK[u * LK + cm];
       post += red + sc[G::oDG + c0 + cm] * exp2_f(sB[(BC - 1) * LK + cm]);
 #pragma unroll
       for (int r = 0; r < RP; ++r) {
