@@ -248,8 +248,11 @@ struct PrepParams {
 // that path's register allocation and schedule free of it. V256 = true fixes a token row of V
 // at 256 bytes (bf16 V = 128, fp32 V = 64): the V copy is then one branch-free batch (at the
 // join points of the generic copy's batch branches the compiler waits for all memory traffic).
-template <int K, typename MT, bool OPTS, bool V256>
+// UREC = true (bf16, V = 128) writes the record's U form: U = T'V formed here, on the matrix
+// cores from V staged in LDS, in place of T' and V.
+template <int K, typename MT, bool OPTS, bool V256, bool UREC = false>
 __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
+  static_assert(!UREC || (V256 && sizeof(MT) == 2 && K <= 128), "the U form: bf16, V = 128");
   using L = PrepLayout<K, MT>;
   using R = Rec<K, MT>;
   using frag = typename Mma<MT>::frag;
@@ -336,6 +339,8 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   // wait for a load issued just after another store; otherwise up to four batches of four, each
   // loaded a phase before it is stored.
   constexpr int VB = 4;
+  constexpr int LDVU = 128 + 8;  // row stride (elements) of V staged in LDS for the U form
+  static_assert(!UREC || (size_t)CHUNK * LDVU * sizeof(MT) <= L::szR1, "V fits region R1");
   u4 vbuf[VB];
   // (tid: the loop's opaque copy of threadIdx.x, so that no address is hoisted and kept live)
   auto v_load = [&](int tid, TaskPos tp, int task, int batch) {
@@ -784,8 +789,18 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   if (vpt > 3 * VB) v_load(tid, pcur, task, 3);
 
   // ---------------- phase 5: T' fragments to the record (whole 16-byte lane slots), then
-  // W^T = Ka^T T'^T -> record (as -W fragments)
-  {
+  // W^T = Ka^T T'^T -> record (as -W fragments). In the U form V goes to LDS (region R1, free
+  // since phase 4) instead, for U = T'V after W.
+  if constexpr (UREC) {
+    MT* sVs = reinterpret_cast<MT*>(smem + L::oR1);  // V, [CHUNK][LDVU] row-major
+#pragma unroll
+    for (int i = 0; i < VB; ++i) {
+      const int id = tid + PREP_THREADS * i;
+      const int row = id >> 4, c = id & 15;
+      *reinterpret_cast<u4*>(sVs + row * LDVU + 8 * c) = vbuf[i];
+    }
+  }
+  if constexpr (!UREC) {
     constexpr int NSL = NSUB * (CHUNK / KS) * 64;
 #pragma unroll
     for (int i = 0; i < NSL / PREP_THREADS; ++i) {
@@ -822,7 +837,28 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   }
 
   if (vpt > 3 * VB) v_store(tid, reinterpret_cast<char*>(recM), 3);
-  if (V256) v_store(tid, reinterpret_cast<char*>(recM), 0);
+  if constexpr (UREC) {
+    // U = T'V: result tile (token tile tt, value tile ct) over the steps T' is not zero in;
+    // wave w takes the tiles with (8 tt + ct) % 4 == w
+    lds_barrier();
+    const MT* sVs = reinterpret_cast<const MT*>(smem + L::oR1);
+#pragma unroll
+    for (int tix = 0; tix < NSUB * 8; ++tix) {
+      if (tix % 4 != w) continue;
+      const int tt = tix / 8, ct = tix % 8;
+      const int nsteps = (16 * tt + 16 + KS - 1) / KS;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < CHUNK / KS; ++s)
+        if (s < nsteps)
+          acc = Mma<MT>::mma(load_frag(sTb + (16 * tt + m) * L::LC, s, g),
+                             frag_t(sVs, LDVU, 16 * ct, s, lane), acc);
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(recM) + R::u_tile_byte(ct, tt, lane)) =
+          __builtin_convertvector(acc, bf16x4);
+    }
+  } else if (V256) {
+    v_store(tid, reinterpret_cast<char*>(recM), 0);
+  }
   lds_barrier();  // the next task reuses every LDS region
   task += gridDim.x;
   if (task >= ntask) break;
@@ -1236,7 +1272,9 @@ struct SplitShape {
   static_assert(THREADS == split_threads<K>(), "one thread count per K");
 };
 
-template <int K, typename MT>
+// UREC: the record's U form (bf16, 128 value columns): wave 0 takes U from the record instead of
+// forming T'V, and V is not staged.
+template <int K, typename MT, bool UREC = false>
 __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per_eu(K > 128 ? 2 : 1, K > 128 ? 2 : 1))) void state_split_kernel(StateParams p) {
   using SH = StateShape<K, MT>;
   using SS = SplitShape<K, MT>;
@@ -1315,7 +1353,7 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
 
   auto body = [&](auto WVc) {
     constexpr int WV = decltype(WVc)::value;
-    constexpr int NFW = WV < 2 ? NF : NA + NB;  // this wave's operations per chunk
+    constexpr int NFW = (WV == 1 || (WV == 0 && !UREC)) ? NF : NA + NB;  // operations per chunk
     // operation j of this wave's stream reads the next chunk's record (wave 0's T') or this one's
     auto next_rec = [](int j) constexpr { return WV == 0 && j >= NA + NB; };
     auto frag_off = [](auto J) constexpr -> uint32_t {
@@ -1374,7 +1412,27 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
     vload vx[NVL];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) U[tt] = O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (WV == 0) {
+    // the U form: this slice's four U tiles of the chunk whose record starts at rc, as two
+    // 16-byte pieces per lane (tiles 2p and 2p + 1)
+    constexpr bool UW0 = UREC && WV == 0;
+    const uint32_t uslice_off = (uint32_t)(R::oVBytes + (size_t)slice * R::vslice_bytes);
+    auto load_u = [&](uint32_t rc, bf16x8 (&x)[2]) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+        x[pp] = buf_load16<bf16x8>(rrec, (uint32_t)(pp * 64 + lane) * 16u, rc + uslice_off);
+    };
+    auto set_u = [&](const bf16x8 (&x)[2]) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        U[2 * pp] = __builtin_convertvector(__builtin_shufflevector(x[pp], x[pp], 0, 1, 2, 3), f32x4);
+        U[2 * pp + 1] = __builtin_convertvector(__builtin_shufflevector(x[pp], x[pp], 4, 5, 6, 7), f32x4);
+      }
+    };
+    bf16x8 unext[UW0 ? 2 : 1][2];
+    if constexpr (UW0) {
+      load_u(rc0, unext[0]);
+      set_u(unext[0]);
+    } else if constexpr (WV == 0) {
       load_v(rc0, vx);
       stage_v(vx);
 #pragma unroll
@@ -1408,7 +1466,7 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
     __builtin_amdgcn_sched_barrier(0);
     uint32_t rc3 = rec_off(rec_index(3));
     int ri_pre = sRun[min(4, run - 1)];  // record index of chunk k + 4, read a chunk ahead
-    if constexpr (WV == 0) load_v(rc1, vx);
+    if constexpr (WV == 0 && !UREC) load_v(rc1, vx);
     rsrc_t ro_prev = rows_rsrc(go, 0);
 
     // one chunk; PAR = k & 1 selects the ring half and the exchange buffers
@@ -1422,6 +1480,7 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
       } else {
         load_gam(rc0, gcur);
       }
+      if constexpr (UW0) load_u(rc1, unext[0]);  // the next chunk's U
       __builtin_amdgcn_sched_barrier(0);
 
       frag Sb[HKS], Db[NTS];
@@ -1467,7 +1526,7 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
           }
         }
         if constexpr (j >= NA && j < NA + HKT) S[j - NA] *= gcur[j - NA];
-        if constexpr (WV == 0 && j == NA + NB / 2) {
+        if constexpr (WV == 0 && !UREC && j == NA + NB / 2) {
           stage_v(vx);
 #pragma unroll
           for (int s = 0; s < NTS; ++s) Vf[s] = frag_t(sV, LDV, 0, s, lane);
@@ -1475,7 +1534,7 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
         if constexpr (j == NA + NB) {
 #pragma unroll
           for (int tt = 0; tt < NTT; ++tt) U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if constexpr (WV == 0) load_v(rc2, vx);
+          if constexpr (WV == 0 && !UREC) load_v(rc2, vx);
         }
         constexpr int slot = (RC == 2 ? par * NFW : 0) + j;
         const frag f = ring[slot];
@@ -1498,7 +1557,9 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
       });
       // waves without the T'V / P Delta operations never reach the reset at NA + NB: their next
       // Delta partial starts from zero here
-      if constexpr (NFW == NA + NB) {
+      if constexpr (UW0) {
+        set_u(unext[0]);  // the U form: the next chunk's Delta partial starts from its U
+      } else if constexpr (NFW == NA + NB) {
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -1643,6 +1704,11 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl, const 
   hipLaunchKernelGGL(segment_kernel, dim3(pl.num_segs), dim3(256), 0, st, entries, header,
                      pl.seg_entries, pl.slots, seg_first, seg_count);
 
+  // The record's U form (U = T'V in place of T' and V): bf16, 128 value columns, the two-wave
+  // chain, and records made and used in this call (the scan's second pass reads the first
+  // pass's records, which carry V).
+  constexpr bool UFORM_OK = sizeof(MT) == 2 && K <= 128 && SplitShape<K, MT>::OK;
+  const bool urec = UFORM_OK && a.dv == 128 && rr == nullptr;
   const int64_t chains = pl.slots * a.num_heads;
   const int64_t chains8 = (chains + 7) / 8 * 8;
   const dim3 sgrid((unsigned)(chains8 * pl.n_slices));
@@ -1659,6 +1725,15 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl, const 
       PrepParams pp{a.q, a.k, a.g, a.beta, entries, header, a.num_heads, s * pl.seg_entries,
                     pl.seg_entries, seg_rec(s), rb, a.options, a.v, a.dv};
       const bool v256 = (size_t)a.dv * sizeof(MT) == 256;
+      if constexpr (UFORM_OK) {
+        if (urec) {
+          if (a.options == 0)
+            hipLaunchKernelGGL((prep_kernel<K, MT, false, true, true>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+          else
+            hipLaunchKernelGGL((prep_kernel<K, MT, true, true, true>), pgrid, dim3(PREP_THREADS), 0, q, pp);
+          return;
+        }
+      }
       if (a.options == 0 && v256)
         hipLaunchKernelGGL((prep_kernel<K, MT, false, true>), pgrid, dim3(PREP_THREADS), 0, q, pp);
       else if (a.options == 0)
@@ -1675,6 +1750,12 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl, const 
                    a.num_heads, a.dv, pl.n_slices, chains, seg_rec(s), (uint32_t)rb,
                    (uint32_t)seg_buf};
     if (pl.vs != 16) return false;
+    if constexpr (UFORM_OK) {
+      if (urec) {
+        hipLaunchKernelGGL((state_split_kernel<K, MT, true>), sgrid, dim3(SplitShape<K, MT>::THREADS), 0, q, sp);
+        return true;
+      }
+    }
     if constexpr (SplitShape<K, MT>::OK)
       hipLaunchKernelGGL((state_split_kernel<K, MT>), sgrid, dim3(SplitShape<K, MT>::THREADS), 0, q, sp);
     else

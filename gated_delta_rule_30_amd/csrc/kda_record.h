@@ -23,9 +23,16 @@ struct Rec {
   static constexpr size_t oGamBytes = nMat * sizeof(MT);         // K fp32
   static constexpr size_t bytes = (oGamBytes + K * 4 + 1023) / 1024 * 1024;  // whole 1 KB slots
   // then V of the chunk, slice-major: slice c (value columns 16c .. 16c+15) is CHUNK rows of 16
-  // values, 16 * CHUNK * sizeof(MT) bytes, at oVBytes + c * 16 * CHUNK * sizeof(MT)
+  // values, 16 * CHUNK * sizeof(MT) bytes, at oVBytes + c * 16 * CHUNK * sizeof(MT).
+  // In the U form of the record (bf16, 128 value columns, up to 128 key channels) the same
+  // bytes hold U = T'V instead, and the T' slots are not written: slice c holds the four
+  // 16 x 16 result tiles of U (token tile t, value columns 16c ..), lane l's four values of
+  // tile t at byte ((t / 2) * 64 + l) * 16 + (t % 2) * 8 of the slice (two tiles per 16 bytes).
   static constexpr size_t oVBytes = bytes;
   static constexpr size_t vslice_bytes = (size_t)16 * CHUNK * sizeof(MT);
+  __device__ __forceinline__ static size_t u_tile_byte(int slice, int t, int lane) {
+    return oVBytes + (size_t)slice * vslice_bytes + ((size_t)(t >> 1) * 64 + lane) * 16 + (t & 1) * 8;
+  }
 };
 
 template <typename MT>
