@@ -190,6 +190,10 @@ template <int SH>
 __device__ __forceinline__ float row_shr(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + SH, 0xf, 0xf, true));
 }
+// The value of lane 15 of each 16-lane row, in every lane of that row (DPP row_newbcast:15).
+__device__ __forceinline__ float row_last(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x15F, 0xf, 0xf, false));
+}
 
 // A fragment (EPL elements) from fp32 values.
 __device__ __forceinline__ bf16x8 to_frag(f32x4 lo, f32x4 hi, bf16) { return frag_from_acc(lo, hi, bf16()); }
@@ -460,7 +464,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   #pragma unroll
     for (int u = 0; u < NG; ++u)
   #pragma unroll
-      for (int r = 0; r < 4; ++r) dI[u][r] = __shfl(lv[u][r], lane | 15);
+      for (int r = 0; r < 4; ++r) dI[u][r] = row_last(lv[u][r]);
     // Diagonal sub-block of this wave. Its MFMA form scales the column operand by the block's
     // inverse decay 2^{-dI} >= 1, which is exact up to rounding while no channel decays by more
     // than 2^DIAG_MAX_LOG2 over the sub-block. Beyond that, the block's A and P entries are
@@ -738,7 +742,9 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
       const int sl = tid + PREP_THREADS * i;
       const int ln = sl & 63, ts = sl >> 6;
       const int s = ts % (CHUNK / KS), tile = ts / (CHUNK / KS);
-      *reinterpret_cast<frag*>(recM + R::oPb + (size_t)sl * EPL) = frag_t(sPnT, L::LC, 16 * tile, s, ln);
+      // the slots above the diagonal (all zero) are never read: not written
+      if (KS * s <= 16 * tile + 15)
+        *reinterpret_cast<frag*>(recM + R::oPb + (size_t)sl * EPL) = frag_t(sPnT, L::LC, 16 * tile, s, ln);
     }
   }
   if (w >= 1) {
@@ -807,8 +813,9 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
       const int sl = tid + PREP_THREADS * i;
       const int ln = sl & 63, ts = sl >> 6;
       const int s = ts % (CHUNK / KS), tile = ts / (CHUNK / KS);
-      *reinterpret_cast<frag*>(recM + R::oTb + (size_t)sl * EPL) =
-          load_frag(sTb + (16 * tile + (ln & 15)) * L::LC, s, ln >> 4);
+      if (KS * s <= 16 * tile + 15)  // as for P: the all-zero slots are not written
+        *reinterpret_cast<frag*>(recM + R::oTb + (size_t)sl * EPL) =
+            load_frag(sTb + (16 * tile + (ln & 15)) * L::LC, s, ln >> 4);
     }
   }
   // Result tile (channel tile a, token tile b): lane (m, g) holds W[16b + m][16a + 4g + r]. A
