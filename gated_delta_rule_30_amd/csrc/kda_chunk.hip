@@ -329,6 +329,24 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     if ((part < 0 || part == 2) && scalar_gate) r.g[0][0] = gg_[tl * H + hh];
     if (part < 0 || part == 2) r.b = gb_[tl * H + hh];
   };
+  // The same for the channel groups u of part 0, 1 or 2 that belong to step i of NSTEP: the
+  // prefetch is spread over the loops of phases 2-4, a few loads at a time, so that no wave
+  // stalls issuing a long burst of loads behind the record stores in flight.
+  auto load_raw_step = [&](Raw& r, TaskPos tp, int task, int part, int i, int nstep) {
+    const int hh = task % H;
+    const int64_t tl = tp.tok + min(t0, tp.len - 1);
+    const int64_t row = tl * (int64_t)H * K + (int64_t)hh * K + 4 * g0;
+#pragma unroll
+    for (int u = i * NG / nstep; u < (i + 1) * NG / nstep; ++u) {
+      if (part == 0) r.q[u] = *reinterpret_cast<const raw4*>(gq_ + row + 16 * u);
+      if (part == 1) r.k[u] = *reinterpret_cast<const raw4*>(gk_ + row + 16 * u);
+      if (part == 2 && !scalar_gate) r.g[u] = *reinterpret_cast<const raw4*>(gg_ + row + 16 * u);
+    }
+    if (part == 2 && i == 0) {
+      if (scalar_gate) r.g[0][0] = gg_[tl * H + hh];
+      r.b = gb_[tl * H + hh];
+    }
+  };
   // V of the current task into its record, slice-major (the state kernel then reads a slice's
   // CHUNK x 16 values as one contiguous block instead of gathering 16 values from each of CHUNK
   // token rows). A token row is vpr 16-byte pieces; each thread copies vpt pieces.
@@ -626,10 +644,9 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   pnext = task_pos(nntsk);
   MT* recM = reinterpret_cast<MT*>(p.rec + (j * H + h) * p.rec_bytes);
 
-  // the next task's inputs load during phases 2-5 (phase 1's fp32 copies are dead by now)
-  // (in three parts, so that the loads enter the memory pipeline in smaller bursts)
+  // the next task's inputs load during phases 2-4 (phase 1's fp32 copies are dead by now):
+  // q in phase 2's loop, k in the loop that stores A and P, log alpha and beta in phase 4's
   v_load(tid, pcur, task, 0);
-  load_raw(raw, pn, ntsk, 0);
 
   // ---------------- phase 2: blocks (I, w), I >= w, of A and P. The column operand (token
   // block w, scaled per channel by D_{Iw}) is this wave's own kc; the row operands are read as
@@ -639,6 +656,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   for (int I = 0; I < NSUB; ++I) {
     tA[I] = f32x4{0.f, 0.f, 0.f, 0.f};
     tP[I] = tA[I];
+    load_raw_step(raw, pn, ntsk, 0, I, NSUB);
     if (I < w) continue;
     if (I == w && diag_exact) {
       tA[I] = adiag_x;
@@ -673,6 +691,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     const int jj = 16 * w + m;
 #pragma unroll
     for (int I = 0; I < NSUB; ++I) {
+      load_raw_step(raw, pn, ntsk, 1, I, NSUB);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * g + r;
@@ -689,7 +708,6 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
     }
   }
 
-  load_raw(raw, pn, ntsk, 1);
   if (!V256) v_store(tid, reinterpret_cast<char*>(recM), 0);
   if (vpt > VB) v_load(tid, pcur, task, 1);
 
@@ -770,13 +788,13 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   }
   lds_barrier();
 
-  load_raw(raw, pn, ntsk, 2);
   if (vpt > VB) v_store(tid, reinterpret_cast<char*>(recM), 1);
   if (vpt > 2 * VB) v_load(tid, pcur, task, 2);
 
   // ---------------- phase 4: T' = T diag(beta) -> LDS (row-major)
 #pragma unroll
   for (int it = 0; it < CHUNK * CHUNK / 4 / PREP_THREADS; ++it) {
+    load_raw_step(raw, pn, ntsk, 2, it, CHUNK * CHUNK / 4 / PREP_THREADS);
     const int idx = tid + PREP_THREADS * it;
     const unsigned i = (unsigned)idx / (CHUNK / 4), j0 = 4u * ((unsigned)idx % (CHUNK / 4));
     const unsigned Ii = i >> 4, Jj = j0 >> 4;
