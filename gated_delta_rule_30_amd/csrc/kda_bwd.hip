@@ -16,7 +16,11 @@
 // Delta X^T. Every product that carries in-chunk decay is formed pairwise as e^{b_i - b_j}
 // with j <= i (at most 1), so nothing overflows for any decay.
 //
-// Everything runs in fp32 (the chunk's inputs, bf16 or fp32, are exact in fp32). Kernels:
+// Every stored value and every sum is fp32 (the chunk's inputs, bf16 or fp32, are exact in
+// fp32). The matrix-core products of the two chains and of the S/X product kernel take each
+// fp32 operand as two bf16 parts (hi = bf16(x), lo = bf16(x - hi); hi*hi + hi*lo + lo*hi on the
+// bf16 matrix cores, about 2^-16 relative error per product); the record kernel, the T-side
+// and the gradient kernel use the fp32 matrix cores. Kernels:
 //   bwd_seq_kernel, bwd_chunk_kernel   the chunk table (sequence boundaries from cu_seqlens)
 //   bwd_prep_kernel                    per (chunk, head): T, P, W, Kt, Qe, U, gamma -> record
 //   bwd_fstate_kernel                  per (sequence, head, 16 value columns), forward in
@@ -269,9 +273,9 @@ __global__ __launch_bounds__(64 * chain_waves<K>()) void bwd_fstate_kernel(
   // steps instead of queueing up at the end of the chunk, where a full memory pipeline would
   // stall the wave). Each refill ends in a compiler fence that keeps it where it is.
   auto rec_of = [&](int c) { return rec + ((size_t)h * (ce - cb) + (c - cb)) * R::floats; };
-  auto ld_w = [&](Frags& f, const float* rc, int j) {
+  auto ld_w = [&](Frags& f, const float* rc, int t) {
 #pragma unroll
-    for (int t = 0; t < NTT; ++t)
+    for (int j = 0; j < HCT; ++j)
       f.w[t][j] = *reinterpret_cast<const f32x4*>(rc + R::oW + (16 * t + lm) * K + r0 + 16 * j + 4 * lg);
   };
   auto ld_kt = [&](Frags& f, const float* rc, int t) {
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(64 * chain_waves<K>()) void bwd_fstate_kernel(
   auto fetch = [&](Frags& f, int c) {
     const float* rc = rec_of(c);
 #pragma unroll
-    for (int j = 0; j < HCT; ++j) ld_w(f, rc, j);
+    for (int t = 0; t < NTT; ++t) ld_w(f, rc, t);
 #pragma unroll
     for (int t = 0; t < NTT; ++t) ld_kt(f, rc, t);
     ld_u(f, rc);
@@ -317,13 +321,11 @@ __global__ __launch_bounds__(64 * chain_waves<K>()) void bwd_fstate_kernel(
     for (int t = 0; t < NTT; ++t) D[t] = (t % NW == v) ? -f.u[t / NW] : f32x4{0.f, 0.f, 0.f, 0.f};
     ld_u(f, rn);
     fence_compiler();
+    const X3<HCT> sx = x3_of<HCT>(S);
 #pragma unroll
-    for (int j = 0; j < HCT; ++j) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int t = 0; t < NTT; ++t) D[t] = mfma4(f.w[t][j][r], S[j][r], D[t]);
-      ld_w(f, rn, j);
+    for (int t = 0; t < NTT; ++t) {
+      D[t] = x3_mma(x3_of<HCT>(f.w[t]), sx, D[t]);
+      ld_w(f, rn, t);
       fence_compiler();
     }
 #pragma unroll
@@ -354,16 +356,19 @@ __global__ __launch_bounds__(64 * chain_waves<K>()) void bwd_fstate_kernel(
     }
     ld_gam(f, rn);
     fence_compiler();
+    // over the tokens in 32-steps (token tiles 2 s and 2 s + 1), one accumulator per step
+    static_assert(NTT == 4, "two 32-token steps per chunk");
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) {
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const X3<2> dx = x3_of(Dd[2 * s2], Dd[2 * s2 + 1]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int j = 0; j < HCT; ++j) {
-          if (t < NTT / 2) A0[j] = mfma4(f.kt[j][t][r], Dd[t][r], A0[j]);
-          else A1[j] = mfma4(f.kt[j][t][r], Dd[t][r], A1[j]);
-        }
-      ld_kt(f, rn, t);
+      for (int j = 0; j < HCT; ++j) {
+        const X3<2> kx = x3_of(f.kt[j][2 * s2], f.kt[j][2 * s2 + 1]);
+        if (s2 == 0) A0[j] = x3_mma(kx, dx, A0[j]);
+        else A1[j] = x3_mma(kx, dx, A1[j]);
+      }
+      ld_kt(f, rn, 2 * s2);
+      ld_kt(f, rn, 2 * s2 + 1);
       fence_compiler();
     }
 #pragma unroll
@@ -431,9 +436,9 @@ __global__ __launch_bounds__(64 * chain_waves<K>()) void bwd_rstate_kernel(
   // token (in bounds) and are zeroed when used. As in the forward chain, each piece has its own
   // loader, so that a step refills a register right after its last use.
   auto rec_of = [&](int c) { return rec + ((size_t)h * (ce - cb) + (c - cb)) * R::floats; };
-  auto ld_kt = [&](Frags& f, const float* rc, int j) {
+  auto ld_kt = [&](Frags& f, const float* rc, int t) {
 #pragma unroll
-    for (int t = 0; t < NTT; ++t)
+    for (int j = 0; j < HCT; ++j)
       f.kt[t][j] = *reinterpret_cast<const f32x4*>(rc + R::oKt + (16 * t + lm) * K + r0 + 16 * j + 4 * lg);
   };
   auto ld_wt = [&](Frags& f, const float* rc, int t) {
@@ -472,7 +477,7 @@ __global__ __launch_bounds__(64 * chain_waves<K>()) void bwd_rstate_kernel(
   auto fetch = [&](Frags& f, int c) {
     const float* rc = rec_of(c);
 #pragma unroll
-    for (int j = 0; j < HCT; ++j) ld_kt(f, rc, j);
+    for (int t = 0; t < NTT; ++t) ld_kt(f, rc, t);
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
       ld_wt(f, rc, t);
@@ -505,24 +510,24 @@ __global__ __launch_bounds__(64 * chain_waves<K>()) void bwd_rstate_kernel(
     fence_compiler();
     // this wave's part of dDelta: Kt X over its rows, plus P^T dO on its own tiles
     f32x4 D[NTT];
+    // dO is exact in bf16 when it comes in bf16: its low part is zero
+    constexpr bool OX = sizeof(MT) == 2;
+    static_assert(NTT == 4, "two 32-token steps per chunk");
+    const X3<2> ox[2] = {x3_of(od[0], od[1]), x3_of(od[2], od[3])};
+    const X3<HCT> xx = x3_of<HCT>(X);
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) D[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < HCT; ++j) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int t = 0; t < NTT; ++t) D[t] = mfma4(f.kt[t][j][r], X[j][r], D[t]);
-      ld_kt(f, rn, j);
+    for (int t = 0; t < NTT; ++t) {
+      D[t] = x3_mma(x3_of<HCT>(f.kt[t]), xx, f32x4{0.f, 0.f, 0.f, 0.f});
+      ld_kt(f, rn, t);
       fence_compiler();
     }
+    // P^T dO on the wave's own tiles, over the 32-token steps at or right of the diagonal
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
       if (tt % NW == v)
 #pragma unroll
-        for (int t = tt; t < NTT; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) D[tt] = mfma4(f.pt[tt / NW][t][r], od[t][r], D[tt]);
+        for (int s2 = tt / 2; s2 < 2; ++s2)
+          D[tt] = x3_mma<OX>(x3_of(f.pt[tt / NW][2 * s2], f.pt[tt / NW][2 * s2 + 1]), ox[s2], D[tt]);
     ld_pt(f, rn);
     fence_compiler();
 #pragma unroll
@@ -537,12 +542,12 @@ __global__ __launch_bounds__(64 * chain_waves<K>()) void bwd_rstate_kernel(
     ld_gam(f, rn);
     fence_compiler();
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) {
+    for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int j = 0; j < HCT; ++j) A0[j] = mfma4(f.qt[j][t][r], od[t][r], A0[j]);
-      ld_qt(f, rn, t);
+      for (int j = 0; j < HCT; ++j)
+        A0[j] = x3_mma<OX>(x3_of(f.qt[j][2 * s2], f.qt[j][2 * s2 + 1]), ox[s2], A0[j]);
+      ld_qt(f, rn, 2 * s2);
+      ld_qt(f, rn, 2 * s2 + 1);
       fence_compiler();
     }
     lds_barrier();
@@ -563,12 +568,13 @@ __global__ __launch_bounds__(64 * chain_waves<K>()) void bwd_rstate_kernel(
     }
     // X_prev = diag(gamma) X + Qe^T dO - W^T dDelta
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) {
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const X3<2> dx = x3_of(dD[2 * s2], dD[2 * s2 + 1]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int j = 0; j < HCT; ++j) A1[j] = mfma4(f.wt[j][t][r], dD[t][r], A1[j]);
-      ld_wt(f, rn, t);
+      for (int j = 0; j < HCT; ++j)
+        A1[j] = x3_mma(x3_of(f.wt[j][2 * s2], f.wt[j][2 * s2 + 1]), dx, A1[j]);
+      ld_wt(f, rn, 2 * s2);
+      ld_wt(f, rn, 2 * s2 + 1);
       fence_compiler();
     }
 #pragma unroll
@@ -648,8 +654,8 @@ __global__ __launch_bounds__(NTGA, 8) void bwd_ga_kernel(
       load_block<VC, L, NTGA, BC, V>(sD, dDl + ch_h * BC * V + c0);
       load_block<VC, L, NTGA, K, V>(sS, S + c0);
       lds_barrier();
-      mmf_acc<K, VC, false, true, L, L, NTGA>(sO, sS, r1);
-      mmf_acc<K, VC, false, true, L, L, NTGA>(sD, sS, dw);
+      mmx_acc<K, VC, false, true, L, L, NTGA>(sO, sS, r1);
+      mmx_acc<K, VC, false, true, L, L, NTGA>(sD, sS, dw);
       lds_barrier();
     }
     mmf_out<K, NTGA>(r1, [&](int r, int m, float x) { sc[G::oR1 + r * K + m] = x; });
@@ -667,8 +673,8 @@ __global__ __launch_bounds__(NTGA, 8) void bwd_ga_kernel(
       load_block<VC, L, NTGA, BC, V>(sD, Dl + ch_h * BC * V + c0);
       load_block<VC, L, NTGA, K, V>(sS, X + c0);
       lds_barrier();
-      mmf_acc<K, VC, false, true, L, L, NTGA>(sD, sS, dk);
-      mmf_acc<BC, VC, false, true, L, L, NTGA>(sO, sD, dp);
+      mmx_acc<K, VC, false, true, L, L, NTGA>(sD, sS, dk);
+      mmx_acc<BC, VC, false, true, L, L, NTGA>(sO, sD, dp);
       lds_barrier();
     }
     mmf_out<K, NTGA>(dk, [&](int r, int m, float x) { sc[G::oDKt + r * K + m] = x; });

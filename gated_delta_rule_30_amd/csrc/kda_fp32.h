@@ -106,6 +106,115 @@ __device__ __forceinline__ void mmf_out(const f32x4* acc, F&& out) {
   }
 }
 
+// The same products with each fp32 operand split into two bf16 parts, x = hi + lo with
+// hi = bf16(x) and lo = bf16(x - hi), and each 16 x 16 x 32 step formed as hi*hi + hi*lo + lo*hi
+// on the bf16 matrix cores (three bf16 steps where the fp32 form takes eight 16 x 16 x 4 steps).
+// The dropped lo*lo term and the rounding of lo leave a relative error of at most about 3 * 2^-18
+// per product (both parts of x keep fp32's exponent range); the sums stay in fp32.
+// Operand fragment of a 32-step: lane (m, g) takes indices k + 4 g + e and k + 16 + 4 g + e
+// (e = 0..3) of row (or column) idx. ROW: element (idx, k) at M[idx * L + k] (two 16-byte
+// reads); otherwise at M[k * L + idx].
+__device__ __forceinline__ void x3_split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
+  hi = __builtin_convertvector(x, bf16x4);
+  lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x4), bf16x4);
+}
+template <bool ROW, int L>
+__device__ __forceinline__ void x3_frag(const float* M, int idx, int k, int g, bf16x8& hi, bf16x8& lo) {
+  f32x4 x0, x1;
+  if constexpr (ROW) {
+    x0 = *reinterpret_cast<const f32x4*>(M + idx * L + k + 4 * g);
+    x1 = *reinterpret_cast<const f32x4*>(M + idx * L + k + 16 + 4 * g);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x0[e] = M[(k + 4 * g + e) * L + idx];
+      x1[e] = M[(k + 16 + 4 * g + e) * L + idx];
+    }
+  }
+  bf16x4 h0, h1, l0, l1;
+  x3_split4(x0, h0, l0);
+  x3_split4(x1, h1, l1);
+  hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+  lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Register operands in the split form, for the state chains. An operand of a 16 x 16 x 16N
+// step (N = 1 or 2) is held as N f32x4 pieces: piece i of lane (m, g) is reduction indices
+// 16 i + 4 g .. + 3 (the fp32 16 x 16 x 4 steps' operands, four at a time). X3<N> is its split.
+template <int N> struct X3;
+template <> struct X3<1> { bf16x4 hi, lo; };
+template <> struct X3<2> { bf16x8 hi, lo; };
+__device__ __forceinline__ X3<1> x3_of(f32x4 x0) {
+  X3<1> r;
+  x3_split4(x0, r.hi, r.lo);
+  return r;
+}
+__device__ __forceinline__ X3<2> x3_of(f32x4 x0, f32x4 x1) {
+  bf16x4 h0, h1, l0, l1;
+  x3_split4(x0, h0, l0);
+  x3_split4(x1, h1, l1);
+  return X3<2>{__builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7),
+                __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7)};
+}
+template <int N>
+__device__ __forceinline__ X3<N> x3_of(const f32x4* x) {
+  if constexpr (N == 1) return x3_of(x[0]);
+  else return x3_of(x[0], x[1]);
+}
+__device__ __forceinline__ f32x4 mma_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
+  typedef __attribute__((ext_vector_type(4))) short s4;
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// acc + A B in the split form; B_EXACT: B's low part is zero (bf16 data), one step fewer
+template <bool B_EXACT = false, int N>
+__device__ __forceinline__ f32x4 x3_mma(const X3<N>& a, const X3<N>& b, f32x4 acc) {
+  acc = mma_bf16(a.lo, b.hi, acc);
+  if constexpr (!B_EXACT) acc = mma_bf16(a.hi, b.lo, acc);
+  return mma_bf16(a.hi, b.hi, acc);
+}
+// acc += the tile (r0, c0) of A B over k < R, by split-bf16 32-steps
+template <int R, bool TA, bool TB, int LA, int LB>
+__device__ __forceinline__ f32x4 x3_tile(const float* sA, const float* sB, int r0, int c0, f32x4 acc) {
+  static_assert(R % 32 == 0, "reduction steps of 32");
+  const int lm = threadIdx.x & 15, lg = (threadIdx.x >> 4) & 3;
+#pragma unroll 1
+  for (int k = 0; k < R; k += 32) {
+    bf16x8 ah, al, bh, bl;
+    x3_frag<!TA, LA>(sA, r0 + lm, k, lg, ah, al);
+    x3_frag<TB, LB>(sB, c0 + lm, k, lg, bh, bl);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+  }
+  return acc;
+}
+// mmf and mmf_acc in the split-bf16 form (same arguments, tiles and output mapping)
+template <int N, int R, bool TA, bool TB, int LA, int LB, int NTB, typename F>
+__device__ __forceinline__ void mmx(const float* sA, const float* sB, F&& out) {
+  constexpr int TILES = 4 * (N / 16), WAVES = NTB / 64;
+  const int wv = threadIdx.x >> 6, lm = threadIdx.x & 15, lg = (threadIdx.x >> 4) & 3;
+  for (int t = wv; t < TILES; t += WAVES) {
+    const int r0 = 16 * (t & 3), c0 = 16 * (t >> 2);
+    const f32x4 acc = x3_tile<R, TA, TB, LA, LB>(sA, sB, r0, c0, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out(r0 + 4 * lg + r, c0 + lm, acc[r]);
+  }
+}
+template <int N, int R, bool TA, bool TB, int LA, int LB, int NTB>
+__device__ __forceinline__ void mmx_acc(const float* sA, const float* sB, f32x4* acc) {
+  constexpr int TILES = 4 * (N / 16), WAVES = NTB / 64;
+  const int wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < mmf_tiles<N, NTB>(); ++i) {
+    const int t = wv + WAVES * i;
+    if (TILES % WAVES != 0 && t >= TILES) break;  // uniform per wave
+    acc[i] = x3_tile<R, TA, TB, LA, LB>(sA, sB, 16 * (t & 3), 16 * (t >> 2), acc[i]);
+  }
+}
+
 // Four consecutive elements as fp32.
 __device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ f32x4 load4(const bf16* p) {

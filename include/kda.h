@@ -227,8 +227,10 @@ kda_status kda_chunk_fwd_scan_ex(const void* q, const void* k, const void* v,
  * (same q, k, v, log_alpha, beta, init_state, cu_seqlens and shapes), by reverse mode through
  * the chunk form ("A Technical Breakdown", section 4; "Kimi Linear" explainer, "WY
  * Representation"): the chunk-start states are recomputed, the state gradient is carried
- * backwards chunk by chunk, and the per-token gradients of each chunk follow from it. All of
- * it runs in fp32.
+ * backwards chunk by chunk, and the per-token gradients of each chunk follow from it. Every
+ * stored value and every sum is fp32; the products of the two state chains and of S and X
+ * with the chunk's rows run on the bf16 matrix cores with each fp32 operand split into two
+ * bf16 parts (about 2^-16 relative error per product), the rest on the fp32 matrix cores.
  *   d_o            : [rows][H][V], dtype
  *   d_final_state  : [N][H][K][V] fp32, or NULL (zero)
  *   grad_q, grad_k, grad_log_alpha : [rows][H][K] fp32 (written)
