@@ -70,12 +70,18 @@ struct VecN {
 };
 
 // ====================================================================== chunk table
-// Entries are ordered depth-major (chunk d of every sequence that has one, then chunk d+1),
-// so one segment advances many sequences at once and short sequences drop out early. Within a
-// depth, sequences are ordered by decreasing chunk count (ties by index). With r_n the rank of
-// sequence n in that order, every sequence ranked before n has at least as many chunks, so
-//     pos(n, d) = base[d] + r_n,   base[d] = sum_{n'} min(nc_{n'}, d),
-// and a sequence's chunk indices follow from base[] alone, without walking the table.
+// Two orders, chosen per call from the head count (ChunkPlan::seq_major):
+//  - depth-major (chunk d of every sequence that has one, then chunk d+1): one segment
+//    advances many sequences at once and short sequences drop out early, which keeps the chip
+//    busy when one sequence's chains (H heads x V/16 slices) are few. Within a depth,
+//    sequences are ordered by decreasing chunk count (ties by index). With r_n the rank of
+//    sequence n in that order, every sequence ranked before n has at least as many chunks, so
+//        pos(n, d) = base[d] + r_n,   base[d] = sum_{n'} min(nc_{n'}, d),
+//    and a sequence's chunk indices follow from base[] alone, without walking the table;
+//  - sequence-major (token order): pos(n, d) = sum_{n' < n} nc_{n'} + d. Where one sequence's
+//    chains fill the chip by themselves, a segment then holds long runs of one or two
+//    sequences instead of E / N chunks of each of N, and a chain pays its start (state load,
+//    the first chunk's record loads) once per segment rather than once every few chunks.
 struct SeqView {
   const int32_t* cu;
   int num_seqs;
@@ -92,16 +98,18 @@ __global__ __launch_bounds__(256) void table_kernel(SeqView sv, int H, int64_t K
                                                     float* __restrict__ fin,
                                                     Entry* __restrict__ entries,
                                                     int32_t* __restrict__ header,
-                                                    int32_t* __restrict__ basetab) {
+                                                    int32_t* __restrict__ basetab, int seq_major) {
   const int n = blockIdx.x;
   const int64_t len = sv.len(n);
   const int64_t nc = sv.nchunks(n);
-  // rank of n: sequences with more chunks, or as many and a smaller index, come first
+  // depth-major: the rank of n (sequences with more chunks, or as many and a smaller index,
+  // come first); sequence-major: the chunks of the sequences before n
   __shared__ int64_t red[256];
   int64_t rk = 0;
   for (int j = threadIdx.x; j < sv.num_seqs; j += blockDim.x) {
     const int64_t cj = sv.nchunks(j);
-    rk += (cj > nc || (cj == nc && j < n)) ? 1 : 0;
+    if (seq_major) rk += j < n ? cj : 0;
+    else rk += (cj > nc || (cj == nc && j < n)) ? 1 : 0;
   }
   red[threadIdx.x] = rk;
   __syncthreads();
@@ -110,7 +118,22 @@ __global__ __launch_bounds__(256) void table_kernel(SeqView sv, int H, int64_t K
     __syncthreads();
   }
   const int64_t rank = red[0];
-  for (int64_t d = threadIdx.x; d < nc; d += blockDim.x) {
+  if (seq_major) {
+    for (int64_t d = threadIdx.x; d < nc; d += blockDim.x) {
+      const int64_t pos = rank + d;
+      Entry en;
+      en.seq = n;
+      en.tok = (int32_t)(sv.start(n) + d * CHUNK);
+      en.len = (int32_t)min((int64_t)CHUNK, len - d * CHUNK);
+      en.depth = (int32_t)d;
+      en.prev = d > 0 ? (int32_t)(pos - 1) : -1;
+      en.next = d + 1 < nc ? (int32_t)(pos + 1) : -1;
+      en.end = (int32_t)(sv.start(n) + len);
+      en.pad = 0;
+      if (pos < ub) entries[pos] = en;  // always true for a well-formed cu_seqlens
+    }
+  }
+  for (int64_t d = threadIdx.x; d < (seq_major ? 0 : nc); d += blockDim.x) {
     int64_t base = 0, cnt = 0, cntm = 0;  // base[d], #{nc > d}, #{nc > d-1}
     for (int j = 0; j < sv.num_seqs; ++j) {
       const int64_t cj = sv.nchunks(j);
@@ -956,7 +979,7 @@ struct StateParams {
   float* state;  // running and final state [N][H][K][V]
   const Entry* entries;
   const int32_t* header;
-  const int32_t* basetab;    // base[d] of the chunk table
+  const int32_t* basetab;    // base[d] of the chunk table (depth-major order)
   const int32_t* seg_first;  // this segment's list
   const int32_t* seg_count;  // this segment's count
   int64_t seg_begin, E;
@@ -965,6 +988,7 @@ struct StateParams {
   const char* rec;
   uint32_t rec_bytes;
   uint32_t rec_buf_bytes;  // the whole record buffer (addressed with 32-bit offsets)
+  int seq_major;           // the chunk table's order
 };
 
 constexpr int STATE_THREADS = 64;
@@ -1034,12 +1058,12 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
   // entry base[d0+k] + rank; the run ends at the sequence's end or the segment's end.
   const int seq_start = en.tok - CHUNK * en.depth;
   const int nc = (en.end - seq_start + CHUNK - 1) / CHUNK;
-  const int64_t rank = e0 - p.basetab[en.depth];
+  const int64_t rank = p.seq_major ? 0 : e0 - p.basetab[en.depth];
   const int kmax = (int)min((int64_t)(nc - en.depth), p.E);
   if (lane == 0) sLen = kmax;
   __syncthreads();
   for (int k = lane; k < kmax; k += STATE_THREADS) {
-    const int64_t ek = p.basetab[en.depth + k] + rank;
+    const int64_t ek = p.seq_major ? e0 + k : p.basetab[en.depth + k] + rank;
     sRun[k] = (int32_t)(ek - p.seg_begin);
     if (ek >= seg_end) atomicMin(&sLen, k);
   }
@@ -1343,12 +1367,12 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
 
   const int seq_start = en.tok - CHUNK * en.depth;
   const int nc = (en.end - seq_start + CHUNK - 1) / CHUNK;
-  const int64_t rank = e0 - p.basetab[en.depth];
+  const int64_t rank = p.seq_major ? 0 : e0 - p.basetab[en.depth];
   const int kmax = (int)min((int64_t)(nc - en.depth), p.E);
   if (tid == 0) sLen = kmax;
   __syncthreads();
   for (int k = tid; k < kmax; k += SS::THREADS) {
-    const int64_t ek = p.basetab[en.depth + k] + rank;
+    const int64_t ek = p.seq_major ? e0 + k : p.basetab[en.depth + k] + rank;
     sRun[k] = (int32_t)(ek - p.seg_begin);
     if (ek >= seg_end) atomicMin(&sLen, k);
   }
@@ -1675,6 +1699,10 @@ bool make_chunk_plan(int N, int64_t T, int H, int K, int V, bool bf16, ChunkPlan
   // V split: slices of 16 columns, one wave each
   p->n_slices = V / 16;
   p->vs = 16;
+  // sequence-major once one sequence's chains at V = 128 (H heads x 8 slices) cover 256 CUs;
+  // a function of H alone, so that calls on the same packing with other V (the scan's two
+  // passes over one set of records) order the table alike
+  p->seq_major = (int64_t)H * 8 >= 256 ? 1 : 0;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = 0;
   p->off_header = off;
@@ -1724,7 +1752,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl, const 
   SeqView sv{a.cu_seqlens, a.num_seqs, a.total_tokens};
   hipLaunchKernelGGL(table_kernel, dim3(a.num_seqs), dim3(256), 0, st, sv, a.num_heads,
                      (int64_t)a.dk * a.dv, pl.ub_entries, a.init_state, a.final_state, entries,
-                     header, basetab);
+                     header, basetab, pl.seq_major);
   if (pl.num_segs == 0) return hipGetLastError();
   hipLaunchKernelGGL(segment_kernel, dim3(pl.num_segs), dim3(256), 0, st, entries, header,
                      pl.seg_entries, pl.slots, seg_first, seg_count);
@@ -1773,7 +1801,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl, const 
     StateParams sp{a.v, a.o, a.init_state, run_state, entries, header, basetab,
                    seg_first + s * pl.slots, seg_count + s, s * pl.seg_entries, pl.seg_entries,
                    a.num_heads, a.dv, pl.n_slices, chains, seg_rec(s), (uint32_t)rb,
-                   (uint32_t)seg_buf};
+                   (uint32_t)seg_buf, pl.seq_major};
     if (pl.vs != 16) return false;
     if constexpr (UFORM_OK) {
       if (urec) {

@@ -53,6 +53,7 @@ struct ChunkPlan {
   int64_t rec_bytes;    // bytes of one (chunk, head) record
   int n_slices;         // V split into n_slices slices of vs columns
   int vs;
+  int seq_major;        // chunk table order: 1 sequence-major (token order), 0 depth-major
   // workspace offsets (bytes)
   size_t off_header, off_entries, off_basetab, off_seg_first, off_seg_count, off_state,
       off_rec, rec_buf_bytes;

@@ -122,6 +122,31 @@ def test_head_dims_ragged_varlen(dtype, K, V):
     assert torch.equal(fin[4], inp["init_state"][4])
 
 
+def test_ragged_varlen_many_heads():
+    # At 32 heads the chunk table is ordered sequence by sequence (at 3 heads, above, chunk
+    # index by chunk index): empty and one-token sequences, runs that cross the 64-chunk
+    # segments, several sequences in one segment; against the oracle, and each sequence
+    # against the same sequence run alone (equal bit for bit).
+    lengths = [1, 0, 4200, 63, 64, 65, 2000, 0, 129]
+    T, H, K, V = sum(lengths), 32, 64, 64
+    inp = _gen(T, H, K, V, torch.bfloat16, seed=31, N=len(lengths))
+    cu = _cu(lengths)
+    o, fin = _fwd(inp, cu=cu)
+    o_ref, f_ref = oracle_fwd(inp, cu=cu)
+    assert_close(np64(o), o_ref, torch.bfloat16, "o")
+    assert_close(np64(fin), f_ref, torch.bfloat16, "final")
+    assert torch.equal(fin[1], inp["init_state"][1])
+    s = 0
+    for n, L in enumerate(lengths):
+        if n in (2, 5):
+            part = {x: inp[x][s:s + L].contiguous() for x in ORDER}
+            part["init_state"] = inp["init_state"][n:n + 1].contiguous()
+            on, fn = _fwd(part)
+            assert torch.equal(on, o[s:s + L])
+            assert torch.equal(fn[0], fin[n])
+        s += L
+
+
 @pytest.mark.parametrize("dtype,K,V,lg,every", [
     (torch.bfloat16, 128, 64, -8.0, 3),
     (torch.bfloat16, 128, 128, -30.0, 3),
