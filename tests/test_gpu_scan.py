@@ -150,6 +150,7 @@ def test_scan_several_record_segments():
     ([1500, 260, 2048], 1, 128, torch.bfloat16, 16, "uniform"),
     ([700, 0, 1300, 65], 2, 32, torch.float32, 3, "slow"),
     ([900, 2000], 1, 64, torch.float32, 1, "uniform"),   # one group per sequence
+    ([1000, 0, 65, 1500], 32, 64, torch.bfloat16, 4, "uniform"),  # chunk table in token order
 ])
 def test_scan_varlen(lengths, H, K, dtype, G, gates):
     """kda_chunk_fwd_scan_ex over packed sequences of different lengths (empty and one-token
