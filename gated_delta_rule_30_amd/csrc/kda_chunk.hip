@@ -213,6 +213,13 @@ template <int SH>
 __device__ __forceinline__ float row_shr(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + SH, 0xf, 0xf, true));
 }
+// Issue priority of the calling wave (0 .. 3; s_setprio takes an immediate).
+__device__ __forceinline__ void wave_prio(int p) {
+  if (p >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (p == 2) __builtin_amdgcn_s_setprio(2);
+  else if (p == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
 // The value of lane 15 of each 16-lane row, in every lane of that row (DPP row_newbcast:15).
 __device__ __forceinline__ float row_last(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x15F, 0xf, 0xf, false));
@@ -675,6 +682,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   // block w, scaled per channel by D_{Iw}) is this wave's own kc; the row operands are read as
   // fragments. Results stay in registers until every wave is done with Q^, K^ and D.
   f32x4 tA[NSUB], tP[NSUB];
+  wave_prio(NSUB - 1 - w);  // wave w forms NSUB - w blocks: the busiest issue first
 #pragma unroll
   for (int I = 0; I < NSUB; ++I) {
     tA[I] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -703,6 +711,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
       tP[I] = Mma<MT>::mma(*reinterpret_cast<const frag*>(sQh + slot), bfr, tP[I]);
     }
   }
+  wave_prio(0);
   lds_barrier();
   // A (row-scaled by beta, strictly lower) -> sA for the off-diagonal blocks; P (lower with the
   // diagonal, zero above) -> sPnT, transposed. The diagonal block A_ww stays in registers for
@@ -790,6 +799,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
   }
   if (w >= 1) {
     const int Ib = w;
+    wave_prio(w);  // row block w has w blocks to solve, one after another
     auto tblock = [&](int I, int M) -> float* {  // base of T_IM (I >= M)
       return (I == M) ? sA + (16 * I) * L::LCF + 16 * I : sA + (16 * M) * L::LCF + 16 * I;
     };
@@ -808,6 +818,7 @@ __global__ __launch_bounds__(PREP_THREADS, 2) void prep_kernel(PrepParams p) {
       const f32x4 Y = Mma<float>::mma(tjj, X, f32x4{0.f, 0.f, 0.f, 0.f});  // (T_IJ)^T
       *reinterpret_cast<f32x4*>(tblock(Ib, J) + m * L::LCF + 4 * g) = -Y;
     }
+    wave_prio(0);
   }
   lds_barrier();
 
