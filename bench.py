@@ -359,7 +359,7 @@ def main():
                 "kernel": "kda_chunk_fwd call (table, segment, then prep + state kernel per segment)"}
     roofline_decode = {"bound": "hbm", "achieved": db / decode_s / 1e9, "peak": PEAK_HBM / 1e9,
                        "unit": "GB/s", "frac": db / decode_s / PEAK_HBM, "traffic": traffic_decode,
-                       "kernel": "decode_step_kernel<128,128,bf16>"}
+                       "kernel": "decode_step_kernel<128,128,bf16,false>"}
     value = (T + Nd) / (ms_per_step * 1e-3)
 
     # ---------------- the input options on the same shapes, timed after the headline steps:

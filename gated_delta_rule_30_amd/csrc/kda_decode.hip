@@ -78,7 +78,8 @@ __device__ __forceinline__ f32x4 shfl_xor4(f32x4 x, int off) {
                __shfl_xor(x[3], off)};
 }
 
-template <int K, int V, typename TI>
+// L2N: the unit-norm option (a compile-time case, so that the plain kernel carries none of it).
+template <int K, int V, typename TI, bool L2N>
 __global__ __launch_bounds__((DecodeShape<K, V>::TPB)) void decode_step_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const TI* __restrict__ g, const TI* __restrict__ beta, float* __restrict__ state,
@@ -93,6 +94,24 @@ __global__ __launch_bounds__((DecodeShape<K, V>::TPB)) void decode_step_kernel(
   const int tid = threadIdx.x;
   const int cg = tid % CG;
   const int rg = tid / CG;
+  const TI* qh = q + (size_t)head * K;
+  const TI* kh = k + (size_t)head * K;
+
+  // unit-norm k and q: every wave sums the squares of the whole k and q (K <= 256 values),
+  // and the sums that are linear in k or q are scaled afterwards. Their loads go out before
+  // the state's, and the sums are formed while the state is in flight, so that the option adds
+  // no step between the state's arrival and its store.
+  constexpr int NKL = L2N ? (K + 63) / 64 : 1;
+  float kn[NKL], qn[NKL];
+  if constexpr (L2N) {
+    const int lane = tid & 63;
+#pragma unroll
+    for (int j = 0; j < NKL; ++j) {
+      const int c = min(lane + 64 * j, K - 1);  // lanes past K (K = 32) repeat an element
+      kn[j] = to_f32(kh[c]);
+      qn[j] = to_f32(qh[c]);
+    }
+  }
 
   // column group cg of this slice, row 0; row r is V / 4 vectors further
   f32x4* S = reinterpret_cast<f32x4*>(state + (size_t)head * K * V + col0) + cg;
@@ -100,8 +119,25 @@ __global__ __launch_bounds__((DecodeShape<K, V>::TPB)) void decode_step_kernel(
 #pragma unroll
   for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(&S[(rg + RG * i) * (V / 4)]);
 
-  const TI* qh = q + (size_t)head * K;
-  const TI* kh = k + (size_t)head * K;
+  float nk = 1.f, nq = 1.f;
+  if constexpr (L2N) {
+    const int lane = tid & 63;
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int j = 0; j < NKL; ++j) {
+      const bool in = lane + 64 * j < K;
+      sk += in ? kn[j] * kn[j] : 0.f;
+      sq += in ? qn[j] * qn[j] : 0.f;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      sk += __shfl_xor(sk, off);
+      sq += __shfl_xor(sq, off);
+    }
+    nk = 1.f / sqrtf(sk + L2NORM_EPS);
+    nq = 1.f / sqrtf(sq + L2NORM_EPS);
+  }
+
   const bool scalar_gate = (opts & OPT_SCALAR_GATE) != 0;
   const bool gate_logits = (opts & OPT_GATE_LOGITS) != 0;
   const TI* gh = g + (size_t)head * (scalar_gate ? 1 : K);
@@ -120,26 +156,6 @@ __global__ __launch_bounds__((DecodeShape<K, V>::TPB)) void decode_step_kernel(
     pkq += kk[i] * qq;
   }
 
-  // unit-norm k and q: every wave sums the squares of the whole k and q (K <= 256 values),
-  // and the sums that are linear in k or q are scaled afterwards
-  float nk = 1.f, nq = 1.f;
-  if (opts & OPT_L2NORM_QK) {
-    const int lane = tid & 63;
-    float sk = 0.f, sq = 0.f;
-#pragma unroll
-    for (int c = lane; c < K; c += 64) {
-      const float x = to_f32(kh[c]), y = to_f32(qh[c]);
-      sk += x * x;
-      sq += y * y;
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      sk += __shfl_xor(sk, off);
-      sq += __shfl_xor(sq, off);
-    }
-    nk = 1.f / sqrtf(sk + L2NORM_EPS);
-    nq = 1.f / sqrtf(sq + L2NORM_EPS);
-  }
   float b = to_f32(beta[head]);
   if (opts & OPT_BETA_LOGITS) b = sigmoid_f(b);
 
@@ -184,10 +200,15 @@ __global__ __launch_bounds__((DecodeShape<K, V>::TPB)) void decode_step_kernel(
 template <int K, int V, typename TI>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int heads = a.num_seqs * a.num_heads;
-  hipLaunchKernelGGL((decode_step_kernel<K, V, TI>), dim3(heads * DecodeShape<K, V>::NSL),
-                     dim3(DecodeShape<K, V>::TPB), 0,
-                     (hipStream_t)a.stream, (const TI*)a.q, (const TI*)a.k, (const TI*)a.v,
-                     (const TI*)a.g, (const TI*)a.beta, a.state, (TI*)a.o, a.options);
+  const dim3 grid(heads * DecodeShape<K, V>::NSL), block(DecodeShape<K, V>::TPB);
+  if (a.options & OPT_L2NORM_QK)
+    hipLaunchKernelGGL((decode_step_kernel<K, V, TI, true>), grid, block, 0, (hipStream_t)a.stream,
+                       (const TI*)a.q, (const TI*)a.k, (const TI*)a.v, (const TI*)a.g,
+                       (const TI*)a.beta, a.state, (TI*)a.o, a.options);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<K, V, TI, false>), grid, block, 0, (hipStream_t)a.stream,
+                       (const TI*)a.q, (const TI*)a.k, (const TI*)a.v, (const TI*)a.g,
+                       (const TI*)a.beta, a.state, (TI*)a.o, a.options);
   return hipGetLastError();
 }
 
