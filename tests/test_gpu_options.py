@@ -107,6 +107,8 @@ def test_chunk_options_match_recurrent():
     (0, torch.bfloat16, 256, 128, 2, 2),
     (BL, torch.float32, 32, 256, 4, 1),
     (GL | L2, torch.bfloat16, 128, 128, 4, 4),
+    (BL | L2, torch.bfloat16, 32, 64, 3, 2),   # unit norm over fewer key channels than lanes
+    (SG | L2, torch.float32, 64, 32, 2, 3),
 ])
 def test_decode_options(opts, dtype, K, V, N, H):
     print("decode options", opts, dtype, K, V, N, H, flush=True)
