@@ -1295,7 +1295,8 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
 // The chain of one (sequence run, head, 16-column slice) split by key channels over the two
 // waves of a workgroup: wave w holds rows [w K/2, (w+1) K/2) of S and streams only the record
 // fragments of its half -- -W and Qe over its reduction steps, Ktilde^T over its rows -- plus
-// T' of the next chunk (wave 0) or P (wave 1). Per chunk:
+// T' of the next chunk (wave 0; in the record's U form that chunk's U instead) or P (wave 1).
+// Per chunk:
 //   Delta_w = [U] + (-W_w) S_w       partial over this wave's half of K (wave 0 starts from U)
 //   exchange Delta_w through LDS, Delta = Delta_0 + Delta_1 (fp32), one barrier
 //   S_w' = Diag(gamma_w) S_w + Ktilde_w^T Delta
@@ -1488,10 +1489,10 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
         U[2 * pp + 1] = __builtin_convertvector(__builtin_shufflevector(x[pp], x[pp], 4, 5, 6, 7), f32x4);
       }
     };
-    bf16x8 unext[UW0 ? 2 : 1][2];
+    bf16x8 unext[2];  // the U form: the next chunk's U, loaded a chunk ahead
     if constexpr (UW0) {
-      load_u(rc0, unext[0]);
-      set_u(unext[0]);
+      load_u(rc0, unext);
+      set_u(unext);
     } else if constexpr (WV == 0) {
       load_v(rc0, vx);
       stage_v(vx);
@@ -1540,7 +1541,7 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
       } else {
         load_gam(rc0, gcur);
       }
-      if constexpr (UW0) load_u(rc1, unext[0]);  // the next chunk's U
+      if constexpr (UW0) load_u(rc1, unext);  // the next chunk's U
       __builtin_amdgcn_sched_barrier(0);
 
       frag Sb[HKS], Db[NTS];
@@ -1618,7 +1619,7 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
       // waves without the T'V / P Delta operations never reach the reset at NA + NB: their next
       // Delta partial starts from zero here
       if constexpr (UW0) {
-        set_u(unext[0]);  // the U form: the next chunk's Delta partial starts from its U
+        set_u(unext);  // the U form: the next chunk's Delta partial starts from its U
       } else if constexpr (NFW == NA + NB) {
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
