@@ -477,6 +477,26 @@ def main():
         ew1.record()
         torch.cuda.synchronize()
         wms = ew0.elapsed_time(ew1) / wsteps
+        # the same shape with every input option (applied inside the record kernel)
+        wopts = (kda.OPT_SCALAR_GATE | kda.OPT_GATE_LOGITS | kda.OPT_BETA_LOGITS |
+                 kda.OPT_L2NORM_QK)
+        del winp
+        winp = workloads.gen_raw(T, H, Kw, Vw, wopts, dtype=torch.bfloat16, device=dev,
+                                 seed=wl["seed"] + 14, init_std=wl["init_std"])
+
+        def wide_opt_call():
+            kda.chunk_fwd(*(winp[x] for x in names), init_state=winp["init_state"], o=ow,
+                          final_state=fw, workspace=wsw, options=wopts)
+
+        for _ in range(max(1, min(args.warmup, 2))):
+            wide_opt_call()
+        torch.cuda.synchronize()
+        ew0.record()
+        for _ in range(wsteps):
+            wide_opt_call()
+        ew1.record()
+        torch.cuda.synchronize()
+        wms_opt = ew0.elapsed_time(ew1) / wsteps
         wfl = chunk_alg_flops(T, H, Kw, Vw)
         wb = chunk_alg_bytes(T, H, Kw, Vw, 2, 1, True, True)
         # bf16 inputs, no options: the fp32 record kernel and the bf16 matrix-core chain
@@ -485,7 +505,9 @@ def main():
                 "ms": wms, "calls": wsteps, "tokens_per_s": T / (wms * 1e-3),
                 "alg_bytes": wb, "hbm_frac": wb / (wms * 1e-3) / PEAK_HBM,
                 "alg_flops": wfl, "mfma_frac_alg": wfl / (wms * 1e-3) / PEAK_BF16,
-                "workspace_GB": wsw.numel() / 1e9}
+                "workspace_GB": wsw.numel() / 1e9,
+                "with_options": {"options": "SCALAR_GATE|GATE_LOGITS|BETA_LOGITS|L2NORM_QK",
+                                 "ms": wms_opt, "tokens_per_s": T / (wms_opt * 1e-3)}}
         del winp, ow, fw, wsw
 
     # ---------------- the other prefill workloads: 16 packed sequences of log-uniform lengths

@@ -13,11 +13,10 @@ bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128 || d == 25
 // fp32 record kernel with the key channels in parts of 64 instead)
 bool supported_chunk_dk(int32_t d) { return d == 32 || d == 64 || d == 128; }
 constexpr int32_t kWideDk = 256;
-// the fp32 wide-key path: fp32 inputs at K >= 128, and K = 256 with input options (bf16 inputs
-// at K = 256 without options run the chunk path: an fp32 record kernel and the bf16 chain)
-bool wide_path(int32_t dk, kda_dtype dtype, uint32_t options) {
-  return (dk == kWideDk && (dtype == KDA_DTYPE_F32 || options != 0)) ||
-         (dk == 128 && dtype == KDA_DTYPE_F32);
+// the fp32 wide-key path: fp32 inputs at K >= 128 (bf16 inputs at K = 256, with or without
+// input options, run the chunk path: an fp32 record kernel and the bf16 chain)
+bool wide_path(int32_t dk, kda_dtype dtype, uint32_t) {
+  return dtype == KDA_DTYPE_F32 && (dk == kWideDk || dk == 128);
 }
 constexpr uint32_t kAllOptions =
     KDA_OPT_SCALAR_GATE | KDA_OPT_GATE_LOGITS | KDA_OPT_BETA_LOGITS | KDA_OPT_L2NORM_QK;
@@ -64,9 +63,8 @@ extern "C" size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_t
                                                int32_t num_heads, int32_t dk, int32_t dv,
                                                kda_dtype dtype) {
   if (check_chunk_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype) != KDA_SUCCESS) return 0;
-  // (the options are not known here: at K = 256 bf16 the larger of the two paths' needs)
   size_t need = 0;
-  if (wide_path(dk, dtype, 0u) || (dk == kWideDk && dtype == KDA_DTYPE_BF16)) {
+  if (wide_path(dk, dtype, 0u)) {
     kda::WidePlan wp;
     if (!kda::make_wide_plan(num_seqs, total_tokens, num_heads, dk, dv, &wp)) return 0;
     need = wp.total_bytes;

@@ -1784,7 +1784,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl, const 
   auto prep = [&](int64_t s, hipStream_t q) {
     if constexpr (K == 256) {  // the fp32 record kernel of 256 key channels
       const Rec256Params rp{a.q, a.k, a.v, a.g, a.beta, entries, header, a.num_heads, a.dv,
-                            s * pl.seg_entries, pl.seg_entries, seg_rec(s), rb};
+                            s * pl.seg_entries, pl.seg_entries, seg_rec(s), rb, a.options};
       launch_rec256(rp, q);
     } else {
       PrepParams pp{a.q, a.k, a.g, a.beta, entries, header, a.num_heads, s * pl.seg_entries,
@@ -1843,7 +1843,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, const ChunkPlan& pl, const Recor
     if (a.dk == 32) return launch_chunk_t<32, bf16>(a, pl, rr);
     if (a.dk == 64) return launch_chunk_t<64, bf16>(a, pl, rr);
     if (a.dk == 128) return launch_chunk_t<128, bf16>(a, pl, rr);
-    if (a.dk == 256 && a.options == 0) return launch_chunk_t<256, bf16>(a, pl, rr);
+    if (a.dk == 256) return launch_chunk_t<256, bf16>(a, pl, rr);
   } else {
     if (a.dk == 32) return launch_chunk_t<32, float>(a, pl, rr);
     if (a.dk == 64) return launch_chunk_t<64, float>(a, pl, rr);

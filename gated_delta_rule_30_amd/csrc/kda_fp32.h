@@ -295,11 +295,12 @@ __device__ __forceinline__ void load_block(float* dst, const float* src) {
   }
 }
 
-// Cumulative log2 decay: sB (64 x K, stride L) holds log alpha on entry, b * log2 e on exit.
+// Cumulative log2 decay: sB (64 x K, stride L) holds log alpha on entry, b * log2 e on exit
+// (scale = 1: sB already holds log2 alpha).
 // P = NTB / K neighbouring threads share a channel: each sums its 64 / P consecutive rows, the
 // running totals of the P threads are scanned with shuffles, and each adds its prefix.
 template <int K, int L, int NTB>
-__device__ __forceinline__ void cumsum_log2(float* sB) {
+__device__ __forceinline__ void cumsum_log2(float* sB, float scale = LOG2E) {
   constexpr int P = NTB / K, RP = BC / P;
   static_assert(P >= 1 && P <= 32 && RP >= 1, "threads per channel");
   const int c = threadIdx.x / P, part = threadIdx.x % P;
@@ -318,7 +319,7 @@ __device__ __forceinline__ void cumsum_log2(float* sB) {
   }
   pre -= run;  // the rows before this thread's
 #pragma unroll
-  for (int r = 0; r < RP; ++r) sB[(part * RP + r) * L + c] = (x[r] + pre) * LOG2E;
+  for (int r = 0; r < RP; ++r) sB[(part * RP + r) * L + c] = (x[r] + pre) * scale;
 }
 
 

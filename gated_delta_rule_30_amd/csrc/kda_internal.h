@@ -108,6 +108,7 @@ struct Rec256Params {
   int64_t seg_begin, E;
   char* rec;
   int64_t rec_bytes;
+  uint32_t opts;  // input option bits (OPT_*)
 };
 void launch_rec256(const Rec256Params& p, hipStream_t st);
 

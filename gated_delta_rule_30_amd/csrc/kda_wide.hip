@@ -127,13 +127,65 @@ __global__ __launch_bounds__(NTP, 4) void wide_prep_kernel(
   }
 }
 
-// Records of the chunk path at 256 key channels (bf16 inputs, no input options): the same
-// chunk form as wide_prep_kernel, in fp32 with the key channels in parts of 64, written as the
-// bf16 MFMA fragment records that prep_kernel writes for K <= 128 -- -W, Qe, Ktilde^T, T' =
+// Records of the chunk path at 256 key channels (bf16 inputs): the same chunk form as
+// wide_prep_kernel, in fp32 with the key channels in parts of 64, written as the bf16 MFMA
+// fragment records that prep_kernel writes for K <= 128 -- -W, Qe, Ktilde^T, T' =
 // T diag(beta), P, gamma and V slice-major -- so that state_split_kernel runs the chain on the
 // bf16 matrix cores. One workgroup of 512 threads per (chunk, head) of the segment: task j is
 // entry seg_begin + j of the chunk table. Each thread writes one 16-byte fragment slot of a
 // 4 x 2 block of slots (token or channel tile ft, reduction step fsl) per matrix part.
+// OPTS = true applies the input options to the raw inputs as they are read, in fp32, as
+// prep_kernel does at K <= 128: q and k scaled by their inverse L2 norms over the 256 channels
+// (formed in a pass before the parts), log2 alpha = log2 sigmoid(z) for gate logits (one value
+// per token with the scalar gate), beta = sigmoid(x) for beta logits.
+
+// The part's log2 alpha (c0 .. c0 + N - 1 of a [T][H][NTOT] tensor, or of [T][H] for the
+// scalar gate) into dst, zero past len; the same thread-to-element map as load_rows.
+template <int N, int L, int NTB, int NTOT>
+__device__ __forceinline__ void gate_rows_opts(float* dst, const bf16* g, int64_t tok, int len,
+                                               int H, int h, int c0, uint32_t opts) {
+  constexpr int PIECES = BC * N / 4, PT = PIECES / NTB;
+  static_assert(PIECES % NTB == 0, "whole pieces per thread");
+  const bool scalar = (opts & OPT_SCALAR_GATE) != 0, logits = (opts & OPT_GATE_LOGITS) != 0;
+  f32x4 t[PT];
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = threadIdx.x + NTB * u;
+    const int r = e / (N / 4), c = 4 * (e % (N / 4));
+    const int64_t row = (tok + min(r, len - 1)) * H + h;
+    if (scalar) {
+      const float z = to_f32(g[row]);
+      t[u] = f32x4{z, z, z, z};
+    } else {
+      t[u] = load4(g + row * (int64_t)NTOT + c0 + c);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = threadIdx.x + NTB * u;
+    const int r = e / (N / 4), c = 4 * (e % (N / 4));
+    f32x4 x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      x[j] = r < len ? (logits ? log2_sigmoid(t[u][j]) : t[u][j] * LOG2E) : 0.f;
+    *reinterpret_cast<f32x4*>(dst + r * L + c) = x;
+  }
+}
+
+// dst[r][c] *= sc[r] over the elements this thread wrote in load_rows (no barrier needed).
+template <int N, int L, int NTB>
+__device__ __forceinline__ void scale_rows(float* dst, const float* sc) {
+  constexpr int PIECES = BC * N / 4, PT = PIECES / NTB;
+  static_assert(PIECES % NTB == 0, "whole pieces per thread");
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = threadIdx.x + NTB * u;
+    const int r = e / (N / 4), c = 4 * (e % (N / 4));
+    *reinterpret_cast<f32x4*>(dst + r * L + c) *= sc[r];
+  }
+}
+
+template <bool OPTS>
 __global__ __launch_bounds__(NTP, 4) void rec256_kernel(Rec256Params p) {
   constexpr int KW = 256;
   using R = Rec<KW, bf16>;
@@ -163,16 +215,60 @@ __global__ __launch_bounds__(NTP, 4) void rec256_kernel(Rec256Params p) {
     for (int el = 0; el < 8; ++el) f[el] = (bf16)x[el];
     *reinterpret_cast<bf16x8*>(recM + elem) = f;
   };
-  if (tid < BC) sBeta[tid] = tid < len ? to_f32(beta[(tok + tid) * H + h]) : 0.f;
+  const uint32_t opts = OPTS ? p.opts : 0u;
+  __shared__ float sNq[OPTS ? BC : 1], sNk[OPTS ? BC : 1];  // inverse L2 norms of q and k rows
+  if (tid < BC) {
+    float b = tid < len ? to_f32(beta[(tok + tid) * H + h]) : 0.f;
+    if (opts & OPT_BETA_LOGITS) b = tid < len ? sigmoid_f(b) : 0.f;
+    sBeta[tid] = b;
+  }
+  if constexpr (OPTS) {
+    if (opts & OPT_L2NORM_QK) {
+      // eight threads per token row, 32 channels each (rows past len repeat the last token)
+      static_assert(NTP == 8 * BC, "eight threads per row");
+      const int r = tid >> 3, part = tid & 7;
+      const int64_t row = ((tok + min(r, len - 1)) * H + h) * (int64_t)KW + 32 * part;
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 xq = *reinterpret_cast<const bf16x8*>(q + row + 8 * i);
+        const bf16x8 xk = *reinterpret_cast<const bf16x8*>(k + row + 8 * i);
+#pragma unroll
+        for (int el = 0; el < 8; ++el) {
+          const float a = (float)xq[el], b = (float)xk[el];
+          sq += a * a;
+          sk += b * b;
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        sq += __shfl_xor(sq, o);
+        sk += __shfl_xor(sk, o);
+      }
+      if (part == 0) {
+        sNq[r] = 1.f / sqrtf(sq + L2NORM_EPS);
+        sNk[r] = 1.f / sqrtf(sk + L2NORM_EPS);
+      }
+    }
+    lds_barrier();
+  }
   PairAcc acc;
   pair_acc_init<NTP>(acc);
   for (int hh = 0; hh < KW / KQ; ++hh) {
     const int c0 = hh * KQ;
     load_rows<KQ, LKQ, NTP, bf16, KW>(sQ, q, tok, len, H, h, c0);
     load_rows<KQ, LKQ, NTP, bf16, KW>(sK, k, tok, len, H, h, c0);
-    load_rows<KQ, LKQ, NTP, bf16, KW>(sB, g, tok, len, H, h, c0);
+    if constexpr (OPTS) {
+      gate_rows_opts<KQ, LKQ, NTP, KW>(sB, g, tok, len, H, h, c0, opts);
+      if (opts & OPT_L2NORM_QK) {
+        scale_rows<KQ, LKQ, NTP>(sQ, sNq);
+        scale_rows<KQ, LKQ, NTP>(sK, sNk);
+      }
+    } else {
+      load_rows<KQ, LKQ, NTP, bf16, KW>(sB, g, tok, len, H, h, c0);
+    }
     lds_barrier();
-    cumsum_log2<KQ, LKQ, NTP>(sB);
+    cumsum_log2<KQ, LKQ, NTP>(sB, OPTS ? 1.f : LOG2E);  // the option path holds log2 alpha
     lds_barrier();
     // Qe = q e^b (token tile ft, channel step 2 hh + fsl) and Ktilde^T = (k e^{b_last - b})^T
     // (channel tile 4 hh + ft, token step fsl); rows past len hold q = k = 0. beta k e^b goes
@@ -264,7 +360,10 @@ __global__ __launch_bounds__(NTP, 4) void rec256_kernel(Rec256Params p) {
 }
 
 void launch_rec256(const Rec256Params& p, hipStream_t st) {
-  hipLaunchKernelGGL(rec256_kernel, dim3((unsigned)p.E, (unsigned)p.H), dim3(NTP), 0, st, p);
+  if (p.opts != 0)
+    hipLaunchKernelGGL(rec256_kernel<true>, dim3((unsigned)p.E, (unsigned)p.H), dim3(NTP), 0, st, p);
+  else
+    hipLaunchKernelGGL(rec256_kernel<false>, dim3((unsigned)p.E, (unsigned)p.H), dim3(NTP), 0, st, p);
 }
 
 // The chain of one (sequence, head, CW value columns); blockIdx = slice * chains8 + chain, so

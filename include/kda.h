@@ -23,7 +23,7 @@
  *    scale is applied and q, k are used as given (no normalisation inside). The _ex entry
  *    points take options that change how these inputs are read (KDA_OPT_* below).
  *  - Supported head dims: kda_chunk_fwd K in {32, 64, 128, 256}, V in {32, 64, 128, 256};
- *    fp32 inputs at K >= 128, and K = 256 with input options, run the wide-key path below;
+ *    fp32 inputs at K >= 128 run the wide-key path below;
  *    kda_decode_step K, V in {32, 64, 128, 256}. Other values give KDA_ERROR_NOT_SUPPORTED.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
  *    returns without waiting. Argument errors are reported synchronously before anything is
@@ -87,9 +87,8 @@ const char* kda_status_string(kda_status s);
  * K <= 64) it covers the device chunk table, a running state and one chunk-record buffer
  * reused by every segment of the call: about 170 MB at H=32, K=V=128, bf16 (300 MB at
  * K=V=256), plus 32 bytes per chunk and 4*N*H*K*V bytes, whatever the sequence length.
- * The wide-key path (fp32 inputs at K >= 128, K = 256 with input options) forms fp32 records
- * one segment of 512 MiB at a time: under about 1 GB at H = 32 whatever the length. At
- * K = 256 with bf16 inputs the value covers both paths (the options are not known here).
+ * The wide-key path (fp32 inputs at K >= 128) forms fp32 records one segment of 512 MiB at a
+ * time: under about 1 GB at H = 32 whatever the length.
  */
 size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                                     int32_t dk, int32_t dv, kda_dtype dtype);
@@ -121,16 +120,16 @@ size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int3
  * sub-block whose decay exceeds 2^96 on some channel is formed from running products of the
  * per-token decays instead (exact up to rounding; vanishing terms underflow to zero).
  * Positive log_alpha values are accepted but lie outside this guarantee.
- * bf16 inputs at K = 256 (no options) run the main path with an fp32 record kernel: the chunk's
- * sums over the key channels in parts of 64, the off-diagonal 16 x 16 blocks of A and P on the
- * fp32 matrix cores with the decay split at a block boundary (both factors at most 1), the
- * diagonal blocks pairwise, then the bf16 chain with four waves per 16 value columns. fp32
- * inputs at K >= 128, and K = 256 with input options, run a separate path in fp32 (the same
- * record arithmetic, the chain on the fp32 matrix cores) that forms the chunks' records one
- * segment of chunks at a time (512 MiB of records), so its workspace stays under about 1 GB
- * at 32 heads whatever the length; with input options a separate pass forms the processed q,
- * k, log alpha and beta of each segment's tokens in fp32 first. Every decay factor on either
- * path is at most 1, so any log_alpha <= 0 is in range.
+ * bf16 inputs at K = 256 run the main path with an fp32 record kernel: the chunk's sums over
+ * the key channels in parts of 64, the off-diagonal 16 x 16 blocks of A and P on the fp32
+ * matrix cores with the decay split at a block boundary (both factors at most 1), the diagonal
+ * blocks pairwise, then the bf16 chain with four waves per 16 value columns (input options are
+ * applied in fp32 as that kernel reads the raw inputs). fp32 inputs at K >= 128 run a separate
+ * path in fp32 (the same record arithmetic, the chain on the fp32 matrix cores) that forms the
+ * chunks' records one segment of chunks at a time (512 MiB of records), so its workspace stays
+ * under about 1 GB at 32 heads whatever the length; with input options a separate pass forms
+ * the processed q, k, log alpha and beta of each segment's tokens in fp32 first. Every decay
+ * factor on either path is at most 1, so any log_alpha <= 0 is in range.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* beta, const float* init_state, const int32_t* cu_seqlens,
@@ -159,8 +158,7 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
  * segments than kda_chunk_fwd_ex. Results are the same as kda_chunk_fwd_ex's.
  * Differences from kda_chunk_fwd_ex:
  *  - final_state is required (KDA_ERROR_INVALID_VALUE if NULL): it carries the running state;
- *  - shapes on the wide-key path (fp32 inputs at K >= 128, K = 256 with input options) give
- *    KDA_ERROR_NOT_SUPPORTED;
+ *  - shapes on the wide-key path (fp32 inputs at K >= 128) give KDA_ERROR_NOT_SUPPORTED;
  *  - a shape whose chunk table plus one chunk record per head exceeds the scratch gives
  *    KDA_ERROR_WORKSPACE_TOO_SMALL (e.g. more than about 2^24 chunks in total);
  *  - every call on a device shares that device's scratch: calls that overlap in time on one

@@ -90,8 +90,8 @@ def _chunk(L, **kw):
     (dict(T=-5), INVALID),
     (dict(T=1 << 31), INVALID),
     (dict(dk=48), NOT_SUPPORTED),
-    (dict(dk=256, opts=15, wsb=4096), WS_SMALL),  # the wide-key path (K = 256) takes options
-    (dict(dk=256, wsb=4096), WS_SMALL),     # K = 256 is supported (the wide-key path)
+    (dict(dk=256, opts=15, wsb=4096), WS_SMALL),  # K = 256 takes options
+    (dict(dk=256, wsb=4096), WS_SMALL),     # K = 256 is supported
     (dict(dk=512), NOT_SUPPORTED),
     (dict(dv=512), NOT_SUPPORTED),
     (dict(opts=16), NOT_SUPPORTED),        # unknown option bit
@@ -139,7 +139,7 @@ def _noalloc(L, **kw):
     (dict(fin=None), INVALID),             # the running state lives in final_state
     (dict(N=0), INVALID),
     (dict(dk=48), NOT_SUPPORTED),
-    (dict(dk=256, opts=4), NOT_SUPPORTED),  # the fp32 wide-key path is not served from the scratch
+    (dict(dk=256, dtype=F32), NOT_SUPPORTED),  # the fp32 wide-key path is not served from the scratch
     (dict(dtype=F32, dk=128), NOT_SUPPORTED),
     (dict(opts=16), NOT_SUPPORTED),
     (dict(q=A + 8), INVALID),

@@ -110,13 +110,17 @@ SG, GL, BL, L2 = kda.OPT_SCALAR_GATE, kda.OPT_GATE_LOGITS, kda.OPT_BETA_LOGITS, 
     (SG, torch.bfloat16, 256, 64, None),
     (GL, torch.bfloat16, 256, 256, None),
     (GL, torch.float32, 256, 128, (-12.0, -6.0)),   # strong decays through the gate logits
+    (GL, torch.bfloat16, 256, 64, (-12.0, -6.0)),
     (BL | L2, torch.bfloat16, 256, 128, None),
+    (SG | GL | BL | L2, torch.bfloat16, 256, 128, None),
     (SG | GL | BL | L2, torch.float32, 256, 32, None),
     (SG | GL | BL | L2, torch.float32, 128, 128, None),  # fp32 at K = 128 takes this path too
 ])
 def test_wide_options_ragged_varlen(opts, dtype, K, V, gates):
-    """The input options on the wide-key path (a pass that forms the processed q, k, log alpha
-    and beta for each segment's tokens) against the oracle running the same fp64 prologue."""
+    """The input options at 256 key channels against the oracle running the same fp64 prologue:
+    bf16 inputs through the record kernel of the chunk path (the options applied as the raw
+    inputs are read), fp32 inputs on the wide-key path (a pass that forms the processed q, k,
+    log alpha and beta for each segment's tokens)."""
     print("wide options", opts, dtype, K, V, flush=True)
     lengths = [1, 63, 64, 65, 0, 127, 200]
     cu = torch.tensor(workloads.cu_from_lengths(lengths), dtype=torch.int32, device=DEV)

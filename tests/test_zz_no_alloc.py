@@ -63,10 +63,10 @@ def test_noalloc_matches_chunk_fwd_two_calls():
 
 
 def test_noalloc_rejects_wide_key():
-    """The fp32 wide-key path (fp32 inputs at K >= 128, K = 256 with input options) keeps fp32
-    records that the scratch does not serve."""
-    for K, dt, opts in ((128, torch.float32, 0), (256, torch.bfloat16, kda.OPT_BETA_LOGITS)):
-        inp = workloads.gen_forward(64, 1, K, 64, dtype=dt, device=DEV, seed=23)
+    """The fp32 wide-key path (fp32 inputs at K >= 128) keeps fp32 records that the scratch does
+    not serve."""
+    for K, opts in ((128, 0), (256, 0), (256, kda.OPT_BETA_LOGITS)):
+        inp = workloads.gen_forward(64, 1, K, 64, dtype=torch.float32, device=DEV, seed=23)
         with pytest.raises(kda.KdaError):
             kda.chunk_fwd_noalloc(*(inp[x] for x in ORDER), options=opts)
 
@@ -84,3 +84,14 @@ def test_noalloc_k256_matches_chunk_fwd():
         o, fin = kda.chunk_fwd(*args, init_state=inp["init_state"], cu_seqlens=cu)
         o2, fin2 = kda.chunk_fwd_noalloc(*args, init_state=inp["init_state"], cu_seqlens=cu)
         assert torch.equal(o, o2) and torch.equal(fin, fin2)
+    # with input options (applied inside the record kernel)
+    opts = kda.OPT_SCALAR_GATE | kda.OPT_GATE_LOGITS | kda.OPT_BETA_LOGITS | kda.OPT_L2NORM_QK
+    lengths = [190, 66]
+    cu = torch.tensor(workloads.cu_from_lengths(lengths), dtype=torch.int32, device=DEV)
+    raw = workloads.gen_raw(sum(lengths), 2, 256, 64, opts, dtype=torch.bfloat16, device=DEV,
+                            seed=5, num_seqs=2, init_std=0.1)
+    args = [raw[x] for x in ORDER]
+    o, fin = kda.chunk_fwd(*args, init_state=raw["init_state"], cu_seqlens=cu, options=opts)
+    o2, fin2 = kda.chunk_fwd_noalloc(*args, init_state=raw["init_state"], cu_seqlens=cu,
+                                     options=opts)
+    assert torch.equal(o, o2) and torch.equal(fin, fin2)
