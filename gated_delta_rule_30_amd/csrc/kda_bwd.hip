@@ -605,7 +605,7 @@ __global__ __launch_bounds__(64 * chain_waves<K>()) void bwd_rstate_kernel(
 // (a) dP = lower(dO Delta^T); with S (chunk start) and X (chunk end) streamed from HBM:
 //     dO S^T, dW = -dDelta S^T, Delta X^T and rowsum(S * X)
 template <int K, int V, typename MT>
-__global__ __launch_bounds__(NTGA, 8) void bwd_ga_kernel(
+__global__ __launch_bounds__(NTGA, 2) void bwd_ga_kernel(
     const MT* __restrict__ dO, const float* __restrict__ ckS, const float* __restrict__ ckX,
     const float* __restrict__ Dl, const float* __restrict__ dDl, int H,
     const ChunkRow* __restrict__ chunks, const int32_t* __restrict__ ntot, int cb,
@@ -627,56 +627,60 @@ __global__ __launch_bounds__(NTGA, 8) void bwd_ga_kernel(
   float* sc = scr + ch_h * G::floats;
   const float* S = ckS + ch_h * K * V;
   const float* X = ckX + ch_h * K * V;
-  // rowsum(S * X): NP neighbouring threads per key channel (K NP is a whole number of waves),
-  // then a shuffle reduction among them
-  {
-    constexpr int NP = NTGA / K < V / 4 ? NTGA / K : V / 4, VP = V / NP;
-    if (threadIdx.x < K * NP) {
-      const int m = threadIdx.x / NP, part = threadIdx.x % NP;
-      float dg = 0.f;
-#pragma unroll
-      for (int vv = 0; vv < VP; vv += 4)
-        dg += dot4(*reinterpret_cast<const f32x4*>(S + m * V + part * VP + vv),
-                   *reinterpret_cast<const f32x4*>(X + m * V + part * VP + vv));
-#pragma unroll
-      for (int o = 1; o < NP; o <<= 1) dg += __shfl_xor(dg, o);
-      if (part == 0) sc[G::oDG + m] = dg;
-    }
-  }
+  // rowsum(S * X) rides along with the products, so that neither state is read twice: while
+  // a part of S is in LDS each thread keeps EPT of its values (key channel rm, columns rc ..;
+  // TPR neighbouring threads share a channel) and multiplies them with the same part of X in
+  // the second loop
+  constexpr int NPART = V / VC, EPT = K * VC / NTGA, TPR = VC / EPT;
+  static_assert(EPT >= 1 && K * VC == EPT * NTGA && TPR <= 64, "rowsum split");
+  const int rm = threadIdx.x / TPR, rc = (threadIdx.x % TPR) * EPT;
+  float keep[NPART][EPT];
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   // dO S^T and dW = -dDelta S^T
   {
     f32x4 r1[TK], dw[TK];
 #pragma unroll
     for (int i = 0; i < TK; ++i) r1[i] = dw[i] = z;
-    for (int c0 = 0; c0 < V; c0 += VC) {
+#pragma unroll
+    for (int pi = 0; pi < NPART; ++pi) {
+      const int c0 = pi * VC;
       load_rows<VC, L, NTGA, MT, V>(sO, dO, ch.tok, ch.len, H, h, c0);
       load_block<VC, L, NTGA, BC, V>(sD, dDl + ch_h * BC * V + c0);
       load_block<VC, L, NTGA, K, V>(sS, S + c0);
       lds_barrier();
       mmx_acc<K, VC, false, true, L, L, NTGA>(sO, sS, r1);
       mmx_acc<K, VC, false, true, L, L, NTGA>(sD, sS, dw);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) keep[pi][e] = sS[rm * L + rc + e];
       lds_barrier();
     }
     mmf_out<K, NTGA>(r1, [&](int r, int m, float x) { sc[G::oR1 + r * K + m] = x; });
     mmf_out<K, NTGA>(dw, [&](int r, int m, float x) { sc[G::oDW + r * K + m] = -x; });
   }
-  // Delta X^T and dP = lower(dO Delta^T)
+  // Delta X^T, dP = lower(dO Delta^T) and rowsum(S * X)
   {
     f32x4 dk[TK], dp[TC];
 #pragma unroll
     for (int i = 0; i < TK; ++i) dk[i] = z;
 #pragma unroll
     for (int i = 0; i < TC; ++i) dp[i] = z;
-    for (int c0 = 0; c0 < V; c0 += VC) {
+    float dg = 0.f;
+#pragma unroll
+    for (int pi = 0; pi < NPART; ++pi) {
+      const int c0 = pi * VC;
       if (V > VC) load_rows<VC, L, NTGA, MT, V>(sO, dO, ch.tok, ch.len, H, h, c0);
       load_block<VC, L, NTGA, BC, V>(sD, Dl + ch_h * BC * V + c0);
       load_block<VC, L, NTGA, K, V>(sS, X + c0);
       lds_barrier();
       mmx_acc<K, VC, false, true, L, L, NTGA>(sD, sS, dk);
       mmx_acc<BC, VC, false, true, L, L, NTGA>(sO, sD, dp);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) dg += keep[pi][e] * sS[rm * L + rc + e];
       lds_barrier();
     }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) dg += __shfl_xor(dg, o);
+    if (threadIdx.x % TPR == 0) sc[G::oDG + rm] = dg;
     mmf_out<K, NTGA>(dk, [&](int r, int m, float x) { sc[G::oDKt + r * K + m] = x; });
     mmf_out<BC, NTGA>(dp, [&](int i, int j, float x) {
       if (j <= i) sc[G::oDPA + i * BC + j] = x;

@@ -13,7 +13,7 @@ constexpr int BC = CHUNK;  // 64 tokens per chunk
 constexpr int NT = NTHREADS;  // the chains and the table kernels
 constexpr int NTP = 512;      // the record kernel: 8 waves per workgroup
 constexpr int NTG = 1024;     // the gradient kernels: 16 waves per workgroup
-constexpr int NTGA = 1024;    // the S/X product kernel: 16 waves, two workgroups per CU
+constexpr int NTGA = 512;     // the S/X product kernel: 8 waves, two workgroups per CU
 
 __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
   return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
