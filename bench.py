@@ -624,7 +624,42 @@ def main():
         finite = bool(all(torch.isfinite(g).all().item() for g in grads))
         del grads
         bms1, _, grads1, same1 = time_bwd(ws_one)
-        del grads1
+        # with the forward's checkpoints: the forward that keeps them (timed), then the backward
+        # from them with the default workspace (no boundary pass)
+        ck = kda.ckpt_empty(1, T, H, K, V, dev)
+        ock = torch.empty((T, H, V), dtype=torch.bfloat16, device=dev)
+        fck = torch.empty((1, H, K, V), dtype=torch.float32, device=dev)
+        wsf = torch.empty(kda.workspace_size(1, T, H, K, V, torch.bfloat16), dtype=torch.uint8,
+                          device=dev)
+
+        def fwd_ck():
+            kda.chunk_fwd(*(inp[x] for x in names), init_state=inp["init_state"], o=ock,
+                          final_state=fck, workspace=wsf, checkpoints=ck)
+
+        def time_calls_(fn, calls, warm):
+            for _ in range(warm):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(calls):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / calls
+
+        fck_ms = time_calls_(fwd_ck, max(1, min(args.steps, 10)), max(1, min(args.warmup, 2)))
+        wsd = torch.empty(int(ws_def), dtype=torch.uint8, device=dev)
+        gck = [None]
+
+        def bwd_ck():
+            gck[0] = kda.chunk_bwd(*(inp[x] for x in names), d_o, init_state=inp["init_state"],
+                                   d_final_state=d_fin, workspace=wsd, checkpoints=ck)
+
+        bck_ms = time_calls_(bwd_ck, max(1, min(args.steps, 5)), max(1, min(args.warmup, 2)))
+        ck_rel = max(float((a - b).abs().max() / b.abs().max().clamp_min(1e-30))
+                     for a, b in zip(gck[0], grads1))
+        del grads1, gck, ck, ock, fck, wsf, wsd
         bfl = bwd_alg_flops(T, H, K, V)
         bwd = {"workload": "B=1 H=32 T=65536 K=V=128 bf16 inputs, fp32 gradients of q, k, v, "
                            "log alpha, beta and the initial state",
@@ -636,7 +671,14 @@ def main():
                "single_segment": {"ms": bms1, "workspace_GB": ws_one / 1e9,
                                   "tokens_per_s": T / (bms1 * 1e-3)},
                "bitwise_repeatable": bool(same and same1),
-               "finite": finite}
+               "finite": finite,
+               "with_checkpoints": {
+                   "ms": bck_ms, "tokens_per_s": T / (bck_ms * 1e-3),
+                   "workspace_GB": ws_def / 1e9,
+                   "forward_with_checkpoints_ms": fck_ms,
+                   "max_rel_diff_vs_single_segment": ck_rel,
+                   "note": "segments start from the states the forward kept at its segment "
+                           "boundaries (no boundary pass)"}}
         del d_o, d_fin
 
     # ---------------- parity spot check and CPU baseline (oracle on the same inputs)

@@ -81,6 +81,17 @@ def _lib():
         lib.kda_chunk_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
                                          ctypes.c_int, ctypes.c_uint32, vp, vp, vp, vp, vp, vp,
                                          vp, vp, vp, sz, vp]
+        lib.kda_chunk_fwd_ckpt.restype = ctypes.c_int
+        lib.kda_chunk_fwd_ckpt.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                           ctypes.c_int, u32, vp, vp, vp, vp, sz, vp]
+        lib.kda_chunk_fwd_ckpt_interval.restype = i64
+        lib.kda_chunk_fwd_ckpt_interval.argtypes = [i32, i64, i32]
+        lib.kda_chunk_fwd_ckpt_bytes.restype = sz
+        lib.kda_chunk_fwd_ckpt_bytes.argtypes = [i32, i64, i32, i32, i32]
+        lib.kda_chunk_bwd_ckpt.restype = ctypes.c_int
+        lib.kda_chunk_bwd_ckpt.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                           ctypes.c_int, ctypes.c_uint32, vp, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, vp, sz, vp]
         lib.kda_decode_step_ex.restype = ctypes.c_int
         lib.kda_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                            ctypes.c_int, u32, vp]
@@ -144,13 +155,29 @@ def bwd_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype, segment
                                                       code, int(options), seg))
 
 
+def ckpt_interval(num_seqs, total_tokens, num_heads) -> int:
+    """Chunks of 64 tokens between the checkpoints chunk_fwd keeps for chunk_bwd."""
+    return int(_lib().kda_chunk_fwd_ckpt_interval(num_seqs, total_tokens, num_heads))
+
+
+def ckpt_empty(num_seqs, total_tokens, num_heads, dk, dv, device):
+    """An uninitialised fp32 checkpoint buffer for chunk_fwd(checkpoints=...): one [H, K, V]
+    state per checkpoint (possibly none)."""
+    nb = int(_lib().kda_chunk_fwd_ckpt_bytes(num_seqs, total_tokens, num_heads, dk, dv))
+    return torch.empty((nb // (4 * num_heads * dk * dv), num_heads, dk, dv), dtype=torch.float32,
+                       device=device)
+
+
 def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, num_seqs=None,
-              output_final_state=True, o=None, final_state=None, workspace=None, options=0):
+              output_final_state=True, o=None, final_state=None, workspace=None, options=0,
+              checkpoints=None):
     """kda_chunk_fwd on torch tensors (token-major [T, H, .], see include/kda.h).
 
     Returns (o [T, H, V] in the input dtype, final_state [N, H, K, V] fp32 or None).
     ``final_state`` may be passed as the same tensor as ``init_state`` (in-place update).
     ``options`` (OPT_* bits) selects kda_chunk_fwd_ex; with OPT_SCALAR_GATE log_alpha is [T, H].
+    ``checkpoints`` (a ckpt_empty buffer) selects kda_chunk_fwd_ckpt, which also keeps the
+    states chunk_bwd(checkpoints=...) starts its segments from.
     """
     device = q.device
     T, H, K = q.shape
@@ -184,6 +211,18 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, num_se
                        "kda_chunk_fwd_workspace_size")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if checkpoints is not None:
+        nb = int(_lib().kda_chunk_fwd_ckpt_bytes(N, T, H, K, V))
+        _check(checkpoints, "checkpoints", (nb // (4 * H * K * V), H, K, V), torch.float32, device)
+        st = _lib().kda_chunk_fwd_ckpt(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                       _ptr(init_state), _ptr(cu_seqlens), N, T, H, K, V, code,
+                                       int(options), _ptr(o), _ptr(final_state),
+                                       _ptr(checkpoints) if nb else None, _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(device))
+        if st != 0:
+            raise KdaError(st, "kda_chunk_fwd_ckpt")
+        return o, final_state
     st = _lib().kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                  _ptr(init_state), _ptr(cu_seqlens), N, T, H, K, V, code,
                                  int(options), _ptr(o), _ptr(final_state), _ptr(workspace),
@@ -279,7 +318,7 @@ def chunk_fwd_scan(q, k, v, log_alpha, beta, init_state=None, num_seqs=None, num
 
 def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final_state=None,
               cu_seqlens=None, num_seqs=None, workspace=None, grads=None, segment_tokens=None,
-              options=0):
+              options=0, checkpoints=None):
     """kda_chunk_bwd_ex on torch tensors: the gradients of sum(d_o * o) + sum(d_final_state *
     final_state) for chunk_fwd on the same inputs and options (OPT_* bits; with OPT_SCALAR_GATE
     log_alpha and its gradient are [T, H]). d_o [T, H, V] in the input dtype; d_final_state
@@ -287,7 +326,9 @@ def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final_state=None
     dv [T, H, V], dlog_alpha, dbeta [T, H], dinit_state [N, H, K, V]). ``grads`` may pass those
     six tensors to be written in place (e.g. under graph capture). Without ``workspace``, one of
     the default size is allocated, or, with ``segment_tokens``, one sized for segments of that
-    many tokens (0: one segment)."""
+    many tokens (0: one segment). ``checkpoints``, filled by chunk_fwd(checkpoints=...) on the
+    same inputs, selects kda_chunk_bwd_ckpt: its segments start from those states instead of a
+    pass that forms them again."""
     device = q.device
     T, H, K = q.shape
     V = v.shape[-1]
@@ -327,6 +368,19 @@ def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final_state=None
             raise KdaError(2 if K not in (32, 64, 128) or V not in (32, 64, 128) else 1,
                            "kda_chunk_bwd_workspace_size_ex")
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if checkpoints is not None:
+        nb = int(_lib().kda_chunk_fwd_ckpt_bytes(N, T, H, K, V))
+        _check(checkpoints, "checkpoints", (nb // (4 * H * K * V), H, K, V), torch.float32, device)
+        st = _lib().kda_chunk_bwd_ckpt(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                       _ptr(init_state), _ptr(cu_seqlens), N, T, H, K, V, code,
+                                       int(options), _ptr(d_o), _ptr(d_final_state),
+                                       _ptr(checkpoints) if nb else None, _ptr(dq), _ptr(dk),
+                                       _ptr(dv), _ptr(dg), _ptr(db), _ptr(dinit), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(device))
+        if st != 0:
+            raise KdaError(st, "kda_chunk_bwd_ckpt")
+        return dq, dk, dv, dg, db, dinit
     st = _lib().kda_chunk_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                  _ptr(init_state), _ptr(cu_seqlens), N, T, H, K, V, code,
                                  int(options), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk),

@@ -167,6 +167,62 @@ extern "C" kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void*
   return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
 }
 
+// Chunks between the forward's checkpoints: its segment length (entries of the chunk table).
+static int64_t ckpt_interval(int32_t num_seqs, int64_t total_tokens, int32_t num_heads) {
+  kda::ChunkPlan pl;
+  if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, 32, 32, true, &pl)) return 0;
+  return pl.seg_entries;
+}
+static size_t ckpt_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t dk,
+                         int32_t dv) {
+  kda::ChunkPlan pl;
+  if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, 32, 32, true, &pl)) return 0;
+  const int64_t slots = pl.num_segs > 1 ? pl.num_segs - 1 : 0;
+  return (size_t)slots * num_heads * dk * dv * sizeof(float);
+}
+
+extern "C" kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const void* v,
+                                         const void* log_alpha, const void* beta,
+                                         const float* init_state, const int32_t* cu_seqlens,
+                                         int32_t num_seqs, int64_t total_tokens,
+                                         int32_t num_heads, int32_t dk, int32_t dv,
+                                         kda_dtype dtype, uint32_t options, void* o,
+                                         float* final_state, float* checkpoints, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  kda::ChunkArgs a;
+  kda_status st = kda::prepare_chunk_fwd(q, k, v, log_alpha, beta, init_state, cu_seqlens,
+                                         num_seqs, total_tokens, num_heads, dk, dv, dtype, options,
+                                         o, final_state, stream, &a);
+  if (st != KDA_SUCCESS) return st;
+  // the shapes the training backward takes, on the chunk path
+  if (!supported_chunk_dk(dk) || !supported_chunk_dk(dv) || wide_path(dk, dtype, options))
+    return KDA_ERROR_NOT_SUPPORTED;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return KDA_ERROR_INVALID_VALUE;
+  const size_t cb = ckpt_bytes(num_seqs, total_tokens, num_heads, dk, dv);
+  if (cb > 0) {
+    if (!checkpoints || !aligned16(checkpoints)) return KDA_ERROR_INVALID_VALUE;
+    const size_t es = esize(dtype), T = (size_t)total_tokens, H = (size_t)num_heads;
+    const size_t gd = (options & KDA_OPT_SCALAR_GATE) ? 1 : (size_t)dk;
+    const size_t sbytes = (size_t)num_seqs * H * dk * dv * sizeof(float);
+    const void* bp[] = {q, k, v, log_alpha, beta, o, init_state, final_state};
+    const size_t bn[] = {T * H * dk * es, T * H * dk * es, T * H * dv * es, T * H * gd * es,
+                         T * H * es, T * H * dv * es, sbytes, sbytes};
+    for (int i = 0; i < 8; ++i)
+      if (bp[i] && bn[i] && overlap(checkpoints, cb, bp[i], bn[i])) return KDA_ERROR_INVALID_VALUE;
+  }
+  kda::ChunkPlan pl;
+  if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16, &pl))
+    return KDA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < pl.total_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+  // segments along token order, so that each segment boundary is a chunk of one sequence
+  pl.seq_major = 1;
+  a.workspace = workspace;
+  a.ckpt = cb > 0 ? checkpoints : nullptr;
+  hipError_t e = kda::launch_chunk_fwd(a, pl);
+  return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+}
+
 extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                                     const void* log_alpha, const void* beta,
                                     const float* init_state, const int32_t* cu_seqlens,
@@ -215,15 +271,16 @@ extern "C" size_t kda_chunk_bwd_workspace_size(int32_t num_seqs, int64_t total_t
   return p.total_bytes;
 }
 
-extern "C" kda_status kda_chunk_bwd_ex(const void* q, const void* k, const void* v,
-                                       const void* log_alpha, const void* beta,
-                                       const float* init_state, const int32_t* cu_seqlens,
-                                       int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
-                                       int32_t dk, int32_t dv, kda_dtype dtype, uint32_t options,
-                                       const void* d_o, const float* d_final_state, float* grad_q,
-                                       float* grad_k, float* grad_v, float* grad_log_alpha,
-                                       float* grad_beta, float* grad_init_state, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
+static kda_status chunk_bwd_impl(const void* q, const void* k, const void* v,
+                                 const void* log_alpha, const void* beta,
+                                 const float* init_state, const int32_t* cu_seqlens,
+                                 int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                 int32_t dk, int32_t dv, kda_dtype dtype, uint32_t options,
+                                 const void* d_o, const float* d_final_state,
+                                 const float* checkpoints, float* grad_q, float* grad_k,
+                                 float* grad_v, float* grad_log_alpha, float* grad_beta,
+                                 float* grad_init_state, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   kda_status st = check_bwd_shape(num_seqs, total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_SUCCESS) return st;
   if (options & ~kAllOptions) return KDA_ERROR_NOT_SUPPORTED;
@@ -263,11 +320,24 @@ extern "C" kda_status kda_chunk_bwd_ex(const void* q, const void* k, const void*
       if (out_p[o2] && out_n[o2] && overlap(out_p[o], out_n[o], out_p[o2], out_n[o2]))
         return KDA_ERROR_INVALID_VALUE;
   }
+  // with checkpoints: segments that start where the forward kept a state
+  int64_t step = 1;
+  const size_t cb = ckpt_bytes(num_seqs, total_tokens, num_heads, dk, dv);
+  if (cb == 0) checkpoints = nullptr;  // one forward segment: no boundary to start from
+  if (checkpoints != nullptr) {
+    if (!aligned16(checkpoints)) return KDA_ERROR_INVALID_VALUE;
+    for (int o = 0; o < 6; ++o)
+      if (out_p[o] && out_n[o] && overlap(out_p[o], out_n[o], checkpoints, cb))
+        return KDA_ERROR_INVALID_VALUE;
+    step = ckpt_interval(num_seqs, total_tokens, num_heads);
+    if (step < 1) return KDA_ERROR_INVALID_VALUE;
+  }
   // the longest segments the caller's workspace holds (one segment when it holds them all)
   kda::BwdPlan p;
   if (!kda::make_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, options, 0, &p))
     return KDA_ERROR_INVALID_VALUE;
-  if (!kda::fit_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, options, workspace_bytes, &p))
+  if (!kda::fit_bwd_plan(num_seqs, total_tokens, num_heads, dk, dv, options, workspace_bytes, &p,
+                         step))
     return KDA_ERROR_WORKSPACE_TOO_SMALL;
   kda::BwdArgs a;
   a.q = q;
@@ -294,8 +364,58 @@ extern "C" kda_status kda_chunk_bwd_ex(const void* q, const void* k, const void*
   a.options = options;
   a.workspace = workspace;
   a.stream = stream;
+  a.ckpt = checkpoints;
+  a.ckpt_interval = step;
   hipError_t e = kda::launch_chunk_bwd(a, p);
   return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+}
+
+extern "C" kda_status kda_chunk_bwd_ex(const void* q, const void* k, const void* v,
+                                       const void* log_alpha, const void* beta,
+                                       const float* init_state, const int32_t* cu_seqlens,
+                                       int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                       int32_t dk, int32_t dv, kda_dtype dtype, uint32_t options,
+                                       const void* d_o, const float* d_final_state, float* grad_q,
+                                       float* grad_k, float* grad_v, float* grad_log_alpha,
+                                       float* grad_beta, float* grad_init_state, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, num_seqs, total_tokens,
+                        num_heads, dk, dv, dtype, options, d_o, d_final_state, nullptr, grad_q,
+                        grad_k, grad_v, grad_log_alpha, grad_beta, grad_init_state, workspace,
+                        workspace_bytes, stream);
+}
+
+extern "C" kda_status kda_chunk_bwd_ckpt(const void* q, const void* k, const void* v,
+                                         const void* log_alpha, const void* beta,
+                                         const float* init_state, const int32_t* cu_seqlens,
+                                         int32_t num_seqs, int64_t total_tokens,
+                                         int32_t num_heads, int32_t dk, int32_t dv,
+                                         kda_dtype dtype, uint32_t options, const void* d_o,
+                                         const float* d_final_state, const float* checkpoints,
+                                         float* grad_q, float* grad_k, float* grad_v,
+                                         float* grad_log_alpha, float* grad_beta,
+                                         float* grad_init_state, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (checkpoints == nullptr && ckpt_bytes(num_seqs, total_tokens, num_heads, dk, dv) > 0)
+    return KDA_ERROR_INVALID_VALUE;
+  return chunk_bwd_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, num_seqs, total_tokens,
+                        num_heads, dk, dv, dtype, options, d_o, d_final_state, checkpoints,
+                        grad_q, grad_k, grad_v, grad_log_alpha, grad_beta, grad_init_state,
+                        workspace, workspace_bytes, stream);
+}
+
+extern "C" int64_t kda_chunk_fwd_ckpt_interval(int32_t num_seqs, int64_t total_tokens,
+                                               int32_t num_heads) {
+  if (num_seqs <= 0 || num_heads <= 0 || total_tokens < 0 || total_tokens > kMaxTokens) return 0;
+  return ckpt_interval(num_seqs, total_tokens, num_heads);
+}
+
+extern "C" size_t kda_chunk_fwd_ckpt_bytes(int32_t num_seqs, int64_t total_tokens,
+                                           int32_t num_heads, int32_t dk, int32_t dv) {
+  if (num_seqs <= 0 || num_heads <= 0 || total_tokens < 0 || total_tokens > kMaxTokens ||
+      !supported_chunk_dk(dk) || !supported_chunk_dk(dv))
+    return 0;
+  return ckpt_bytes(num_seqs, total_tokens, num_heads, dk, dv);
 }
 
 extern "C" kda_status kda_chunk_bwd(const void* q, const void* k, const void* v,

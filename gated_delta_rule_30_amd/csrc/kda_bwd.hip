@@ -1082,16 +1082,17 @@ bool make_bwd_plan(int N, int64_t T, int H, int K, int V, uint32_t options, int6
 }
 
 bool fit_bwd_plan(int N, int64_t T, int H, int K, int V, uint32_t options, size_t bytes,
-                  BwdPlan* p) {
+                  BwdPlan* p, int64_t step) {
   if (!make_bwd_plan(N, T, H, K, V, options, 0, p)) return false;
   if (p->total_bytes <= bytes) return true;
+  if (step < 1) step = 1;
   // the longest segments that fit: from the per-chunk bytes down, shorter until it fits
   const size_t per_chunk = (size_t)H * bwd_floats(K, V).all * 4;
-  int64_t e = (int64_t)min(bytes / per_chunk, (size_t)p->ub - 1);
-  while (e >= 1) {
+  int64_t e = (int64_t)min(bytes / per_chunk, (size_t)p->ub - 1) / step * step;
+  while (e >= step) {
     if (!make_bwd_plan(N, T, H, K, V, options, e, p)) return false;
     if (p->total_bytes <= bytes) return true;
-    e = e > 64 ? e - e / 32 : e - 1;
+    e = step > 1 ? e - step : e > 64 ? e - e / 32 : e - 1;
   }
   return false;
 }
@@ -1137,9 +1138,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
                          dim3((unsigned)(ce - cb), (unsigned)H), dim3(NTP), 0, st, q, k, v, g,
                          beta, H, (const ChunkRow*)chunks, ntot, cb, rec);
   };
-  // Forward through the segments but the last: each one's state at its end, for the sequence
-  // that goes on into the next
-  for (int64_t s = 0; s + 1 < p.nseg; ++s) {
+  // The state of the sequence that spans the start of segment s (chunk s * seg): from the
+  // forward's checkpoint of that chunk, or from a forward pass through the segments but the
+  // last that keeps each one's state at its end
+  auto ck_start = [&](int64_t s) -> const float* {
+    if (s == 0) return nullptr;
+    return a.ckpt ? a.ckpt + (size_t)(s * p.seg / a.ckpt_interval - 1) * ckb : bound(s);
+  };
+  for (int64_t s = 0; a.ckpt == nullptr && s + 1 < p.nseg; ++s) {
     int cb, ce;
     range(s, &cb, &ce);
     prep(cb, ce, std::true_type());
@@ -1157,8 +1163,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& p) {
     prep(cb, ce, std::false_type());
     hipLaunchKernelGGL((bwd_fstate_kernel<K, V, true>), sgrid, dim3(64 * chain_waves<K>()), 0, st,
                        (const float*)rec, a.init_state, (const int32_t*)seq_first, N, H, chains8,
-                       cb, ce, (const float*)(s > 0 ? bound(s) : nullptr), (float*)nullptr, ckS,
-                       Dl);
+                       cb, ce, ck_start(s), (float*)nullptr, ckS, Dl);
     hipLaunchKernelGGL((bwd_rstate_kernel<K, V, MT>), sgrid, dim3(64 * chain_waves<K>()), 0, st, (const float*)rec,
                        dO, a.dfinal, a.cu_seqlens, a.total_tokens, (const int32_t*)seq_first, N, H,
                        chains8, cb, ce, (const float*)(s + 1 < p.nseg ? bound(s + 1) : nullptr),

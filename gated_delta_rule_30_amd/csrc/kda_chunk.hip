@@ -1000,6 +1000,7 @@ struct StateParams {
   uint32_t rec_bytes;
   uint32_t rec_buf_bytes;  // the whole record buffer (addressed with 32-bit offsets)
   int seq_major;           // the chunk table's order
+  float* ckpt;             // checkpoint states (ChunkArgs::ckpt; sequence-major tables only)
 };
 
 constexpr int STATE_THREADS = 64;
@@ -1288,6 +1289,19 @@ __global__ __launch_bounds__(STATE_THREADS) __attribute__((amdgpu_waves_per_eu(1
     ps[V] = S[kt][1];
     ps[2 * V] = S[kt][2];
     ps[3 * V] = S[kt][3];
+  }
+  // a sequence that goes on past the segment: its state before chunk seg_end, the checkpoint
+  // of boundary seg_end / E (sequence-major table: entry index = chunk index in token order)
+  if (p.ckpt != nullptr && en.depth + run < nc) {
+    float* pc = p.ckpt + ((size_t)(seg_end / p.E - 1) * H + h) * (size_t)K * V + col0;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      float* ps = pc + (size_t)(16 * kt + 4 * g) * V + m;
+      ps[0] = S[kt][0];
+      ps[V] = S[kt][1];
+      ps[2 * V] = S[kt][2];
+      ps[3 * V] = S[kt][3];
+    }
   }
 }
 
@@ -1662,6 +1676,19 @@ __global__ __launch_bounds__(split_threads<K>()) __attribute__((amdgpu_waves_per
       ps[2 * V] = S[i][2];
       ps[3 * V] = S[i][3];
     }
+    // a sequence that goes on past the segment: its state before chunk seg_end, the checkpoint
+    // of boundary seg_end / E (sequence-major table: entry index = chunk index in token order)
+    if (p.ckpt != nullptr && en.depth + run < nc) {
+      float* pc = p.ckpt + ((size_t)(seg_end / p.E - 1) * H + h) * (size_t)K * V + col0;
+#pragma unroll
+      for (int i = 0; i < HKT; ++i) {
+        float* ps = pc + (size_t)(16 * (WV * HKT + i) + 4 * g) * V + m;
+        ps[0] = S[i][0];
+        ps[V] = S[i][1];
+        ps[2 * V] = S[i][2];
+        ps[3 * V] = S[i][3];
+      }
+    }
   };
   const int wv = __builtin_amdgcn_readfirstlane(wave_id());
   if (wv == 0) body(std::integral_constant<int, 0>());
@@ -1813,7 +1840,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, const ChunkPlan& pl, const 
     StateParams sp{a.v, a.o, a.init_state, run_state, entries, header, basetab,
                    seg_first + s * pl.slots, seg_count + s, s * pl.seg_entries, pl.seg_entries,
                    a.num_heads, a.dv, pl.n_slices, chains, seg_rec(s), (uint32_t)rb,
-                   (uint32_t)seg_buf, pl.seq_major};
+                   (uint32_t)seg_buf, pl.seq_major, pl.seq_major ? a.ckpt : nullptr};
     if (pl.vs != 16) return false;
     if constexpr (UFORM_OK) {
       if (urec) {

@@ -80,6 +80,10 @@ struct ChunkArgs {
   float* final_state;
   void* workspace;
   void* stream;
+  // with a sequence-major chunk table: per segment boundary s + 1 (entry (s + 1) E, E chunks per
+  // segment) the state before that chunk of the sequence it belongs to, [s][H][K][V], when the
+  // chunk is not the sequence's first (no slot is written otherwise); nullptr: none
+  float* ckpt = nullptr;
 };
 
 hipError_t launch_decode(const DecodeArgs& a);

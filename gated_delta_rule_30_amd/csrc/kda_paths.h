@@ -100,8 +100,10 @@ constexpr size_t BWD_SEGMENT_BYTES = (size_t)4 << 30;
 bool make_bwd_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv,
                    uint32_t options, int64_t seg_chunks, BwdPlan* p);
 // The plan with the longest segments whose workspace fits in `bytes` (false if none does).
+// The longest segments that fit in bytes; with step > 1, several segments are each a multiple
+// of step chunks long.
 bool fit_bwd_plan(int num_seqs, int64_t total_tokens, int num_heads, int dk, int dv,
-                  uint32_t options, size_t bytes, BwdPlan* p);
+                  uint32_t options, size_t bytes, BwdPlan* p, int64_t step = 1);
 // Chunks per segment of the default plan.
 int64_t default_bwd_segment(int num_heads, int dk, int dv);
 
@@ -119,6 +121,10 @@ struct BwdArgs {
   uint32_t options;  // KDA_OPT_* bits
   void* workspace;
   void* stream;
+  // the forward's checkpoint states (ChunkArgs::ckpt, every ckpt_interval chunks); the plan's
+  // segments are then multiples of ckpt_interval and no boundary pass runs. nullptr: none
+  const float* ckpt = nullptr;
+  int64_t ckpt_interval = 0;
 };
 hipError_t launch_chunk_bwd(const BwdArgs& a, const BwdPlan& p);
 

@@ -289,6 +289,50 @@ kda_status kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const v
                             size_t workspace_bytes, void* stream);
 
 /*
+ * Checkpoints for training: the forward keeps the state at the start of every E-th chunk
+ * (E = kda_chunk_fwd_ckpt_interval, its segment length: 2048 / H chunks of 64 tokens, at
+ * most the chunk count), and the backward starts its segments from those states instead of
+ * forming them with a pass of its own ("A Technical Breakdown", section 4: the state passed
+ * from chunk to chunk is all that links the chunks).
+ * Chunks are numbered in token order over the packed sequences (sequence n's chunks follow
+ * sequence n - 1's; a sequence's last chunk may be partial). Slot j of checkpoints
+ * ([slots][H][K][V] fp32, slots = kda_chunk_fwd_ckpt_bytes / (4 H K V)) holds, for every
+ * head, the state of the sequence that chunk (j + 1) E belongs to, just before that chunk,
+ * when that chunk is not the sequence's first; other slots are not written (the backward
+ * starts such a sequence from its initial state).
+ * kda_chunk_fwd_ckpt is kda_chunk_fwd_ex with this output (same results bit for bit; the
+ * chunk table is in token order whatever H); it supports the shapes of the training backward
+ * on the chunk path: K, V in {32, 64, 128}, bf16 inputs, or fp32 inputs at K <= 64
+ * (KDA_ERROR_NOT_SUPPORTED otherwise). checkpoints may be NULL when there are no slots, must
+ * be 16-byte aligned and must not overlap another buffer of the call.
+ * kda_chunk_bwd_ckpt is kda_chunk_bwd_ex starting from the checkpoints of a
+ * kda_chunk_fwd_ckpt call on the same inputs and options; its segments are multiples of E
+ * chunks (the longest that workspace_bytes holds; KDA_ERROR_WORKSPACE_TOO_SMALL when not even E
+ * chunks fit), and no boundary pass runs. The gradients then carry the forward's rounding of
+ * the states at the segment boundaries (the bf16 forward's states are within its 2e-2
+ * tolerance; the backward's own boundary pass keeps fp32 records); with one segment the result
+ * equals kda_chunk_bwd_ex's. checkpoints may be NULL only when there are no slots.
+ */
+int64_t kda_chunk_fwd_ckpt_interval(int32_t num_seqs, int64_t total_tokens, int32_t num_heads);
+size_t kda_chunk_fwd_ckpt_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                int32_t dk, int32_t dv);
+kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const void* log_alpha,
+                              const void* beta, const float* init_state,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                              int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype,
+                              uint32_t options, void* o, float* final_state, float* checkpoints,
+                              void* workspace, size_t workspace_bytes, void* stream);
+kda_status kda_chunk_bwd_ckpt(const void* q, const void* k, const void* v, const void* log_alpha,
+                              const void* beta, const float* init_state,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                              int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype,
+                              uint32_t options, const void* d_o, const float* d_final_state,
+                              const float* checkpoints, float* grad_q, float* grad_k,
+                              float* grad_v, float* grad_log_alpha, float* grad_beta,
+                              float* grad_init_state, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * One recurrent KDA token step per (sequence, head), state updated in place (decode).
  * The decay, prediction u = (Diag(alpha) S)^T k, erase-and-write and read are fused into one
  * pass that streams each fp32 state once from HBM and writes it once.

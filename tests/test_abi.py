@@ -23,6 +23,8 @@ def test_every_declared_symbol_is_exported():
                           "kda_chunk_fwd_scan_ex",
                           "kda_chunk_bwd", "kda_chunk_bwd_workspace_size",
                           "kda_chunk_bwd_workspace_size_ex", "kda_chunk_bwd_ex",
+                          "kda_chunk_fwd_ckpt", "kda_chunk_bwd_ckpt",
+                          "kda_chunk_fwd_ckpt_interval", "kda_chunk_fwd_ckpt_bytes",
                           "kda_decode_step", "kda_decode_step_ex", "kda_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -380,3 +382,75 @@ def test_wide_key_workspace_size():
     assert int(kda.lib().kda_chunk_fwd_scan_workspace_size(1, 1024, 2, 128, 128, 1, 4)) > 0
     # the scan keeps K = V <= 128
     assert int(kda.lib().kda_chunk_fwd_scan_workspace_size(1, 4096, 2, 256, 256, 1, 4)) == 0
+
+
+def test_ckpt_sizes():
+    """The checkpoint interval is the forward's segment length (2048 / H chunks, at most the
+    chunk count) and there is one [H][K][V] fp32 slot per segment boundary."""
+    L = kda.lib()
+    assert L.kda_chunk_fwd_ckpt_interval(1, 65536, 32) == 64
+    assert L.kda_chunk_fwd_ckpt_bytes(1, 65536, 32, 128, 128) == 15 * 32 * 128 * 128 * 4
+    assert L.kda_chunk_fwd_ckpt_interval(1, 65536, 1) == 1024    # capped at the 1024 chunks
+    assert L.kda_chunk_fwd_ckpt_bytes(1, 65536, 1, 64, 64) == 0  # one segment: no boundary
+    assert L.kda_chunk_fwd_ckpt_interval(4, 40000, 4) == 512
+    # chunk upper bound min(T, (T + N * 63) / 64) = 629 -> two segments of 512, one slot
+    assert L.kda_chunk_fwd_ckpt_bytes(4, 40000, 4, 32, 64) == 1 * 4 * 32 * 64 * 4
+    assert L.kda_chunk_fwd_ckpt_interval(0, 64, 1) == 0
+    assert L.kda_chunk_fwd_ckpt_bytes(1, 64, 1, 256, 64) == 0  # not a backward shape
+
+
+B = 1 << 36  # far enough apart that no two of these buffers overlap
+
+
+def _fwd_ckpt(L, **kw):
+    a = dict(q=B, k=2 * B, v=3 * B, g=4 * B, beta=5 * B, init=None, cu=None, N=1, T=1 << 17,
+             H=32, dk=64, dv=64, dtype=BF16, opts=0, o=6 * B, fin=7 * B, ck=8 * B, ws=9 * B,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kda_chunk_fwd_ckpt(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]),
+                                vp(a["init"]), vp(a["cu"]), a["N"], a["T"], a["H"], a["dk"],
+                                a["dv"], a["dtype"], a["opts"], vp(a["o"]), vp(a["fin"]),
+                                vp(a["ck"]), vp(a["ws"]), a["wsb"], vp(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dk=256), NOT_SUPPORTED),                 # not a backward shape
+    (dict(dtype=F32, dk=128, dv=64), NOT_SUPPORTED),  # fp32 at K = 128: the wide-key path
+    (dict(ck=None), INVALID),                      # 31 boundaries need their slots
+    (dict(ck=8 * B + 4), INVALID),                 # 16-byte alignment
+    (dict(ck=6 * B), INVALID),                     # overlaps o
+    (dict(ws=None), INVALID),
+    (dict(wsb=4096), WS_SMALL),
+    (dict(N=0), INVALID),
+])
+def test_chunk_fwd_ckpt_argument_errors(kw, expect):
+    """kda_chunk_fwd_ckpt checks its checkpoint buffer and shapes before anything is enqueued
+    (nothing is launched on these paths)."""
+    assert _fwd_ckpt(kda.lib(), **kw) == expect
+
+
+def _bwd_ckpt(L, **kw):
+    a = dict(q=B, k=2 * B, v=3 * B, g=4 * B, beta=5 * B, init=None, cu=None, N=1, T=1 << 17,
+             H=32, dk=64, dv=64, dtype=BF16, opts=0, do=6 * B, dfin=None, ck=7 * B, gq=8 * B,
+             gk=9 * B, gv=10 * B, gg=11 * B, gb=12 * B, gi=None, ws=13 * B, wsb=1 << 40,
+             stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kda_chunk_bwd_ckpt(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["beta"]),
+                                vp(a["init"]), vp(a["cu"]), a["N"], a["T"], a["H"], a["dk"],
+                                a["dv"], a["dtype"], a["opts"], vp(a["do"]), vp(a["dfin"]),
+                                vp(a["ck"]), vp(a["gq"]), vp(a["gk"]), vp(a["gv"]), vp(a["gg"]),
+                                vp(a["gb"]), vp(a["gi"]), vp(a["ws"]), a["wsb"], vp(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(ck=None), INVALID),          # the boundaries' states are required
+    (dict(ck=7 * B + 8), INVALID),     # 16-byte alignment
+    (dict(ck=8 * B), INVALID),         # overlaps a gradient
+    (dict(wsb=1 << 20), WS_SMALL),     # not even one interval of chunks fits
+    (dict(dk=256), NOT_SUPPORTED),
+])
+def test_chunk_bwd_ckpt_argument_errors(kw, expect):
+    """kda_chunk_bwd_ckpt's synchronous checks (nothing is launched on these paths)."""
+    assert _bwd_ckpt(kda.lib(), **kw) == expect
