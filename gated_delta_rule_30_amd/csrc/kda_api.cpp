@@ -210,6 +210,8 @@ extern "C" kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const voi
                          T * H * es, T * H * dv * es, sbytes, sbytes};
     for (int i = 0; i < 8; ++i)
       if (bp[i] && bn[i] && overlap(checkpoints, cb, bp[i], bn[i])) return KDA_ERROR_INVALID_VALUE;
+    if (workspace_bytes && overlap(checkpoints, cb, workspace, workspace_bytes))
+      return KDA_ERROR_INVALID_VALUE;
   }
   kda::ChunkPlan pl;
   if (!kda::make_chunk_plan(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_DTYPE_BF16, &pl))
@@ -329,6 +331,8 @@ static kda_status chunk_bwd_impl(const void* q, const void* k, const void* v,
     for (int o = 0; o < 6; ++o)
       if (out_p[o] && out_n[o] && overlap(out_p[o], out_n[o], checkpoints, cb))
         return KDA_ERROR_INVALID_VALUE;
+    if (workspace_bytes && overlap(workspace, workspace_bytes, checkpoints, cb))
+      return KDA_ERROR_INVALID_VALUE;
     step = ckpt_interval(num_seqs, total_tokens, num_heads);
     if (step < 1) return KDA_ERROR_INVALID_VALUE;
   }

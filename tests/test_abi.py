@@ -420,6 +420,7 @@ def _fwd_ckpt(L, **kw):
     (dict(ck=None), INVALID),                      # 31 boundaries need their slots
     (dict(ck=8 * B + 4), INVALID),                 # 16-byte alignment
     (dict(ck=6 * B), INVALID),                     # overlaps o
+    (dict(ck=9 * B + 256), INVALID),               # inside the workspace
     (dict(ws=None), INVALID),
     (dict(wsb=4096), WS_SMALL),
     (dict(N=0), INVALID),
@@ -448,6 +449,7 @@ def _bwd_ckpt(L, **kw):
     (dict(ck=None), INVALID),          # the boundaries' states are required
     (dict(ck=7 * B + 8), INVALID),     # 16-byte alignment
     (dict(ck=8 * B), INVALID),         # overlaps a gradient
+    (dict(ck=13 * B + 1024), INVALID),  # inside the workspace
     (dict(wsb=1 << 20), WS_SMALL),     # not even one interval of chunks fits
     (dict(dk=256), NOT_SUPPORTED),
 ])
