@@ -129,3 +129,66 @@ def test_graph_replay_scan_and_backward():
             assert torch.equal(g, r), "replay %d: gradient %d" % (rep, i)
         step()
         torch.cuda.synchronize()
+
+
+def test_graph_replay_checkpointed_training_pair():
+    """kda_chunk_fwd_ckpt then kda_chunk_bwd_ckpt (32 heads, three checkpoint boundaries,
+    backward segments of one interval) captured into one graph and replayed three times with
+    eager work between: outputs, checkpoints and gradients equal the eager ones bit for bit."""
+    print("graph capture of chunk_fwd_ckpt + chunk_bwd_ckpt", flush=True)
+    T, H, K = 16384, 32, 32
+    inp = workloads.gen_forward(T, H, K, K, dtype=torch.bfloat16, device=DEV, seed=23,
+                                init_std=0.1)
+    E = kda.ckpt_interval(1, T, H)
+    ck = kda.ckpt_empty(1, T, H, K, K, DEV)
+    assert ck.shape[0] == 3
+    wsf = torch.empty(kda.workspace_size(1, T, H, K, K, torch.bfloat16), dtype=torch.uint8,
+                      device=DEV)
+    wsb = torch.empty(kda.bwd_workspace_size(1, T, H, K, K, torch.bfloat16,
+                                             segment_tokens=64 * E), dtype=torch.uint8, device=DEV)
+    o = torch.empty((T, H, K), dtype=torch.bfloat16, device=DEV)
+    fin = torch.empty((1, H, K, K), device=DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    d_o = torch.randn((T, H, K), generator=gen, device=DEV).to(torch.bfloat16)
+    dfin = torch.randn((1, H, K, K), generator=gen, device=DEV)
+    f32 = dict(dtype=torch.float32, device=DEV)
+    grads = (torch.empty((T, H, K), **f32), torch.empty((T, H, K), **f32),
+             torch.empty((T, H, K), **f32), torch.empty((T, H, K), **f32),
+             torch.empty((T, H), **f32), torch.empty((1, H, K, K), **f32))
+
+    def step():
+        kda.chunk_fwd(*(inp[x] for x in ORDER), init_state=inp["init_state"], o=o,
+                      final_state=fin, workspace=wsf, checkpoints=ck)
+        kda.chunk_bwd(*(inp[x] for x in ORDER), d_o, init_state=inp["init_state"],
+                      d_final_state=dfin, workspace=wsb, grads=grads, checkpoints=ck)
+
+    step()
+    torch.cuda.synchronize()
+    o_ref, fin_ref, ck_ref = o.clone(), fin.clone(), ck.clone()
+    g_ref = [g.clone() for g in grads]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        o.fill_(float("nan"))
+        fin.zero_()
+        ck.fill_(float("nan"))
+        for g in grads:
+            g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), "replay %d: o" % rep
+        assert torch.equal(fin, fin_ref), "replay %d: final state" % rep
+        assert torch.equal(ck, ck_ref), "replay %d: checkpoints" % rep
+        for i, (g, r) in enumerate(zip(grads, g_ref)):
+            assert torch.equal(g, r), "replay %d: gradient %d" % (rep, i)
+        step()
+        torch.cuda.synchronize()
