@@ -195,7 +195,8 @@ extern "C" kda_status kda_chunk_fwd_ckpt(const void* q, const void* k, const voi
                                          o, final_state, stream, &a);
   if (st != KDA_SUCCESS) return st;
   // the shapes the training backward takes, on the chunk path
-  if (!supported_chunk_dk(dk) || !supported_chunk_dk(dv) || wide_path(dk, dtype, options))
+  if (!supported_chunk_dk(dk) || !(supported_chunk_dk(dv) || dv == 256) ||
+      wide_path(dk, dtype, options))
     return KDA_ERROR_NOT_SUPPORTED;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return KDA_ERROR_INVALID_VALUE;
@@ -242,8 +243,9 @@ static kda_status check_bwd_shape(int32_t num_seqs, int64_t total_tokens, int32_
                                   int32_t dk, int32_t dv, kda_dtype dtype) {
   if (num_seqs <= 0 || num_heads <= 0 || total_tokens < 0 || total_tokens > kMaxTokens)
     return KDA_ERROR_INVALID_VALUE;
-  // the gradient kernels hold up to three 64 x V fp32 blocks in LDS: V <= 128
-  if (!valid_dtype(dtype) || !supported_chunk_dk(dk) || !supported_chunk_dk(dv))
+  // K <= 128 (the record kernel's and gradient kernels' channel parts); V up to 256 (value
+  // columns in parts of 64)
+  if (!valid_dtype(dtype) || !supported_chunk_dk(dk) || !(supported_chunk_dk(dv) || dv == 256))
     return KDA_ERROR_NOT_SUPPORTED;
   return KDA_SUCCESS;
 }
@@ -417,7 +419,7 @@ extern "C" int64_t kda_chunk_fwd_ckpt_interval(int32_t num_seqs, int64_t total_t
 extern "C" size_t kda_chunk_fwd_ckpt_bytes(int32_t num_seqs, int64_t total_tokens,
                                            int32_t num_heads, int32_t dk, int32_t dv) {
   if (num_seqs <= 0 || num_heads <= 0 || total_tokens < 0 || total_tokens > kMaxTokens ||
-      !supported_chunk_dk(dk) || !supported_chunk_dk(dv))
+      !supported_chunk_dk(dk) || !(supported_chunk_dk(dv) || dv == 256))
     return 0;
   return ckpt_bytes(num_seqs, total_tokens, num_heads, dk, dv);
 }

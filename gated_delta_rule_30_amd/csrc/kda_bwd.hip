@@ -630,11 +630,27 @@ __global__ __launch_bounds__(NTGA, 2) void bwd_ga_kernel(
   // rowsum(S * X) rides along with the products, so that neither state is read twice: while
   // a part of S is in LDS each thread keeps EPT of its values (key channel rm, columns rc ..;
   // TPR neighbouring threads share a channel) and multiplies them with the same part of X in
-  // the second loop
+  // the second loop. With more than two parts (V = 256) the kept values would not fit in
+  // registers: a pass of its own over both states forms the sum first instead.
   constexpr int NPART = V / VC, EPT = K * VC / NTGA, TPR = VC / EPT;
+  constexpr bool FUSE = NPART <= 2;
   static_assert(EPT >= 1 && K * VC == EPT * NTGA && TPR <= 64, "rowsum split");
   const int rm = threadIdx.x / TPR, rc = (threadIdx.x % TPR) * EPT;
-  float keep[NPART][EPT];
+  float keep[FUSE ? NPART : 1][EPT];
+  if constexpr (!FUSE) {
+    constexpr int NP = NTGA / K < V / 4 ? NTGA / K : V / 4, VP = V / NP;
+    if (threadIdx.x < K * NP) {
+      const int m = threadIdx.x / NP, part = threadIdx.x % NP;
+      float s = 0.f;
+#pragma unroll
+      for (int vv = 0; vv < VP; vv += 4)
+        s += dot4(*reinterpret_cast<const f32x4*>(S + m * V + part * VP + vv),
+                  *reinterpret_cast<const f32x4*>(X + m * V + part * VP + vv));
+#pragma unroll
+      for (int o = 1; o < NP; o <<= 1) s += __shfl_xor(s, o);
+      if (part == 0) sc[G::oDG + m] = s;
+    }
+  }
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   // dO S^T and dW = -dDelta S^T
   {
@@ -650,8 +666,10 @@ __global__ __launch_bounds__(NTGA, 2) void bwd_ga_kernel(
       lds_barrier();
       mmx_acc<K, VC, false, true, L, L, NTGA>(sO, sS, r1);
       mmx_acc<K, VC, false, true, L, L, NTGA>(sD, sS, dw);
+      if constexpr (FUSE) {
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) keep[pi][e] = sS[rm * L + rc + e];
+        for (int e = 0; e < EPT; ++e) keep[pi][e] = sS[rm * L + rc + e];
+      }
       lds_barrier();
     }
     mmf_out<K, NTGA>(r1, [&](int r, int m, float x) { sc[G::oR1 + r * K + m] = x; });
@@ -674,13 +692,17 @@ __global__ __launch_bounds__(NTGA, 2) void bwd_ga_kernel(
       lds_barrier();
       mmx_acc<K, VC, false, true, L, L, NTGA>(sD, sS, dk);
       mmx_acc<BC, VC, false, true, L, L, NTGA>(sO, sD, dp);
+      if constexpr (FUSE) {
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) dg += keep[pi][e] * sS[rm * L + rc + e];
+        for (int e = 0; e < EPT; ++e) dg += keep[FUSE ? pi : 0][e] * sS[rm * L + rc + e];
+      }
       lds_barrier();
     }
+    if constexpr (FUSE) {
 #pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) dg += __shfl_xor(dg, o);
-    if (threadIdx.x % TPR == 0) sc[G::oDG + rm] = dg;
+      for (int o = 1; o < TPR; o <<= 1) dg += __shfl_xor(dg, o);
+      if (threadIdx.x % TPR == 0) sc[G::oDG + rm] = dg;
+    }
     mmf_out<K, NTGA>(dk, [&](int r, int m, float x) { sc[G::oDKt + r * K + m] = x; });
     mmf_out<BC, NTGA>(dp, [&](int i, int j, float x) {
       if (j <= i) sc[G::oDPA + i * BC + j] = x;
@@ -1024,6 +1046,7 @@ static BwdFloats bwd_floats(int K, int V) {
   KDA_BWD_FLOATS(32, 32) KDA_BWD_FLOATS(32, 64) KDA_BWD_FLOATS(32, 128)
   KDA_BWD_FLOATS(64, 32) KDA_BWD_FLOATS(64, 64) KDA_BWD_FLOATS(64, 128)
   KDA_BWD_FLOATS(128, 32) KDA_BWD_FLOATS(128, 64) KDA_BWD_FLOATS(128, 128)
+  KDA_BWD_FLOATS(32, 256) KDA_BWD_FLOATS(64, 256) KDA_BWD_FLOATS(128, 256)
 #undef KDA_BWD_FLOATS
   return BwdFloats{0, 0, 0};
 }
@@ -1214,6 +1237,7 @@ hipError_t launch_chunk_bwd(const BwdArgs& a, const BwdPlan& p) {
   KDA_BWD_CASE(32, 32) KDA_BWD_CASE(32, 64) KDA_BWD_CASE(32, 128)
   KDA_BWD_CASE(64, 32) KDA_BWD_CASE(64, 64) KDA_BWD_CASE(64, 128)
   KDA_BWD_CASE(128, 32) KDA_BWD_CASE(128, 64) KDA_BWD_CASE(128, 128)
+  KDA_BWD_CASE(32, 256) KDA_BWD_CASE(64, 256) KDA_BWD_CASE(128, 256)
 #undef KDA_BWD_CASE
   if (e != hipSuccess || a.options == 0) return e;
   launch_bwd_epilogue(OptInputs{a.q, a.k, a.g, a.beta}, a.dtype_bf16, a.total_tokens,

@@ -238,9 +238,9 @@ kda_status kda_chunk_fwd_scan_ex(const void* q, const void* k, const void* v,
  *                    it is still the gradient with respect to the zero initial state.
  * Gradients of rows past the end of every sequence are not written (there are none: cu_seqlens
  * covers all rows). No gradient buffer may overlap an input or another gradient
- * (KDA_ERROR_INVALID_VALUE). Head dims K, V in {32, 64, 128}, both dtypes; others give
- * KDA_ERROR_NOT_SUPPORTED. Every gradient is the same bit for bit on every run (no atomics;
- * sums in a fixed order).
+ * (KDA_ERROR_INVALID_VALUE). Head dims K in {32, 64, 128}, V in {32, 64, 128, 256}, both
+ * dtypes; others give KDA_ERROR_NOT_SUPPORTED. Every gradient is the same bit for bit on every
+ * run (no atomics; sums in a fixed order).
  *
  * Workspace (256-byte aligned): the chunks are taken in segments, processed from the last
  * backwards; each segment holds, per (chunk, head), an fp32 record, the chunk-start state, the
@@ -302,7 +302,8 @@ kda_status kda_chunk_bwd_ex(const void* q, const void* k, const void* v, const v
  * starts such a sequence from its initial state).
  * kda_chunk_fwd_ckpt is kda_chunk_fwd_ex with this output (same results bit for bit; the
  * chunk table is in token order whatever H); it supports the shapes of the training backward
- * on the chunk path: K, V in {32, 64, 128}, bf16 inputs, or fp32 inputs at K <= 64
+ * on the chunk path: K in {32, 64, 128}, V in {32, 64, 128, 256}, bf16 inputs, or fp32 inputs at
+ * K <= 64
  * (KDA_ERROR_NOT_SUPPORTED otherwise). checkpoints may be NULL when there are no slots, must
  * be 16-byte aligned and must not overlap another buffer of the call.
  * kda_chunk_bwd_ckpt is kda_chunk_bwd_ex starting from the checkpoints of a

@@ -269,7 +269,8 @@ def _bwd(L, **kw):
     (dict(T=-1), INVALID),
     (dict(N=3, T=128), INVALID),            # equal lengths need T % N == 0
     (dict(dk=48), NOT_SUPPORTED),
-    (dict(dv=256), NOT_SUPPORTED),          # the gradient kernels hold V <= 128 in LDS
+    (dict(dk=256), NOT_SUPPORTED),          # K <= 128 (V may be 256)
+    (dict(dv=512), NOT_SUPPORTED),
     (dict(dtype=7), NOT_SUPPORTED),
     (dict(q=None), INVALID),
     (dict(do=None), INVALID),
@@ -297,7 +298,8 @@ def test_bwd_workspace_size():
     # segment of the default size)
     a, b = ws(1, 16384, 4, 128, 128, 1), ws(1, 2 * 16384, 4, 128, 128, 1)
     assert 1.9 < b / a < 2.1
-    assert ws(1, 65536, 4, 128, 256, 1) == 0
+    assert ws(1, 65536, 4, 128, 256, 1) > 0     # V = 256 (value columns in parts of 64)
+    assert ws(1, 65536, 4, 256, 128, 1) == 0
     assert ws(0, 100, 4, 64, 64, 1) == 0
     assert ws(1, 0, 4, 64, 64, 0) > 0
 
@@ -322,7 +324,7 @@ def test_bwd_workspace_is_bounded():
     # segments of three chunks: a third of the boundary states
     assert ex(1, 65536, 32, 128, 128, 1, 192) < 0.4 * small
     assert ex(1, 65536, 32, 128, 128, 1, 1) == small  # rounded up to whole chunks
-    assert ex(1, 65536, 32, 128, 256, 1, 64) == 0
+    assert ex(1, 65536, 32, 256, 128, 1, 64) == 0
     # input options add the processed q, k, log alpha (fp32) and beta for every token, and with
     # the scalar gate the per-channel gradient of log alpha
     T, H, K = 65536, 4, 128
@@ -364,9 +366,9 @@ def test_chunk_bwd_ex_argument_errors(opts, kw, expect):
 def test_wide_key_workspace_size():
     import torch
     ws = lambda *a: kda.workspace_size(*a)
-    # K = 256 takes the wide-key path: fp32 records for one segment of chunks at a time (512 MiB
-    # of records) and the option pass's output for its tokens, so past one segment only the
-    # chunk table and a running state grow with T
+    # K = 256: one segment's records at a time (bf16 inputs: the chunk path's buffer of 2048
+    # records; fp32: the wide-key path's 512 MiB of fp32 records and the option pass's output),
+    # so past one segment only the chunk table and a running state grow with T
     a, b = ws(1, 16384, 4, 256, 128, torch.bfloat16), ws(1, 32768, 4, 256, 128, torch.bfloat16)
     assert a > 0 and 1.9 < b / a < 2.1                 # one segment each (256 and 512 chunks)
     c, d = ws(1, 65536, 32, 256, 256, torch.bfloat16), ws(1, 1 << 20, 32, 256, 256, torch.bfloat16)

@@ -48,6 +48,8 @@ def _run(inp, cu=None, N=1, with_init=True, with_dfinal=True, seed=0, dtype=torc
     (1000, 1, 128, 128, torch.bfloat16),
     (700, 2, 64, 128, torch.bfloat16),    # K != V
     (333, 2, 128, 32, torch.bfloat16),
+    (333, 2, 128, 256, torch.bfloat16),   # V = 256: four parts of 64 value columns
+    (200, 2, 32, 256, torch.float32),
 ])
 def test_bwd_matches_oracle(T, H, K, V, dtype):
     print("bwd", T, H, K, V, dtype, flush=True)

@@ -23,6 +23,7 @@ CASES = [
     (32, 64, 64, torch.bfloat16, [5000, 0, 7000, 300]),
     (4, 32, 64, torch.bfloat16, [20000, 15000, 6000]),
     (32, 32, 32, torch.float32, [9000, 4100]),
+    (32, 64, 256, torch.bfloat16, [6000, 2500]),
 ]
 
 
