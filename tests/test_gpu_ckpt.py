@@ -24,6 +24,9 @@ CASES = [
     (4, 32, 64, torch.bfloat16, [20000, 15000, 6000]),
     (32, 32, 32, torch.float32, [9000, 4100]),
     (32, 64, 256, torch.bfloat16, [6000, 2500]),
+    # a sequence starting exactly at a boundary (chunk 64): that slot is not written, and the
+    # backward segment starting there begins from the sequence's initial state
+    (32, 32, 64, torch.bfloat16, [4096, 5000, 3000]),
 ]
 
 
